@@ -1,0 +1,447 @@
+/*
+ * Selected-token sparse attention with KV append: the CPU ORACLE.
+ *
+ * This file is test infrastructure. It is the plain, slow, obviously-correct
+ * statement of what the hot path computes, and only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it. The product library
+ * never links, calls or includes anything from here, and nothing here includes
+ * the product's headers: the constants, codecs and rules below are written
+ * out independently.
+ *
+ * Sources (docs.rs source pages):
+ *   [IS]  onnx-runtime-ep-cuda, src/kernels/index_share.rs (IndexShare):
+ *         module doc "Determinism / bit-parity", kernels `build_present`,
+ *         `build_present_capacity`, `validate_index_rows`, `index_share_row`,
+ *         host `validate_indices` / `index_error`, `launch_rows` (default scale).
+ *   [CPU] onnx-runtime-ep-cpu, src/kernels/compressed_sparse_attention.rs
+ *         (CSA CPU oracle): `CacheFormat` (record layout, `stored_width`),
+ *         `dequantize_cache`, `finalize_attention_record` (pack loop),
+ *         `dot` / `accumulate_value` (strict ascending fp32 folds).
+ *   [CSA] onnx-runtime-ep-cuda, src/kernels/compressed_sparse_attention.rs:
+ *         the sink-attention kernels' in-line record decode (E8M0 scale times
+ *         E4M3FN code; BF16 tail read as bits << 16), exp via double.
+ *   [ATT] onnx-runtime-ep-cuda, src/kernels/standard_attention.rs: module doc
+ *         "Semantics" (softcap after the scaled scores, before the softmax).
+ *
+ * Arithmetic rules: every float operation is a single fp32 operation, in the
+ * order written, with no FMA contraction and no reassociation (build with
+ * -O2 -ffp-contract=off -fno-fast-math). exp and tanh are evaluated in double
+ * and rounded to fp32 once, as the CSA kernels do for exp.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - K and V may be one shared-latent cache (V = first Dv dims of the K row).
+ *  - The E8M0 scale of the fp8 quantizer is floor(log2(amax)) - 8 + 127
+ *    (OCP MX rule); E4M3FN codes round to nearest even and saturate to 448.
+ *  - A row whose scores are all -inf yields zeros ([IS] `index_share_row`).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+/* ---- storage codes (oracle-local numbering) ----------------------------- */
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_FP8_BLOCK64 = 3 };
+enum { OR_LAYOUT_SEPARATE = 0, OR_LAYOUT_SHARED_LATENT = 1 };
+
+/* validation classes, in the pages' check order ([IS] `validate_indices`) */
+enum {
+  OR_OK = 0,
+  OR_SENTINEL = 1,   /* index < -1                                   */
+  OR_AFTER_PAD = 2,  /* a non-(-1) index after trailing -1 padding    */
+  OR_RANGE = 3,      /* index >= cache length of the batch            */
+  OR_DUPLICATE = 4,  /* index == previous valid index                 */
+  OR_ORDER = 5,      /* index <  previous valid index                 */
+  OR_ALL_PAD = 6     /* no valid index in the row                     */
+};
+
+/* ---- bf16 / f16 widening and bf16 narrowing ----------------------------- */
+
+/* bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits. */
+static float or_bf16_to_f32(uint16_t bits) {
+  uint32_t w = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &w, 4);
+  return f;
+}
+
+/* IEEE binary16 -> fp32, exact, written from the format definition. */
+static float or_f16_to_f32(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int exp = (h >> 10) & 0x1f;
+  int man = h & 0x3ff;
+  double v;
+  if (exp == 0) {
+    v = ldexp((double)man, -24); /* subnormal: man * 2^-24 */
+  } else if (exp == 31) {
+    v = man ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(man + 1024), exp - 25); /* (1 + man/1024) * 2^(exp-15) */
+  }
+  return (float)(sign ? -v : v);
+}
+
+/* fp32 -> bf16 round to nearest, ties to even; NaN stays a quiet NaN. */
+uint16_t oracle_bf16_from_f32(float x) {
+  uint32_t w;
+  memcpy(&w, &x, 4);
+  if ((w & 0x7f800000u) == 0x7f800000u && (w & 0x007fffffu)) {
+    return (uint16_t)((w >> 16) | 0x0040u);
+  }
+  uint32_t upper = w >> 16;
+  uint32_t lower = w & 0xffffu;
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+  return (uint16_t)upper;
+}
+
+static float or_load(const void* base, int64_t i, int dtype) {
+  switch (dtype) {
+    case OR_F32: return ((const float*)base)[i];
+    case OR_F16: return or_f16_to_f32(((const uint16_t*)base)[i]);
+    default: return or_bf16_to_f32(((const uint16_t*)base)[i]);
+  }
+}
+
+/* ---- fp8_e4m3_block64 record codec ([CPU] `CacheFormat`) ----------------- */
+
+/* E8M0 scale byte: 2^(e-127); 255 is NaN. */
+double oracle_e8m0_value(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* E4M3FN code: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; exponent 0 encodes subnormals M * 2^-9. */
+double oracle_e4m3fn_value(uint8_t code) {
+  int s = code >> 7, E = (code >> 3) & 0xf, M = code & 7;
+  double v;
+  if (E == 15 && M == 7) return NAN;
+  if (E == 0) v = ldexp((double)M, -9);
+  else v = ldexp(1.0 + M / 8.0, E - 7);
+  return s ? -v : v;
+}
+
+/* Round a non-negative double to the nearest integer, ties to even. */
+static double or_rne(double q) {
+  double f = floor(q), r = q - f;
+  if (r > 0.5 || (r == 0.5 && fmod(f, 2.0) != 0.0)) f += 1.0;
+  return f;
+}
+
+/* Encode one already-scaled value into E4M3FN: nearest-even, saturate at 448. */
+static uint8_t or_e4m3fn_encode(double v) {
+  uint8_t s = (v < 0 || (v == 0 && signbit(v))) ? 0x80 : 0x00;
+  double a = fabs(v);
+  uint8_t mag;
+  if (a >= 448.0) {
+    mag = 0x7e; /* 1.75 * 2^8, the largest finite code */
+  } else if (a < ldexp(1.0, -6)) {
+    /* subnormal range: spacing 2^-9; 8 * 2^-9 is the smallest normal, whose
+     * code 0x08 follows code 0x07 in the bit pattern, so m == 8 needs no case */
+    mag = (uint8_t)or_rne(a / ldexp(1.0, -9));
+  } else {
+    int e = (int)floor(log2(a));
+    /* guard log2 rounding at exact powers of two */
+    if (ldexp(1.0, e) > a) e -= 1;
+    if (ldexp(1.0, e + 1) <= a) e += 1;
+    double m = or_rne(a / ldexp(1.0, e - 3)); /* in [8, 16] */
+    if (m == 16.0) { e += 1; m = 8.0; }
+    int code = ((e + 7) << 3) | ((int)m - 8);
+    mag = (uint8_t)(code > 0x7e ? 0x7e : code);
+  }
+  return (uint8_t)(s | mag);
+}
+
+/* Quantize one 64-value block: returns 0, or -1 if a value is not finite
+ * (the CSA oracle rejects non-finite inputs before packing).
+ * amax == 0 -> scale byte 127 and all-zero codes. Otherwise
+ * e = clamp(floor(log2 amax) - 8 + 127, 0, 254) and
+ * code_i = E4M3FN_RNE_sat(x_i * 2^-(e-127)); the scaling is exact in double. */
+int oracle_fp8_quantize_block64(const float* x, uint8_t* scale_out, uint8_t* codes) {
+  float amax = 0.0f;
+  for (int i = 0; i < 64; i++) {
+    if (!isfinite(x[i])) return -1;
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  if (amax == 0.0f) {
+    *scale_out = 127;
+    memset(codes, 0, 64);
+    return 0;
+  }
+  int k;
+  frexp((double)amax, &k); /* amax = f * 2^k with f in [0.5, 1) */
+  k -= 1;                  /* floor(log2(amax)) */
+  int e = k - 8 + 127;
+  if (e < 0) e = 0;
+  if (e > 254) e = 254;
+  *scale_out = (uint8_t)e;
+  for (int i = 0; i < 64; i++) codes[i] = or_e4m3fn_encode(ldexp((double)x[i], 127 - e));
+  return 0;
+}
+
+/* Width in bytes of one record holding `dk` logical dims whose last `rope`
+ * dims are a BF16 tail: (dk - rope)/64 blocks of 65 bytes + 2 * rope. */
+int64_t oracle_fp8_record_bytes(int64_t dk, int64_t rope) {
+  if (rope < 0 || rope > dk || (dk - rope) % 64 != 0) return -1;
+  return (dk - rope) / 64 * 65 + 2 * rope;
+}
+
+/* Pack one logical row (fp32 values; the tail values must already be bf16
+ * representable or they are rounded RNE) into a record. Returns 0 or -1. */
+int oracle_fp8_pack_record(const float* row, int64_t dk, int64_t rope, uint8_t* rec) {
+  int64_t blocks = (dk - rope) / 64;
+  for (int64_t j = 0; j < blocks; j++) {
+    if (oracle_fp8_quantize_block64(row + 64 * j, rec + 65 * j, rec + 65 * j + 1) != 0) return -1;
+  }
+  uint8_t* tail = rec + 65 * blocks;
+  for (int64_t i = 0; i < rope; i++) {
+    float v = row[dk - rope + i];
+    if (!isfinite(v)) return -1;
+    uint16_t b = oracle_bf16_from_f32(v);
+    tail[2 * i] = (uint8_t)(b & 0xff); /* little-endian */
+    tail[2 * i + 1] = (uint8_t)(b >> 8);
+  }
+  return 0;
+}
+
+/* Decode one record to `dk` fp32 values ([CPU] `dequantize_cache`).
+ * Returns 0, or -1 if a scale byte or a code is NaN. */
+int oracle_fp8_decode_record(const uint8_t* rec, int64_t dk, int64_t rope, float* out) {
+  int64_t blocks = (dk - rope) / 64;
+  for (int64_t j = 0; j < blocks; j++) {
+    double s = oracle_e8m0_value(rec[65 * j]);
+    if (isnan(s)) return -1;
+    for (int i = 0; i < 64; i++) {
+      double c = oracle_e4m3fn_value(rec[65 * j + 1 + i]);
+      if (isnan(c)) return -1;
+      out[64 * j + i] = (float)(c * s);
+    }
+  }
+  const uint8_t* tail = rec + 65 * blocks;
+  for (int64_t i = 0; i < rope; i++) {
+    uint16_t b = (uint16_t)(tail[2 * i] | (tail[2 * i + 1] << 8));
+    out[dk - rope + i] = or_bf16_to_f32(b);
+  }
+  return 0;
+}
+
+/* ---- A1: KV append ([IS] `build_present` / `build_present_capacity`) ---- */
+
+/* present[b,h,t,:] = past[b,h,t,:] for t < past_len[b];
+ *                  = cur[b,h,t-past_len[b],:] for past_len[b] <= t < past_len[b]+cur_len.
+ * Rows are `row_bytes` wide and copied as bytes (the concat is a pure copy).
+ * When present == past (in-place, capacity layout) only the new rows are
+ * written. Rows of present at or beyond past_len[b]+cur_len are untouched.
+ * Returns 0, or -1 if a length does not fit its capacity. */
+int oracle_kv_append(const uint8_t* past, int64_t past_cap, const int64_t* past_len,
+                     const uint8_t* cur, int64_t cur_len, uint8_t* present,
+                     int64_t present_cap, int64_t batch, int64_t heads, int64_t row_bytes) {
+  for (int64_t b = 0; b < batch; b++) {
+    if (past_len[b] < 0 || past_len[b] > past_cap || past_len[b] + cur_len > present_cap) return -1;
+  }
+  for (int64_t b = 0; b < batch; b++) {
+    for (int64_t h = 0; h < heads; h++) {
+      uint8_t* dst = present + (b * heads + h) * present_cap * row_bytes;
+      if (present != past) {
+        const uint8_t* src = past + (b * heads + h) * past_cap * row_bytes;
+        for (int64_t t = 0; t < past_len[b]; t++)
+          memcpy(dst + t * row_bytes, src + t * row_bytes, (size_t)row_bytes);
+      }
+      const uint8_t* c = cur + (b * heads + h) * cur_len * row_bytes;
+      for (int64_t t = 0; t < cur_len; t++)
+        memcpy(dst + (past_len[b] + t) * row_bytes, c + t * row_bytes, (size_t)row_bytes);
+    }
+  }
+  return 0;
+}
+
+/* ---- A3: index validation ([IS] host `validate_indices`) ---------------- */
+
+static int64_t or_load_index(const void* idx, int64_t i, int is_i64) {
+  return is_i64 ? ((const int64_t*)idx)[i] : (int64_t)((const int32_t*)idx)[i];
+}
+
+/* Scan one row's columns in ascending order, exactly as the host validator
+ * does, and return its class (OR_OK if valid). *bad_col receives the column
+ * of the first violation, or `width` for an all-padding row. */
+static int or_validate_row(const void* idx, int is_i64, int64_t base, int64_t width,
+                           int64_t bound, int64_t* bad_col) {
+  int padding = 0;
+  int64_t count = 0, previous = 0;
+  for (int64_t col = 0; col < width; col++) {
+    int64_t v = or_load_index(idx, base + col, is_i64);
+    if (v == -1) { padding = 1; continue; }
+    int cls = OR_OK;
+    if (v < -1) cls = OR_SENTINEL;
+    else if (padding) cls = OR_AFTER_PAD;
+    else if (v >= bound) cls = OR_RANGE;
+    else if (count > 0 && v == previous) cls = OR_DUPLICATE;
+    else if (count > 0 && v < previous) cls = OR_ORDER;
+    if (cls != OR_OK) { *bad_col = col; return cls; }
+    previous = v;
+    count += 1;
+  }
+  if (count == 0) { *bad_col = width; return OR_ALL_PAD; }
+  *bad_col = -1;
+  return OR_OK;
+}
+
+/* Validate all rows in (batch, index_head, query) order. row_class[r] gets
+ * each row's class. Returns the OR of (1 << (class-1)) over invalid rows,
+ * plus 512 if any row is invalid (the IndexShare capture-error bit); the
+ * first failing row/column/class and the pages' message are reported. */
+uint32_t oracle_validate_indices(const void* idx, int is_i64, int64_t batch, int64_t index_heads,
+                                 int64_t q_seq, int64_t width, const int64_t* bound,
+                                 uint8_t* row_class, int64_t* first_row, int64_t* first_col,
+                                 int* first_class, char* msg, int64_t msg_len) {
+  uint32_t word = 0;
+  *first_row = -1;
+  *first_col = -1;
+  *first_class = OR_OK;
+  if (msg && msg_len > 0) msg[0] = 0;
+  for (int64_t b = 0; b < batch; b++) {
+    for (int64_t h = 0; h < index_heads; h++) {
+      for (int64_t q = 0; q < q_seq; q++) {
+        int64_t row = (b * index_heads + h) * q_seq + q;
+        int64_t col;
+        int cls = or_validate_row(idx, is_i64, row * width, width, bound[b], &col);
+        row_class[row] = (uint8_t)cls;
+        if (cls == OR_OK) continue;
+        word |= (1u << (cls - 1)) | 512u;
+        if (*first_row >= 0) continue;
+        *first_row = row;
+        *first_col = col;
+        *first_class = cls;
+        if (!msg || msg_len <= 0) continue;
+        int64_t v = cls == OR_ALL_PAD ? -1 : or_load_index(idx, row * width + col, is_i64);
+        int64_t prev = col > 0 ? or_load_index(idx, row * width + col - 1, is_i64) : 0;
+        char head[160];
+        snprintf(head, sizeof head, "selected_indices [batch=%lld, head=%lld, query=%lld, column=%lld]: ",
+                 (long long)b, (long long)h, (long long)q, (long long)col);
+        switch (cls) {
+          case OR_SENTINEL:
+            snprintf(msg, (size_t)msg_len, "%sinvalid sentinel %lld", head, (long long)v);
+            break;
+          case OR_AFTER_PAD:
+            snprintf(msg, (size_t)msg_len, "%sindex %lld follows trailing -1 padding", head, (long long)v);
+            break;
+          case OR_RANGE:
+            snprintf(msg, (size_t)msg_len, "%sindex %lld is out of range for cache length %lld", head,
+                     (long long)v, (long long)bound[b]);
+            break;
+          case OR_DUPLICATE:
+            snprintf(msg, (size_t)msg_len, "%sduplicate index %lld", head, (long long)v);
+            break;
+          case OR_ORDER:
+            snprintf(msg, (size_t)msg_len, "%sindices are not strictly increasing: %lld then %lld", head,
+                     (long long)prev, (long long)v);
+            break;
+          default:
+            snprintf(msg, (size_t)msg_len, "selected_indices row [batch=%lld, head=%lld, query=%lld] is all -1",
+                     (long long)b, (long long)h, (long long)q);
+        }
+      }
+    }
+  }
+  return word;
+}
+
+/* ---- A4-A8, A10: the forward ([IS] `index_share_row`) ------------------- */
+
+/* Load logical dim d of cache row (b, h, t) as fp32. For fp8 records the
+ * whole row is decoded into `scratch` once per (row, key) by the caller. */
+static const float* or_cache_row(const void* cache, int fmt, int64_t row_index, int64_t row_elems,
+                                 int64_t dk, int64_t rope, int64_t record_bytes, float* scratch) {
+  if (fmt == OR_FP8_BLOCK64) {
+    if (oracle_fp8_decode_record((const uint8_t*)cache + row_index * record_bytes, dk, rope, scratch) != 0)
+      return NULL;
+    return scratch;
+  }
+  for (int64_t d = 0; d < row_elems; d++) scratch[d] = or_load(cache, row_index * row_elems + d, fmt);
+  return scratch;
+}
+
+/*
+ * Output rows [row_begin, row_end) of the flattened (b, h, q) order.
+ *   q      [B, Hq, Sq, Dk]   in q_dtype (0 f32, 1 f16, 2 bf16)
+ *   kcache [B, Hkv, cap, Dk] in cache_fmt (0/1/2, or 3 = fp8 records)
+ *   vcache [B, Hkv, cap, Dv] (SEPARATE) or NULL (SHARED_LATENT: V = K[..., :Dv])
+ *   idx    [B, Hi, Sq, W]    i32 or i64, rows already valid
+ *   y      [B, Hq, Sq, Dv]   fp32 (the caller rounds to its storage dtype)
+ * scale == 0 means 1/sqrtf(Dk); softcap == 0 means off.
+ * work: 2*Dk + W floats of scratch.
+ * Returns 0, or -1 on a record that decodes to NaN or an index out of range.
+ */
+int oracle_forward_rows(const void* q, int q_dtype, const void* kcache, const void* vcache,
+                        int cache_fmt, int kv_layout, int64_t cap, const void* idx, int idx_is_i64,
+                        int64_t batch, int64_t hq, int64_t hkv, int64_t sq, int64_t index_heads,
+                        int64_t width, int64_t dk, int64_t dv, int64_t rope, float scale,
+                        float softcap, int64_t row_begin, int64_t row_end, float* y, float* work) {
+  (void)batch;
+  const int64_t group = hq / hkv;
+  const int64_t record_bytes = cache_fmt == OR_FP8_BLOCK64 ? oracle_fp8_record_bytes(dk, rope) : 0;
+  if (scale == 0.0f) scale = 1.0f / sqrtf((float)dk); /* [IS] `launch_rows` default */
+  const float ss = sqrtf(scale);
+  float* krow = work;
+  float* vrow = work + dk;
+  float* p = work + 2 * dk;
+  for (int64_t row = row_begin; row < row_end; row++) {
+    const int64_t qi = row % sq;
+    const int64_t h = (row / sq) % hq;
+    const int64_t b = row / (sq * hq);
+    const int64_t kvh = h / group;
+    const int64_t ih = index_heads == 1 ? 0 : h;
+    const int64_t ibase = ((b * index_heads + ih) * sq + qi) * width;
+    const int64_t qbase = row * dk;
+    float* yrow = y + row * dv;
+    /* A4: n = entries before the first -1 */
+    int64_t n = 0;
+    while (n < width && or_load_index(idx, ibase + n, idx_is_i64) != -1) n++;
+    /* A5 + A6: gather each selected key, scaled dot product, then softcap */
+    for (int64_t s = 0; s < n; s++) {
+      int64_t key = or_load_index(idx, ibase + s, idx_is_i64);
+      if (key < 0 || key >= cap) return -1;
+      int64_t kr = (b * hkv + kvh) * cap + key;
+      if (!or_cache_row(kcache, cache_fmt, kr, dk, dk, rope, record_bytes, krow)) return -1;
+      float acc = 0.0f;
+      for (int64_t d = 0; d < dk; d++) {
+        float qd = or_load(q, qbase + d, q_dtype) * ss;
+        float kd = krow[d] * ss;
+        float prod = qd * kd;
+        acc = acc + prod;
+      }
+      if (softcap != 0.0f) acc = softcap * (float)tanh((double)(acc / softcap));
+      p[s] = acc;
+    }
+    /* A7: max, exp, ascending sum, multiply by the reciprocal */
+    float m = -INFINITY;
+    for (int64_t s = 0; s < n; s++) m = fmaxf(m, p[s]);
+    if (m == -INFINITY) {
+      for (int64_t d = 0; d < dv; d++) yrow[d] = 0.0f;
+      continue;
+    }
+    float l = 0.0f;
+    for (int64_t s = 0; s < n; s++) {
+      float e = (float)exp((double)(p[s] - m));
+      p[s] = e;
+      l = l + e;
+    }
+    const float inv = 1.0f / l;
+    for (int64_t s = 0; s < n; s++) p[s] = p[s] * inv;
+    /* A8: y_d = sum_s p_s * v_{key_s, d}, ascending over s */
+    for (int64_t d = 0; d < dv; d++) yrow[d] = 0.0f;
+    for (int64_t s = 0; s < n; s++) {
+      int64_t key = or_load_index(idx, ibase + s, idx_is_i64);
+      int64_t kr = (b * hkv + kvh) * cap + key;
+      const float* v;
+      if (kv_layout == OR_LAYOUT_SHARED_LATENT) {
+        v = or_cache_row(kcache, cache_fmt, kr, dk, dk, rope, record_bytes, vrow);
+      } else {
+        v = or_cache_row(vcache, cache_fmt, kr, dv, dv, rope, record_bytes, vrow);
+      }
+      if (!v) return -1;
+      for (int64_t d = 0; d < dv; d++) {
+        float prod = p[s] * v[d];
+        yrow[d] = yrow[d] + prod;
+      }
+    }
+  }
+  return 0;
+}

@@ -1,0 +1,228 @@
+"""Seeded synthetic inputs for selected-token sparse attention with KV append.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic, and it is the one piece that the oracle side and the
+device side share. Storage conventions: bf16 and f16 tensors are returned as
+their raw 16-bit patterns (uint16), f32 as float32, indices as int32.
+
+Draw order for every workload (numpy ``default_rng(seed)``): Q, then the past
+cache (K then V, or the single shared-latent cache), then the current rows,
+then the index rows in (batch, index_head, query) order. Normal draws are
+fp32 N(0, 1); bf16 values are torch's round-to-nearest-even cast of them.
+
+Workloads (sizes are the ones the pages' operators are exercised at; the
+"scaled" variants keep the structure at sizes the CPU oracle finishes fast):
+
+* ``tiny_f32``     batch 1, 4 q heads / 4 kv heads, head dim 64, past 60 +
+                   4 current, 4 query rows each selecting 16 sorted distinct
+                   keys from [0, 64), width 20 with trailing -1; f32; scale 1/8.
+* ``decode_bf16``  batch 32, 1 query, 64 q heads sharing 1 kv head, shared
+                   latent rows of 576 (512 latent + 64 rope; V = first 512),
+                   past 32768 + 1 current, top-2048 uniform without
+                   replacement from [0, 32769), sorted; bf16.
+* ``decode_fp8``   as decode_bf16 with batch 64, past 65536 + 1; the cache is
+                   fp8_e4m3_block64 records (made by a block quantizer from
+                   the bf16 values this module returns).
+* ``prefill_bf16`` batch 1, empty past, 4096 current = query rows, 64 q heads
+                   sharing 1 kv head, row i selects min(i+1, 2048) sorted keys
+                   of [0, i] (all of them below 2048), width 2048.
+* ``dense_gqa``    batch 8, 32 q heads / 8 kv heads, head dim 128, past 8064 +
+                   128 current, 128 query rows; row q selects every key of
+                   [0, 8064 + q] (causal with per-batch offset 8064), width
+                   8192; softcap 50; bf16.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+DT_F32, DT_F16, DT_BF16 = 0, 1, 2
+LAYOUT_SEPARATE, LAYOUT_SHARED_LATENT = 0, 1
+CACHE_DENSE, CACHE_FP8 = 0, 1
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    q_seq: int
+    dk: int
+    dv: int
+    past: int          # past length of every batch entry
+    cur: int           # current rows appended this step
+    width: int         # index row width
+    topk: int          # selected keys per row (before any per-row cap)
+    dtype: int         # DT_*
+    layout: int        # LAYOUT_*
+    cache_format: int  # CACHE_*
+    rope: int = 0
+    scale: float = 0.0     # 0 -> 1/sqrt(dk)
+    softcap: float = 0.0
+    index_heads: int = 1
+    pattern: str = "uniform"   # uniform | causal_prefill | causal_all
+    seed: int = 0
+    capacity: int = 0          # cache rows allocated per (b, kv head); 0 -> past + cur
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def cap(self) -> int:
+        return self.capacity or (self.past + self.cur)
+
+    @property
+    def total(self) -> int:
+        return self.past + self.cur
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.hq * self.q_seq
+
+    def scaled(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", batch=1, hq=4, hkv=4, q_seq=4, dk=64, dv=64, past=60, cur=4,
+                         width=20, topk=16, dtype=DT_F32, layout=LAYOUT_SEPARATE,
+                         cache_format=CACHE_DENSE, scale=1.0 / 8.0, seed=0),
+    "decode_bf16": Workload("decode_bf16", batch=32, hq=64, hkv=1, q_seq=1, dk=576, dv=512,
+                            past=32768, cur=1, width=2048, topk=2048, dtype=DT_BF16,
+                            layout=LAYOUT_SHARED_LATENT, cache_format=CACHE_DENSE, rope=64,
+                            scale=1.0 / 24.0, seed=1),
+    "decode_fp8": Workload("decode_fp8", batch=64, hq=64, hkv=1, q_seq=1, dk=576, dv=512,
+                           past=65536, cur=1, width=2048, topk=2048, dtype=DT_BF16,
+                           layout=LAYOUT_SHARED_LATENT, cache_format=CACHE_FP8, rope=64,
+                           scale=1.0 / 24.0, seed=2),
+    "prefill_bf16": Workload("prefill_bf16", batch=1, hq=64, hkv=1, q_seq=4096, dk=576, dv=512,
+                             past=0, cur=4096, width=2048, topk=2048, dtype=DT_BF16,
+                             layout=LAYOUT_SHARED_LATENT, cache_format=CACHE_DENSE, rope=64,
+                             scale=1.0 / 24.0, pattern="causal_prefill", seed=3),
+    "dense_gqa": Workload("dense_gqa", batch=8, hq=32, hkv=8, q_seq=128, dk=128, dv=128,
+                          past=8064, cur=128, width=8192, topk=8192, dtype=DT_BF16,
+                          layout=LAYOUT_SEPARATE, cache_format=CACHE_DENSE,
+                          scale=float(1.0 / np.sqrt(np.float32(128.0))), softcap=50.0,
+                          pattern="causal_all", seed=4),
+}
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _f16_bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _store(x: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == DT_F32:
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == DT_F16:
+        return _f16_bits(x)
+    return _bf16_bits(x)
+
+
+def index_rows(w: Workload, rng: np.random.Generator, bound=None) -> np.ndarray:
+    """[B, Hi, Sq, W] int32 index rows for workload `w` (draws in row order)."""
+    B, Hi, Sq, W = w.batch, w.index_heads, w.q_seq, w.width
+    bound = np.full(B, w.total, np.int64) if bound is None else np.asarray(bound, np.int64)
+    out = np.full((B, Hi, Sq, W), -1, np.int32)
+    for b in range(B):
+        T = int(bound[b])
+        for h in range(Hi):
+            for q in range(Sq):
+                if w.pattern == "uniform":
+                    k = min(w.topk, T, W)
+                    sel = np.sort(rng.choice(T, size=k, replace=False))
+                elif w.pattern == "causal_prefill":
+                    # query row q is at absolute position (T - Sq) + q
+                    pos = T - Sq + q
+                    avail = pos + 1
+                    if avail <= w.topk:
+                        sel = np.arange(avail)
+                    else:
+                        sel = np.sort(rng.choice(avail, size=w.topk, replace=False))
+                elif w.pattern == "causal_all":
+                    pos = T - Sq + q
+                    sel = np.arange(min(pos + 1, W))
+                else:
+                    raise ValueError(w.pattern)
+                out[b, h, q, :len(sel)] = sel
+    return out
+
+
+def make_numpy(w: Workload) -> dict:
+    """All inputs of workload `w`, drawn on the host.
+
+    Returns q, past_k, past_v (None for shared latent), cur_k, cur_v, indices,
+    past_len, valid_len and, for shared-latent workloads, the logical fp32
+    latent values (``past_kv_f32``/``cur_kv_f32``) that fp8 records encode."""
+    rng = np.random.default_rng(w.seed)
+    B, Hq, Hkv, Sq, Dk, Dv = w.batch, w.hq, w.hkv, w.q_seq, w.dk, w.dv
+    q32 = rng.standard_normal((B, Hq, Sq, Dk), dtype=np.float32)
+    out = {"workload": w, "q": _store(q32, w.dtype)}
+    cap = w.cap
+    if w.layout == LAYOUT_SEPARATE:
+        pk = rng.standard_normal((B, Hkv, w.past, Dk), dtype=np.float32)
+        pv = rng.standard_normal((B, Hkv, w.past, Dv), dtype=np.float32)
+        ck = rng.standard_normal((B, Hkv, w.cur, Dk), dtype=np.float32)
+        cv = rng.standard_normal((B, Hkv, w.cur, Dv), dtype=np.float32)
+        out["past_k"] = _pad_cap(_store(pk, w.dtype), cap)
+        out["past_v"] = _pad_cap(_store(pv, w.dtype), cap)
+        out["cur_k"] = _store(ck, w.dtype)
+        out["cur_v"] = _store(cv, w.dtype)
+    else:
+        pkv = rng.standard_normal((B, Hkv, w.past, Dk), dtype=np.float32)
+        ckv = rng.standard_normal((B, Hkv, w.cur, Dk), dtype=np.float32)
+        pkv_b = _store(pkv, w.dtype)
+        ckv_b = _store(ckv, w.dtype)
+        out["past_k"] = _pad_cap(pkv_b, cap)
+        out["past_v"] = None
+        out["cur_k"] = ckv_b
+        out["cur_v"] = None
+        # logical values the cache rows hold (bf16 widened), for fp8 packing
+        out["past_kv_f32"] = _widen(pkv_b, w.dtype)
+        out["cur_kv_f32"] = _widen(ckv_b, w.dtype)
+    out["past_len"] = np.full(B, w.past, np.int32)
+    out["valid_len"] = np.full(B, w.total, np.int32)
+    out["indices"] = index_rows(w, rng)
+    return out
+
+
+def _widen(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Storage -> fp32 by reinterpretation (bf16: bits << 16). Layout only."""
+    if dtype == DT_F32:
+        return bits.astype(np.float32)
+    if dtype == DT_F16:
+        return bits.view(np.float16).astype(np.float32)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _pad_cap(a: np.ndarray, cap: int) -> np.ndarray:
+    """Place [B, H, past, ...] into a [B, H, cap, ...] buffer; spare rows get
+    finite garbage (7.5 / -4.25 patterns) so a read of them shows."""
+    B, H, P = a.shape[:3]
+    if cap == P:
+        return np.ascontiguousarray(a)
+    out = np.empty((B, H, cap) + a.shape[3:], a.dtype)
+    out[:, :, :P] = a
+    if a.dtype == np.float32:
+        garbage = np.float32(7.5)
+    elif a.dtype == np.uint16:
+        garbage = np.uint16(0x40F0)  # 7.5 in bf16
+    else:
+        garbage = a.dtype.type(0x55)
+    out[:, :, P:] = garbage
+    return out
+
+
+def torch_normal_bf16(shape, seed: int, device: str = "cuda"):
+    """Large N(0,1) bf16 tensors drawn on the device with a seeded torch
+    generator (for the full-size decode caches, too large to draw on the host)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
