@@ -1,0 +1,371 @@
+#!/usr/bin/env python3
+"""Benchmark of selected-token sparse attention with KV append on one MI355X.
+
+A step is one pass of the whole path over one batch: reset the device error
+word, append the current token(s) to the cache in place, validate the index
+rows, gather + score + softmax + PV (+ split-K combine), store Y.
+
+Default workload (decode, bf16, shared-latent MLA rows): batch 32, one query
+per sequence, 64 query heads sharing one kv head, 576-dim rows (V = first
+512), past 32768 + 1 current, top-2048 uniform sorted indices. Inputs are
+seeded synthetic N(0,1) values drawn on the device and stay resident in HBM.
+To keep the 256 MB Infinity Cache from serving the gathers, the timed steps
+rotate over R independent (query, index) sets, whose gathered rows together
+exceed it several times.
+
+Timing: W warmup steps, then K steps replayed from a captured HIP graph
+between HIP events; value = selected tokens attended per second. The main
+attention kernel's own duration is measured with the library's event pair
+over a second, eager pass of K steps on the same stream; the roofline figure
+divides the kernel's algorithmic bytes (or flops) by that duration. The CPU
+baseline is the oracle on a bounded sample of the same workload.
+
+Output: one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+VALU_FP32_PEAK_TFLOPS = 157.3
+PROFILES = ROOT / "profiles"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--workload", default="decode_bf16",
+                   choices=["decode_bf16", "decode_fp8", "prefill_bf16", "dense_gqa"])
+    p.add_argument("--rotate", type=int, default=8, help="independent (query, index) sets")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        h.update((ROOT / "sparse_attention_kv_append_amd" / "csrc" / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+class Setup:
+    """Device-resident inputs and the step closure for one workload."""
+
+    def __init__(self, name, rotate):
+        import numpy as np
+        import torch
+
+        import sa_workloads as W
+        import sparse_attention_kv_append_amd as sa
+        self.np, self.torch, self.W, self.sa = np, torch, W, sa
+        self.w = w = W.WORKLOADS[name]
+        self.name = name
+        self.R = rotate
+        dev = "cuda"
+        B, Hq, Sq, Dk, Dv = w.batch, w.hq, w.q_seq, w.dk, w.dv
+        cap = w.cap
+        fp8 = w.cache_format == W.CACHE_FP8
+        self.ctx = sa.Context(num_heads=Hq, kv_num_heads=w.hkv, head_dim_qk=Dk, head_dim_v=Dv,
+                              dtype=w.dtype, kv_layout=w.layout,
+                              cache_format=sa.SA_CACHE_FP8_E4M3_BLOCK64 if fp8 else sa.SA_CACHE_DENSE,
+                              rope_dim=w.rope, scale=w.scale, softcap=w.softcap, max_batch=B,
+                              max_q_seq=Sq, max_index_width=w.width, max_cache_len=cap)
+        seed = w.seed
+        gen = lambda shape, s: W.torch_normal_bf16(shape, s, dev)
+        # caches
+        if w.layout == W.LAYOUT_SHARED_LATENT:
+            if fp8:
+                rec = (Dk - w.rope) // 64 * 65 + 2 * w.rope
+                self.k = torch.empty((B, 1, cap, rec), dtype=torch.uint8, device=dev)
+                # the latent rows are quantized into records by the library's
+                # own quantize-on-append (the oracle's block-quantizer rule)
+                chunk = 4096
+                for t0 in range(0, w.past, chunk):
+                    n = min(chunk, w.past - t0)
+                    rows = gen((B, 1, n, Dk), seed * 1000 + t0 // chunk)
+                    plen = torch.full((B,), t0, dtype=torch.int32, device=dev)
+                    self.ctx.kv_append(B, self.k, None, cap, plen, rows, None, n, self.k, None, cap,
+                                       cur_is_unquantized_bf16=True)
+                torch.cuda.synchronize()
+                self.past_host_seed = seed * 1000
+            else:
+                self.k = gen((B, 1, cap, Dk), seed * 1000)
+            self.v = None
+            self.cur_k = gen((B, 1, w.cur, Dk), seed * 1000 + 999)
+            self.cur_v = None
+        else:
+            self.k = gen((B, w.hkv, cap, Dk), seed * 1000)
+            self.v = gen((B, w.hkv, cap, Dv), seed * 1000 + 1)
+            self.cur_k = gen((B, w.hkv, w.cur, Dk), seed * 1000 + 998)
+            self.cur_v = gen((B, w.hkv, w.cur, Dv), seed * 1000 + 999)
+        self.fp8 = fp8
+        self.plen = torch.full((B,), w.past, dtype=torch.int32, device=dev)
+        self.vlen = torch.zeros((B,), dtype=torch.int32, device=dev)
+        # rotating query / index sets
+        self.qs, self.idx_host, self.idxs = [], [], []
+        for r in range(self.R):
+            self.qs.append(gen((B, Hq, Sq, Dk), seed * 1000 + 500 + r))
+            rng = np.random.default_rng(seed * 100 + r)
+            ih = W.index_rows(w, rng)
+            self.idx_host.append(ih)
+            self.idxs.append(torch.from_numpy(ih).to(dev))
+            if w.pattern != "uniform":
+                break  # the causal patterns are deterministic: one set
+        ydt = {W.DT_F32: torch.float32, W.DT_F16: torch.float16, W.DT_BF16: torch.bfloat16}[w.dtype]
+        self.y = torch.empty((B, Hq, Sq, Dv), dtype=ydt, device=dev)
+        self.selected = [int((ih >= 0).sum()) // 1 for ih in self.idx_host]
+        self.path, self.splits = self.ctx.query_plan(B, Sq, 1, w.width)
+
+    def step(self, i):
+        w, c = self.w, self.ctx
+        r = i % len(self.idxs)
+        c.reset_error_async()
+        c.kv_append(w.batch, self.k, self.v, w.cap, self.plen, self.cur_k, self.cur_v, w.cur, self.k,
+                    self.v, w.cap, cur_is_unquantized_bf16=self.fp8, present_len=self.vlen)
+        c.forward(self.qs[r % len(self.qs)], w.batch, w.q_seq, self.k, self.v, w.cap, self.vlen,
+                  self.idxs[r], 1, w.width, self.y, fused_validate=True)
+
+    # ---- work accounting (per step, averaged over the rotation sets)
+    def tokens_per_step(self):
+        """Selected (row, key) pairs attended per step, all heads of a row counted once."""
+        return sum(self.selected) / len(self.selected)
+
+    def kernel_work(self):
+        """Algorithmic bytes and flops of ONE launch of the main attention kernel."""
+        w = self.w
+        sel = self.tokens_per_step()
+        if w.layout == self.W.LAYOUT_SHARED_LATENT:
+            row_bytes = ((w.dk - w.rope) // 64 * 65 + 2 * w.rope) if self.fp8 else w.dk * 2
+            gather = sel * row_bytes
+            heads_per_key = w.hq
+        else:
+            # generic path: each (row, kv head) gathers K and V rows of 2*D bytes
+            gather = sel * w.hkv * (w.dk + w.dv) * 2
+            heads_per_key = w.hq
+        qbytes = w.batch * w.hq * w.q_seq * w.dk * 2
+        ibytes = sum(ih.size for ih in self.idx_host) / len(self.idx_host) * 4
+        flops = sel * heads_per_key * 2 * (w.dk + w.dv)
+        return dict(bytes=gather + qbytes + ibytes, gather_bytes=gather, flops=flops)
+
+    def step_bytes(self):
+        w = self.w
+        kw = self.kernel_work()
+        ybytes = w.batch * w.hq * w.q_seq * w.dv * 2
+        row_bytes = ((w.dk - w.rope) // 64 * 65 + 2 * w.rope) if self.fp8 else w.dk * 2
+        append = w.batch * w.hkv * w.cur * (row_bytes + (w.dv * 2 if self.v is not None else 0))
+        return kw["bytes"] + ybytes + 2 * append
+
+
+def kernel_name(setup):
+    return "mla_forward_kernel" if setup.path == 1 else "generic_forward_kernel"
+
+
+def counters_for(setup):
+    """HBM traffic of the main kernel from a committed rocprofv3 --pmc summary,
+    if it was taken on the current kernel source; else None."""
+    f = PROFILES / f"{kernel_name(setup)}_{setup.name}_counters.json"
+    if not f.exists():
+        return None
+    try:
+        d = json.loads(f.read_text())
+    except Exception:
+        return None
+    if d.get("source_hash") != source_hash(*d.get("sources", [])):
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(setup, target_s):
+    """The oracle (unchanged) on a bounded sample: the first rows of the same
+    workload, gathered into a compact cache (order-preserving relabelling of
+    the selected keys leaves the oracle's result unchanged)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    w = setup.w
+    threads = max(1, min(16, os.cpu_count() or 1))
+    W = setup.W
+    ih = setup.idx_host[0]
+
+    def sample(nrows_b):
+        """host inputs for the first nrows_b (batch, query) rows, all heads"""
+        qs, caches, vcs, idxs = [], [], [], []
+        for rb in range(nrows_b):
+            b, qi = rb // w.q_seq, rb % w.q_seq
+            sel = ih[b, 0, qi]
+            sel = sel[sel >= 0]
+            t = torch.from_numpy(sel.astype(np.int64)).cuda()
+            past = t < w.past
+            if setup.fp8:
+                # records as they sit in the device cache (timing input only)
+                caches.append(setup.k[b, 0].index_select(0, t).cpu())
+            elif w.layout == W.LAYOUT_SHARED_LATENT:
+                src = setup.k[b, 0]
+                rows = src.index_select(0, t.clamp(max=w.past - 1 if w.past > 0 else 0))
+                if w.cur:
+                    cur_rows = setup.cur_k[b, 0].index_select(0, (t - w.past).clamp(min=0))
+                    rows = torch.where(past[:, None], rows, cur_rows)
+                caches.append(rows.cpu())
+            else:
+                k = setup.k[b, :].index_select(1, t.clamp(max=w.past - 1))
+                v = setup.v[b, :].index_select(1, t.clamp(max=w.past - 1))
+                ck = setup.cur_k[b, :].index_select(1, (t - w.past).clamp(min=0))
+                cv = setup.cur_v[b, :].index_select(1, (t - w.past).clamp(min=0))
+                caches.append(torch.where(past[None, :, None], k, ck).cpu())
+                vcs.append(torch.where(past[None, :, None], v, cv).cpu())
+            qs.append(setup.qs[0][b, :, qi].cpu())
+            idxs.append(np.arange(len(sel), dtype=np.int32))
+        return qs, caches, vcs, idxs
+
+    def as_bits(t):
+        if t.dtype == torch.uint8:
+            return t.numpy()
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    def run(nrows_b):
+        qs, caches, vcs, idxs = sample(nrows_b)
+        n_total = 0
+        t0 = time.perf_counter()
+        for j in range(nrows_b):
+            n = len(idxs[j])
+            q = as_bits(qs[j])[None, :, None, :]
+            kc = as_bits(caches[j])
+            if w.layout == W.LAYOUT_SHARED_LATENT:
+                kc = kc[None, None]
+                vc = None
+            else:
+                kc = kc[None]
+                vc = as_bits(vcs[j])[None]
+            ix = idxs[j][None, None, None, :]
+            fmt = oracle.FP8_BLOCK64 if setup.fp8 else w.dtype
+            oracle.forward(q, kc, vc, ix, q_dtype=w.dtype, cache_fmt=fmt, kv_layout=w.layout,
+                           hkv=w.hkv, dv=w.dv, rope=w.rope, scale=w.scale, softcap=w.softcap,
+                           threads=threads)
+            n_total += n
+        return n_total, time.perf_counter() - t0
+
+    n1, t1 = run(1)
+    total_rows = w.batch * w.q_seq
+    nb = max(1, min(total_rows, int(target_s / max(t1, 1e-3))))
+    n, t = run(nb) if nb > 1 else (n1, t1)
+    return {"value": n / t, "unit": "selected tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {nb} of {total_rows} (batch, query) rows of the same workload, all "
+                      f"{w.hq} heads, {n} selected keys, {t:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards by batch with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    print(f"bench: workload {args.workload}, building inputs", file=sys.stderr, flush=True)
+    s = Setup(args.workload, args.rotate)
+    w = s.w
+    print(f"bench: path {kernel_name(s)} splits {s.splits}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        s.step(i)
+    torch.cuda.synchronize()
+    word, _, msg = s.ctx.read_error()
+    assert word == 0, msg
+
+    nset = len(s.idxs)
+    use_graph = not args.no_graph
+    steps = args.steps
+    if use_graph:
+        steps = max(nset, (steps // nset) * nset)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nset):
+                s.step(i)
+        g.replay()
+        torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if use_graph:
+        for _ in range(steps // nset):
+            g.replay()
+    else:
+        for i in range(steps):
+            s.step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    word, _, msg = s.ctx.read_error()
+    assert word == 0, msg
+    ms_per_step = ms_total / steps
+
+    # eager pass with the library's event pair around the main kernel
+    s.ctx.profile_enable(steps)
+    for i in range(steps):
+        s.step(i)
+    k_ms, k_n = s.ctx.profile_read()
+    s.ctx.profile_enable(0)
+    k_avg_s = k_ms / max(k_n, 1) / 1e3
+
+    tokens = s.tokens_per_step()
+    kw = s.kernel_work()
+    if w.pattern == "causal_prefill":
+        bound, peak, unit = "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved = kw["flops"] / k_avg_s / 1e12
+    elif w.layout == s.W.LAYOUT_SEPARATE:
+        bound, peak, unit = "alu", VALU_FP32_PEAK_TFLOPS, "TFLOP/s"
+        achieved = kw["flops"] / k_avg_s / 1e12
+    else:
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+        achieved = kw["bytes"] / k_avg_s / 1e9
+    traffic = counters_for(s)
+    result = {
+        "metric": "selected KV tokens attended/sec (decode) + achieved HBM GB/s % of peak",
+        "value": tokens / (ms_per_step / 1e3),
+        "unit": "selected tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if s.fp8 else {0: "f32", 1: "f16", 2: "bf16"}[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {w.batch}, q_seq {w.q_seq}, {w.hq} q heads / "
+                               f"{w.hkv} kv heads, Dk {w.dk} / Dv {w.dv}, past {w.past} + {w.cur}, "
+                               f"index width {w.width}, {'graph replay' if use_graph else 'eager'}, "
+                               f"{nset} rotating index sets",
+                   "selected_tokens_per_step": tokens, "splits": s.splits,
+                   "step_hbm_GBps": s.step_bytes() / (ms_per_step / 1e3) / 1e9},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic, "kernel": kernel_name(s),
+                     "kernel_avg_us": k_avg_s * 1e6,
+                     "algorithmic_bytes_per_launch": kw["bytes"],
+                     "algorithmic_flops_per_launch": kw["flops"]},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(s, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    s.ctx.destroy()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

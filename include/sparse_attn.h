@@ -1,0 +1,231 @@
+/*
+ * sparse_attn.h -- C ABI of the MI355X (gfx950) selected-token sparse
+ * attention library with KV-cache append.
+ *
+ * The operation is the one the IndexShare operator defines (docs.rs page
+ * onnx-runtime-ep-cuda, src/kernels/index_share.rs): append the current K/V
+ * rows to the past cache (past ++ current -> present), validate each row of
+ * selected_indices, gather the selected keys, score them as
+ * (Q*sqrt(scale)) . (K*sqrt(scale)), take a numerically stable fp32 softmax
+ * over the selected keys and reduce probs . V. Two storage forms come from the
+ * compressed-sparse-attention pages (onnx-runtime-ep-cpu/-cuda,
+ * src/kernels/compressed_sparse_attention.rs): a single shared-latent cache
+ * row that is both key and value, and fp8_e4m3_block64 records (`CacheFormat`).
+ * The optional softcap is the standard Attention page's (onnx-runtime-ep-cuda,
+ * src/kernels/standard_attention.rs, module doc "Semantics").
+ *
+ * Conventions for every entry point below:
+ *  - Every tensor pointer is a HIP DEVICE pointer owned by the caller; the
+ *    library never frees or retains it past the call. Tensors are dense and
+ *    row-major in the shapes stated.
+ *  - Calls are asynchronous on the context's stream. sparse_attn_kv_append,
+ *    sparse_attn_validate_indices, sparse_attn_forward and
+ *    sparse_attn_reset_error_async perform no allocation, no host
+ *    synchronisation and no device-to-host copy, so they may be recorded into
+ *    a HIP graph.
+ *  - A bad argument, shape, dtype, capacity or unsupported combination is
+ *    reported by the return status BEFORE anything is launched, and
+ *    sparse_attn_last_error() then holds a message.
+ *  - Conditions only the device can see (index-row violations, append lengths
+ *    held in device arrays, non-finite values given to the fp8 quantizer) are
+ *    OR-latched into the context's device error word; sparse_attn_read_error
+ *    returns it. A caller discards the outputs of a call whose word is nonzero.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sparse_attn_ctx sparse_attn_ctx;
+
+typedef enum {
+  SA_OK = 0,
+  SA_E_ARG = 1,          /* NULL pointer, non-positive size, bad enum value     */
+  SA_E_SHAPE = 2,        /* sizes inconsistent with each other or the config    */
+  SA_E_DTYPE = 3,        /* dtype / cache format combination not allowed        */
+  SA_E_CAPACITY = 4,     /* past_len + cur_len does not fit the present capacity */
+  SA_E_UNSUPPORTED = 5,  /* valid request outside what this build implements     */
+  SA_E_HIP = 6,          /* a HIP runtime call failed                            */
+  SA_E_STATE = 7,        /* NULL or destroyed context, or sizes beyond create's max */
+  SA_E_INDEX = 8         /* sparse_attn_read_error: the error word is nonzero    */
+} sa_status;
+
+/* element dtype of query, Y and a dense cache (codes as the IndexShare
+ * kernels' load_float/store_float: 0 f32, 1 f16, 2 bf16) */
+enum { SA_F32 = 0, SA_F16 = 1, SA_BF16 = 2 };
+/* cache storage: dense rows of the element dtype, or fp8_e4m3_block64 records
+ * ((Dk - rope)/64 blocks of [1 E8M0 scale byte, 64 E4M3FN bytes], then `rope`
+ * little-endian BF16 values; the CSA CPU page's `CacheFormat`) */
+enum { SA_CACHE_DENSE = 0, SA_CACHE_FP8_E4M3_BLOCK64 = 1 };
+/* SEPARATE: K and V caches, Dk == Dv (IndexShare). SHARED_LATENT: one cache
+ * whose row is the key and whose first Dv dims are the value (the CSA pages'
+ * records are both key and value). */
+enum { SA_KV_SEPARATE = 0, SA_KV_SHARED_LATENT = 1 };
+enum { SA_IDX_I32 = 0, SA_IDX_I64 = 1 };
+
+/* Device error-word bits. The first six are index-row classes in the check
+ * order of the IndexShare host `validate_indices`; 512 is IndexShare's
+ * capture-error bit (INDEX_SHARE_CAPTURE_ERROR_INDEX), set with any of them. */
+#define SA_ERR_SENTINEL 0x01u        /* an index below -1                        */
+#define SA_ERR_AFTER_PAD 0x02u       /* a non-(-1) index after trailing padding  */
+#define SA_ERR_RANGE 0x04u           /* an index >= the batch's cache length     */
+#define SA_ERR_DUPLICATE 0x08u       /* an index equal to the previous one       */
+#define SA_ERR_ORDER 0x10u           /* an index below the previous one          */
+#define SA_ERR_ALL_PAD 0x20u         /* a row with no valid index                */
+#define SA_ERR_APPEND_CAPACITY 0x40u /* device past_len[b] < 0, > past capacity, or
+                                        past_len[b] + cur_len > present capacity;
+                                        that batch's rows are not written         */
+#define SA_ERR_QUANT_NONFINITE 0x80u /* fp8 quantize-on-append met a NaN/Inf     */
+#define SA_ERR_INDEX_ANY 512u
+#define SA_ERR_APPEND_ANY 1024u
+
+typedef struct {
+  int32_t num_heads;      /* Hq > 0 (IndexShare attr num_heads)                         */
+  int32_t kv_num_heads;   /* Hkv > 0, Hq % Hkv == 0 (attr kv_num_heads)                 */
+  int32_t head_dim_qk;    /* Dk: query/key head dim                                     */
+  int32_t head_dim_v;     /* Dv: value head dim; SEPARATE requires Dv == Dk, SHARED_LATENT Dv <= Dk */
+  int32_t rope_dim;       /* fp8 records only: BF16 tail width; (Dk - rope) % 64 == 0   */
+  int32_t dtype;          /* SA_F32 / SA_F16 / SA_BF16                                  */
+  int32_t cache_format;   /* SA_CACHE_*; fp8 requires SHARED_LATENT and dtype bf16      */
+  int32_t kv_layout;      /* SA_KV_*                                                    */
+  int32_t index_dtype;    /* SA_IDX_*                                                   */
+  float scale;            /* 0 -> 1/sqrtf(Dk); else finite and > 0 (attr scale)         */
+  float softcap;          /* 0 -> off; else finite and > 0: s = softcap*tanh(s/softcap) */
+  int64_t max_batch;      /* largest batch any call will pass                           */
+  int64_t max_q_seq;      /* largest query length                                       */
+  int64_t max_index_width;/* largest selected_indices row width                         */
+  int64_t max_cache_len;  /* largest cache capacity (rows per (batch, kv head))         */
+} sa_config;
+
+/* Create a context: checks the config, allocates the device error word and
+ * the split-K partial buffers sized from the max_* fields (stable addresses
+ * for the context's lifetime). hip_stream may be NULL (the null stream).
+ * Returns SA_E_ARG / SA_E_DTYPE / SA_E_UNSUPPORTED for a bad config. */
+sa_status sparse_attn_create(const sa_config* cfg, void* hip_stream, sparse_attn_ctx** out);
+
+/* Release the context's device buffers after draining its stream. NULL is
+ * accepted and ignored. */
+sa_status sparse_attn_destroy(sparse_attn_ctx* ctx);
+
+/* Change the stream later calls are launched on. */
+sa_status sparse_attn_set_stream(sparse_attn_ctx* ctx, void* hip_stream);
+
+/*
+ * A1/A2: KV append (IndexShare `build_present`, `build_present_capacity`).
+ *   present[b,h,t] = past[b,h,t]                 for t < past_len[b]
+ *                  = cur[b,h,t - past_len[b]]    for past_len[b] <= t < past_len[b] + cur_len
+ * Rows at or beyond past_len[b] + cur_len are not touched.
+ *   past_k/past_v       [B, Hkv, past_capacity, row]; may be NULL when past_capacity == 0
+ *   past_len            device int32 [B], or NULL meaning every batch holds past_capacity rows
+ *   cur_k/cur_v         [B, Hkv, cur_len, row]
+ *   present_k/present_v [B, Hkv, present_capacity, row]
+ * `row` is Dk (K) / Dv (V) elements of the config dtype, or one fp8 record.
+ * present == past is the in-place capacity mode: only the cur_len new rows
+ * are written. present != past is concat mode: past rows are copied too.
+ * SHARED_LATENT: pass past_v, cur_v and present_v as NULL.
+ * cur_is_unquantized_bf16 (fp8 caches only): cur_k is bf16 [B, Hkv, cur_len, Dk]
+ * and each new row is quantized on the device into a record (block scale
+ * floor(log2 amax) - 8 + 127, E4M3FN nearest-even saturating at 448; the CSA
+ * CPU page's `finalize_attention_record` pack loop); otherwise cur_k holds
+ * records and the append is a byte copy.
+ * present_len: optional device int32 [B] output, past_len[b] + cur_len.
+ * Host errors: SA_E_CAPACITY when past_len is NULL and
+ * past_capacity + cur_len > present_capacity. Device errors:
+ * SA_ERR_APPEND_CAPACITY, SA_ERR_QUANT_NONFINITE.
+ */
+sa_status sparse_attn_kv_append(sparse_attn_ctx* ctx, int64_t batch, const void* past_k,
+                                const void* past_v, int64_t past_capacity, const int32_t* past_len,
+                                const void* cur_k, const void* cur_v, int64_t cur_len,
+                                int32_t cur_is_unquantized_bf16, void* present_k, void* present_v,
+                                int64_t present_capacity, int32_t* present_len);
+
+/*
+ * A3: validate selected_indices [B, Hi, Sq, W] (Hi is 1 or Hq), int32 or
+ * int64 per the config. Per row, columns are checked left to right with the
+ * IndexShare host `validate_indices` rules; the first failing column decides
+ * the row's class (SA_ERR_* bit index + 1; 0 = valid). A row of only -1 is
+ * ALL_PAD.
+ *   valid_len   device int32 [B]: cache length of each batch (an index must be
+ *               below it); NULL means every batch has cache_len.
+ *   error_word  device uint32: OR of the invalid rows' class bits | 512;
+ *               NULL means the context's word.
+ *   row_class   optional device uint8 [B*Hi*Sq]: each row's class.
+ *   first_bad   device uint64: smallest row*(W+1)+col over invalid rows
+ *               (col == W for ALL_PAD). NULL means the context's slot, which
+ *               keeps the FIRST failing call since the last reset (with the
+ *               failing value, its left neighbour and the bound, for the
+ *               message sparse_attn_read_error builds); a caller-owned slot
+ *               takes the atomic minimum over calls.
+ * The word and slot accumulate across calls until
+ * sparse_attn_reset_error_async.
+ */
+sa_status sparse_attn_validate_indices(sparse_attn_ctx* ctx, const void* indices, int64_t batch,
+                                       int64_t index_heads, int64_t q_seq, int64_t width,
+                                       const int32_t* valid_len, int64_t cache_len,
+                                       uint32_t* error_word, uint8_t* row_class,
+                                       uint64_t* first_bad);
+
+/*
+ * A4-A10: the forward (IndexShare `index_share_row` semantics).
+ *   q          [B, Hq, Sq, Dk] config dtype
+ *   present_k  [B, Hkv, cache_capacity, Dk] dense, or records
+ *   present_v  [B, Hkv, cache_capacity, Dv] (SEPARATE) or NULL (SHARED_LATENT)
+ *   valid_len  device int32 [B] or NULL (= cache_capacity): gather bound
+ *   indices    [B, Hi, Sq, W], rows of strictly increasing keys padded with -1
+ *   y          [B, Hq, Sq, Dv] config dtype (bf16/f16 rounded to nearest even)
+ * For each output row (b, h, q): kvh = h / (Hq/Hkv), index row ih = Hi==1 ? 0 : h,
+ * n = entries before the first -1; y = softmax_s(softcap(scale * q.k_s)) . v_s
+ * over the n selected keys, fp32 throughout. A key outside [0, bound) is read
+ * as key 0 (IndexShare clamps so a bad row stays in bounds); its row is
+ * reported by validation, not here. fused_validate != 0 also runs
+ * sparse_attn_validate_indices into the context's word first, on the stream.
+ */
+sa_status sparse_attn_forward(sparse_attn_ctx* ctx, const void* q, int64_t batch, int64_t q_seq,
+                              const void* present_k, const void* present_v,
+                              int64_t cache_capacity, const int32_t* valid_len,
+                              const void* indices, int64_t index_heads, int64_t width, void* y,
+                              int32_t fused_validate);
+
+/* Zero the context's error word and set first_bad to UINT64_MAX, with a tiny
+ * kernel on the stream (no memset node, so it is safe inside a graph). */
+sa_status sparse_attn_reset_error_async(sparse_attn_ctx* ctx);
+
+/* Synchronise the stream and copy the context's error word and first_bad slot
+ * to the host (either pointer may be NULL). NOT capturable. Returns
+ * SA_E_INDEX when the word is nonzero and, for an index error, puts the
+ * IndexShare wording of the first failing row into sparse_attn_last_error(). */
+sa_status sparse_attn_read_error(sparse_attn_ctx* ctx, uint32_t* word, uint64_t* first_bad);
+
+/* The last host-side message for this context ("" if none). */
+const char* sparse_attn_last_error(const sparse_attn_ctx* ctx);
+
+/* Report which forward path and split count a call with these sizes takes:
+ * *path = 0 generic (VALU), 1 shared-latent MFMA; *splits >= 1. */
+sa_status sparse_attn_query_plan(const sparse_attn_ctx* ctx, int64_t batch, int64_t q_seq,
+                                 int64_t index_heads, int64_t width, int32_t* path,
+                                 int32_t* splits);
+
+/* Optional kernel timing. With max_launches > 0, each later
+ * sparse_attn_forward records a HIP event pair on the context stream right
+ * before and after its main attention kernel (the per-split kernel when the
+ * keys are split; not the validation or combine kernels), for up to
+ * max_launches calls. The events are created here, not on the launch path.
+ * max_launches == 0 turns it off and releases the events. */
+sa_status sparse_attn_profile_enable(sparse_attn_ctx* ctx, int32_t max_launches);
+
+/* Synchronise, then return the summed duration in milliseconds and the
+ * number of timed launches since the last read, and start counting again. */
+sa_status sparse_attn_profile_read(sparse_attn_ctx* ctx, double* total_ms, int64_t* launches);
+
+/* Library version string. */
+const char* sparse_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,223 @@
+"""Python binding of libsparse_attn.so (selected-token sparse attention with KV
+append on MI355X / gfx950).
+
+The binding only marshals arguments: every step of the path runs in the HIP
+kernels of the shared library. torch supplies device memory and the stream.
+If the library is not built, importing the ``native`` handle raises -- there
+is no fallback implementation of any step.
+
+The C entry points are exposed under their own names (``sparse_attn_create``,
+``sparse_attn_kv_append``, ...) taking raw pointers and sizes, and the
+``Context`` class wraps them for torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+_HERE = Path(__file__).resolve().parent
+LIB_PATH = _HERE / "libsparse_attn.so"
+
+# ---- constants mirrored from include/sparse_attn.h
+SA_OK, SA_E_ARG, SA_E_SHAPE, SA_E_DTYPE, SA_E_CAPACITY, SA_E_UNSUPPORTED, SA_E_HIP, SA_E_STATE, \
+    SA_E_INDEX = range(9)
+SA_F32, SA_F16, SA_BF16 = 0, 1, 2
+SA_CACHE_DENSE, SA_CACHE_FP8_E4M3_BLOCK64 = 0, 1
+SA_KV_SEPARATE, SA_KV_SHARED_LATENT = 0, 1
+SA_IDX_I32, SA_IDX_I64 = 0, 1
+SA_ERR_SENTINEL, SA_ERR_AFTER_PAD, SA_ERR_RANGE = 0x01, 0x02, 0x04
+SA_ERR_DUPLICATE, SA_ERR_ORDER, SA_ERR_ALL_PAD = 0x08, 0x10, 0x20
+SA_ERR_APPEND_CAPACITY, SA_ERR_QUANT_NONFINITE = 0x40, 0x80
+SA_ERR_INDEX_ANY, SA_ERR_APPEND_ANY = 512, 1024
+
+STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_DTYPE", 4: "SA_E_CAPACITY",
+                5: "SA_E_UNSUPPORTED", 6: "SA_E_HIP", 7: "SA_E_STATE", 8: "SA_E_INDEX"}
+
+EXPORTS = [
+    "sparse_attn_create", "sparse_attn_destroy", "sparse_attn_set_stream",
+    "sparse_attn_kv_append", "sparse_attn_validate_indices", "sparse_attn_forward",
+    "sparse_attn_reset_error_async", "sparse_attn_read_error", "sparse_attn_last_error",
+    "sparse_attn_query_plan", "sparse_attn_profile_enable", "sparse_attn_profile_read",
+    "sparse_attn_version",
+]
+
+
+class sa_config(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32), ("kv_num_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("cache_format", ctypes.c_int32), ("kv_layout", ctypes.c_int32),
+        ("index_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
+        ("max_batch", ctypes.c_int64), ("max_q_seq", ctypes.c_int64),
+        ("max_index_width", ctypes.c_int64), ("max_cache_len", ctypes.c_int64),
+    ]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def load(path: Path | str | None = None) -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(
+            f"{p} is missing: build the HIP library first (python -m "
+            "sparse_attention_kv_append_amd.build or __graft_entry__.build())")
+    lib = ctypes.CDLL(str(p))
+    V, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    st = ctypes.c_int
+    sig = {
+        "sparse_attn_create": ([ctypes.POINTER(sa_config), V, ctypes.POINTER(V)], st),
+        "sparse_attn_destroy": ([V], st),
+        "sparse_attn_set_stream": ([V, V], st),
+        "sparse_attn_kv_append": ([V, I64, V, V, I64, V, V, V, I64, I32, V, V, I64, V], st),
+        "sparse_attn_validate_indices": ([V, V, I64, I64, I64, I64, V, I64, V, V, V], st),
+        "sparse_attn_forward": ([V, V, I64, I64, V, V, I64, V, V, I64, I64, V, I32], st),
+        "sparse_attn_reset_error_async": ([V], st),
+        "sparse_attn_read_error": ([V, ctypes.POINTER(ctypes.c_uint32),
+                                    ctypes.POINTER(ctypes.c_uint64)], st),
+        "sparse_attn_last_error": ([V], ctypes.c_char_p),
+        "sparse_attn_query_plan": ([V, I64, I64, I64, I64, ctypes.POINTER(I32),
+                                    ctypes.POINTER(I32)], st),
+        "sparse_attn_profile_enable": ([V, I32], st),
+        "sparse_attn_profile_read": ([V, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)], st),
+        "sparse_attn_version": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream_handle(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class Context:
+    """One library context (config, device error word, split-K buffers).
+
+    Methods launch on the torch stream current at call time."""
+
+    def __init__(self, *, num_heads, kv_num_heads, head_dim_qk, head_dim_v, dtype,
+                 kv_layout=SA_KV_SEPARATE, cache_format=SA_CACHE_DENSE, rope_dim=0,
+                 index_dtype=SA_IDX_I32, scale=0.0, softcap=0.0, max_batch=1, max_q_seq=1,
+                 max_index_width=1, max_cache_len=1):
+        self.lib = load()
+        self.cfg = sa_config(num_heads, kv_num_heads, head_dim_qk, head_dim_v, rope_dim, dtype,
+                             cache_format, kv_layout, index_dtype, scale, softcap, max_batch,
+                             max_q_seq, max_index_width, max_cache_len)
+        h = ctypes.c_void_p()
+        st = self.lib.sparse_attn_create(ctypes.byref(self.cfg), _stream_handle(), ctypes.byref(h))
+        if st != SA_OK:
+            raise SparseAttnError(st, "sparse_attn_create rejected the configuration")
+        self.handle = h.value
+
+    # -- plumbing
+    def _sync_stream(self):
+        self.lib.sparse_attn_set_stream(self.handle, _stream_handle())
+
+    def _check(self, st):
+        if st != SA_OK:
+            raise SparseAttnError(st, self.last_error())
+
+    def last_error(self) -> str:
+        return self.lib.sparse_attn_last_error(self.handle).decode()
+
+    def destroy(self):
+        if self.handle:
+            self.lib.sparse_attn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    # -- entry points
+    def kv_append(self, batch, past_k, past_v, past_capacity, past_len, cur_k, cur_v, cur_len,
+                  present_k, present_v, present_capacity, *, cur_is_unquantized_bf16=False,
+                  present_len=None):
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_kv_append(
+            self.handle, batch, _ptr(past_k), _ptr(past_v), past_capacity, _ptr(past_len),
+            _ptr(cur_k), _ptr(cur_v), cur_len, int(cur_is_unquantized_bf16), _ptr(present_k),
+            _ptr(present_v), present_capacity, _ptr(present_len)))
+
+    def validate_indices(self, indices, batch, index_heads, q_seq, width, valid_len=None,
+                         cache_len=0, error_word=None, row_class=None, first_bad=None):
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_validate_indices(
+            self.handle, _ptr(indices), batch, index_heads, q_seq, width, _ptr(valid_len),
+            cache_len, _ptr(error_word), _ptr(row_class), _ptr(first_bad)))
+
+    def forward(self, q, batch, q_seq, present_k, present_v, cache_capacity, valid_len, indices,
+                index_heads, width, y, fused_validate=False):
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_forward(
+            self.handle, _ptr(q), batch, q_seq, _ptr(present_k), _ptr(present_v), cache_capacity,
+            _ptr(valid_len), _ptr(indices), index_heads, width, _ptr(y), int(fused_validate)))
+
+    def reset_error_async(self):
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_reset_error_async(self.handle))
+
+    def read_error(self, raise_on_error=False):
+        """Synchronise and return (word, first_bad, message)."""
+        self._sync_stream()
+        w, fb = ctypes.c_uint32(), ctypes.c_uint64()
+        st = self.lib.sparse_attn_read_error(self.handle, ctypes.byref(w), ctypes.byref(fb))
+        msg = self.last_error()
+        if st not in (SA_OK, SA_E_INDEX):
+            raise SparseAttnError(st, msg)
+        if raise_on_error and st == SA_E_INDEX:
+            raise SparseAttnError(st, msg)
+        return int(w.value), int(fb.value), msg
+
+    def profile_enable(self, max_launches):
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_profile_enable(self.handle, max_launches))
+
+    def profile_read(self):
+        """(summed ms, launches) of the main forward kernel since the last read."""
+        self._sync_stream()
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        self._check(self.lib.sparse_attn_profile_read(self.handle, ctypes.byref(ms), ctypes.byref(n)))
+        return float(ms.value), int(n.value)
+
+    def query_plan(self, batch, q_seq, index_heads, width):
+        p, s = ctypes.c_int32(), ctypes.c_int32()
+        self._check(self.lib.sparse_attn_query_plan(self.handle, batch, q_seq, index_heads, width,
+                                                    ctypes.byref(p), ctypes.byref(s)))
+        return int(p.value), int(s.value)
+
+
+def __getattr__(name):
+    # module-level access to the raw C entry points under their own names
+    if name in EXPORTS:
+        return getattr(load(), name)
+    raise AttributeError(name)

@@ -1,0 +1,159 @@
+// On-device selected_indices validation (IndexShare `validate_index_rows`,
+// with the per-row verdict of the host `validate_indices`).
+//
+// The host rule scans a row left to right. Its first violation can be found
+// in parallel: while the prefix before column c is valid, the scanner's state
+// at c is fixed by column c-1 alone (padding has started iff c-1 holds -1; the
+// previous valid index is c-1's value otherwise). So every column is checked
+// against its left neighbour at once, and the row's verdict is the violation
+// with the smallest column; a row with no violation and -1 in column 0 is
+// all padding. One wave owns one row and walks it 64 columns at a time.
+//
+// Into the context's error block, the launch's smallest failing (row, col)
+// is gathered with an atomic minimum; the last block to finish then records
+// that violation's class and values (for the host message) if no earlier
+// launch since the last reset has failed, and re-arms the per-launch slot.
+#include "sa_internal.h"
+
+namespace sa {
+
+template <bool I64>
+__device__ __forceinline__ int64_t shfl_up1(int64_t v) {
+  if constexpr (I64) {
+    const int lo = __shfl_up((int)(v & 0xffffffff), 1, 64);
+    const int hi = __shfl_up((int)(v >> 32), 1, 64);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+  } else {
+    return (int64_t)__shfl_up((int)v, 1, 64);
+  }
+}
+
+template <bool I64>
+__device__ __forceinline__ int64_t shfl_from(int64_t v, int src) {
+  if constexpr (I64) {
+    const int lo = __shfl((int)(v & 0xffffffff), src, 64);
+    const int hi = __shfl((int)(v >> 32), src, 64);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+  } else {
+    return (int64_t)__shfl((int)v, src, 64);
+  }
+}
+
+// Class of column c given its value v, its left neighbour u and the bound,
+// assuming every column left of c passed (0 = no violation at c).
+__device__ __forceinline__ int column_class(int64_t c, int64_t v, int64_t u, int64_t bound) {
+  if (v == -1) return 0;
+  if (v < -1) return 1;                 // invalid sentinel
+  if (c > 0 && u == -1) return 2;       // follows trailing padding
+  if (v >= bound) return 3;             // out of range
+  if (c > 0 && v == u) return 4;        // duplicate
+  if (c > 0 && v < u) return 5;         // not strictly increasing
+  return 0;
+}
+
+template <bool I64>
+__global__ void __launch_bounds__(256)
+validate_kernel(const void* __restrict__ idx, int64_t rows, int64_t q_seq, int64_t rows_per_batch,
+                int64_t width,
+                const int32_t* __restrict__ valid_len, int64_t cache_len,
+                uint32_t* __restrict__ word, uint8_t* __restrict__ row_class,
+                uint64_t* __restrict__ first_bad, ErrorBlock* __restrict__ eb) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row < rows) {
+    const int64_t b = row / rows_per_batch;
+    const int64_t bound = valid_len ? (int64_t)valid_len[b] : cache_len;
+    const int64_t base = row * width;
+    const int64_t first_val = load_index<I64>(idx, base);
+    int64_t carry = 0;  // value of the column left of this chunk
+    int cls = 0;
+    int64_t col = -1;
+    for (int64_t c0 = 0; c0 < width; c0 += 64) {
+      const int64_t c = c0 + lane;
+      const bool in = c < width;
+      const int64_t v = in ? load_index<I64>(idx, base + c) : -1;
+      int64_t u = shfl_up1<I64>(v);
+      if (lane == 0) u = carry;
+      const int k = in ? column_class(c, v, u, bound) : 0;
+      const uint64_t m = __ballot(k != 0);
+      if (m != 0ull) {
+        const int src = __ffsll((long long)m) - 1;
+        cls = __shfl(k, src, 64);
+        col = c0 + src;
+        break;
+      }
+      carry = shfl_from<I64>(v, 63);
+    }
+    if (cls == 0 && first_val == -1) {
+      cls = 6;  // the row holds only -1
+      col = width;
+    }
+    if (lane == 0) {
+      if (row_class) row_class[row] = (uint8_t)cls;
+      if (cls) {
+        atomicOr(word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
+        const unsigned long long key = (unsigned long long)(row * (width + 1) + col);
+        atomicMin((unsigned long long*)(eb ? &eb->call_key : first_bad), key);
+      }
+    }
+  }
+  if (eb == nullptr) return;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  __threadfence();
+  const unsigned done = atomicAdd(&eb->done_blocks, 1u);
+  if (done != gridDim.x - 1) return;
+  // last block of this launch
+  __threadfence();
+  const unsigned long long key = atomicMin((unsigned long long*)&eb->call_key, ~0ull);
+  if (key != ~0ull && eb->detail_class == 0) {
+    const int64_t r = (int64_t)(key / (unsigned long long)(width + 1));
+    const int64_t c = (int64_t)(key % (unsigned long long)(width + 1));
+    const int64_t b = r / rows_per_batch;
+    const int64_t bound = valid_len ? (int64_t)valid_len[b] : cache_len;
+    int64_t v = -1, u = 0;
+    int k = 6;
+    if (c < width) {
+      v = load_index<I64>(idx, r * width + c);
+      u = c > 0 ? load_index<I64>(idx, r * width + c - 1) : 0;
+      k = column_class(c, v, u, bound);
+    }
+    eb->detail_value = v;
+    eb->detail_prev = u;
+    eb->detail_bound = bound;
+    eb->detail_b = b;
+    eb->detail_h = (r - b * rows_per_batch) / q_seq;
+    eb->detail_q = (r - b * rows_per_batch) % q_seq;
+    eb->detail_col = c;
+    eb->first_bad = key;
+    __threadfence();
+    eb->detail_class = k;
+  }
+  eb->call_key = ~0ull;
+  eb->done_blocks = 0u;
+}
+
+sa_status launch_validate(sparse_attn_ctx* c, const void* idx, int64_t batch, int64_t heads,
+                          int64_t q_seq, int64_t width, const int32_t* valid_len,
+                          int64_t cache_len, uint32_t* word, uint8_t* row_class,
+                          uint64_t* first_bad) {
+  const int64_t rows = batch * heads * q_seq;
+  if (rows <= 0) return SA_OK;
+  const int64_t blocks = (rows + 3) / 4;
+  if (blocks > 0x7fffffffLL) return set_error(c, SA_E_SHAPE, "validate_indices: too many rows");
+  // the context's block gathers the first failure's detail; caller-owned
+  // words and slots only get the OR and the atomic minimum
+  ErrorBlock* eb = (word == &c->err->word && first_bad == &c->err->first_bad) ? c->err : nullptr;
+  if (c->cfg.index_dtype == SA_IDX_I64) {
+    hipLaunchKernelGGL(validate_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, c->stream, idx,
+                       rows, q_seq, heads * q_seq, width, valid_len, cache_len, word, row_class,
+                       first_bad, eb);
+  } else {
+    hipLaunchKernelGGL(validate_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, c->stream,
+                       idx, rows, q_seq, heads * q_seq, width, valid_len, cache_len, word,
+                       row_class, first_bad, eb);
+  }
+  return check_hip(c, hipGetLastError(), "validate_indices");
+}
+
+}  // namespace sa

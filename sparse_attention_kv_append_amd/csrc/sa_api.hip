@@ -1,0 +1,412 @@
+// C ABI entry points: argument and shape checks (before any launch), the
+// context, dispatch to the kernels, and error reporting. Messages for index
+// errors use the IndexShare host validator's wording (`validate_indices`,
+// `index_error`).
+#include <math.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <mutex>
+#include <set>
+#include <string>
+
+#include "sa_internal.h"
+
+namespace {
+
+std::mutex g_reg_mu;
+std::set<const sparse_attn_ctx*> g_live;
+
+bool live(const sparse_attn_ctx* c) {
+  if (!c) return false;
+  std::lock_guard<std::mutex> lk(g_reg_mu);
+  return g_live.count(c) != 0 && c->magic == sa::kMagic;
+}
+
+int64_t elem_bytes(int dt) { return dt == SA_F32 ? 4 : 2; }
+
+int64_t record_bytes(int64_t dk, int64_t rope) { return (dk - rope) / 64 * 65 + 2 * rope; }
+
+std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0, long long d = 0) {
+  char buf[256];
+  snprintf(buf, sizeof buf, f, a, b, c, d);
+  return buf;
+}
+
+}  // namespace
+
+namespace sa {
+
+sa_status set_error(sparse_attn_ctx* c, sa_status s, const std::string& msg) {
+  if (c) c->last_error = msg;
+  return s;
+}
+
+sa_status check_hip(sparse_attn_ctx* c, hipError_t e, const char* what) {
+  if (e == hipSuccess) return SA_OK;
+  return set_error(c, SA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void prof_begin(sparse_attn_ctx* c) {
+  if (c->prof_n < (int64_t)c->prof_start.size()) (void)hipEventRecord(c->prof_start[c->prof_n], c->stream);
+}
+
+void prof_end(sparse_attn_ctx* c) {
+  if (c->prof_n < (int64_t)c->prof_stop.size()) {
+    (void)hipEventRecord(c->prof_stop[c->prof_n], c->stream);
+    c->prof_n++;
+  }
+}
+
+static void prof_release(sparse_attn_ctx* c) {
+  for (hipEvent_t e : c->prof_start) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->prof_stop) (void)hipEventDestroy(e);
+  c->prof_start.clear();
+  c->prof_stop.clear();
+  c->prof_n = 0;
+}
+
+}  // namespace sa
+
+using sa::check_hip;
+using sa::set_error;
+
+extern "C" {
+
+const char* sparse_attn_version(void) { return "sparse_attn 0.1.0 gfx950"; }
+
+sa_status sparse_attn_create(const sa_config* cfg, void* hip_stream, sparse_attn_ctx** out) {
+  if (!cfg || !out) return SA_E_ARG;
+  *out = nullptr;
+  const sa_config& k = *cfg;
+  if (k.num_heads <= 0 || k.kv_num_heads <= 0 || k.num_heads % k.kv_num_heads != 0) return SA_E_ARG;
+  if (k.head_dim_qk <= 0 || k.head_dim_v <= 0) return SA_E_ARG;
+  if (k.dtype < SA_F32 || k.dtype > SA_BF16) return SA_E_DTYPE;
+  if (k.kv_layout != SA_KV_SEPARATE && k.kv_layout != SA_KV_SHARED_LATENT) return SA_E_ARG;
+  if (k.index_dtype != SA_IDX_I32 && k.index_dtype != SA_IDX_I64) return SA_E_DTYPE;
+  if (k.cache_format != SA_CACHE_DENSE && k.cache_format != SA_CACHE_FP8_E4M3_BLOCK64) return SA_E_ARG;
+  if (k.kv_layout == SA_KV_SEPARATE && k.head_dim_v != k.head_dim_qk) return SA_E_SHAPE;
+  if (k.kv_layout == SA_KV_SHARED_LATENT && k.head_dim_v > k.head_dim_qk) return SA_E_SHAPE;
+  if (k.cache_format == SA_CACHE_FP8_E4M3_BLOCK64) {
+    if (k.kv_layout != SA_KV_SHARED_LATENT || k.dtype != SA_BF16) return SA_E_DTYPE;
+    if (k.rope_dim < 0 || k.rope_dim > k.head_dim_qk || (k.head_dim_qk - k.rope_dim) % 64 != 0)
+      return SA_E_SHAPE;
+  }
+  if (!isfinite(k.scale) || k.scale < 0.0f) return SA_E_ARG;
+  if (!isfinite(k.softcap) || k.softcap < 0.0f) return SA_E_ARG;
+  if (k.max_batch <= 0 || k.max_q_seq <= 0 || k.max_index_width <= 0 || k.max_cache_len <= 0)
+    return SA_E_ARG;
+  if (k.max_cache_len > 0x7fffffffLL || k.max_index_width > 0x7fffffffLL) return SA_E_UNSUPPORTED;
+  const bool mla = sa::mla_supported(k, 1);
+  // the generic kernel holds up to 8 heads x Dv/2 channel pairs per 256 threads
+  if (!mla && (k.head_dim_v % 2 != 0 || k.head_dim_v > 512 || k.head_dim_qk > 1024))
+    return SA_E_UNSUPPORTED;
+
+  sparse_attn_ctx* c = new sparse_attn_ctx();
+  c->magic = sa::kMagic;
+  c->cfg = k;
+  if (c->cfg.scale == 0.0f) c->cfg.scale = 1.0f / sqrtf((float)k.head_dim_qk);
+  c->stream = (hipStream_t)hip_stream;
+  c->err = nullptr;
+  c->partial_o = nullptr;
+  c->partial_ml = nullptr;
+  c->partial_rows = 0;
+  c->prof_n = 0;
+  hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess) e = hipMalloc((void**)&c->err, sizeof(sa::ErrorBlock));
+  if (e == hipSuccess && mla) {
+    const int64_t rows_max = k.max_batch * k.max_q_seq;
+    int64_t need = 0;
+    for (int64_t r = 1; r <= std::min<int64_t>(rows_max, sa::kNumCUs); r++) {
+      const int s = sa::mla_splits(r, k.max_index_width);
+      if (s > 1) need = std::max<int64_t>(need, r * s);
+    }
+    c->partial_rows = need;
+    if (need > 0) {
+      e = hipMalloc((void**)&c->partial_o, (size_t)need * k.num_heads * k.head_dim_v * sizeof(float));
+      if (e == hipSuccess)
+        e = hipMalloc((void**)&c->partial_ml, (size_t)need * k.num_heads * 2 * sizeof(float));
+    }
+  }
+  if (e == hipSuccess) {
+    sa::launch_reset_error(c);
+    e = hipStreamSynchronize(c->stream);
+  }
+  if (e != hipSuccess) {
+    if (c->err) (void)hipFree(c->err);
+    if (c->partial_o) (void)hipFree(c->partial_o);
+    if (c->partial_ml) (void)hipFree(c->partial_ml);
+    delete c;
+    return SA_E_HIP;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    g_live.insert(c);
+  }
+  *out = c;
+  return SA_OK;
+}
+
+sa_status sparse_attn_destroy(sparse_attn_ctx* c) {
+  if (!c) return SA_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    if (!g_live.count(c)) return SA_E_STATE;
+    g_live.erase(c);
+  }
+  (void)hipStreamSynchronize(c->stream);
+  sa::prof_release(c);
+  if (c->err) (void)hipFree(c->err);
+  if (c->partial_o) (void)hipFree(c->partial_o);
+  if (c->partial_ml) (void)hipFree(c->partial_ml);
+  c->magic = 0;
+  delete c;
+  return SA_OK;
+}
+
+sa_status sparse_attn_set_stream(sparse_attn_ctx* c, void* hip_stream) {
+  if (!live(c)) return SA_E_STATE;
+  c->stream = (hipStream_t)hip_stream;
+  return SA_OK;
+}
+
+sa_status sparse_attn_reset_error_async(sparse_attn_ctx* c) {
+  if (!live(c)) return SA_E_STATE;
+  return sa::launch_reset_error(c);
+}
+
+sa_status sparse_attn_kv_append(sparse_attn_ctx* c, int64_t batch, const void* past_k,
+                                const void* past_v, int64_t past_capacity, const int32_t* past_len,
+                                const void* cur_k, const void* cur_v, int64_t cur_len,
+                                int32_t cur_is_unquantized_bf16, void* present_k, void* present_v,
+                                int64_t present_capacity, int32_t* present_len) {
+  if (!live(c)) return SA_E_STATE;
+  const sa_config& k = c->cfg;
+  c->last_error.clear();
+  if (batch <= 0 || batch > k.max_batch)
+    return set_error(c, SA_E_STATE, fmt("kv_append: batch %lld outside [1, max_batch %lld]", batch, k.max_batch));
+  if (cur_len < 0 || past_capacity < 0 || present_capacity <= 0)
+    return set_error(c, SA_E_ARG, "kv_append: negative length or non-positive present capacity");
+  if (!cur_k || !present_k) return set_error(c, SA_E_ARG, "kv_append: cur_k and present_k are required");
+  const bool latent = k.kv_layout == SA_KV_SHARED_LATENT;
+  if (latent && (past_v || cur_v || present_v))
+    return set_error(c, SA_E_ARG, "kv_append: shared-latent caches take no value tensors");
+  if (!latent && (!cur_v || !present_v))
+    return set_error(c, SA_E_ARG, "kv_append: cur_v and present_v are required");
+  if (past_capacity > 0 && (!past_k || (!latent && !past_v)))
+    return set_error(c, SA_E_ARG, "kv_append: past tensors are required when past_capacity > 0");
+  const bool fp8 = k.cache_format == SA_CACHE_FP8_E4M3_BLOCK64;
+  if (cur_is_unquantized_bf16 && !fp8)
+    return set_error(c, SA_E_DTYPE, "kv_append: cur_is_unquantized_bf16 needs an fp8_e4m3_block64 cache");
+  if (!past_len && past_capacity + cur_len > present_capacity)
+    return set_error(c, SA_E_CAPACITY,
+                     fmt("kv_append: past %lld + current %lld rows exceed present capacity %lld",
+                         past_capacity, cur_len, present_capacity));
+  if (cur_len > present_capacity)
+    return set_error(c, SA_E_CAPACITY, "kv_append: current rows exceed present capacity");
+  const int64_t heads = k.kv_num_heads;
+  const int64_t krow = fp8 ? record_bytes(k.head_dim_qk, k.rope_dim) : k.head_dim_qk * elem_bytes(k.dtype);
+  const bool copy_past = past_capacity > 0 && present_k != past_k;
+  sa_status s;
+  if (fp8 && cur_is_unquantized_bf16) {
+    if (copy_past) {
+      s = sa::launch_append_copy(c, batch, heads, krow, past_k, past_capacity, past_len, nullptr, 0,
+                                 present_k, present_capacity, true, nullptr);
+      if (s != SA_OK) return s;
+    }
+    s = sa::launch_append_quantize(c, batch, heads, k.head_dim_qk, k.rope_dim, cur_k, cur_len,
+                                   past_len, past_capacity, present_k, present_capacity, present_len);
+    return s;
+  }
+  s = sa::launch_append_copy(c, batch, heads, krow, past_k, past_capacity, past_len, cur_k, cur_len,
+                             present_k, present_capacity, copy_past, present_len);
+  if (s != SA_OK || latent) return s;
+  const int64_t vrow = k.head_dim_v * elem_bytes(k.dtype);
+  const bool copy_past_v = past_capacity > 0 && present_v != past_v;
+  return sa::launch_append_copy(c, batch, heads, vrow, past_v, past_capacity, past_len, cur_v,
+                                cur_len, present_v, present_capacity, copy_past_v, nullptr);
+}
+
+static sa_status check_index_geometry(sparse_attn_ctx* c, int64_t batch, int64_t index_heads,
+                                      int64_t q_seq, int64_t width) {
+  const sa_config& k = c->cfg;
+  if (batch <= 0 || batch > k.max_batch)
+    return set_error(c, SA_E_STATE, fmt("batch %lld outside [1, max_batch %lld]", batch, k.max_batch));
+  if (q_seq <= 0 || q_seq > k.max_q_seq)
+    return set_error(c, SA_E_STATE, fmt("q_seq %lld outside [1, max_q_seq %lld]", q_seq, k.max_q_seq));
+  if (width <= 0) return set_error(c, SA_E_SHAPE, "selected_indices K dimension must be nonzero");
+  if (width > k.max_index_width)
+    return set_error(c, SA_E_STATE, fmt("index width %lld above max_index_width %lld", width, k.max_index_width));
+  if (index_heads != 1 && index_heads != k.num_heads)
+    return set_error(c, SA_E_SHAPE, fmt("selected_indices must have shape [B, 1|N, S_q, K] (N = %lld), got %lld heads",
+                                         k.num_heads, index_heads));
+  return SA_OK;
+}
+
+sa_status sparse_attn_validate_indices(sparse_attn_ctx* c, const void* indices, int64_t batch,
+                                       int64_t index_heads, int64_t q_seq, int64_t width,
+                                       const int32_t* valid_len, int64_t cache_len,
+                                       uint32_t* error_word, uint8_t* row_class,
+                                       uint64_t* first_bad) {
+  if (!live(c)) return SA_E_STATE;
+  c->last_error.clear();
+  if (!indices) return set_error(c, SA_E_ARG, "validate_indices: indices is NULL");
+  sa_status s = check_index_geometry(c, batch, index_heads, q_seq, width);
+  if (s != SA_OK) return s;
+  if (!valid_len && cache_len < 0) return set_error(c, SA_E_ARG, "validate_indices: negative cache_len");
+  if (!error_word) error_word = &c->err->word;
+  if (!first_bad) first_bad = &c->err->first_bad;
+  return sa::launch_validate(c, indices, batch, index_heads, q_seq, width, valid_len, cache_len,
+                             error_word, row_class, first_bad);
+}
+
+sa_status sparse_attn_query_plan(const sparse_attn_ctx* c, int64_t batch, int64_t q_seq,
+                                 int64_t index_heads, int64_t width, int32_t* path, int32_t* splits) {
+  if (!live(c) || !path || !splits) return SA_E_STATE;
+  if (sa::mla_supported(c->cfg, index_heads)) {
+    *path = 1;
+    *splits = sa::mla_splits(batch * q_seq, width);
+  } else {
+    *path = 0;
+    *splits = 1;
+  }
+  return SA_OK;
+}
+
+sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq,
+                              const void* present_k, const void* present_v,
+                              int64_t cache_capacity, const int32_t* valid_len,
+                              const void* indices, int64_t index_heads, int64_t width, void* y,
+                              int32_t fused_validate) {
+  if (!live(c)) return SA_E_STATE;
+  c->last_error.clear();
+  const sa_config& k = c->cfg;
+  if (!q || !present_k || !indices || !y) return set_error(c, SA_E_ARG, "forward: q, present_k, indices and y are required");
+  const bool latent = k.kv_layout == SA_KV_SHARED_LATENT;
+  if (latent && present_v) return set_error(c, SA_E_ARG, "forward: shared-latent caches take no present_v");
+  if (!latent && !present_v) return set_error(c, SA_E_ARG, "forward: present_v is required");
+  if (cache_capacity <= 0 || cache_capacity > k.max_cache_len)
+    return set_error(c, SA_E_STATE, fmt("forward: cache capacity %lld outside [1, max_cache_len %lld]",
+                                        cache_capacity, k.max_cache_len));
+  sa_status s = check_index_geometry(c, batch, index_heads, q_seq, width);
+  if (s != SA_OK) return s;
+  if (fused_validate) {
+    s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
+                                     cache_capacity, nullptr, nullptr, nullptr);
+    if (s != SA_OK) return s;
+  }
+  sa::FwdArgs a;
+  a.q = q;
+  a.k = present_k;
+  a.v = present_v;
+  a.idx = indices;
+  a.valid_len = valid_len;
+  a.y = y;
+  a.batch = batch;
+  a.hq = k.num_heads;
+  a.hkv = k.kv_num_heads;
+  a.q_seq = q_seq;
+  a.dk = k.head_dim_qk;
+  a.dv = k.head_dim_v;
+  a.rope = k.rope_dim;
+  a.cap = cache_capacity;
+  a.index_heads = index_heads;
+  a.width = width;
+  a.scale = k.scale;
+  a.softcap = k.softcap;
+  a.dtype = k.dtype;
+  a.cache_format = k.cache_format;
+  a.kv_layout = k.kv_layout;
+  a.idx64 = k.index_dtype == SA_IDX_I64;
+  if (sa::mla_supported(k, index_heads)) {
+    return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
+  }
+  return sa::launch_forward_generic(c, a);
+}
+
+sa_status sparse_attn_read_error(sparse_attn_ctx* c, uint32_t* word, uint64_t* first_bad) {
+  if (!live(c)) return SA_E_STATE;
+  sa::ErrorBlock eb;
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e == hipSuccess) e = hipMemcpy(&eb, c->err, sizeof eb, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return check_hip(c, e, "read_error");
+  if (word) *word = eb.word;
+  if (first_bad) *first_bad = eb.first_bad;
+  if (eb.word == 0) {
+    c->last_error.clear();
+    return SA_OK;
+  }
+  std::string msg;
+  if ((eb.word & SA_ERR_INDEX_ANY) && eb.detail_class != 0) {
+    const long long b = eb.detail_b, h = eb.detail_h, q = eb.detail_q, col = eb.detail_col;
+    const long long v = eb.detail_value, u = eb.detail_prev, bound = eb.detail_bound;
+    const std::string head =
+        fmt("selected_indices [batch=%lld, head=%lld, query=%lld, column=%lld]: ", b, h, q, col);
+    switch (eb.detail_class) {
+      case 1: msg = head + fmt("invalid sentinel %lld", v); break;
+      case 2: msg = head + fmt("index %lld follows trailing -1 padding", v); break;
+      case 3: msg = head + fmt("index %lld is out of range for cache length %lld", v, bound); break;
+      case 4: msg = head + fmt("duplicate index %lld", v); break;
+      case 5: msg = head + fmt("indices are not strictly increasing: %lld then %lld", u, v); break;
+      default: msg = fmt("selected_indices row [batch=%lld, head=%lld, query=%lld] is all -1", b, h, q);
+    }
+  }
+  if (eb.word & SA_ERR_APPEND_CAPACITY) {
+    if (!msg.empty()) msg += "; ";
+    msg += "kv_append: a batch's past_len + cur_len does not fit its capacity";
+  }
+  if (eb.word & SA_ERR_QUANT_NONFINITE) {
+    if (!msg.empty()) msg += "; ";
+    msg += "kv_append: non-finite value in a row given to the fp8 quantizer";
+  }
+  if (msg.empty()) msg = fmt("device error word 0x%llx", (long long)eb.word);
+  c->last_error = msg;
+  return SA_E_INDEX;
+}
+
+sa_status sparse_attn_profile_enable(sparse_attn_ctx* c, int32_t max_launches) {
+  if (!live(c)) return SA_E_STATE;
+  if (max_launches < 0) return set_error(c, SA_E_ARG, "profile_enable: negative max_launches");
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return check_hip(c, e, "profile_enable");
+  sa::prof_release(c);
+  for (int32_t i = 0; i < max_launches; i++) {
+    hipEvent_t a, b;
+    e = hipEventCreate(&a);
+    if (e == hipSuccess) {
+      e = hipEventCreate(&b);
+      if (e != hipSuccess) (void)hipEventDestroy(a);
+    }
+    if (e != hipSuccess) {
+      sa::prof_release(c);
+      return check_hip(c, e, "profile_enable");
+    }
+    c->prof_start.push_back(a);
+    c->prof_stop.push_back(b);
+  }
+  return SA_OK;
+}
+
+sa_status sparse_attn_profile_read(sparse_attn_ctx* c, double* total_ms, int64_t* launches) {
+  if (!live(c)) return SA_E_STATE;
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return check_hip(c, e, "profile_read");
+  double sum = 0.0;
+  for (int64_t i = 0; i < c->prof_n; i++) {
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, c->prof_start[i], c->prof_stop[i]);
+    if (e != hipSuccess) return check_hip(c, e, "profile_read");
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = c->prof_n;
+  c->prof_n = 0;
+  return SA_OK;
+}
+
+const char* sparse_attn_last_error(const sparse_attn_ctx* c) {
+  if (!live(c)) return "invalid or destroyed sparse_attn context";
+  return c->last_error.c_str();
+}
+
+}  // extern "C"

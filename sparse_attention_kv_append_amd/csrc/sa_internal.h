@@ -1,0 +1,148 @@
+// Internal declarations shared by the library's translation units (host
+// launchers, the context, small device helpers). Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/sparse_attn.h"
+
+namespace sa {
+
+constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
+
+struct ErrorBlock {  // device layout of the context's error state
+  uint32_t word;        // OR-latched error bits
+  uint32_t done_blocks; // validation blocks finished in the current launch
+  uint64_t first_bad;   // row*(W+1)+col of the first failing call's first violation
+  uint64_t call_key;    // the same, within the current validation launch
+  int64_t detail_value; // index at first_bad
+  int64_t detail_prev;  // index left of it (column > 0)
+  int64_t detail_bound; // cache length of its batch
+  int64_t detail_b, detail_h, detail_q, detail_col;  // where it is
+  int32_t detail_class; // 1..6, 0 = no detail recorded
+  int32_t pad;
+};
+
+}  // namespace sa
+
+struct sparse_attn_ctx {
+  uint32_t magic;
+  sa_config cfg;
+  hipStream_t stream;
+  int device;
+  sa::ErrorBlock* err;  // device
+  float* partial_o;     // device: split-K unnormalised outputs
+  float* partial_ml;    // device: split-K (max, sum) pairs
+  int64_t partial_rows; // capacity of the partial buffers in (row, split) units
+  std::string last_error;
+  // optional timing of the main forward kernel
+  std::vector<hipEvent_t> prof_start, prof_stop;
+  int64_t prof_n;
+};
+
+namespace sa {
+
+constexpr uint32_t kMagic = 0x53504154u;  // "SPAT"
+
+// ---- device helpers ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t w = __float_as_uint(f);
+  if ((w & 0x7f800000u) == 0x7f800000u && (w & 0x007fffffu)) return (uint16_t)((w >> 16) | 0x40u);
+  w += 0x7fffu + ((w >> 16) & 1u);
+  return (uint16_t)(w >> 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if constexpr (DT == SA_F32) {
+    return ((const float*)p)[i];
+  } else if constexpr (DT == SA_F16) {
+    return (float)((const _Float16*)p)[i];
+  } else {
+    return bf16_to_f32(((const uint16_t*)p)[i]);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
+  if constexpr (DT == SA_F32) {
+    ((float*)p)[i] = v;
+  } else if constexpr (DT == SA_F16) {
+    ((_Float16*)p)[i] = (_Float16)v;  // round to nearest even
+  } else {
+    ((uint16_t*)p)[i] = f32_to_bf16_rne(v);
+  }
+}
+
+template <bool I64>
+__device__ __forceinline__ int64_t load_index(const void* p, int64_t i) {
+  if constexpr (I64) {
+    return ((const int64_t*)p)[i];
+  } else {
+    return (int64_t)((const int32_t*)p)[i];
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---- host launchers (one per translation unit) ---------------------------
+
+sa_status launch_reset_error(sparse_attn_ctx* c);
+sa_status launch_append_copy(sparse_attn_ctx* c, int64_t batch, int64_t heads, int64_t row_bytes,
+                             const void* past, int64_t past_cap, const int32_t* past_len,
+                             const void* cur, int64_t cur_len, void* present, int64_t present_cap,
+                             bool copy_past, int32_t* present_len);
+sa_status launch_append_quantize(sparse_attn_ctx* c, int64_t batch, int64_t heads, int64_t dk,
+                                 int64_t rope, const void* cur_bf16, int64_t cur_len,
+                                 const int32_t* past_len, int64_t past_cap, void* present,
+                                 int64_t present_cap, int32_t* present_len);
+sa_status launch_validate(sparse_attn_ctx* c, const void* idx, int64_t batch, int64_t heads,
+                          int64_t q_seq, int64_t width, const int32_t* valid_len,
+                          int64_t cache_len, uint32_t* word, uint8_t* row_class,
+                          uint64_t* first_bad);
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* idx;
+  const int32_t* valid_len;
+  void* y;
+  int64_t batch, hq, hkv, q_seq, dk, dv, rope, cap, index_heads, width;
+  float scale, softcap;
+  int dtype, cache_format, kv_layout, idx64;
+};
+
+bool mla_supported(const sa_config& cfg, int64_t index_heads);
+int mla_splits(int64_t rows, int64_t width);
+sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a);
+sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
+
+sa_status set_error(sparse_attn_ctx* c, sa_status s, const std::string& msg);
+// event pair around the main forward kernel when profiling is on
+void prof_begin(sparse_attn_ctx* c);
+void prof_end(sparse_attn_ctx* c);
+sa_status check_hip(sparse_attn_ctx* c, hipError_t e, const char* what);
+
+}  // namespace sa
