@@ -171,7 +171,8 @@ class Setup:
 
 
 def kernel_name(setup):
-    return "mla_forward_kernel" if setup.path == 1 else "generic_forward_kernel"
+    return {0: "generic_forward_kernel", 1: "mla_forward_kernel",
+            2: "latent_forward_kernel"}[setup.path]
 
 
 def counters_for(setup):

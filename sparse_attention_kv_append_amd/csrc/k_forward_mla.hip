@@ -345,14 +345,14 @@ mla_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ c
 
 // Log-sum-exp merge of the split partials (standard Attention page,
 // `attention_combine`): M = max_j m_j, y = sum_j o_j 2^(m_j-M) / sum_j l_j 2^(m_j-M).
-// One 128-thread workgroup per (row, head); thread owns 4 channels.
+// One 128-thread workgroup per (row, head); thread owns 4 channels. Block b
+// serves row b % rows, so it runs on the XCD whose L2 took that row's partials.
 __global__ void __launch_bounds__(128)
 mla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                   uint16_t* __restrict__ y, int64_t q_seq, int splits) {
+                   uint16_t* __restrict__ y, int64_t rows, int64_t q_seq, int splits) {
   using namespace mla;
-  const int64_t rh = blockIdx.x;
-  const int64_t row = rh / NH;
-  const int head = (int)(rh - row * NH);
+  const int64_t row = (int64_t)(blockIdx.x % (unsigned)rows);
+  const int head = (int)(blockIdx.x / (unsigned)rows);
   const int64_t b = row / q_seq, qi = row - b * q_seq;
   float M = -INFINITY;
   for (int j = 0; j < splits; j++) M = fmaxf(M, part_ml[((row * splits + j) * NH + head) * 2]);
@@ -376,6 +376,12 @@ mla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
   const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
   const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
   *(uint2*)yp = make_uint2(lo, hi);
+}
+
+sa_status launch_mla_combine(sparse_attn_ctx* c, int64_t rows, int64_t q_seq, int splits, uint16_t* y) {
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * mla::NH)), dim3(mla::DV / 4), 0,
+                     c->stream, c->partial_o, c->partial_ml, y, rows, q_seq, splits);
+  return check_hip(c, hipGetLastError(), "forward (combine)");
 }
 
 bool mla_supported(const sa_config& cfg, int64_t index_heads) {
@@ -436,9 +442,7 @@ sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits) {
   prof_end(c);
   sa_status s = check_hip(c, hipGetLastError(), "forward (mla)");
   if (s != SA_OK || splits == 1) return s;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * NH)), dim3(DV / 4), 0, c->stream,
-                     c->partial_o, c->partial_ml, (uint16_t*)a.y, a.q_seq, splits);
-  return check_hip(c, hipGetLastError(), "forward (mla combine)");
+  return launch_mla_combine(c, rows, a.q_seq, splits, (uint16_t*)a.y);
 }
 
 }  // namespace sa

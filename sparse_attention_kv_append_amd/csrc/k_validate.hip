@@ -13,7 +13,7 @@
 // is gathered with an atomic minimum; the last block to finish then records
 // that violation's class and values (for the host message) if no earlier
 // launch since the last reset has failed, and re-arms the per-launch slot.
-#include "sa_internal.h"
+#include "sa_validate_dev.h"
 
 namespace sa {
 
@@ -39,18 +39,6 @@ __device__ __forceinline__ int64_t shfl_from(int64_t v, int src) {
   }
 }
 
-// Class of column c given its value v, its left neighbour u and the bound,
-// assuming every column left of c passed (0 = no violation at c).
-__device__ __forceinline__ int column_class(int64_t c, int64_t v, int64_t u, int64_t bound) {
-  if (v == -1) return 0;
-  if (v < -1) return 1;                 // invalid sentinel
-  if (c > 0 && u == -1) return 2;       // follows trailing padding
-  if (v >= bound) return 3;             // out of range
-  if (c > 0 && v == u) return 4;        // duplicate
-  if (c > 0 && v < u) return 5;         // not strictly increasing
-  return 0;
-}
-
 template <bool I64>
 __global__ void __launch_bounds__(256)
 validate_kernel(const void* __restrict__ idx, int64_t rows, int64_t q_seq, int64_t rows_per_batch,
@@ -65,24 +53,34 @@ validate_kernel(const void* __restrict__ idx, int64_t rows, int64_t q_seq, int64
     const int64_t bound = valid_len ? (int64_t)valid_len[b] : cache_len;
     const int64_t base = row * width;
     const int64_t first_val = load_index<I64>(idx, base);
-    int64_t carry = 0;  // value of the column left of this chunk
+    int64_t carry = 0;  // value of the column left of the current chunk
     int cls = 0;
     int64_t col = -1;
-    for (int64_t c0 = 0; c0 < width; c0 += 64) {
-      const int64_t c = c0 + lane;
-      const bool in = c < width;
-      const int64_t v = in ? load_index<I64>(idx, base + c) : -1;
-      int64_t u = shfl_up1<I64>(v);
-      if (lane == 0) u = carry;
-      const int k = in ? column_class(c, v, u, bound) : 0;
-      const uint64_t m = __ballot(k != 0);
-      if (m != 0ull) {
-        const int src = __ffsll((long long)m) - 1;
-        cls = __shfl(k, src, 64);
-        col = c0 + src;
-        break;
+    // 8 chunks of 64 columns per round trip: their loads are all in flight
+    // before the first chunk is checked
+    for (int64_t c0 = 0; c0 < width && cls == 0; c0 += 8 * 64) {
+      int64_t vals[8];
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int64_t c = c0 + 64 * k + lane;
+        vals[k] = c < width ? load_index<I64>(idx, base + c) : -1;
       }
-      carry = shfl_from<I64>(v, 63);
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int64_t c = c0 + 64 * k + lane;
+        if (c0 + 64 * k >= width || cls != 0) break;
+        const int64_t v = vals[k];
+        int64_t u = shfl_up1<I64>(v);
+        if (lane == 0) u = carry;
+        const int kc = c < width ? column_class(c, v, u, bound) : 0;
+        const uint64_t m = __ballot(kc != 0);
+        if (m != 0ull) {
+          const int src = __ffsll((long long)m) - 1;
+          cls = __shfl(kc, src, 64);
+          col = c0 + 64 * k + src;
+        }
+        carry = shfl_from<I64>(v, 63);
+      }
     }
     if (cls == 0 && first_val == -1) {
       cls = 6;  // the row holds only -1
@@ -99,38 +97,7 @@ validate_kernel(const void* __restrict__ idx, int64_t rows, int64_t q_seq, int64
   }
   if (eb == nullptr) return;
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  __threadfence();
-  const unsigned done = atomicAdd(&eb->done_blocks, 1u);
-  if (done != gridDim.x - 1) return;
-  // last block of this launch
-  __threadfence();
-  const unsigned long long key = atomicMin((unsigned long long*)&eb->call_key, ~0ull);
-  if (key != ~0ull && eb->detail_class == 0) {
-    const int64_t r = (int64_t)(key / (unsigned long long)(width + 1));
-    const int64_t c = (int64_t)(key % (unsigned long long)(width + 1));
-    const int64_t b = r / rows_per_batch;
-    const int64_t bound = valid_len ? (int64_t)valid_len[b] : cache_len;
-    int64_t v = -1, u = 0;
-    int k = 6;
-    if (c < width) {
-      v = load_index<I64>(idx, r * width + c);
-      u = c > 0 ? load_index<I64>(idx, r * width + c - 1) : 0;
-      k = column_class(c, v, u, bound);
-    }
-    eb->detail_value = v;
-    eb->detail_prev = u;
-    eb->detail_bound = bound;
-    eb->detail_b = b;
-    eb->detail_h = (r - b * rows_per_batch) / q_seq;
-    eb->detail_q = (r - b * rows_per_batch) % q_seq;
-    eb->detail_col = c;
-    eb->first_bad = key;
-    __threadfence();
-    eb->detail_class = k;
-  }
-  eb->call_key = ~0ull;
-  eb->done_blocks = 0u;
+  if (threadIdx.x == 0) finish_launch<I64>(eb, idx, width, q_seq, rows_per_batch, valid_len, cache_len);
 }
 
 sa_status launch_validate(sparse_attn_ctx* c, const void* idx, int64_t batch, int64_t heads,

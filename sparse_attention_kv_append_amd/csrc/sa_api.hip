@@ -58,6 +58,17 @@ void prof_end(sparse_attn_ctx* c) {
   }
 }
 
+void free_buffers(sparse_attn_ctx* c) {
+  void* bufs[] = {c->err, c->partial_o, c->partial_ml, c->zeros, c->row_key, c->row_done};
+  for (void* p : bufs)
+    if (p) (void)hipFree(p);
+  c->err = nullptr;
+  c->partial_o = c->partial_ml = nullptr;
+  c->zeros = nullptr;
+  c->row_key = nullptr;
+  c->row_done = nullptr;
+}
+
 static void prof_release(sparse_attn_ctx* c) {
   for (hipEvent_t e : c->prof_start) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof_stop) (void)hipEventDestroy(e);
@@ -111,6 +122,10 @@ sa_status sparse_attn_create(const sa_config* cfg, void* hip_stream, sparse_attn
   c->partial_o = nullptr;
   c->partial_ml = nullptr;
   c->partial_rows = 0;
+  c->zeros = nullptr;
+  c->row_key = nullptr;
+  c->row_done = nullptr;
+  c->rows_cap = k.max_batch * k.max_q_seq;
   c->prof_n = 0;
   hipError_t e = hipGetDevice(&c->device);
   if (e == hipSuccess) e = hipMalloc((void**)&c->err, sizeof(sa::ErrorBlock));
@@ -128,14 +143,20 @@ sa_status sparse_attn_create(const sa_config* cfg, void* hip_stream, sparse_attn
         e = hipMalloc((void**)&c->partial_ml, (size_t)need * k.num_heads * 2 * sizeof(float));
     }
   }
+  if (e == hipSuccess) e = hipMalloc((void**)&c->zeros, 1024);
+  if (e == hipSuccess) e = hipMemset(c->zeros, 0, 1024);
+  if (e == hipSuccess && mla) {
+    e = hipMalloc((void**)&c->row_key, (size_t)c->rows_cap * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipMemset(c->row_key, 0xff, (size_t)c->rows_cap * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipMalloc((void**)&c->row_done, (size_t)c->rows_cap * sizeof(unsigned));
+    if (e == hipSuccess) e = hipMemset(c->row_done, 0, (size_t)c->rows_cap * sizeof(unsigned));
+  }
   if (e == hipSuccess) {
     sa::launch_reset_error(c);
     e = hipStreamSynchronize(c->stream);
   }
   if (e != hipSuccess) {
-    if (c->err) (void)hipFree(c->err);
-    if (c->partial_o) (void)hipFree(c->partial_o);
-    if (c->partial_ml) (void)hipFree(c->partial_ml);
+    sa::free_buffers(c);
     delete c;
     return SA_E_HIP;
   }
@@ -156,9 +177,7 @@ sa_status sparse_attn_destroy(sparse_attn_ctx* c) {
   }
   (void)hipStreamSynchronize(c->stream);
   sa::prof_release(c);
-  if (c->err) (void)hipFree(c->err);
-  if (c->partial_o) (void)hipFree(c->partial_o);
-  if (c->partial_ml) (void)hipFree(c->partial_ml);
+  sa::free_buffers(c);
   c->magic = 0;
   delete c;
   return SA_OK;
@@ -264,7 +283,7 @@ sa_status sparse_attn_query_plan(const sparse_attn_ctx* c, int64_t batch, int64_
                                  int64_t index_heads, int64_t width, int32_t* path, int32_t* splits) {
   if (!live(c) || !path || !splits) return SA_E_STATE;
   if (sa::mla_supported(c->cfg, index_heads)) {
-    *path = 1;
+    *path = c->cfg.cache_format == SA_CACHE_DENSE ? 2 : 1;
     *splits = sa::mla_splits(batch * q_seq, width);
   } else {
     *path = 0;
@@ -290,7 +309,10 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
                                         cache_capacity, k.max_cache_len));
   sa_status s = check_index_geometry(c, batch, index_heads, q_seq, width);
   if (s != SA_OK) return s;
-  if (fused_validate) {
+  // the bf16 shared-latent kernel validates its own columns; other paths
+  // run the validation kernel first on the same stream
+  const bool latent_bf16 = sa::mla_supported(k, index_heads) && k.cache_format == SA_CACHE_DENSE;
+  if (fused_validate && !latent_bf16) {
     s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
                                      cache_capacity, nullptr, nullptr, nullptr);
     if (s != SA_OK) return s;
@@ -318,6 +340,9 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
   a.cache_format = k.cache_format;
   a.kv_layout = k.kv_layout;
   a.idx64 = k.index_dtype == SA_IDX_I64;
+  if (latent_bf16) {
+    return sa::launch_forward_latent(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
+  }
   if (sa::mla_supported(k, index_heads)) {
     return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
   }

@@ -39,6 +39,10 @@ struct sparse_attn_ctx {
   float* partial_o;     // device: split-K unnormalised outputs
   float* partial_ml;    // device: split-K (max, sum) pairs
   int64_t partial_rows; // capacity of the partial buffers in (row, split) units
+  uint8_t* zeros;       // device: 1 KB of zeros (source of padded tile slots)
+  unsigned long long* row_key;  // device [rows_cap]: per-row first violation, fused validation
+  unsigned* row_done;           // device [rows_cap]: splits of a row that finished validation
+  int64_t rows_cap;
   std::string last_error;
   // optional timing of the main forward kernel
   std::vector<hipEvent_t> prof_start, prof_stop;
@@ -138,8 +142,11 @@ bool mla_supported(const sa_config& cfg, int64_t index_heads);
 int mla_splits(int64_t rows, int64_t width);
 sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a);
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
+sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused);
+sa_status launch_mla_combine(sparse_attn_ctx* c, int64_t rows, int64_t q_seq, int splits, uint16_t* y);
 
 sa_status set_error(sparse_attn_ctx* c, sa_status s, const std::string& msg);
+void free_buffers(sparse_attn_ctx* c);
 // event pair around the main forward kernel when profiling is on
 void prof_begin(sparse_attn_ctx* c);
 void prof_end(sparse_attn_ctx* c);

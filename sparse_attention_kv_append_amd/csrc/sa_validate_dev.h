@@ -1,0 +1,66 @@
+// Device-side pieces of index validation shared by the standalone validation
+// kernel and the fused validation inside the shared-latent forward kernel.
+// The rules are the IndexShare host `validate_indices` checks, applied to one
+// column given its left neighbour (valid whenever every column before it
+// passed, which is all the first violation needs).
+#pragma once
+
+#include "sa_internal.h"
+
+namespace sa {
+
+// Class of column c holding v, with left neighbour u and cache bound
+// (0 = no violation at c). Check order: sentinel, padding, range, duplicate,
+// order.
+__device__ __forceinline__ int column_class(int64_t c, int64_t v, int64_t u, int64_t bound) {
+  if (v == -1) return 0;
+  if (v < -1) return 1;                 // invalid sentinel
+  if (c > 0 && u == -1) return 2;       // follows trailing padding
+  if (v >= bound) return 3;             // out of range
+  if (c > 0 && v == u) return 4;        // duplicate
+  if (c > 0 && v < u) return 5;         // not strictly increasing
+  return 0;
+}
+
+// Called by one thread of every block of a launch that gathers into the
+// context's error block, after the block's contributions to eb->call_key are
+// visible. The last block to arrive records the launch's first violation
+// (class, values, position) if no earlier launch since the reset failed, then
+// re-arms the per-launch slot and counter for the next launch on the stream.
+template <bool I64>
+__device__ __forceinline__ void finish_launch(ErrorBlock* __restrict__ eb, const void* __restrict__ idx,
+                                              int64_t width, int64_t q_seq, int64_t rows_per_batch,
+                                              const int32_t* __restrict__ valid_len, int64_t cache_len) {
+  __threadfence();
+  const unsigned done = atomicAdd(&eb->done_blocks, 1u);
+  if (done != gridDim.x * gridDim.y * gridDim.z - 1) return;
+  __threadfence();
+  const unsigned long long key = atomicMin((unsigned long long*)&eb->call_key, ~0ull);
+  if (key != ~0ull && eb->detail_class == 0) {
+    const int64_t r = (int64_t)(key / (unsigned long long)(width + 1));
+    const int64_t c = (int64_t)(key % (unsigned long long)(width + 1));
+    const int64_t b = r / rows_per_batch;
+    const int64_t bound = valid_len ? (int64_t)valid_len[b] : cache_len;
+    int64_t v = -1, u = 0;
+    int k = 6;  // column == width: the row holds only -1
+    if (c < width) {
+      v = load_index<I64>(idx, r * width + c);
+      u = c > 0 ? load_index<I64>(idx, r * width + c - 1) : 0;
+      k = column_class(c, v, u, bound);
+    }
+    eb->detail_value = v;
+    eb->detail_prev = u;
+    eb->detail_bound = bound;
+    eb->detail_b = b;
+    eb->detail_h = (r - b * rows_per_batch) / q_seq;
+    eb->detail_q = (r - b * rows_per_batch) % q_seq;
+    eb->detail_col = c;
+    eb->first_bad = key;
+    __threadfence();
+    eb->detail_class = k;
+  }
+  eb->call_key = ~0ull;
+  eb->done_blocks = 0u;
+}
+
+}  // namespace sa

@@ -60,7 +60,7 @@ def test_parity(name, mode):
 
 
 def test_plan_selects_expected_paths():
-    for name, want in [("decode_bf16_small", 1), ("prefill_small", 1), ("tiny_f32", 0),
+    for name, want in [("decode_bf16_small", 2), ("prefill_small", 2), ("tiny_f32", 0),
                        ("dense_gqa_small", 0), ("mqa_generic_bf16", 0), ("decode_fp8_small", 1)]:
         w = CASES[name]
         ctx = make_ctx(w)
