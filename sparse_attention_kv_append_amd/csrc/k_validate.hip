@@ -97,7 +97,8 @@ validate_kernel(const void* __restrict__ idx, int64_t rows, int64_t q_seq, int64
   }
   if (eb == nullptr) return;
   __syncthreads();
-  if (threadIdx.x == 0) finish_launch<I64>(eb, idx, width, q_seq, rows_per_batch, valid_len, cache_len);
+  if (threadIdx.x == 0)
+    finish_launch<I64>(eb, idx, width, q_seq, rows_per_batch, valid_len, cache_len, gridDim.x);
 }
 
 sa_status launch_validate(sparse_attn_ctx* c, const void* idx, int64_t batch, int64_t heads,

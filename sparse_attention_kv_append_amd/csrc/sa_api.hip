@@ -283,7 +283,7 @@ sa_status sparse_attn_query_plan(const sparse_attn_ctx* c, int64_t batch, int64_
                                  int64_t index_heads, int64_t width, int32_t* path, int32_t* splits) {
   if (!live(c) || !path || !splits) return SA_E_STATE;
   if (sa::mla_supported(c->cfg, index_heads)) {
-    *path = c->cfg.cache_format == SA_CACHE_DENSE ? 2 : 1;
+    *path = sa::latent_supported(c->cfg, index_heads) ? 2 : 1;
     *splits = sa::mla_splits(batch * q_seq, width);
   } else {
     *path = 0;
@@ -311,7 +311,7 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
   if (s != SA_OK) return s;
   // the bf16 shared-latent kernel validates its own columns; other paths
   // run the validation kernel first on the same stream
-  const bool latent_bf16 = sa::mla_supported(k, index_heads) && k.cache_format == SA_CACHE_DENSE;
+  const bool latent_bf16 = sa::latent_supported(k, index_heads);
   if (fused_validate && !latent_bf16) {
     s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
                                      cache_capacity, nullptr, nullptr, nullptr);

@@ -139,6 +139,9 @@ struct FwdArgs {
 };
 
 bool mla_supported(const sa_config& cfg, int64_t index_heads);
+// the LDS-ring kernel: bf16 shared-latent rows, per-batch cache below 2 GiB
+// (its gathers use 32-bit offsets from the batch's cache base)
+bool latent_supported(const sa_config& cfg, int64_t index_heads);
 int mla_splits(int64_t rows, int64_t width);
 sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a);
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
