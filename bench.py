@@ -63,7 +63,8 @@ def parse():
 # sources whose text decides each main kernel's code (the counters summary is
 # only used while their hash is unchanged)
 KERNEL_SOURCES = {
-    "latent_forward_kernel": ["k_forward_latent.hip", "sa_internal.h", "sa_validate_dev.h"],
+    "latent_forward_kernel": ["k_forward_latent.hip", "sa_internal.h", "sa_validate_dev.h", "sa_mfma_dev.h"],
+    "pair_forward_kernel": ["k_forward_pair.hip", "sa_internal.h", "sa_validate_dev.h", "sa_mfma_dev.h"],
     "mla_forward_kernel": ["k_forward_mla.hip", "sa_internal.h"],
     "generic_forward_kernel": ["k_forward_generic.hip", "sa_internal.h"],
 }
@@ -189,7 +190,7 @@ class Setup:
 
 def kernel_name(setup):
     return {0: "generic_forward_kernel", 1: "mla_forward_kernel",
-            2: "latent_forward_kernel"}[setup.path]
+            2: "latent_forward_kernel", 3: "pair_forward_kernel"}[setup.path]
 
 
 def counters_for(setup):

@@ -205,7 +205,9 @@ const char* sparse_attn_last_error(const sparse_attn_ctx* ctx);
 
 /* Report which forward path and split count a call with these sizes takes:
  * *path = 0 generic (VALU), 1 shared-latent MFMA over fp8_e4m3_block64
- * records, 2 shared-latent MFMA over a bf16 cache; *splits >= 1. */
+ * records (register-staged), 2 shared-latent MFMA over a bf16 cache,
+ * 3 shared-latent MFMA over fp8_e4m3_block64 records with 64 RoPE dims
+ * (wave-pair kernel); *splits >= 1. */
 sa_status sparse_attn_query_plan(const sparse_attn_ctx* ctx, int64_t batch, int64_t q_seq,
                                  int64_t index_heads, int64_t width, int32_t* path,
                                  int32_t* splits);

@@ -29,8 +29,7 @@
 //  * with fused validation each workgroup checks its own columns of the index
 //    row (IndexShare host-validator rules) while it stages the keys, and only
 //    the finisher of each row touches the error block, after the attention.
-#include <utility>
-
+#include "sa_mfma_dev.h"
 #include "sa_validate_dev.h"
 
 namespace sa {
@@ -55,101 +54,10 @@ constexpr size_t LDS_BYTES = (size_t)RING_BYTES + KEYCAP * 4 + 64;
 constexpr float TAU_HARD = 100.0f;              // largest exponent taken against the reference
 }  // namespace lat
 
-typedef __bf16 bf16x8_l __attribute__((ext_vector_type(8)));
-typedef float f32x4_l __attribute__((ext_vector_type(4)));
-typedef short s16x4_l __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_l __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_l __attribute__((ext_vector_type(2)));
-typedef float f32x2_l __attribute__((ext_vector_type(2)));
-typedef unsigned u32x2_l __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) u32x4_l lds_u32x4;
-
-constexpr float kLog2eL = 1.4426950408889634f;
-
-// compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// two fp32 -> bf16 (round to nearest even) packed in one word, low = a
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_l){a, b}, bf16x2_l));
-}
-
-// vmcnt-only wait (gfx9 encoding: expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// LDS reads issued as inline asm with an immediate offset. The compiler
-// would wait for every outstanding LDS DMA before its own LDS reads, and
-// drains all reads at each of its waits; these are waited for explicitly.
-template <int OFF>
-__device__ __forceinline__ u32x4_l ds_read_b128_at(uint32_t addr) {
-  u32x4_l r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
-  return r;
-}
-template <int OFF>
-__device__ __forceinline__ s16x4_l ds_read_tr16_at(uint32_t addr) {
-  s16x4_l r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
-  return r;
-}
-
-// Wait until at most N LDS/scalar-memory operations are outstanding and make
-// the two values depend on the wait. LDS operations complete in issue order,
-// so every LDS read issued more than N LDS operations ago has landed.
-template <int N, typename T>
-__device__ __forceinline__ void lgkm_wait_tied(T& a, T& b) {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
-}
-
-template <int N, typename A, typename B>
-__device__ __forceinline__ void lgkm_wait6(A& a0, A& a1, B& b0, B& b1, B& b2, B& b3) {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3) : "n"(N) : "memory");
-}
-
 // LDS reads of step j of the interleaved S / PV loop: the two K reads of
 // k-step j (j < 18) and the four transpose reads of dv tiles 2j, 2j + 1 (j < 16)
 __host__ __device__ constexpr int step_reads(int j) {
   return (j < lat::KSTEPS ? 2 : 0) + (2 * j + 1 < lat::DVT ? 4 : 0);
-}
-
-// Reductions over the lanes l, l ^ 16 and l ^ 32 with the gfx950 permlane
-// swaps (plain VALU ops; a shuffle would be an LDS round trip).
-__device__ __forceinline__ float max_x16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_x32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_x16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_x32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Workgroup barrier for the tile pipeline: this wave's LDS operations have
-// completed, global loads stay in flight. (__syncthreads() also waits for
-// every outstanding global load, which would drain the ring's DMA at every
-// tile; each wave waits for its own share of a tile with wait_vm instead.)
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <bool I64, bool FUSED, bool SOFTCAP>
@@ -402,8 +310,8 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
         for (int kh = 0; kh < 2; kh++) sa[kh][0] = sa[kh][1] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
       };
       // softmax of tile tt from sa; lane holds keys 4g + r and 16 + 4g + r of
-      // its head. Scores stay raw; the log2-domain scale f is folded into one
-      // FMA per key (f > 0, so the max commutes with it). Returns P^T.
+      // its head. Scores are taken to log2 units with one multiply by f.
+      // Returns P^T.
       auto softmax = [&](int tt) {
         const f32x4_l s0 = sa[0][0] + sa[0][1], s1 = sa[1][0] + sa[1][1];
         float x[8];
@@ -422,8 +330,12 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
           for (int i = 0; i < 8; i++)
             if (slot_base + (i < 4 ? i : 12 + i) >= kcount) x[i] = -INFINITY;
         }
+        // scores in log2 units, rounded once: the maximum then gives exp2(0)
+        // exactly (an FMA against a rounded maximum can overflow for huge scores)
+#pragma unroll
+        for (int i = 0; i < 8; i++) x[i] *= f;
         float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        tmax = max_x32(max_x16(tmax)) * f;
+        tmax = max_x32(max_x16(tmax));
         m_seen = fmaxf(m_seen, tmax);
         if (m_ref == -INFINITY) m_ref = tmax;  // first tile of this head: O and l are still 0
         // a score more than 2^TAU_HARD above the reference: this pass is
@@ -432,7 +344,7 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
         const float nm = m_ref == -INFINITY ? 0.0f : -m_ref;
         float p[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], f, nm));
+        for (int i = 0; i < 8; i++) p[i] = __builtin_amdgcn_exp2f(x[i] + nm);
         const float psum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         l_run += sum_x32(sum_x16(psum));
         const u32x4_l pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),

@@ -283,7 +283,7 @@ sa_status sparse_attn_query_plan(const sparse_attn_ctx* c, int64_t batch, int64_
                                  int64_t index_heads, int64_t width, int32_t* path, int32_t* splits) {
   if (!live(c) || !path || !splits) return SA_E_STATE;
   if (sa::mla_supported(c->cfg, index_heads)) {
-    *path = sa::latent_supported(c->cfg, index_heads) ? 2 : 1;
+    *path = sa::latent_supported(c->cfg, index_heads) ? 2 : sa::pair_supported(c->cfg, index_heads) ? 3 : 1;
     *splits = sa::mla_splits(batch * q_seq, width);
   } else {
     *path = 0;
@@ -309,10 +309,11 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
                                         cache_capacity, k.max_cache_len));
   sa_status s = check_index_geometry(c, batch, index_heads, q_seq, width);
   if (s != SA_OK) return s;
-  // the bf16 shared-latent kernel validates its own columns; other paths
+  // the shared-latent MFMA kernels validate their own columns; other paths
   // run the validation kernel first on the same stream
   const bool latent_bf16 = sa::latent_supported(k, index_heads);
-  if (fused_validate && !latent_bf16) {
+  const bool pair_fp8 = sa::pair_supported(k, index_heads);
+  if (fused_validate && !latent_bf16 && !pair_fp8) {
     s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
                                      cache_capacity, nullptr, nullptr, nullptr);
     if (s != SA_OK) return s;
@@ -342,6 +343,9 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
   a.idx64 = k.index_dtype == SA_IDX_I64;
   if (latent_bf16) {
     return sa::launch_forward_latent(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
+  }
+  if (pair_fp8) {
+    return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
   }
   if (sa::mla_supported(k, index_heads)) {
     return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));

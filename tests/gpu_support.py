@@ -99,7 +99,7 @@ def oracle_records(rows_bits, w):
 
 
 def run_device(w, inp, *, mode="inplace", idx64=False, fused=True, fp8_cur="records",
-               indices=None, ctx=None):
+               indices=None, ctx=None, records=None):
     """Append + forward on the device. Returns (y_f32, present_k, present_v,
     error_word). For fp8 workloads the past cache is the oracle's records of
     the generator's bf16 rows and the current rows are given either as
@@ -110,7 +110,9 @@ def run_device(w, inp, *, mode="inplace", idx64=False, fused=True, fp8_cur="reco
         ctx = make_ctx(w, idx64=idx64)
     B, H = w.batch, w.hkv
     fp8 = w.cache_format == W.CACHE_FP8
-    if fp8:
+    if fp8 and records is not None:
+        past_host, cur_host = records  # caller-built records (planted bytes)
+    elif fp8:
         past_host = oracle_records(inp["past_k"], w)
         cur_host = inp["cur_k"] if fp8_cur == "bf16" else oracle_records(inp["cur_k"], w)
     else:
@@ -168,14 +170,18 @@ def check_present(w, dev, pk_ref, pv_ref):
         assert np.array_equal(raw_bytes(got[:, :, T:]), raw_bytes(before[:, :, T:]))
 
 
-def run_oracle(w, inp, indices=None, threads=8):
+def run_oracle(w, inp, indices=None, threads=8, records=None):
     """Oracle append + forward. Returns (y, present_k, present_v) where
-    present_k is records for fp8 workloads."""
+    present_k is records for fp8 workloads (records: caller-built
+    (past, current) records appended as bytes)."""
     pk, pv = oracle_present(inp)
     fmt = w.dtype
     kcache = pk
     if w.cache_format == W.CACHE_FP8:
-        kcache = oracle_records(pk, w)
+        if records is not None:
+            kcache = oracle.kv_append(records[0].copy(), inp["past_len"], records[1])
+        else:
+            kcache = oracle_records(pk, w)
         fmt = oracle.FP8_BLOCK64
     idx = inp["indices"] if indices is None else indices
     y = oracle.forward(inp["q"], kcache, pv, idx, q_dtype=w.dtype, cache_fmt=fmt,

@@ -61,7 +61,7 @@ def test_parity(name, mode):
 
 def test_plan_selects_expected_paths():
     for name, want in [("decode_bf16_small", 2), ("prefill_small", 2), ("tiny_f32", 0),
-                       ("dense_gqa_small", 0), ("mqa_generic_bf16", 0), ("decode_fp8_small", 1)]:
+                       ("dense_gqa_small", 0), ("mqa_generic_bf16", 0), ("decode_fp8_small", 3)]:
         w = CASES[name]
         ctx = make_ctx(w)
         path, splits = ctx.query_plan(w.batch, w.q_seq, w.index_heads, w.width)
@@ -244,3 +244,85 @@ def test_graph_capture_replays_match_eager():
     assert word & 0x08 and "duplicate" in msg
     assert torch.isfinite(y.float()).all()
     ctx.destroy()
+
+
+def planted_records(w, inp, seed):
+    """Oracle records of the generator's rows with planted bytes: blocks whose
+    scale byte is outside the range the fast hardware decode covers (3..9 with
+    their codes; 247..250 with only +0 / -0 codes, since any other code would
+    overflow the scores), and blocks carrying every finite E4M3FN code
+    (subnormals, zeros, both signs) at the block's own scale."""
+    rng = np.random.default_rng(seed)
+    past = oracle_records_of(inp["past_k"], w)
+    cur = oracle_records_of(inp["cur_k"], w)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    for rec in (past[:, :, :w.past], cur):
+        flat = rec.reshape(-1, rec.shape[-1])
+        for r in range(flat.shape[0]):
+            for j in range(8):
+                kind = rng.integers(0, 4)
+                blk = flat[r, 65 * j: 65 * j + 65]
+                if kind == 0:      # every finite code, shuffled
+                    blk[1:] = rng.permutation(finite)[:64]
+                elif kind == 1:    # tiny scale: values near the bottom of fp32 normals
+                    blk[0] = rng.integers(3, 10)
+                elif kind == 2:    # huge scale, signed zeros only
+                    blk[0] = rng.integers(247, 251)
+                    blk[1:] = rng.integers(0, 2, size=64).astype(np.uint8) << 7
+    return past, cur
+
+
+def oracle_records_of(bits, w):
+    from gpu_support import oracle_records
+    return oracle_records(bits, w)
+
+
+@pytest.mark.parametrize("single", [False, True])
+def test_fp8_planted_scales_and_codes(single):
+    """fp8 records with planted scale bytes and codes through the wave-pair
+    kernel: every block decodes like the oracle's record decoder."""
+    w = scaled("decode_fp8", batch=2, past=200, topk=96, width=100)
+    banner(f"fp8 planted records single={single}")
+    inp = W.make_numpy(w)
+    recs = planted_records(w, inp, 5)
+    idx = None
+    if single:
+        idx = np.full_like(inp["indices"], -1)
+        idx[..., 0] = np.random.default_rng(6).integers(0, w.total, size=idx.shape[:3])
+    dev = run_device(w, inp, records=recs, indices=idx)
+    assert dev["word"] == 0, dev["msg"]
+    y_ref, rec_ref, _ = run_oracle(w, inp, records=recs, indices=idx)
+    check_present(w, dev, rec_ref, None)
+    check_close(dev["y"], y_ref, w.dtype, "planted fp8 records")
+    if single:
+        # p = 1 exactly: Y is the decoded V row; bf16-normal values are exact
+        big = np.abs(y_ref) >= 2.0 ** -126
+        assert np.array_equal(dev["y"][big], y_ref[big])
+
+
+@pytest.mark.parametrize("name", ["decode_bf16_small", "prefill_small"])
+def test_huge_late_scores_restart_and_match(name):
+    """A key whose score is about 2^100 above the first tile's maximum sits in a
+    later tile: the shared-latent kernel redoes its key range with the larger
+    reference and still matches the oracle (no overflow to inf / NaN)."""
+    w = CASES[name]
+    inp = W.make_numpy(w)
+    k = inp["past_k"].copy()
+    f32 = (k.astype(np.uint32) << 16).view(np.float32)
+    idx = inp["indices"]
+    b, qi = 0, w.q_seq - 1
+    row = idx[b, 0, qi]
+    key = int(row[row >= 0][-1])  # the row's last selected key: a late tile
+    if key < w.past:
+        f32[b, 0, key, :64] = np.float32(3.0e4)
+        inp["past_k"] = (f32.view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        c = (inp["cur_k"].astype(np.uint32) << 16).view(np.float32).copy()
+        c[b, 0, key - w.past, :64] = np.float32(3.0e4)
+        inp["cur_k"] = (c.view(np.uint32) >> 16).astype(np.uint16)
+    dev = run_device(w, inp)
+    assert dev["word"] == 0, dev["msg"]
+    y_ref, _, _ = run_oracle(w, inp)
+    assert np.isfinite(y_ref).all()
+    check_close(dev["y"], y_ref, w.dtype, f"huge late score {name}")
+
