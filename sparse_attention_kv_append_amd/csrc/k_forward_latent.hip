@@ -185,13 +185,6 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
           v[k] = c < st1 ? load_index<I64>(idx, ibase + c) : -1;
           u[k] = (check && c < st1 && c > 0) ? load_index<I64>(idx, ibase + c - 1) : 0;
         }
-        if (!q_loaded) {
-          // Q^T of this wave's 16 heads, in flight with the index loads; lane
-          // (c16, g) holds dims 32 s + 8g .. +8 of its head
-          const uint16_t* qp = q + ((b * NH + head) * q_seq + qi) * DK + 8 * g;
-#pragma unroll
-          for (int s = 0; s < KSTEPS; s++) qraw[s] = __builtin_bit_cast(u32x4_l, *(const uint4*)(qp + s * 32));
-        }
 #pragma unroll
         for (int k = 0; k < PER; k++) {
           const int s = tid + THREADS * k;
@@ -243,6 +236,14 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
         lds_u8* dst = ring + (tt % NSTAGE) * TILE_BYTES + (WAVE_LOADS * wave + i) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (__attribute__((address_space(3))) void*)dst, 16, goff[i], 0, 0, 0);
       };
+      if (!q_loaded) {
+        // Q^T of this wave's 16 heads, in flight with the first gathers (and
+        // older than them, so the gathers' counted waits cover it); lane
+        // (c16, g) holds dims 32 s + 8g .. +8 of its head
+        const uint16_t* qp = q + ((b * NH + head) * q_seq + qi) * DK + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; s++) qraw[s] = __builtin_bit_cast(u32x4_l, *(const uint4*)(qp + s * 32));
+      }
       // prologue: tiles 0 .. NSTAGE-2 in flight
 #pragma unroll
       for (int p = 0; p < NSTAGE - 1; p++) {

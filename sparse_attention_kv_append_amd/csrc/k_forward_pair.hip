@@ -206,7 +206,6 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       }
       __syncthreads();
       int last = 0;
-      u32x4_l qraw[KSTEPS];
       {
         constexpr int PER = KEYCAP / THREADS;
         const bool check = FUSED && !validated;
@@ -216,13 +215,6 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
           const int c = st0 + tid + THREADS * k;
           v[k] = c < st1 ? load_index<I64>(idx, ibase + c) : -1;
           u[k] = (check && c < st1 && c > 0) ? load_index<I64>(idx, ibase + c - 1) : 0;
-        }
-        if (!q_loaded) {
-          // Q^T of head block 0, in flight with the index loads; lane (c16, g)
-          // holds dims 32 s + 8g .. +8 of head head0
-          const uint16_t* qp = q + ((b * NH + head0) * q_seq + qi) * DK + 8 * g;
-#pragma unroll
-          for (int s = 0; s < KSTEPS; s++) qraw[s] = __builtin_bit_cast(u32x4_l, *(const uint4*)(qp + s * 32));
         }
 #pragma unroll
         for (int k = 0; k < PER; k++) {
@@ -242,26 +234,6 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       const int kcount = misc[0];
       const int ntile = (kcount + KT - 1) / KT;
 
-      if (!q_loaded) {
-        // the MFMA B operands read Q from AGPRs (all of block 0, most of
-        // block 1): the vector registers stay free for the pipeline
-#pragma unroll
-        for (int s = 0; s < KSTEPS; s++) {
-          u32x4_l r = qraw[s];
-          asm volatile("" : "+a"(r));
-          qa[s] = __builtin_bit_cast(bf16x8_l, r);
-        }
-        const uint16_t* qp = q + ((b * NH + head0 + 16) * q_seq + qi) * DK + 8 * g;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; s++) qraw[s] = __builtin_bit_cast(u32x4_l, *(const uint4*)(qp + s * 32));
-#pragma unroll
-        for (int s = 0; s < KSTEPS; s++) {
-          u32x4_l r = qraw[s];
-          if (s < QB_AGPR) asm volatile("" : "+a"(r));
-          qb[s] = __builtin_bit_cast(bf16x8_l, r);
-        }
-        q_loaded = true;
-      }
       if (ntile == 0) continue;  // uniform: no key in this stage
 
       auto tile_addr = [&](int tt) { return (uint32_t)(uintptr_t)(ring + (tt % NSTAGE) * TILE_BYTES); };
@@ -321,6 +293,32 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       issue(ra, rec_base(0));
       issue(rb, rec_base(1));
       uint32_t base_next = rec_base(2);
+      if (!q_loaded) {
+        // Q^T of the pair's heads, loaded while the first records are in
+        // flight; lane (c16, g) holds dims 32 s + 8g .. +8 of heads head0 and
+        // head0 + 16. The MFMA B operands read Q from AGPRs (all of block 0,
+        // most of block 1): the vector registers stay free for the pipeline
+        u32x4_l qraw[KSTEPS];
+        const uint16_t* qp0 = q + ((b * NH + head0) * q_seq + qi) * DK + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; s++) qraw[s] = __builtin_bit_cast(u32x4_l, *(const uint4*)(qp0 + s * 32));
+#pragma unroll
+        for (int s = 0; s < KSTEPS; s++) {
+          u32x4_l r = qraw[s];
+          asm volatile("" : "+a"(r));
+          qa[s] = __builtin_bit_cast(bf16x8_l, r);
+        }
+        const uint16_t* qp = q + ((b * NH + head0 + 16) * q_seq + qi) * DK + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; s++) qraw[s] = __builtin_bit_cast(u32x4_l, *(const uint4*)(qp + s * 32));
+#pragma unroll
+        for (int s = 0; s < KSTEPS; s++) {
+          u32x4_l r = qraw[s];
+          if (s < QB_AGPR) asm volatile("" : "+a"(r));
+          qb[s] = __builtin_bit_cast(bf16x8_l, r);
+        }
+        q_loaded = true;
+      }
       wait_vm<LOADS>();
       store(ra, 0);
       issue(ra, base_next);
