@@ -344,9 +344,13 @@ mla_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ c
 }
 
 // Log-sum-exp merge of the split partials (standard Attention page,
-// `attention_combine`): M = max_j m_j, y = sum_j o_j 2^(m_j-M) / sum_j l_j 2^(m_j-M).
-// One 128-thread workgroup per (row, head); thread owns 4 channels. Block b
-// serves row b % rows, so it runs on the XCD whose L2 took that row's partials.
+// `attention_combine`): M = max_j m_j, y = sum_j o_j 2^(m_j-M) / sum_j l_j 2^(m_j-M)
+// (m in log2 units). One 128-thread workgroup per (row, head); thread owns 4
+// channels. Block b serves row b % rows, so it runs on the XCD whose L2 took
+// that row's partials. Every split's (m, l) and partial output in a round of
+// CH splits is loaded before any is used, so the merge costs one memory round
+// trip per CH splits, not one per split.
+template <int CH>
 __global__ void __launch_bounds__(128)
 mla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                    uint16_t* __restrict__ y, int64_t rows, int64_t q_seq, int splits) {
@@ -354,22 +358,43 @@ mla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
   const int64_t row = (int64_t)(blockIdx.x % (unsigned)rows);
   const int head = (int)(blockIdx.x / (unsigned)rows);
   const int64_t b = row / q_seq, qi = row - b * q_seq;
-  float M = -INFINITY;
-  for (int j = 0; j < splits; j++) M = fmaxf(M, part_ml[((row * splits + j) * NH + head) * 2]);
-  float L = 0.0f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int d = threadIdx.x * 4;
-  if (M != -INFINITY) {
-    for (int j = 0; j < splits; j++) {
-      const int64_t pr = (row * splits + j) * NH + head;
-      const float w = exp2f(part_ml[pr * 2] - M);
-      L += part_ml[pr * 2 + 1] * w;
-      const float4 v = *(const float4*)(part_o + pr * DV + d);
-      acc.x += v.x * w;
-      acc.y += v.y * w;
-      acc.z += v.z * w;
-      acc.w += v.w * w;
+  float M = -INFINITY, L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < splits; j0 += CH) {
+    float2 ml[CH];
+    float4 v[CH];
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+      const int64_t pr = (row * splits + j0 + j) * NH + head;
+      if (j0 + j < splits) {
+        ml[j] = *(const float2*)(part_ml + pr * 2);
+        v[j] = *(const float4*)(part_o + pr * DV + d);
+      } else {
+        ml[j] = make_float2(-INFINITY, 0.0f);
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < CH; j++) Mn = fmaxf(Mn, ml[j].x);
+    if (Mn == -INFINITY) continue;  // no key in these splits yet
+    const float r = M == -INFINITY ? 0.0f : exp2f(M - Mn);  // rescale what is merged so far
+    L *= r;
+    acc.x *= r;
+    acc.y *= r;
+    acc.z *= r;
+    acc.w *= r;
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+      const float w = ml[j].x == -INFINITY ? 0.0f : exp2f(ml[j].x - Mn);
+      L += ml[j].y * w;
+      acc.x += v[j].x * w;
+      acc.y += v[j].y * w;
+      acc.z += v[j].z * w;
+      acc.w += v[j].w * w;
+    }
+    M = Mn;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   uint16_t* yp = y + ((b * NH + head) * q_seq + qi) * DV + d;
@@ -379,7 +404,7 @@ mla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
 }
 
 sa_status launch_mla_combine(sparse_attn_ctx* c, int64_t rows, int64_t q_seq, int splits, uint16_t* y) {
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(rows * mla::NH)), dim3(mla::DV / 4), 0,
+  hipLaunchKernelGGL(mla_combine_kernel<8>, dim3((unsigned)(rows * mla::NH)), dim3(mla::DV / 4), 0,
                      c->stream, c->partial_o, c->partial_ml, y, rows, q_seq, splits);
   return check_hip(c, hipGetLastError(), "forward (combine)");
 }
