@@ -52,6 +52,7 @@ constexpr int KEYCAP = 2048;                    // keys staged in LDS at a time
 constexpr int RING_BYTES = NSTAGE * TILE_BYTES;
 constexpr size_t LDS_BYTES = (size_t)RING_BYTES + KEYCAP * 4 + 64;
 constexpr float TAU_HARD = 100.0f;              // largest exponent taken against the reference
+static_assert(NSTAGE >= 3, "the steady state keeps tiles t, t+1 and the refill in the ring");
 }  // namespace lat
 
 // LDS reads of step j of the interleaved S / PV loop: the two K reads of
@@ -73,7 +74,7 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lds_u8* ring = (lds_u8*)lds_raw;
   int* keys_s = (int*)(lds_raw + RING_BYTES);
-  int* misc = keys_s + KEYCAP;  // [0] key count, [1] restart request
+  int* misc = keys_s + KEYCAP;  // [1] restart request, [8 + w] wave w's key count
   unsigned long long* minkey_s = (unsigned long long*)(misc + 4);
 
   const int tid = threadIdx.x;
@@ -155,7 +156,43 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
   f32x4_l o[DVT];
   float m_ref, l_run;
   unsigned long long mk = ~0ull;  // first violating column of this workgroup's columns
-  bool validated = false;
+  int vhi = c0;                   // columns below vhi have been validated
+
+  // Stage columns [st0, st1) of the index row: the keys (clamped into the
+  // cache) go to keys_s, each wave's count of keys up to the row's last
+  // non-padding entry to misc[8 + wave], and columns not validated before
+  // are checked. Called with no reader of keys_s / misc left.
+  auto stage_keys = [&](int st0, int st1) {
+    constexpr int PER = KEYCAP / THREADS;  // every load in flight at once
+    const bool check = FUSED && st0 >= vhi;
+    int64_t v[PER], u[PER];
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int c = st0 + tid + THREADS * k;
+      v[k] = c < st1 ? load_index<I64>(idx, ibase + c) : -1;
+      u[k] = (check && c < st1 && c > 0) ? load_index<I64>(idx, ibase + c - 1) : 0;
+    }
+    int last = 0;
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int s = tid + THREADS * k;
+      const int c = st0 + s;
+      if (c < st1) {
+        keys_s[s] = (int)((v[k] >= 0 && v[k] < bound) ? v[k] : 0);  // clamp: a bad row stays in bounds
+        if (v[k] != -1) last = s + 1;
+        if (check && column_class(c, v[k], u[k], bound))
+          mk = min(mk, (unsigned long long)(row * (width + 1) + c));
+      }
+    }
+    if (check) vhi = st1;
+    last = wave_max_nonneg(last);
+    if (lane == 0) misc[8 + wave] = last;
+    if (tid == 0) misc[1] = 0;
+  };
+  // the first stage's index loads go out before anything waits on memory
+  bool staged = c0 < c1;
+  if (staged) stage_keys(c0, min(c0 + KEYCAP, c1));
+
   for (;;) {
 #pragma unroll
     for (int t = 0; t < DVT; t++) o[t] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
@@ -166,42 +203,16 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
 
     for (int st0 = c0; st0 < c1 && !restart; st0 += KEYCAP) {
       const int st1 = min(st0 + KEYCAP, c1);
-      __syncthreads();  // the previous stage's readers are done with keys_s / the ring
-      if (tid == 0) {
-        misc[0] = 0;
-        misc[1] = 0;
+      if (!staged) {
+        __syncthreads();  // the previous stage's readers are done with keys_s / misc / the ring
+        stage_keys(st0, st1);
       }
+      staged = false;
       __syncthreads();
-      int last = 0;
-      u32x4_l qraw[KSTEPS];
-      {
-        // KEYCAP / THREADS columns per thread, every load in flight at once
-        constexpr int PER = KEYCAP / THREADS;
-        const bool check = FUSED && !validated;
-        int64_t v[PER], u[PER];
-#pragma unroll
-        for (int k = 0; k < PER; k++) {
-          const int c = st0 + tid + THREADS * k;
-          v[k] = c < st1 ? load_index<I64>(idx, ibase + c) : -1;
-          u[k] = (check && c < st1 && c > 0) ? load_index<I64>(idx, ibase + c - 1) : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < PER; k++) {
-          const int s = tid + THREADS * k;
-          const int c = st0 + s;
-          if (c < st1) {
-            keys_s[s] = (int)((v[k] >= 0 && v[k] < bound) ? v[k] : 0);  // clamp: a bad row stays in bounds
-            if (v[k] != -1) last = s + 1;
-            if (check && column_class(c, v[k], u[k], bound))
-              mk = min(mk, (unsigned long long)(row * (width + 1) + c));
-          }
-        }
-      }
-      validated = true;
-      if (last) atomicMax(&misc[0], last);
-      __syncthreads();
-      const int kcount = misc[0];
+      const int kcount = max(max(misc[8], misc[9]), max(misc[10], misc[11]));
       const int ntile = (kcount + KT - 1) / KT;
+      if (ntile == 0) continue;  // uniform: only padding in these columns
+      u32x4_l qraw[KSTEPS];
 
       // The gather of tile tt: this wave's nine 1 KB loads, buffer loads
       // from the batch's cache rows at byte offsets goff[i]. A slot past the
@@ -377,7 +388,7 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
       // k-step and two dv tiles per step (4 MFMAs and 4 KB of LDS reads per
       // wave), the reads PL steps ahead; then the softmax of tile t+1
       for (int t = 0; t + 1 < ntile; t++) {
-        wait_vm<WAVE_LOADS>();  // tile t+1 has landed for this wave (t+2 may stay in flight)
+        wait_vm<(NSTAGE - 3) * WAVE_LOADS>();  // tile t+1 has landed for this wave (later ones may stay in flight)
         lds_barrier();          // and for everyone; tile t-1's slot is free
         const int tn = t + NSTAGE - 1;  // refills tile t-1's slot; offsets read last iteration
         gather_keys(tn + 1);  // in order ahead of the step reads; consumed after the softmax

@@ -100,7 +100,7 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   lds_u8* ring = (lds_u8*)lds_raw;
   lds_u8* px = ring + RING_BYTES;
   int* keys_s = (int*)(lds_raw + RING_BYTES + PX_BYTES);
-  int* misc = keys_s + KEYCAP;  // [0] key count, [1] restart request
+  int* misc = keys_s + KEYCAP;  // [1] restart request, [8 + w] wave w's key count
   unsigned long long* minkey_s = (unsigned long long*)(misc + 4);
 
   const int tid = threadIdx.x;
@@ -186,7 +186,43 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   f32x4_l o0[DVT], o1[DVT];
   float m_ref0, m_ref1, l0, l1;
   unsigned long long mk = ~0ull;
-  bool validated = false;
+  int vhi = c0;  // columns below vhi have been validated
+
+  // Stage columns [st0, st1) of the index row: the keys (clamped into the
+  // cache) go to keys_s, each wave's count of keys up to the row's last
+  // non-padding entry to misc[8 + wave], and columns not validated before
+  // are checked. Called with no reader of keys_s / misc left.
+  auto stage_keys = [&](int st0, int st1) {
+    constexpr int PER = KEYCAP / THREADS;  // every load in flight at once
+    const bool check = FUSED && st0 >= vhi;
+    int64_t v[PER], u[PER];
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int c = st0 + tid + THREADS * k;
+      v[k] = c < st1 ? load_index<I64>(idx, ibase + c) : -1;
+      u[k] = (check && c < st1 && c > 0) ? load_index<I64>(idx, ibase + c - 1) : 0;
+    }
+    int last = 0;
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int s = tid + THREADS * k;
+      const int c = st0 + s;
+      if (c < st1) {
+        keys_s[s] = (int)((v[k] >= 0 && v[k] < bound) ? v[k] : 0);  // clamp: a bad row stays in bounds
+        if (v[k] != -1) last = s + 1;
+        if (check && column_class(c, v[k], u[k], bound))
+          mk = min(mk, (unsigned long long)(row * (width + 1) + c));
+      }
+    }
+    if (check) vhi = st1;
+    last = wave_max_nonneg(last);
+    if (lane == 0) misc[8 + wave] = last;
+    if (tid == 0) misc[1] = 0;
+  };
+  // the first stage's index loads go out before anything waits on memory
+  bool staged = c0 < c1;
+  if (staged) stage_keys(c0, min(c0 + KEYCAP, c1));
+
   for (;;) {
 #pragma unroll
     for (int t = 0; t < DVT; t++) o0[t] = o1[t] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
@@ -199,39 +235,13 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     for (int st0 = c0; st0 < c1 && !restart; st0 += KEYCAP) {
       const int st1 = min(st0 + KEYCAP, c1);
       const bool need_ref = first_pass && st0 == c0;  // uniform
-      __syncthreads();
-      if (tid == 0) {
-        misc[0] = 0;
-        misc[1] = 0;
+      if (!staged) {
+        __syncthreads();  // the previous stage's readers are done with keys_s / misc / the ring
+        stage_keys(st0, st1);
       }
+      staged = false;
       __syncthreads();
-      int last = 0;
-      {
-        constexpr int PER = KEYCAP / THREADS;
-        const bool check = FUSED && !validated;
-        int64_t v[PER], u[PER];
-#pragma unroll
-        for (int k = 0; k < PER; k++) {
-          const int c = st0 + tid + THREADS * k;
-          v[k] = c < st1 ? load_index<I64>(idx, ibase + c) : -1;
-          u[k] = (check && c < st1 && c > 0) ? load_index<I64>(idx, ibase + c - 1) : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < PER; k++) {
-          const int s = tid + THREADS * k;
-          const int c = st0 + s;
-          if (c < st1) {
-            keys_s[s] = (int)((v[k] >= 0 && v[k] < bound) ? v[k] : 0);  // clamp: a bad row stays in bounds
-            if (v[k] != -1) last = s + 1;
-            if (check && column_class(c, v[k], u[k], bound))
-              mk = min(mk, (unsigned long long)(row * (width + 1) + c));
-          }
-        }
-      }
-      validated = true;
-      if (last) atomicMax(&misc[0], last);
-      __syncthreads();
-      const int kcount = misc[0];
+      const int kcount = max(max(misc[8], misc[9]), max(misc[10], misc[11]));
       const int ntile = (kcount + KT - 1) / KT;
 
       if (ntile == 0) continue;  // uniform: no key in this stage

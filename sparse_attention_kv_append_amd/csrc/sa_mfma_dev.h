@@ -112,6 +112,13 @@ __device__ __forceinline__ float sum_x32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Maximum of a non-negative int over the 64 lanes of the wave (uniform result).
+__device__ __forceinline__ int wave_max_nonneg(int x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = max(x, __shfl_xor(x, m));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
 // Workgroup barrier for the tile pipelines: this wave's LDS operations have
 // completed, global loads stay in flight. (__syncthreads() also waits for
 // every outstanding global load, which would drain the gathers in flight.)

@@ -1,0 +1,113 @@
+"""Forward launches with fused validation over index rows holding planted
+violations: the error word, the first failing (row, column) and the message
+equal the oracle validator's verdict, on every forward path. The generic path
+runs the standalone validation kernel before its forward; the shared-latent
+paths validate inside the attention kernels, each workgroup its own columns.
+
+Y of such a launch is not compared (the caller discards it): the launch only
+has to stay in bounds and finish. Rows wider than one 2048-key stage of a
+workgroup and rows holding only padding are included, since both change how
+a workgroup walks its columns."""
+import numpy as np
+import pytest
+
+import oracle
+import sa_workloads as W
+from gpu_support import make_ctx, tt
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(msg):
+    print(f"\n[gpu] {msg}", flush=True)
+
+
+def plant_violations(idx, bound, seed, min_col=0):
+    """Copy of the valid rows `idx` [B, 1, Sq, W] with one planted violation
+    in most rows. Columns near each row's end are favoured. With min_col > 0
+    every violation lies at column min_col or later (rows that short stay
+    valid), so a workgroup that skipped its later columns would report none."""
+    rng = np.random.default_rng(seed)
+    out = idx.astype(np.int64).copy()
+    B, Hi, Sq, Wd = out.shape
+    rows = out.reshape(-1, Wd)
+    for r in range(rows.shape[0]):
+        T = int(bound[r // (Hi * Sq)])
+        n = int((rows[r] >= 0).sum())
+        kind = int(rng.integers(0, 8 if min_col == 0 else 6))
+        lo = max(0, n - 80) if rng.random() < 0.7 else 0
+        lo = max(lo, min_col)
+        if lo >= n:
+            continue
+        c = int(rng.integers(lo, n))
+        if kind == 1:
+            rows[r, c] = -int(rng.integers(2, 9))                  # sentinel
+        elif kind == 2 and n < Wd:
+            rows[r, int(rng.integers(max(n, min_col), Wd))] = int(rng.integers(0, T))  # after padding
+        elif kind == 3:
+            rows[r, c] = T + int(rng.integers(0, 5))                # range
+        elif kind == 4 and c >= 1:
+            rows[r, c] = rows[r, c - 1]                              # duplicate
+        elif kind == 5 and c >= 1:
+            rows[r, c - 1], rows[r, c] = rows[r, c], rows[r, c - 1]  # order
+        elif kind == 6:
+            rows[r, :] = -1                                          # all padding
+    return out
+
+
+CASES = {
+    # name: (workload, expected plan path, planting seed, first column planted)
+    "latent_split": (W.WORKLOADS["decode_bf16"].scaled(batch=12, past=1500, topk=700, width=710), 2, 11, 0),
+    "latent_wide_rows": (W.WORKLOADS["prefill_bf16"].scaled(q_seq=260, cur=260, past=2000, width=2100,
+                                                            topk=2100), 2, 12, 0),
+    "latent_wide_rows_late": (W.WORKLOADS["prefill_bf16"].scaled(q_seq=260, cur=260, past=2000, width=2100,
+                                                                 topk=2100), 2, 16, 2048),
+    "pair_split": (W.WORKLOADS["decode_fp8"].scaled(batch=12, past=1200, topk=650, width=650), 3, 13, 0),
+    "pair_wide_rows_late": (W.WORKLOADS["decode_fp8"].scaled(batch=1, q_seq=260, cur=260, past=2000,
+                                                             width=2100, topk=2100, pattern="causal_prefill"),
+                            3, 14, 2048),
+    "generic": (W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=12, past=500, cur=12,
+                                                width=520, topk=520), 0, 15, 0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("i64", [False, True])
+def test_fused_verdict_matches_oracle(name, i64):
+    import torch
+    w, path, seed, min_col = CASES[name]
+    banner(f"fused verdict {name} i64={i64}")
+    B, Sq, Wd = w.batch, w.q_seq, w.width
+    bound = np.full(B, w.total, np.int32)
+    rng = np.random.default_rng(seed)
+    idx = plant_violations(W.index_rows(w, rng), bound, seed + 100 * i64, min_col)
+    if not i64:
+        idx = idx.astype(np.int32)
+    word, _, first, msg = oracle.validate_indices(idx, bound)
+    assert word != 0  # the planting produced violations
+
+    ctx = make_ctx(w, idx64=i64)
+    assert ctx.query_plan(B, Sq, 1, Wd)[0] == path
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    if w.cache_format == W.CACHE_FP8:
+        # any bytes make valid-shaped records: NaN scale / code bytes are
+        # avoided so the launch computes finite values (Y is not compared)
+        cache = torch.randint(0, 120, (B, 1, w.cap, w.dk + 72), dtype=torch.uint8, device="cuda",
+                              generator=gen)
+        vcache = None
+    else:
+        dt = torch.bfloat16 if w.dtype == W.DT_BF16 else torch.float32
+        cache = torch.randn((B, w.hkv, w.cap, w.dk), device="cuda", generator=gen).to(dt)
+        vcache = None if w.layout == W.LAYOUT_SHARED_LATENT else \
+            torch.randn((B, w.hkv, w.cap, w.dv), device="cuda", generator=gen).to(dt)
+    q = torch.randn((B, w.hq, Sq, w.dk), device="cuda", generator=gen).to(torch.bfloat16)
+    y = torch.empty((B, w.hq, Sq, w.dv), dtype=torch.bfloat16, device="cuda")
+    vlen = tt(bound)
+    for rep in range(2):  # the per-row slots re-arm: a second launch gives the same verdict
+        ctx.reset_error_async()
+        ctx.forward(q, B, Sq, cache, vcache, w.cap, vlen, tt(idx), 1, Wd, y, fused_validate=True)
+        dword, dfirst, dmsg = ctx.read_error()
+        assert dword == word, f"launch {rep}: word {dword:#x} != {word:#x}"
+        assert dfirst == first[0] * (Wd + 1) + first[1], f"launch {rep}"
+        assert dmsg == msg
+    ctx.destroy()
