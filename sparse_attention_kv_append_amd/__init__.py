@@ -74,6 +74,10 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
         raise RuntimeError(
             f"{p} is missing: build the HIP library first (python -m "
             "sparse_attention_kv_append_amd.build or __graft_entry__.build())")
+    # torch ships its own HIP runtime (soname libamdhip64.so.7) and loads it by
+    # a name that does not match an already loaded system copy; loaded first,
+    # it is the one this library binds to, so the process keeps one runtime
+    import torch  # noqa: F401
     lib = ctypes.CDLL(str(p))
     V, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     st = ctypes.c_int

@@ -279,16 +279,23 @@ sa_status sparse_attn_validate_indices(sparse_attn_ctx* c, const void* indices, 
                              error_word, row_class, first_bad);
 }
 
+namespace sa {
+// The kernel that runs a forward launch: 0 = generic, 1 = register-staged
+// shared-latent fallback, 2 = shared-latent LDS-ring kernel over bf16 rows,
+// 3 = wave-pair kernel over fp8 records.
+static int forward_path(const sa_config& k, int64_t index_heads) {
+  if (!mla_supported(k, index_heads)) return 0;
+  if (latent_supported(k, index_heads)) return 2;
+  if (pair_supported(k, index_heads)) return 3;
+  return 1;
+}
+}  // namespace sa
+
 sa_status sparse_attn_query_plan(const sparse_attn_ctx* c, int64_t batch, int64_t q_seq,
                                  int64_t index_heads, int64_t width, int32_t* path, int32_t* splits) {
   if (!live(c) || !path || !splits) return SA_E_STATE;
-  if (sa::mla_supported(c->cfg, index_heads)) {
-    *path = sa::latent_supported(c->cfg, index_heads) ? 2 : sa::pair_supported(c->cfg, index_heads) ? 3 : 1;
-    *splits = sa::mla_splits(batch * q_seq, width);
-  } else {
-    *path = 0;
-    *splits = 1;
-  }
+  *path = sa::forward_path(c->cfg, index_heads);
+  *splits = *path ? sa::mla_splits(batch * q_seq, width) : 1;
   return SA_OK;
 }
 
@@ -311,9 +318,8 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
   if (s != SA_OK) return s;
   // the shared-latent MFMA kernels validate their own columns; other paths
   // run the validation kernel first on the same stream
-  const bool latent_bf16 = sa::latent_supported(k, index_heads);
-  const bool pair_fp8 = sa::pair_supported(k, index_heads);
-  if (fused_validate && !latent_bf16 && !pair_fp8) {
+  const int path = sa::forward_path(k, index_heads);
+  if (fused_validate && path < 2) {
     s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
                                      cache_capacity, nullptr, nullptr, nullptr);
     if (s != SA_OK) return s;
@@ -341,16 +347,12 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
   a.cache_format = k.cache_format;
   a.kv_layout = k.kv_layout;
   a.idx64 = k.index_dtype == SA_IDX_I64;
-  if (latent_bf16) {
-    return sa::launch_forward_latent(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
+  switch (path) {
+    case 2: return sa::launch_forward_latent(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
+    case 3: return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
+    case 1: return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
+    default: return sa::launch_forward_generic(c, a);
   }
-  if (pair_fp8) {
-    return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
-  }
-  if (sa::mla_supported(k, index_heads)) {
-    return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
-  }
-  return sa::launch_forward_generic(c, a);
 }
 
 sa_status sparse_attn_read_error(sparse_attn_ctx* c, uint32_t* word, uint64_t* first_bad) {

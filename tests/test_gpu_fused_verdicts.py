@@ -22,28 +22,33 @@ def banner(msg):
     print(f"\n[gpu] {msg}", flush=True)
 
 
-def plant_violations(idx, bound, seed, min_col=0):
+def plant_violations(idx, bound, seed, cols=None):
     """Copy of the valid rows `idx` [B, 1, Sq, W] with one planted violation
-    in most rows. Columns near each row's end are favoured. With min_col > 0
-    every violation lies at column min_col or later (rows that short stay
-    valid), so a workgroup that skipped its later columns would report none."""
+    in most rows. Columns near each row's end are favoured. With cols =
+    (lo, hi) every violation lies in columns [lo, hi) (rows with no such
+    column stay valid), so a workgroup that skipped those columns would
+    report none of them."""
     rng = np.random.default_rng(seed)
     out = idx.astype(np.int64).copy()
     B, Hi, Sq, Wd = out.shape
     rows = out.reshape(-1, Wd)
+    lo_c, hi_c = cols if cols is not None else (0, Wd)
     for r in range(rows.shape[0]):
         T = int(bound[r // (Hi * Sq)])
         n = int((rows[r] >= 0).sum())
-        kind = int(rng.integers(0, 8 if min_col == 0 else 6))
+        kind = int(rng.integers(0, 8 if cols is None else 6))
         lo = max(0, n - 80) if rng.random() < 0.7 else 0
-        lo = max(lo, min_col)
-        if lo >= n:
+        lo, hi = max(lo, lo_c), min(n, hi_c)
+        if kind == 2:  # a value after the padding: needs a padding column in range
+            plo, phi = max(n, lo_c), min(Wd, hi_c)
+            if plo < phi:
+                rows[r, int(rng.integers(plo, phi))] = int(rng.integers(0, T))
             continue
-        c = int(rng.integers(lo, n))
+        if lo >= hi:
+            continue
+        c = int(rng.integers(lo, hi))
         if kind == 1:
             rows[r, c] = -int(rng.integers(2, 9))                  # sentinel
-        elif kind == 2 and n < Wd:
-            rows[r, int(rng.integers(max(n, min_col), Wd))] = int(rng.integers(0, T))  # after padding
         elif kind == 3:
             rows[r, c] = T + int(rng.integers(0, 5))                # range
         elif kind == 4 and c >= 1:
@@ -55,19 +60,26 @@ def plant_violations(idx, bound, seed, min_col=0):
     return out
 
 
+PREFILL = W.WORKLOADS["prefill_bf16"]
+FP8 = W.WORKLOADS["decode_fp8"]
+# rows of 4001 + q keys (q < 128) over width 4200 split in two workgroups of
+# 2112 and 2088 columns: each workgroup walks two stages
+LATENT_WIDE = PREFILL.scaled(q_seq=128, cur=128, past=4100, width=4200, topk=4200)
+# one workgroup per row over 2100 columns: two stages
+ONE_WG_WIDE = PREFILL.scaled(q_seq=260, cur=260, past=2000, width=2100, topk=2100)
+
 CASES = {
-    # name: (workload, expected plan path, planting seed, first column planted)
-    "latent_split": (W.WORKLOADS["decode_bf16"].scaled(batch=12, past=1500, topk=700, width=710), 2, 11, 0),
-    "latent_wide_rows": (W.WORKLOADS["prefill_bf16"].scaled(q_seq=260, cur=260, past=2000, width=2100,
-                                                            topk=2100), 2, 12, 0),
-    "latent_wide_rows_late": (W.WORKLOADS["prefill_bf16"].scaled(q_seq=260, cur=260, past=2000, width=2100,
-                                                                 topk=2100), 2, 16, 2048),
-    "pair_split": (W.WORKLOADS["decode_fp8"].scaled(batch=12, past=1200, topk=650, width=650), 3, 13, 0),
-    "pair_wide_rows_late": (W.WORKLOADS["decode_fp8"].scaled(batch=1, q_seq=260, cur=260, past=2000,
-                                                             width=2100, topk=2100, pattern="causal_prefill"),
-                            3, 14, 2048),
+    # name: (workload, expected plan path, planting seed, planted column range)
+    "latent_split": (W.WORKLOADS["decode_bf16"].scaled(batch=12, past=1500, topk=700, width=710), 2, 11, None),
+    "latent_wide_first_wg_late": (LATENT_WIDE, 2, 12, (2048, 2112)),
+    "latent_wide_second_wg_late": (LATENT_WIDE, 2, 13, (4160, 4200)),
+    "latent_one_wg_wide": (ONE_WG_WIDE, 2, 14, None),
+    "latent_one_wg_wide_late": (ONE_WG_WIDE, 2, 15, (2048, 2100)),
+    "pair_fp8_split": (FP8.scaled(batch=12, past=1200, topk=650, width=650), 3, 16, None),
+    "pair_fp8_wide_late": (FP8.scaled(batch=1, q_seq=260, cur=260, past=2000, width=2100, topk=2100,
+                                      pattern="causal_prefill"), 3, 17, (2048, 2100)),
     "generic": (W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=12, past=500, cur=12,
-                                                width=520, topk=520), 0, 15, 0),
+                                                width=520, topk=520), 0, 18, None),
 }
 
 
@@ -75,12 +87,12 @@ CASES = {
 @pytest.mark.parametrize("i64", [False, True])
 def test_fused_verdict_matches_oracle(name, i64):
     import torch
-    w, path, seed, min_col = CASES[name]
+    w, path, seed, cols = CASES[name]
     banner(f"fused verdict {name} i64={i64}")
     B, Sq, Wd = w.batch, w.q_seq, w.width
     bound = np.full(B, w.total, np.int32)
     rng = np.random.default_rng(seed)
-    idx = plant_violations(W.index_rows(w, rng), bound, seed + 100 * i64, min_col)
+    idx = plant_violations(W.index_rows(w, rng), bound, seed + 100 * i64, cols)
     if not i64:
         idx = idx.astype(np.int32)
     word, _, first, msg = oracle.validate_indices(idx, bound)
