@@ -165,12 +165,14 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
   auto stage_keys = [&](int st0, int st1) {
     constexpr int PER = KEYCAP / THREADS;  // every load in flight at once
     const bool check = FUSED && st0 >= vhi;
+    // every load is unconditional (addresses clamped into the stage) so all
+    // of them are in flight together; out-of-stage lanes are fixed up after
     int64_t v[PER], u[PER];
 #pragma unroll
     for (int k = 0; k < PER; k++) {
-      const int c = st0 + tid + THREADS * k;
-      v[k] = c < st1 ? load_index<I64>(idx, ibase + c) : -1;
-      u[k] = (check && c < st1 && c > 0) ? load_index<I64>(idx, ibase + c - 1) : 0;
+      const int c = min(st0 + tid + THREADS * k, st1 - 1);
+      v[k] = load_index<I64>(idx, ibase + c);
+      if (check) u[k] = load_index<I64>(idx, ibase + max(c - 1, 0));
     }
     int last = 0;
 #pragma unroll

@@ -59,12 +59,17 @@ validate_kernel(const void* __restrict__ idx, int64_t rows, int64_t q_seq, int64
     // 8 chunks of 64 columns per round trip: their loads are all in flight
     // before the first chunk is checked
     for (int64_t c0 = 0; c0 < width && cls == 0; c0 += 8 * 64) {
+      // unconditional loads (addresses clamped into the row) so all eight are
+      // issued before the first wait; columns past the row are fixed up after
       int64_t vals[8];
 #pragma unroll
       for (int k = 0; k < 8; k++) {
         const int64_t c = c0 + 64 * k + lane;
-        vals[k] = c < width ? load_index<I64>(idx, base + c) : -1;
+        vals[k] = load_index<I64>(idx, base + (c < width ? c : width - 1));
       }
+#pragma unroll
+      for (int k = 0; k < 8; k++)
+        if (c0 + 64 * k + lane >= width) vals[k] = -1;
 #pragma unroll
       for (int k = 0; k < 8; k++) {
         const int64_t c = c0 + 64 * k + lane;
