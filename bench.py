@@ -67,6 +67,7 @@ KERNEL_SOURCES = {
     "pair_forward_kernel": ["k_forward_pair.hip", "sa_internal.h", "sa_validate_dev.h", "sa_mfma_dev.h"],
     "mla_forward_kernel": ["k_forward_mla.hip", "sa_internal.h"],
     "generic_forward_kernel": ["k_forward_generic.hip", "sa_internal.h"],
+    "gqa_forward_kernel": ["k_forward_gqa.hip", "sa_internal.h", "sa_mfma_dev.h"],
 }
 CALIB_BYTES = 256 << 20
 
@@ -171,7 +172,8 @@ class Setup:
             gather = sel * row_bytes
             heads_per_key = w.hq
         else:
-            # generic path: each (row, kv head) gathers K and V rows of 2*D bytes
+            # separate K/V: each (row, kv head) selects K and V rows of 2*D bytes
+            # (the grouped-query kernel gathers a shared tile once for all its rows)
             gather = sel * w.hkv * (w.dk + w.dv) * 2
             heads_per_key = w.hq
         qbytes = w.batch * w.hq * w.q_seq * w.dk * 2
@@ -190,7 +192,7 @@ class Setup:
 
 def kernel_name(setup):
     return {0: "generic_forward_kernel", 1: "mla_forward_kernel",
-            2: "latent_forward_kernel", 3: "pair_forward_kernel"}[setup.path]
+            2: "latent_forward_kernel", 3: "pair_forward_kernel", 4: "gqa_forward_kernel"}[setup.path]
 
 
 def counters_for(setup):
@@ -476,7 +478,7 @@ def main():
 
     tokens = s.tokens_per_step()
     kw = s.kernel_work()
-    if w.pattern == "causal_prefill":
+    if w.pattern == "causal_prefill" or s.path == 4:
         bound, peak, unit = "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
         achieved = kw["flops"] / k_avg_s / 1e12
     elif w.layout == s.W.LAYOUT_SEPARATE:

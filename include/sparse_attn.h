@@ -207,7 +207,8 @@ const char* sparse_attn_last_error(const sparse_attn_ctx* ctx);
  * *path = 0 generic (VALU), 1 shared-latent MFMA over fp8_e4m3_block64
  * records (register-staged), 2 shared-latent MFMA over a bf16 cache,
  * 3 shared-latent MFMA over fp8_e4m3_block64 records with 64 RoPE dims
- * (wave-pair kernel); *splits >= 1. */
+ * (wave-pair kernel), 4 grouped-query MFMA (bf16 separate K/V caches of
+ * 128 dims, one index list per (batch, query)); *splits >= 1. */
 sa_status sparse_attn_query_plan(const sparse_attn_ctx* ctx, int64_t batch, int64_t q_seq,
                                  int64_t index_heads, int64_t width, int32_t* path,
                                  int32_t* splits);

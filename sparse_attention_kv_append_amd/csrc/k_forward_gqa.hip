@@ -1,0 +1,552 @@
+// Grouped-query selected-token attention on the gfx950 matrix cores, with the
+// gathered key tile shared by several query rows.
+//
+// Semantics are IndexShare's `index_share_row` for separate K and V caches,
+// bf16 rows of 128 dims, and one index list per (batch, query) shared by all
+// query heads (the standard Attention page's softcap applies when set). In a
+// grouped-query layout the `group` heads of one kv head read the same K and V
+// rows, so a workgroup takes one (batch, kv head) and R = min(32, 128 / group)
+// consecutive queries: up to 128 (query, head) rows, 32 per wave as two
+// blocks of 16. Walking the index rows 32 columns at a time, a tile is
+// shared when every one of the R rows holds, in each column, either the same
+// key or padding (-1): then the tile's 32 K and V rows are gathered once and
+// S^T = K_tile . Q^T and O^T += V_tile^T . P^T run for all the rows on
+// v_mfma_f32_16x16x32_bf16 (each K or V read from LDS feeds both row blocks
+// of a wave). Dense causal selections - the degenerate case where every
+// query selects a prefix of the keys - share every tile. A tile that is not
+// shared is redone row by row (R small passes, each gathering that row's own
+// keys and updating only its rows), so any valid index rows give IndexShare's
+// result, only more slowly.
+//
+// Per row the softmax is the usual online form (running maximum and sum in
+// log2 units, the accumulators rescaled when the maximum grows). A row's
+// key count n is its number of entries before the first -1; a workgroup stops
+// at the first tile in which every one of its rows is padding.
+//
+// Data movement per 32-column tile: the R index rows' 32 columns are copied
+// into LDS six tiles ahead (direct-to-LDS, one dword per lane); four tiles
+// ahead every thread folds its share of them into per-column partial maxima
+// and minima (and the first -1 of each row); three tiles ahead each wave
+// combines the partials into the tile's keys and flags and issues the tile's
+// K and V gathers (direct-to-LDS, 16 bytes per lane) into a four-tile ring.
+// LDS rows of 256 bytes are stored with 16-byte chunk c of row R at chunk
+// c ^ (R & 15) for K (the K reads of 16 rows x one chunk hit 16 distinct
+// bank groups per pass) and c ^ 2 (R & 7) for V (the transposing V reads of
+// 8 rows x 32 bytes hit 64 distinct banks).
+#include "sa_mfma_dev.h"
+
+namespace sa {
+
+namespace gq {
+constexpr int D = 128;                           // head dim of Q, K and V
+constexpr int ROWB = D * 2;                      // 256 bytes per cache row
+constexpr int KT = 32;                           // columns (keys) per tile
+constexpr int THREADS = 256;
+constexpr int WAVES = THREADS / 64;
+constexpr int MROWS = 128;                       // (query, head) rows per workgroup
+constexpr int RMAX = 32;                         // queries per workgroup at most
+constexpr int KSTEPS = D / 32;                   // 4 k-steps of S^T
+constexpr int DVT = D / 16;                      // 8 dv tiles of O^T
+constexpr int NSTAGE = 4;                        // K/V tiles in the ring
+constexpr int KV_TILE = 2 * KT * ROWB;           // K rows then V rows: 16 KB
+constexpr int RING_BYTES = NSTAGE * KV_TILE;
+constexpr int SPARE_OFF = RING_BYTES;            // one more K/V tile for row-by-row passes
+constexpr int GLOADS = KV_TILE / 1024 / WAVES;   // 4 one-KB K/V loads per wave and tile
+constexpr int IDX_SLOTS = 4;                     // index tiles in flight or being folded
+template <bool I64> constexpr int idx_tile_bytes() { return RMAX * KT * (I64 ? 8 : 4); }
+template <bool I64> constexpr int ILOADS = idx_tile_bytes<I64>() / 256 / WAVES;  // dword loads per wave
+constexpr int IDX_OFF = SPARE_OFF + KV_TILE;
+template <bool I64> constexpr int part_off() { return IDX_OFF + IDX_SLOTS * idx_tile_bytes<I64>(); }
+constexpr int PART_BYTES = 2 * 8 * KT * 8;       // per slot: [8 thread groups][32 columns] max, min (int64)
+template <bool I64> constexpr int nrow_off() { return part_off<I64>() + 2 * PART_BYTES; }
+template <bool I64> constexpr int flag_off() { return nrow_off<I64>() + RMAX * 4; }
+template <bool I64> constexpr size_t lds_bytes() { return (size_t)flag_off<I64>() + WAVES * 8 * 4; }
+}  // namespace gq
+
+// LDS reads of step j of the interleaved S / PV loop: the K read of (k-step
+// j >> 1, key half j & 1) and the two transposing V reads of dv tile j
+__host__ __device__ constexpr int gqa_step_reads(int j) { return j < 8 ? 3 : 0; }
+
+template <bool I64, bool SOFTCAP>
+__global__ void __launch_bounds__(gq::THREADS, 1)
+gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                   const void* __restrict__ idx, const int32_t* __restrict__ valid_len, uint16_t* __restrict__ y,
+                   int64_t batch, int64_t hkv, int64_t q_seq, int64_t cap, int64_t width, int group, int nqb,
+                   float scale, float softcap) {
+  using namespace gq;
+  constexpr int ITB = idx_tile_bytes<I64>();
+  constexpr int IL = ILOADS<I64>;
+  constexpr int ISZ = I64 ? 8 : 4;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  lds_u8* lds = (lds_u8*)lds_raw;
+  int64_t* part = (int64_t*)(lds_raw + part_off<I64>());  // [2 slots][max | min][8][32]
+  int* n_s = (int*)(lds_raw + nrow_off<I64>());          // [RMAX] first -1 column of each query row
+  int* flag_s = (int*)(lds_raw + flag_off<I64>());       // [wave][8] tile flags, per wave
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+
+  // ---- workgroup -> (batch, kv head, query block); the query blocks of one
+  // (batch, kv head) share blockIdx % 8 (one XCD, one L2)
+  const int xcd = (int)(blockIdx.x & 7u);
+  const int rest = (int)(blockIdx.x >> 3);
+  const int qb = rest % nqb;
+  const int64_t pr = (int64_t)(rest / nqb) * 8 + xcd;  // (batch, kv head) pair
+  if (pr >= batch * hkv) return;                       // grid padding (uniform)
+  const int64_t b = pr / hkv;
+  const int64_t kvh = pr - b * hkv;
+  const int R = group >= MROWS ? 1 : min(RMAX, MROWS / group);  // queries of this workgroup
+  const int64_t q0 = (int64_t)qb * R;
+  const int rlive = (int)min((int64_t)R, q_seq - q0);  // queries that exist
+  const int hq = (int)(hkv * group);
+  int64_t bound = valid_len ? (int64_t)valid_len[b] : cap;
+  bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
+  const int ntile_w = (int)((width + KT - 1) / KT);
+
+  // this lane's rows: block rb holds row m = 32 wave + 16 rb + c16
+  int row_q[2], row_h[2];
+  bool row_on[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; rb++) {
+    const int m = 32 * wave + 16 * rb + c16;
+    const int r = m / group;
+    row_q[rb] = r;
+    row_h[rb] = (int)(kvh * group) + (m - r * group);
+    row_on[rb] = m < R * group && r < rlive;
+  }
+
+  // ---- buffers: this (batch, kv head)'s K and V rows; the index rows of the
+  // workgroup's queries (reads past the live queries return zeros)
+  const int64_t kv_base = (b * hkv + kvh) * cap * ROWB;
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kc + kv_base), (short)0, (int)(cap * ROWB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vc + kv_base), (short)0, (int)(cap * ROWB), 0x00020000);
+  const uint8_t* ibase = (const uint8_t*)idx + (b * q_seq + q0) * width * ISZ;
+  const __amdgpu_buffer_rsrc_t irsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ibase, (short)0, (int)min((int64_t)0x7fffffff, (int64_t)rlive * width * ISZ), 0x00020000);
+
+  for (int i = tid; i < RMAX; i += THREADS) n_s[i] = 0x7fffffff;
+
+  // ---- index tiles: lane l of load i of wave w copies dword d = 64 (IL w + i) + l
+  // of the tile's [RMAX][32] block (row r = d / (32 ISZ / 4), column j)
+  auto issue_idx = [&](int x) {
+    lds_u8* slot = lds + IDX_OFF + (x % IDX_SLOTS) * ITB;
+#pragma unroll
+    for (int i = 0; i < IL; i++) {
+      const int d = 64 * (IL * wave + i) + lane;
+      const int r = d / (KT * ISZ / 4);
+      const int wj = d - r * (KT * ISZ / 4);  // dword within the row's 32 columns
+      const int64_t col = (int64_t)x * KT + wj / (ISZ / 4);
+      uint32_t off = 0x80000000u;  // past the buffer: zeros
+      if (r < rlive && col < width) off = (uint32_t)(((int64_t)r * width + col) * ISZ + (wj % (ISZ / 4)) * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(irsrc, (__attribute__((address_space(3))) void*)(slot + 256 * (IL * wave + i)),
+                                              4, off, 0, 0, 0);
+    }
+  };
+  auto idx_at = [&](const lds_u8* slot, int r, int j) -> int64_t {
+    if constexpr (I64) return *(const __attribute__((address_space(3))) int64_t*)(slot + (r * KT + j) * 8);
+    else return *(const __attribute__((address_space(3))) int32_t*)(slot + (r * KT + j) * 4);
+  };
+  // fold index tile x: thread (column j = tid & 31, group tg = tid >> 5) over
+  // rows tg, tg + 8, ...: partial max and min (min over non-padding entries)
+  // and the first -1 of each row
+  auto fold = [&](int x) {
+    const lds_u8* slot = lds + IDX_OFF + (x % IDX_SLOTS) * ITB;
+    const int j = tid & 31, tg = tid >> 5;
+    const int64_t col = (int64_t)x * KT + j;
+    int64_t mx = -1, mn = INT64_MAX;
+    for (int r = tg; r < rlive; r += 8) {
+      const int64_t v = col < width ? idx_at(slot, r, j) : -1;
+      mx = max(mx, v);
+      if (v != -1) mn = min(mn, v);
+      else atomicMin(&n_s[r], (int)col);
+    }
+    int64_t* pp = part + (x & 1) * (2 * 8 * KT);
+    pp[tg * KT + j] = mx;
+    pp[8 * KT + tg * KT + j] = mn;
+  };
+
+  // ---- K/V gather of a tile: lane l of load i of wave w fills 16-byte
+  // chunk 64 (4 w + i) + l of the slot: waves 0, 1 the K rows, waves 2, 3 the V rows
+  int ld_row[GLOADS], ld_off[GLOADS];
+#pragma unroll
+  for (int i = 0; i < GLOADS; i++) {
+    const int ci = (64 * (GLOADS * wave + i) + lane) & 511;
+    const int Rr = ci >> 4, pc = ci & 15;
+    ld_row[i] = Rr;
+    ld_off[i] = (wave < 2 ? (pc ^ (Rr & 15)) : (pc ^ (2 * (Rr & 7)))) << 4;
+  }
+  const __amdgpu_buffer_rsrc_t grsrc = wave < 2 ? krsrc : vrsrc;
+  uint32_t goff[GLOADS];
+  auto gather_issue = [&](lds_u8* slot) {
+#pragma unroll
+    for (int i = 0; i < GLOADS; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(grsrc, (__attribute__((address_space(3))) void*)(slot + 1024 * (GLOADS * wave + i)),
+                                              16, goff[i], 0, 0, 0);
+  };
+  // gather offsets from each lane's column key (column lane & 31); keys
+  // outside the cache read zeros
+  auto key_offsets = [&](int64_t kfor_lane) {
+    const int kc32 = kfor_lane >= 0 && kfor_lane < bound ? (int)kfor_lane : -1;
+#pragma unroll
+    for (int i = 0; i < GLOADS; i++) {
+      const int kk = __shfl(kc32, ld_row[i], 64);
+      goff[i] = kk >= 0 ? (uint32_t)kk * ROWB + (uint32_t)ld_off[i] : 0x80000000u;
+    }
+  };
+  // combine the partials of tile x (every wave for itself): this lane's
+  // column key, and the tile's flags (bit 0 shared, bit 1 all padding) in
+  // this wave's flag slot
+  int ntile = ntile_w;
+  auto finalize = [&](int x) -> int64_t {
+    const int64_t* pp = part + (x & 1) * (2 * 8 * KT);
+    const int j = lane & 31;
+    int64_t mx = -1, mn = INT64_MAX;
+#pragma unroll
+    for (int tg = 0; tg < 8; tg++) {
+      mx = max(mx, pp[tg * KT + j]);
+      mn = min(mn, pp[8 * KT + tg * KT + j]);
+    }
+    const bool pad = mx == -1;
+    const bool shared = pad || mn == mx;
+    const uint64_t sh = __ballot(shared), pd = __ballot(pad);
+    const int flags = (sh == ~0ull ? 1 : 0) | (pd == ~0ull ? 2 : 0);
+    if (x < ntile_w && (flags & 2) && x < ntile) ntile = x;  // every row has ended
+    if (lane == 0) flag_s[wave * 8 + (x & 7)] = flags;
+    return mx;
+  };
+
+  // ---- Q^T as the B operand: lane (c16, g) holds dims 32 S + 8 g .. +8 of
+  // row c16 of each block
+  bf16x8_l qreg[2][KSTEPS];
+#pragma unroll
+  for (int rb = 0; rb < 2; rb++) {
+    const uint16_t* qp = q + (((b * hq + row_h[rb]) * q_seq + q0 + row_q[rb]) * D) + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; s++) {
+      u32x4_l raw = {0u, 0u, 0u, 0u};
+      if (row_on[rb]) raw = __builtin_bit_cast(u32x4_l, *(const uint4*)(qp + 32 * s));
+      qreg[rb][s] = __builtin_bit_cast(bf16x8_l, raw);
+    }
+  }
+
+  // ---- per-lane LDS addresses within a K/V tile
+  // K: row c16 (+16 for keys 16..31), chunk 4 S + g stored at (4 S + g) ^ c16
+  uint32_t kofs[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; s++) kofs[s] = (uint32_t)(c16 * ROWB + 16 * ((4 * s + g) ^ c16));
+  // V^T: lane 4 jj + qq of group g reads row 4 g + jj (+16), dv 16 dt + 4 qq:
+  // chunk 2 dt + (qq >> 1) stored at 2 (dt ^ fr) + (qq >> 1), fr = row & 7
+  uint32_t vofs[DVT];
+  {
+    const int jj = c16 >> 2, qq = c16 & 3;
+    const int Rr = 4 * g + jj;
+    const int fr = Rr & 7;
+#pragma unroll
+    for (int dt = 0; dt < DVT; dt++)
+      vofs[dt] = (uint32_t)(KT * ROWB + Rr * ROWB + 16 * (2 * (dt ^ fr) + (qq >> 1)) + 8 * (qq & 1));
+  }
+  constexpr int HALF = 16 * ROWB;  // keys 16..31 of a tile
+
+  // scores in log2 units: raw dot product times scale * log2 e; with a softcap
+  // c, c tanh(s / c) log2 e with tanh(x) = 1 - 2 / (exp(2x) + 1) on the
+  // hardware exp2 and reciprocal (a few fp32 ulps of tanh, exact limits +-1)
+  const float f = scale * kLog2eL;
+  const float cap_k = SOFTCAP ? 2.0f * scale * kLog2eL / softcap : 0.0f;  // exp2 argument per raw dot unit
+  const float cap_a = SOFTCAP ? softcap * kLog2eL : 0.0f;
+  const float cap_b = 2.0f * cap_a;
+  f32x4_l o[2][DVT];
+#pragma unroll
+  for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+    for (int dt = 0; dt < DVT; dt++) o[rb][dt] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+  f32x4_l sa[2][2];  // [row block][key half]
+  auto zero_s = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++) sa[rb][0] = sa[rb][1] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
+  };
+  u32x4_l kr[8];
+  s16x4_l vr0[DVT], vr1[DVT];
+  uint32_t kslot = 0, vslot = 0;
+  auto kread = [&](auto jc) {
+    constexpr int J = decltype(jc)::value;  // k-step J >> 1, key half J & 1
+    kr[J] = ds_read_b128_at<(J & 1) * HALF>(kslot + kofs[J >> 1]);
+  };
+  auto kmfma = [&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    const bf16x8_l a = __builtin_bit_cast(bf16x8_l, kr[J]);
+    sa[0][J & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[0][J >> 1], sa[0][J & 1], 0, 0, 0);
+    sa[1][J & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[1][J >> 1], sa[1][J & 1], 0, 0, 0);
+  };
+  auto vread = [&](auto dc) {
+    constexpr int DT = decltype(dc)::value;
+    vr0[DT] = ds_read_tr16_at<0>(vslot + vofs[DT]);
+    vr1[DT] = ds_read_tr16_at<HALF>(vslot + vofs[DT]);
+  };
+  bf16x8_l pb[2];
+  auto vmfma = [&](auto dc) {
+    constexpr int DT = decltype(dc)::value;
+    const s16x4_l a8[2] = {vr0[DT], vr1[DT]};
+    const bf16x8_l a = __builtin_bit_cast(bf16x8_l, a8);
+    o[0][DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0], o[0][DT], 0, 0, 0);
+    o[1][DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1], o[1][DT], 0, 0, 0);
+  };
+  // S of the tile at kslot alone (reads two steps ahead)
+  auto s_alone = [&]() {
+    zero_s();
+    static_for<2>(kread);
+    static_for<8>([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      if constexpr (J + 2 < 8) kread(std::integral_constant<int, J + 2>{});
+      constexpr int LATER = (J + 2 < 8) ? 2 : 7 - J;
+      lgkm_wait_tied1<LATER>(kr[J]);
+      kmfma(jc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // PV of the tile at vslot alone
+  auto pv_alone = [&]() {
+    static_for<4>(vread);
+    static_for<DVT>([&](auto dc) {
+      constexpr int DT = decltype(dc)::value;
+      constexpr int AHEAD = (3 < DVT - 1 - DT ? 3 : DVT - 1 - DT);
+      lgkm_wait_tied<2 * AHEAD>(vr0[DT], vr1[DT]);
+      vmfma(dc);
+      if constexpr (DT + 4 < DVT) vread(std::integral_constant<int, DT + 4>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // online softmax of the scores in sa for tile x; `only` < 0: every row,
+  // else only the rows of query `only`; `none`: every row masked (the
+  // tile is redone row by row). Rescales O and returns P^T in pb.
+  auto softmax = [&](int x, int only, bool none) {
+    const int64_t c0 = (int64_t)x * KT;
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++) {
+      float xs[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        xs[i] = sa[rb][0][i];
+        xs[4 + i] = sa[rb][1][i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        if constexpr (SOFTCAP) xs[i] = cap_a - cap_b * __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(xs[i] * cap_k) + 1.0f);
+        else xs[i] *= f;
+      }
+      const bool live = row_on[rb] && !none && (only < 0 || only == row_q[rb]);
+      const int64_t n = live ? (int64_t)n_s[row_q[rb]] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int64_t col = c0 + (i < 4 ? 4 * g + i : 16 + 4 * g + i - 4);
+        xs[i] = col < n ? xs[i] : -INFINITY;
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])), fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7])));
+      tmax = max_x32(max_x16(tmax));
+      const float mn = fmaxf(m_run[rb], tmax);
+      const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[rb] - mn);
+      m_run[rb] = mn;
+      const float nm = mn == -INFINITY ? 0.0f : -mn;
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) p[i] = __builtin_amdgcn_exp2f(xs[i] + nm);
+      const float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      l_run[rb] = l_run[rb] * alpha + sum_x32(sum_x16(ps));
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < DVT; dt++) o[rb][dt] *= alpha;
+      }
+      const u32x4_l pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                          pack_bf16x2(p[6], p[7])};
+      pb[rb] = __builtin_bit_cast(bf16x8_l, pw);
+    }
+  };
+  auto slot_of = [&](int x) { return (uint32_t)(uintptr_t)(lds + (x % NSTAGE) * KV_TILE); };
+  auto tile_flags = [&](int x) { return flag_s[wave * 8 + (x & 7)]; };
+
+  // A tile that is not shared, redone one query at a time through the spare
+  // slot: that query's own keys are gathered (clamped into the cache), its
+  // rows updated, every other row masked. Waits for every load in flight.
+  auto row_by_row = [&](int x) {
+    const uint32_t spare = (uint32_t)(uintptr_t)(lds + SPARE_OFF);
+    for (int r = 0; r < rlive; r++) {
+      if ((int64_t)n_s[r] <= (int64_t)x * KT) continue;  // uniform: the row ended before this tile
+      const int64_t col = (int64_t)x * KT + (lane & 31);
+      int64_t kl = -1;
+      if (col < width) kl = load_index<I64>(ibase, (int64_t)r * width + col);
+      key_offsets(kl);
+      wait_vm<0>();
+      __syncthreads();  // every wave is done with the spare slot
+      gather_issue(lds + SPARE_OFF);
+      wait_vm<0>();
+      __syncthreads();
+      kslot = spare;
+      vslot = spare;
+      s_alone();
+      softmax(x, r, false);
+      pv_alone();
+    }
+    // the tile's PV in the pipeline must add nothing
+    pb[0] = pb[1] = __builtin_bit_cast(bf16x8_l, (u32x4_l){0u, 0u, 0u, 0u});
+  };
+
+  // ---- prologue: index tiles 0..3 folded, keys of tiles 0..2 gathered,
+  // index tiles 4, 5 in flight
+#pragma unroll 1
+  for (int x = 0; x < 4; x++) issue_idx(x);
+  wait_vm<0>();
+  __syncthreads();  // n_s initialised, index tiles 0..3 in LDS
+  fold(0);
+  fold(1);
+  __syncthreads();
+  int64_t kk = finalize(0);
+  key_offsets(kk);
+  gather_issue(lds + 0 * KV_TILE);
+  issue_idx(4);
+  kk = finalize(1);
+  key_offsets(kk);
+  lds_barrier();  // partial slots of tiles 0, 1 are read
+  fold(2);
+  fold(3);
+  gather_issue(lds + 1 * KV_TILE);
+  lds_barrier();
+  kk = finalize(2);
+  key_offsets(kk);
+  gather_issue(lds + 2 * KV_TILE);
+  issue_idx(5);
+  // the iteration-0 fold reads tile 4's index slot: everything but the last
+  // tile's loads has landed
+  if (ntile > 0) {
+    wait_vm<GLOADS + IL>();  // tile 0 and index tile 4 have landed for this wave
+    lds_barrier();
+    kslot = slot_of(0);
+    if (tile_flags(0) & 1) {
+      s_alone();
+      softmax(0, -1, false);
+    } else {
+      zero_s();
+      softmax(0, -1, true);
+      row_by_row(0);
+    }
+  }
+
+  // ---- steady state: iteration t scores tile t+1 interleaved with the PV
+  // of tile t, issues the gather of tile t+3 and the index load of tile t+6,
+  // folds index tile t+4 and finalizes tile t+3
+  for (int t = 0; t + 1 < ntile; t++) {
+    wait_vm<GLOADS + IL>();  // tile t+1 and index tile t+4 have landed (the last iteration's loads may not)
+    lds_barrier();           // for every wave; tile t-1's slot and partial slot t+3 & 1 are free
+    kk = finalize(t + 3);    // partials folded in the last iteration
+    key_offsets(kk);
+    const bool shared_next = (tile_flags(t + 1) & 1) != 0;
+    kslot = slot_of(t + 1);
+    vslot = slot_of(t);
+    zero_s();
+    constexpr int PL = 2;
+    auto sread = [&](auto jc) {
+      kread(jc);
+      vread(jc);
+    };
+    static_for<PL>(sread);
+    static_for<8>([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      if constexpr (J + PL < 8) sread(std::integral_constant<int, J + PL>{});
+      if constexpr (J < GLOADS) {  // the gather of tile t+3, one load per step
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(grsrc, (__attribute__((address_space(3))) void*)(lds + ((t + 3) % NSTAGE) * KV_TILE + 1024 * (GLOADS * wave + J)),
+                                                16, goff[J], 0, 0, 0);
+      }
+      constexpr int LATER = gqa_step_reads(J + 1) * (J + 1 < 8) + gqa_step_reads(J + 2) * (J + 2 < 8);
+      lgkm_wait3<LATER>(kr[J], vr0[J], vr1[J]);
+      kmfma(jc);
+      vmfma(jc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    issue_idx(t + 6);
+    fold(t + 4);
+    if (shared_next) {
+      softmax(t + 1, -1, false);
+    } else {
+      softmax(t + 1, -1, true);
+      row_by_row(t + 1);
+    }
+  }
+
+  // ---- the last tile's PV alone
+  if (ntile > 0) {
+    vslot = slot_of(ntile - 1);
+    pv_alone();
+  }
+  wait_vm<0>();  // loads issued past the last tile
+
+  // ---- store: lane holds O^T[16 dt + 4 g + r][row c16] of each block
+#pragma unroll
+  for (int rb = 0; rb < 2; rb++) {
+    if (!row_on[rb]) continue;
+    const float inv = l_run[rb] > 0.0f ? 1.0f / l_run[rb] : 0.0f;
+    uint16_t* yp = y + (((b * hq + row_h[rb]) * q_seq + q0 + row_q[rb]) * D) + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DVT; dt++) {
+      const u32x2_l w2 = {pack_bf16x2(o[rb][dt][0] * inv, o[rb][dt][1] * inv),
+                          pack_bf16x2(o[rb][dt][2] * inv, o[rb][dt][3] * inv)};
+      *(u32x2_l*)(yp + 16 * dt) = w2;
+    }
+  }
+}
+
+bool gqa_supported(const sa_config& cfg, int64_t index_heads) {
+  if (cfg.dtype != SA_BF16 || cfg.kv_layout != SA_KV_SEPARATE || cfg.cache_format != SA_CACHE_DENSE) return false;
+  if (index_heads != 1 || cfg.head_dim_qk != gq::D || cfg.head_dim_v != gq::D) return false;
+  if (cfg.kv_num_heads <= 0 || cfg.num_heads % cfg.kv_num_heads != 0) return false;
+  const int64_t group = cfg.num_heads / cfg.kv_num_heads;
+  if (group > gq::MROWS) return false;
+  return cfg.max_cache_len <= (int64_t)(0x7fffffffLL / gq::ROWB);
+}
+
+static bool g_gqa_attr[4] = {false, false, false, false};
+
+sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
+  using namespace gq;
+  const int group = (int)(a.hq / a.hkv);
+  const int R = group >= MROWS ? 1 : std::min(RMAX, MROWS / group);
+  const int64_t nqb = (a.q_seq + R - 1) / R;
+  const int64_t pairs = a.batch * a.hkv;
+  if (pairs <= 0 || nqb <= 0) return SA_OK;
+  const int64_t wgs = (pairs + 7) / 8 * 8 * nqb;
+  if (wgs > 0x7fffffffLL || nqb > 0x7fffffffLL) return set_error(c, SA_E_SHAPE, "forward: too many rows for one launch");
+  if (a.cap > (int64_t)(0x7fffffffLL / ROWB)) return set_error(c, SA_E_SHAPE, "forward: cache too long for 32-bit row offsets");
+  if ((int64_t)R * a.width * (a.idx64 ? 8 : 4) > 0x7fffffffLL)
+    return set_error(c, SA_E_SHAPE, "forward: index rows too wide for 32-bit offsets");
+  const bool cap_on = a.softcap != 0.0f;
+  const int variant = (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0);
+  const void* fns[4] = {(const void*)gqa_forward_kernel<false, false>, (const void*)gqa_forward_kernel<true, false>,
+                        (const void*)gqa_forward_kernel<false, true>, (const void*)gqa_forward_kernel<true, true>};
+  const size_t lds = a.idx64 ? lds_bytes<true>() : lds_bytes<false>();
+  if (!g_gqa_attr[variant]) {
+    hipError_t e = hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return check_hip(c, e, "forward (gqa) LDS attribute");
+    g_gqa_attr[variant] = true;
+  }
+  const dim3 grid((unsigned)wgs), block(THREADS);
+  prof_begin(c);
+#define SA_GQA(I, C)                                                                                         \
+  hipLaunchKernelGGL((gqa_forward_kernel<I, C>), grid, block, lds, c->stream, (const uint16_t*)a.q,          \
+                     (const uint8_t*)a.k, (const uint8_t*)a.v, a.idx, a.valid_len, (uint16_t*)a.y, a.batch, \
+                     a.hkv, a.q_seq, a.cap, a.width, group, (int)nqb, a.scale, a.softcap)
+  switch (variant) {
+    case 0: SA_GQA(false, false); break;
+    case 1: SA_GQA(true, false); break;
+    case 2: SA_GQA(false, true); break;
+    default: SA_GQA(true, true); break;
+  }
+#undef SA_GQA
+  prof_end(c);
+  return check_hip(c, hipGetLastError(), "forward (gqa)");
+}
+
+}  // namespace sa

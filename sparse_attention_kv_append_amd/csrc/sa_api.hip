@@ -282,8 +282,9 @@ sa_status sparse_attn_validate_indices(sparse_attn_ctx* c, const void* indices, 
 namespace sa {
 // The kernel that runs a forward launch: 0 = generic, 1 = register-staged
 // shared-latent fallback, 2 = shared-latent LDS-ring kernel over bf16 rows,
-// 3 = wave-pair kernel over fp8 records.
+// 3 = wave-pair kernel over fp8 records, 4 = grouped-query kernel.
 static int forward_path(const sa_config& k, int64_t index_heads) {
+  if (gqa_supported(k, index_heads)) return 4;
   if (!mla_supported(k, index_heads)) return 0;
   if (latent_supported(k, index_heads)) return 2;
   if (pair_supported(k, index_heads)) return 3;
@@ -295,7 +296,7 @@ sa_status sparse_attn_query_plan(const sparse_attn_ctx* c, int64_t batch, int64_
                                  int64_t index_heads, int64_t width, int32_t* path, int32_t* splits) {
   if (!live(c) || !path || !splits) return SA_E_STATE;
   *path = sa::forward_path(c->cfg, index_heads);
-  *splits = *path ? sa::mla_splits(batch * q_seq, width) : 1;
+  *splits = (*path >= 1 && *path <= 3) ? sa::mla_splits(batch * q_seq, width) : 1;
   return SA_OK;
 }
 
@@ -319,7 +320,7 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
   // the shared-latent MFMA kernels validate their own columns; other paths
   // run the validation kernel first on the same stream
   const int path = sa::forward_path(k, index_heads);
-  if (fused_validate && path < 2) {
+  if (fused_validate && path != 2 && path != 3) {
     s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
                                      cache_capacity, nullptr, nullptr, nullptr);
     if (s != SA_OK) return s;
@@ -351,6 +352,7 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
     case 2: return sa::launch_forward_latent(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
     case 3: return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
     case 1: return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
+    case 4: return sa::launch_forward_gqa(c, a);
     default: return sa::launch_forward_generic(c, a);
   }
 }

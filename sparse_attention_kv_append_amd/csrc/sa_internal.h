@@ -145,11 +145,15 @@ bool latent_supported(const sa_config& cfg, int64_t index_heads);
 // the wave-pair kernel: fp8_e4m3_block64 shared-latent records (64 RoPE dims),
 // per-batch cache below 2 GiB (32-bit record offsets from the batch's base)
 bool pair_supported(const sa_config& cfg, int64_t index_heads);
+// the grouped-query kernel: bf16 separate K/V caches of 128 dims, one index
+// list per (batch, query), group size up to 128, per-head cache below 2 GiB
+bool gqa_supported(const sa_config& cfg, int64_t index_heads);
 int mla_splits(int64_t rows, int64_t width);
 sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a);
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
 sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused);
 sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused);
+sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a);
 sa_status launch_mla_combine(sparse_attn_ctx* c, int64_t rows, int64_t q_seq, int splits, uint16_t* y);
 
 sa_status set_error(sparse_attn_ctx* c, sa_status s, const std::string& msg);

@@ -1,8 +1,9 @@
 """Forward launches with fused validation over index rows holding planted
 violations: the error word, the first failing (row, column) and the message
-equal the oracle validator's verdict, on every forward path. The generic path
-runs the standalone validation kernel before its forward; the shared-latent
-paths validate inside the attention kernels, each workgroup its own columns.
+equal the oracle validator's verdict, on every forward path. The generic and
+grouped-query paths run the standalone validation kernel before their
+forward; the shared-latent paths validate inside the attention kernels, each
+workgroup its own columns.
 
 Y of such a launch is not compared (the caller discards it): the launch only
 has to stay in bounds and finish. Rows wider than one 2048-key stage of a
@@ -78,8 +79,10 @@ CASES = {
     "pair_fp8_split": (FP8.scaled(batch=12, past=1200, topk=650, width=650), 3, 16, None),
     "pair_fp8_wide_late": (FP8.scaled(batch=1, q_seq=260, cur=260, past=2000, width=2100, topk=2100,
                                       pattern="causal_prefill"), 3, 17, (2048, 2100)),
+    "gqa": (W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=12, past=500, cur=12,
+                                            width=520, topk=520), 4, 18, None),
     "generic": (W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=12, past=500, cur=12,
-                                                width=520, topk=520), 0, 18, None),
+                                                width=520, topk=520, dtype=W.DT_F16), 0, 19, None),
 }
 
 
@@ -108,12 +111,13 @@ def test_fused_verdict_matches_oracle(name, i64):
                               generator=gen)
         vcache = None
     else:
-        dt = torch.bfloat16 if w.dtype == W.DT_BF16 else torch.float32
+        dt = {W.DT_BF16: torch.bfloat16, W.DT_F16: torch.float16, W.DT_F32: torch.float32}[w.dtype]
         cache = torch.randn((B, w.hkv, w.cap, w.dk), device="cuda", generator=gen).to(dt)
         vcache = None if w.layout == W.LAYOUT_SHARED_LATENT else \
             torch.randn((B, w.hkv, w.cap, w.dv), device="cuda", generator=gen).to(dt)
-    q = torch.randn((B, w.hq, Sq, w.dk), device="cuda", generator=gen).to(torch.bfloat16)
-    y = torch.empty((B, w.hq, Sq, w.dv), dtype=torch.bfloat16, device="cuda")
+    qdt = {W.DT_BF16: torch.bfloat16, W.DT_F16: torch.float16, W.DT_F32: torch.float32}[w.dtype]
+    q = torch.randn((B, w.hq, Sq, w.dk), device="cuda", generator=gen).to(qdt)
+    y = torch.empty((B, w.hq, Sq, w.dv), dtype=qdt, device="cuda")
     vlen = tt(bound)
     for rep in range(2):  # the per-row slots re-arm: a second launch gives the same verdict
         ctx.reset_error_async()
