@@ -6,13 +6,12 @@
 // query heads (the standard Attention page's softcap applies when set). In a
 // grouped-query layout the `group` heads of one kv head read the same K and V
 // rows, so a workgroup takes one (batch, kv head) and R = min(32, 128 / group)
-// consecutive queries: up to 128 (query, head) rows, 32 per wave as two
-// blocks of 16. Walking the index rows 32 columns at a time, a tile is
+// consecutive queries: up to 128 (query, head) rows, 16 per wave (eight
+// waves, two per SIMD, so one wave's softmax overlaps the other's MFMAs). Walking the index rows 32 columns at a time, a tile is
 // shared when every one of the R rows holds, in each column, either the same
 // key or padding (-1): then the tile's 32 K and V rows are gathered once and
 // S^T = K_tile . Q^T and O^T += V_tile^T . P^T run for all the rows on
-// v_mfma_f32_16x16x32_bf16 (each K or V read from LDS feeds both row blocks
-// of a wave). Dense causal selections - the degenerate case where every
+// v_mfma_f32_16x16x32_bf16. Dense causal selections - the degenerate case where every
 // query selects a prefix of the keys - share every tile. A tile that is not
 // shared is redone row by row (R small passes, each gathering that row's own
 // keys and updating only its rows), so any valid index rows give IndexShare's
@@ -41,9 +40,10 @@ namespace gq {
 constexpr int D = 128;                           // head dim of Q, K and V
 constexpr int ROWB = D * 2;                      // 256 bytes per cache row
 constexpr int KT = 32;                           // columns (keys) per tile
-constexpr int THREADS = 256;
-constexpr int WAVES = THREADS / 64;
 constexpr int MROWS = 128;                       // (query, head) rows per workgroup
+constexpr int RB = 1;                            // 16-row blocks per wave
+constexpr int WAVES = MROWS / (16 * RB);         // 8 waves, two per SIMD
+constexpr int THREADS = 64 * WAVES;
 constexpr int RMAX = 32;                         // queries per workgroup at most
 constexpr int KSTEPS = D / 32;                   // 4 k-steps of S^T
 constexpr int DVT = D / 16;                      // 8 dv tiles of O^T
@@ -57,7 +57,7 @@ template <bool I64> constexpr int idx_tile_bytes() { return RMAX * KT * (I64 ? 8
 template <bool I64> constexpr int ILOADS = idx_tile_bytes<I64>() / 256 / WAVES;  // dword loads per wave
 constexpr int IDX_OFF = SPARE_OFF + KV_TILE;
 template <bool I64> constexpr int part_off() { return IDX_OFF + IDX_SLOTS * idx_tile_bytes<I64>(); }
-constexpr int PART_BYTES = 2 * 8 * KT * 8;       // per slot: [8 thread groups][32 columns] max, min (int64)
+constexpr int PART_BYTES = 2 * KT * WAVES * 4;   // per slot: max, min [32 columns][wave] (int32)
 template <bool I64> constexpr int nrow_off() { return part_off<I64>() + 2 * PART_BYTES; }
 template <bool I64> constexpr int flag_off() { return nrow_off<I64>() + RMAX * 4; }
 template <bool I64> constexpr size_t lds_bytes() { return (size_t)flag_off<I64>() + WAVES * 8 * 4; }
@@ -79,7 +79,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   constexpr int ISZ = I64 ? 8 : 4;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lds_u8* lds = (lds_u8*)lds_raw;
-  int64_t* part = (int64_t*)(lds_raw + part_off<I64>());  // [2 slots][max | min][8][32]
+  int* part = (int*)(lds_raw + part_off<I64>());          // [2 slots][max | min][32 columns][wave]
   int* n_s = (int*)(lds_raw + nrow_off<I64>());          // [RMAX] first -1 column of each query row
   int* flag_s = (int*)(lds_raw + flag_off<I64>());       // [wave][8] tile flags, per wave
 
@@ -106,12 +106,12 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
   const int ntile_w = (int)((width + KT - 1) / KT);
 
-  // this lane's rows: block rb holds row m = 32 wave + 16 rb + c16
-  int row_q[2], row_h[2];
-  bool row_on[2];
+  // this lane's rows: block rb holds row m = 16 (RB wave + rb) + c16
+  int row_q[RB], row_h[RB];
+  bool row_on[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++) {
-    const int m = 32 * wave + 16 * rb + c16;
+  for (int rb = 0; rb < RB; rb++) {
+    const int m = 16 * (RB * wave + rb) + c16;
     const int r = m / group;
     row_q[rb] = r;
     row_h[rb] = (int)(kvh * group) + (m - r * group);
@@ -151,36 +151,53 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     if constexpr (I64) return *(const __attribute__((address_space(3))) int64_t*)(slot + (r * KT + j) * 8);
     else return *(const __attribute__((address_space(3))) int32_t*)(slot + (r * KT + j) * 4);
   };
-  // fold index tile x: thread (column j = tid & 31, group tg = tid >> 5) over
-  // rows tg, tg + 8, ...: partial max and min (min over non-padding entries)
-  // and the first -1 of each row
+  // fold index tile x: thread (column j = tid & 31, group tg = tid >> 5)
+  // over rows tg, tg + THREADS / 32, ...: maximum and minimum over the
+  // non-padding entries (values taken as int32: below -1 -> -2, from the
+  // cache length up -> the cache length, which keeps every valid row exact),
+  // and the first -1 of each row; the two halves of a wave are merged, and
+  // lanes 0..31 store the wave's partials
   auto fold = [&](int x) {
     const lds_u8* slot = lds + IDX_OFF + (x % IDX_SLOTS) * ITB;
     const int j = tid & 31, tg = tid >> 5;
     const int64_t col = (int64_t)x * KT + j;
-    int64_t mx = -1, mn = INT64_MAX;
-    for (int r = tg; r < rlive; r += 8) {
-      const int64_t v = col < width ? idx_at(slot, r, j) : -1;
-      mx = max(mx, v);
-      if (v != -1) mn = min(mn, v);
-      else atomicMin(&n_s[r], (int)col);
+    int mx = -1, mn = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < RMAX / (THREADS / 32); k++) {
+      const int r = tg + (THREADS / 32) * k;
+      if (r < rlive) {
+        const int64_t v = col < width ? idx_at(slot, r, j) : -1;
+        const int v32 = v == -1 ? -1 : (v < -1 ? -2 : (v >= bound ? (int)bound : (int)v));
+        mx = max(mx, v32);
+        if (v32 != -1) mn = min(mn, v32);
+        else atomicMin(&n_s[r], (int)col);
+      }
     }
-    int64_t* pp = part + (x & 1) * (2 * 8 * KT);
-    pp[tg * KT + j] = mx;
-    pp[8 * KT + tg * KT + j] = mn;
+    {
+      const auto sx = __builtin_amdgcn_permlane32_swap((unsigned)mx, (unsigned)mx, false, false);
+      const auto sn = __builtin_amdgcn_permlane32_swap((unsigned)mn, (unsigned)mn, false, false);
+      mx = max((int)sx[0], (int)sx[1]);
+      mn = min((int)sn[0], (int)sn[1]);
+    }
+    int* pp = part + (x & 1) * (2 * KT * WAVES);
+    if (lane < 32) {
+      pp[j * WAVES + wave] = mx;
+      pp[KT * WAVES + j * WAVES + wave] = mn;
+    }
   };
 
   // ---- K/V gather of a tile: lane l of load i of wave w fills 16-byte
   // chunk 64 (4 w + i) + l of the slot: waves 0, 1 the K rows, waves 2, 3 the V rows
   int ld_row[GLOADS], ld_off[GLOADS];
+  const bool kwave = wave < WAVES / 2;  // the first half of the waves loads K rows
 #pragma unroll
   for (int i = 0; i < GLOADS; i++) {
     const int ci = (64 * (GLOADS * wave + i) + lane) & 511;
     const int Rr = ci >> 4, pc = ci & 15;
     ld_row[i] = Rr;
-    ld_off[i] = (wave < 2 ? (pc ^ (Rr & 15)) : (pc ^ (2 * (Rr & 7)))) << 4;
+    ld_off[i] = (kwave ? (pc ^ (Rr & 15)) : (pc ^ (2 * (Rr & 7)))) << 4;
   }
-  const __amdgpu_buffer_rsrc_t grsrc = wave < 2 ? krsrc : vrsrc;
+  const __amdgpu_buffer_rsrc_t grsrc = kwave ? krsrc : vrsrc;
   uint32_t goff[GLOADS];
   auto gather_issue = [&](lds_u8* slot) {
 #pragma unroll
@@ -203,13 +220,17 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   // this wave's flag slot
   int ntile = ntile_w;
   auto finalize = [&](int x) -> int64_t {
-    const int64_t* pp = part + (x & 1) * (2 * 8 * KT);
-    const int j = lane & 31;
-    int64_t mx = -1, mn = INT64_MAX;
+    const int* pp = part + (x & 1) * (2 * KT * WAVES) + (lane & 31) * WAVES;
+    int mx = -1, mn = 0x7fffffff;
 #pragma unroll
-    for (int tg = 0; tg < 8; tg++) {
-      mx = max(mx, pp[tg * KT + j]);
-      mn = min(mn, pp[8 * KT + tg * KT + j]);
+    for (int w4 = 0; w4 < WAVES; w4 += 4) {
+      const u32x4_l a = *(const lds_u32x4*)(pp + w4);
+      const u32x4_l c = *(const lds_u32x4*)(pp + KT * WAVES + w4);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        mx = max(mx, (int)a[e]);
+        mn = min(mn, (int)c[e]);
+      }
     }
     const bool pad = mx == -1;
     const bool shared = pad || mn == mx;
@@ -222,9 +243,9 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
 
   // ---- Q^T as the B operand: lane (c16, g) holds dims 32 S + 8 g .. +8 of
   // row c16 of each block
-  bf16x8_l qreg[2][KSTEPS];
+  bf16x8_l qreg[RB][KSTEPS];
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++) {
+  for (int rb = 0; rb < RB; rb++) {
     const uint16_t* qp = q + (((b * hq + row_h[rb]) * q_seq + q0 + row_q[rb]) * D) + 8 * g;
 #pragma unroll
     for (int s = 0; s < KSTEPS; s++) {
@@ -259,17 +280,20 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   const float cap_k = SOFTCAP ? 2.0f * scale * kLog2eL / softcap : 0.0f;  // exp2 argument per raw dot unit
   const float cap_a = SOFTCAP ? softcap * kLog2eL : 0.0f;
   const float cap_b = 2.0f * cap_a;
-  f32x4_l o[2][DVT];
+  f32x4_l o[RB][DVT];
+  float m_run[RB], l_run[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++)
+  for (int rb = 0; rb < RB; rb++) {
 #pragma unroll
     for (int dt = 0; dt < DVT; dt++) o[rb][dt] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.0f;
+  }
 
-  f32x4_l sa[2][2];  // [row block][key half]
+  f32x4_l sa[RB][2];  // [row block][key half]
   auto zero_s = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < 2; rb++) sa[rb][0] = sa[rb][1] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; rb++) sa[rb][0] = sa[rb][1] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
   };
   u32x4_l kr[8];
   s16x4_l vr0[DVT], vr1[DVT];
@@ -281,21 +305,23 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   auto kmfma = [&](auto jc) {
     constexpr int J = decltype(jc)::value;
     const bf16x8_l a = __builtin_bit_cast(bf16x8_l, kr[J]);
-    sa[0][J & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[0][J >> 1], sa[0][J & 1], 0, 0, 0);
-    sa[1][J & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[1][J >> 1], sa[1][J & 1], 0, 0, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++)
+      sa[rb][J & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[rb][J >> 1], sa[rb][J & 1], 0, 0, 0);
   };
   auto vread = [&](auto dc) {
     constexpr int DT = decltype(dc)::value;
     vr0[DT] = ds_read_tr16_at<0>(vslot + vofs[DT]);
     vr1[DT] = ds_read_tr16_at<HALF>(vslot + vofs[DT]);
   };
-  bf16x8_l pb[2];
+  bf16x8_l pb[RB];
   auto vmfma = [&](auto dc) {
     constexpr int DT = decltype(dc)::value;
     const s16x4_l a8[2] = {vr0[DT], vr1[DT]};
     const bf16x8_l a = __builtin_bit_cast(bf16x8_l, a8);
-    o[0][DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0], o[0][DT], 0, 0, 0);
-    o[1][DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1], o[1][DT], 0, 0, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++)
+      o[rb][DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rb], o[rb][DT], 0, 0, 0);
   };
   // S of the tile at kslot alone (reads two steps ahead)
   auto s_alone = [&]() {
@@ -328,7 +354,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   auto softmax = [&](int x, int only, bool none) {
     const int64_t c0 = (int64_t)x * KT;
 #pragma unroll
-    for (int rb = 0; rb < 2; rb++) {
+    for (int rb = 0; rb < RB; rb++) {
       float xs[8];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
@@ -393,7 +419,8 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
       pv_alone();
     }
     // the tile's PV in the pipeline must add nothing
-    pb[0] = pb[1] = __builtin_bit_cast(bf16x8_l, (u32x4_l){0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++) pb[rb] = __builtin_bit_cast(bf16x8_l, (u32x4_l){0u, 0u, 0u, 0u});
   };
 
   // ---- prologue: index tiles 0..3 folded, keys of tiles 0..2 gathered,
@@ -486,7 +513,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
 
   // ---- store: lane holds O^T[16 dt + 4 g + r][row c16] of each block
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++) {
+  for (int rb = 0; rb < RB; rb++) {
     if (!row_on[rb]) continue;
     const float inv = l_run[rb] > 0.0f ? 1.0f / l_run[rb] : 0.0f;
     uint16_t* yp = y + (((b * hq + row_h[rb]) * q_seq + q0 + row_q[rb]) * D) + 4 * g;
