@@ -3,7 +3,10 @@
 
 A step is one pass of the whole path over one batch: reset the device error
 word, append the current token(s) to the cache in place, validate the index
-rows, gather + score + softmax + PV (+ split-K combine), store Y.
+rows, gather + score + softmax + PV (+ split-K combine), store Y. On the bf16
+shared-latent path this is one sparse_attn_step call (one attention launch
+that also appends and resets, plus the combine); elsewhere the three calls
+reset_error_async, kv_append and forward.
 
 Default workload (decode, bf16, shared-latent MLA rows): batch 32, one query
 per sequence, 64 query heads sharing one kv head, 576-dim rows (V = first
@@ -149,9 +152,18 @@ class Setup:
         self.selected = [int((ih >= 0).sum()) // 1 for ih in self.idx_host]
         self.path, self.splits = self.ctx.query_plan(B, Sq, 1, w.width)
 
+    def fused_step(self):
+        """True when the step is one sparse_attn_step call: the bf16 shared-latent
+        path takes reset + in-place append + forward in one launch."""
+        return self.path == 2 and self.w.cur <= 8
+
     def step(self, i):
         w, c = self.w, self.ctx
         r = i % len(self.idxs)
+        if self.fused_step():
+            c.step(self.qs[r % len(self.qs)], w.batch, w.q_seq, self.k, w.cap, self.plen, self.cur_k, w.cur,
+                   self.vlen, self.idxs[r], 1, w.width, self.y, reset_error=True)
+            return
         c.reset_error_async()
         c.kv_append(w.batch, self.k, self.v, w.cap, self.plen, self.cur_k, self.cur_v, w.cur, self.k,
                     self.v, w.cap, cur_is_unquantized_bf16=self.fp8, present_len=self.vlen)
@@ -506,6 +518,8 @@ def main():
                                f"index width {w.width}, {'graph replay' if use_graph else 'eager'}, "
                                f"{nset} rotating index sets",
                    "selected_tokens_per_step": tokens, "splits": s.splits,
+                   "step_calls": ("sparse_attn_step (reset + append + forward in one launch)" if s.fused_step()
+                                  else "reset_error_async + kv_append + forward"),
                    "step_hbm_GBps": s.step_bytes() / (ms_per_step / 1e3) / 1e9},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "kernel": kernel_name(s),

@@ -17,6 +17,7 @@ __global__ void reset_error_kernel(ErrorBlock* err) {
     err->first_bad = ~0ull;
     err->call_key = ~0ull;
     err->detail_class = 0;
+    err->call_word = 0u;
   }
 }
 

@@ -61,15 +61,22 @@ __host__ __device__ constexpr int step_reads(int j) {
   return (j < lat::KSTEPS ? 2 : 0) + (2 * j + 1 < lat::DVT ? 4 : 0);
 }
 
-template <bool I64, bool FUSED, bool SOFTCAP>
+// APPEND (with FUSED): the launch also appends the batch's cur_len current
+// rows to the cache in place (rows past_len[b] ..) and writes present_len[b];
+// every workgroup writes its batch's new rows itself before it gathers, so it
+// reads its own writes whatever other workgroups do; with `reset` the
+// launch's last workgroup replaces the error word instead of adding to it.
+template <bool I64, bool FUSED, bool SOFTCAP, bool APPEND>
 __global__ void __launch_bounds__(lat::THREADS, 1)
-latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache,
+latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
                       const void* __restrict__ idx, const int32_t* __restrict__ valid_len,
                       uint16_t* __restrict__ y,
                       float* __restrict__ part_o, float* __restrict__ part_ml, int64_t q_seq,
                       int64_t rows, int64_t cap, int64_t width, int splits, float scale,
                       float softcap, ErrorBlock* __restrict__ eb,
-                      unsigned long long* __restrict__ row_key, unsigned* __restrict__ row_done) {
+                      unsigned long long* __restrict__ row_key, unsigned* __restrict__ row_done,
+                      const uint8_t* __restrict__ cur, const int32_t* __restrict__ past_len,
+                      int32_t* __restrict__ present_len, int64_t cur_len, int reset) {
   using namespace lat;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lds_u8* ring = (lds_u8*)lds_raw;
@@ -95,7 +102,16 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
   }
   const int64_t b = row / q_seq;
   const int64_t qi = row - b * q_seq;
-  int64_t bound = valid_len ? (int64_t)valid_len[b] : cap;
+  int64_t bound;
+  int64_t app_p = 0;
+  bool app_ok = false;
+  if constexpr (APPEND) {
+    app_p = (int64_t)past_len[b];
+    app_ok = app_p >= 0 && app_p + cur_len <= cap;  // else nothing is appended and the word says so
+    bound = app_p + cur_len;
+  } else {
+    bound = valid_len ? (int64_t)valid_len[b] : cap;
+  }
   bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
   const int64_t ibase = row * width;
   const uint8_t* cache_b = cache + b * cap * ROWB;
@@ -174,7 +190,7 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
       v[k] = load_index<I64>(idx, ibase + c);
       if (check) u[k] = load_index<I64>(idx, ibase + max(c - 1, 0));
     }
-    int last = 0;
+    int last = 0, fresh = 0;
 #pragma unroll
     for (int k = 0; k < PER; k++) {
       const int s = tid + THREADS * k;
@@ -182,6 +198,7 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
       if (c < st1) {
         keys_s[s] = (int)((v[k] >= 0 && v[k] < bound) ? v[k] : 0);  // clamp: a bad row stays in bounds
         if (v[k] != -1) last = s + 1;
+        if (APPEND && v[k] >= app_p && v[k] < bound) fresh = 1;     // selects a row this launch appends
         if (check && column_class(c, v[k], u[k], bound))
           mk = min(mk, (unsigned long long)(row * (width + 1) + c));
       }
@@ -189,11 +206,51 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
     if (check) vhi = st1;
     last = wave_max_nonneg(last);
     if (lane == 0) misc[8 + wave] = last;
+    if constexpr (APPEND) {
+      fresh = wave_max_nonneg(fresh);
+      if (lane == 0) misc[12 + wave] = fresh;
+    }
     if (tid == 0) misc[1] = 0;
   };
+  // the batch's current rows (APPEND): loaded before the index loads, stored
+  // once the first stage's keys are known (by every workgroup of the batch);
+  // a workgroup that selects one of them waits for its own stores before it
+  // gathers, so it reads them back from its own L2
+  constexpr int APP_CHUNKS = ROWB / 16;                          // 72 16-byte chunks per row
+  constexpr int APP_PER = (kFusedAppendRows * APP_CHUNKS + THREADS - 1) / THREADS;
+  uint4 app_v[APP_PER];
+  if constexpr (APPEND) {
+    if (app_ok) {
+      const uint4* src = (const uint4*)(cur + b * cur_len * ROWB);
+#pragma unroll
+      for (int k = 0; k < APP_PER; k++) {
+        const int u = tid + THREADS * k;
+        if (u < cur_len * APP_CHUNKS) app_v[k] = src[u];
+      }
+    }
+  }
   // the first stage's index loads go out before anything waits on memory
   bool staged = c0 < c1;
   if (staged) stage_keys(c0, min(c0 + KEYCAP, c1));
+  bool app_pending = APPEND;  // uniform: the stores and the report are still to be made
+  auto append_rows = [&]() {
+    const bool duty = split == 0 && qi == 0;  // one workgroup per batch reports the append
+    if (app_ok) {
+      uint4* dst = (uint4*)(cache + (b * cap + app_p) * ROWB);
+#pragma unroll
+      for (int k = 0; k < APP_PER; k++) {
+        const int u = tid + THREADS * k;
+        if (u < cur_len * APP_CHUNKS) dst[u] = app_v[k];
+      }
+      if (duty && tid == 0) present_len[b] = (int32_t)(app_p + cur_len);
+    } else if (duty && tid == 0) {
+      atomicOr(&eb->call_word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
+    }
+    app_pending = false;
+  };
+  if constexpr (APPEND) {
+    if (!staged) append_rows();  // no columns here: only the stores (and the report)
+  }
 
   for (;;) {
 #pragma unroll
@@ -213,6 +270,12 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
       __syncthreads();
       const int kcount = max(max(misc[8], misc[9]), max(misc[10], misc[11]));
       const int ntile = (kcount + KT - 1) / KT;
+      if constexpr (APPEND) {
+        if (app_pending) append_rows();
+        // this stage gathers appended rows: every store of this workgroup has
+        // landed before the gathers (the barrier waits for them)
+        if ((misc[12] | misc[13] | misc[14] | misc[15]) != 0) __syncthreads();
+      }
       if (ntile == 0) continue;  // uniform: only padding in these columns
       u32x4_l qraw[KSTEPS];
 
@@ -519,10 +582,12 @@ latent_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
           const int64_t u = col > 0 ? load_index<I64>(idx, ibase + col - 1) : 0;
           cls = column_class(col, v, u, bound);
         }
-        atomicOr(&eb->word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
+        atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
         atomicMin((unsigned long long*)&eb->call_key, k);
       }
-      if (finisher) finish_launch<I64>(eb, idx, width, q_seq, q_seq, valid_len, cap, (unsigned)rows);
+      if (finisher)
+        finish_launch<I64>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap, (unsigned)rows,
+                           reset != 0);
     }
   }
 }
@@ -532,9 +597,9 @@ bool latent_supported(const sa_config& cfg, int64_t index_heads) {
          cfg.max_cache_len <= (int64_t)(0x7fffffffLL / lat::ROWB);
 }
 
-static bool g_latent_attr[8] = {false, false, false, false, false, false, false, false};
+static bool g_latent_attr[12] = {};
 
-sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused) {
+sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused, const AppendArgs* app) {
   using namespace lat;
   const int64_t rows = a.batch * a.q_seq;
   if (rows <= 0) return SA_OK;
@@ -544,15 +609,22 @@ sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits
   const int64_t wgs = rows * splits;
   if (wgs > 0x7fffffffLL) return set_error(c, SA_E_SHAPE, "forward: too many rows for one launch");
   const bool cap_on = a.softcap != 0.0f;
-  const int variant = (a.idx64 ? 1 : 0) + (fused ? 2 : 0) + (cap_on ? 4 : 0);
-  const void* fns[8] = {(const void*)latent_forward_kernel<false, false, false>,
-                        (const void*)latent_forward_kernel<true, false, false>,
-                        (const void*)latent_forward_kernel<false, true, false>,
-                        (const void*)latent_forward_kernel<true, true, false>,
-                        (const void*)latent_forward_kernel<false, false, true>,
-                        (const void*)latent_forward_kernel<true, false, true>,
-                        (const void*)latent_forward_kernel<false, true, true>,
-                        (const void*)latent_forward_kernel<true, true, true>};
+  if (app && (!fused || app->cur_len < 0 || app->cur_len > kFusedAppendRows))
+    return set_error(c, SA_E_STATE, "forward: in-launch append needs fused validation and at most 8 rows");
+  const int variant = app ? 8 + (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0)
+                          : (a.idx64 ? 1 : 0) + (fused ? 2 : 0) + (cap_on ? 4 : 0);
+  const void* fns[12] = {(const void*)latent_forward_kernel<false, false, false, false>,
+                         (const void*)latent_forward_kernel<true, false, false, false>,
+                         (const void*)latent_forward_kernel<false, true, false, false>,
+                         (const void*)latent_forward_kernel<true, true, false, false>,
+                         (const void*)latent_forward_kernel<false, false, true, false>,
+                         (const void*)latent_forward_kernel<true, false, true, false>,
+                         (const void*)latent_forward_kernel<false, true, true, false>,
+                         (const void*)latent_forward_kernel<true, true, true, false>,
+                         (const void*)latent_forward_kernel<false, true, false, true>,
+                         (const void*)latent_forward_kernel<true, true, false, true>,
+                         (const void*)latent_forward_kernel<false, true, true, true>,
+                         (const void*)latent_forward_kernel<true, true, true, true>};
   if (!g_latent_attr[variant]) {
     hipError_t e = hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
     if (e != hipSuccess) return check_hip(c, e, "forward (latent) LDS attribute");
@@ -560,20 +632,29 @@ sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits
   }
   const dim3 grid((unsigned)wgs), block(THREADS);
   prof_begin(c);
-#define SA_LAT(I, F, C)                                                                              \
-  hipLaunchKernelGGL((latent_forward_kernel<I, F, C>), grid, block, LDS_BYTES, c->stream,            \
-                     (const uint16_t*)a.q, (const uint8_t*)a.k, a.idx, a.valid_len,                  \
-                     (uint16_t*)a.y, c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width,    \
-                     splits, a.scale, a.softcap, c->err, c->row_key, c->row_done)
+  const uint8_t* cur = app ? (const uint8_t*)app->cur : nullptr;
+  const int32_t* plen = app ? app->past_len : nullptr;
+  int32_t* prlen = app ? app->present_len : nullptr;
+  const int64_t clen = app ? app->cur_len : 0;
+  const int reset = app ? app->reset : 0;
+#define SA_LAT(I, F, C, A)                                                                            \
+  hipLaunchKernelGGL((latent_forward_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,          \
+                     (const uint16_t*)a.q, (uint8_t*)a.k, a.idx, a.valid_len, (uint16_t*)a.y,         \
+                     c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width, splits, a.scale,     \
+                     a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset)
   switch (variant) {
-    case 0: SA_LAT(false, false, false); break;
-    case 1: SA_LAT(true, false, false); break;
-    case 2: SA_LAT(false, true, false); break;
-    case 3: SA_LAT(true, true, false); break;
-    case 4: SA_LAT(false, false, true); break;
-    case 5: SA_LAT(true, false, true); break;
-    case 6: SA_LAT(false, true, true); break;
-    default: SA_LAT(true, true, true); break;
+    case 0: SA_LAT(false, false, false, false); break;
+    case 1: SA_LAT(true, false, false, false); break;
+    case 2: SA_LAT(false, true, false, false); break;
+    case 3: SA_LAT(true, true, false, false); break;
+    case 4: SA_LAT(false, false, true, false); break;
+    case 5: SA_LAT(true, false, true, false); break;
+    case 6: SA_LAT(false, true, true, false); break;
+    case 7: SA_LAT(true, true, true, false); break;
+    case 8: SA_LAT(false, true, false, true); break;
+    case 9: SA_LAT(true, true, false, true); break;
+    case 10: SA_LAT(false, true, true, true); break;
+    default: SA_LAT(true, true, true, true); break;
   }
 #undef SA_LAT
   prof_end(c);

@@ -642,7 +642,7 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
           const int64_t u = col > 0 ? load_index<I64>(idx, ibase + col - 1) : 0;
           cls = column_class(col, v, u, bound);
         }
-        atomicOr(&eb->word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
+        atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
         atomicMin((unsigned long long*)&eb->call_key, k);
       }
       if (finisher) finish_launch<I64>(eb, idx, width, q_seq, q_seq, valid_len, cap, (unsigned)rows);

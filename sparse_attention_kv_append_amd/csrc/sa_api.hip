@@ -300,13 +300,11 @@ sa_status sparse_attn_query_plan(const sparse_attn_ctx* c, int64_t batch, int64_
   return SA_OK;
 }
 
-sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq,
-                              const void* present_k, const void* present_v,
-                              int64_t cache_capacity, const int32_t* valid_len,
-                              const void* indices, int64_t index_heads, int64_t width, void* y,
-                              int32_t fused_validate) {
-  if (!live(c)) return SA_E_STATE;
-  c->last_error.clear();
+// forward, optionally with the in-launch append of the shared-latent kernel
+static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq,
+                              const void* present_k, const void* present_v, int64_t cache_capacity,
+                              const int32_t* valid_len, const void* indices, int64_t index_heads,
+                              int64_t width, void* y, int32_t fused_validate, const sa::AppendArgs* app) {
   const sa_config& k = c->cfg;
   if (!q || !present_k || !indices || !y) return set_error(c, SA_E_ARG, "forward: q, present_k, indices and y are required");
   const bool latent = k.kv_layout == SA_KV_SHARED_LATENT;
@@ -348,13 +346,63 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
   a.cache_format = k.cache_format;
   a.kv_layout = k.kv_layout;
   a.idx64 = k.index_dtype == SA_IDX_I64;
+  if (app && path != 2) return set_error(c, SA_E_UNSUPPORTED, "step: the in-launch append needs the bf16 shared-latent path");
   switch (path) {
-    case 2: return sa::launch_forward_latent(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
+    case 2: return sa::launch_forward_latent(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0, app);
     case 3: return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
     case 1: return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
     case 4: return sa::launch_forward_gqa(c, a);
     default: return sa::launch_forward_generic(c, a);
   }
+}
+
+sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq,
+                              const void* present_k, const void* present_v,
+                              int64_t cache_capacity, const int32_t* valid_len,
+                              const void* indices, int64_t index_heads, int64_t width, void* y,
+                              int32_t fused_validate) {
+  if (!live(c)) return SA_E_STATE;
+  c->last_error.clear();
+  return forward_impl(c, q, batch, q_seq, present_k, present_v, cache_capacity, valid_len, indices,
+                      index_heads, width, y, fused_validate, nullptr);
+}
+
+sa_status sparse_attn_step(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq, void* cache,
+                           int64_t cache_capacity, const int32_t* past_len, const void* cur, int64_t cur_len,
+                           int32_t* present_len, const void* indices, int64_t index_heads, int64_t width,
+                           void* y, int32_t reset_error) {
+  if (!live(c)) return SA_E_STATE;
+  c->last_error.clear();
+  const sa_config& k = c->cfg;
+  if (k.kv_layout != SA_KV_SHARED_LATENT)
+    return set_error(c, SA_E_UNSUPPORTED, "step: shared-latent caches only (use kv_append + forward)");
+  if (!cache || !cur || !past_len || !present_len)
+    return set_error(c, SA_E_ARG, "step: cache, cur, past_len and present_len are required");
+  if (batch <= 0 || batch > k.max_batch)
+    return set_error(c, SA_E_STATE, fmt("step: batch %lld outside [1, max_batch %lld]", batch, k.max_batch));
+  if (cur_len < 0 || cache_capacity <= 0 || cache_capacity > k.max_cache_len)
+    return set_error(c, SA_E_ARG, "step: negative cur_len or cache capacity outside [1, max_cache_len]");
+  if (cur_len > cache_capacity)
+    return set_error(c, SA_E_CAPACITY, "step: current rows exceed the cache capacity");
+  if (sa::forward_path(k, index_heads) == 2 && cur_len <= sa::kFusedAppendRows) {
+    sa::AppendArgs app;
+    app.cur = cur;
+    app.past_len = past_len;
+    app.present_len = present_len;
+    app.cur_len = cur_len;
+    app.reset = reset_error != 0;
+    return forward_impl(c, q, batch, q_seq, cache, nullptr, cache_capacity, present_len, indices, index_heads,
+                        width, y, 1, &app);
+  }
+  sa_status s = SA_OK;
+  if (reset_error) s = sa::launch_reset_error(c);
+  if (s == SA_OK)
+    s = sparse_attn_kv_append(c, batch, cache, nullptr, cache_capacity, past_len, cur, nullptr, cur_len, 0,
+                              cache, nullptr, cache_capacity, present_len);
+  if (s == SA_OK)
+    s = sparse_attn_forward(c, q, batch, q_seq, cache, nullptr, cache_capacity, present_len, indices,
+                            index_heads, width, y, 1);
+  return s;
 }
 
 sa_status sparse_attn_read_error(sparse_attn_ctx* c, uint32_t* word, uint64_t* first_bad) {

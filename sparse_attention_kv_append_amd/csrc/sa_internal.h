@@ -25,7 +25,7 @@ struct ErrorBlock {  // device layout of the context's error state
   int64_t detail_bound; // cache length of its batch
   int64_t detail_b, detail_h, detail_q, detail_col;  // where it is
   int32_t detail_class; // 1..6, 0 = no detail recorded
-  int32_t pad;
+  uint32_t call_word;   // bits latched by the current forward launch, merged into word by its last arrival
 };
 
 }  // namespace sa
@@ -138,6 +138,17 @@ struct FwdArgs {
   int dtype, cache_format, kv_layout, idx64;
 };
 
+// the in-launch append of the shared-latent LDS-ring kernel: current rows
+// already in the cache's storage format, written in place
+struct AppendArgs {
+  const void* cur;
+  const int32_t* past_len;
+  int32_t* present_len;
+  int64_t cur_len;
+  int reset;  // the launch replaces the error word (reset, then this launch)
+};
+constexpr int64_t kFusedAppendRows = 8;  // current rows per batch the in-launch append takes
+
 bool mla_supported(const sa_config& cfg, int64_t index_heads);
 // the LDS-ring kernel: bf16 shared-latent rows, per-batch cache below 2 GiB
 // (its gathers use 32-bit offsets from the batch's cache base)
@@ -151,7 +162,8 @@ bool gqa_supported(const sa_config& cfg, int64_t index_heads);
 int mla_splits(int64_t rows, int64_t width);
 sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a);
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
-sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused);
+sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
+                                const AppendArgs* app = nullptr);
 sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused);
 sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a);
 sa_status launch_mla_combine(sparse_attn_ctx* c, int64_t rows, int64_t q_seq, int splits, uint16_t* y);

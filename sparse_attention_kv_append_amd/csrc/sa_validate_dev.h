@@ -25,19 +25,29 @@ __device__ __forceinline__ int column_class(int64_t c, int64_t v, int64_t u, int
 // Called by one thread of each of the `expected` participants of a launch
 // that gathers into the context's error block (every block of the validation
 // kernel; the finisher of every row in the forward kernel), after its
-// contributions to eb->call_key are visible. The last one to arrive records
-// the launch's first violation (class, values, position) if no earlier launch
-// since the reset failed, then re-arms the per-launch slot and counter for the
-// next launch on the stream.
+// contributions to eb->call_key / eb->call_word are visible. The last one to
+// arrive merges the launch's bits into the word (with `reset`, the word and
+// the recorded first violation are cleared first: the launch then stands for
+// a reset followed by itself), records the launch's first violation (class,
+// values, position) if no earlier launch since the reset failed, then re-arms
+// the per-launch slots and counter for the next launch on the stream.
 template <bool I64>
 __device__ __forceinline__ void finish_launch(ErrorBlock* __restrict__ eb, const void* __restrict__ idx,
                                               int64_t width, int64_t q_seq, int64_t rows_per_batch,
                                               const int32_t* __restrict__ valid_len, int64_t cache_len,
-                                              unsigned expected) {
+                                              unsigned expected, bool reset = false) {
   __threadfence();
   const unsigned done = atomicAdd(&eb->done_blocks, 1u);
   if (done != expected - 1) return;
   __threadfence();
+  const unsigned bits = atomicExch(&eb->call_word, 0u);
+  if (reset) {
+    eb->word = bits;
+    eb->first_bad = ~0ull;
+    eb->detail_class = 0;
+  } else if (bits) {
+    atomicOr(&eb->word, bits);
+  }
   const unsigned long long key = atomicMin((unsigned long long*)&eb->call_key, ~0ull);
   if (key != ~0ull && eb->detail_class == 0) {
     const int64_t r = (int64_t)(key / (unsigned long long)(width + 1));
