@@ -2,11 +2,12 @@
 """Benchmark of selected-token sparse attention with KV append on one MI355X.
 
 A step is one pass of the whole path over one batch: reset the device error
-word, append the current token(s) to the cache in place, validate the index
-rows, gather + score + softmax + PV (+ split-K combine), store Y. On the bf16
-shared-latent path this is one sparse_attn_step call (one attention launch
-that also appends and resets, plus the combine); elsewhere the three calls
-reset_error_async, kv_append and forward.
+word, append the current token(s) to the cache in place (quantizing them for
+fp8 records), validate the index rows, gather + score + softmax + PV (+ split-K
+combine), store Y. On the shared-latent MFMA paths this is one
+sparse_attn_step call (one attention launch that also appends and resets, plus
+the combine); elsewhere the three calls reset_error_async, kv_append and
+forward.
 
 Default workload (decode, bf16, shared-latent MLA rows): batch 32, one query
 per sequence, 64 query heads sharing one kv head, 576-dim rows (V = first
@@ -153,16 +154,17 @@ class Setup:
         self.path, self.splits = self.ctx.query_plan(B, Sq, 1, w.width)
 
     def fused_step(self):
-        """True when the step is one sparse_attn_step call: the bf16 shared-latent
-        path takes reset + in-place append + forward in one launch."""
-        return self.path == 2 and self.w.cur <= 8
+        """True when the step is one sparse_attn_step call: the shared-latent
+        MFMA paths take reset + in-place append (+ quantize) + forward in one launch."""
+        return self.path in (2, 3) and self.w.cur <= 8
 
     def step(self, i):
         w, c = self.w, self.ctx
         r = i % len(self.idxs)
         if self.fused_step():
             c.step(self.qs[r % len(self.qs)], w.batch, w.q_seq, self.k, w.cap, self.plen, self.cur_k, w.cur,
-                   self.vlen, self.idxs[r], 1, w.width, self.y, reset_error=True)
+                   self.vlen, self.idxs[r], 1, w.width, self.y, reset_error=True,
+                   cur_is_unquantized_bf16=self.fp8)
             return
         c.reset_error_async()
         c.kv_append(w.batch, self.k, self.v, w.cap, self.plen, self.cur_k, self.cur_v, w.cur, self.k,

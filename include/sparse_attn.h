@@ -193,27 +193,32 @@ sa_status sparse_attn_forward(sparse_attn_ctx* ctx, const void* q, int64_t batch
 /* One attention step over a shared-latent cache kept in place (capacity
  * mode): the same as
  *   [sparse_attn_reset_error_async if reset_error]
- *   sparse_attn_kv_append(past = present = cache, cur in the cache's storage
- *                         format, present_len)
+ *   sparse_attn_kv_append(past = present = cache, cur,
+ *                         cur_is_unquantized_bf16, present_len)
  *   sparse_attn_forward(present = cache, valid_len = present_len,
  *                       fused_validate = 1)
  * (IndexShare's capacity-mode present build followed by the operator; the
  * append and the attention row are the ones documented above).
  * cache [B, 1, cache_capacity, row] is read and written; cur [B, 1, cur_len,
- * row] holds bf16 rows (or packed fp8_e4m3_block64 records); past_len [B] is
- * read and present_len [B] written on the device.
- * On the bf16 shared-latent path (query_plan path 2) with cur_len <= 8 this is
- * ONE forward launch (plus the split-K combine): every workgroup writes its
- * batch's current rows into the cache before it gathers, and the launch's
- * last workgroup merges (or, with reset_error, replaces) the error word. In
- * every other case the three calls above run in sequence. Errors: host-side
- * statuses of those calls; device-side bits as they latch them (a capacity
- * failure appends nothing and sets SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY).
+ * .] holds rows in the cache's storage format (bf16 rows, or packed
+ * fp8_e4m3_block64 records), or bf16 rows to quantize when
+ * cur_is_unquantized_bf16 (fp8 caches only); past_len [B] is read and
+ * present_len [B] written on the device.
+ * On the shared-latent MFMA paths (query_plan path 2 or 3) with cur_len <= 8
+ * this is ONE forward launch (plus the split-K combine): every workgroup
+ * writes (or quantizes) its batch's current rows into the cache before it
+ * gathers, and the launch's last workgroup merges (or, with reset_error,
+ * replaces) the error word. In every other case the three calls above run in
+ * sequence. Errors: host-side statuses of those calls; device-side bits as
+ * they latch them (a capacity failure appends nothing and sets
+ * SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY; a non-finite bf16 row is left
+ * unwritten and sets SA_ERR_QUANT_NONFINITE | SA_ERR_APPEND_ANY).
  * SA_E_UNSUPPORTED for separate K/V caches. Asynchronous and capturable. */
 sa_status sparse_attn_step(sparse_attn_ctx* ctx, const void* q, int64_t batch, int64_t q_seq, void* cache,
                            int64_t cache_capacity, const int32_t* past_len, const void* cur,
-                           int64_t cur_len, int32_t* present_len, const void* indices,
-                           int64_t index_heads, int64_t width, void* y, int32_t reset_error);
+                           int64_t cur_len, int32_t cur_is_unquantized_bf16, int32_t* present_len,
+                           const void* indices, int64_t index_heads, int64_t width, void* y,
+                           int32_t reset_error);
 
 /* Zero the context's error word and set first_bad to UINT64_MAX, with a tiny
  * kernel on the stream (no memset node, so it is safe inside a graph). */

@@ -88,7 +88,7 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
         "sparse_attn_kv_append": ([V, I64, V, V, I64, V, V, V, I64, I32, V, V, I64, V], st),
         "sparse_attn_validate_indices": ([V, V, I64, I64, I64, I64, V, I64, V, V, V], st),
         "sparse_attn_forward": ([V, V, I64, I64, V, V, I64, V, V, I64, I64, V, I32], st),
-        "sparse_attn_step": ([V, V, I64, I64, V, I64, V, V, I64, V, V, I64, I64, V, I32], st),
+        "sparse_attn_step": ([V, V, I64, I64, V, I64, V, V, I64, I32, V, V, I64, I64, V, I32], st),
         "sparse_attn_reset_error_async": ([V], st),
         "sparse_attn_read_error": ([V, ctypes.POINTER(ctypes.c_uint32),
                                     ctypes.POINTER(ctypes.c_uint64)], st),
@@ -188,13 +188,14 @@ class Context:
             _ptr(valid_len), _ptr(indices), index_heads, width, _ptr(y), int(fused_validate)))
 
     def step(self, q, batch, q_seq, cache, cache_capacity, past_len, cur, cur_len, present_len, indices,
-             index_heads, width, y, reset_error=True):
+             index_heads, width, y, reset_error=True, cur_is_unquantized_bf16=False):
         """Reset (optional) + in-place append + forward with fused validation
         on a shared-latent cache, one launch where the library can."""
         self._sync_stream()
         self._check(self.lib.sparse_attn_step(
             self.handle, _ptr(q), batch, q_seq, _ptr(cache), cache_capacity, _ptr(past_len), _ptr(cur),
-            cur_len, _ptr(present_len), _ptr(indices), index_heads, width, _ptr(y), int(reset_error)))
+            cur_len, int(cur_is_unquantized_bf16), _ptr(present_len), _ptr(indices), index_heads, width,
+            _ptr(y), int(reset_error)))
 
     def reset_error_async(self):
         self._sync_stream()

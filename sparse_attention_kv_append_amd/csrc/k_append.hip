@@ -6,7 +6,7 @@
 // [0, P) and the new rows land in one contiguous byte range of the present
 // buffer, so each launch copies flat ranges with the widest vector the row
 // width and pointer alignment allow; there is no per-element index math.
-#include "sa_internal.h"
+#include "sa_quant_dev.h"
 
 namespace sa {
 
@@ -117,38 +117,6 @@ sa_status launch_append_copy(sparse_attn_ctx* c, int64_t batch, int64_t heads, i
 
 // ---- fp8_e4m3_block64 quantize-on-append -----------------------------------
 
-// E4M3FN code of x * 2^(127 - e), x given by its fp32 bits: round to nearest
-// even, saturate at 448 (code 0x7E), sign kept (a negative value that rounds
-// to zero gives 0x80). Integer-exact: x = sig * 2^ex, and the quantum of the
-// target binade is 2^q with q = max(floor(log2 v), -6) - 3 (the subnormal
-// quantum 2^-9 below 2^-6). The code bits are (max(lg,-6)+7)*8 + n - 8, which
-// runs continuously across the subnormal/normal seam and binade carries.
-__device__ __forceinline__ uint32_t e4m3fn_encode_scaled(uint32_t w, int e) {
-  const uint32_t sign = (w >> 31) << 7;
-  const uint32_t a = w & 0x7fffffffu;
-  if (a == 0) return sign;
-  const int E = (int)(a >> 23);
-  const uint32_t sig = E ? ((a & 0x7fffffu) | 0x800000u) : (a & 0x7fffffu);
-  const int ex = (E ? E - 150 : -149) + 127 - e;
-  const int lg = (31 - __clz((int)sig)) + ex;
-  const int lgc = lg < -6 ? -6 : lg;
-  const int shift = (lgc - 3) - ex;
-  uint32_t n;
-  if (shift <= 0) {
-    n = sig << (-shift);
-  } else if (shift >= 32) {
-    n = 0;
-  } else {
-    n = sig >> shift;
-    const uint32_t rem = sig & ((1u << shift) - 1u);
-    const uint32_t half = 1u << (shift - 1);
-    if (rem > half || (rem == half && (n & 1u))) n += 1u;
-  }
-  int code = ((lgc + 7) << 3) + (int)n - 8;
-  if (code > 0x7e) code = 0x7e;
-  return sign | (uint32_t)code;
-}
-
 // One wave per new row; lane l owns element l of every 64-value block.
 __global__ void __launch_bounds__(256)
 append_quantize_kernel(const uint16_t* __restrict__ cur, int64_t cur_len,
@@ -170,37 +138,9 @@ append_quantize_kernel(const uint16_t* __restrict__ cur, int64_t cur_len,
   if (present_len && lane == 0 && t == 0 && bh % heads == 0) present_len[b] = (int32_t)(P + cur_len);
   const uint16_t* src = cur + row * dk;
   uint8_t* dst = present + (bh * present_cap + P + t) * rec_bytes;
-  const int nblk = (dk - rope) / 64;
-  // non-finite values anywhere in the row: latch and leave the row unwritten
-  bool bad = false;
-  for (int d = lane; d < dk; d += 64) bad |= ((src[d] & 0x7f80u) == 0x7f80u);
-  if (__ballot(bad) != 0ull) {
-    if (lane == 0) atomicOr(&err->word, SA_ERR_QUANT_NONFINITE | SA_ERR_APPEND_ANY);
-    return;
-  }
-  for (int j = 0; j < nblk; j++) {
-    const uint32_t w = (uint32_t)src[64 * j + lane] << 16;
-    uint32_t amax = w & 0x7fffffffu;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
-    uint32_t code = 0;
-    int e = 127;
-    if (amax != 0) {
-      const int E = (int)(amax >> 23);
-      const int k = E ? E - 127 : (31 - __clz((int)(amax & 0x7fffffu))) - 149;
-      e = k - 8 + 127;
-      e = e < 0 ? 0 : (e > 254 ? 254 : e);
-      code = e4m3fn_encode_scaled(w, e);
-    }
-    if (lane == 0) dst[65 * j] = (uint8_t)e;
-    dst[65 * j + 1 + lane] = (uint8_t)code;
-  }
-  uint8_t* tail = dst + 65 * nblk;
-  for (int i = lane; i < rope; i += 64) {
-    const uint16_t bits = src[dk - rope + i];
-    tail[2 * i] = (uint8_t)(bits & 0xff);
-    tail[2 * i + 1] = (uint8_t)(bits >> 8);
-  }
+  // a row holding a NaN or an infinity is latched and left unwritten
+  if (quantize_row_wave(src, dst, dk, rope, lane) && lane == 0)
+    atomicOr(&err->word, SA_ERR_QUANT_NONFINITE | SA_ERR_APPEND_ANY);
 }
 
 sa_status launch_append_quantize(sparse_attn_ctx* c, int64_t batch, int64_t heads, int64_t dk,

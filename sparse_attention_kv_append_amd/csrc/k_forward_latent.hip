@@ -212,45 +212,24 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
     }
     if (tid == 0) misc[1] = 0;
   };
-  // the batch's current rows (APPEND): loaded before the index loads, stored
-  // once the first stage's keys are known (by every workgroup of the batch);
-  // a workgroup that selects one of them waits for its own stores before it
-  // gathers, so it reads them back from its own L2
-  constexpr int APP_CHUNKS = ROWB / 16;                          // 72 16-byte chunks per row
-  constexpr int APP_PER = (kFusedAppendRows * APP_CHUNKS + THREADS - 1) / THREADS;
-  uint4 app_v[APP_PER];
-  if constexpr (APPEND) {
-    if (app_ok) {
-      const uint4* src = (const uint4*)(cur + b * cur_len * ROWB);
-#pragma unroll
-      for (int k = 0; k < APP_PER; k++) {
-        const int u = tid + THREADS * k;
-        if (u < cur_len * APP_CHUNKS) app_v[k] = src[u];
-      }
-    }
-  }
   // the first stage's index loads go out before anything waits on memory
   bool staged = c0 < c1;
   if (staged) stage_keys(c0, min(c0 + KEYCAP, c1));
-  bool app_pending = APPEND;  // uniform: the stores and the report are still to be made
+
+  // APPEND: the batch's current rows go into the cache from a workgroup that
+  // gathers one of them (before its gathers, and it waits for its stores, so
+  // it reads them back from its own L2), and from one workgroup per batch at
+  // its end (which also reports the append); no other workgroup touches them
+  const bool duty = split == 0 && qi == 0;
+  bool app_done = false;  // uniform
   auto append_rows = [&]() {
-    const bool duty = split == 0 && qi == 0;  // one workgroup per batch reports the append
     if (app_ok) {
+      const uint4* src = (const uint4*)(cur + b * cur_len * ROWB);
       uint4* dst = (uint4*)(cache + (b * cap + app_p) * ROWB);
-#pragma unroll
-      for (int k = 0; k < APP_PER; k++) {
-        const int u = tid + THREADS * k;
-        if (u < cur_len * APP_CHUNKS) dst[u] = app_v[k];
-      }
-      if (duty && tid == 0) present_len[b] = (int32_t)(app_p + cur_len);
-    } else if (duty && tid == 0) {
-      atomicOr(&eb->call_word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
+      for (int u = tid; u < cur_len * (ROWB / 16); u += THREADS) dst[u] = src[u];
     }
-    app_pending = false;
+    app_done = true;
   };
-  if constexpr (APPEND) {
-    if (!staged) append_rows();  // no columns here: only the stores (and the report)
-  }
 
   for (;;) {
 #pragma unroll
@@ -271,10 +250,12 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
       const int kcount = max(max(misc[8], misc[9]), max(misc[10], misc[11]));
       const int ntile = (kcount + KT - 1) / KT;
       if constexpr (APPEND) {
-        if (app_pending) append_rows();
-        // this stage gathers appended rows: every store of this workgroup has
-        // landed before the gathers (the barrier waits for them)
-        if ((misc[12] | misc[13] | misc[14] | misc[15]) != 0) __syncthreads();
+        // this stage gathers appended rows: they are stored and have landed
+        // before the gathers (the barrier waits for the stores)
+        if ((misc[12] | misc[13] | misc[14] | misc[15]) != 0) {
+          if (!app_done) append_rows();
+          __syncthreads();
+        }
       }
       if (ntile == 0) continue;  // uniform: only padding in these columns
       u32x4_l qraw[KSTEPS];
@@ -553,6 +534,15 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
     if (g == 0) {
       part_ml[pr * 2] = m_ref;
       part_ml[pr * 2 + 1] = l_run;
+    }
+  }
+  if constexpr (APPEND) {
+    if (duty) {
+      if (!app_done) append_rows();
+      if (tid == 0) {
+        if (app_ok) present_len[b] = (int32_t)(app_p + cur_len);
+        else atomicOr(&eb->call_word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
+      }
     }
   }
   if constexpr (FUSED) __syncthreads();  // minkey_s is complete

@@ -33,6 +33,7 @@
 // row (IndexShare host-validator rules) while it stages the keys, and the
 // finisher of each row records the row's first violation.
 #include "sa_mfma_dev.h"
+#include "sa_quant_dev.h"
 #include "sa_validate_dev.h"
 
 namespace sa {
@@ -87,14 +88,22 @@ struct PairRaw {
   u32x4_l rope;
 };
 
-template <bool I64, bool FUSED, bool SOFTCAP>
+// APPEND (with FUSED): the launch also appends the batch's cur_len current
+// rows in place (rows past_len[b] ..; bf16 rows quantized when cur_quant,
+// else records copied) and writes present_len[b]; every workgroup writes its
+// batch's new records itself and waits for them before it loads any, so it
+// reads its own writes; with `reset` the launch's last workgroup replaces
+// the error word instead of adding to it.
+template <bool I64, bool FUSED, bool SOFTCAP, bool APPEND>
 __global__ void __launch_bounds__(pk::THREADS, 1)
-pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache,
+pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
                     const void* __restrict__ idx, const int32_t* __restrict__ valid_len,
                     uint16_t* __restrict__ y, float* __restrict__ part_o, float* __restrict__ part_ml,
                     int64_t q_seq, int64_t rows, int64_t cap, int64_t width, int splits, float scale,
                     float softcap, ErrorBlock* __restrict__ eb,
-                    unsigned long long* __restrict__ row_key, unsigned* __restrict__ row_done) {
+                    unsigned long long* __restrict__ row_key, unsigned* __restrict__ row_done,
+                    const void* __restrict__ cur, const int32_t* __restrict__ past_len,
+                    int32_t* __restrict__ present_len, int64_t cur_len, int reset, int cur_quant) {
   using namespace pk;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lds_u8* ring = (lds_u8*)lds_raw;
@@ -123,7 +132,16 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   }
   const int64_t b = row / q_seq;
   const int64_t qi = row - b * q_seq;
-  int64_t bound = valid_len ? (int64_t)valid_len[b] : cap;
+  int64_t bound;
+  int64_t app_p = 0;
+  bool app_ok = false;
+  if constexpr (APPEND) {
+    app_p = (int64_t)past_len[b];
+    app_ok = app_p >= 0 && app_p + cur_len <= cap;  // else nothing is appended and the word says so
+    bound = app_p + cur_len;
+  } else {
+    bound = valid_len ? (int64_t)valid_len[b] : cap;
+  }
   bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
   const int64_t ibase = row * width;
   const uint8_t* cache_b = cache + b * cap * REC;
@@ -204,7 +222,7 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       v[k] = load_index<I64>(idx, ibase + c);
       if (check) u[k] = load_index<I64>(idx, ibase + max(c - 1, 0));
     }
-    int last = 0;
+    int last = 0, fresh = 0;
 #pragma unroll
     for (int k = 0; k < PER; k++) {
       const int s = tid + THREADS * k;
@@ -212,6 +230,7 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       if (c < st1) {
         keys_s[s] = (int)((v[k] >= 0 && v[k] < bound) ? v[k] : 0);  // clamp: a bad row stays in bounds
         if (v[k] != -1) last = s + 1;
+        if (APPEND && v[k] >= app_p && v[k] < bound) fresh = 1;     // selects a row this launch appends
         if (check && column_class(c, v[k], u[k], bound))
           mk = min(mk, (unsigned long long)(row * (width + 1) + c));
       }
@@ -219,11 +238,38 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     if (check) vhi = st1;
     last = wave_max_nonneg(last);
     if (lane == 0) misc[8 + wave] = last;
+    if constexpr (APPEND) {
+      fresh = wave_max_nonneg(fresh);
+      if (lane == 0) misc[12 + wave] = fresh;
+    }
     if (tid == 0) misc[1] = 0;
   };
   // the first stage's index loads go out before anything waits on memory
   bool staged = c0 < c1;
   if (staged) stage_keys(c0, min(c0 + KEYCAP, c1));
+
+  // APPEND: the batch's current rows go into the cache (quantized by one
+  // wave per row, or copied 8 bytes per lane) from a workgroup that loads one
+  // of them (before its loads, and it waits for its stores, so it reads them
+  // back from its own L2), and from one workgroup per batch at its end (which
+  // also reports the append); no other workgroup touches them
+  const bool duty = split == 0 && qi == 0;
+  bool app_done = false;  // uniform
+  bool app_bad = false;   // a current row held a NaN or an infinity (this wave's rows)
+  auto append_rows = [&]() {
+    if (app_ok) {
+      uint8_t* dst0 = cache + (b * cap + app_p) * REC;
+      if (cur_quant) {
+        for (int t = wave; t < cur_len; t += WAVES)
+          app_bad |= quantize_row_wave((const uint16_t*)cur + (b * cur_len + t) * DK, dst0 + t * REC, DK,
+                                       DK - NOPE, lane);
+      } else {
+        const uint2* src = (const uint2*)((const uint8_t*)cur + b * cur_len * REC);
+        for (int u = tid; u < cur_len * (REC / 8); u += THREADS) ((uint2*)dst0)[u] = src[u];
+      }
+    }
+    app_done = true;
+  };
 
   for (;;) {
 #pragma unroll
@@ -245,6 +291,14 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       __syncthreads();
       const int kcount = max(max(misc[8], misc[9]), max(misc[10], misc[11]));
       const int ntile = (kcount + KT - 1) / KT;
+      if constexpr (APPEND) {
+        // this stage loads appended records: they are stored and have landed
+        // before the loads (the barrier waits for the stores)
+        if ((misc[12] | misc[13] | misc[14] | misc[15]) != 0) {
+          if (!app_done) append_rows();
+          __syncthreads();
+        }
+      }
 
       if (ntile == 0) continue;  // uniform: no key in this stage
 
@@ -615,6 +669,16 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       part_ml[(pr0 + 16) * 2 + 1] = l1;
     }
   }
+  if constexpr (APPEND) {
+    if (duty) {
+      if (!app_done) append_rows();
+      if (app_bad && lane == 0) atomicOr(&eb->call_word, SA_ERR_QUANT_NONFINITE | SA_ERR_APPEND_ANY);
+      if (tid == 0) {
+        if (app_ok) present_len[b] = (int32_t)(app_p + cur_len);
+        else atomicOr(&eb->call_word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
+      }
+    }
+  }
   if constexpr (FUSED) __syncthreads();  // minkey_s is complete
 
   // ---- error block: the finisher of each row records the row's first
@@ -645,7 +709,9 @@ pair_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
         atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
         atomicMin((unsigned long long*)&eb->call_key, k);
       }
-      if (finisher) finish_launch<I64>(eb, idx, width, q_seq, q_seq, valid_len, cap, (unsigned)rows);
+      if (finisher)
+        finish_launch<I64>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap, (unsigned)rows,
+                           reset != 0);
     }
   }
 }
@@ -655,9 +721,9 @@ bool pair_supported(const sa_config& cfg, int64_t index_heads) {
          cfg.rope_dim == pk::DK - pk::NOPE && cfg.max_cache_len <= (int64_t)(0x7fffffffLL / pk::REC);
 }
 
-static bool g_pair_attr[8] = {false, false, false, false, false, false, false, false};
+static bool g_pair_attr[12] = {};
 
-sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused) {
+sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused, const AppendArgs* app) {
   using namespace pk;
   const int64_t rows = a.batch * a.q_seq;
   if (rows <= 0) return SA_OK;
@@ -668,15 +734,22 @@ sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, 
   const int64_t wgs = rows * splits;
   if (wgs > 0x7fffffffLL) return set_error(c, SA_E_SHAPE, "forward: too many rows for one launch");
   const bool cap_on = a.softcap != 0.0f;
-  const int variant = (a.idx64 ? 1 : 0) + (fused ? 2 : 0) + (cap_on ? 4 : 0);
-  const void* fns[8] = {(const void*)pair_forward_kernel<false, false, false>,
-                        (const void*)pair_forward_kernel<true, false, false>,
-                        (const void*)pair_forward_kernel<false, true, false>,
-                        (const void*)pair_forward_kernel<true, true, false>,
-                        (const void*)pair_forward_kernel<false, false, true>,
-                        (const void*)pair_forward_kernel<true, false, true>,
-                        (const void*)pair_forward_kernel<false, true, true>,
-                        (const void*)pair_forward_kernel<true, true, true>};
+  if (app && (!fused || app->cur_len < 0 || app->cur_len > kFusedAppendRows))
+    return set_error(c, SA_E_STATE, "forward: in-launch append needs fused validation and at most 8 rows");
+  const int variant = app ? 8 + (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0)
+                          : (a.idx64 ? 1 : 0) + (fused ? 2 : 0) + (cap_on ? 4 : 0);
+  const void* fns[12] = {(const void*)pair_forward_kernel<false, false, false, false>,
+                         (const void*)pair_forward_kernel<true, false, false, false>,
+                         (const void*)pair_forward_kernel<false, true, false, false>,
+                         (const void*)pair_forward_kernel<true, true, false, false>,
+                         (const void*)pair_forward_kernel<false, false, true, false>,
+                         (const void*)pair_forward_kernel<true, false, true, false>,
+                         (const void*)pair_forward_kernel<false, true, true, false>,
+                         (const void*)pair_forward_kernel<true, true, true, false>,
+                         (const void*)pair_forward_kernel<false, true, false, true>,
+                         (const void*)pair_forward_kernel<true, true, false, true>,
+                         (const void*)pair_forward_kernel<false, true, true, true>,
+                         (const void*)pair_forward_kernel<true, true, true, true>};
   if (!g_pair_attr[variant]) {
     hipError_t e = hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
     if (e != hipSuccess) return check_hip(c, e, "forward (fp8 pair) LDS attribute");
@@ -684,20 +757,30 @@ sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, 
   }
   const dim3 grid((unsigned)wgs), block(THREADS);
   prof_begin(c);
-#define SA_PAIR(I, F, C)                                                                             \
-  hipLaunchKernelGGL((pair_forward_kernel<I, F, C>), grid, block, LDS_BYTES, c->stream,              \
-                     (const uint16_t*)a.q, (const uint8_t*)a.k, a.idx, a.valid_len,                  \
-                     (uint16_t*)a.y, c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width,    \
-                     splits, a.scale, a.softcap, c->err, c->row_key, c->row_done)
+  const void* cur = app ? app->cur : nullptr;
+  const int32_t* plen = app ? app->past_len : nullptr;
+  int32_t* prlen = app ? app->present_len : nullptr;
+  const int64_t clen = app ? app->cur_len : 0;
+  const int reset = app ? app->reset : 0;
+  const int quant = app ? app->quant : 0;
+#define SA_PAIR(I, F, C, A)                                                                           \
+  hipLaunchKernelGGL((pair_forward_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,            \
+                     (const uint16_t*)a.q, (uint8_t*)a.k, a.idx, a.valid_len, (uint16_t*)a.y,         \
+                     c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width, splits, a.scale,     \
+                     a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset, quant)
   switch (variant) {
-    case 0: SA_PAIR(false, false, false); break;
-    case 1: SA_PAIR(true, false, false); break;
-    case 2: SA_PAIR(false, true, false); break;
-    case 3: SA_PAIR(true, true, false); break;
-    case 4: SA_PAIR(false, false, true); break;
-    case 5: SA_PAIR(true, false, true); break;
-    case 6: SA_PAIR(false, true, true); break;
-    default: SA_PAIR(true, true, true); break;
+    case 0: SA_PAIR(false, false, false, false); break;
+    case 1: SA_PAIR(true, false, false, false); break;
+    case 2: SA_PAIR(false, true, false, false); break;
+    case 3: SA_PAIR(true, true, false, false); break;
+    case 4: SA_PAIR(false, false, true, false); break;
+    case 5: SA_PAIR(true, false, true, false); break;
+    case 6: SA_PAIR(false, true, true, false); break;
+    case 7: SA_PAIR(true, true, true, false); break;
+    case 8: SA_PAIR(false, true, false, true); break;
+    case 9: SA_PAIR(true, true, false, true); break;
+    case 10: SA_PAIR(false, true, true, true); break;
+    default: SA_PAIR(true, true, true, true); break;
   }
 #undef SA_PAIR
   prof_end(c);

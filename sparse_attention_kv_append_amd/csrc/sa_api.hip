@@ -346,10 +346,11 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
   a.cache_format = k.cache_format;
   a.kv_layout = k.kv_layout;
   a.idx64 = k.index_dtype == SA_IDX_I64;
-  if (app && path != 2) return set_error(c, SA_E_UNSUPPORTED, "step: the in-launch append needs the bf16 shared-latent path");
+  if (app && path != 2 && path != 3)
+    return set_error(c, SA_E_UNSUPPORTED, "step: the in-launch append needs a shared-latent MFMA path");
   switch (path) {
     case 2: return sa::launch_forward_latent(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0, app);
-    case 3: return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0);
+    case 3: return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0, app);
     case 1: return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
     case 4: return sa::launch_forward_gqa(c, a);
     default: return sa::launch_forward_generic(c, a);
@@ -369,8 +370,8 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
 
 sa_status sparse_attn_step(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq, void* cache,
                            int64_t cache_capacity, const int32_t* past_len, const void* cur, int64_t cur_len,
-                           int32_t* present_len, const void* indices, int64_t index_heads, int64_t width,
-                           void* y, int32_t reset_error) {
+                           int32_t cur_is_unquantized_bf16, int32_t* present_len, const void* indices,
+                           int64_t index_heads, int64_t width, void* y, int32_t reset_error) {
   if (!live(c)) return SA_E_STATE;
   c->last_error.clear();
   const sa_config& k = c->cfg;
@@ -384,21 +385,25 @@ sa_status sparse_attn_step(sparse_attn_ctx* c, const void* q, int64_t batch, int
     return set_error(c, SA_E_ARG, "step: negative cur_len or cache capacity outside [1, max_cache_len]");
   if (cur_len > cache_capacity)
     return set_error(c, SA_E_CAPACITY, "step: current rows exceed the cache capacity");
-  if (sa::forward_path(k, index_heads) == 2 && cur_len <= sa::kFusedAppendRows) {
+  if (cur_is_unquantized_bf16 && k.cache_format != SA_CACHE_FP8_E4M3_BLOCK64)
+    return set_error(c, SA_E_DTYPE, "step: cur_is_unquantized_bf16 needs an fp8_e4m3_block64 cache");
+  const int path = sa::forward_path(k, index_heads);
+  if ((path == 2 || path == 3) && cur_len <= sa::kFusedAppendRows) {
     sa::AppendArgs app;
     app.cur = cur;
     app.past_len = past_len;
     app.present_len = present_len;
     app.cur_len = cur_len;
     app.reset = reset_error != 0;
+    app.quant = cur_is_unquantized_bf16 != 0;
     return forward_impl(c, q, batch, q_seq, cache, nullptr, cache_capacity, present_len, indices, index_heads,
                         width, y, 1, &app);
   }
   sa_status s = SA_OK;
   if (reset_error) s = sa::launch_reset_error(c);
   if (s == SA_OK)
-    s = sparse_attn_kv_append(c, batch, cache, nullptr, cache_capacity, past_len, cur, nullptr, cur_len, 0,
-                              cache, nullptr, cache_capacity, present_len);
+    s = sparse_attn_kv_append(c, batch, cache, nullptr, cache_capacity, past_len, cur, nullptr, cur_len,
+                              cur_is_unquantized_bf16, cache, nullptr, cache_capacity, present_len);
   if (s == SA_OK)
     s = sparse_attn_forward(c, q, batch, q_seq, cache, nullptr, cache_capacity, present_len, indices,
                             index_heads, width, y, 1);

@@ -146,6 +146,7 @@ struct AppendArgs {
   int32_t* present_len;
   int64_t cur_len;
   int reset;  // the launch replaces the error word (reset, then this launch)
+  int quant;  // fp8 records: cur holds bf16 rows to quantize (else packed records)
 };
 constexpr int64_t kFusedAppendRows = 8;  // current rows per batch the in-launch append takes
 
@@ -164,7 +165,8 @@ sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a);
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
 sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                                 const AppendArgs* app = nullptr);
-sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused);
+sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
+                              const AppendArgs* app = nullptr);
 sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a);
 sa_status launch_mla_combine(sparse_attn_ctx* c, int64_t rows, int64_t q_seq, int splits, uint16_t* y);
 

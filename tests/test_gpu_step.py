@@ -13,17 +13,22 @@ import pytest
 
 import oracle
 import sa_workloads as W
-from gpu_support import check_close, make_ctx, tt
+from gpu_support import check_close, make_ctx, oracle_records, tt
 
 pytestmark = pytest.mark.gpu
 
 DEC = W.WORKLOADS["decode_bf16"]
+FP8 = W.WORKLOADS["decode_fp8"]
 CASES = {
     "decode_split": DEC.scaled(batch=6, past=1500, topk=700, width=710, capacity=1600),
     "multi_row": DEC.scaled(batch=2, q_seq=4, cur=4, past=300, topk=200, width=210, capacity=320),
     "eight_rows": DEC.scaled(batch=3, q_seq=8, cur=8, past=260, topk=100, width=100, capacity=300),
     "long_cur": DEC.scaled(batch=2, q_seq=12, cur=12, past=300, topk=200, width=210, capacity=330),
+    "fp8_split": FP8.scaled(batch=6, past=1200, topk=650, width=650, capacity=1300),
+    "fp8_multi_row": FP8.scaled(batch=2, q_seq=3, cur=3, past=400, topk=300, width=300, capacity=420),
 }
+# fp8 current rows as packed records (byte append) or as bf16 rows quantized on the device
+QUANT = {"fp8_split": [False, True], "fp8_multi_row": [True]}
 
 
 def banner(msg):
@@ -45,6 +50,12 @@ def setup(w, seed=0):
     inp = W.make_numpy(w)
     idx = with_newest(inp["indices"], w.total)
     gen = torch.Generator(device="cuda").manual_seed(seed)
+    if w.cache_format == W.CACHE_FP8:
+        recs = oracle_records(inp["past_k"][:, :, :w.past], w)
+        cache = torch.randint(0, 120, (w.batch, 1, w.cap, recs.shape[-1]), dtype=torch.uint8, device="cuda",
+                              generator=gen)
+        cache[:, :, :w.past] = tt(recs)
+        return inp, idx, cache
     garbage = torch.randint(-30000, 30000, (w.batch, 1, w.cap, w.dk), dtype=torch.int16, device="cuda",
                             generator=gen)
     cache = garbage.clone()
@@ -52,7 +63,14 @@ def setup(w, seed=0):
     return inp, idx, cache
 
 
-def run_separate(ctx, w, inp, idx, cache, reset=True):
+def cur_rows(w, inp, quant):
+    """Current rows as passed: bf16 rows (bf16 caches, or fp8 to quantize) or records."""
+    if w.cache_format == W.CACHE_FP8 and not quant:
+        return tt(oracle_records(inp["cur_k"], w))
+    return tt(inp["cur_k"])
+
+
+def run_separate(ctx, w, inp, idx, cache, reset=True, quant=False):
     import torch
     B = w.batch
     plen = tt(inp["past_len"])
@@ -60,45 +78,74 @@ def run_separate(ctx, w, inp, idx, cache, reset=True):
     y = torch.full((B, w.hq, w.q_seq, w.dv), float("nan"), dtype=torch.bfloat16, device="cuda")
     if reset:
         ctx.reset_error_async()
-    ctx.kv_append(B, cache, None, w.cap, plen, tt(inp["cur_k"]), None, w.cur, cache, None, w.cap,
-                  present_len=prl)
+    ctx.kv_append(B, cache, None, w.cap, plen, cur_rows(w, inp, quant), None, w.cur, cache, None, w.cap,
+                  present_len=prl, cur_is_unquantized_bf16=quant)
     ctx.forward(tt(inp["q"]), B, w.q_seq, cache, None, w.cap, prl, tt(idx), 1, w.width, y,
                 fused_validate=True)
     word, fb, msg = ctx.read_error()
     return y, prl, word, fb, msg
 
 
-def run_step(ctx, w, inp, idx, cache, reset=True):
+def run_step(ctx, w, inp, idx, cache, reset=True, quant=False):
     import torch
     B = w.batch
     plen = tt(inp["past_len"])
     prl = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     y = torch.full((B, w.hq, w.q_seq, w.dv), float("nan"), dtype=torch.bfloat16, device="cuda")
-    ctx.step(tt(inp["q"]), B, w.q_seq, cache, w.cap, plen, tt(inp["cur_k"]), w.cur, prl, tt(idx), 1,
-             w.width, y, reset_error=reset)
+    ctx.step(tt(inp["q"]), B, w.q_seq, cache, w.cap, plen, cur_rows(w, inp, quant), w.cur, prl, tt(idx), 1,
+             w.width, y, reset_error=reset, cur_is_unquantized_bf16=quant)
     word, fb, msg = ctx.read_error()
     return y, prl, word, fb, msg
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_step_matches_separate_calls(name):
+STEP_CASES = [(n, qz) for n in CASES for qz in QUANT.get(n, [False])]
+
+
+@pytest.mark.parametrize("name,quant", STEP_CASES)
+def test_step_matches_separate_calls(name, quant):
     import torch
     w = CASES[name]
-    banner(f"step {name}")
+    banner(f"step {name} quant={quant}")
     inp, idx, cache = setup(w)
     ctx = make_ctx(w)
     c1, c2 = cache.clone(), cache.clone()
-    ya, pa, wa, _, ma = run_separate(ctx, w, inp, idx, c1)
-    yb, pb, wb, _, mb = run_step(ctx, w, inp, idx, c2)
+    ya, pa, wa, _, ma = run_separate(ctx, w, inp, idx, c1, quant=quant)
+    yb, pb, wb, _, mb = run_step(ctx, w, inp, idx, c2, quant=quant)
     assert wa == 0 and wb == 0, (ma, mb)
     assert torch.equal(pa, pb) and torch.equal(pb, tt(inp["valid_len"]))
     assert torch.equal(c1, c2)
     assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
     # and the oracle
-    pk = oracle.kv_append(inp["past_k"].copy(), inp["past_len"], inp["cur_k"])
-    ref = oracle.forward(inp["q"], pk, None, idx, q_dtype=w.dtype, cache_fmt=w.dtype, kv_layout=w.layout,
+    if w.cache_format == W.CACHE_FP8:
+        pk = oracle.kv_append(oracle_records(inp["past_k"], w), inp["past_len"], oracle_records(inp["cur_k"], w))
+        assert np.array_equal(c2[:, :, :w.total].cpu().numpy(), pk[:, :, :w.total])
+        fmt = oracle.FP8_BLOCK64
+    else:
+        pk = oracle.kv_append(inp["past_k"].copy(), inp["past_len"], inp["cur_k"])
+        fmt = w.dtype
+    ref = oracle.forward(inp["q"], pk, None, idx, q_dtype=w.dtype, cache_fmt=fmt, kv_layout=w.layout,
                          hkv=w.hkv, dv=w.dv, rope=w.rope, scale=w.scale, softcap=w.softcap, threads=8)
     check_close(yb.float().cpu().numpy(), ref, w.dtype, name)
+    ctx.destroy()
+
+
+def test_step_fp8_nonfinite_row_left_unwritten():
+    """A current bf16 row holding an infinity: nothing is written for it and
+    the word says so, in one launch as in the separate calls."""
+    import torch
+    w = CASES["fp8_split"]
+    banner("step fp8 non-finite row")
+    inp, idx, cache = setup(w)
+    inp = dict(inp)
+    inp["cur_k"] = inp["cur_k"].copy()
+    inp["cur_k"][4, 0, 0, 77] = 0x7f80  # +inf in batch 4's current row
+    ctx = make_ctx(w)
+    c1, c2 = cache.clone(), cache.clone()
+    _, _, wa, _, _ = run_separate(ctx, w, inp, idx, c1, quant=True)
+    _, _, wb, _, _ = run_step(ctx, w, inp, idx, c2, quant=True)
+    want = sa_bits("QUANT_NONFINITE") | sa_bits("APPEND_ANY")
+    assert wa & want == want and wb & want == want
+    assert torch.equal(c1, c2) and torch.equal(c2[4, :, w.past], cache[4, :, w.past])
     ctx.destroy()
 
 
