@@ -86,6 +86,9 @@ def _load():
                                             P, ctypes.c_int, I64, I64, I64, I64, I64, I64, I64, I64,
                                             I64, ctypes.c_float, ctypes.c_float, I64, I64, P, P]
         lib.oracle_forward_rows.restype = ctypes.c_int
+        lib.oracle_csa_sink_attention.argtypes = [P, I64, I64, I64, P, I64, P, I64, P, I64, I64,
+                                                  P, P, P, I64, ctypes.c_float, P]
+        lib.oracle_csa_sink_attention.restype = ctypes.c_uint32
         _lib = lib
         return lib
 
@@ -268,6 +271,46 @@ def forward(q, kcache, vcache, indices, *, q_dtype: int, cache_fmt: int, kv_layo
     if errors:
         raise ValueError("oracle forward: index out of range or NaN record")
     return y.reshape(B, Hq, Sq, dv)
+
+
+# ---------------------------------------------------------------- CSA sink attention
+CSA_DIM, CSA_ROPE, CSA_RECORD_BYTES, CSA_WINDOW = 512, 64, 583, 128
+CSA_RANGE, CSA_DENOM, CSA_GEOMETRY = 1, 2, 4
+
+
+def csa_sink_attention(query, current_kv, records, selected, sink, total: int, *,
+                       scale: float = 0.0, bias=None):
+    """CSA ratio-4 selected sink attention (oracle C `oracle_csa_sink_attention`).
+
+    query [B, S, H, 512] fp32; current_kv [B, Tcur, 512] fp32; records
+    [B, Rcap, 583] uint8; selected [B, Hidx, S, K] int32 (index head 0 read);
+    sink [H] fp32; bias None or fp32 of rank <= 4 broadcastable to
+    [B, H, S, Cd + K]. Returns (y [B, S, H, 512] fp32, flags)."""
+    lib = _load()
+    q = np.ascontiguousarray(query, np.float32)
+    ckv = np.ascontiguousarray(current_kv, np.float32)
+    rec = np.ascontiguousarray(records, np.uint8)
+    sel = np.ascontiguousarray(selected, np.int32)
+    snk = np.ascontiguousarray(sink, np.float32)
+    B, S, H, D = q.shape
+    assert D == CSA_DIM and ckv.shape[0] == B and ckv.shape[2] == D
+    assert rec.shape[0] == B and rec.shape[2] == CSA_RECORD_BYTES
+    assert sel.ndim == 4 and sel.shape[0] == B and sel.shape[2] == S and snk.shape == (H,)
+    dims = np.ones(4, np.int64)
+    b = None
+    if bias is not None:
+        b = np.ascontiguousarray(bias, np.float32)
+        assert b.ndim <= 4
+        if b.ndim:
+            dims[4 - b.ndim:] = b.shape
+    y = np.zeros((B, S, H, D), np.float32)
+    flags = lib.oracle_csa_sink_attention(
+        _ptr(q), B, S, H, _ptr(ckv), ckv.shape[1], _ptr(rec), rec.shape[1], _ptr(sel), sel.shape[1],
+        sel.shape[3], _ptr(snk), None if b is None else _ptr(b), _ptr(dims), int(total),
+        float(scale), _ptr(y))
+    if flags == 0xFFFFFFFF:
+        raise MemoryError("oracle csa_sink_attention: allocation failed")
+    return y, int(flags)
 
 
 # ---------------------------------------------------------------- textbook

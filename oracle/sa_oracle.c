@@ -37,6 +37,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ---- storage codes (oracle-local numbering) ----------------------------- */
@@ -444,4 +445,165 @@ int oracle_forward_rows(const void* q, int q_dtype, const void* kcache, const vo
     }
   }
   return 0;
+}
+
+/* ---- CSA ratio-4 selected sink attention ---------------------------------
+ * [CPU] `ratio4_attention` (and the driver that derives its cursors from
+ * total_sequence_length), [CSA] `csa_ratio4_sink_attention`, the head sink of
+ * [CPU] `CompressedSparseAttentionKernel::execute`, and [CPU] `AttentionBias`.
+ *
+ *   q        [B, S, H, 512] fp32
+ *   ckv      [B, Tcur, 512] fp32: the dense rows at absolute positions
+ *            total - Tcur .. total - 1
+ *   records  [B, Rcap, 583] fp8_e4m3_block64 records (448 coded dims + 64
+ *            BF16 tail dims); the first total/4 of each batch are complete
+ *   selected [B, Hidx, S, K] int32; every index-head row holds the same
+ *            selection, index head 0 is read
+ *   sink     [H] fp32, bias NULL or fp32 of the right-aligned shape
+ *            bias_dims[4] (each 1 or the full extent of [B, H, S, Cand])
+ *   y        [B, S, H, 512] fp32
+ * For query s at position p = total - S + s the candidates are the dense
+ * positions max(total - Tcur, p + 1 - 128) .. p (Cd of them counted from the
+ * window start, Cd = min(Tcur, 128) when total == S, else 128), then the K
+ * selected records; Cand = Cd + K. Scores are the ascending fp32 dot times
+ * scale (0 -> 1/sqrtf(512)) plus the bias; a negative index is skipped; the
+ * softmax denominator adds exp(sink[h] - max) after the candidates' max; a
+ * row with no candidate gives zeros.
+ *
+ * Readings (the pages' CPU path raises an error where their device kernel
+ * skips; these are the readings taken here):
+ *  - a selected record >= total/4 is skipped and flagged OR_CSA_RANGE;
+ *  - a denominator that is not a finite positive fp32 flags OR_CSA_DENOM
+ *    (that row's outputs are then meaningless);
+ *  - total < S, total < Tcur, total - Tcur > max(0, total - S + 1 - 128),
+ *    total/4 > Rcap or a bias extent that does not fit flags
+ *    OR_CSA_GEOMETRY and nothing is computed.
+ * Returns the flags; -1 cast to uint32 on an allocation failure.
+ */
+#define OR_CSA_DIM 512
+#define OR_CSA_ROPE 64
+#define OR_CSA_WINDOW 128
+#define OR_CSA_RANGE 1u
+#define OR_CSA_DENOM 2u
+#define OR_CSA_GEOMETRY 4u
+
+uint32_t oracle_csa_sink_attention(const float* q, int64_t batch, int64_t seq, int64_t heads,
+                                   const float* ckv, int64_t cur_len, const uint8_t* records,
+                                   int64_t record_cap, const int32_t* selected, int64_t index_heads,
+                                   int64_t topk, const float* sink, const float* bias,
+                                   const int64_t* bias_dims, int64_t total, float scale, float* y) {
+  const int64_t D = OR_CSA_DIM;
+  const int64_t rec_bytes = oracle_fp8_record_bytes(D, OR_CSA_ROPE); /* 583 */
+  if (total < seq || total < cur_len) return OR_CSA_GEOMETRY;
+  const int64_t start = total - seq;           /* position of query 0 */
+  const int64_t base = total - cur_len;        /* position of ckv row 0 */
+  const int64_t earliest = start + 1 - OR_CSA_WINDOW > 0 ? start + 1 - OR_CSA_WINDOW : 0;
+  if (base > earliest) return OR_CSA_GEOMETRY;
+  const int64_t valid_records = total / 4;
+  if (valid_records > record_cap) return OR_CSA_GEOMETRY;
+  const int64_t dense = start == 0 ? (cur_len < OR_CSA_WINDOW ? cur_len : OR_CSA_WINDOW) : OR_CSA_WINDOW;
+  const int64_t cand = dense + topk;
+  const int64_t target[4] = {batch, heads, seq, cand};
+  if (bias) {
+    for (int a = 0; a < 4; a++)
+      if (bias_dims[a] != 1 && bias_dims[a] != target[a]) return OR_CSA_GEOMETRY;
+  }
+  if (scale == 0.0f) scale = 1.0f / sqrtf((float)D);
+
+  float* score = (float*)malloc(sizeof(float) * (size_t)cand);
+  float* row = (float*)malloc(sizeof(float) * (size_t)D);
+  if (!score || !row) {
+    free(score);
+    free(row);
+    return (uint32_t)-1;
+  }
+  uint32_t flags = 0;
+  for (int64_t b = 0; b < batch; b++) {
+    for (int64_t s = 0; s < seq; s++) {
+      const int64_t pos = start + s;
+      const int64_t wstart = pos + 1 - OR_CSA_WINDOW > base ? pos + 1 - OR_CSA_WINDOW : base;
+      const int32_t* sel = selected + ((b * index_heads + 0) * seq + s) * topk;
+      for (int64_t h = 0; h < heads; h++) {
+        const float* qrow = q + ((b * seq + s) * heads + h) * D;
+        float* yrow = y + ((b * seq + s) * heads + h) * D;
+        float m = -INFINITY;
+        for (int64_t c = 0; c < cand; c++) score[c] = -INFINITY;
+        /* the dense window */
+        for (int64_t c = 0; c < dense; c++) {
+          const int64_t p = wstart + c;
+          if (p > pos) continue;
+          const float* kv = ckv + (b * cur_len + (p - base)) * D;
+          float acc = 0.0f;
+          for (int64_t d = 0; d < D; d++) {
+            float prod = qrow[d] * kv[d];
+            acc = acc + prod;
+          }
+          score[c] = acc * scale;
+        }
+        /* the selected records */
+        for (int64_t j = 0; j < topk; j++) {
+          const int64_t r = sel[j];
+          if (r < 0) continue;
+          if (r >= valid_records) {
+            flags |= OR_CSA_RANGE;
+            continue;
+          }
+          if (oracle_fp8_decode_record(records + (b * record_cap + r) * rec_bytes, D, OR_CSA_ROPE, row) != 0) {
+            /* a NaN scale byte or code: the score is NaN, as the device decode gives */
+            score[dense + j] = NAN;
+            continue;
+          }
+          float acc = 0.0f;
+          for (int64_t d = 0; d < D; d++) {
+            float prod = qrow[d] * row[d];
+            acc = acc + prod;
+          }
+          score[dense + j] = acc * scale;
+        }
+        /* additive bias, broadcast over extents of 1 ([CPU] `AttentionBias::at`) */
+        if (bias) {
+          for (int64_t c = 0; c < cand; c++) {
+            if (score[c] == -INFINITY) continue;
+            const int64_t at[4] = {b, h, s, c};
+            int64_t off = 0;
+            for (int a = 0; a < 4; a++) off = off * bias_dims[a] + (bias_dims[a] == 1 ? 0 : at[a]);
+            score[c] = score[c] + bias[off];
+          }
+        }
+        for (int64_t c = 0; c < cand; c++) m = fmaxf(m, score[c]); /* NaN is passed over */
+        for (int64_t d = 0; d < D; d++) yrow[d] = 0.0f;
+        if (m == -INFINITY) continue;
+        float den = 0.0f;
+        for (int64_t c = 0; c < cand; c++) {
+          if (score[c] == -INFINITY) continue;
+          den = den + (float)exp((double)(score[c] - m));
+        }
+        den = den + (float)exp((double)(sink[h] - m));
+        if (!(den > 0.0f) || isinf(den)) {
+          flags |= OR_CSA_DENOM;
+          continue;
+        }
+        for (int64_t c = 0; c < cand; c++) {
+          if (score[c] == -INFINITY) continue;
+          const float p = (float)exp((double)(score[c] - m)) / den;
+          const float* v;
+          if (c < dense) {
+            v = ckv + (b * cur_len + (wstart + c - base)) * D;
+          } else {
+            const int64_t r = sel[c - dense];
+            if (oracle_fp8_decode_record(records + (b * record_cap + r) * rec_bytes, D, OR_CSA_ROPE, row) != 0)
+              for (int64_t d = 0; d < D; d++) row[d] = NAN;
+            v = row;
+          }
+          for (int64_t d = 0; d < D; d++) {
+            float prod = p * v[d];
+            yrow[d] = yrow[d] + prod;
+          }
+        }
+      }
+    }
+  }
+  free(score);
+  free(row);
+  return flags;
 }

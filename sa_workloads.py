@@ -30,6 +30,18 @@ Workloads (sizes are the ones the pages' operators are exercised at; the
                    128 current, 128 query rows; row q selects every key of
                    [0, 8064 + q] (causal with per-batch offset 8064), width
                    8192; softcap 50; bf16.
+
+CSA ratio-4 sink attention (``CSA_WORKLOADS``, drawn by ``make_csa_numpy``):
+query [B, S, H, 512] and current_kv [B, Tcur, 512] fp32 N(0, 1); the record
+source rows [B, total/4, 512] N(0, 1) rounded to bf16 (a block quantizer turns
+them into 583-byte records); head_sink [H] N(0, 1); query s (position
+total - S + s) selects min(K, (pos + 1) // 4) distinct complete records drawn
+uniformly, in random order (the order a top-k by score leaves), padded with
+-1 and repeated over the index heads.
+
+* ``csa_small``    batch 2, 3 queries, 32 heads, Tcur 140, total 300, K 40.
+* ``csa_decode``   batch 64, 1 query, 64 heads, Tcur 128, total 65536 (16384
+                   records per batch entry), K 512.
 """
 from __future__ import annotations
 
@@ -226,3 +238,67 @@ def torch_normal_bf16(shape, seed: int, device: str = "cuda"):
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+@dataclass(frozen=True)
+class CsaWorkload:
+    name: str
+    batch: int
+    seq: int
+    heads: int
+    cur_len: int        # current_kv rows (absolute positions total - cur_len ..)
+    total: int          # total_sequence_length
+    topk: int           # selected_indices width K
+    index_heads: int = 1
+    record_cap: int = 0  # record rows allocated per batch entry; 0 -> total // 4
+    seed: int = 0
+    scale: float = 0.0   # 0 -> 1/sqrt(512)
+
+    @property
+    def records(self) -> int:
+        return self.total // 4
+
+    @property
+    def cap(self) -> int:
+        return self.record_cap or self.records
+
+    def scaled(self, **kw) -> "CsaWorkload":
+        return replace(self, **kw)
+
+
+CSA_DIM = 512
+CSA_WORKLOADS = {
+    "csa_small": CsaWorkload("csa_small", batch=2, seq=3, heads=32, cur_len=140, total=300,
+                             topk=40, index_heads=2, seed=20),
+    "csa_decode": CsaWorkload("csa_decode", batch=64, seq=1, heads=64, cur_len=128, total=65536,
+                              topk=512, seed=21),
+}
+
+
+def csa_selection(w: CsaWorkload, rng: np.random.Generator) -> np.ndarray:
+    """[B, Hidx, S, K] int32: per query, distinct complete records in random order."""
+    B, S, K = w.batch, w.seq, w.topk
+    out = np.full((B, w.index_heads, S, K), -1, np.int32)
+    for b in range(B):
+        for s in range(S):
+            pos = w.total - S + s
+            avail = (pos + 1) // 4
+            k = min(K, avail)
+            if k > 0:
+                out[b, :, s, :k] = rng.choice(avail, size=k, replace=False)
+    return out
+
+
+def make_csa_numpy(w: CsaWorkload) -> dict:
+    """Host inputs of a CSA workload: query, current_kv, record_rows (fp32
+    values, bf16-representable, [B, total/4, 512]), sink, selected."""
+    rng = np.random.default_rng(w.seed)
+    B, S, H = w.batch, w.seq, w.heads
+    q = rng.standard_normal((B, S, H, CSA_DIM), dtype=np.float32)
+    ckv = rng.standard_normal((B, w.cur_len, CSA_DIM), dtype=np.float32)
+    rows = rng.standard_normal((B, w.records, CSA_DIM), dtype=np.float32)
+    rows = _widen(_bf16_bits(rows), DT_BF16)
+    sink = rng.standard_normal(H, dtype=np.float32)
+    sel = csa_selection(w, rng)
+    return {"workload": w, "query": q, "current_kv": ckv, "record_rows": rows, "sink": sink,
+            "selected": sel}
