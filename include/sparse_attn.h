@@ -80,8 +80,12 @@ enum { SA_IDX_I32 = 0, SA_IDX_I64 = 1 };
                                         past_len[b] + cur_len > present capacity;
                                         that batch's rows are not written         */
 #define SA_ERR_QUANT_NONFINITE 0x80u /* fp8 quantize-on-append met a NaN/Inf     */
+#define SA_ERR_CSA_GEOMETRY 0x100u   /* sparse_attn_csa_forward: total_len does not
+                                        fit the sizes (see there); nothing written */
 #define SA_ERR_INDEX_ANY 512u
 #define SA_ERR_APPEND_ANY 1024u
+#define SA_ERR_CSA_DENOM 0x800u      /* sparse_attn_csa_forward: a softmax
+                                        denominator not finite and positive      */
 
 typedef struct {
   int32_t num_heads;      /* Hq > 0 (IndexShare attr num_heads)                         */
@@ -219,6 +223,57 @@ sa_status sparse_attn_step(sparse_attn_ctx* ctx, const void* q, int64_t batch, i
                            int64_t cur_len, int32_t cur_is_unquantized_bf16, int32_t* present_len,
                            const void* indices, int64_t index_heads, int64_t width, void* y,
                            int32_t reset_error);
+
+/* CSA ratio-4 selected sink attention: the attention stage of the
+ * compressed-sparse-attention operator's ratio-4 path (onnx-runtime-ep-cuda,
+ * src/kernels/compressed_sparse_attention.rs, kernel
+ * `csa_ratio4_sink_attention`; onnx-runtime-ep-cpu, same file,
+ * `ratio4_attention`, the cursor checks of its driver, and `AttentionBias`).
+ * For batch b, query s at position p = total - S + s and head h, the
+ * candidates are
+ *   - the dense causal window: current_kv rows at positions
+ *     max(total - Tcur, p + 1 - 128) .. p, numbered c = 0, 1, ... from the
+ *     window start, of which there are Cd = min(Tcur, 128) when total == S and
+ *     Cd = 128 otherwise (a number above p is no candidate);
+ *   - the K selected records, numbered Cd + j for slot j; a negative index is
+ *     no candidate, an index >= total / 4 (not yet complete) is no candidate
+ *     and sets SA_ERR_RANGE | SA_ERR_INDEX_ANY.
+ * Score = (query . row) * scale (+ bias[b, h, s, c] broadcast over extents of
+ * 1); m = max over the candidates; y = sum_c e^(score_c - m) row_c / (sum_c
+ * e^(score_c - m) + e^(head_sink[h] - m)); a head with no candidate gives
+ * zeros. Arithmetic: the products run on the matrix cores with every fp32
+ * operand split into three bf16 pieces (exact for record rows), fp32
+ * accumulation, fp32 softmax; within 1e-5 of the fp32 definition.
+ *   query       [B, S, H, 512] fp32; H a multiple of 16
+ *   current_kv  [B, Tcur, 512] fp32 (absolute positions total - Tcur .. total - 1)
+ *   records     [B, record_cap, 583] bytes: fp8_e4m3_block64 records of 512
+ *               dims (7 blocks of [E8M0 scale, 64 E4M3FN codes], then 64
+ *               little-endian BF16 values); record_cap * 583 < 2^31
+ *   selected    [B, index_heads, S, K] int32; the rows of index head 0 are
+ *               read (the pages repeat one selection over the index heads);
+ *               1 <= K <= 2048
+ *   head_sink   [H] fp32
+ *   bias        NULL, or fp32 with the right-aligned shape bias_dims[4]
+ *               (host array; each 1 or the extent of [B, H, S, Cd + K]; the
+ *               last extent is checked on the device, as Cd needs total)
+ *   total_len   DEVICE pointer to one int64: total_sequence_length
+ *   scale       0 -> 1/sqrt(512); else finite and > 0
+ *   y           [B, S, H, 512] fp32
+ * Host errors: SA_E_ARG (NULL pointer, size < 1, bad scale), SA_E_SHAPE
+ * (bias extents), SA_E_UNSUPPORTED (H % 16, K > 2048, Tcur * 2048 or
+ * record_cap * 583 >= 2^31). Device: SA_ERR_CSA_GEOMETRY when total < S,
+ * total < Tcur, total - Tcur > max(0, total - S + 1 - 128), total / 4 >
+ * record_cap or the bias's last extent is neither 1 nor Cd + K (then nothing
+ * is written); SA_ERR_CSA_DENOM when a denominator is not finite and positive
+ * (NaN or overflowing inputs). Uses the context's stream and error word only
+ * (not its config). Asynchronous and capturable. */
+sa_status sparse_attn_csa_forward(sparse_attn_ctx* ctx, const float* query, int64_t batch,
+                                  int64_t q_seq, int64_t heads, const float* current_kv,
+                                  int64_t cur_len, const uint8_t* records, int64_t record_cap,
+                                  const int32_t* selected, int64_t index_heads, int64_t topk,
+                                  const float* head_sink, const float* bias,
+                                  const int64_t* bias_dims, const int64_t* total_len, float scale,
+                                  float* y);
 
 /* Zero the context's error word and set first_bad to UINT64_MAX, with a tiny
  * kernel on the stream (no memset node, so it is safe inside a graph). */

@@ -29,6 +29,7 @@ SA_ERR_SENTINEL, SA_ERR_AFTER_PAD, SA_ERR_RANGE = 0x01, 0x02, 0x04
 SA_ERR_DUPLICATE, SA_ERR_ORDER, SA_ERR_ALL_PAD = 0x08, 0x10, 0x20
 SA_ERR_APPEND_CAPACITY, SA_ERR_QUANT_NONFINITE = 0x40, 0x80
 SA_ERR_INDEX_ANY, SA_ERR_APPEND_ANY = 512, 1024
+SA_ERR_CSA_GEOMETRY, SA_ERR_CSA_DENOM = 0x100, 0x800
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_DTYPE", 4: "SA_E_CAPACITY",
                 5: "SA_E_UNSUPPORTED", 6: "SA_E_HIP", 7: "SA_E_STATE", 8: "SA_E_INDEX"}
@@ -36,6 +37,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_DTYPE", 4: 
 EXPORTS = [
     "sparse_attn_create", "sparse_attn_destroy", "sparse_attn_set_stream",
     "sparse_attn_kv_append", "sparse_attn_validate_indices", "sparse_attn_forward", "sparse_attn_step",
+    "sparse_attn_csa_forward",
     "sparse_attn_reset_error_async", "sparse_attn_read_error", "sparse_attn_last_error",
     "sparse_attn_query_plan", "sparse_attn_profile_enable", "sparse_attn_profile_read",
     "sparse_attn_version",
@@ -89,6 +91,8 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
         "sparse_attn_validate_indices": ([V, V, I64, I64, I64, I64, V, I64, V, V, V], st),
         "sparse_attn_forward": ([V, V, I64, I64, V, V, I64, V, V, I64, I64, V, I32], st),
         "sparse_attn_step": ([V, V, I64, I64, V, I64, V, V, I64, I32, V, V, I64, I64, V, I32], st),
+        "sparse_attn_csa_forward": ([V, V, I64, I64, I64, V, I64, V, I64, V, I64, I64, V, V, V, V,
+                                     ctypes.c_float, V], st),
         "sparse_attn_reset_error_async": ([V], st),
         "sparse_attn_read_error": ([V, ctypes.POINTER(ctypes.c_uint32),
                                     ctypes.POINTER(ctypes.c_uint64)], st),
@@ -196,6 +200,24 @@ class Context:
             self.handle, _ptr(q), batch, q_seq, _ptr(cache), cache_capacity, _ptr(past_len), _ptr(cur),
             cur_len, int(cur_is_unquantized_bf16), _ptr(present_len), _ptr(indices), index_heads, width,
             _ptr(y), int(reset_error)))
+
+    def csa_forward(self, query, current_kv, records, selected, head_sink, total_len, y, *,
+                    scale=0.0, bias=None):
+        """CSA ratio-4 selected sink attention. query [B, S, H, 512] f32,
+        current_kv [B, Tcur, 512] f32, records [B, Rcap, 583] u8, selected
+        [B, Hidx, S, K] i32, head_sink [H] f32, total_len int64 device tensor
+        of one element, y [B, S, H, 512] f32, bias None or f32 of rank <= 4."""
+        B, S, H, _ = query.shape
+        bias_dims = None
+        if bias is not None:
+            dims = [1] * (4 - bias.dim()) + list(bias.shape)
+            bias_dims = (ctypes.c_int64 * 4)(*dims)
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_csa_forward(
+            self.handle, _ptr(query), B, S, H, _ptr(current_kv), current_kv.shape[1], _ptr(records),
+            records.shape[1], _ptr(selected), selected.shape[1], selected.shape[3], _ptr(head_sink),
+            _ptr(bias), None if bias_dims is None else ctypes.cast(bias_dims, ctypes.c_void_p),
+            _ptr(total_len), float(scale), _ptr(y)))
 
     def reset_error_async(self):
         self._sync_stream()

@@ -68,17 +68,6 @@ __host__ __device__ constexpr int pair_step_reads(int j) {
   return (j < pk::KSTEPS ? 1 : 0) + (j < pk::DVT ? 2 : 0);
 }
 
-// E4M3FN code c times 2^(e - 127) as bf16 bits, exact where representable
-// (round to nearest even otherwise); the NaN code and scale byte 255 give NaN.
-__device__ __forceinline__ uint32_t fp8_code_to_bf16_exact(uint32_t c, uint32_t e) {
-  const uint32_t mag = c & 0x7fu;
-  if (mag == 0x7fu || e == 255u) return 0x7fc0u;
-  const uint32_t E = mag >> 3, M = mag & 7u;
-  float v = E ? __uint_as_float(((E + 120u) << 23) | (M << 20)) : (float)M * 0.001953125f;
-  v = ldexpf(v, (int)e - 127);
-  return (uint32_t)f32_to_bf16_rne(v) | ((c & 0x80u) << 8);
-}
-
 // one lane's share of one tile's records: 17 words from the aligned word
 // holding its block's first code, the scale byte, 16 RoPE bytes
 struct PairRaw {

@@ -410,6 +410,57 @@ sa_status sparse_attn_step(sparse_attn_ctx* c, const void* q, int64_t batch, int
   return s;
 }
 
+sa_status sparse_attn_csa_forward(sparse_attn_ctx* c, const float* query, int64_t batch, int64_t q_seq,
+                                  int64_t heads, const float* current_kv, int64_t cur_len,
+                                  const uint8_t* records, int64_t record_cap, const int32_t* selected,
+                                  int64_t index_heads, int64_t topk, const float* head_sink,
+                                  const float* bias, const int64_t* bias_dims, const int64_t* total_len,
+                                  float scale, float* y) {
+  if (!live(c)) return SA_E_STATE;
+  c->last_error.clear();
+  if (!query || !current_kv || !records || !selected || !head_sink || !total_len || !y)
+    return set_error(c, SA_E_ARG, "csa_forward: a required pointer is NULL");
+  if (batch < 1 || q_seq < 1 || heads < 1 || cur_len < 1 || record_cap < 1 || index_heads < 1 || topk < 1)
+    return set_error(c, SA_E_ARG, "csa_forward: every size must be at least 1");
+  if (!isfinite(scale) || scale < 0.0f) return set_error(c, SA_E_ARG, "csa_forward: scale must be finite and >= 0");
+  if (heads % 16 != 0) return set_error(c, SA_E_UNSUPPORTED, "csa_forward: heads must be a multiple of 16");
+  if (topk > 2048) return set_error(c, SA_E_UNSUPPORTED, "csa_forward: selected width above 2048");
+  if (cur_len * 2048 >= (1LL << 31) || record_cap * 583 >= (1LL << 31))
+    return set_error(c, SA_E_UNSUPPORTED, "csa_forward: current_kv or record buffer of a batch entry >= 2 GiB");
+  if (batch * q_seq * (heads / 16) >= (1LL << 31) || batch * index_heads * q_seq * topk >= (1LL << 40))
+    return set_error(c, SA_E_UNSUPPORTED, "csa_forward: grid too large");
+  sa::CsaArgs a;
+  a.q = query;
+  a.ckv = current_kv;
+  a.rec = records;
+  a.sel = selected;
+  a.sink = head_sink;
+  a.bias = bias;
+  a.total = total_len;
+  a.y = y;
+  a.batch = batch;
+  a.q_seq = q_seq;
+  a.heads = heads;
+  a.cur_len = cur_len;
+  a.record_cap = record_cap;
+  a.index_heads = index_heads;
+  a.topk = topk;
+  a.scale = scale == 0.0f ? 1.0f / sqrtf(512.0f) : scale;
+  for (int i = 0; i < 4; i++) a.bias_dims[i] = 1;
+  if (bias) {
+    if (!bias_dims) return set_error(c, SA_E_ARG, "csa_forward: bias needs bias_dims");
+    const int64_t full[3] = {batch, heads, q_seq};
+    for (int i = 0; i < 3; i++)
+      if (bias_dims[i] != 1 && bias_dims[i] != full[i])
+        return set_error(c, SA_E_SHAPE, fmt("csa_forward: bias extent %d is %lld, not 1 or %lld", i,
+                                            (long long)bias_dims[i], (long long)full[i]));
+    if (bias_dims[3] != 1 && (bias_dims[3] < topk + 1 || bias_dims[3] > topk + 128))
+      return set_error(c, SA_E_SHAPE, "csa_forward: bias last extent is neither 1 nor (window candidates + K)");
+    for (int i = 0; i < 4; i++) a.bias_dims[i] = bias_dims[i];
+  }
+  return sa::launch_csa_attention(c, a);
+}
+
 sa_status sparse_attn_read_error(sparse_attn_ctx* c, uint32_t* word, uint64_t* first_bad) {
   if (!live(c)) return SA_E_STATE;
   sa::ErrorBlock eb;
@@ -444,6 +495,18 @@ sa_status sparse_attn_read_error(sparse_attn_ctx* c, uint32_t* word, uint64_t* f
   if (eb.word & SA_ERR_QUANT_NONFINITE) {
     if (!msg.empty()) msg += "; ";
     msg += "kv_append: non-finite value in a row given to the fp8 quantizer";
+  }
+  if ((eb.word & SA_ERR_RANGE) && eb.detail_class == 0) {
+    if (!msg.empty()) msg += "; ";
+    msg += "csa_forward: a selected record index is not yet complete (>= total_len / 4)";
+  }
+  if (eb.word & SA_ERR_CSA_GEOMETRY) {
+    if (!msg.empty()) msg += "; ";
+    msg += "csa_forward: total_len does not fit the query, current_kv, record or bias sizes";
+  }
+  if (eb.word & SA_ERR_CSA_DENOM) {
+    if (!msg.empty()) msg += "; ";
+    msg += "csa_forward: a softmax denominator is not finite and positive";
   }
   if (msg.empty()) msg = fmt("device error word 0x%llx", (long long)eb.word);
   c->last_error = msg;

@@ -168,6 +168,21 @@ sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits
 sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                               const AppendArgs* app = nullptr);
 sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a);
+// CSA ratio-4 selected sink attention (512-dim rows, 583-byte records)
+struct CsaArgs {
+  const float* q;          // [B, S, H, 512]
+  const float* ckv;        // [B, Tcur, 512]
+  const uint8_t* rec;      // [B, record_cap, 583]
+  const int32_t* sel;      // [B, index_heads, S, topk]
+  const float* sink;       // [H]
+  const float* bias;       // NULL or right-aligned [bias_dims]
+  const int64_t* total;    // device: total_sequence_length
+  float* y;                // [B, S, H, 512]
+  int64_t batch, q_seq, heads, cur_len, record_cap, index_heads, topk;
+  int64_t bias_dims[4];
+  float scale;
+};
+sa_status launch_csa_attention(sparse_attn_ctx* c, const CsaArgs& a);
 sa_status launch_mla_combine(sparse_attn_ctx* c, int64_t rows, int64_t q_seq, int splits, uint16_t* y);
 
 sa_status set_error(sparse_attn_ctx* c, sa_status s, const std::string& msg);

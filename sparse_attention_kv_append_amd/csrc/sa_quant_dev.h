@@ -102,4 +102,30 @@ __device__ __forceinline__ bool quantize_row_wave(const uint16_t* __restrict__ s
   return false;
 }
 
+// E4M3FN code c times 2^(e - 127) as bf16 bits, exact where representable
+// (round to nearest even otherwise); the NaN code and scale byte 255 give NaN.
+__device__ __forceinline__ uint32_t fp8_code_to_bf16_exact(uint32_t c, uint32_t e) {
+  const uint32_t mag = c & 0x7fu;
+  if (mag == 0x7fu || e == 255u) return 0x7fc0u;
+  const uint32_t E = mag >> 3, M = mag & 7u;
+  float v = E ? __uint_as_float(((E + 120u) << 23) | (M << 20)) : (float)M * 0.001953125f;
+  v = ldexpf(v, (int)e - 127);
+  return (uint32_t)f32_to_bf16_rne(v) | ((c & 0x80u) << 8);
+}
+
+// E4M3FN decode of one packed word of four codes at block scale byte e into
+// two words of bf16 pairs (codes 0,1 -> lo; 2,3 -> hi). For scale bytes
+// 10..246 v_cvt_scalef32_pk_bf16_fp8 is exact (every code times 2^(e-127) is a
+// bf16 normal); other bytes take the integer path above.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t cw, uint32_t e, uint32_t& lo, uint32_t& hi) {
+  if (e >= 10u && e <= 246u) {
+    const float s = __uint_as_float(e << 23);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw, s, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw, s, true));
+  } else {
+    lo = fp8_code_to_bf16_exact(cw & 0xffu, e) | (fp8_code_to_bf16_exact((cw >> 8) & 0xffu, e) << 16);
+    hi = fp8_code_to_bf16_exact((cw >> 16) & 0xffu, e) | (fp8_code_to_bf16_exact(cw >> 24, e) << 16);
+  }
+}
+
 }  // namespace sa
