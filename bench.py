@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--workload", default="decode_bf16",
-                   choices=["decode_bf16", "decode_fp8", "prefill_bf16", "dense_gqa"])
+                   choices=["decode_bf16", "decode_fp8", "prefill_bf16", "dense_gqa", "csa_decode"])
     p.add_argument("--rotate", type=int, default=8, help="independent (query, index) sets")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
@@ -68,10 +68,12 @@ def parse():
 # only used while their hash is unchanged)
 KERNEL_SOURCES = {
     "latent_forward_kernel": ["k_forward_latent.hip", "sa_internal.h", "sa_validate_dev.h", "sa_mfma_dev.h"],
-    "pair_forward_kernel": ["k_forward_pair.hip", "sa_internal.h", "sa_validate_dev.h", "sa_mfma_dev.h"],
+    "pair_forward_kernel": ["k_forward_pair.hip", "sa_internal.h", "sa_validate_dev.h", "sa_mfma_dev.h",
+                            "sa_quant_dev.h"],
     "mla_forward_kernel": ["k_forward_mla.hip", "sa_internal.h"],
     "generic_forward_kernel": ["k_forward_generic.hip", "sa_internal.h"],
     "gqa_forward_kernel": ["k_forward_gqa.hip", "sa_internal.h", "sa_mfma_dev.h"],
+    "csa_attention_kernel": ["k_csa_attention.hip", "sa_internal.h", "sa_mfma_dev.h", "sa_quant_dev.h"],
 }
 CALIB_BYTES = 256 << 20
 
@@ -203,10 +205,216 @@ class Setup:
         append = w.batch * w.hkv * w.cur * (row_bytes + (w.dv * 2 if self.v is not None else 0))
         return kw["bytes"] + ybytes + 2 * append
 
+    # ---- reporting
+    def roofline(self, kw, k_avg_s):
+        w = self.w
+        if w.pattern == "causal_prefill" or self.path == 4:
+            return "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", kw["flops"] / k_avg_s / 1e12
+        if w.layout == self.W.LAYOUT_SEPARATE:
+            return "alu", VALU_FP32_PEAK_TFLOPS, "TFLOP/s", kw["flops"] / k_avg_s / 1e12
+        return "hbm", HBM_PEAK_GBS, "GB/s", kw["bytes"] / k_avg_s / 1e9
+
+    def dtype_name(self):
+        return "fp8" if self.fp8 else {0: "f32", 1: "f16", 2: "bf16"}[self.w.dtype]
+
+    def config(self, use_graph, nset, tokens, ms_per_step):
+        w = self.w
+        return {"workload": f"{w.name}: batch {w.batch}, q_seq {w.q_seq}, {w.hq} q heads / "
+                            f"{w.hkv} kv heads, Dk {w.dk} / Dv {w.dv}, past {w.past} + {w.cur}, "
+                            f"index width {w.width}, {'graph replay' if use_graph else 'eager'}, "
+                            f"{nset} rotating index sets",
+                "selected_tokens_per_step": tokens, "splits": self.splits,
+                "step_calls": ("sparse_attn_step (reset + append + forward in one launch)" if self.fused_step()
+                               else "reset_error_async + kv_append + forward"),
+                "step_hbm_GBps": self.step_bytes() / (ms_per_step / 1e3) / 1e9}
+
+    def cpu_baseline(self, target_s):
+        return cpu_baseline(self, target_s)
+
+
+class CsaSetup:
+    """Device-resident inputs and the step closure of CSA ratio-4 selected sink
+    attention: fp32 query and current_kv, 583-byte fp8 records made from bf16
+    rows by the library's quantize-on-append, a random-order top-k selection of
+    complete records per query, a head sink. The timed steps rotate over R
+    (query, current_kv, selection) sets so the gathered bytes of one rotation
+    exceed the Infinity Cache."""
+
+    path = 5
+    splits = 1
+
+    def __init__(self, name, rotate):
+        import numpy as np
+        import torch
+
+        import sa_workloads as W
+        import sparse_attention_kv_append_amd as sa
+        self.np, self.torch, self.W, self.sa = np, torch, W, sa
+        self.w = w = W.CSA_WORKLOADS[name]
+        self.name = name
+        self.R = rotate
+        dev = "cuda"
+        B, S, H, T = w.batch, w.seq, w.heads, w.cur_len
+        self.ctx = sa.Context(num_heads=16, kv_num_heads=1, head_dim_qk=64, head_dim_v=64, dtype=sa.SA_F32)
+        seed = w.seed
+        self.chunk = 4096
+        self.chunk_seed = lambda c: seed * 1000 + c
+        qctx = sa.Context(num_heads=1, kv_num_heads=1, head_dim_qk=512, head_dim_v=512, dtype=sa.SA_BF16,
+                          kv_layout=sa.SA_KV_SHARED_LATENT, cache_format=sa.SA_CACHE_FP8_E4M3_BLOCK64,
+                          rope_dim=64, max_batch=B, max_q_seq=1, max_index_width=1, max_cache_len=w.cap)
+        rec = torch.zeros((B, 1, w.cap, 583), dtype=torch.uint8, device=dev)
+        for t0 in range(0, w.records, self.chunk):
+            n = min(self.chunk, w.records - t0)
+            rows = W.torch_normal_bf16((B, 1, n, 512), self.chunk_seed(t0 // self.chunk), dev)
+            plen = torch.full((B,), t0, dtype=torch.int32, device=dev)
+            qctx.kv_append(B, rec, None, w.cap, plen, rows, None, n, rec, None, w.cap,
+                           cur_is_unquantized_bf16=True)
+        torch.cuda.synchronize()
+        word, _, msg = qctx.read_error()
+        assert word == 0, msg
+        qctx.destroy()
+        self.rec = rec.view(B, w.cap, 583)
+        self.qs, self.ckvs, self.idx_host, self.idxs = [], [], [], []
+        for r in range(self.R):
+            self.qs.append(W.torch_normal_f32((B, S, H, 512), seed * 1000 + 500 + r, dev))
+            self.ckvs.append(W.torch_normal_f32((B, T, 512), seed * 1000 + 700 + r, dev))
+            sel = W.csa_selection(w, np.random.default_rng(seed * 100 + r))
+            self.idx_host.append(sel)
+            self.idxs.append(torch.from_numpy(sel).to(dev))
+        self.sink_host = np.random.default_rng(seed).standard_normal(H).astype(np.float32)
+        self.sink = torch.from_numpy(self.sink_host).to(dev)
+        self.total = torch.tensor([w.total], dtype=torch.int64, device=dev)
+        self.y = torch.empty((B, S, H, 512), dtype=torch.float32, device=dev)
+        self.fp8 = True
+
+    def fused_step(self):
+        return False
+
+    def step(self, i):
+        r = i % len(self.idxs)
+        self.ctx.reset_error_async()
+        self.ctx.csa_forward(self.qs[r], self.ckvs[r], self.rec, self.idxs[r], self.sink, self.total, self.y,
+                             scale=self.w.scale)
+
+    def _dense(self):
+        """Dense candidates per query (the window rows at or before it)."""
+        w = self.w
+        start, base = w.total - w.seq, w.total - w.cur_len
+        dn = min(w.cur_len, 128) if start == 0 else 128
+        out = []
+        for s in range(w.seq):
+            pos = start + s
+            ws = max(base, pos + 1 - 128)
+            out.append(min(dn, pos - ws + 1))
+        return out
+
+    def tokens_per_step(self):
+        """Candidates attended per step (dense window rows + valid selected
+        records), all heads of a (batch, query) counted once."""
+        w = self.w
+        sel = sum(int(((ih[:, 0] >= 0) & (ih[:, 0] < w.records)).sum()) for ih in self.idx_host) / len(self.idx_host)
+        return w.batch * sum(self._dense()) + sel
+
+    def kernel_work(self):
+        w = self.w
+        nsel = sum(int((ih[:, 0] >= 0).sum()) for ih in self.idx_host) / len(self.idx_host)
+        ndense = w.batch * sum(self._dense())
+        qy = 2 * w.batch * w.seq * w.heads * 512 * 4
+        # current_kv rows: a (batch) reads the union of its queries' windows once
+        rows = w.batch * min(w.cur_len, sum(self._dense()) if w.seq == 1 else w.cur_len)
+        gather = nsel * 583 + rows * 512 * 4
+        ibytes = w.batch * w.seq * w.topk * 4
+        flops = (nsel + ndense) * w.heads * 2 * 2 * 512
+        return dict(bytes=qy + gather + ibytes, gather_bytes=gather, flops=flops)
+
+    def step_bytes(self):
+        return self.kernel_work()["bytes"]
+
+    def roofline(self, kw, k_avg_s):
+        return "hbm", HBM_PEAK_GBS, "GB/s", kw["bytes"] / k_avg_s / 1e9
+
+    def dtype_name(self):
+        return "f32"
+
+    def config(self, use_graph, nset, tokens, ms_per_step):
+        w = self.w
+        return {"workload": f"{w.name}: CSA ratio-4 selected sink attention, batch {w.batch}, q_seq {w.seq}, "
+                            f"{w.heads} heads, dim 512, current_kv {w.cur_len} fp32 rows (window 128), "
+                            f"total {w.total} ({w.records} fp8_e4m3_block64 583-byte records), top-{w.topk} "
+                            f"selected, {'graph replay' if use_graph else 'eager'}, {nset} rotating sets",
+                "candidates_per_step": tokens, "splits": 1,
+                "step_calls": "reset_error_async + csa_forward",
+                "step_hbm_GBps": self.step_bytes() / (ms_per_step / 1e3) / 1e9}
+
+    def oracle_inputs(self, bs):
+        """The oracle's inputs for batch entries bs (rotation set 0), from the
+        seeded generators: query and current_kv as drawn, the selected records
+        packed by the oracle's own quantizer from the generator's bf16 rows (the
+        other records are zeros, never read)."""
+        import oracle
+        np, torch, w = self.np, self.torch, self.w
+        sels = [self.idx_host[0][b:b + 1] for b in bs]
+        needs = [np.unique(sel[sel >= 0]) for sel in sels]
+        recs = [np.zeros((1, w.cap, 583), np.uint8) for _ in bs]
+        chunks = np.unique(np.concatenate([n // self.chunk for n in needs]))
+        for c in chunks:
+            t0 = int(c) * self.chunk
+            n = min(self.chunk, w.records - t0)
+            rows = self.W.torch_normal_bf16((w.batch, 1, n, 512), self.chunk_seed(int(c)), "cuda")
+            for j, b in enumerate(bs):
+                keys = needs[j][(needs[j] >= t0) & (needs[j] < t0 + n)]
+                if len(keys):
+                    v = rows[b, 0].index_select(0, torch.from_numpy(keys - t0).cuda()).float().cpu().numpy()
+                    recs[j][0, keys] = oracle.fp8_pack_rows(v, 64)
+            del rows
+        return [dict(query=self.qs[0][b:b + 1].cpu().numpy(), current_kv=self.ckvs[0][b:b + 1].cpu().numpy(),
+                     records=recs[j], selected=sels[j], sink=self.sink_host) for j, b in enumerate(bs)]
+
+    def oracle_y(self, inp):
+        import oracle
+        y, flags = oracle.csa_sink_attention(inp["query"], inp["current_kv"], inp["records"], inp["selected"],
+                                             inp["sink"], self.w.total, scale=self.w.scale)
+        assert flags == 0, flags
+        return y
+
+    def cpu_baseline(self, target_s):
+        """The oracle (unchanged) on a bounded sample: the first batch entries of
+        the same workload, one per thread (each C call releases the GIL),
+        repeated until the target time is reached."""
+        import threading
+        w = self.w
+        threads = max(1, min(16, os.cpu_count() or 1))
+        nb = min(w.batch, threads)
+        inputs = self.oracle_inputs(list(range(nb)))
+        ndense = sum(self._dense())
+        cands = sum(ndense + int((inp["selected"][0, 0] >= 0).sum()) for inp in inputs)
+
+        def run():
+            t0 = time.perf_counter()
+            ts = [threading.Thread(target=self.oracle_y, args=(inp,)) for inp in inputs]
+            for t in ts:
+                t.start()
+            for t in ts:
+                t.join()
+            return time.perf_counter() - t0
+
+        reps, total_t = 0, 0.0
+        while total_t < target_s and reps < 200:
+            total_t += run()
+            reps += 1
+        return {"value": cands * reps / total_t, "unit": "candidates/s", "cores": nb, "kind": "oracle",
+                "sample": f"the first {nb} (batch, query) rows of the same workload x {reps}, one thread each, "
+                          f"all {w.heads} heads, {cands * reps} candidates, {total_t:.1f} s of oracle time"}
+
+
+def make_setup(name, rotate):
+    import sa_workloads as W
+    return CsaSetup(name, rotate) if name in W.CSA_WORKLOADS else Setup(name, rotate)
+
 
 def kernel_name(setup):
-    return {0: "generic_forward_kernel", 1: "mla_forward_kernel",
-            2: "latent_forward_kernel", 3: "pair_forward_kernel", 4: "gqa_forward_kernel"}[setup.path]
+    return {0: "generic_forward_kernel", 1: "mla_forward_kernel", 2: "latent_forward_kernel",
+            3: "pair_forward_kernel", 4: "gqa_forward_kernel", 5: "csa_attention_kernel"}[setup.path]
 
 
 def counters_for(setup):
@@ -234,7 +442,7 @@ def pmc_run(args):
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    s = Setup(args.workload, args.rotate)
+    s = make_setup(args.workload, args.rotate)
     print(f"pmc-run: {args.workload} kernel {kernel_name(s)}", file=sys.stderr, flush=True)
     for i in range(args.warmup + args.steps):
         s.step(i)
@@ -446,8 +654,7 @@ def main():
         pmc_run(args)
         return
     print(f"bench: workload {args.workload}, building inputs", file=sys.stderr, flush=True)
-    s = Setup(args.workload, args.rotate)
-    w = s.w
+    s = make_setup(args.workload, args.rotate)
     print(f"bench: path {kernel_name(s)} splits {s.splits}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         s.step(i)
@@ -492,20 +699,12 @@ def main():
 
     tokens = s.tokens_per_step()
     kw = s.kernel_work()
-    if w.pattern == "causal_prefill" or s.path == 4:
-        bound, peak, unit = "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-        achieved = kw["flops"] / k_avg_s / 1e12
-    elif w.layout == s.W.LAYOUT_SEPARATE:
-        bound, peak, unit = "alu", VALU_FP32_PEAK_TFLOPS, "TFLOP/s"
-        achieved = kw["flops"] / k_avg_s / 1e12
-    else:
-        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
-        achieved = kw["bytes"] / k_avg_s / 1e9
+    bound, peak, unit, achieved = s.roofline(kw, k_avg_s)
     traffic = counters_for(s)
     result = {
         "metric": "selected KV tokens attended/sec (decode) + achieved HBM GB/s % of peak",
         "value": tokens / (ms_per_step / 1e3),
-        "unit": "selected tokens/s",
+        "unit": "selected tokens/s" if s.path != 5 else "candidates/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
@@ -513,16 +712,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if s.fp8 else {0: "f32", 1: "f16", 2: "bf16"}[w.dtype],
+        "dtype": s.dtype_name(),
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: batch {w.batch}, q_seq {w.q_seq}, {w.hq} q heads / "
-                               f"{w.hkv} kv heads, Dk {w.dk} / Dv {w.dv}, past {w.past} + {w.cur}, "
-                               f"index width {w.width}, {'graph replay' if use_graph else 'eager'}, "
-                               f"{nset} rotating index sets",
-                   "selected_tokens_per_step": tokens, "splits": s.splits,
-                   "step_calls": ("sparse_attn_step (reset + append + forward in one launch)" if s.fused_step()
-                                  else "reset_error_async + kv_append + forward"),
-                   "step_hbm_GBps": s.step_bytes() / (ms_per_step / 1e3) / 1e9},
+        "config": s.config(use_graph, nset, tokens, ms_per_step),
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "kernel": kernel_name(s),
                      "kernel_avg_us": k_avg_s * 1e6,
@@ -531,7 +723,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(s, args.cpu_seconds)
+        result["cpu_baseline"] = s.cpu_baseline(args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     s.ctx.destroy()

@@ -231,6 +231,14 @@ def _pad_cap(a: np.ndarray, cap: int) -> np.ndarray:
     return out
 
 
+def torch_normal_f32(shape, seed: int, device: str = "cuda"):
+    """N(0,1) fp32 tensors drawn on the device with a seeded torch generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+
 def torch_normal_bf16(shape, seed: int, device: str = "cuda"):
     """Large N(0,1) bf16 tensors drawn on the device with a seeded torch
     generator (for the full-size decode caches, too large to draw on the host)."""

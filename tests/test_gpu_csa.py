@@ -190,3 +190,26 @@ def test_csa_host_errors(ctx):
         ctx.csa_forward(q16, ckv, rec, sel, sink[:16], tot, torch.zeros_like(q16),
                         bias=torch.zeros((2, 1, 1, 1), device=dev))  # batch extent 2 != 1
     assert e.value.status == sa.SA_E_SHAPE
+
+
+def test_csa_fullsize_decode_sampled_rows():
+    """The benchmark's CSA decode workload (batch 64, 64 heads, 16384 records
+    per entry, top-512, window 128) in its launch configuration; Y of sampled
+    batch entries, all heads, against the oracle run on those entries alone
+    (records packed by the oracle's quantizer from the generator's rows)."""
+    import torch
+
+    import bench
+    banner("csa full-size decode: building inputs")
+    s = bench.CsaSetup("csa_decode", 1)
+    banner("csa full-size decode: one step")
+    s.step(0)
+    torch.cuda.synchronize()
+    word, _, msg = s.ctx.read_error()
+    assert word == 0, msg
+    y = s.y.cpu().numpy()
+    bs = [0, 5, 40, 63]
+    for b, inp in zip(bs, s.oracle_inputs(bs)):
+        banner(f"csa full-size decode: oracle on batch entry {b}")
+        expect_close(y[b:b + 1], s.oracle_y(inp))
+    s.ctx.destroy()
