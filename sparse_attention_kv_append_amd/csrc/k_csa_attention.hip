@@ -52,8 +52,8 @@ constexpr int EXCH_OFF = 4 * SLOT;      // partial-score exchange, two buffers
 constexpr int EXCH_WAVE = 64 * 32;
 constexpr int EXCH_BUF = 4 * EXCH_WAVE;
 constexpr int IDX_OFF = EXCH_OFF + 2 * EXCH_BUF;
-constexpr size_t LDS_BYTES = (size_t)IDX_OFF + KMAX * 4;
-constexpr int RAWN = 16;                // 16-byte loads per lane and tile (dense); records use 5 or 8 + 3 bytes
+constexpr int MISC_OFF = IDX_OFF + KMAX * 4;
+constexpr size_t LDS_BYTES = (size_t)MISC_OFF + 16;
 }  // namespace cs
 
 __device__ __forceinline__ int csa_swz(int R, int ch) { return ch ^ (2 * (R & 7)) ^ ((R >> 3) & 1); }
@@ -79,14 +79,16 @@ __device__ __forceinline__ f32x4_l mfma_bf16(u32x4_l a, u32x4_l b, f32x4_l c) {
                                                  c, 0, 0, 0);
 }
 
-template <bool BIAS>
-__global__ void __launch_bounds__(cs::THREADS, 1)
-csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
-                     const uint8_t* __restrict__ rec, const int32_t* __restrict__ sel,
-                     const float* __restrict__ sink, const float* __restrict__ bias,
-                     const int64_t* __restrict__ total_ptr, float* __restrict__ y, int B, int S, int H,
-                     int Tcur, int64_t rcap, int idx_heads, int K, int bb, int bh, int bs, int bk,
-                     float scale, ErrorBlock* __restrict__ eb) {
+// The body of one wave. TAILW: the wave whose slice holds the BF16 tail
+// (wave 3); the two instantiations issue fixed, different load counts per
+// tile, so the compiler's wait counts stay exact across the loop.
+template <bool BIAS, bool TAILW>
+__device__ __forceinline__ void
+csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8_t* __restrict__ rec,
+         const int32_t* __restrict__ sel, const float* __restrict__ sink, const float* __restrict__ bias,
+         const int64_t* __restrict__ total_ptr, float* __restrict__ y, int B, int S, int H, int Tcur,
+         int64_t rcap, int idx_heads, int K, int bb, int bh, int bs, int bk, float scale,
+         ErrorBlock* __restrict__ eb) {
   using namespace cs;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -122,10 +124,10 @@ csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
 
   // ---- the index row (index head 0) into LDS, padded with -1
   __attribute__((address_space(3))) int32_t* idxl = (__attribute__((address_space(3))) int32_t*)(smem + IDX_OFF);
-  __shared__ int s_last, s_bad;
+  int* const misc = (int*)(smem + MISC_OFF);  // [0] slots up to the last index >= 0, [1] range flag
   if (tid == 0) {
-    s_last = 0;
-    s_bad = 0;
+    misc[0] = 0;
+    misc[1] = 0;
   }
   __syncthreads();
   {
@@ -137,13 +139,15 @@ csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
       if (v >= 0) last = j + 1;
       if ((int64_t)v >= vr) bad = 1;
     }
-    if (last) atomicMax(&s_last, last);
-    if (bad) atomicOr(&s_bad, 1);
+    if (last) atomicMax(&misc[0], last);
+    if (bad) atomicOr(&misc[1], 1);
   }
   __syncthreads();
-  const int nsel = s_last;  // slots up to the last non-negative index
-  if (s_bad && tid == 0) atomicOr(&eb->word, SA_ERR_RANGE | SA_ERR_INDEX_ANY);
-  const int nDT = (nd + KT - 1) / KT;
+  // wave-uniform by construction; readfirstlane tells the compiler so, and
+  // the tile loop's branches stay scalar (no exec-masked paths)
+  const int nsel = __builtin_amdgcn_readfirstlane(misc[0]);  // slots up to the last index >= 0
+  if (misc[1] && tid == 0) atomicOr(&eb->word, SA_ERR_RANGE | SA_ERR_INDEX_ANY);
+  const int nDT = __builtin_amdgcn_readfirstlane((nd + KT - 1) / KT);
   const int T = nDT + (nsel + KT - 1) / KT;
 
   // ---- the query slice as three bf16 pieces (B operand of S^T = K . Q^T):
@@ -182,84 +186,93 @@ csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
   if (BIAS)
     bias_row = ((((int64_t)(bb == 1 ? 0 : b) * bh + (bh == 1 ? 0 : head)) * bs + (bs == 1 ? 0 : s)) * bk);
   const int64_t cand_last = Dn + K - 1;
-  const bool tailw = w == 3;  // wave 3's slice is block 6 plus the BF16 tail
+  constexpr bool tailw = TAILW;  // wave 3's slice is block 6 plus the BF16 tail
 
-  u32x4_l raw[2][RAWN];
+  // Loads run in units: a dense tile is two units (keys 0..15, 16..31), a
+  // record tile one. Every unit issues the same instructions (8 x 16 bytes per
+  // lane, plus 3 single bytes in the tail wave and 8 bias words with a bias),
+  // addressed by the unit's kind and out of range where unused, so the
+  // compiler's wait counts are exact and loads run two units ahead.
+  const int NU = 2 * nDT + (T - nDT);
+  u32x4_l raw[2][8];
+  uint32_t rby[2][3];
   uint32_t rsh[2];
   float braw[2][8];
   float bcur[8];  // the bias of the tile being computed (taken out of braw when staged)
+  constexpr uint32_t OOB = 0x80000000u;
 
-  // issue the global loads of tile t into register set SET
-  auto issue = [&](int t, auto setc) {
+  auto issue = [&](int u, auto setc) {
     constexpr int SET = decltype(setc)::value;
-    if (t >= T) return;
-    if (t < nDT) {
-      // lane: rows (lane >> 4) + 4 gI, 32-byte chunk lane & 15 of the slice
-      const int cc = lane & 15;
+    const bool dn = u < 2 * nDT;  // uniform
+    const int tile = dn ? (u >> 1) : nDT + (u - 2 * nDT);
+    const int half = dn ? (u & 1) : 0;
+    // dense unit: lane loads key 16 half + (lane >> 4) + 4 gI, 32-byte chunk lane & 15
+    const int cc = lane & 15;
+    uint32_t doff[4];
 #pragma unroll
-      for (int gI = 0; gI < 8; gI++) {
-        const int k = (lane >> 4) + 4 * gI;
-        const int c = KT * t + k;
-        const uint32_t off = c < nd ? (uint32_t)(((r0 + c) * D + 128 * w + 8 * cc) * 4) : 0x80000000u;
-        raw[SET][2 * gI] = __builtin_bit_cast(u32x4_l, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off, 0, 0));
-        raw[SET][2 * gI + 1] = __builtin_bit_cast(u32x4_l, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off + 16, 0, 0));
-      }
-    } else {
-      const int k = lane & 31, hb = lane >> 5;
-      const int j = KT * (t - nDT) + k;
-      const int32_t r = idxl[j];
-      const bool ok = r >= 0 && (int64_t)r < vr;
-      const bool tail = tailw && hb;
-      const int64_t a = (int64_t)r * REC + (tail ? TAILB : 65 * (2 * w + hb));
-      rsh[SET] = (uint32_t)(a & 3);
-      const uint32_t off = ok ? (uint32_t)(a & ~(int64_t)3) : 0x80000000u;
+    for (int gI = 0; gI < 4; gI++) {
+      const int c = KT * tile + 16 * half + (lane >> 4) + 4 * gI;
+      doff[gI] = (dn && c < nd) ? (uint32_t)(((r0 + c) * D + 128 * w + 8 * cc) * 4) : OOB;
+    }
+    // record unit: lane loads 64 dims (block 2 w + hb, or the tail) of slot k
+    const int k = lane & 31, hb = lane >> 5;
+    int j = KT * (tile - nDT) + k;
+    j = j < 0 ? 0 : (j > KMAX - 1 ? KMAX - 1 : j);
+    const int32_t r = idxl[j];
+    const bool ok = !dn && tile < T && r >= 0 && (int64_t)r < vr;
+    const bool tail = tailw && hb;
+    const int64_t a = (int64_t)r * REC + (tail ? TAILB : 65 * (2 * w + hb));
+    const uint32_t a4 = ok ? (uint32_t)(a & ~(int64_t)3) : OOB;
+    rsh[SET] = (uint32_t)(a & 3);
+    const __amdgpu_buffer_rsrc_t rs = dn ? krsrc : rrsrc;
 #pragma unroll
-      for (int i = 0; i < 5; i++)
-        raw[SET][i] = __builtin_bit_cast(u32x4_l, __builtin_amdgcn_raw_buffer_load_b128(rrsrc, off + 16 * i, 0, 0));
-      if (tailw) {
-        // the tail's last bytes sit in dword 32 of the window; for the last
-        // record of the buffer a 16-byte (or 4-byte) load of it would straddle
-        // the buffer end and be dropped by the range check, so its three
-        // possibly needed bytes are loaded one by one
+    for (int i = 0; i < 8; i++) {
+      // records: 80 bytes cover a coded block; the tail wave's lanes take 128
+      const uint32_t ro = (i < 5 || tailw) ? (a4 == OOB ? OOB : a4 + 16 * i) : OOB;
+      const uint32_t off = dn ? (doff[i >> 1] == OOB ? OOB : doff[i >> 1] + 16 * (i & 1)) : ro;
+      raw[SET][i] = __builtin_bit_cast(u32x4_l, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+    if (tailw) {
+      // the tail's last bytes sit in dword 32 of the window; for the last
+      // record of the buffer a 4- or 16-byte load of it would straddle the
+      // buffer end and be dropped by the range check, so its three possibly
+      // needed bytes are loaded one by one
 #pragma unroll
-        for (int i = 5; i < 8; i++)
-          raw[SET][i] = __builtin_bit_cast(u32x4_l, __builtin_amdgcn_raw_buffer_load_b128(rrsrc, off + 16 * i, 0, 0));
-#pragma unroll
-        for (int i = 0; i < 3; i++)
-          raw[SET][8][i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rrsrc, off + 128 + i, 0, 0);
-      }
+      for (int i = 0; i < 3; i++)
+        rby[SET][i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rrsrc, a4 == OOB ? OOB : a4 + 128 + i, 0, 0);
     }
     if (BIAS) {
       // lane (head i16, g): keys 16 hh + 4 g + r of the tile
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const int k = 16 * (i >> 2) + 4 * g + (i & 3);
-        int64_t c = t < nDT ? (int64_t)(KT * t + k) : Dn + (int64_t)(KT * (t - nDT) + k);
+        const int kk = 16 * (i >> 2) + 4 * g + (i & 3);
+        int64_t c = dn ? (int64_t)(KT * tile + kk) : Dn + (int64_t)(KT * (tile - nDT) + kk);
         c = c < cand_last ? c : cand_last;
         braw[SET][i] = bias[bias_row + (bk == 1 ? 0 : c)];
       }
     }
   };
 
-  // write tile t's slice from register set SET into the wave's LDS slot
-  auto stage = [&](int t, auto setc) {
+  // write unit u from register set SET into the wave's LDS slot
+  auto stage = [&](int u, auto setc) {
     constexpr int SET = decltype(setc)::value;
     if (BIAS) {
 #pragma unroll
       for (int i = 0; i < 8; i++) bcur[i] = braw[SET][i];
     }
-    if (t < nDT) {
+    if (u < 2 * nDT) {
       const int cc = lane & 15;
+      const int half = u & 1;
 #pragma unroll
-      for (int gI = 0; gI < 8; gI++) {
-        const int k = (lane >> 4) + 4 * gI;
+      for (int gI = 0; gI < 4; gI++) {
+        const int kr = 16 * half + (lane >> 4) + 4 * gI;
         const u32x4_l lo = raw[SET][2 * gI], hi = raw[SET][2 * gI + 1];
         const float xv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]),
                              __uint_as_float(lo[3]), __uint_as_float(hi[0]), __uint_as_float(hi[1]),
                              __uint_as_float(hi[2]), __uint_as_float(hi[3])};
         u32x4_l p1, p2, p3;
         split3x8(xv, p1, p2, p3);
-        const uint32_t o = (uint32_t)(k * ROWB + 16 * csa_swz(k, cc));
+        const uint32_t o = (uint32_t)(kr * ROWB + 16 * csa_swz(kr, cc));
         *(lds_u32x4*)(slotp + o) = p1;
         *(lds_u32x4*)(slotp + PLANE + o) = p2;
         *(lds_u32x4*)(slotp + 2 * PLANE + o) = p3;
@@ -277,7 +290,7 @@ csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
           Dw[4 * i + 2] = raw[SET][i][2];
           Dw[4 * i + 3] = raw[SET][i][3];
         }
-        Dw[32] = (raw[SET][8][0] & 0xffu) | ((raw[SET][8][1] & 0xffu) << 8) | ((raw[SET][8][2] & 0xffu) << 16);
+        Dw[32] = (rby[SET][0] & 0xffu) | ((rby[SET][1] & 0xffu) << 8) | ((rby[SET][2] & 0xffu) << 16);
 #pragma unroll
         for (int i = 0; i < 32; i++) wv[i] = __builtin_amdgcn_alignbyte(Dw[i + 1], Dw[i], sh);
       } else {
@@ -291,10 +304,19 @@ csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
         }
         const uint32_t e = (Dw[0] >> (8 * sh)) & 0xffu;
         const uint32_t o1 = sh + 1;  // byte offset of the first code, 1..4
+        uint32_t cw[16];
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const uint32_t cw = o1 == 4 ? Dw[i + 1] : __builtin_amdgcn_alignbyte(Dw[i + 1], Dw[i], o1);
-          fp8x4_to_bf16x4(cw, e, wv[2 * i], wv[2 * i + 1]);
+        for (int i = 0; i < 16; i++) cw[i] = o1 == 4 ? Dw[i + 1] : __builtin_amdgcn_alignbyte(Dw[i + 1], Dw[i], o1);
+        if (__builtin_amdgcn_ballot_w64(e < 10u || e > 246u) == 0) {
+          const float sc = __uint_as_float(e << 23);
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            wv[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[i], sc, false));
+            wv[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[i], sc, true));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; i++) fp8x4_to_bf16x4(cw[i], e, wv[2 * i], wv[2 * i + 1]);
         }
       }
 #pragma unroll
@@ -311,44 +333,56 @@ csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
   for (int dt = 0; dt < 8; dt++) o[dt] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  auto compute = [&](int t, auto setc) {
-    constexpr int SET = decltype(setc)::value;  // also the exchange buffer
+  auto compute = [&](int t, int xb) {
     const bool dense = t < nDT;
-    // ---- partial S^T over this wave's dims
-    f32x4_l acc[2] = {(f32x4_l){0.f, 0.f, 0.f, 0.f}, (f32x4_l){0.f, 0.f, 0.f, 0.f}};
+    // ---- partial S^T over this wave's dims: one accumulator per (key half,
+    // query piece), so consecutive MFMAs are independent
+    f32x4_l acc[2][3];
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+      for (int pc = 0; pc < 3; pc++) acc[hh][pc] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
     if (dense) {
 #pragma unroll
       for (int c = 0; c < 4; c++) {
+        u32x4_l k[2][3];
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-          const uint32_t a = kofs[c] + hh * HALF;
-          const u32x4_l k1 = *(const lds_u32x4*)(slotp + a);
-          const u32x4_l k2 = *(const lds_u32x4*)(slotp + PLANE + a);
-          const u32x4_l k3 = *(const lds_u32x4*)(slotp + 2 * PLANE + a);
-          acc[hh] = mfma_bf16(k1, qb[0][c], acc[hh]);
-          acc[hh] = mfma_bf16(k1, qb[1][c], acc[hh]);
-          acc[hh] = mfma_bf16(k2, qb[0][c], acc[hh]);
-          acc[hh] = mfma_bf16(k1, qb[2][c], acc[hh]);
-          acc[hh] = mfma_bf16(k2, qb[1][c], acc[hh]);
-          acc[hh] = mfma_bf16(k3, qb[0][c], acc[hh]);
-        }
+        for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+          for (int pl = 0; pl < 3; pl++) k[hh][pl] = *(const lds_u32x4*)(slotp + pl * PLANE + kofs[c] + hh * HALF);
+        // piece products of weight >= 2^-16: (1,1) (1,2) (2,1) (1,3) (2,2) (3,1)
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) acc[hh][0] = mfma_bf16(k[hh][0], qb[0][c], acc[hh][0]);
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) acc[hh][1] = mfma_bf16(k[hh][0], qb[1][c], acc[hh][1]);
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) acc[hh][2] = mfma_bf16(k[hh][1], qb[0][c], acc[hh][2]);
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) acc[hh][1] = mfma_bf16(k[hh][0], qb[2][c], acc[hh][1]);
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) acc[hh][2] = mfma_bf16(k[hh][1], qb[1][c], acc[hh][2]);
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) acc[hh][0] = mfma_bf16(k[hh][2], qb[0][c], acc[hh][0]);
       }
     } else {
 #pragma unroll
       for (int c = 0; c < 4; c++) {
+        u32x4_l k[2];
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-          const u32x4_l k1 = *(const lds_u32x4*)(slotp + kofs[c] + hh * HALF);
-          acc[hh] = mfma_bf16(k1, qb[0][c], acc[hh]);
-          acc[hh] = mfma_bf16(k1, qb[1][c], acc[hh]);
-          acc[hh] = mfma_bf16(k1, qb[2][c], acc[hh]);
-        }
+        for (int hh = 0; hh < 2; hh++) k[hh] = *(const lds_u32x4*)(slotp + kofs[c] + hh * HALF);
+#pragma unroll
+        for (int pc = 0; pc < 3; pc++)
+#pragma unroll
+          for (int hh = 0; hh < 2; hh++) acc[hh][pc] = mfma_bf16(k[hh], qb[pc][c], acc[hh][pc]);
       }
     }
+    f32x4_l accs[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) accs[hh] = (acc[hh][0] + acc[hh][1]) + acc[hh][2];
     // ---- sum the four waves' partials (fixed order: identical in every wave)
-    uint8_t* ex = smem + EXCH_OFF + SET * EXCH_BUF;
-    *(lds_u32x4*)(ex + w * EXCH_WAVE + lane * 32) = __builtin_bit_cast(u32x4_l, acc[0]);
-    *(lds_u32x4*)(ex + w * EXCH_WAVE + lane * 32 + 16) = __builtin_bit_cast(u32x4_l, acc[1]);
+    uint8_t* ex = smem + EXCH_OFF + xb * EXCH_BUF;
+    *(lds_u32x4*)(ex + w * EXCH_WAVE + lane * 32) = __builtin_bit_cast(u32x4_l, accs[0]);
+    *(lds_u32x4*)(ex + w * EXCH_WAVE + lane * 32 + 16) = __builtin_bit_cast(u32x4_l, accs[1]);
     lds_barrier();
     float sv[8];
     {
@@ -406,48 +440,72 @@ csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
     for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
     u32x4_l pb[3];
     split3x8(pv, pb[0], pb[1], pb[2]);
-    // ---- O^T += V^T . P^T over this wave's 128 output dims
+    // ---- O^T += V^T . P^T over this wave's 128 output dims; the eight dv
+    // tiles' MFMAs of one piece product are independent of each other
     typedef __attribute__((address_space(3))) s16x4_l lds_s16x4;
+    auto vload = [&](int pl, int dt) {
+      const s16x4_l a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + pl * PLANE + vofs[dt]));
+      const s16x4_l a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + pl * PLANE + vofs[dt] + HALF));
+      const s16x4_l a8[2] = {a0, a1};
+      return __builtin_bit_cast(u32x4_l, a8);
+    };
+    if (dense) {
+      u32x4_l v0[8], v1[8];
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++) {
-      if (dense) {
-        u32x4_l v[3];
+      for (int dt = 0; dt < 8; dt++) v0[dt] = vload(0, dt);
 #pragma unroll
-        for (int pl = 0; pl < 3; pl++) {
-          const s16x4_l a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + pl * PLANE + vofs[dt]));
-          const s16x4_l a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + pl * PLANE + vofs[dt] + HALF));
-          const s16x4_l a8[2] = {a0, a1};
-          v[pl] = __builtin_bit_cast(u32x4_l, a8);
-        }
-        o[dt] = mfma_bf16(v[0], pb[0], o[dt]);
-        o[dt] = mfma_bf16(v[0], pb[1], o[dt]);
-        o[dt] = mfma_bf16(v[1], pb[0], o[dt]);
-        o[dt] = mfma_bf16(v[0], pb[2], o[dt]);
-        o[dt] = mfma_bf16(v[1], pb[1], o[dt]);
-        o[dt] = mfma_bf16(v[2], pb[0], o[dt]);
-      } else {
-        const s16x4_l a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + vofs[dt]));
-        const s16x4_l a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + vofs[dt] + HALF));
-        const s16x4_l a8[2] = {a0, a1};
-        const u32x4_l v = __builtin_bit_cast(u32x4_l, a8);
-        o[dt] = mfma_bf16(v, pb[0], o[dt]);
-        o[dt] = mfma_bf16(v, pb[1], o[dt]);
-        o[dt] = mfma_bf16(v, pb[2], o[dt]);
-      }
+      for (int dt = 0; dt < 8; dt++) v1[dt] = vload(1, dt);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v0[dt], pb[0], o[dt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v0[dt], pb[1], o[dt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v1[dt], pb[0], o[dt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v0[dt], pb[2], o[dt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v1[dt], pb[1], o[dt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) v0[dt] = vload(2, dt);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v0[dt], pb[0], o[dt]);
+    } else {
+      u32x4_l v[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) v[dt] = vload(0, dt);
+#pragma unroll
+      for (int pc = 0; pc < 3; pc++)
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v[dt], pb[pc], o[dt]);
     }
   };
 
-  issue(0, std::integral_constant<int, 0>{});
-  issue(1, std::integral_constant<int, 1>{});
-  for (int t = 0; t < T; t += 2) {
-    stage(t, std::integral_constant<int, 0>{});
-    issue(t + 2, std::integral_constant<int, 0>{});
-    compute(t, std::integral_constant<int, 0>{});
-    if (t + 1 < T) {
-      stage(t + 1, std::integral_constant<int, 1>{});
-      issue(t + 3, std::integral_constant<int, 1>{});
-      compute(t + 1, std::integral_constant<int, 1>{});
+  const std::integral_constant<int, 0> set0;
+  const std::integral_constant<int, 1> set1;
+  // unit u completes a tile when it is a record unit or a dense tile's second half
+  auto unit_tile = [&](int u) { return u < 2 * nDT ? (u >> 1) : nDT + (u - 2 * nDT); };
+  auto completes = [&](int u) { return u >= 2 * nDT || (u & 1); };
+  int xb = 0;
+  issue(0, set0);
+  issue(1, set1);
+  int u = 0;
+  for (; u + 1 < NU; u += 2) {
+    stage(u, set0);
+    issue(u + 2, set0);
+    if (completes(u)) {
+      compute(unit_tile(u), xb);
+      xb ^= 1;
     }
+    stage(u + 1, set1);
+    issue(u + 3, set1);
+    if (completes(u + 1)) {
+      compute(unit_tile(u + 1), xb);
+      xb ^= 1;
+    }
+  }
+  if (u < NU) {
+    stage(u, set0);
+    compute(unit_tile(u), xb);
   }
 
   // ---- Y = O / (l + exp(sink - m)); a head with no candidate gives zeros
@@ -462,6 +520,22 @@ csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
     const f32x4_l r = o[dt] * inv;
     *(float4*)(yrow + 16 * dt) = make_float4(r[0], r[1], r[2], r[3]);
   }
+}
+
+template <bool BIAS>
+__global__ void __launch_bounds__(cs::THREADS, 1)
+csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
+                     const uint8_t* __restrict__ rec, const int32_t* __restrict__ sel,
+                     const float* __restrict__ sink, const float* __restrict__ bias,
+                     const int64_t* __restrict__ total_ptr, float* __restrict__ y, int B, int S, int H,
+                     int Tcur, int64_t rcap, int idx_heads, int K, int bb, int bh, int bs, int bk,
+                     float scale, ErrorBlock* __restrict__ eb) {
+  if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) == 3)
+    csa_wave<BIAS, true>(q, ckv, rec, sel, sink, bias, total_ptr, y, B, S, H, Tcur, rcap, idx_heads, K, bb, bh,
+                         bs, bk, scale, eb);
+  else
+    csa_wave<BIAS, false>(q, ckv, rec, sel, sink, bias, total_ptr, y, B, S, H, Tcur, rcap, idx_heads, K, bb, bh,
+                          bs, bk, scale, eb);
 }
 
 sa_status launch_csa_attention(sparse_attn_ctx* c, const CsaArgs& a) {
