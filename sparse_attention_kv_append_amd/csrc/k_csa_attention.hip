@@ -133,10 +133,13 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
   {
     const int32_t* srow = sel + ((int64_t)b * idx_heads * S + s) * K;
     int last = 0, bad = 0;
+    // stored sanitized: an index that is no candidate (negative, or not a
+    // complete record) becomes -1, so a candidate is simply an entry >= 0
     for (int j = tid; j < KMAX; j += THREADS) {
       const int32_t v = j < K ? srow[j] : -1;
-      idxl[j] = v;
-      if (v >= 0) last = j + 1;
+      const bool cand = v >= 0 && (int64_t)v < vr;
+      idxl[j] = cand ? v : -1;
+      if (cand) last = j + 1;
       if ((int64_t)v >= vr) bad = 1;
     }
     if (last) atomicMax(&misc[0], last);
@@ -196,7 +199,7 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
   const int NU = 2 * nDT + (T - nDT);
   u32x4_l raw[2][8];
   uint32_t rby[2][3];
-  uint32_t rsh[2];
+  uint32_t rsh[2], rsc[2];
   float braw[2][8];
   float bcur[8];  // the bias of the tile being computed (taken out of braw when staged)
   constexpr uint32_t OOB = 0x80000000u;
@@ -219,11 +222,14 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
     int j = KT * (tile - nDT) + k;
     j = j < 0 ? 0 : (j > KMAX - 1 ? KMAX - 1 : j);
     const int32_t r = idxl[j];
-    const bool ok = !dn && tile < T && r >= 0 && (int64_t)r < vr;
+    const bool ok = !dn && tile < T && r >= 0;
     const bool tail = tailw && hb;
-    const int64_t a = (int64_t)r * REC + (tail ? TAILB : 65 * (2 * w + hb));
+    // a coded block's window starts at the dword of its first code (the scale
+    // byte, one before, is loaded by itself); the tail's at its first byte
+    const int64_t a = (int64_t)r * REC + (tail ? TAILB : 65 * (2 * w + hb) + 1);
     const uint32_t a4 = ok ? (uint32_t)(a & ~(int64_t)3) : OOB;
     rsh[SET] = (uint32_t)(a & 3);
+    rsc[SET] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rrsrc, ok ? (uint32_t)(a - 1) : OOB, 0, 0);
     const __amdgpu_buffer_rsrc_t rs = dn ? krsrc : rrsrc;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -253,6 +259,19 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
     }
   };
 
+  // per-lane LDS write offsets of a unit (fixed over the loop)
+  uint32_t dwo[2][4], rwo[8];
+#pragma unroll
+  for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+    for (int gI = 0; gI < 4; gI++) {
+      const int kr = 16 * hf + (lane >> 4) + 4 * gI;
+      dwo[hf][gI] = (uint32_t)(kr * ROWB + 16 * csa_swz(kr, lane & 15));
+    }
+#pragma unroll
+  for (int qd = 0; qd < 8; qd++)
+    rwo[qd] = (uint32_t)((lane & 31) * ROWB + 16 * csa_swz(lane & 31, 8 * (lane >> 5) + qd));
+
   // write unit u from register set SET into the wave's LDS slot
   auto stage = [&](int u, auto setc) {
     constexpr int SET = decltype(setc)::value;
@@ -272,7 +291,7 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
                              __uint_as_float(hi[2]), __uint_as_float(hi[3])};
         u32x4_l p1, p2, p3;
         split3x8(xv, p1, p2, p3);
-        const uint32_t o = (uint32_t)(kr * ROWB + 16 * csa_swz(kr, cc));
+        const uint32_t o = half ? dwo[1][gI] : dwo[0][gI];
         *(lds_u32x4*)(slotp + o) = p1;
         *(lds_u32x4*)(slotp + PLANE + o) = p2;
         *(lds_u32x4*)(slotp + 2 * PLANE + o) = p3;
@@ -294,7 +313,7 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
 #pragma unroll
         for (int i = 0; i < 32; i++) wv[i] = __builtin_amdgcn_alignbyte(Dw[i + 1], Dw[i], sh);
       } else {
-        uint32_t Dw[20];
+        uint32_t Dw[20];  // codes from byte sh of Dw[0]: 64 + 3 bytes fit 17 dwords
 #pragma unroll
         for (int i = 0; i < 5; i++) {
           Dw[4 * i] = raw[SET][i][0];
@@ -302,11 +321,10 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
           Dw[4 * i + 2] = raw[SET][i][2];
           Dw[4 * i + 3] = raw[SET][i][3];
         }
-        const uint32_t e = (Dw[0] >> (8 * sh)) & 0xffu;
-        const uint32_t o1 = sh + 1;  // byte offset of the first code, 1..4
+        const uint32_t e = rsc[SET] & 0xffu;
         uint32_t cw[16];
 #pragma unroll
-        for (int i = 0; i < 16; i++) cw[i] = o1 == 4 ? Dw[i + 1] : __builtin_amdgcn_alignbyte(Dw[i + 1], Dw[i], o1);
+        for (int i = 0; i < 16; i++) cw[i] = __builtin_amdgcn_alignbyte(Dw[i + 1], Dw[i], sh);
         if (__builtin_amdgcn_ballot_w64(e < 10u || e > 246u) == 0) {
           const float sc = __uint_as_float(e << 23);
 #pragma unroll
@@ -320,10 +338,8 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
         }
       }
 #pragma unroll
-      for (int qd = 0; qd < 8; qd++) {
-        const uint32_t o = (uint32_t)(k * ROWB + 16 * csa_swz(k, 8 * hb + qd));
-        *(lds_u32x4*)(slotp + o) = (u32x4_l){wv[4 * qd], wv[4 * qd + 1], wv[4 * qd + 2], wv[4 * qd + 3]};
-      }
+      for (int qd = 0; qd < 8; qd++)
+        *(lds_u32x4*)(slotp + rwo[qd]) = (u32x4_l){wv[4 * qd], wv[4 * qd + 1], wv[4 * qd + 2], wv[4 * qd + 3]};
     }
   };
 
@@ -331,7 +347,8 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
   f32x4_l o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; dt++) o[dt] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, m_ref = -INFINITY, l_run = 0.0f;
+  constexpr float kTau = 8.0f;  // p <= 2^8 against the reference
 
   auto compute = [&](int t, int xb) {
     const bool dense = t < nDT;
@@ -411,8 +428,7 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
         const u32x4_l iv = *(const __attribute__((address_space(3))) u32x4_l*)(idxl + j0 + 16 * hh);
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-          const int32_t rr = (int32_t)iv[r];
-          valid[4 * hh + r] = rr >= 0 && (int64_t)rr < vr;
+          valid[4 * hh + r] = (int32_t)iv[r] >= 0;
         }
       }
     }
@@ -425,19 +441,26 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
       tmax = fmaxf(tmax, sv[i]);
     }
     tmax = max_x32(max_x16(tmax));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
+    // exponents are taken against a reference m_ref that moves only when a
+    // score exceeds it by more than 2^TAU (then O and l are rescaled), so O is
+    // rarely touched; the true maximum m_run is kept for the final scaling
+    m_run = fmaxf(m_run, tmax);
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kTau) != 0) {
+      const float m_new = tmax > m_ref + kTau ? m_run : m_ref;
+      const float alpha = m_new == m_ref ? 1.0f : exp2f(m_ref - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
+      m_ref = m_new;
+    }
     float pv[8], psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      pv[i] = sv[i] == -INFINITY ? 0.0f : exp2f(sv[i] - m_new);
+      pv[i] = sv[i] == -INFINITY ? 0.0f : exp2f(sv[i] - m_ref);
       psum += pv[i];
     }
     psum = sum_x32(sum_x16(psum));
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
+    l_run += psum;
     u32x4_l pb[3];
     split3x8(pv, pb[0], pb[1], pb[2]);
     // ---- O^T += V^T . P^T over this wave's 128 output dims; the eight dv
@@ -509,11 +532,13 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
   }
 
   // ---- Y = O / (l + exp(sink - m)); a head with no candidate gives zeros
-  const float den = l_run + exp2f(sink[head] * kLog2eL - m_run);
+  // against the true maximum m: den = l e^(m_ref - m) + e^(sink - m)
   const bool none = m_run == -INFINITY;
+  const float fr = none ? 0.0f : exp2f(m_ref - m_run);
+  const float den = l_run * fr + exp2f(sink[head] * kLog2eL - m_run);
   const bool bad = !none && !(den > 0.0f && den < INFINITY);
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(&eb->word, SA_ERR_CSA_DENOM);
-  const float inv = none ? 0.0f : 1.0f / den;
+  const float inv = none ? 0.0f : fr / den;
   float* yrow = y + qrow + 128 * w + 4 * g;
 #pragma unroll
   for (int dt = 0; dt < 8; dt++) {
