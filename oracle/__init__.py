@@ -89,6 +89,20 @@ def _load():
         lib.oracle_csa_sink_attention.argtypes = [P, I64, I64, I64, P, I64, P, I64, P, I64, I64,
                                                   P, P, P, I64, ctypes.c_float, P]
         lib.oracle_csa_sink_attention.restype = ctypes.c_uint32
+        lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_value.restype = ctypes.c_double
+        lib.oracle_fp4_quantize_block32.argtypes = [P, P, P, P]
+        lib.oracle_fp4_quantize_block32.restype = ctypes.c_int
+        lib.oracle_fp4_decode_key.argtypes = [P, I64, P]
+        lib.oracle_fp4_decode_key.restype = None
+        lib.oracle_compressed_rope.argtypes = [P, I64, I64]
+        lib.oracle_compressed_rope.restype = None
+        lib.oracle_hadamard_f32.argtypes = [P, I64]
+        lib.oracle_hadamard_f32.restype = None
+        lib.oracle_finalize_index_query.argtypes = [P, I64, I64, I64, P]
+        lib.oracle_finalize_index_query.restype = ctypes.c_int
+        lib.oracle_csa_index_select.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P, P]
+        lib.oracle_csa_index_select.restype = ctypes.c_uint32
         _lib = lib
         return lib
 
@@ -311,6 +325,88 @@ def csa_sink_attention(query, current_kv, records, selected, sink, total: int, *
     if flags == 0xFFFFFFFF:
         raise MemoryError("oracle csa_sink_attention: allocation failed")
     return y, int(flags)
+
+
+# ---------------------------------------------------------------- CSA selection producer
+SEL_NONFINITE, SEL_TIE, SEL_GEOMETRY = 1, 2, 4
+
+
+def e2m1_value(code: int) -> float:
+    return _load().oracle_e2m1_value(code)
+
+
+def fp4_quantize_block32(x):
+    """32 fp32 values -> (scale byte, 16 packed bytes, dequantized fp32[32])."""
+    x = np.ascontiguousarray(x, np.float32)
+    assert x.shape == (32,)
+    sc, packed, out = np.zeros(1, np.uint8), np.zeros(16, np.uint8), np.zeros(32, np.float32)
+    if _load().oracle_fp4_quantize_block32(_ptr(x), _ptr(sc), _ptr(packed), _ptr(out)) != 0:
+        raise ValueError("fp4 quantize: non-finite value")
+    return int(sc[0]), packed, out
+
+
+def fp4_pack_keys(rows) -> np.ndarray:
+    """[..., dim] fp32 -> [..., dim/32*17] FP4 index keys (blocks of scale + 16 bytes)."""
+    rows = np.ascontiguousarray(rows, np.float32)
+    dim = rows.shape[-1]
+    flat = rows.reshape(-1, dim)
+    out = np.zeros((flat.shape[0], dim // 32 * 17), np.uint8)
+    for i in range(flat.shape[0]):
+        for b in range(dim // 32):
+            sc, packed, _ = fp4_quantize_block32(flat[i, 32 * b:32 * b + 32])
+            out[i, 17 * b] = sc
+            out[i, 17 * b + 1:17 * b + 17] = packed
+    return out.reshape(rows.shape[:-1] + (dim // 32 * 17,))
+
+
+def fp4_decode_keys(keys, dim: int) -> np.ndarray:
+    keys = np.ascontiguousarray(keys, np.uint8)
+    flat = keys.reshape(-1, keys.shape[-1])
+    out = np.empty((flat.shape[0], dim), np.float32)
+    lib = _load()
+    for i in range(flat.shape[0]):
+        lib.oracle_fp4_decode_key(_ptr(flat[i]), dim, _ptr(out[i]))
+    return out.reshape(keys.shape[:-1] + (dim,))
+
+
+def compressed_rope(tail, position: int) -> np.ndarray:
+    t = np.array(tail, np.float32, copy=True)
+    _load().oracle_compressed_rope(_ptr(t), t.shape[0], int(position))
+    return t
+
+
+def hadamard_f32(v) -> np.ndarray:
+    t = np.array(v, np.float32, copy=True)
+    _load().oracle_hadamard_f32(_ptr(t), t.shape[0])
+    return t
+
+
+def finalize_index_query(src, rope: int, position: int) -> np.ndarray:
+    src = np.ascontiguousarray(src, np.float32)
+    q = np.empty_like(src)
+    if _load().oracle_finalize_index_query(_ptr(src), src.shape[0], rope, int(position), _ptr(q)) != 0:
+        raise ValueError("finalize_index_query: non-finite value")
+    return q
+
+
+def csa_index_select(index_query, index_weight, index_keys, total: int, topk: int, *, rope: int = 64,
+                     with_scores: bool = False):
+    """index_query [B, S, H, dim] fp32, index_weight [B, S, H] fp32, index_keys
+    [B, Rcap, dim/32*17] uint8. Returns (selected [B, S, topk] int32, flags[, scores
+    [B, S, Rcap] fp32 with NaN past each query's causal records])."""
+    iq = np.ascontiguousarray(index_query, np.float32)
+    iw = np.ascontiguousarray(index_weight, np.float32)
+    keys = np.ascontiguousarray(index_keys, np.uint8)
+    B, S, H, dim = iq.shape
+    assert iw.shape == (B, S, H) and keys.shape[0] == B and keys.shape[2] == dim // 32 * 17
+    sel = np.full((B, S, topk), -1, np.int32)
+    scores = np.empty((B, S, keys.shape[1]), np.float32) if with_scores else None
+    flags = _load().oracle_csa_index_select(_ptr(iq), _ptr(iw), _ptr(keys), B, S, H, dim, rope, keys.shape[1],
+                                            int(total), int(topk), _ptr(sel),
+                                            None if scores is None else _ptr(scores))
+    if flags == 0xFFFFFFFF:
+        raise MemoryError("oracle csa_index_select: allocation failed")
+    return (sel, int(flags), scores) if with_scores else (sel, int(flags))
 
 
 # ---------------------------------------------------------------- textbook

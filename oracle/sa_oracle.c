@@ -607,3 +607,230 @@ uint32_t oracle_csa_sink_attention(const float* q, int64_t batch, int64_t seq, i
   free(row);
   return flags;
 }
+
+/* ---- CSA ratio-4 selection producer (the indexer) -------------------------
+ * [CPU] `select_ratio4_topk`, `finalize_index_query`, `apply_compressed_rope`,
+ * `hadamard_bf16`, `fp4_roundtrip`; [CSA] `csa_ratio4_index_select` (record
+ * layout of the FP4 index keys, the (-score, +record) order, -1 padding).
+ *
+ * FP4 E2M1 block-32: per 32 values an E8M0 scale byte and 16 bytes of codes,
+ * element 2i in the low nibble, 2i+1 in the high one. An E2M1 code is 1 sign,
+ * 2 exponent bits (bias 1) and 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ * The quantizer's source is not on the pages; the reading taken (the OCP MX
+ * rule, as for the fp8 blocks): scale byte = floor(log2(amax)) - 2 + 127
+ * (127 for an all-zero block), codes = nearest E2M1 value of x / 2^(e - 127),
+ * ties to the even code, saturating at 6, sign kept. */
+
+double oracle_e2m1_value(uint8_t code) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const double v = mag[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* nearest E2M1 magnitude code of a non-negative double, ties to even code */
+static uint8_t or_e2m1_encode_mag(double v) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  if (v >= 6.0) return 7;
+  for (int c = 0; c < 7; c++) {
+    const double lo = mag[c], hi = mag[c + 1];
+    if (v <= hi) {
+      const double dl = v - lo, dh = hi - v;
+      if (dl < dh) return (uint8_t)c;
+      if (dh < dl) return (uint8_t)(c + 1);
+      return (uint8_t)((c & 1) ? c + 1 : c); /* tie: the even code */
+    }
+  }
+  return 7;
+}
+
+/* Quantize 32 values: returns 0, or -1 for a non-finite value. out[] gets the
+ * dequantized values (code times scale). */
+int oracle_fp4_quantize_block32(const float* x, uint8_t* scale_out, uint8_t* packed, float* out) {
+  double amax = 0.0;
+  for (int i = 0; i < 32; i++) {
+    if (!isfinite(x[i])) return -1;
+    const double a = fabs((double)x[i]);
+    if (a > amax) amax = a;
+  }
+  int e = 127;
+  if (amax > 0.0) {
+    int ex;
+    frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+    e = (ex - 1) - 2 + 127;
+    if (e < 0) e = 0;
+    if (e > 254) e = 254;
+  }
+  const double s = ldexp(1.0, e - 127);
+  for (int i = 0; i < 16; i++) packed[i] = 0;
+  for (int i = 0; i < 32; i++) {
+    const double v = (double)x[i] / s;
+    uint8_t c = or_e2m1_encode_mag(fabs(v));
+    if (signbit(v)) c |= 8;
+    packed[i / 2] |= (uint8_t)(c << (4 * (i & 1)));
+    out[i] = (float)(oracle_e2m1_value(c) * s);
+  }
+  *scale_out = (uint8_t)e;
+  return 0;
+}
+
+/* Decode one FP4 index key of `dim` values (dim/32 blocks of 17 bytes). */
+void oracle_fp4_decode_key(const uint8_t* key, int64_t dim, float* out) {
+  for (int64_t b = 0; b < dim / 32; b++) {
+    const double s = oracle_e8m0_value(key[17 * b]);
+    for (int i = 0; i < 32; i++) {
+      const uint8_t byte = key[17 * b + 1 + i / 2];
+      const uint8_t c = (uint8_t)((byte >> (4 * (i & 1))) & 15);
+      out[32 * b + i] = (float)(oracle_e2m1_value(c) * s);
+    }
+  }
+}
+
+static float or_bf16_round(float x) { return or_bf16_to_f32(oracle_bf16_from_f32(x)); }
+
+/* [CPU] `apply_compressed_rope`: pairs (2p, 2p+1) of the tail rotated by
+ * position * frequency(p), frequency blending base^(-2p/rope) with a sixteenth
+ * of it over pairs 15..25; fp32 arithmetic, each result rounded to bf16. */
+void oracle_compressed_rope(float* tail, int64_t rope, int64_t position) {
+  const float base = 160000.0f, factor = 16.0f, low = 15.0f, high = 25.0f;
+  const float pos = (float)position;
+  for (int64_t p = 0; p < rope / 2; p++) {
+    float ramp = ((float)p - low) / (high - low);
+    if (ramp < 0.0f) ramp = 0.0f;
+    if (ramp > 1.0f) ramp = 1.0f;
+    const float bf = powf(base, -((float)(2 * p)) / (float)rope);
+    const float a = bf * (1.0f - ramp);
+    const float c = bf / factor * ramp;
+    const float freq = a + c;
+    const float ang = pos * freq;
+    const float sn = sinf(ang), cs = cosf(ang);
+    const float re = tail[2 * p], im = tail[2 * p + 1];
+    const float r0 = re * cs, r1 = im * sn, i0 = re * sn, i1 = im * cs;
+    tail[2 * p] = or_bf16_round(r0 - r1);
+    tail[2 * p + 1] = or_bf16_round(i0 + i1);
+  }
+}
+
+/* The fast Walsh-Hadamard butterflies in fp32 (no scaling), n a power of two. */
+void oracle_hadamard_f32(float* v, int64_t n) {
+  for (int64_t span = 1; span < n; span *= 2)
+    for (int64_t start = 0; start < n; start += 2 * span)
+      for (int64_t o = 0; o < span; o++) {
+        const float a = v[start + o], b = v[start + o + span];
+        v[start + o] = a + b;
+        v[start + o + span] = a - b;
+      }
+}
+
+/* [CPU] `finalize_index_query`: bf16 round, compressed RoPE on the last `rope`
+ * dims at `position`, Hadamard then times 1/sqrtf(dim) rounded to bf16, FP4
+ * round trip. Returns 0, or -1 on a non-finite value in the FP4 step. */
+int oracle_finalize_index_query(const float* src, int64_t dim, int64_t rope, int64_t position, float* q) {
+  for (int64_t d = 0; d < dim; d++) q[d] = or_bf16_round(src[d]);
+  oracle_compressed_rope(q + dim - rope, rope, position);
+  oracle_hadamard_f32(q, dim);
+  const float scale = 1.0f / sqrtf((float)dim);
+  for (int64_t d = 0; d < dim; d++) q[d] = or_bf16_round(q[d] * scale);
+  for (int64_t b = 0; b < dim / 32; b++) {
+    uint8_t sc, packed[16];
+    float out[32];
+    if (oracle_fp4_quantize_block32(q + 32 * b, &sc, packed, out) != 0) return -1;
+    for (int i = 0; i < 32; i++) q[32 * b + i] = out[i];
+  }
+  return 0;
+}
+
+/* Rust `f32::total_cmp` key: a strictly monotone map of the bits to int32. */
+static int32_t or_total_key(float x) {
+  int32_t i;
+  memcpy(&i, &x, 4);
+  return i ^ (int32_t)(((uint32_t)(i >> 31)) >> 1);
+}
+
+#define OR_SEL_NONFINITE 1u /* a score is not finite (the CPU page raises)       */
+#define OR_SEL_TIE 2u       /* two candidate scores are equal (the CPU page raises) */
+#define OR_SEL_GEOMETRY 4u  /* total < S                                          */
+
+/* Scores and selection for every (b, s).
+ *   iq  [B, S, H, dim] fp32 index queries; iw [B, S, H] fp32 weights
+ *   keys [B, Rcap, dim/32*17] FP4 index keys
+ *   sel  [B, S, K] int32 out: records by (-score, +record), -1 padded
+ *   scores (optional) [B, S, Rcap] fp32 out: the candidates' scores (others NaN)
+ * Query s sits at position total - S + s and scores records
+ * r < min((position + 1) / 4, Rcap). score = sum over heads in ascending order
+ * of max(dot, 0) * w * ((1/sqrtf(dim)) / sqrtf(H)), dot the ascending fp32 dot
+ * of the finalized query with the decoded key. */
+uint32_t oracle_csa_index_select(const float* iq, const float* iw, const uint8_t* keys, int64_t batch,
+                                 int64_t seq, int64_t heads, int64_t dim, int64_t rope, int64_t record_cap,
+                                 int64_t total, int64_t topk, int32_t* sel, float* scores_out) {
+  if (total < seq) return OR_SEL_GEOMETRY;
+  const int64_t kb = dim / 32 * 17;
+  float ws = 1.0f / sqrtf((float)dim);
+  ws = ws / sqrtf((float)heads);
+  float* tq = (float*)malloc(sizeof(float) * (size_t)(heads * dim));
+  float* key = (float*)malloc(sizeof(float) * (size_t)dim);
+  float* sc = (float*)malloc(sizeof(float) * (size_t)(record_cap > 0 ? record_cap : 1));
+  unsigned char* taken = (unsigned char*)malloc((size_t)(record_cap > 0 ? record_cap : 1));
+  if (!tq || !key || !sc || !taken) {
+    free(tq);
+    free(key);
+    free(sc);
+    free(taken);
+    return (uint32_t)-1;
+  }
+  uint32_t flags = 0;
+  for (int64_t b = 0; b < batch; b++) {
+    for (int64_t s = 0; s < seq; s++) {
+      const int64_t pos = total - seq + s;
+      int64_t n = (pos + 1) / 4;
+      if (n > record_cap) n = record_cap;
+      if (n < 0) n = 0;
+      for (int64_t h = 0; h < heads; h++)
+        if (oracle_finalize_index_query(iq + ((b * seq + s) * heads + h) * dim, dim, rope, pos, tq + h * dim) != 0)
+          flags |= OR_SEL_NONFINITE;
+      const float* w = iw + (b * seq + s) * heads;
+      for (int64_t r = 0; r < n; r++) {
+        oracle_fp4_decode_key(keys + (b * record_cap + r) * kb, dim, key);
+        float score = 0.0f;
+        for (int64_t h = 0; h < heads; h++) {
+          float acc = 0.0f;
+          for (int64_t d = 0; d < dim; d++) {
+            const float prod = tq[h * dim + d] * key[d];
+            acc = acc + prod;
+          }
+          const float relu = acc > 0.0f ? acc : 0.0f;
+          const float t0 = relu * w[h];
+          const float t1 = t0 * ws;
+          score = score + t1;
+        }
+        if (!isfinite(score)) flags |= OR_SEL_NONFINITE;
+        sc[r] = score;
+      }
+      if (scores_out) {
+        float* so = scores_out + (b * seq + s) * record_cap;
+        for (int64_t r = 0; r < record_cap; r++) so[r] = r < n ? sc[r] : NAN;
+      }
+      /* exact ties (the CPU page rejects them) */
+      for (int64_t i = 0; i < n; i++)
+        for (int64_t j = i + 1; j < n; j++)
+          if (sc[i] == sc[j]) flags |= OR_SEL_TIE;
+      /* repeated selection of the first record in the (-score, +record) order */
+      int32_t* out = sel + (b * seq + s) * topk;
+      for (int64_t j = 0; j < topk; j++) out[j] = -1;
+      memset(taken, 0, (size_t)n);
+      for (int64_t j = 0; j < topk && j < n; j++) {
+        int64_t best = -1;
+        for (int64_t r = 0; r < n; r++) {
+          if (taken[r]) continue;
+          if (best < 0 || or_total_key(sc[r]) > or_total_key(sc[best])) best = r;
+        }
+        taken[best] = 1;
+        out[j] = (int32_t)best;
+      }
+    }
+  }
+  free(tq);
+  free(key);
+  free(sc);
+  free(taken);
+  return flags;
+}
