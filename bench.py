@@ -51,7 +51,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--workload", default="decode_bf16",
-                   choices=["decode_bf16", "decode_fp8", "prefill_bf16", "dense_gqa", "csa_decode"])
+                   choices=["decode_bf16", "decode_fp8", "prefill_bf16", "dense_gqa", "csa_decode",
+                            "csa_index_decode"])
     p.add_argument("--rotate", type=int, default=8, help="independent (query, index) sets")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
@@ -74,6 +75,7 @@ KERNEL_SOURCES = {
     "generic_forward_kernel": ["k_forward_generic.hip", "sa_internal.h"],
     "gqa_forward_kernel": ["k_forward_gqa.hip", "sa_internal.h", "sa_mfma_dev.h"],
     "csa_attention_kernel": ["k_csa_attention.hip", "sa_internal.h", "sa_mfma_dev.h", "sa_quant_dev.h"],
+    "csa_index_score_kernel": ["k_csa_index.hip", "sa_internal.h", "sa_mfma_dev.h"],
 }
 CALIB_BYTES = 256 << 20
 
@@ -407,14 +409,136 @@ class CsaSetup:
                           f"all {w.heads} heads, {cands * reps} candidates, {total_t:.1f} s of oracle time"}
 
 
+class CsaIndexSetup:
+    """Device-resident inputs and the step of the CSA selection producer:
+    index queries and weights fp32, FP4 index keys drawn as random bytes on the
+    device, the caller-owned workspace, R rotating (query, weight) sets."""
+
+    path = 6
+    splits = 1
+
+    def __init__(self, name, rotate):
+        import torch
+
+        import sa_workloads as W
+        import sparse_attention_kv_append_amd as sa
+        self.torch, self.W, self.sa = torch, W, sa
+        self.w = w = W.CSA_INDEX_WORKLOADS[name]
+        self.name = name
+        self.R = rotate
+        dev = "cuda"
+        B, S, H = w.batch, w.seq, w.heads
+        self.ctx = sa.Context(num_heads=16, kv_num_heads=1, head_dim_qk=64, head_dim_v=64, dtype=sa.SA_F32)
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed * 1000 + 77)
+        keys = torch.randint(0, 256, (B, w.key_cap, 68), generator=g, device=dev, dtype=torch.uint8)
+        keys[:, :, 0::17] = torch.randint(122, 127, (B, w.key_cap, 4), generator=g, device=dev,
+                                          dtype=torch.uint8)
+        self.keys = keys
+        self.iqs = [W.torch_normal_f32((B, S, H, 128), w.seed * 1000 + 500 + r, dev) for r in range(self.R)]
+        self.iws = [W.torch_normal_f32((B, S, H), w.seed * 1000 + 600 + r, dev) for r in range(self.R)]
+        self.idxs = self.iqs  # rotation sets
+        self.total = torch.tensor([w.total], dtype=torch.int64, device=dev)
+        self.sel = torch.empty((B, w.out_heads, S, w.topk), dtype=torch.int32, device=dev)
+        self.ws = torch.empty(self.ctx.csa_index_workspace_bytes(B, S, H, w.key_cap), dtype=torch.uint8,
+                              device=dev)
+        self.fp8 = False
+
+    def fused_step(self):
+        return False
+
+    def step(self, i):
+        r = i % len(self.iqs)
+        self.ctx.reset_error_async()
+        self.ctx.csa_index_select(self.iqs[r], self.iws[r], self.keys, self.total, self.sel, self.ws)
+
+    def _n(self):
+        w = self.w
+        return [min((w.total - w.seq + s + 1) // 4, w.key_cap) for s in range(w.seq)]
+
+    def tokens_per_step(self):
+        """Records scored per step (all index heads of a (batch, query) counted once)."""
+        return self.w.batch * sum(self._n())
+
+    def kernel_work(self):
+        """Algorithmic bytes and flops of one score launch."""
+        w = self.w
+        n = self.tokens_per_step()
+        keys = n * 68
+        q = w.batch * w.seq * w.heads * (128 * 2 + 4)   # the finalized query (bf16) and the weights
+        scores = n * 4
+        flops = n * w.heads * 2 * 128
+        return dict(bytes=keys + q + scores, gather_bytes=keys, flops=flops)
+
+    def step_bytes(self):
+        w = self.w
+        n = self.tokens_per_step()
+        return (n * 68 + n * 4 * 2 + w.batch * w.seq * w.heads * (128 * 4 * 2 + 128 * 2 + 4)
+                + w.batch * w.out_heads * w.seq * w.topk * 4)
+
+    def roofline(self, kw, k_avg_s):
+        return "hbm", HBM_PEAK_GBS, "GB/s", kw["bytes"] / k_avg_s / 1e9
+
+    def dtype_name(self):
+        return "fp4"
+
+    def config(self, use_graph, nset, tokens, ms_per_step):
+        w = self.w
+        return {"workload": f"{w.name}: CSA ratio-4 selection producer, batch {w.batch}, q_seq {w.seq}, "
+                            f"{w.heads} index heads of 128 dims, {w.key_cap} FP4 E2M1 block-32 index keys "
+                            f"(68 B), total {w.total}, top-{w.topk}, {'graph replay' if use_graph else 'eager'}, "
+                            f"{nset} rotating query sets",
+                "records_scored_per_step": tokens, "splits": 1,
+                "step_calls": "reset_error_async + csa_index_select (finalize, score, select launches)",
+                "step_hbm_GBps": self.step_bytes() / (ms_per_step / 1e3) / 1e9}
+
+    def oracle_inputs(self, b):
+        """Batch entry b of rotation set 0 as host arrays (generator outputs)."""
+        return {"index_query": self.iqs[0][b:b + 1].cpu().numpy(),
+                "index_weight": self.iws[0][b:b + 1].cpu().numpy(),
+                "index_keys": self.keys[b:b + 1].cpu().numpy()}
+
+    def cpu_baseline(self, target_s):
+        """The oracle (unchanged) on the first batch entries, one per thread,
+        repeated until the target time is reached."""
+        import threading
+
+        import oracle
+        w = self.w
+        threads = max(1, min(16, os.cpu_count() or 1))
+        nb = min(w.batch, threads)
+        inputs = [self.oracle_inputs(b) for b in range(nb)]
+
+        def one(inp):
+            oracle.csa_index_select(inp["index_query"], inp["index_weight"], inp["index_keys"], w.total, w.topk)
+
+        reps, total_t = 0, 0.0
+        while total_t < target_s and reps < 200:
+            t0 = time.perf_counter()
+            ts = [threading.Thread(target=one, args=(inp,)) for inp in inputs]
+            for t in ts:
+                t.start()
+            for t in ts:
+                t.join()
+            total_t += time.perf_counter() - t0
+            reps += 1
+        recs = nb * sum(self._n()) * reps
+        return {"value": recs / total_t, "unit": "records scored/s", "cores": nb, "kind": "oracle",
+                "sample": f"the first {nb} (batch, query) rows of the same workload x {reps}, one thread each, "
+                          f"all {w.heads} index heads, {recs} records scored and ranked, {total_t:.1f} s"}
+
+
 def make_setup(name, rotate):
     import sa_workloads as W
+    if name in W.CSA_INDEX_WORKLOADS:
+        return CsaIndexSetup(name, rotate)
     return CsaSetup(name, rotate) if name in W.CSA_WORKLOADS else Setup(name, rotate)
 
 
 def kernel_name(setup):
     return {0: "generic_forward_kernel", 1: "mla_forward_kernel", 2: "latent_forward_kernel",
-            3: "pair_forward_kernel", 4: "gqa_forward_kernel", 5: "csa_attention_kernel"}[setup.path]
+            3: "pair_forward_kernel", 4: "gqa_forward_kernel", 5: "csa_attention_kernel",
+            6: "csa_index_score_kernel"}[setup.path]
 
 
 def counters_for(setup):
@@ -704,7 +828,7 @@ def main():
     result = {
         "metric": "selected KV tokens attended/sec (decode) + achieved HBM GB/s % of peak",
         "value": tokens / (ms_per_step / 1e3),
-        "unit": "selected tokens/s" if s.path != 5 else "candidates/s",
+        "unit": {5: "candidates/s", 6: "records scored/s"}.get(s.path, "selected tokens/s"),
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,

@@ -86,6 +86,8 @@ enum { SA_IDX_I32 = 0, SA_IDX_I64 = 1 };
 #define SA_ERR_APPEND_ANY 1024u
 #define SA_ERR_CSA_DENOM 0x800u      /* sparse_attn_csa_forward: a softmax
                                         denominator not finite and positive      */
+#define SA_ERR_INDEX_NONFINITE 0x1000u /* sparse_attn_csa_index_select: a record's
+                                          score is not finite                     */
 
 typedef struct {
   int32_t num_heads;      /* Hq > 0 (IndexShare attr num_heads)                         */
@@ -223,6 +225,47 @@ sa_status sparse_attn_step(sparse_attn_ctx* ctx, const void* q, int64_t batch, i
                            int64_t cur_len, int32_t cur_is_unquantized_bf16, int32_t* present_len,
                            const void* indices, int64_t index_heads, int64_t width, void* y,
                            int32_t reset_error);
+
+/* CSA ratio-4 selection producer (the indexer): the index-selection stage of
+ * the compressed-sparse-attention operator's ratio-4 path (onnx-runtime-ep-cpu,
+ * src/kernels/compressed_sparse_attention.rs, `select_ratio4_topk` and
+ * `finalize_index_query`; onnx-runtime-ep-cuda, same file, kernel
+ * `csa_ratio4_index_select`). For batch b and query s at position
+ * p = total - S + s:
+ *   - each index head's query is finalized: rounded to bf16, the compressed
+ *     RoPE applied to its last 64 dims at position p, Walsh-Hadamard
+ *     transformed and scaled by 1/sqrt(128) (rounded to bf16), and rounded
+ *     through FP4 E2M1 block-32 (E8M0 scale floor(log2 amax) - 2 + 127,
+ *     nearest E2M1 value, ties to the even code);
+ *   - every record r < min((p + 1) / 4, key_cap) is scored
+ *     sum over heads h (ascending) of max(q_h . k_r, 0) * w_h * ((1/sqrt(128)) / sqrt(H)),
+ *     in fp32;
+ *   - the first K records in (-score, +record) order are written, then -1.
+ *   index_query   [B, S, H, 128] fp32; H a multiple of 16, at most 64
+ *   index_weight  [B, S, H] fp32
+ *   index_keys    [B, key_cap, 68] bytes: 4 blocks of [E8M0 scale, 16 bytes of
+ *                 E2M1 codes, element 2i in the low nibble]; key_cap <= 32768
+ *   total_len     DEVICE pointer to one int64: total_sequence_length
+ *   selected      [B, out_heads, S, K] int32 out; every index-head row gets the
+ *                 same selection (as the pages replicate it); 1 <= K <= 2048
+ *   workspace     device scratch of sparse_attn_csa_index_workspace_bytes(B, S, H,
+ *                 key_cap) bytes, owned by the caller (the scores and the
+ *                 finalized queries); contents on return are unspecified
+ * Exact score ties, which the CPU page rejects, are ordered by ascending
+ * record. Host errors: SA_E_ARG (NULL pointer, size < 1), SA_E_UNSUPPORTED
+ * (H, K or key_cap out of range). Device: SA_ERR_CSA_GEOMETRY when total < S
+ * (nothing written); SA_ERR_INDEX_NONFINITE when a score is not finite (it is
+ * still ranked, by the fp32 total order). Asynchronous and capturable. */
+sa_status sparse_attn_csa_index_select(sparse_attn_ctx* ctx, const float* index_query,
+                                       const float* index_weight, const uint8_t* index_keys,
+                                       int64_t batch, int64_t q_seq, int64_t heads, int64_t key_cap,
+                                       const int64_t* total_len, int64_t topk, int64_t out_heads,
+                                       int32_t* selected, void* workspace);
+
+/* Bytes of scratch sparse_attn_csa_index_select needs for these sizes (0 on a
+ * size < 1). */
+size_t sparse_attn_csa_index_workspace_bytes(int64_t batch, int64_t q_seq, int64_t heads,
+                                             int64_t key_cap);
 
 /* CSA ratio-4 selected sink attention: the attention stage of the
  * compressed-sparse-attention operator's ratio-4 path (onnx-runtime-ep-cuda,

@@ -689,7 +689,11 @@ static float or_bf16_round(float x) { return or_bf16_to_f32(oracle_bf16_from_f32
 
 /* [CPU] `apply_compressed_rope`: pairs (2p, 2p+1) of the tail rotated by
  * position * frequency(p), frequency blending base^(-2p/rope) with a sixteenth
- * of it over pairs 15..25; fp32 arithmetic, each result rounded to bf16. */
+ * of it over pairs 15..25; fp32 arithmetic, each result rounded to bf16.
+ * Reading: the page calls fp32 pow, sin and cos; here each is the exactly
+ * rounded fp32 value (evaluated in double, rounded once), which any
+ * implementation can reproduce; an fp32 library's last-bit differences would
+ * otherwise flip FP4 codes downstream (many FP4 roundings land on ties). */
 void oracle_compressed_rope(float* tail, int64_t rope, int64_t position) {
   const float base = 160000.0f, factor = 16.0f, low = 15.0f, high = 25.0f;
   const float pos = (float)position;
@@ -697,12 +701,12 @@ void oracle_compressed_rope(float* tail, int64_t rope, int64_t position) {
     float ramp = ((float)p - low) / (high - low);
     if (ramp < 0.0f) ramp = 0.0f;
     if (ramp > 1.0f) ramp = 1.0f;
-    const float bf = powf(base, -((float)(2 * p)) / (float)rope);
+    const float bf = (float)pow((double)base, (double)(-((float)(2 * p)) / (float)rope));
     const float a = bf * (1.0f - ramp);
     const float c = bf / factor * ramp;
     const float freq = a + c;
     const float ang = pos * freq;
-    const float sn = sinf(ang), cs = cosf(ang);
+    const float sn = (float)sin((double)ang), cs = (float)cos((double)ang);
     const float re = tail[2 * p], im = tail[2 * p + 1];
     const float r0 = re * cs, r1 = im * sn, i0 = re * sn, i1 = im * cs;
     tail[2 * p] = or_bf16_round(r0 - r1);

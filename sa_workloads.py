@@ -42,6 +42,15 @@ uniformly, in random order (the order a top-k by score leaves), padded with
 * ``csa_small``    batch 2, 3 queries, 32 heads, Tcur 140, total 300, K 40.
 * ``csa_decode``   batch 64, 1 query, 64 heads, Tcur 128, total 65536 (16384
                    records per batch entry), K 512.
+
+CSA selection producer (``CSA_INDEX_WORKLOADS``, ``make_csa_index_numpy``):
+index queries [B, S, H, 128] and weights [B, S, H] fp32 N(0, 1); FP4 index
+keys [B, key_cap, 68] drawn as bytes: every code nibble uniform over the 16
+E2M1 codes, every block's scale byte uniform over 122..126.
+
+* ``csa_index_small``  batch 2, 3 queries, 16 index heads, 300 keys, total 900, K 40.
+* ``csa_index_decode`` batch 64, 1 query, 64 index heads, 16384 keys, total
+                       65536, K 512.
 """
 from __future__ import annotations
 
@@ -310,3 +319,42 @@ def make_csa_numpy(w: CsaWorkload) -> dict:
     sel = csa_selection(w, rng)
     return {"workload": w, "query": q, "current_kv": ckv, "record_rows": rows, "sink": sink,
             "selected": sel}
+
+
+@dataclass(frozen=True)
+class CsaIndexWorkload:
+    name: str
+    batch: int
+    seq: int
+    heads: int
+    key_cap: int
+    total: int
+    topk: int
+    out_heads: int = 1
+    seed: int = 0
+
+    def scaled(self, **kw) -> "CsaIndexWorkload":
+        return replace(self, **kw)
+
+
+CSA_INDEX_WORKLOADS = {
+    "csa_index_small": CsaIndexWorkload("csa_index_small", batch=2, seq=3, heads=16, key_cap=300, total=900,
+                                        topk=40, out_heads=2, seed=30),
+    "csa_index_decode": CsaIndexWorkload("csa_index_decode", batch=64, seq=1, heads=64, key_cap=16384,
+                                         total=65536, topk=512, seed=31),
+}
+
+
+def csa_index_keys(rng: np.random.Generator, batch: int, key_cap: int) -> np.ndarray:
+    """[B, key_cap, 68] FP4 index keys as random bytes (codes uniform, scale bytes 122..126)."""
+    keys = rng.integers(0, 256, (batch, key_cap, 68), dtype=np.uint8)
+    keys[:, :, 0::17] = rng.integers(122, 127, (batch, key_cap, 4), dtype=np.uint8)
+    return keys
+
+
+def make_csa_index_numpy(w: CsaIndexWorkload) -> dict:
+    rng = np.random.default_rng(w.seed)
+    iq = rng.standard_normal((w.batch, w.seq, w.heads, 128), dtype=np.float32)
+    iw = rng.standard_normal((w.batch, w.seq, w.heads), dtype=np.float32)
+    keys = csa_index_keys(rng, w.batch, w.key_cap)
+    return {"workload": w, "index_query": iq, "index_weight": iw, "index_keys": keys}

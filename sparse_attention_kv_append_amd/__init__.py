@@ -29,7 +29,7 @@ SA_ERR_SENTINEL, SA_ERR_AFTER_PAD, SA_ERR_RANGE = 0x01, 0x02, 0x04
 SA_ERR_DUPLICATE, SA_ERR_ORDER, SA_ERR_ALL_PAD = 0x08, 0x10, 0x20
 SA_ERR_APPEND_CAPACITY, SA_ERR_QUANT_NONFINITE = 0x40, 0x80
 SA_ERR_INDEX_ANY, SA_ERR_APPEND_ANY = 512, 1024
-SA_ERR_CSA_GEOMETRY, SA_ERR_CSA_DENOM = 0x100, 0x800
+SA_ERR_CSA_GEOMETRY, SA_ERR_CSA_DENOM, SA_ERR_INDEX_NONFINITE = 0x100, 0x800, 0x1000
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_DTYPE", 4: "SA_E_CAPACITY",
                 5: "SA_E_UNSUPPORTED", 6: "SA_E_HIP", 7: "SA_E_STATE", 8: "SA_E_INDEX"}
@@ -37,7 +37,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_DTYPE", 4: 
 EXPORTS = [
     "sparse_attn_create", "sparse_attn_destroy", "sparse_attn_set_stream",
     "sparse_attn_kv_append", "sparse_attn_validate_indices", "sparse_attn_forward", "sparse_attn_step",
-    "sparse_attn_csa_forward",
+    "sparse_attn_csa_forward", "sparse_attn_csa_index_select", "sparse_attn_csa_index_workspace_bytes",
     "sparse_attn_reset_error_async", "sparse_attn_read_error", "sparse_attn_last_error",
     "sparse_attn_query_plan", "sparse_attn_profile_enable", "sparse_attn_profile_read",
     "sparse_attn_version",
@@ -93,6 +93,8 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
         "sparse_attn_step": ([V, V, I64, I64, V, I64, V, V, I64, I32, V, V, I64, I64, V, I32], st),
         "sparse_attn_csa_forward": ([V, V, I64, I64, I64, V, I64, V, I64, V, I64, I64, V, V, V, V,
                                      ctypes.c_float, V], st),
+        "sparse_attn_csa_index_select": ([V, V, V, V, I64, I64, I64, I64, V, I64, I64, V, V], st),
+        "sparse_attn_csa_index_workspace_bytes": ([I64, I64, I64, I64], ctypes.c_size_t),
         "sparse_attn_reset_error_async": ([V], st),
         "sparse_attn_read_error": ([V, ctypes.POINTER(ctypes.c_uint32),
                                     ctypes.POINTER(ctypes.c_uint64)], st),
@@ -218,6 +220,21 @@ class Context:
             records.shape[1], _ptr(selected), selected.shape[1], selected.shape[3], _ptr(head_sink),
             _ptr(bias), None if bias_dims is None else ctypes.cast(bias_dims, ctypes.c_void_p),
             _ptr(total_len), float(scale), _ptr(y)))
+
+    def csa_index_workspace_bytes(self, batch, q_seq, heads, key_cap):
+        return int(self.lib.sparse_attn_csa_index_workspace_bytes(batch, q_seq, heads, key_cap))
+
+    def csa_index_select(self, index_query, index_weight, index_keys, total_len, selected, workspace):
+        """CSA ratio-4 selection producer. index_query [B, S, H, 128] f32,
+        index_weight [B, S, H] f32, index_keys [B, key_cap, 68] u8, total_len
+        int64 device tensor of one element, selected [B, out_heads, S, K] i32
+        (written), workspace a device tensor of csa_index_workspace_bytes bytes."""
+        B, S, H, _ = index_query.shape
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_csa_index_select(
+            self.handle, _ptr(index_query), _ptr(index_weight), _ptr(index_keys), B, S, H,
+            index_keys.shape[1], _ptr(total_len), selected.shape[3], selected.shape[1], _ptr(selected),
+            _ptr(workspace)))
 
     def reset_error_async(self):
         self._sync_stream()

@@ -461,6 +461,42 @@ sa_status sparse_attn_csa_forward(sparse_attn_ctx* c, const float* query, int64_
   return sa::launch_csa_attention(c, a);
 }
 
+size_t sparse_attn_csa_index_workspace_bytes(int64_t batch, int64_t q_seq, int64_t heads, int64_t key_cap) {
+  if (batch < 1 || q_seq < 1 || heads < 1 || key_cap < 1) return 0;
+  return sa::csa_index_workspace_bytes(batch * q_seq, heads, key_cap);
+}
+
+sa_status sparse_attn_csa_index_select(sparse_attn_ctx* c, const float* index_query, const float* index_weight,
+                                       const uint8_t* index_keys, int64_t batch, int64_t q_seq, int64_t heads,
+                                       int64_t key_cap, const int64_t* total_len, int64_t topk,
+                                       int64_t out_heads, int32_t* selected, void* workspace) {
+  if (!live(c)) return SA_E_STATE;
+  c->last_error.clear();
+  if (!index_query || !index_weight || !index_keys || !total_len || !selected || !workspace)
+    return set_error(c, SA_E_ARG, "csa_index_select: a required pointer is NULL");
+  if (batch < 1 || q_seq < 1 || heads < 1 || key_cap < 1 || topk < 1 || out_heads < 1)
+    return set_error(c, SA_E_ARG, "csa_index_select: every size must be at least 1");
+  if (heads % 16 != 0 || heads > 64)
+    return set_error(c, SA_E_UNSUPPORTED, "csa_index_select: index heads must be 16, 32, 48 or 64");
+  if (topk > 2048) return set_error(c, SA_E_UNSUPPORTED, "csa_index_select: selected width above 2048");
+  if (key_cap > 32768) return set_error(c, SA_E_UNSUPPORTED, "csa_index_select: more than 32768 index keys");
+  if (batch * q_seq >= 65536) return set_error(c, SA_E_UNSUPPORTED, "csa_index_select: batch * q_seq >= 65536");
+  sa::CsaIndexArgs a;
+  a.iq = index_query;
+  a.iw = index_weight;
+  a.keys = index_keys;
+  a.total = total_len;
+  a.selected = selected;
+  a.workspace = workspace;
+  a.batch = batch;
+  a.q_seq = q_seq;
+  a.heads = heads;
+  a.key_cap = key_cap;
+  a.topk = topk;
+  a.out_heads = out_heads;
+  return sa::launch_csa_index_select(c, a);
+}
+
 sa_status sparse_attn_read_error(sparse_attn_ctx* c, uint32_t* word, uint64_t* first_bad) {
   if (!live(c)) return SA_E_STATE;
   sa::ErrorBlock eb;
@@ -503,6 +539,10 @@ sa_status sparse_attn_read_error(sparse_attn_ctx* c, uint32_t* word, uint64_t* f
   if (eb.word & SA_ERR_CSA_GEOMETRY) {
     if (!msg.empty()) msg += "; ";
     msg += "csa_forward: total_len does not fit the query, current_kv, record or bias sizes";
+  }
+  if (eb.word & SA_ERR_INDEX_NONFINITE) {
+    if (!msg.empty()) msg += "; ";
+    msg += "csa_index_select: a record's score is not finite";
   }
   if (eb.word & SA_ERR_CSA_DENOM) {
     if (!msg.empty()) msg += "; ";

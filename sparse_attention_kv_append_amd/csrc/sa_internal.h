@@ -183,6 +183,18 @@ struct CsaArgs {
   float scale;
 };
 sa_status launch_csa_attention(sparse_attn_ctx* c, const CsaArgs& a);
+// CSA ratio-4 selection producer (index head dim 128, RoPE 64, 68-byte FP4 keys)
+struct CsaIndexArgs {
+  const float* iq;         // [B, S, H, 128]
+  const float* iw;         // [B, S, H]
+  const uint8_t* keys;     // [B, key_cap, 68]
+  const int64_t* total;    // device: total_sequence_length
+  int32_t* selected;       // [B, out_heads, S, topk]
+  void* workspace;         // csa_index_workspace_bytes(B S, H, key_cap)
+  int64_t batch, q_seq, heads, key_cap, topk, out_heads;
+};
+size_t csa_index_workspace_bytes(int64_t rows, int64_t H, int64_t kcap);
+sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a);
 sa_status launch_mla_combine(sparse_attn_ctx* c, int64_t rows, int64_t q_seq, int splits, uint16_t* y);
 
 sa_status set_error(sparse_attn_ctx* c, sa_status s, const std::string& msg);
