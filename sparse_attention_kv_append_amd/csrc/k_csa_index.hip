@@ -22,10 +22,10 @@
 //     The head sum is then taken one record per thread, in ascending head
 //     order with the pages' fp32 operations (relu, times w, times the scale,
 //     add), so a score is the pages' fp32 score.
-//  3. select: a workgroup per (batch, query): the scores' total-order keys in
-//     LDS, a radix select of the k-th largest key, the winners (ties in
-//     ascending record order) sorted by (-score, +record) with a bitonic sort,
-//     written to every index-head row of the output.
+//  3. select: a workgroup per (batch, query): the k-th largest total-order
+//     key of the scores by a binary search over key values, the winners (ties
+//     in ascending record order) ranked by (-score, +record), written to
+//     every index-head row of the output.
 #include "sa_mfma_dev.h"
 
 // the pages' fp32 arithmetic here is separate multiplies and adds (no fused
@@ -40,10 +40,10 @@ constexpr int ROPE = 64;          // RoPE tail of the index query
 constexpr int KB = 68;            // key bytes: 4 x (1 scale + 16 code bytes)
 constexpr int HMAX = 64;          // index heads
 constexpr int RC = 1024;          // records per score workgroup
-constexpr int RB = 256;           // records per score pass (one per thread)
-constexpr int DSTR = 65;          // LDS row stride (floats) of the dot table
+constexpr int RB = 128;           // records per score pass (one per thread of waves 0, 1)
+constexpr int DSTR = 68;          // LDS row stride (floats) of the dot table (16-byte rows)
 constexpr int KMAX = 2048;        // selected width
-constexpr int NMAX = 32768;       // records per (batch, query) the select keeps in LDS
+constexpr int NMAX = 32768;       // records per (batch, query) (index keys per batch entry)
 }  // namespace cx
 
 // ---------------------------------------------------------------- finalize
@@ -129,11 +129,18 @@ csa_index_finalize_kernel(const float* __restrict__ iq, uint16_t* __restrict__ q
 
 // ---------------------------------------------------------------- score
 
-__global__ void __launch_bounds__(256, 1)
+// A workgroup scores RC records of one (batch, query) in passes of RB: the
+// pass's keys (68 B each, contiguous) are copied to LDS from registers loaded
+// during the previous pass; each wave computes S^T for two 16-record tiles and
+// all heads, writes the fp32 dot products to an LDS table, and threads
+// 0..RB-1 take the head sums (one record each).
+template <int HT>
+__global__ void __launch_bounds__(256)
 csa_index_score_kernel(const uint16_t* __restrict__ qf, const float* __restrict__ iw,
-                       const uint8_t* __restrict__ keys, float* __restrict__ scores, int S, int H,
+                       const uint8_t* __restrict__ keys, float* __restrict__ scores, int S,
                        int64_t kcap, const int64_t* __restrict__ total_ptr, ErrorBlock* __restrict__ eb) {
   using namespace cx;
+  constexpr int H = 16 * HT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
@@ -146,86 +153,104 @@ csa_index_score_kernel(const uint16_t* __restrict__ qf, const float* __restrict_
   if (n > kcap) n = kcap;
   const int64_t c0 = (int64_t)blockIdx.x * RC;
   if (c0 >= n) return;
-  const int HT = H / 16;
+  const int64_t c1 = min(c0 + RC, n);
 
   // the finalized query as B operands: lane (head i16 of tile ht, g) holds
   // dims 32 c + 8 g .. + 7
-  u32x4_l qb[HMAX / 16][4];
+  u32x4_l qb[HT][4];
   const uint16_t* qrow = qf + row * H * D;
 #pragma unroll
-  for (int ht = 0; ht < HMAX / 16; ht++)
+  for (int ht = 0; ht < HT; ht++)
 #pragma unroll
-    for (int c = 0; c < 4; c++)
-      qb[ht][c] = ht < HT ? *(const u32x4_l*)(qrow + (int64_t)(16 * ht + i16) * D + 32 * c + 8 * g)
-                          : (u32x4_l){0u, 0u, 0u, 0u};
+    for (int c = 0; c < 4; c++) qb[ht][c] = *(const u32x4_l*)(qrow + (int64_t)(16 * ht + i16) * D + 32 * c + 8 * g);
   const float ws = (1.0f / sqrtf((float)D)) / sqrtf((float)H);
+  float wv[H];  // the (batch, query)'s head weights, uniform
+#pragma unroll
+  for (int h = 0; h < H; h++) wv[h] = iw[row * H + h];
 
-  uint8_t* kl = smem;                                     // RB keys, 68 B each
-  float* dt = (float*)(smem + RB * KB);                   // [RB][DSTR] dot products
-  float* wl = dt + RB * DSTR;                             // [H] weights
-  if (tid < H) wl[tid] = iw[row * H + tid];
-  const uint8_t* kb = keys + (b * kcap) * KB;
+  uint8_t* kl = smem;                          // RB keys, 68 B each
+  float* dt = (float*)(smem + RB * KB);        // [RB][DSTR] dot products
+  const uint32_t* kb = (const uint32_t*)(keys + (b * kcap) * KB);
+  constexpr int KW = RB * KB / 4;              // dwords of a pass's keys
+  constexpr int KL = (KW + 255) / 256;         // loads per thread
+  uint32_t kr[KL];
+  auto load_keys = [&](int64_t r0) {
+    const int64_t lim = (min((int64_t)RB, kcap - r0)) * (KB / 4);  // dwords inside the capacity
+#pragma unroll
+    for (int j = 0; j < KL; j++) {
+      const int i = tid + 256 * j;
+      kr[j] = (i < KW && i < lim) ? kb[r0 * (KB / 4) + i] : 0u;
+    }
+  };
   bool bad = false;
-
-  for (int64_t r0 = c0; r0 < c0 + RC && r0 < n; r0 += RB) {
+  load_keys(c0);
+  for (int64_t r0 = c0; r0 < c1; r0 += RB) {
     __syncthreads();  // the previous pass's LDS reads are done
-    // stage RB keys (coalesced dwords; records past the capacity read as zeros)
-    const int64_t nk = min((int64_t)RB, kcap - r0);
-    const uint32_t* src = (const uint32_t*)(kb + r0 * KB);
-    for (int i = tid; i < RB * KB / 4; i += 256)
-      ((uint32_t*)kl)[i] = i < nk * (KB / 4) ? src[i] : 0u;
+#pragma unroll
+    for (int j = 0; j < KL; j++) {
+      const int i = tid + 256 * j;
+      if (i < KW) ((uint32_t*)kl)[i] = kr[j];
+    }
+    if (r0 + RB < c1) load_keys(r0 + RB);
     __syncthreads();
-    // S^T for the wave's 64 records: record tiles rt, head tiles ht, blocks c
-    f32x4_l acc[4][HMAX / 16];
+    // S^T for the wave's two record tiles: all operand reads first, then the MFMAs
+    bf16x8_l av[2][4];
 #pragma unroll
-    for (int rt = 0; rt < 4; rt++)
-#pragma unroll
-      for (int ht = 0; ht < HMAX / 16; ht++) acc[rt][ht] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int rt = 0; rt < 4; rt++) {
-      const int rec = 64 * w + 16 * rt + i16;
-      const uint8_t* kr = kl + rec * KB;
+    for (int rt = 0; rt < 2; rt++) {
+      const uint8_t* kq = kl + (32 * w + 16 * rt + i16) * KB;
 #pragma unroll
       for (int c = 0; c < 4; c++) {
         // 4 code bytes at 17 c + 1 + 4 g (unaligned) and the block's scale byte
         const int o = 17 * c + 1 + 4 * g;
-        const uint32_t* wp = (const uint32_t*)(kr + (o & ~3));
+        const uint32_t* wp = (const uint32_t*)(kq + (o & ~3));
         const uint32_t cw = __builtin_amdgcn_alignbyte(wp[1], wp[0], (uint32_t)(o & 3));
-        const uint32_t e = kr[17 * c];
+        const uint32_t e = kq[17 * c];
         const float sc = e == 255u ? __uint_as_float(0x7fc00000u) : (e ? __uint_as_float(e << 23) : 5.877471754e-39f);
         u32x4_l a;
         a[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0));
         a[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1));
         a[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2));
         a[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3));
-        const bf16x8_l av = __builtin_bit_cast(bf16x8_l, a);
-#pragma unroll
-        for (int ht = 0; ht < HMAX / 16; ht++)
-          if (ht < HT)
-            acc[rt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_l, qb[ht][c]),
-                                                                 acc[rt][ht], 0, 0, 0);
+        av[rt][c] = __builtin_bit_cast(bf16x8_l, a);
       }
     }
+    f32x4_l acc[2][HT];
+#pragma unroll
+    for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+      for (int ht = 0; ht < HT; ht++) acc[rt][ht] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+#pragma unroll
+      for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+        for (int ht = 0; ht < HT; ht++)
+          acc[rt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rt][c], __builtin_bit_cast(bf16x8_l, qb[ht][c]),
+                                                               acc[rt][ht], 0, 0, 0);
     // lane (head i16 of tile ht, g) holds records 4 g .. 4 g + 3 of tile rt
 #pragma unroll
-    for (int rt = 0; rt < 4; rt++)
+    for (int rt = 0; rt < 2; rt++)
 #pragma unroll
-      for (int ht = 0; ht < HMAX / 16; ht++)
-        if (ht < HT)
+      for (int ht = 0; ht < HT; ht++)
 #pragma unroll
-          for (int j = 0; j < 4; j++) dt[(64 * w + 16 * rt + 4 * g + j) * DSTR + 16 * ht + i16] = acc[rt][ht][j];
+        for (int j = 0; j < 4; j++) dt[(32 * w + 16 * rt + 4 * g + j) * DSTR + 16 * ht + i16] = acc[rt][ht][j];
     __syncthreads();
     // one record per thread: the head sum in ascending head order
     const int64_t r = r0 + tid;
-    if (r < n) {
-      const float* d = dt + tid * DSTR;
+    if (tid < RB && r < c1) {
+      const f32x4_l* d4 = (const f32x4_l*)(dt + tid * DSTR);
       float score = 0.0f;
-      for (int h = 0; h < H; h++) {
-        const float x = d[h];
-        const float relu = x > 0.0f ? x : 0.0f;
-        const float t0 = relu * wl[h];
-        const float t1 = t0 * ws;
-        score = score + t1;
+#pragma unroll
+      for (int h4 = 0; h4 < H / 4; h4++) {
+        const f32x4_l x4 = d4[h4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const float x = x4[j];
+          const float relu = x > 0.0f ? x : 0.0f;
+          const float t0 = relu * wv[4 * h4 + j];
+          const float t1 = t0 * ws;
+          score = score + t1;
+        }
       }
       bad |= !isfinite(score);
       scores[row * kcap + r] = score;
@@ -242,128 +267,177 @@ __device__ __forceinline__ uint32_t total_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ void __launch_bounds__(256)
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// sum over the 64 lanes (every lane gets it): row rotations (DPP) within each
+// 16-lane row, then the gfx950 permlane swaps across rows
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);  // row_ror:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false);  // row_ror:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false);  // row_ror:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false);  // row_ror:1
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] + a[1];
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return c[0] + c[1];
+}
+
+// One workgroup per (batch, query). Thread t holds the total-order keys of
+// records t, t + 256, ... in registers (key 0 for padding, below every
+// score's key); the k-th largest key is found by a binary search over key
+// values (counting probes reduced without atomics), the winners are placed by
+// a scan, and sorted by rank (each winner counts the larger ones).
+template <int NJ>
+__device__ __forceinline__ void select_row(const float* __restrict__ src, int32_t* __restrict__ outb, int n,
+                                           int K, int S, int out_heads, uint8_t* smem) {
+  using namespace cx;
+  constexpr int NT = 1024, NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t* tot = (uint32_t*)smem;                            // [3 NW] probe (two) and scan partials
+  unsigned long long* win = (unsigned long long*)(tot + 64);  // [KMAX] winners (key, ~record)
+  uint32_t kv[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; j++) {
+    const int i = tid + NT * j;
+    const uint32_t x = total_key(src[i < n ? i : 0]);
+    kv[j] = i < n ? x : 0u;
+  }
+  const int k = min(K, n);
+  uint32_t T = 0;
+  int need = k;
+  if (k > 0 && k < n) {
+    uint64_t lo = 1, hi = 1ull << 32;  // count(>= lo) >= k (every real key is >= 1), count(>= hi) < k
+    uint32_t c_hi = 0;
+    int par = 0;
+    while (hi - lo > 1) {
+      const uint64_t mid = lo + ((hi - lo) >> 1);
+      const uint32_t t = (uint32_t)mid;
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; j++) cnt += kv[j] >= t ? 1u : 0u;
+      cnt = wave_sum_u32(cnt);
+      if (lane == 0) tot[NW * par + w] = cnt;
+      __syncthreads();
+      uint32_t c = 0;
+#pragma unroll
+      for (int q = 0; q < NW; q++) c += tot[NW * par + q];
+      par ^= 1;
+      if (c >= (uint32_t)k) {
+        lo = mid;
+      } else {
+        hi = mid;
+        c_hi = c;
+      }
+    }
+    T = (uint32_t)lo;
+    need = k - (int)c_hi;  // keys > T number c_hi < k; the rest are keys == T
+  }
+  // winners: keys > T, and keys == T unless they straddle the cut
+  uint32_t eq = 0;
+  if (k < n) {
+#pragma unroll
+    for (int j = 0; j < NJ; j++) eq += (kv[j] == T) ? 1u : 0u;
+  }
+  eq = wave_sum_u32(eq);
+  __syncthreads();
+  if (lane == 0) tot[w] = eq;
+  __syncthreads();
+  uint32_t n_eq = 0;
+#pragma unroll
+  for (int q = 0; q < NW; q++) n_eq += tot[q];
+  const bool split_ties = k < n && n_eq > (uint32_t)need;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; j++) {
+    const uint32_t x = kv[j];
+    mine += (tid + NT * j < n && (k >= n || x > T || (x == T && !split_ties))) ? 1u : 0u;
+  }
+  const uint32_t inc = wave_incl_scan(mine);
+  if (lane == 63) tot[2 * NW + w] = inc;
+  __syncthreads();
+  uint32_t slot = inc - mine, n_win = 0;
+  for (int q = 0; q < NW; q++) {
+    const uint32_t v = tot[2 * NW + q];
+    if (q < w) slot += v;
+    n_win += v;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; j++) {
+    const int i = tid + NT * j;
+    const uint32_t x = kv[j];
+    if (i < n && (k >= n || x > T || (x == T && !split_ties)))
+      win[slot++] = ((unsigned long long)x << 32) | (uint32_t)(~(uint32_t)i);
+  }
+  if (split_ties && w == 0) {
+    // equal keys at the cut: the first `need` of them in ascending record order
+    uint32_t taken = 0;
+    for (int i0 = 0; i0 < n && taken < (uint32_t)need; i0 += 64) {
+      const int i = i0 + lane;
+      const bool isT = i < n && total_key(src[i]) == T;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(isT);
+      const uint32_t before = (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
+      if (isT && taken + before < (uint32_t)need)
+        win[n_win + taken + before] = ((unsigned long long)T << 32) | (uint32_t)(~(uint32_t)i);
+      taken += (uint32_t)__builtin_popcountll(bal);
+    }
+  }
+  __syncthreads();
+  // rank sort: the winners' composite keys are distinct; a winner's output
+  // position is the number of larger ones (every thread reads the same
+  // winner at the same time: LDS broadcast)
+  int32_t* out0 = outb;
+  for (int a = tid; a < k; a += NT) {
+    const unsigned long long x = win[a];
+    int r8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int q = 0;
+    for (; q + 8 <= k; q += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; u++) r8[u] += win[q + u] > x ? 1 : 0;
+    }
+    for (; q < k; q++) r8[0] += win[q] > x ? 1 : 0;
+    const int rank = ((r8[0] + r8[1]) + (r8[2] + r8[3])) + ((r8[4] + r8[5]) + (r8[6] + r8[7]));
+    const int32_t rec = (int32_t)(~(uint32_t)(x & 0xffffffffull));
+    for (int h = 0; h < out_heads; h++) out0[(int64_t)h * S * K + rank] = rec;
+  }
+  for (int j = k + tid; j < K; j += NT)
+    for (int h = 0; h < out_heads; h++) out0[(int64_t)h * S * K + j] = -1;
+}
+
+__global__ void __launch_bounds__(1024)
 csa_index_select_kernel(const float* __restrict__ scores, int32_t* __restrict__ sel, int S, int out_heads,
                         int64_t kcap, int K, const int64_t* __restrict__ total_ptr,
                         ErrorBlock* __restrict__ eb) {
   using namespace cx;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;  // (b, s)
   const int s = (int)(row % S);
   const int64_t b = row / S;
-  const int64_t total = *total_ptr;
-  const int64_t pos = total - S + s;
+  const int64_t pos = *total_ptr - S + s;
   int32_t* outb = sel + (b * out_heads * S + s) * K;  // head 0 row; head h at + h S K
   if (pos < s) {  // total < S
-    if (row == 0 && tid == 0) atomicOr(&eb->word, SA_ERR_CSA_GEOMETRY);
+    if (row == 0 && threadIdx.x == 0) atomicOr(&eb->word, SA_ERR_CSA_GEOMETRY);
     return;
   }
   int64_t n64 = (pos + 1) / 4;
   if (n64 > kcap) n64 = kcap;
   const int n = (int)n64;
-  uint32_t* key = (uint32_t*)smem;                       // [NMAX] total-order keys
-  unsigned long long* win = (unsigned long long*)(smem + NMAX * 4);  // [KMAX] winners
-  uint32_t* hist = (uint32_t*)(win + KMAX);              // [256]
-  uint32_t* misc = hist + 256;                           // [8]
   const float* src = scores + row * kcap;
-  for (int i = tid; i < n; i += 256) key[i] = total_key(src[i]);
-  const int k = min(K, n);
-  // threshold T: the k-th largest key (radix select, 8 bits at a time)
-  uint32_t prefix = 0, pmask = 0;
-  int need = k;  // how many of the keys matching the prefix are still to take
-  if (k > 0 && k < n) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      __syncthreads();
-      hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += 256) {
-        const uint32_t x = key[i];
-        if ((x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int acc = 0, d = 255;
-        for (; d > 0; d--) {
-          if (acc + (int)hist[d] >= need) break;
-          acc += (int)hist[d];
-        }
-        misc[0] = (uint32_t)d;
-        misc[1] = (uint32_t)(need - acc);
-      }
-      __syncthreads();
-      prefix |= misc[0] << shift;
-      pmask |= 255u << shift;
-      need = (int)misc[1];
-    }
-  }
-  const uint32_t T = prefix;  // with k < n: keys > T all win, `need` of the keys == T win
-  // gather the winners as (key, ~record) pairs: keys > T anywhere, ties by
-  // ascending record (a scan over contiguous per-thread ranges)
-  __syncthreads();
-  if (tid == 0) misc[2] = 0;
-  const int per = (n + 255) / 256;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int eq = 0;
-  if (k < n)
-    for (int i = lo; i < hi; i++) eq += key[i] == T;
-  // exclusive scan of eq over threads (in LDS)
-  hist[tid] = (uint32_t)eq;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int t = 0; t < 256; t++) {
-      const uint32_t v = hist[t];
-      hist[t] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  int eq_before = (int)hist[tid];
-  for (int i = lo; i < hi; i++) {
-    const uint32_t x = key[i];
-    bool take;
-    if (k >= n) {
-      take = true;
-    } else if (x > T) {
-      take = true;
-    } else if (x == T) {
-      take = eq_before < need;
-      eq_before++;
-    } else {
-      take = false;
-    }
-    if (take) {
-      const uint32_t slot = atomicAdd(&misc[2], 1u);
-      win[slot] = ((unsigned long long)x << 32) | (uint32_t)(~(uint32_t)i);
-    }
-  }
-  __syncthreads();
-  // bitonic sort, descending, over the next power of two >= k (padding 0)
-  int m = 1;
-  while (m < k) m <<= 1;
-  for (int i = k + tid; i < m; i += 256) win[i] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= m; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < m / 2; i += 256) {
-        const int lo_i = (i / stride) * 2 * stride + (i % stride);
-        const int hi_i = lo_i + stride;
-        const bool desc = ((lo_i & size) == 0);
-        const unsigned long long a = win[lo_i], c = win[hi_i];
-        if ((a < c) == desc) {
-          win[lo_i] = c;
-          win[hi_i] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // write every index-head row
-  for (int j = tid; j < K; j += 256) {
-    const int32_t v = j < k ? (int32_t)(~(uint32_t)(win[j] & 0xffffffffull)) : -1;
-    for (int h = 0; h < out_heads; h++) outb[(int64_t)h * S * K + j] = v;
-  }
+  // registers per thread sized to the records (uniform branch)
+  if (n <= 1024 * 4)
+    select_row<4>(src, outb, n, K, S, out_heads, smem);
+  else if (n <= 1024 * 16)
+    select_row<16>(src, outb, n, K, S, out_heads, smem);
+  else
+    select_row<NMAX / 1024>(src, outb, n, K, S, out_heads, smem);
 }
 
 size_t csa_index_workspace_bytes(int64_t rows, int64_t H, int64_t kcap) {
@@ -378,12 +452,15 @@ sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
   float* scores = (float*)a.workspace;
   const size_t sb = ((size_t)rows * (size_t)a.key_cap * 4 + 255) & ~(size_t)255;
   uint16_t* qf = (uint16_t*)((uint8_t*)a.workspace + sb);
-  const size_t score_lds = (size_t)RB * KB + (size_t)RB * DSTR * 4 + HMAX * 4;
-  const size_t select_lds = (size_t)NMAX * 4 + (size_t)KMAX * 8 + 264 * 4;
+  const size_t score_lds = (size_t)RB * KB + (size_t)RB * DSTR * 4;
+  const size_t select_lds = (size_t)64 * 4 + (size_t)KMAX * 8;
+  const void* score_fns[4] = {(const void*)csa_index_score_kernel<1>, (const void*)csa_index_score_kernel<2>,
+                              (const void*)csa_index_score_kernel<3>, (const void*)csa_index_score_kernel<4>};
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)csa_index_score_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)score_lds);
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 4 && e == hipSuccess; i++)
+      e = hipFuncSetAttribute(score_fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)score_lds);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)csa_index_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)select_lds);
@@ -396,13 +473,21 @@ sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
   sa_status st = check_hip(c, hipGetLastError(), "csa index finalize");
   if (st != SA_OK) return st;
   prof_begin(c);
-  hipLaunchKernelGGL(csa_index_score_kernel, dim3((unsigned)((a.key_cap + RC - 1) / RC), (unsigned)rows),
-                     dim3(256), score_lds, c->stream, qf, a.iw, a.keys, scores, (int)a.q_seq, (int)a.heads,
-                     a.key_cap, a.total, c->err);
+  const dim3 sgrid((unsigned)((a.key_cap + RC - 1) / RC), (unsigned)rows);
+#define SA_IDX_SCORE(HTV)                                                                                       \
+  hipLaunchKernelGGL(csa_index_score_kernel<HTV>, sgrid, dim3(256), score_lds, c->stream, qf, a.iw, a.keys, scores, \
+                     (int)a.q_seq, a.key_cap, a.total, c->err)
+  switch (a.heads / 16) {
+    case 1: SA_IDX_SCORE(1); break;
+    case 2: SA_IDX_SCORE(2); break;
+    case 3: SA_IDX_SCORE(3); break;
+    default: SA_IDX_SCORE(4); break;
+  }
+#undef SA_IDX_SCORE
   prof_end(c);
   st = check_hip(c, hipGetLastError(), "csa index score");
   if (st != SA_OK) return st;
-  hipLaunchKernelGGL(csa_index_select_kernel, dim3((unsigned)rows), dim3(256), select_lds, c->stream, scores,
+  hipLaunchKernelGGL(csa_index_select_kernel, dim3((unsigned)rows), dim3(1024), select_lds, c->stream, scores,
                      a.selected, (int)a.q_seq, (int)a.out_heads, a.key_cap, (int)a.topk, a.total, c->err);
   return check_hip(c, hipGetLastError(), "csa index select");
 }

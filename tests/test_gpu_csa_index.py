@@ -153,3 +153,19 @@ def test_index_select_fullsize_sampled_rows():
         same += check_selection(gsel[b:b + 1], osel, scores, s.w.total, s.w.key_cap)
     assert same == len(bs)
     s.ctx.destroy()
+
+
+def test_index_select_ties_at_the_cut(ctx):
+    """Identical keys give identical scores: every cut falls inside a tie, and
+    both sides take the tied records in ascending record order."""
+    w = W.CSA_INDEX_WORKLOADS["csa_index_small"]
+    inp = W.make_csa_index_numpy(w)
+    inp["index_keys"][:, 100:220] = inp["index_keys"][:, 7:8]   # 120 copies of record 7
+    inp["index_keys"][1, :] = inp["index_keys"][1, 3:4]         # batch entry 1: all identical
+    osel, flags, scores = oracle.csa_index_select(inp["index_query"], inp["index_weight"], inp["index_keys"],
+                                                  w.total, w.topk, with_scores=True)
+    assert flags & oracle.SEL_TIE
+    gsel, word, msg, gscores = run_gpu(ctx, inp, w.total, w.topk, w.out_heads)
+    assert word == 0, msg
+    np.testing.assert_array_equal(gsel[:, 0], osel)
+    np.testing.assert_array_equal(gsel[1, 0, :, :w.topk], np.broadcast_to(np.arange(w.topk), (w.seq, w.topk)))
