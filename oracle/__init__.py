@@ -84,8 +84,11 @@ def _load():
         lib.oracle_validate_indices.restype = ctypes.c_uint32
         lib.oracle_forward_rows.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, I64,
                                             P, ctypes.c_int, I64, I64, I64, I64, I64, I64, I64, I64,
-                                            I64, ctypes.c_float, ctypes.c_float, I64, I64, P, P]
+                                            I64, ctypes.c_float, ctypes.c_float, P, ctypes.c_int, P,
+                                            I64, I64, P, P]
         lib.oracle_forward_rows.restype = ctypes.c_int
+        lib.oracle_capacity_lengths.argtypes = [P, ctypes.c_int, P, I64, I64, I64, I64, I64, P, P]
+        lib.oracle_capacity_lengths.restype = None
         lib.oracle_csa_sink_attention.argtypes = [P, I64, I64, I64, P, I64, P, I64, P, I64, I64,
                                                   P, P, P, I64, ctypes.c_float, P]
         lib.oracle_csa_sink_attention.restype = ctypes.c_uint32
@@ -229,12 +232,40 @@ def validate_indices(indices: np.ndarray, bound, *, raise_first: bool = False):
 
 
 # ---------------------------------------------------------------- forward
+def bias_dims(shape, keys=None) -> np.ndarray:
+    """A bias shape of rank <= 4 right-aligned against [B, H, S, keys] and
+    padded with 1 on the left (int64[4])."""
+    shape = tuple(int(d) for d in shape)
+    if len(shape) > 4:
+        raise ValueError(f"attention_bias rank {len(shape)} exceeds 4")
+    return np.array((1,) * (4 - len(shape)) + shape, np.int64)
+
+
+def capacity_lengths(bias, keys: int, cur_len: int, *, batch: int, heads: int, q_seq: int,
+                     bias_dtype: int = 0):
+    """Capacity-mode length recovery (oracle C `oracle_capacity_lengths`):
+    per batch, valid = 1 + the last key column where the bias is finite for
+    any (head, query), and write_pos = valid - cur_len (0 below cur_len).
+    bias holds raw storage of bias_dtype (float32, or uint16 bits)."""
+    bias = np.ascontiguousarray(bias)
+    dims = bias_dims(bias.shape)
+    valid = np.zeros(batch, np.int64)
+    wpos = np.zeros(batch, np.int64)
+    _load().oracle_capacity_lengths(_ptr(bias), bias_dtype, _ptr(dims), batch, heads, q_seq, keys,
+                                    cur_len, _ptr(valid), _ptr(wpos))
+    return valid, wpos
+
+
 def forward(q, kcache, vcache, indices, *, q_dtype: int, cache_fmt: int, kv_layout: int,
             hkv: int, dv: int, rope: int = 0, scale: float = 0.0, softcap: float = 0.0,
+            bias=None, bias_dtype: int | None = None,
             rows=None, threads: int | None = None) -> np.ndarray:
     """Oracle forward. Arrays hold raw storage (bf16/f16 as uint16 bits, fp8 as
     uint8 records). q [B, Hq, Sq, Dk]; kcache [B, Hkv, cap, Dk or record];
     vcache [B, Hkv, cap, Dv] or None; indices [B, Hi, Sq, W].
+    bias: None, or an additive bias of rank <= 4 broadcast right-aligned
+    against [B, Hq, Sq, cap] (raw storage of bias_dtype, default q_dtype),
+    indexed by the selected key's cache position and added after the softcap.
 
     rows: None for all output rows, or an iterable of flattened (b, h, q) row
     ids -- only those rows of the returned fp32 [B*Hq*Sq, Dv] array are set.
@@ -250,6 +281,14 @@ def forward(q, kcache, vcache, indices, *, q_dtype: int, cache_fmt: int, kv_layo
     cap = kcache.shape[2]
     Hi, W = idx.shape[1], idx.shape[3]
     total = B * Hq * Sq
+    bdims = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias)
+        bdims = bias_dims(bias.shape)
+        for a, t in enumerate((B, Hq, Sq, cap)):
+            if bdims[a] not in (1, t):
+                raise ValueError(f"attention_bias shape {bias.shape} is not broadcastable to {(B, Hq, Sq, cap)}")
+        bias_dtype = q_dtype if bias_dtype is None else bias_dtype
     y = np.zeros((total, dv), np.float32)
     row_list = np.arange(total, dtype=np.int64) if rows is None else np.asarray(list(rows), np.int64)
     nthreads = max(1, min(threads or 1, len(row_list)))
@@ -266,7 +305,9 @@ def forward(q, kcache, vcache, indices, *, q_dtype: int, cache_fmt: int, kv_layo
             rc = lib.oracle_forward_rows(
                 _ptr(q), q_dtype, _ptr(kcache), None if vcache is None else _ptr(vcache),
                 cache_fmt, kv_layout, cap, _ptr(idx), int(idx.dtype == np.int64), B, Hq, hkv, Sq,
-                Hi, W, Dk, dv, rope, float(scale), float(softcap), int(chunk[start]),
+                Hi, W, Dk, dv, rope, float(scale), float(softcap),
+                None if bias is None else _ptr(bias), 0 if bias is None else int(bias_dtype),
+                None if bdims is None else _ptr(bdims), int(chunk[start]),
                 int(chunk[end - 1]) + 1, _ptr(y), _ptr(work))
             if rc != 0:
                 errors.append(rc)

@@ -12,7 +12,9 @@
  *   [IS]  onnx-runtime-ep-cuda, src/kernels/index_share.rs (IndexShare):
  *         module doc "Determinism / bit-parity", kernels `build_present`,
  *         `build_present_capacity`, `validate_index_rows`, `index_share_row`,
- *         host `validate_indices` / `index_error`, `launch_rows` (default scale).
+ *         host `validate_indices` / `index_error`, `launch_rows` (default scale),
+ *         `bias_at` and `capacity_write_pos` (the optional additive bias and
+ *         the capacity-mode length it carries).
  *   [CPU] onnx-runtime-ep-cpu, src/kernels/compressed_sparse_attention.rs
  *         (CSA CPU oracle): `CacheFormat` (record layout, `stored_width`),
  *         `dequantize_cache`, `finalize_attention_record` (pack loop),
@@ -346,6 +348,39 @@ uint32_t oracle_validate_indices(const void* idx, int is_i64, int64_t batch, int
 
 /* ---- A4-A8, A10: the forward ([IS] `index_share_row`) ------------------- */
 
+/* The additive bias at logical (b, h, q, k) ([IS] `bias_at`; the CPU page's
+ * `AttentionBias::at`): dims[4] is the bias shape right-aligned against
+ * [B, Hq, Sq, keys] and padded with 1; an extent of 1 broadcasts (index 0),
+ * any other extent takes the coordinate; the offset is row-major. */
+static float or_bias_at(const void* bias, int dtype, const int64_t* dims, int64_t b, int64_t h,
+                        int64_t q, int64_t k) {
+  const int64_t coord[4] = {b, h, q, k};
+  int64_t off = 0;
+  for (int a = 0; a < 4; a++) off = off * dims[a] + (dims[a] == 1 ? 0 : coord[a]);
+  return or_load(bias, off, dtype);
+}
+
+/* Capacity-mode length recovery ([IS] `capacity_write_pos`): when the present
+ * cache aliases a fixed-capacity past, its shape no longer says how many rows
+ * are live, and the bias frontier does. For each batch b:
+ *   valid[b]     = 1 + the largest k < keys with bias(b, h, q, k) finite for
+ *                  some (h, q); 0 when there is none
+ *   write_pos[b] = valid[b] - cur_len, or 0 when valid[b] < cur_len
+ * (the row where this step's cur_len rows go). */
+void oracle_capacity_lengths(const void* bias, int dtype, const int64_t* dims, int64_t batch,
+                             int64_t hq, int64_t sq, int64_t keys, int64_t cur_len, int64_t* valid,
+                             int64_t* write_pos) {
+  for (int64_t b = 0; b < batch; b++) {
+    int64_t v = 0;
+    for (int64_t h = 0; h < hq; h++)
+      for (int64_t q = 0; q < sq; q++)
+        for (int64_t k = 0; k < keys; k++)
+          if (isfinite(or_bias_at(bias, dtype, dims, b, h, q, k)) && k + 1 > v) v = k + 1;
+    valid[b] = v;
+    write_pos[b] = v >= cur_len ? v - cur_len : 0;
+  }
+}
+
 /* Load logical dim d of cache row (b, h, t) as fp32. For fp8 records the
  * whole row is decoded into `scratch` once per (row, key) by the caller. */
 static const float* or_cache_row(const void* cache, int fmt, int64_t row_index, int64_t row_elems,
@@ -366,6 +401,10 @@ static const float* or_cache_row(const void* cache, int fmt, int64_t row_index, 
  *   vcache [B, Hkv, cap, Dv] (SEPARATE) or NULL (SHARED_LATENT: V = K[..., :Dv])
  *   idx    [B, Hi, Sq, W]    i32 or i64, rows already valid
  *   y      [B, Hq, Sq, Dv]   fp32 (the caller rounds to its storage dtype)
+ *   bias   NULL, or the additive attention bias in bias_dtype (0/1/2) whose
+ *          shape, right-aligned against [B, Hq, Sq, cap] and padded with 1 on
+ *          the left, is bias_dims[4]; each extent is 1 (broadcast) or the
+ *          target's
  * scale == 0 means 1/sqrtf(Dk); softcap == 0 means off.
  * work: 2*Dk + W floats of scratch.
  * Returns 0, or -1 on a record that decodes to NaN or an index out of range.
@@ -374,7 +413,8 @@ int oracle_forward_rows(const void* q, int q_dtype, const void* kcache, const vo
                         int cache_fmt, int kv_layout, int64_t cap, const void* idx, int idx_is_i64,
                         int64_t batch, int64_t hq, int64_t hkv, int64_t sq, int64_t index_heads,
                         int64_t width, int64_t dk, int64_t dv, int64_t rope, float scale,
-                        float softcap, int64_t row_begin, int64_t row_end, float* y, float* work) {
+                        float softcap, const void* bias, int bias_dtype, const int64_t* bias_dims,
+                        int64_t row_begin, int64_t row_end, float* y, float* work) {
   (void)batch;
   const int64_t group = hq / hkv;
   const int64_t record_bytes = cache_fmt == OR_FP8_BLOCK64 ? oracle_fp8_record_bytes(dk, rope) : 0;
@@ -409,6 +449,10 @@ int oracle_forward_rows(const void* q, int q_dtype, const void* kcache, const vo
         acc = acc + prod;
       }
       if (softcap != 0.0f) acc = softcap * (float)tanh((double)(acc / softcap));
+      /* [IS] `index_share_row`: the bias of (b, h, q, key) is added to the
+       * scaled score; with a softcap it comes after it, as the standard
+       * Attention page applies the softcap before its masks */
+      if (bias) acc = acc + or_bias_at(bias, bias_dtype, bias_dims, b, h, qi, key);
       p[s] = acc;
     }
     /* A7: max, exp, ascending sum, multiply by the reciprocal */
