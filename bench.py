@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--workload", default="decode_bf16",
                    choices=["decode_bf16", "decode_fp8", "prefill_bf16", "dense_gqa", "csa_decode",
-                            "csa_index_decode"])
+                            "csa_index_decode", "capacity_decode"])
     p.add_argument("--rotate", type=int, default=8, help="independent (query, index) sets")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
@@ -232,6 +232,133 @@ class Setup:
 
     def cpu_baseline(self, target_s):
         return cpu_baseline(self, target_s)
+
+
+class CapacitySetup(Setup):
+    """Capacity-mode decode with the optional attention bias (IndexShare's
+    fixed-capacity present): bf16 K and V caches of `capacity` rows drawn on
+    the device, per-batch live lengths carried only by the bias's -inf
+    frontier, and a step of capacity_lengths (valid length and write position
+    from the bias) -> in-place kv_append at the write position ->
+    forward_bias with fused validation against the recovered lengths."""
+
+    def __init__(self, name, rotate):
+        import numpy as np
+        import torch
+
+        import sa_workloads as W
+        import sparse_attention_kv_append_amd as sa
+        self.np, self.torch, self.W, self.sa = np, torch, W, sa
+        self.w = w = W.CAPACITY_WORKLOADS[name]
+        self.name = name
+        self.R = rotate
+        dev = "cuda"
+        B, Hq, Hkv, Sq, Dk, Dv, cap = w.batch, w.hq, w.hkv, w.q_seq, w.dk, w.dv, w.cap
+        assert w.dtype == W.DT_BF16 and w.layout == W.LAYOUT_SEPARATE
+        self.ctx = sa.Context(num_heads=Hq, kv_num_heads=Hkv, head_dim_qk=Dk, head_dim_v=Dv, dtype=w.dtype,
+                              kv_layout=sa.SA_KV_SEPARATE, scale=w.scale, softcap=w.softcap, max_batch=B,
+                              max_q_seq=Sq, max_index_width=w.width, max_cache_len=cap)
+        seed = w.seed
+        gen = lambda shape, s: W.torch_normal_bf16(shape, s, dev)
+        self.k = gen((B, Hkv, cap, Dk), seed * 1000)
+        self.v = gen((B, Hkv, cap, Dv), seed * 1000 + 1)
+        self.cur_k = gen((B, Hkv, w.cur, Dk), seed * 1000 + 998)
+        self.cur_v = gen((B, Hkv, w.cur, Dv), seed * 1000 + 999)
+        # the caches as drawn, before any step writes the current rows (oracle inputs)
+        self.k0, self.v0 = self.k.clone(), self.v.clone()
+        rng = np.random.default_rng(seed)
+        self.valid, bias32 = W.capacity_frontier(w, rng)
+        self.bias_host = W.store_elems(bias32, w.dtype)
+        self.bias = torch.from_numpy(self.bias_host.view(np.int16)).to(dev)
+        self.qs, self.idx_host, self.idxs = [], [], []
+        for r in range(self.R):
+            self.qs.append(gen((B, Hq, Sq, Dk), seed * 1000 + 500 + r))
+            ih = W.index_rows(w, np.random.default_rng(seed * 100 + r), bound=self.valid)
+            self.idx_host.append(ih)
+            self.idxs.append(torch.from_numpy(ih).to(dev))
+        self.y = torch.empty((B, Hq, Sq, Dv), dtype=torch.bfloat16, device=dev)
+        self.vl = torch.zeros((B,), dtype=torch.int32, device=dev)
+        self.wp = torch.zeros((B,), dtype=torch.int32, device=dev)
+        self.fp8 = False
+        self.selected = [int((ih >= 0).sum()) for ih in self.idx_host]
+        self.path, self.splits = 0, 1   # a biased forward runs on the generic kernel
+
+    def fused_step(self):
+        return False
+
+    def step(self, i):
+        w, c = self.w, self.ctx
+        r = i % len(self.idxs)
+        c.reset_error_async()
+        c.capacity_lengths(self.bias, w.batch, w.q_seq, w.cap, w.cur, self.vl, self.wp)
+        c.kv_append(w.batch, self.k, self.v, w.cap, self.wp, self.cur_k, self.cur_v, w.cur, self.k, self.v, w.cap)
+        c.forward_bias(self.qs[r], w.batch, w.q_seq, self.k, self.v, w.cap, self.vl, self.idxs[r], 1, w.width,
+                       self.bias, self.y, fused_validate=True)
+
+    def kernel_work(self):
+        kw = Setup.kernel_work(self)
+        kw["bytes"] += self.tokens_per_step() * 2    # the bias at each selected (row, key)
+        return kw
+
+    def step_bytes(self):
+        w = self.w
+        return Setup.step_bytes(self) + w.batch * w.q_seq * w.cap * 2   # the frontier scan
+
+    def roofline(self, kw, k_avg_s):
+        return "hbm", HBM_PEAK_GBS, "GB/s", kw["bytes"] / k_avg_s / 1e9
+
+    def config(self, use_graph, nset, tokens, ms_per_step):
+        w = self.w
+        return {"workload": f"{w.name}: capacity mode, batch {w.batch}, q_seq {w.q_seq}, {w.hq} q heads / "
+                            f"{w.hkv} kv heads, head dim {w.dk}, capacity {w.cap}, live lengths "
+                            f"{int(self.valid.min())}..{int(self.valid.max())} from a [B, 1, {w.q_seq}, {w.cap}] "
+                            f"bf16 bias, {w.cur} current row, top-{w.topk}, "
+                            f"{'graph replay' if use_graph else 'eager'}, {nset} rotating index sets",
+                "selected_tokens_per_step": tokens, "splits": self.splits,
+                "step_calls": "reset_error_async + capacity_lengths + kv_append + forward_bias",
+                "step_hbm_GBps": self.step_bytes() / (ms_per_step / 1e3) / 1e9}
+
+    def oracle_inputs(self, b, r=0):
+        """Host copies of batch entry b's inputs (storage bits): q, past_k,
+        past_v (as drawn), cur_k, cur_v, indices, bias."""
+        np = self.np
+        bits = lambda t: t.contiguous().view(self.torch.int16).cpu().numpy().view(np.uint16)
+        return dict(q=bits(self.qs[r][b:b + 1]), past_k=bits(self.k0[b:b + 1]), past_v=bits(self.v0[b:b + 1]),
+                    cur_k=bits(self.cur_k[b:b + 1]), cur_v=bits(self.cur_v[b:b + 1]),
+                    indices=self.idx_host[r][b:b + 1], bias=self.bias_host[b:b + 1])
+
+    def oracle_y(self, inp, threads):
+        """The oracle's capacity step for one batch entry: lengths from the
+        bias, in-place append at the write position, biased forward."""
+        import oracle
+        w = self.w
+        valid, wpos = oracle.capacity_lengths(inp["bias"], w.cap, w.cur, batch=1, heads=w.hq, q_seq=w.q_seq,
+                                              bias_dtype=w.dtype)
+        pk = oracle.kv_append(inp["past_k"].copy(), wpos, inp["cur_k"])
+        pv = oracle.kv_append(inp["past_v"].copy(), wpos, inp["cur_v"])
+        y = oracle.forward(inp["q"], pk, pv, inp["indices"], q_dtype=w.dtype, cache_fmt=w.dtype,
+                           kv_layout=w.layout, hkv=w.hkv, dv=w.dv, scale=w.scale, softcap=w.softcap,
+                           bias=inp["bias"], threads=threads)
+        return y, valid, wpos
+
+    def cpu_baseline(self, target_s):
+        """The oracle's whole capacity step (lengths, append, biased forward)
+        on batch entries taken in order until about target_s seconds of oracle
+        time; only the oracle calls are timed."""
+        w = self.w
+        threads = max(1, min(16, os.cpu_count() or 1))
+        n, t, done = 0, 0.0, 0
+        while t < target_s and done < 4 * w.batch:
+            b = done % w.batch
+            inp = self.oracle_inputs(b)
+            t0 = time.perf_counter()
+            self.oracle_y(inp, threads)
+            t += time.perf_counter() - t0
+            n += int((inp["indices"] >= 0).sum())
+            done += 1
+        return {"value": n / t, "unit": "selected tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"{done} batch entries (in order, cycling over {w.batch}) of the same workload, "
+                          f"all {w.hq} heads, {n} selected keys, {t:.1f} s of oracle time"}
 
 
 class CsaSetup:
@@ -530,6 +657,8 @@ class CsaIndexSetup:
 
 def make_setup(name, rotate):
     import sa_workloads as W
+    if name in W.CAPACITY_WORKLOADS:
+        return CapacitySetup(name, rotate)
     if name in W.CSA_INDEX_WORKLOADS:
         return CsaIndexSetup(name, rotate)
     return CsaSetup(name, rotate) if name in W.CSA_WORKLOADS else Setup(name, rotate)

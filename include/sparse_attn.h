@@ -196,6 +196,50 @@ sa_status sparse_attn_forward(sparse_attn_ctx* ctx, const void* q, int64_t batch
                               const void* indices, int64_t index_heads, int64_t width, void* y,
                               int32_t fused_validate);
 
+/* The forward with IndexShare's optional 7th input, the additive
+ * attention_bias (IndexShare page: `bias_at`, `index_share_row`,
+ * `validate_bias_shape`; the CPU page's `AttentionBias`). Arguments as
+ * sparse_attn_forward, plus
+ *   bias        NULL (then exactly sparse_attn_forward), or a dense row-major
+ *               tensor of the config dtype whose shape bias_shape[bias_rank]
+ *               (host array, 0 <= rank <= 4) is right-aligned against
+ *               [B, Hq, Sq, cache_capacity]; each extent is 1 (broadcast) or
+ *               the target's.
+ * For output row (b, h, q) and selected key k (its cache position, clamped as
+ * in sparse_attn_forward) the score becomes softcap(scale * q.k) +
+ * bias[b, h, q, k]; a row whose scores are all -inf gives zeros. A biased
+ * call runs on the generic vector kernel (sparse_attn_query_plan path 0)
+ * whatever the configuration. Host errors: those of sparse_attn_forward, and
+ * SA_E_SHAPE for a rank above 4 or an extent that does not broadcast.
+ * Asynchronous and capturable. */
+sa_status sparse_attn_forward_bias(sparse_attn_ctx* ctx, const void* q, int64_t batch, int64_t q_seq,
+                                   const void* present_k, const void* present_v,
+                                   int64_t cache_capacity, const int32_t* valid_len,
+                                   const void* indices, int64_t index_heads, int64_t width,
+                                   const void* bias, const int64_t* bias_shape, int32_t bias_rank,
+                                   void* y, int32_t fused_validate);
+
+/* Capacity-mode length recovery (IndexShare page, kernel `capacity_write_pos`
+ * and the capacity branch of its launch sequence). When the present cache
+ * aliases a fixed-capacity past, its shape no longer carries the live length;
+ * the attention_bias's causal/padding frontier does. For each batch entry b:
+ *   valid_len[b] = 1 + the largest k < cache_capacity with bias[b, h, q, k]
+ *                  finite for some (h, q); 0 when there is none
+ *   write_pos[b] = valid_len[b] - cur_len, or 0 when valid_len[b] < cur_len
+ * write_pos is the past_len of the in-place sparse_attn_kv_append that places
+ * this step's cur_len rows, valid_len the bound of sparse_attn_validate_indices
+ * and sparse_attn_forward_bias.
+ *   bias, bias_shape, bias_rank  as sparse_attn_forward_bias, against
+ *               [B, Hq, Sq, cache_capacity]; required
+ *   valid_len, write_pos         device int32 [B] outputs
+ * Host errors: SA_E_ARG (NULL bias or outputs, q_seq or cache_capacity < 1,
+ * cache_capacity >= 2^31, cur_len < 0), SA_E_STATE (batch outside
+ * [1, max_batch]), SA_E_SHAPE (bias shape). Asynchronous and capturable. */
+sa_status sparse_attn_capacity_lengths(sparse_attn_ctx* ctx, const void* bias, const int64_t* bias_shape,
+                                       int32_t bias_rank, int64_t batch, int64_t q_seq,
+                                       int64_t cache_capacity, int64_t cur_len, int32_t* valid_len,
+                                       int32_t* write_pos);
+
 /* One attention step over a shared-latent cache kept in place (capacity
  * mode): the same as
  *   [sparse_attn_reset_error_async if reset_error]

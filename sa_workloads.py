@@ -31,6 +31,21 @@ Workloads (sizes are the ones the pages' operators are exercised at; the
                    [0, 8064 + q] (causal with per-batch offset 8064), width
                    8192; softcap 50; bf16.
 
+Capacity mode with an attention bias (``CAPACITY_WORKLOADS``, drawn by
+``make_capacity_numpy``): separate K and V caches of ``capacity`` rows per
+(batch, kv head) drawn in full (rows past the live length hold stale values
+that must not be read), then the current rows; per batch entry a live length
+valid_b uniform over [valid_lo, capacity]; then the bias [B, 1, Sq,
+capacity], N(0, 1) * 0.5 up to the query's position and -inf after it (the
+causal/padding frontier that carries valid_b); then index rows as
+``causal_prefill`` against valid_b (query s sits at position valid_b - Sq + s).
+
+* ``capacity_small``  batch 3, 8 q heads / 2 kv heads, head dim 64, 2 queries
+                      and 2 current rows, capacity 300, top-40 of width 48; f32.
+* ``capacity_decode`` batch 32, 32 q heads / 8 kv heads, head dim 128, 1 query
+                      and 1 current row, capacity 16384, live lengths
+                      8192..16384, top-2048; bf16.
+
 CSA ratio-4 sink attention (``CSA_WORKLOADS``, drawn by ``make_csa_numpy``):
 query [B, S, H, 512] and current_kv [B, Tcur, 512] fp32 N(0, 1); the record
 source rows [B, total/4, 512] N(0, 1) rounded to bf16 (a block quantizer turns
@@ -211,6 +226,58 @@ def make_numpy(w: Workload) -> dict:
     out["valid_len"] = np.full(B, w.total, np.int32)
     out["indices"] = index_rows(w, rng)
     return out
+
+
+CAPACITY_WORKLOADS = {
+    "capacity_small": Workload("capacity_small", batch=3, hq=8, hkv=2, q_seq=2, dk=64, dv=64, past=0, cur=2,
+                               width=48, topk=40, dtype=DT_F32, layout=LAYOUT_SEPARATE,
+                               cache_format=CACHE_DENSE, scale=1.0 / 8.0, pattern="causal_prefill",
+                               seed=5, capacity=300, extra={"valid_lo": 2}),
+    "capacity_decode": Workload("capacity_decode", batch=32, hq=32, hkv=8, q_seq=1, dk=128, dv=128, past=0,
+                                cur=1, width=2048, topk=2048, dtype=DT_BF16, layout=LAYOUT_SEPARATE,
+                                cache_format=CACHE_DENSE, scale=float(1.0 / np.sqrt(np.float32(128.0))),
+                                pattern="causal_prefill", seed=6, capacity=16384,
+                                extra={"valid_lo": 8192}),
+}
+
+
+def make_capacity_numpy(w: Workload) -> dict:
+    """Inputs of a capacity-mode workload: q, past_k, past_v (all capacity
+    rows), cur_k, cur_v, valid (int64 [B], the live length after this step),
+    indices, bias (config dtype storage, [B, 1, Sq, capacity])."""
+    rng = np.random.default_rng(w.seed)
+    B, Hq, Hkv, Sq, Dk, Dv, cap = w.batch, w.hq, w.hkv, w.q_seq, w.dk, w.dv, w.cap
+    out = {"workload": w}
+    out["q"] = _store(rng.standard_normal((B, Hq, Sq, Dk), dtype=np.float32), w.dtype)
+    out["past_k"] = _store(rng.standard_normal((B, Hkv, cap, Dk), dtype=np.float32), w.dtype)
+    out["past_v"] = _store(rng.standard_normal((B, Hkv, cap, Dv), dtype=np.float32), w.dtype)
+    out["cur_k"] = _store(rng.standard_normal((B, Hkv, w.cur, Dk), dtype=np.float32), w.dtype)
+    out["cur_v"] = _store(rng.standard_normal((B, Hkv, w.cur, Dv), dtype=np.float32), w.dtype)
+    valid, bias = capacity_frontier(w, rng)
+    out["valid"] = valid
+    out["bias_f32"] = bias
+    out["bias"] = _store(bias, w.dtype)
+    out["indices"] = index_rows(w, rng, bound=valid)
+    return out
+
+
+def capacity_frontier(w: Workload, rng: np.random.Generator):
+    """Live lengths valid [B] (int64, uniform over [valid_lo, capacity]) and
+    the fp32 bias [B, 1, Sq, capacity]: N(0, 1) * 0.5 up to query s's
+    position valid_b - Sq + s, -inf after it."""
+    B, Sq, cap = w.batch, w.q_seq, w.cap
+    lo = max(int(w.extra["valid_lo"]), w.cur, Sq)
+    valid = rng.integers(lo, cap + 1, B).astype(np.int64)
+    bias = (rng.standard_normal((B, 1, Sq, cap), dtype=np.float32) * np.float32(0.5)).astype(np.float32)
+    for b in range(B):
+        for s in range(Sq):
+            bias[b, 0, s, valid[b] - Sq + s + 1:] = -np.inf
+    return valid, bias
+
+
+def store_elems(x: np.ndarray, dtype: int) -> np.ndarray:
+    """fp32 values -> storage of dtype (bf16/f16 as uint16 bits, RNE)."""
+    return _store(x, dtype)
 
 
 def _widen(bits: np.ndarray, dtype: int) -> np.ndarray:

@@ -60,7 +60,8 @@ generic_forward_kernel(const void* __restrict__ q, const void* __restrict__ kc,
                        const int32_t* __restrict__ valid_len, void* __restrict__ y,
                        int64_t hq, int64_t hkv, int64_t q_seq, int dk, int dv, int rope,
                        int64_t cap, int64_t index_heads, int64_t width, int64_t head_chunks,
-                       float scale, float softcap) {
+                       float scale, float softcap, const void* __restrict__ bias, int64_t bd0,
+                       int64_t bd1, int64_t bd2, int64_t bd3) {
   extern __shared__ float smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,10 +181,15 @@ generic_forward_kernel(const void* __restrict__ q, const void* __restrict__ kc,
             if (h < nh) acc[h] = fmaf(q_s[h * dk + d], kd, acc[h]);
         }
       }
+      // the optional bias of (b, head, query, key): an extent of 1 broadcasts
+      // (IndexShare `bias_at`); added after the softcap
+      int64_t boff = 0;
+      if (bias) boff = (((bd0 == 1 ? 0 : b) * bd1) * bd2 + (bd2 == 1 ? 0 : qi)) * bd3 + (bd3 == 1 ? 0 : key);
 #pragma unroll
       for (int h = 0; h < kGenMaxHeads; h++) {
         float s = acc[h] * scale;
         if (softcap != 0.0f) s = softcap * tanhf(s / softcap);
+        if (bias && h < nh) s += load_elem<DT>(bias, boff + (bd1 == 1 ? 0 : (h0 + h) * bd2 * bd3));
         sc[h] = s * kLog2e;
       }
     } else {
@@ -309,7 +315,8 @@ sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a) {
 #define SA_GEN(DT, F8, I)                                                                        \
   hipLaunchKernelGGL((generic_forward_kernel<DT, F8, I>), grid, block, smem, c->stream, a.q, a.k, \
                      a.v, a.idx, a.valid_len, a.y, a.hq, a.hkv, a.q_seq, (int)a.dk, (int)a.dv,    \
-                     (int)a.rope, a.cap, a.index_heads, a.width, head_chunks, a.scale, a.softcap)
+                     (int)a.rope, a.cap, a.index_heads, a.width, head_chunks, a.scale, a.softcap,  \
+                     a.bias, a.bd[0], a.bd[1], a.bd[2], a.bd[3])
 #define SA_GEN_I(DT, F8) \
   if (a.idx64) { SA_GEN(DT, F8, true); } else { SA_GEN(DT, F8, false); }
   if (fp8) {

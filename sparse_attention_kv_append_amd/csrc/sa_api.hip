@@ -304,7 +304,8 @@ sa_status sparse_attn_query_plan(const sparse_attn_ctx* c, int64_t batch, int64_
 static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq,
                               const void* present_k, const void* present_v, int64_t cache_capacity,
                               const int32_t* valid_len, const void* indices, int64_t index_heads,
-                              int64_t width, void* y, int32_t fused_validate, const sa::AppendArgs* app) {
+                              int64_t width, void* y, int32_t fused_validate, const sa::AppendArgs* app,
+                              const void* bias = nullptr, const int64_t* bd = nullptr) {
   const sa_config& k = c->cfg;
   if (!q || !present_k || !indices || !y) return set_error(c, SA_E_ARG, "forward: q, present_k, indices and y are required");
   const bool latent = k.kv_layout == SA_KV_SHARED_LATENT;
@@ -317,7 +318,8 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
   if (s != SA_OK) return s;
   // the shared-latent MFMA kernels validate their own columns; other paths
   // run the validation kernel first on the same stream
-  const int path = sa::forward_path(k, index_heads);
+  // a biased forward runs on the generic kernel
+  const int path = bias ? 0 : sa::forward_path(k, index_heads);
   if (fused_validate && path != 2 && path != 3) {
     s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
                                      cache_capacity, nullptr, nullptr, nullptr);
@@ -346,6 +348,10 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
   a.cache_format = k.cache_format;
   a.kv_layout = k.kv_layout;
   a.idx64 = k.index_dtype == SA_IDX_I64;
+  if (bias) {
+    a.bias = bias;
+    for (int i = 0; i < 4; i++) a.bd[i] = bd[i];
+  }
   if (app && path != 2 && path != 3)
     return set_error(c, SA_E_UNSUPPORTED, "step: the in-launch append needs a shared-latent MFMA path");
   switch (path) {
@@ -366,6 +372,65 @@ sa_status sparse_attn_forward(sparse_attn_ctx* c, const void* q, int64_t batch, 
   c->last_error.clear();
   return forward_impl(c, q, batch, q_seq, present_k, present_v, cache_capacity, valid_len, indices,
                       index_heads, width, y, fused_validate, nullptr);
+}
+
+// A bias shape of rank <= 4, right-aligned against `target` and padded with
+// 1 on the left into bd; every extent must be 1 or the target's (IndexShare
+// `validate_bias_shape`).
+static sa_status bias_dims(sparse_attn_ctx* c, const char* who, const int64_t* shape, int32_t rank,
+                           const int64_t target[4], int64_t bd[4]) {
+  if (rank < 0 || rank > 4)
+    return set_error(c, SA_E_SHAPE, std::string(who) + fmt(": attention_bias rank %lld exceeds 4", rank));
+  if (rank > 0 && !shape) return set_error(c, SA_E_ARG, std::string(who) + ": attention_bias shape is NULL");
+  for (int a = 0; a < 4; a++) bd[a] = 1;
+  for (int i = 0; i < rank; i++) bd[4 - rank + i] = shape[i];
+  for (int a = 0; a < 4; a++)
+    if (bd[a] != 1 && bd[a] != target[a])
+      return set_error(c, SA_E_SHAPE,
+                       std::string(who) + fmt(": attention_bias dimension %lld is not broadcastable to ", bd[a]) +
+                           fmt("[%lld, %lld, %lld, %lld]", target[0], target[1], target[2], target[3]));
+  return SA_OK;
+}
+
+sa_status sparse_attn_forward_bias(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq,
+                                   const void* present_k, const void* present_v, int64_t cache_capacity,
+                                   const int32_t* valid_len, const void* indices, int64_t index_heads,
+                                   int64_t width, const void* bias, const int64_t* bias_shape,
+                                   int32_t bias_rank, void* y, int32_t fused_validate) {
+  if (!live(c)) return SA_E_STATE;
+  c->last_error.clear();
+  if (!bias)
+    return forward_impl(c, q, batch, q_seq, present_k, present_v, cache_capacity, valid_len, indices,
+                        index_heads, width, y, fused_validate, nullptr);
+  const int64_t target[4] = {batch, c->cfg.num_heads, q_seq, cache_capacity};
+  int64_t bd[4];
+  sa_status s = bias_dims(c, "forward", bias_shape, bias_rank, target, bd);
+  if (s != SA_OK) return s;
+  return forward_impl(c, q, batch, q_seq, present_k, present_v, cache_capacity, valid_len, indices,
+                      index_heads, width, y, fused_validate, nullptr, bias, bd);
+}
+
+sa_status sparse_attn_capacity_lengths(sparse_attn_ctx* c, const void* bias, const int64_t* bias_shape,
+                                       int32_t bias_rank, int64_t batch, int64_t q_seq,
+                                       int64_t cache_capacity, int64_t cur_len, int32_t* valid_len,
+                                       int32_t* write_pos) {
+  if (!live(c)) return SA_E_STATE;
+  const sa_config& k = c->cfg;
+  c->last_error.clear();
+  if (!bias)
+    return set_error(c, SA_E_ARG,
+                     "capacity_lengths: capacity-mode IndexShare requires attention_bias to derive the valid length");
+  if (!valid_len || !write_pos) return set_error(c, SA_E_ARG, "capacity_lengths: valid_len and write_pos are required");
+  if (batch <= 0 || batch > k.max_batch)
+    return set_error(c, SA_E_STATE, fmt("capacity_lengths: batch %lld outside [1, max_batch %lld]", batch, k.max_batch));
+  if (q_seq <= 0 || cur_len < 0 || cache_capacity <= 0 || cache_capacity > 0x7fffffffLL)
+    return set_error(c, SA_E_ARG, "capacity_lengths: q_seq and cache_capacity must be positive (capacity below "
+                                  "2^31) and cur_len non-negative");
+  const int64_t target[4] = {batch, k.num_heads, q_seq, cache_capacity};
+  int64_t bd[4];
+  sa_status s = bias_dims(c, "capacity_lengths", bias_shape, bias_rank, target, bd);
+  if (s != SA_OK) return s;
+  return sa::launch_capacity_lengths(c, bias, k.dtype, bd, batch, cache_capacity, cur_len, valid_len, write_pos);
 }
 
 sa_status sparse_attn_step(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq, void* cache,

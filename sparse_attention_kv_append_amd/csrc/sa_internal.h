@@ -136,6 +136,10 @@ struct FwdArgs {
   int64_t batch, hq, hkv, q_seq, dk, dv, rope, cap, index_heads, width;
   float scale, softcap;
   int dtype, cache_format, kv_layout, idx64;
+  // optional additive bias (config dtype), its shape right-aligned against
+  // [B, Hq, Sq, cap] and padded with 1 on the left
+  const void* bias = nullptr;
+  int64_t bd[4] = {1, 1, 1, 1};
 };
 
 // the in-launch append of the shared-latent LDS-ring kernel: current rows
@@ -162,6 +166,12 @@ bool pair_supported(const sa_config& cfg, int64_t index_heads);
 bool gqa_supported(const sa_config& cfg, int64_t index_heads);
 int mla_splits(int64_t rows, int64_t width);
 sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a);
+// capacity-mode length recovery from the bias frontier: per batch entry,
+// valid = 1 + the last key column with a finite bias, write = valid - cur_len
+// (0 below cur_len); bd is the bias shape padded to rank 4
+sa_status launch_capacity_lengths(sparse_attn_ctx* c, const void* bias, int dtype, const int64_t* bd,
+                                  int64_t batch, int64_t keys, int64_t cur_len, int32_t* valid_len,
+                                  int32_t* write_pos);
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
 sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                                 const AppendArgs* app = nullptr);

@@ -1,0 +1,256 @@
+"""GPU parity of the optional attention bias (sparse_attn_forward_bias) and
+capacity-mode length recovery (sparse_attn_capacity_lengths), through the C
+ABI, against the oracle on the same seeded inputs.
+
+Bar: lengths and write positions bit-exact (integer); the in-place present
+byte-identical to the oracle's append at the recovered write positions; Y
+within the floating tolerance of its dtype (f32 1e-5; bf16/f16 2e-2 + 1e-2
+relative); the error word zero on valid inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sa_workloads as W
+from gpu_support import check_close, make_ctx, oracle_records, raw_bytes, to_np, tt, y_as_f32, y_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(msg):
+    print(f"\n[gpu] {msg}", flush=True)
+
+
+def present_host(inp):
+    pk = oracle.kv_append(inp["past_k"].copy(), inp["past_len"], inp["cur_k"])
+    pv = None if inp["past_v"] is None else oracle.kv_append(inp["past_v"].copy(), inp["past_len"], inp["cur_v"])
+    return pk, pv
+
+
+def bias_store(b32, dtype):
+    if dtype == W.DT_F32:
+        return np.ascontiguousarray(b32, np.float32)
+    if dtype == W.DT_F16:
+        return np.ascontiguousarray(b32, np.float32).astype(np.float16).view(np.uint16)
+    return oracle.bf16_bits(np.ascontiguousarray(b32, np.float32))
+
+
+def run_bias(w, inp, bias, *, fp8=False):
+    """Device forward_bias over the oracle's present; returns (y, word, msg)."""
+    import torch
+    pk, pv = present_host(inp)
+    kc = oracle_records(pk, w) if fp8 else pk
+    ctx = make_ctx(w)
+    y = torch.full((w.batch, w.hq, w.q_seq, w.dv), float("nan"), dtype=y_dtype(w), device="cuda")
+    vl = torch.tensor(np.full(w.batch, w.total, np.int32), device="cuda")
+    ctx.reset_error_async()
+    ctx.forward_bias(tt(inp["q"]), w.batch, w.q_seq, tt(kc), None if pv is None else tt(pv), w.cap, vl,
+                     tt(inp["indices"]), inp["indices"].shape[1], w.width, None if bias is None else tt(bias),
+                     y, fused_validate=True)
+    word, _, msg = ctx.read_error()
+    ctx.destroy()
+    return y_as_f32(y), word, msg
+
+
+def oracle_bias(w, inp, bias, *, fp8=False):
+    pk, pv = present_host(inp)
+    kc, fmt = (oracle_records(pk, w), oracle.FP8_BLOCK64) if fp8 else (pk, w.dtype)
+    return oracle.forward(inp["q"], kc, pv, inp["indices"], q_dtype=w.dtype, cache_fmt=fmt,
+                          kv_layout=w.layout, hkv=w.hkv, dv=w.dv, rope=w.rope, scale=w.scale,
+                          softcap=w.softcap, bias=bias, threads=8)
+
+
+CASES = {
+    "tiny_f32": W.WORKLOADS["tiny_f32"].scaled(batch=2),
+    "grouped_bf16_per_head": W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=3, past=200, cur=3,
+                                                             width=120, topk=100, pattern="uniform",
+                                                             index_heads=8, softcap=0.0),
+    "gqa_softcap_f16": W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=5, past=300, cur=5,
+                                                       width=305, topk=305, dtype=W.DT_F16),
+    "fp8_records": W.WORKLOADS["decode_fp8"].scaled(batch=2, hq=16, past=300, topk=100, width=128),
+    "latent_bf16": W.WORKLOADS["decode_bf16"].scaled(batch=3, hq=16, past=400, topk=260, width=300),
+}
+SHAPES = ["full", "b11k", "sk", "h11", "scalar"]
+
+
+def make_bias(w, shape, seed=3, holes=True):
+    dims = {"full": (w.batch, w.hq, w.q_seq, w.cap), "b11k": (w.batch, 1, 1, w.cap), "sk": (w.q_seq, w.cap),
+            "h11": (w.hq, 1, 1), "scalar": ()}[shape]
+    rng = np.random.default_rng(seed)
+    b = rng.standard_normal(dims).astype(np.float32)
+    if holes and b.ndim and b.shape[-1] == w.cap:
+        b[rng.random(dims) < 0.15] = -np.inf
+    return bias_store(b, w.dtype)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("shape", SHAPES)
+def test_forward_bias_matches_oracle(name, shape):
+    w = CASES[name]
+    fp8 = w.cache_format == W.CACHE_FP8
+    inp = W.make_numpy(w)
+    bias = make_bias(w, shape)
+    banner(f"forward_bias {name} bias {shape} {bias.shape}")
+    ref = oracle_bias(w, inp, bias, fp8=fp8)
+    y, word, msg = run_bias(w, inp, bias, fp8=fp8)
+    assert word == 0, msg
+    check_close(y, ref, w.dtype, f"{name}/{shape}")
+
+
+def test_forward_bias_none_is_the_plain_forward():
+    w = CASES["tiny_f32"]
+    inp = W.make_numpy(w)
+    ref = oracle_bias(w, inp, None)
+    y, word, msg = run_bias(w, inp, None)
+    assert word == 0, msg
+    check_close(y, ref, w.dtype, "no bias")
+
+
+def test_forward_bias_masked_rows_give_zeros():
+    w = CASES["grouped_bf16_per_head"]
+    inp = W.make_numpy(w)
+    b32 = np.zeros((w.batch, w.hq, w.q_seq, 1), np.float32)
+    b32[1, 3, 2] = -np.inf
+    b32[0, :, 0] = -np.inf
+    bias = bias_store(b32, w.dtype)
+    ref = oracle_bias(w, inp, bias)
+    assert not ref[1, 3, 2].any() and not ref[0, :, 0].any()
+    y, word, msg = run_bias(w, inp, bias)
+    assert word == 0, msg
+    assert not y[1, 3, 2].any() and not y[0, :, 0].any()
+    check_close(y, ref, w.dtype, "masked rows")
+
+
+def test_bias_host_errors():
+    import torch
+
+    import sparse_attention_kv_append_amd as sa
+    w = CASES["tiny_f32"]
+    ctx = make_ctx(w)
+    dev = "cuda"
+    q = torch.zeros((w.batch, w.hq, w.q_seq, w.dk), device=dev)
+    k = torch.zeros((w.batch, w.hkv, w.cap, w.dk), device=dev)
+    idx = torch.zeros((w.batch, 1, w.q_seq, w.width), dtype=torch.int32, device=dev)
+    y = torch.zeros_like(q)
+    vl = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    for bad in [(1, 1, 1, 1, 1), (3, 1, 1, 1), (w.cap + 1,), (1, 2, 1, 1)]:
+        with pytest.raises(sa.SparseAttnError) as e:
+            ctx.forward_bias(q, w.batch, w.q_seq, k, k, w.cap, vl, idx, 1, w.width,
+                             torch.zeros(bad, device=dev), y)
+        assert e.value.status == sa.SA_E_SHAPE, bad
+    with pytest.raises(sa.SparseAttnError) as e:
+        ctx.capacity_lengths(torch.zeros((w.cap + 2,), device=dev), w.batch, w.q_seq, w.cap, 1, vl, vl)
+    assert e.value.status == sa.SA_E_SHAPE
+    assert ctx.lib.sparse_attn_capacity_lengths(ctx.handle, None, None, 0, w.batch, w.q_seq, w.cap, 1,
+                                                vl.data_ptr(), vl.data_ptr()) == sa.SA_E_ARG
+    ctx.destroy()
+
+
+@pytest.mark.parametrize("dtype,shape", [(W.DT_F32, (3, 8, 2, 300)), (W.DT_F32, (3, 1, 1, 300)),
+                                         (W.DT_BF16, (300,)), (W.DT_BF16, (3, 1, 2, 300)),
+                                         (W.DT_F16, (1, 8, 1, 300)), (W.DT_F32, (3, 8, 2, 1))])
+def test_capacity_lengths_match_oracle(dtype, shape):
+    import torch
+    w = W.CAPACITY_WORKLOADS["capacity_small"].scaled(dtype=dtype)
+    rng = np.random.default_rng(12)
+    b32 = rng.standard_normal(shape).astype(np.float32)
+    lead = b32.reshape(-1, shape[-1])
+    for i in range(lead.shape[0]):
+        f = int(rng.integers(0, shape[-1] + 1))
+        lead[i, f:] = -np.inf
+        lead[i, rng.integers(0, shape[-1], 3)] = np.nan
+    if len(shape) == 4 and shape[0] == 3:
+        b32[1] = -np.inf      # no live row in batch entry 1
+    bias = bias_store(b32, dtype)
+    banner(f"capacity_lengths dtype {dtype} shape {shape}")
+    for cur in (1, 2, 250):
+        valid, wpos = oracle.capacity_lengths(bias, w.cap, cur, batch=w.batch, heads=w.hq, q_seq=w.q_seq,
+                                              bias_dtype=dtype)
+        ctx = make_ctx(w)
+        vl = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
+        wp = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
+        ctx.capacity_lengths(tt(bias), w.batch, w.q_seq, w.cap, cur, vl, wp)
+        np.testing.assert_array_equal(to_np(vl), valid)
+        np.testing.assert_array_equal(to_np(wp), wpos)
+        ctx.destroy()
+
+
+def capacity_oracle(w, inp):
+    valid, wpos = oracle.capacity_lengths(inp["bias"], w.cap, w.cur, batch=w.batch, heads=w.hq, q_seq=w.q_seq,
+                                          bias_dtype=w.dtype)
+    assert np.array_equal(valid, inp["valid"])
+    word, _, _, _ = oracle.validate_indices(inp["indices"], valid)
+    assert word == 0
+    pk = oracle.kv_append(inp["past_k"].copy(), wpos, inp["cur_k"])
+    pv = oracle.kv_append(inp["past_v"].copy(), wpos, inp["cur_v"])
+    return valid, wpos, pk, pv
+
+
+def capacity_device(w, inp, ctx=None):
+    """capacity_lengths -> in-place kv_append at write_pos -> forward_bias with
+    fused validation against valid_len, all on the context's stream."""
+    import torch
+    own = ctx is None
+    if own:
+        ctx = make_ctx(w)
+    kc, vc = tt(inp["past_k"]), tt(inp["past_v"])
+    bias = tt(inp["bias"])
+    vl = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
+    wp = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
+    y = torch.full((w.batch, w.hq, w.q_seq, w.dv), float("nan"), dtype=y_dtype(w), device="cuda")
+    ctx.reset_error_async()
+    ctx.capacity_lengths(bias, w.batch, w.q_seq, w.cap, w.cur, vl, wp)
+    ctx.kv_append(w.batch, kc, vc, w.cap, wp, tt(inp["cur_k"]), tt(inp["cur_v"]), w.cur, kc, vc, w.cap)
+    ctx.forward_bias(tt(inp["q"]), w.batch, w.q_seq, kc, vc, w.cap, vl, tt(inp["indices"]), 1, w.width, bias, y,
+                     fused_validate=True)
+    word, _, msg = ctx.read_error()
+    out = dict(valid=to_np(vl), wpos=to_np(wp), k=to_np(kc), v=to_np(vc), y=y_as_f32(y), word=word, msg=msg)
+    if own:
+        ctx.destroy()
+    return out
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(dtype=W.DT_BF16, seed=8), dict(q_seq=1, cur=1, seed=9),
+                                dict(batch=2, hq=4, hkv=4, q_seq=4, cur=4, width=300, topk=300, seed=10)])
+def test_capacity_step_matches_oracle(kw):
+    w = W.CAPACITY_WORKLOADS["capacity_small"].scaled(**kw)
+    inp = W.make_capacity_numpy(w)
+    banner(f"capacity step {w.name} {kw}")
+    valid, wpos, pk, pv = capacity_oracle(w, inp)
+    ref = oracle.forward(inp["q"], pk, pv, inp["indices"], q_dtype=w.dtype, cache_fmt=w.dtype,
+                         kv_layout=w.layout, hkv=w.hkv, dv=w.dv, scale=w.scale, bias=inp["bias"], threads=8)
+    d = capacity_device(w, inp)
+    assert d["word"] == 0, d["msg"]
+    np.testing.assert_array_equal(d["valid"], valid)
+    np.testing.assert_array_equal(d["wpos"], wpos)
+    assert np.array_equal(raw_bytes(d["k"]), raw_bytes(pk)) and np.array_equal(raw_bytes(d["v"]), raw_bytes(pv))
+    check_close(d["y"], ref, w.dtype, "capacity step")
+
+
+def test_capacity_decode_fullsize_sampled_rows():
+    """The benchmark's capacity-mode decode (batch 32, 32 q heads / 8 kv heads,
+    head dim 128, capacity 16384, top-2048, bf16) in its launch
+    configuration: lengths and write positions exact, the appended rows
+    exact, Y of sampled batch entries (all heads) against the oracle's
+    capacity step on those entries."""
+    import torch
+
+    import bench
+    banner("capacity decode full size: building inputs")
+    s = bench.CapacitySetup("capacity_decode", 1)
+    s.step(0)
+    torch.cuda.synchronize()
+    word, _, msg = s.ctx.read_error()
+    assert word == 0, msg
+    w = s.w
+    vl, wp = to_np(s.vl), to_np(s.wp)
+    y = y_as_f32(s.y)
+    for b in [0, 7, 19, 31]:
+        banner(f"capacity decode full size: oracle on batch entry {b}")
+        inp = s.oracle_inputs(b)
+        ref, valid, wpos = s.oracle_y(inp, 8)
+        assert vl[b] == valid[0] and wp[b] == wpos[0]
+        kb = s.k[b:b + 1, :, wpos[0]:wpos[0] + w.cur].contiguous().view(torch.int16).cpu().numpy()
+        np.testing.assert_array_equal(kb.view(np.uint16), inp["cur_k"])
+        check_close(y[b:b + 1], ref, w.dtype, f"batch entry {b}")
+    s.ctx.destroy()
