@@ -281,7 +281,9 @@ class CapacitySetup(Setup):
         self.wp = torch.zeros((B,), dtype=torch.int32, device=dev)
         self.fp8 = False
         self.selected = [int((ih >= 0).sum()) for ih in self.idx_host]
-        self.path, self.splits = 0, 1   # a biased forward runs on the generic kernel
+        # a biased forward runs on the grouped-query kernel where the plan takes it, else generic
+        plan, _ = self.ctx.query_plan(B, Sq, 1, w.width)
+        self.path, self.splits = (4 if plan == 4 else 0), 1
 
     def fused_step(self):
         return False

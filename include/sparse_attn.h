@@ -208,8 +208,8 @@ sa_status sparse_attn_forward(sparse_attn_ctx* ctx, const void* q, int64_t batch
  * For output row (b, h, q) and selected key k (its cache position, clamped as
  * in sparse_attn_forward) the score becomes softcap(scale * q.k) +
  * bias[b, h, q, k]; a row whose scores are all -inf gives zeros. A biased
- * call runs on the generic vector kernel (sparse_attn_query_plan path 0)
- * whatever the configuration. Host errors: those of sparse_attn_forward, and
+ * call runs on the grouped-query kernel (sparse_attn_query_plan path 4) when
+ * the configuration takes it, else on the generic vector kernel (path 0). Host errors: those of sparse_attn_forward, and
  * SA_E_SHAPE for a rank above 4 or an extent that does not broadcast.
  * Asynchronous and capturable. */
 sa_status sparse_attn_forward_bias(sparse_attn_ctx* ctx, const void* q, int64_t batch, int64_t q_seq,

@@ -67,12 +67,14 @@ template <bool I64> constexpr size_t lds_bytes() { return (size_t)flag_off<I64>(
 // j >> 1, key half j & 1) and the two transposing V reads of dv tile j
 __host__ __device__ constexpr int gqa_step_reads(int j) { return j < 8 ? 3 : 0; }
 
-template <bool I64, bool SOFTCAP>
+template <bool I64, bool SOFTCAP, bool BIAS>
 __global__ void __launch_bounds__(gq::THREADS, 1)
 gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                    const void* __restrict__ idx, const int32_t* __restrict__ valid_len, uint16_t* __restrict__ y,
                    int64_t batch, int64_t hkv, int64_t q_seq, int64_t cap, int64_t width, int group, int nqb,
-                   float scale, float softcap) {
+                   float scale, float softcap, const uint16_t* __restrict__ bias, int64_t bd0, int64_t bd1,
+                   int64_t bd2, int64_t bd3) {
+  static_assert(gq::RB == 1, "the bias prefetch holds one row block per wave");
   using namespace gq;
   constexpr int ITB = idx_tile_bytes<I64>();
   constexpr int IL = ILOADS<I64>;
@@ -116,6 +118,18 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     row_q[rb] = r;
     row_h[rb] = (int)(kvh * group) + (m - r * group);
     row_on[rb] = m < R * group && r < rlive;
+  }
+
+  // ---- the optional bias (IndexShare `bias_at`): each row's element at key
+  // 0 (an extent of 1 broadcasts); rows that do not exist read element 0
+  const uint16_t* brow[RB];
+  const bool bkey = bd3 != 1;
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    int64_t off = 0;
+    if (BIAS && row_on[rb])
+      off = (((bd0 == 1 ? 0 : b) * bd1 + (bd1 == 1 ? 0 : row_h[rb])) * bd2 + (bd2 == 1 ? 0 : q0 + row_q[rb])) * bd3;
+    brow[rb] = bias + off;
   }
 
   // ---- buffers: this (batch, kv head)'s K and V rows; the index rows of the
@@ -348,6 +362,28 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
       __builtin_amdgcn_sched_barrier(0);
     });
   };
+  // bias of this lane's eight (row, column) scores of a tile: columns 4 g + i
+  // and 16 + 4 g + i, whose keys lanes 0..31 hold (one column each); issued
+  // as untracked loads into braw, waited for by bias_ready
+  uint32_t braw[8];
+  float bvf[8];
+  auto bias_issue = [&](int64_t colkey) {
+    if constexpr (BIAS) {
+      const int kc32 = (bkey && colkey >= 0 && colkey < bound) ? (int)colkey : 0;  // clamp as the gather does
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int kcol = __shfl(kc32, i < 4 ? 4 * g + i : 16 + 4 * g + i - 4, 64);
+        braw[i] = global_load_u16_asm(brow[0] + (row_on[0] ? kcol : 0));
+      }
+    }
+  };
+  auto bias_ready = [&](auto nc) {
+    if constexpr (BIAS) {
+      vm_wait_tied8<decltype(nc)::value>(braw);
+#pragma unroll
+      for (int i = 0; i < 8; i++) bvf[i] = __uint_as_float(braw[i] << 16) * kLog2eL;
+    }
+  };
   // online softmax of the scores in sa for tile x; `only` < 0: every row,
   // else only the rows of query `only`; `none`: every row masked (the
   // tile is redone row by row). Rescales O and returns P^T in pb.
@@ -365,6 +401,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
       for (int i = 0; i < 8; i++) {
         if constexpr (SOFTCAP) xs[i] = cap_a - cap_b * __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(xs[i] * cap_k) + 1.0f);
         else xs[i] *= f;
+        if constexpr (BIAS) xs[i] += bvf[i];  // after the softcap, in log2 units
       }
       const bool live = row_on[rb] && !none && (only < 0 || only == row_q[rb]);
       const int64_t n = live ? (int64_t)n_s[row_q[rb]] : 0;
@@ -407,10 +444,12 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
       int64_t kl = -1;
       if (col < width) kl = load_index<I64>(ibase, (int64_t)r * width + col);
       key_offsets(kl);
+      bias_issue(kl);
       wait_vm<0>();
       __syncthreads();  // every wave is done with the spare slot
       gather_issue(lds + SPARE_OFF);
       wait_vm<0>();
+      bias_ready(std::integral_constant<int, 0>{});
       __syncthreads();
       kslot = spare;
       vslot = spare;
@@ -433,10 +472,12 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   fold(1);
   __syncthreads();
   int64_t kk = finalize(0);
+  const int64_t key0 = kk;
   key_offsets(kk);
   gather_issue(lds + 0 * KV_TILE);
   issue_idx(4);
   kk = finalize(1);
+  int64_t key_n1 = kk;  // keys of the tile after the one being scored, then the one after that
   key_offsets(kk);
   lds_barrier();  // partial slots of tiles 0, 1 are read
   fold(2);
@@ -444,6 +485,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   gather_issue(lds + 1 * KV_TILE);
   lds_barrier();
   kk = finalize(2);
+  int64_t key_n2 = kk;
   key_offsets(kk);
   gather_issue(lds + 2 * KV_TILE);
   issue_idx(5);
@@ -455,6 +497,8 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     kslot = slot_of(0);
     if (tile_flags(0) & 1) {
       s_alone();
+      bias_issue(key0);
+      bias_ready(std::integral_constant<int, 0>{});
       softmax(0, -1, false);
     } else {
       zero_s();
@@ -472,6 +516,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     kk = finalize(t + 3);    // partials folded in the last iteration
     key_offsets(kk);
     const bool shared_next = (tile_flags(t + 1) & 1) != 0;
+    bias_issue(key_n1);  // lands during the MFMAs below (unused when the tile is not shared)
     kslot = slot_of(t + 1);
     vslot = slot_of(t);
     zero_s();
@@ -496,12 +541,17 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     });
     issue_idx(t + 6);
     fold(t + 4);
+    // every load but the gathers and index loads above (the registers are
+    // defined by this wait on every path, so none is copied while in flight)
+    bias_ready(std::integral_constant<int, GLOADS + IL>{});
     if (shared_next) {
       softmax(t + 1, -1, false);
     } else {
       softmax(t + 1, -1, true);
       row_by_row(t + 1);
     }
+    key_n1 = key_n2;
+    key_n2 = kk;
   }
 
   // ---- the last tile's PV alone
@@ -535,7 +585,7 @@ bool gqa_supported(const sa_config& cfg, int64_t index_heads) {
   return cfg.max_cache_len <= (int64_t)(0x7fffffffLL / gq::ROWB);
 }
 
-static bool g_gqa_attr[4] = {false, false, false, false};
+static bool g_gqa_attr[8] = {false, false, false, false, false, false, false, false};
 
 sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
   using namespace gq;
@@ -550,9 +600,13 @@ sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
   if ((int64_t)R * a.width * (a.idx64 ? 8 : 4) > 0x7fffffffLL)
     return set_error(c, SA_E_SHAPE, "forward: index rows too wide for 32-bit offsets");
   const bool cap_on = a.softcap != 0.0f;
-  const int variant = (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0);
-  const void* fns[4] = {(const void*)gqa_forward_kernel<false, false>, (const void*)gqa_forward_kernel<true, false>,
-                        (const void*)gqa_forward_kernel<false, true>, (const void*)gqa_forward_kernel<true, true>};
+  const bool bias_on = a.bias != nullptr;
+  const int variant = (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0) + (bias_on ? 4 : 0);
+  const void* fns[8] = {
+      (const void*)gqa_forward_kernel<false, false, false>, (const void*)gqa_forward_kernel<true, false, false>,
+      (const void*)gqa_forward_kernel<false, true, false>,  (const void*)gqa_forward_kernel<true, true, false>,
+      (const void*)gqa_forward_kernel<false, false, true>,  (const void*)gqa_forward_kernel<true, false, true>,
+      (const void*)gqa_forward_kernel<false, true, true>,   (const void*)gqa_forward_kernel<true, true, true>};
   const size_t lds = a.idx64 ? lds_bytes<true>() : lds_bytes<false>();
   if (!g_gqa_attr[variant]) {
     hipError_t e = hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -561,15 +615,20 @@ sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
   }
   const dim3 grid((unsigned)wgs), block(THREADS);
   prof_begin(c);
-#define SA_GQA(I, C)                                                                                         \
-  hipLaunchKernelGGL((gqa_forward_kernel<I, C>), grid, block, lds, c->stream, (const uint16_t*)a.q,          \
+#define SA_GQA(I, C, BI)                                                                                     \
+  hipLaunchKernelGGL((gqa_forward_kernel<I, C, BI>), grid, block, lds, c->stream, (const uint16_t*)a.q,      \
                      (const uint8_t*)a.k, (const uint8_t*)a.v, a.idx, a.valid_len, (uint16_t*)a.y, a.batch, \
-                     a.hkv, a.q_seq, a.cap, a.width, group, (int)nqb, a.scale, a.softcap)
+                     a.hkv, a.q_seq, a.cap, a.width, group, (int)nqb, a.scale, a.softcap,                    \
+                     (const uint16_t*)a.bias, a.bd[0], a.bd[1], a.bd[2], a.bd[3])
   switch (variant) {
-    case 0: SA_GQA(false, false); break;
-    case 1: SA_GQA(true, false); break;
-    case 2: SA_GQA(false, true); break;
-    default: SA_GQA(true, true); break;
+    case 0: SA_GQA(false, false, false); break;
+    case 1: SA_GQA(true, false, false); break;
+    case 2: SA_GQA(false, true, false); break;
+    case 3: SA_GQA(true, true, false); break;
+    case 4: SA_GQA(false, false, true); break;
+    case 5: SA_GQA(true, false, true); break;
+    case 6: SA_GQA(false, true, true); break;
+    default: SA_GQA(true, true, true); break;
   }
 #undef SA_GQA
   prof_end(c);

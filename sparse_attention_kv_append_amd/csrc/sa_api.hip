@@ -318,8 +318,9 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
   if (s != SA_OK) return s;
   // the shared-latent MFMA kernels validate their own columns; other paths
   // run the validation kernel first on the same stream
-  // a biased forward runs on the generic kernel
-  const int path = bias ? 0 : sa::forward_path(k, index_heads);
+  // a biased forward runs on the grouped-query kernel where it applies, else
+  // on the generic kernel
+  const int path = bias ? (sa::gqa_supported(k, index_heads) ? 4 : 0) : sa::forward_path(k, index_heads);
   if (fused_validate && path != 2 && path != 3) {
     s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
                                      cache_capacity, nullptr, nullptr, nullptr);

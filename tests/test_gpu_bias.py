@@ -67,6 +67,13 @@ CASES = {
                                                              index_heads=8, softcap=0.0),
     "gqa_softcap_f16": W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=5, past=300, cur=5,
                                                        width=305, topk=305, dtype=W.DT_F16),
+    # bf16, 128 dims, one index list per query: the grouped-query MFMA kernel
+    "gqa_causal_softcap": W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=12, past=500, cur=12,
+                                                          width=512, topk=512),
+    "gqa_uniform_decode": W.WORKLOADS["dense_gqa"].scaled(batch=3, hq=16, hkv=4, q_seq=1, past=3000, cur=1,
+                                                          width=700, topk=650, pattern="uniform", softcap=0.0),
+    "gqa_uniform_rows": W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=4, hkv=2, q_seq=3, past=400, cur=3,
+                                                        width=100, topk=90, pattern="uniform", softcap=0.0),
     "fp8_records": W.WORKLOADS["decode_fp8"].scaled(batch=2, hq=16, past=300, topk=100, width=128),
     "latent_bf16": W.WORKLOADS["decode_bf16"].scaled(batch=3, hq=16, past=400, topk=260, width=300),
 }
@@ -211,7 +218,10 @@ def capacity_device(w, inp, ctx=None):
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(dtype=W.DT_BF16, seed=8), dict(q_seq=1, cur=1, seed=9),
-                                dict(batch=2, hq=4, hkv=4, q_seq=4, cur=4, width=300, topk=300, seed=10)])
+                                dict(batch=2, hq=4, hkv=4, q_seq=4, cur=4, width=300, topk=300, seed=10),
+                                # bf16 with 128 dims: the grouped-query kernel
+                                dict(dtype=W.DT_BF16, dk=128, dv=128, q_seq=1, cur=1, seed=11),
+                                dict(dtype=W.DT_BF16, dk=128, dv=128, hq=16, hkv=2, seed=12)])
 def test_capacity_step_matches_oracle(kw):
     w = W.CAPACITY_WORKLOADS["capacity_small"].scaled(**kw)
     inp = W.make_capacity_numpy(w)
