@@ -8,6 +8,8 @@
 // width and pointer alignment allow; there is no per-element index math.
 #include "sa_quant_dev.h"
 
+#include <algorithm>
+
 namespace sa {
 
 __global__ void reset_error_kernel(ErrorBlock* err) {
@@ -30,20 +32,27 @@ constexpr int kCopyBlock = 256;
 constexpr int kCopyUnroll = 4;
 
 // grid.x = (batch * heads) * chunks; each block copies kCopyBlock*kCopyUnroll
-// vector units of one (batch, head) segment.
+// vector units of one (batch, head) segment. grid.y = 2 copies a second
+// tensor of the same geometry (V beside K) in the same launch.
 template <typename V>
 __global__ void __launch_bounds__(kCopyBlock)
-append_copy_kernel(const char* __restrict__ past, int64_t past_cap,
-                   const int32_t* __restrict__ past_len, const char* __restrict__ cur,
-                   int64_t cur_len, char* __restrict__ present, int64_t present_cap,
+append_copy_kernel(const char* __restrict__ past_a, const char* __restrict__ past_b, int64_t past_cap,
+                   const int32_t* __restrict__ past_len, const char* __restrict__ cur_a,
+                   const char* __restrict__ cur_b, int64_t cur_len, char* __restrict__ present_a,
+                   char* __restrict__ present_b, int64_t present_cap,
                    int64_t heads, int64_t row_bytes, int64_t chunks, int copy_past,
                    int32_t* __restrict__ present_len, ErrorBlock* __restrict__ err) {
+  const bool second = blockIdx.y != 0;
+  const char* __restrict__ past = second ? past_b : past_a;
+  const char* __restrict__ cur = second ? cur_b : cur_a;
+  char* __restrict__ present = second ? present_b : present_a;
+  if (second) present_len = nullptr;
   const int64_t bh = blockIdx.x / chunks;
   const int64_t chunk = blockIdx.x - bh * chunks;
   const int64_t b = bh / heads;
   const int64_t P = past_len ? (int64_t)past_len[b] : past_cap;
   if (P < 0 || P > past_cap || P + cur_len > present_cap) {
-    if (chunk == 0 && threadIdx.x == 0) atomicOr(&err->word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
+    if (!second && chunk == 0 && threadIdx.x == 0) atomicOr(&err->word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
     return;
   }
   if (present_len && chunk == 0 && threadIdx.x == 0 && bh % heads == 0) {
@@ -89,8 +98,11 @@ static int pick_vec(int64_t row_bytes, const void* a, const void* b, const void*
 sa_status launch_append_copy(sparse_attn_ctx* c, int64_t batch, int64_t heads, int64_t row_bytes,
                              const void* past, int64_t past_cap, const int32_t* past_len,
                              const void* cur, int64_t cur_len, void* present, int64_t present_cap,
-                             bool copy_past, int32_t* present_len) {
-  const int vec = pick_vec(row_bytes, copy_past ? past : nullptr, cur, present);
+                             bool copy_past, int32_t* present_len, const void* past2, const void* cur2,
+                             void* present2) {
+  const bool two = present2 != nullptr;
+  int vec = pick_vec(row_bytes, copy_past ? past : nullptr, cur, present);
+  if (two) vec = std::min(vec, pick_vec(row_bytes, copy_past ? past2 : nullptr, cur2, present2));
   const int64_t max_rows = (copy_past ? past_cap : 0) + cur_len;
   const int64_t units = max_rows * (row_bytes / vec);
   const int64_t per_block = (int64_t)kCopyBlock * kCopyUnroll;
@@ -98,12 +110,12 @@ sa_status launch_append_copy(sparse_attn_ctx* c, int64_t batch, int64_t heads, i
   const int64_t blocks = batch * heads * chunks;
   if (blocks <= 0) return SA_OK;
   if (blocks > 0x7fffffffLL) return set_error(c, SA_E_SHAPE, "kv_append: cache too large for one launch");
-  const dim3 grid((unsigned)blocks), block(kCopyBlock);
-#define SA_COPY(T)                                                                          \
-  hipLaunchKernelGGL(append_copy_kernel<T>, grid, block, 0, c->stream, (const char*)past,   \
-                     past_cap, past_len, (const char*)cur, cur_len, (char*)present,          \
-                     present_cap, heads, row_bytes, chunks, copy_past ? 1 : 0, present_len,   \
-                     c->err)
+  const dim3 grid((unsigned)blocks, two ? 2u : 1u), block(kCopyBlock);
+#define SA_COPY(T)                                                                                      \
+  hipLaunchKernelGGL(append_copy_kernel<T>, grid, block, 0, c->stream, (const char*)past,               \
+                     (const char*)past2, past_cap, past_len, (const char*)cur, (const char*)cur2, cur_len, \
+                     (char*)present, (char*)present2, present_cap, heads, row_bytes, chunks,              \
+                     copy_past ? 1 : 0, present_len, c->err)
   switch (vec) {
     case 16: SA_COPY(uint4); break;
     case 8: SA_COPY(uint2); break;

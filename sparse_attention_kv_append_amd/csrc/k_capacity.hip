@@ -8,18 +8,46 @@
 //
 // The pages give one thread per batch entry looping over every broadcast
 // (h, q, k). Here one 256-thread workgroup per batch entry reads each element
-// of the entry's slice of the bias exactly once, coalesced: an extent of 1
-// along heads or queries is not expanded, and an extent of 1 along keys makes
-// a finite element stand for every column. The per-thread maxima are reduced
-// with wave shuffles and one LDS atomic per wave.
+// of the entry's slice of the bias exactly once, coalesced, in 16-byte
+// vectors (four per thread in flight) when the rows are whole vectors: an
+// extent of 1 along heads or queries is not expanded, and an extent of 1
+// along keys makes a finite element stand for every column. Finiteness is
+// read from the exponent bits. The per-thread maxima are reduced with wave
+// shuffles and one LDS atomic per wave.
 #include "sa_internal.h"
 #include "sa_mfma_dev.h"
 
 namespace sa {
 
 constexpr int kCapThreads = 256;
+constexpr int kCapUnroll = 4;  // 16-byte loads per thread in flight at once
 
+// finite test on the raw bits of one element (exponent not all ones)
 template <int DT>
+__device__ __forceinline__ bool bits_finite(uint32_t bits) {
+  if constexpr (DT == SA_F32) return (bits & 0x7f800000u) != 0x7f800000u;
+  else if constexpr (DT == SA_F16) return (bits & 0x7c00u) != 0x7c00u;
+  else return (bits & 0x7f80u) != 0x7f80u;
+}
+
+// 1 + the largest in-row column (e % bd3, or keys - 1 when bd3 == 1) over the
+// finite elements of one 16-byte vector starting at element e0 (the vector
+// lies within one row: bd3 is a multiple of its element count)
+template <int DT>
+__device__ __forceinline__ int vec_best(uint4 v, int64_t e0, int64_t bd3, int64_t keys) {
+  constexpr int PER = DT == SA_F32 ? 4 : 8;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  int last = -1;  // last finite element of the vector
+#pragma unroll
+  for (int j = 0; j < PER; j++) {
+    const uint32_t bits = PER == 4 ? w[j] : ((w[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+    if (bits_finite<DT>(bits)) last = j;
+  }
+  if (last < 0) return 0;
+  return bd3 == 1 ? (int)keys : (int)(e0 % bd3) + last + 1;
+}
+
+template <int DT, bool VEC>
 __global__ void __launch_bounds__(kCapThreads)
 capacity_lengths_kernel(const void* __restrict__ bias, int64_t bd0, int64_t bd1, int64_t bd2, int64_t bd3,
                         int64_t keys, int64_t cur_len, int32_t* __restrict__ valid_len,
@@ -31,11 +59,29 @@ capacity_lengths_kernel(const void* __restrict__ bias, int64_t bd0, int64_t bd1,
   if (threadIdx.x == 0) best_s = 0;
   __syncthreads();
   int best = 0;  // 1 + largest finite column seen by this thread
-  for (int64_t e = threadIdx.x; e < n; e += kCapThreads) {
-    const float v = load_elem<DT>(bias, base + e);
-    if (isfinite(v)) {
-      const int64_t k = bd3 == 1 ? keys - 1 : e % bd3;
-      best = max(best, (int)(k + 1));
+  if constexpr (VEC) {
+    // n and bd3 are multiples of the vector width, the slice is 16-byte aligned
+    constexpr int PER = DT == SA_F32 ? 4 : 8;
+    const uint4* __restrict__ vp = (const uint4*)((const char*)bias + base * (DT == SA_F32 ? 4 : 2));
+    const int64_t nv = n / PER;
+    for (int64_t v0 = threadIdx.x; v0 < nv; v0 += (int64_t)kCapThreads * kCapUnroll) {
+      uint4 vals[kCapUnroll];
+#pragma unroll
+      for (int u = 0; u < kCapUnroll; u++) {
+        const int64_t v = v0 + (int64_t)u * kCapThreads;
+        vals[u] = v < nv ? vp[v] : make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);  // NaN: skipped
+      }
+#pragma unroll
+      for (int u = 0; u < kCapUnroll; u++)
+        best = max(best, vec_best<DT>(vals[u], (v0 + (int64_t)u * kCapThreads) * PER, bd3, keys));
+    }
+  } else {
+    for (int64_t e = threadIdx.x; e < n; e += kCapThreads) {
+      const float v = load_elem<DT>(bias, base + e);
+      if (isfinite(v)) {
+        const int64_t k = bd3 == 1 ? keys - 1 : e % bd3;
+        best = max(best, (int)(k + 1));
+      }
     }
   }
   best = wave_max_nonneg(best);
@@ -52,16 +98,22 @@ sa_status launch_capacity_lengths(sparse_attn_ctx* c, const void* bias, int dtyp
                                   int64_t batch, int64_t keys, int64_t cur_len, int32_t* valid_len,
                                   int32_t* write_pos) {
   const dim3 grid((unsigned)batch), block(kCapThreads);
-#define SA_CAP(DT)                                                                                     \
-  hipLaunchKernelGGL((capacity_lengths_kernel<DT>), grid, block, 0, c->stream, bias, bd[0], bd[1], bd[2], \
+  // 16-byte vectors when every slice and row is a whole number of them
+  const int per = dtype == SA_F32 ? 4 : 8;
+  const bool vec = bd[3] % per == 0 && ((uintptr_t)bias & 15) == 0;
+#define SA_CAP(DT, V)                                                                                      \
+  hipLaunchKernelGGL((capacity_lengths_kernel<DT, V>), grid, block, 0, c->stream, bias, bd[0], bd[1], bd[2], \
                      bd[3], keys, cur_len, valid_len, write_pos)
+#define SA_CAP_V(DT) \
+  if (vec) { SA_CAP(DT, true); } else { SA_CAP(DT, false); }
   if (dtype == SA_F32) {
-    SA_CAP(SA_F32);
+    SA_CAP_V(SA_F32);
   } else if (dtype == SA_F16) {
-    SA_CAP(SA_F16);
+    SA_CAP_V(SA_F16);
   } else {
-    SA_CAP(SA_BF16);
+    SA_CAP_V(SA_BF16);
   }
+#undef SA_CAP_V
 #undef SA_CAP
   return check_hip(c, hipGetLastError(), "capacity_lengths");
 }

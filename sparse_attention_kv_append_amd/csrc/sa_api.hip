@@ -237,11 +237,17 @@ sa_status sparse_attn_kv_append(sparse_attn_ctx* c, int64_t batch, const void* p
                                    past_len, past_capacity, present_k, present_capacity, present_len);
     return s;
   }
-  s = sa::launch_append_copy(c, batch, heads, krow, past_k, past_capacity, past_len, cur_k, cur_len,
-                             present_k, present_capacity, copy_past, present_len);
-  if (s != SA_OK || latent) return s;
+  if (latent)
+    return sa::launch_append_copy(c, batch, heads, krow, past_k, past_capacity, past_len, cur_k, cur_len,
+                                  present_k, present_capacity, copy_past, present_len);
   const int64_t vrow = k.head_dim_v * elem_bytes(k.dtype);
   const bool copy_past_v = past_capacity > 0 && present_v != past_v;
+  if (vrow == krow && copy_past_v == copy_past)  // K and V in one launch
+    return sa::launch_append_copy(c, batch, heads, krow, past_k, past_capacity, past_len, cur_k, cur_len,
+                                  present_k, present_capacity, copy_past, present_len, past_v, cur_v, present_v);
+  s = sa::launch_append_copy(c, batch, heads, krow, past_k, past_capacity, past_len, cur_k, cur_len,
+                             present_k, present_capacity, copy_past, present_len);
+  if (s != SA_OK) return s;
   return sa::launch_append_copy(c, batch, heads, vrow, past_v, past_capacity, past_len, cur_v,
                                 cur_len, present_v, present_capacity, copy_past_v, nullptr);
 }

@@ -116,7 +116,8 @@ sa_status launch_reset_error(sparse_attn_ctx* c);
 sa_status launch_append_copy(sparse_attn_ctx* c, int64_t batch, int64_t heads, int64_t row_bytes,
                              const void* past, int64_t past_cap, const int32_t* past_len,
                              const void* cur, int64_t cur_len, void* present, int64_t present_cap,
-                             bool copy_past, int32_t* present_len);
+                             bool copy_past, int32_t* present_len, const void* past2 = nullptr,
+                             const void* cur2 = nullptr, void* present2 = nullptr);
 sa_status launch_append_quantize(sparse_attn_ctx* c, int64_t batch, int64_t heads, int64_t dk,
                                  int64_t rope, const void* cur_bf16, int64_t cur_len,
                                  const int32_t* past_len, int64_t past_cap, void* present,

@@ -155,10 +155,14 @@ def test_bias_host_errors():
 
 @pytest.mark.parametrize("dtype,shape", [(W.DT_F32, (3, 8, 2, 300)), (W.DT_F32, (3, 1, 1, 300)),
                                          (W.DT_BF16, (300,)), (W.DT_BF16, (3, 1, 2, 300)),
-                                         (W.DT_F16, (1, 8, 1, 300)), (W.DT_F32, (3, 8, 2, 1))])
+                                         (W.DT_F16, (1, 8, 1, 300)), (W.DT_F32, (3, 8, 2, 1)),
+                                         # rows of whole 16-byte vectors: the vector path
+                                         (W.DT_BF16, (3, 1, 2, 320)), (W.DT_F16, (1, 8, 2, 4096)),
+                                         (W.DT_F32, (3, 8, 1, 4100)), (W.DT_BF16, (16384,))])
 def test_capacity_lengths_match_oracle(dtype, shape):
     import torch
-    w = W.CAPACITY_WORKLOADS["capacity_small"].scaled(dtype=dtype)
+    cap = shape[-1] if shape[-1] > 1 else 300
+    w = W.CAPACITY_WORKLOADS["capacity_small"].scaled(dtype=dtype, capacity=cap)
     rng = np.random.default_rng(12)
     b32 = rng.standard_normal(shape).astype(np.float32)
     lead = b32.reshape(-1, shape[-1])
