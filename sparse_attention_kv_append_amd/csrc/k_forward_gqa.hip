@@ -17,6 +17,10 @@
 // keys and updating only its rows), so any valid index rows give IndexShare's
 // result, only more slowly.
 //
+// The optional additive bias (IndexShare `bias_at`, read at each selected
+// key's cache position, after the softcap) is loaded per lane for its eight
+// (row, column) scores of a tile, one iteration before that tile's softmax.
+//
 // Per row the softmax is the usual online form (running maximum and sum in
 // log2 units, the accumulators rescaled when the maximum grows). A row's
 // key count n is its number of entries before the first -1; a workgroup stops
@@ -184,7 +188,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
         const int v32 = v == -1 ? -1 : (v < -1 ? -2 : (v >= bound ? (int)bound : (int)v));
         mx = max(mx, v32);
         if (v32 != -1) mn = min(mn, v32);
-        else atomicMin(&n_s[r], (int)col);
+        else ds_min_i32_at((uint32_t)(uintptr_t)(lds + nrow_off<I64>()) + 4u * (uint32_t)r, (int)col);
       }
     }
     {
@@ -363,25 +367,25 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     });
   };
   // bias of this lane's eight (row, column) scores of a tile: columns 4 g + i
-  // and 16 + 4 g + i, whose keys lanes 0..31 hold (one column each); issued
-  // as untracked loads into braw, waited for by bias_ready
-  uint32_t braw[8];
+  // and 16 + 4 g + i, whose keys lanes 0..31 hold (one column each). The
+  // steady state loads a tile's values one iteration before its softmax, so
+  // they land behind that iteration's gathers (ordinary loads: the compiler
+  // places the wait at the use).
   float bvf[8];
-  auto bias_issue = [&](int64_t colkey) {
+  auto bias_load = [&](int64_t colkey, uint16_t (&dst)[8]) {
     if constexpr (BIAS) {
       const int kc32 = (bkey && colkey >= 0 && colkey < bound) ? (int)colkey : 0;  // clamp as the gather does
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         const int kcol = __shfl(kc32, i < 4 ? 4 * g + i : 16 + 4 * g + i - 4, 64);
-        braw[i] = global_load_u16_asm(brow[0] + (row_on[0] ? kcol : 0));
+        dst[i] = brow[0][row_on[0] ? kcol : 0];
       }
     }
   };
-  auto bias_ready = [&](auto nc) {
+  auto bias_use = [&](const uint16_t (&src)[8]) {
     if constexpr (BIAS) {
-      vm_wait_tied8<decltype(nc)::value>(braw);
 #pragma unroll
-      for (int i = 0; i < 8; i++) bvf[i] = __uint_as_float(braw[i] << 16) * kLog2eL;
+      for (int i = 0; i < 8; i++) bvf[i] = bf16_to_f32(src[i]) * kLog2eL;
     }
   };
   // online softmax of the scores in sa for tile x; `only` < 0: every row,
@@ -444,12 +448,13 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
       int64_t kl = -1;
       if (col < width) kl = load_index<I64>(ibase, (int64_t)r * width + col);
       key_offsets(kl);
-      bias_issue(kl);
+      uint16_t brr[8];
+      bias_load(kl, brr);
       wait_vm<0>();
       __syncthreads();  // every wave is done with the spare slot
       gather_issue(lds + SPARE_OFF);
       wait_vm<0>();
-      bias_ready(std::integral_constant<int, 0>{});
+      bias_use(brr);
       __syncthreads();
       kslot = spare;
       vslot = spare;
@@ -477,7 +482,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   gather_issue(lds + 0 * KV_TILE);
   issue_idx(4);
   kk = finalize(1);
-  int64_t key_n1 = kk;  // keys of the tile after the one being scored, then the one after that
+  const int64_t key_n1 = kk;  // keys of tile 1, then of the tile two after the one being scored
   key_offsets(kk);
   lds_barrier();  // partial slots of tiles 0, 1 are read
   fold(2);
@@ -497,8 +502,9 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     kslot = slot_of(0);
     if (tile_flags(0) & 1) {
       s_alone();
-      bias_issue(key0);
-      bias_ready(std::integral_constant<int, 0>{});
+      uint16_t br0[8];
+      bias_load(key0, br0);
+      bias_use(br0);
       softmax(0, -1, false);
     } else {
       zero_s();
@@ -509,14 +515,27 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
 
   // ---- steady state: iteration t scores tile t+1 interleaved with the PV
   // of tile t, issues the gather of tile t+3 and the index load of tile t+6,
-  // folds index tile t+4 and finalizes tile t+3
-  for (int t = 0; t + 1 < ntile; t++) {
+  // folds index tile t+4 and finalizes tile t+3. With a bias it also loads
+  // tile t+2's bias (into bload) and uses tile t+1's, loaded one iteration
+  // earlier (buse).
+  // With a bias, two iterations per trip with the bias registers alternating,
+  // so a tile's values stay in the same registers from their load to their use.
+  constexpr int UN = BIAS ? 2 : 1;
+  uint16_t ba[8], bb[8];
+  bias_load(key_n1, ba);
+  for (int t0 = 0; t0 + 1 < ntile; t0 += UN) {
+#pragma unroll
+   for (int u = 0; u < UN; u++) {
+    const int t = t0 + u;
+    if (u > 0 && t + 1 >= ntile) break;
+    const uint16_t(&buse)[8] = u == 0 ? ba : bb;
+    uint16_t(&bload)[8] = u == 0 ? bb : ba;
     wait_vm<GLOADS + IL>();  // tile t+1 and index tile t+4 have landed (the last iteration's loads may not)
     lds_barrier();           // for every wave; tile t-1's slot and partial slot t+3 & 1 are free
     kk = finalize(t + 3);    // partials folded in the last iteration
     key_offsets(kk);
     const bool shared_next = (tile_flags(t + 1) & 1) != 0;
-    bias_issue(key_n1);  // lands during the MFMAs below (unused when the tile is not shared)
+    bias_load(key_n2, bload);  // unused when tile t+2 is not shared
     kslot = slot_of(t + 1);
     vslot = slot_of(t);
     zero_s();
@@ -541,17 +560,15 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     });
     issue_idx(t + 6);
     fold(t + 4);
-    // every load but the gathers and index loads above (the registers are
-    // defined by this wait on every path, so none is copied while in flight)
-    bias_ready(std::integral_constant<int, GLOADS + IL>{});
     if (shared_next) {
+      bias_use(buse);
       softmax(t + 1, -1, false);
     } else {
       softmax(t + 1, -1, true);
       row_by_row(t + 1);
     }
-    key_n1 = key_n2;
     key_n2 = kk;
+   }
   }
 
   // ---- the last tile's PV alone

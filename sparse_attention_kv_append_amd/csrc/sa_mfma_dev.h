@@ -43,23 +43,12 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// A 16-bit global load issued as inline asm (zero-extended into a dword).
-// The compiler does not track it, so it neither drains the loads in flight
-// before it nor waits for it: vm_wait_tied8 below is the wait.
-__device__ __forceinline__ uint32_t global_load_u16_asm(const uint16_t* p) {
-  uint32_t r;
-  asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
-// Wait until at most N vector-memory loads are outstanding and make the eight
-// values depend on the wait (loads complete in issue order).
-template <int N>
-__device__ __forceinline__ void vm_wait_tied8(uint32_t (&a)[8]) {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%8)"
-               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
-               : "n"(N)
-               : "memory");
+// LDS atomic minimum issued as inline asm. The compiler treats a visible LDS
+// atomic as possibly touching what the direct-to-LDS gathers in flight write
+// and waits for all of them first; this one does not. LDS operations complete
+// in order, so the compiler's own later LDS waits still cover it.
+__device__ __forceinline__ void ds_min_i32_at(uint32_t addr, int v) {
+  asm volatile("ds_min_i32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
 // LDS reads issued as inline asm with an immediate offset. The compiler
