@@ -123,6 +123,9 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     row_h[rb] = (int)(kvh * group) + (m - r * group);
     row_on[rb] = m < R * group && r < rlive;
   }
+  // live rows are a prefix of the workgroup's rows: a wave with none (decode
+  // leaves most of the 128 rows empty) only gathers, folds and syncs
+  const bool wlive = 16 * RB * wave < rlive * group;
 
   // ---- the optional bias (IndexShare `bias_at`): each row's element at key
   // 0 (an extent of 1 broadcasts); rows that do not exist read element 0
@@ -458,9 +461,11 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
       __syncthreads();
       kslot = spare;
       vslot = spare;
-      s_alone();
-      softmax(x, r, false);
-      pv_alone();
+      if (wlive) {
+        s_alone();
+        softmax(x, r, false);
+        pv_alone();
+      }
     }
     // the tile's PV in the pipeline must add nothing
 #pragma unroll
@@ -501,14 +506,18 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     lds_barrier();
     kslot = slot_of(0);
     if (tile_flags(0) & 1) {
-      s_alone();
-      uint16_t br0[8];
-      bias_load(key0, br0);
-      bias_use(br0);
-      softmax(0, -1, false);
+      if (wlive) {
+        s_alone();
+        uint16_t br0[8];
+        bias_load(key0, br0);
+        bias_use(br0);
+        softmax(0, -1, false);
+      }
     } else {
-      zero_s();
-      softmax(0, -1, true);
+      if (wlive) {
+        zero_s();
+        softmax(0, -1, true);
+      }
       row_by_row(0);
     }
   }
@@ -522,6 +531,24 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   // so a tile's values stay in the same registers from their load to their use.
   constexpr int UN = BIAS ? 2 : 1;
   uint16_t ba[8], bb[8];
+  if (!wlive) {
+    // a wave with no live row: the same gathers, index loads, folds and
+    // barriers, no reads, products or softmax
+    for (int t = 0; t + 1 < ntile; t++) {
+      wait_vm<GLOADS + IL>();
+      lds_barrier();
+      kk = finalize(t + 3);
+      key_offsets(kk);
+      const bool shared_next = (tile_flags(t + 1) & 1) != 0;
+#pragma unroll
+      for (int j = 0; j < GLOADS; j++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(grsrc, (__attribute__((address_space(3))) void*)(lds + ((t + 3) % NSTAGE) * KV_TILE + 1024 * (GLOADS * wave + j)),
+                                                16, goff[j], 0, 0, 0);
+      issue_idx(t + 6);
+      fold(t + 4);
+      if (!shared_next) row_by_row(t + 1);
+    }
+  } else {
   bias_load(key_n1, ba);
   for (int t0 = 0; t0 + 1 < ntile; t0 += UN) {
 #pragma unroll
@@ -570,9 +597,10 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     key_n2 = kk;
    }
   }
+  }
 
   // ---- the last tile's PV alone
-  if (ntile > 0) {
+  if (ntile > 0 && wlive) {
     vslot = slot_of(ntile - 1);
     pv_alone();
   }
