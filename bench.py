@@ -722,9 +722,10 @@ def digest(args):
                 v = float(r["Counter_Value"])
                 per_kernel.setdefault(r["Kernel_Name"], []).append(v)
                 if "copyBuffer" in r["Kernel_Name"]:
-                    calib.append((int(r["Grid_Size"]), v))
-        # the calibration copy is the run's first and largest device copy
-        return per_kernel, max(calib)[1]
+                    calib.append(v)
+        # the calibration copy is the run's first device copy (pmc_run makes
+        # it before building any input; later copies may be larger)
+        return per_kernel, calib[0]
 
     fetch, f_copy = read(args.digest[0], "FETCH_SIZE")
     write, w_copy = read(args.digest[1], "WRITE_SIZE")
