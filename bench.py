@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--workload", default="decode_bf16",
                    choices=["decode_bf16", "decode_fp8", "prefill_bf16", "dense_gqa", "csa_decode",
-                            "csa_index_decode", "capacity_decode"])
+                            "csa_index_decode", "capacity_decode", "gqa_decode_b2"])
     p.add_argument("--rotate", type=int, default=8, help="independent (query, index) sets")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
@@ -210,8 +210,10 @@ class Setup:
     # ---- reporting
     def roofline(self, kw, k_avg_s):
         w = self.w
-        if w.pattern == "causal_prefill" or self.path == 4:
+        if w.pattern == "causal_prefill" or (self.path == 4 and w.q_seq > 1):
             return "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", kw["flops"] / k_avg_s / 1e12
+        if self.path == 4:  # grouped-query decode: the gathers bound it
+            return "hbm", HBM_PEAK_GBS, "GB/s", kw["bytes"] / k_avg_s / 1e9
         if w.layout == self.W.LAYOUT_SEPARATE:
             return "alu", VALU_FP32_PEAK_TFLOPS, "TFLOP/s", kw["flops"] / k_avg_s / 1e12
         return "hbm", HBM_PEAK_GBS, "GB/s", kw["bytes"] / k_avg_s / 1e9
@@ -282,8 +284,8 @@ class CapacitySetup(Setup):
         self.fp8 = False
         self.selected = [int((ih >= 0).sum()) for ih in self.idx_host]
         # a biased forward runs on the grouped-query kernel where the plan takes it, else generic
-        plan, _ = self.ctx.query_plan(B, Sq, 1, w.width)
-        self.path, self.splits = (4 if plan == 4 else 0), 1
+        plan, nsplit = self.ctx.query_plan(B, Sq, 1, w.width)
+        self.path, self.splits = (4, nsplit) if plan == 4 else (0, 1)
 
     def fused_step(self):
         return False

@@ -30,6 +30,9 @@ Workloads (sizes are the ones the pages' operators are exercised at; the
                    128 current, 128 query rows; row q selects every key of
                    [0, 8064 + q] (causal with per-batch offset 8064), width
                    8192; softcap 50; bf16.
+* ``gqa_decode_b2`` batch 2, 32 q heads / 8 kv heads, head dim 128, past
+                   32767 + 1 current, 1 query, top-8192 uniform sorted; bf16
+                   (few (batch, kv head) pairs: the split-KV decode).
 
 Capacity mode with an attention bias (``CAPACITY_WORKLOADS``, drawn by
 ``make_capacity_numpy``): separate K and V caches of ``capacity`` rows per
@@ -140,6 +143,10 @@ WORKLOADS = {
                           layout=LAYOUT_SEPARATE, cache_format=CACHE_DENSE,
                           scale=float(1.0 / np.sqrt(np.float32(128.0))), softcap=50.0,
                           pattern="causal_all", seed=4),
+    "gqa_decode_b2": Workload("gqa_decode_b2", batch=2, hq=32, hkv=8, q_seq=1, dk=128, dv=128,
+                              past=32767, cur=1, width=8192, topk=8192, dtype=DT_BF16,
+                              layout=LAYOUT_SEPARATE, cache_format=CACHE_DENSE,
+                              scale=float(1.0 / np.sqrt(np.float32(128.0))), seed=7),
 }
 
 

@@ -77,7 +77,8 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
                    const void* __restrict__ idx, const int32_t* __restrict__ valid_len, uint16_t* __restrict__ y,
                    int64_t batch, int64_t hkv, int64_t q_seq, int64_t cap, int64_t width, int group, int nqb,
                    float scale, float softcap, const uint16_t* __restrict__ bias, int64_t bd0, int64_t bd1,
-                   int64_t bd2, int64_t bd3) {
+                   int64_t bd2, int64_t bd3, int splits, float* __restrict__ part_o,
+                   float* __restrict__ part_ml) {
   static_assert(gq::RB == 1, "the bias prefetch holds one row block per wave");
   using namespace gq;
   constexpr int ITB = idx_tile_bytes<I64>();
@@ -98,7 +99,9 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   // ---- workgroup -> (batch, kv head, query block); the query blocks of one
   // (batch, kv head) share blockIdx % 8 (one XCD, one L2)
   const int xcd = (int)(blockIdx.x & 7u);
-  const int rest = (int)(blockIdx.x >> 3);
+  const int rest0 = (int)(blockIdx.x >> 3);
+  const int sp = rest0 % splits;  // split-KV: this workgroup's share of the index columns
+  const int rest = rest0 / splits;
   const int qb = rest % nqb;
   const int64_t pr = (int64_t)(rest / nqb) * 8 + xcd;  // (batch, kv head) pair
   if (pr >= batch * hkv) return;                       // grid padding (uniform)
@@ -110,7 +113,11 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   const int hq = (int)(hkv * group);
   int64_t bound = valid_len ? (int64_t)valid_len[b] : cap;
   bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
-  const int ntile_w = (int)((width + KT - 1) / KT);
+  // tiles [xo, xo + ntile_w) of the index rows; the kernel numbers them from 0
+  const int ntile_all = (int)((width + KT - 1) / KT);
+  const int tps = (ntile_all + splits - 1) / splits;
+  const int xo = min(ntile_all, sp * tps);
+  const int ntile_w = min(ntile_all, xo + tps) - xo;
 
   // this lane's rows: block rb holds row m = 16 (RB wave + rb) + c16
   int row_q[RB], row_h[RB];
@@ -161,7 +168,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
       const int d = 64 * (IL * wave + i) + lane;
       const int r = d / (KT * ISZ / 4);
       const int wj = d - r * (KT * ISZ / 4);  // dword within the row's 32 columns
-      const int64_t col = (int64_t)x * KT + wj / (ISZ / 4);
+      const int64_t col = (int64_t)(xo + x) * KT + wj / (ISZ / 4);
       uint32_t off = 0x80000000u;  // past the buffer: zeros
       if (r < rlive && col < width) off = (uint32_t)(((int64_t)r * width + col) * ISZ + (wj % (ISZ / 4)) * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(irsrc, (__attribute__((address_space(3))) void*)(slot + 256 * (IL * wave + i)),
@@ -181,7 +188,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   auto fold = [&](int x) {
     const lds_u8* slot = lds + IDX_OFF + (x % IDX_SLOTS) * ITB;
     const int j = tid & 31, tg = tid >> 5;
-    const int64_t col = (int64_t)x * KT + j;
+    const int64_t col = (int64_t)(xo + x) * KT + j;
     int mx = -1, mn = 0x7fffffff;
 #pragma unroll
     for (int k = 0; k < RMAX / (THREADS / 32); k++) {
@@ -395,7 +402,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   // else only the rows of query `only`; `none`: every row masked (the
   // tile is redone row by row). Rescales O and returns P^T in pb.
   auto softmax = [&](int x, int only, bool none) {
-    const int64_t c0 = (int64_t)x * KT;
+    const int64_t c0 = (int64_t)(xo + x) * KT;
 #pragma unroll
     for (int rb = 0; rb < RB; rb++) {
       float xs[8];
@@ -446,8 +453,8 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   auto row_by_row = [&](int x) {
     const uint32_t spare = (uint32_t)(uintptr_t)(lds + SPARE_OFF);
     for (int r = 0; r < rlive; r++) {
-      if ((int64_t)n_s[r] <= (int64_t)x * KT) continue;  // uniform: the row ended before this tile
-      const int64_t col = (int64_t)x * KT + (lane & 31);
+      if ((int64_t)n_s[r] <= (int64_t)(xo + x) * KT) continue;  // uniform: the row ended before this tile
+      const int64_t col = (int64_t)(xo + x) * KT + (lane & 31);
       int64_t kl = -1;
       if (col < width) kl = load_index<I64>(ibase, (int64_t)r * width + col);
       key_offsets(kl);
@@ -607,6 +614,20 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   wait_vm<0>();  // loads issued past the last tile
 
   // ---- store: lane holds O^T[16 dt + 4 g + r][row c16] of each block
+  if (splits > 1) {
+    // split-KV: the unnormalised O, the running maximum (log2 units) and sum
+    // of each row for the combine
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++) {
+      if (!row_on[rb]) continue;
+      const int64_t prow = ((b * hq + row_h[rb]) * q_seq + q0 + row_q[rb]) * splits + sp;
+      float* op = part_o + prow * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < DVT; dt++) *(f32x4_l*)(op + 16 * dt) = o[rb][dt];
+      if (g == 0) *(float2*)(part_ml + prow * 2) = make_float2(m_run[rb], l_run[rb]);
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; rb++) {
     if (!row_on[rb]) continue;
@@ -619,6 +640,63 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
       *(u32x2_l*)(yp + 16 * dt) = w2;
     }
   }
+}
+
+// Split-KV combine: per output row, y = sum_j O_j 2^(m_j - M) / sum_j l_j 2^(m_j - M)
+// over the splits j (M the largest m_j), stored as bf16; a row no split saw gives zeros.
+// 32 lanes per row, 4 dims each.
+__global__ void __launch_bounds__(256)
+gqa_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                   uint16_t* __restrict__ y, int64_t rows, int splits) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= rows) return;
+  const int d = (threadIdx.x & 31) * 4;
+  float M = -INFINITY;
+  for (int j = 0; j < splits; j++) M = fmaxf(M, part_ml[(row * splits + j) * 2]);
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+    for (int j = 0; j < splits; j++) {
+      const float2 ml = *(const float2*)(part_ml + (row * splits + j) * 2);
+      if (ml.x == -INFINITY) continue;  // this split saw no key of the row
+      const float w = exp2f(ml.x - M);
+      const float4 v = *(const float4*)(part_o + (row * splits + j) * gq::D + d);
+      L += ml.y * w;
+      acc.x += v.x * w;
+      acc.y += v.y * w;
+      acc.z += v.z * w;
+      acc.w += v.w * w;
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
+  *(uint2*)(y + row * gq::D + d) = make_uint2(lo, hi);
+}
+
+// (row, split) units the split-KV buffers hold: splits are only taken while
+// (batch, kv head, query block) units number fewer than the CUs, and a unit
+// holds at most 128 rows, so rows x splits < 128 x (2 x 256)
+int64_t gqa_partial_rows(const sa_config& cfg) {
+  const int64_t rows_max = cfg.max_batch * cfg.max_q_seq * cfg.num_heads;
+  return std::min<int64_t>(rows_max * 16, (int64_t)gq::MROWS * 2 * kNumCUs);
+}
+
+// Splits per (batch, kv head, query block) so that the launch covers the CUs,
+// at least four 32-key tiles per split (the pipeline's prologue is six tiles
+// deep), at most 16; 1 when the buffers cannot hold the partials.
+int gqa_splits(const sparse_attn_ctx* c, int64_t batch, int64_t q_seq, int64_t width) {
+  using namespace gq;
+  const sa_config& k = c->cfg;
+  const int64_t group = k.num_heads / k.kv_num_heads;
+  const int64_t R = group >= MROWS ? 1 : std::min<int64_t>(RMAX, MROWS / group);
+  const int64_t units = batch * k.kv_num_heads * ((q_seq + R - 1) / R);
+  if (units <= 0 || units >= kNumCUs) return 1;
+  const int64_t want = (kNumCUs + units - 1) / units;
+  const int64_t by_tiles = std::max<int64_t>(1, ((width + KT - 1) / KT) / 4);
+  const int64_t s = std::min<int64_t>(std::min<int64_t>(want, by_tiles), 16);
+  if (s <= 1 || batch * q_seq * k.num_heads * s > c->gpart_rows) return 1;
+  return (int)s;
 }
 
 bool gqa_supported(const sa_config& cfg, int64_t index_heads) {
@@ -639,7 +717,8 @@ sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
   const int64_t nqb = (a.q_seq + R - 1) / R;
   const int64_t pairs = a.batch * a.hkv;
   if (pairs <= 0 || nqb <= 0) return SA_OK;
-  const int64_t wgs = (pairs + 7) / 8 * 8 * nqb;
+  const int splits = gqa_splits(c, a.batch, a.q_seq, a.width);
+  const int64_t wgs = (pairs + 7) / 8 * 8 * nqb * splits;
   if (wgs > 0x7fffffffLL || nqb > 0x7fffffffLL) return set_error(c, SA_E_SHAPE, "forward: too many rows for one launch");
   if (a.cap > (int64_t)(0x7fffffffLL / ROWB)) return set_error(c, SA_E_SHAPE, "forward: cache too long for 32-bit row offsets");
   if ((int64_t)R * a.width * (a.idx64 ? 8 : 4) > 0x7fffffffLL)
@@ -664,7 +743,8 @@ sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
   hipLaunchKernelGGL((gqa_forward_kernel<I, C, BI>), grid, block, lds, c->stream, (const uint16_t*)a.q,      \
                      (const uint8_t*)a.k, (const uint8_t*)a.v, a.idx, a.valid_len, (uint16_t*)a.y, a.batch, \
                      a.hkv, a.q_seq, a.cap, a.width, group, (int)nqb, a.scale, a.softcap,                    \
-                     (const uint16_t*)a.bias, a.bd[0], a.bd[1], a.bd[2], a.bd[3])
+                     (const uint16_t*)a.bias, a.bd[0], a.bd[1], a.bd[2], a.bd[3], splits, c->gpart_o,    \
+                     c->gpart_ml)
   switch (variant) {
     case 0: SA_GQA(false, false, false); break;
     case 1: SA_GQA(true, false, false); break;
@@ -677,7 +757,12 @@ sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
   }
 #undef SA_GQA
   prof_end(c);
-  return check_hip(c, hipGetLastError(), "forward (gqa)");
+  sa_status st = check_hip(c, hipGetLastError(), "forward (gqa)");
+  if (st != SA_OK || splits == 1) return st;
+  const int64_t rows = a.batch * a.hq * a.q_seq;
+  hipLaunchKernelGGL(gqa_combine_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, c->stream, c->gpart_o,
+                     c->gpart_ml, (uint16_t*)a.y, rows, splits);
+  return check_hip(c, hipGetLastError(), "forward (gqa combine)");
 }
 
 }  // namespace sa

@@ -59,11 +59,12 @@ void prof_end(sparse_attn_ctx* c) {
 }
 
 void free_buffers(sparse_attn_ctx* c) {
-  void* bufs[] = {c->err, c->partial_o, c->partial_ml, c->zeros, c->row_key, c->row_done};
+  void* bufs[] = {c->err, c->partial_o, c->partial_ml, c->zeros, c->row_key, c->row_done, c->gpart_o, c->gpart_ml};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
   c->err = nullptr;
   c->partial_o = c->partial_ml = nullptr;
+  c->gpart_o = c->gpart_ml = nullptr;
   c->zeros = nullptr;
   c->row_key = nullptr;
   c->row_done = nullptr;
@@ -121,6 +122,9 @@ sa_status sparse_attn_create(const sa_config* cfg, void* hip_stream, sparse_attn
   c->err = nullptr;
   c->partial_o = nullptr;
   c->partial_ml = nullptr;
+  c->gpart_o = nullptr;
+  c->gpart_ml = nullptr;
+  c->gpart_rows = 0;
   c->partial_rows = 0;
   c->zeros = nullptr;
   c->row_key = nullptr;
@@ -142,6 +146,12 @@ sa_status sparse_attn_create(const sa_config* cfg, void* hip_stream, sparse_attn
       if (e == hipSuccess)
         e = hipMalloc((void**)&c->partial_ml, (size_t)need * k.num_heads * 2 * sizeof(float));
     }
+  }
+  if (e == hipSuccess && sa::gqa_supported(k, 1)) {
+    const int64_t need = sa::gqa_partial_rows(k);
+    e = hipMalloc((void**)&c->gpart_o, (size_t)need * 128 * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&c->gpart_ml, (size_t)need * 2 * sizeof(float));
+    if (e == hipSuccess) c->gpart_rows = need;
   }
   if (e == hipSuccess) e = hipMalloc((void**)&c->zeros, 1024);
   if (e == hipSuccess) e = hipMemset(c->zeros, 0, 1024);
@@ -302,7 +312,8 @@ sa_status sparse_attn_query_plan(const sparse_attn_ctx* c, int64_t batch, int64_
                                  int64_t index_heads, int64_t width, int32_t* path, int32_t* splits) {
   if (!live(c) || !path || !splits) return SA_E_STATE;
   *path = sa::forward_path(c->cfg, index_heads);
-  *splits = (*path >= 1 && *path <= 3) ? sa::mla_splits(batch * q_seq, width) : 1;
+  *splits = (*path >= 1 && *path <= 3) ? sa::mla_splits(batch * q_seq, width)
+            : (*path == 4 ? sa::gqa_splits(c, batch, q_seq, width) : 1);
   return SA_OK;
 }
 

@@ -39,6 +39,9 @@ struct sparse_attn_ctx {
   float* partial_o;     // device: split-K unnormalised outputs
   float* partial_ml;    // device: split-K (max, sum) pairs
   int64_t partial_rows; // capacity of the partial buffers in (row, split) units
+  float* gpart_o;       // device: grouped-query split-KV unnormalised outputs [(row, split)][128]
+  float* gpart_ml;      // device: grouped-query split-KV (max, sum) pairs
+  int64_t gpart_rows;   // capacity of those in (row, split) units
   uint8_t* zeros;       // device: 1 KB of zeros (source of padded tile slots)
   unsigned long long* row_key;  // device [rows_cap]: per-row first violation, fused validation
   unsigned* row_done;           // device [rows_cap]: splits of a row that finished validation
@@ -165,6 +168,10 @@ bool pair_supported(const sa_config& cfg, int64_t index_heads);
 // the grouped-query kernel: bf16 separate K/V caches of 128 dims, one index
 // list per (batch, query), group size up to 128, per-head cache below 2 GiB
 bool gqa_supported(const sa_config& cfg, int64_t index_heads);
+// split-KV count of the grouped-query kernel for these sizes (1 = no split)
+int gqa_splits(const sparse_attn_ctx* c, int64_t batch, int64_t q_seq, int64_t width);
+// (row, split) capacity of the grouped-query split-KV buffers a config needs
+int64_t gqa_partial_rows(const sa_config& cfg);
 int mla_splits(int64_t rows, int64_t width);
 sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a);
 // capacity-mode length recovery from the bias frontier: per batch entry,

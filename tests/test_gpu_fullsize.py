@@ -27,6 +27,7 @@ SAMPLES = {
     "decode_fp8": [(0, 0), (5, 0), (40, 0), (63, 0)],
     "prefill_bf16": [(0, 0), (0, 1), (0, 2046), (0, 2047), (0, 2048), (0, 3001), (0, 4095)],
     "dense_gqa": [(0, 0), (3, 64), (7, 127)],
+    "gqa_decode_b2": [(0, 0), (1, 0)],
 }
 
 

@@ -99,3 +99,41 @@ def test_gqa_mixed_rows_and_ragged_lengths(i64):
     assert np.array_equal(dev["valid_len"], vl)
     err = check_close(dev["y"], y_ref, w.dtype, "gqa mixed")
     banner(f"gqa mixed: max |Y - oracle| = {err:.3e}")
+
+
+SPLIT_CASES = {
+    # few (batch, kv head) units: the key columns are split over several
+    # workgroups and a combine merges their partial (max, sum, O)
+    "decode_b1_long": GQA.scaled(batch=1, hq=8, hkv=2, q_seq=1, past=5000, cur=1, width=4000, topk=3900,
+                                 pattern="uniform", softcap=0.0),
+    # uneven last split, rows of different lengths (some end before the last splits)
+    "decode_ragged": GQA.scaled(batch=2, hq=32, hkv=4, q_seq=1, past=3000, cur=1, width=1900, topk=1850,
+                                pattern="uniform"),
+    # several queries per workgroup, causal (shared tiles), with a split
+    "causal_split": GQA.scaled(batch=1, hq=8, hkv=2, q_seq=12, past=1200, cur=12, width=1212, topk=1212),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_gqa_split_kv(name):
+    """Split-KV decode: the plan splits, and Y equals the oracle's."""
+    w = SPLIT_CASES[name]
+    ctx = make_ctx(w)
+    path, splits = ctx.query_plan(w.batch, w.q_seq, 1, w.width)
+    banner(f"gqa split-kv {name}: path {path} splits {splits}")
+    assert path == 4 and splits > 1
+    inp = W.make_numpy(w)
+    if name == "decode_ragged":
+        # cut rows short: entries past a per-row length become -1 padding
+        rng = np.random.default_rng(3)
+        idx = inp["indices"]
+        for b in range(w.batch):
+            n = int(rng.integers(1, w.width))
+            idx[b, 0, 0, n:] = -1
+    dev = run_device(w, inp, ctx=ctx)
+    ctx.destroy()
+    assert dev["word"] == 0, dev["msg"]
+    y_ref, pk, pv = run_oracle(w, inp)
+    check_present(w, dev, pk, pv)
+    err = check_close(dev["y"], y_ref, w.dtype, name)
+    banner(f"{name}: max |Y - oracle| = {err:.3e}")
