@@ -7,7 +7,10 @@
 // previous valid index is c-1's value otherwise). So every column is checked
 // against its left neighbour at once, and the row's verdict is the violation
 // with the smallest column; a row with no violation and -1 in column 0 is
-// all padding. One wave owns one row and walks it 64 columns at a time.
+// all padding. One wave owns one row and walks it 64 columns at a time; when
+// there are few rows and they are long, a workgroup owns one row and each of
+// its four waves walks a quarter of the columns, the first quarter with a
+// violation giving the row's verdict.
 //
 // Into the context's error block, the launch's smallest failing (row, col)
 // is gathered with an atomic minimum; the last block to finish then records
@@ -45,39 +48,49 @@ validate_kernel(const void* __restrict__ idx, int64_t rows, int64_t q_seq, int64
                 int64_t width,
                 const int32_t* __restrict__ valid_len, int64_t cache_len,
                 uint32_t* __restrict__ word, uint8_t* __restrict__ row_class,
-                uint64_t* __restrict__ first_bad, ErrorBlock* __restrict__ eb) {
+                uint64_t* __restrict__ first_bad, ErrorBlock* __restrict__ eb, int wide) {
+  // wide == 0: one wave per row (4 rows per block); wide != 0: one block per
+  // row, wave w scanning the w-th quarter of its columns (few, long rows)
+  __shared__ int w_cls[4];
+  __shared__ long long w_col[4];
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int64_t row = wide ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * 4 + wv;
+  int cls = 0;
+  int64_t col = -1;
+  int64_t first_val = 0;
   if (row < rows) {
     const int64_t b = row / rows_per_batch;
     const int64_t bound = valid_len ? (int64_t)valid_len[b] : cache_len;
     const int64_t base = row * width;
-    const int64_t first_val = load_index<I64>(idx, base);
-    int64_t carry = 0;  // value of the column left of the current chunk
-    int cls = 0;
-    int64_t col = -1;
+    const int64_t seg = wide ? (width + 3) / 4 : width;
+    const int64_t cbeg = wide ? min(width, (int64_t)wv * seg) : 0;
+    const int64_t cend = min(width, cbeg + seg);
+    first_val = load_index<I64>(idx, base);
+    // value of the column left of the current chunk (column 0 has none)
+    int64_t carry = cbeg > 0 ? load_index<I64>(idx, base + cbeg - 1) : 0;
     // 8 chunks of 64 columns per round trip: their loads are all in flight
     // before the first chunk is checked
-    for (int64_t c0 = 0; c0 < width && cls == 0; c0 += 8 * 64) {
-      // unconditional loads (addresses clamped into the row) so all eight are
-      // issued before the first wait; columns past the row are fixed up after
+    for (int64_t c0 = cbeg; c0 < cend && cls == 0; c0 += 8 * 64) {
+      // unconditional loads (addresses clamped into the range) so all eight
+      // are issued before the first wait; columns past it are fixed up after
       int64_t vals[8];
 #pragma unroll
       for (int k = 0; k < 8; k++) {
         const int64_t c = c0 + 64 * k + lane;
-        vals[k] = load_index<I64>(idx, base + (c < width ? c : width - 1));
+        vals[k] = load_index<I64>(idx, base + (c < cend ? c : cend - 1));
       }
 #pragma unroll
       for (int k = 0; k < 8; k++)
-        if (c0 + 64 * k + lane >= width) vals[k] = -1;
+        if (c0 + 64 * k + lane >= cend) vals[k] = -1;
 #pragma unroll
       for (int k = 0; k < 8; k++) {
         const int64_t c = c0 + 64 * k + lane;
-        if (c0 + 64 * k >= width || cls != 0) break;
+        if (c0 + 64 * k >= cend || cls != 0) break;
         const int64_t v = vals[k];
         int64_t u = shfl_up1<I64>(v);
         if (lane == 0) u = carry;
-        const int kc = c < width ? column_class(c, v, u, bound) : 0;
+        const int kc = c < cend ? column_class(c, v, u, bound) : 0;
         const uint64_t m = __ballot(kc != 0);
         if (m != 0ull) {
           const int src = __ffsll((long long)m) - 1;
@@ -87,6 +100,22 @@ validate_kernel(const void* __restrict__ idx, int64_t rows, int64_t q_seq, int64
         carry = shfl_from<I64>(v, 63);
       }
     }
+  }
+  if (wide) {
+    // the row's verdict: the first quarter holding a violation (the prefix
+    // before it is valid, so its local verdict is the row's)
+    if (lane == 0) {
+      w_cls[wv] = cls;
+      w_col[wv] = col;
+    }
+    __syncthreads();
+    cls = 0;
+    for (int w = 0; w < 4 && cls == 0; w++) {
+      cls = w_cls[w];
+      col = w_col[w];
+    }
+  }
+  if (row < rows && (!wide || wv == 0)) {
     if (cls == 0 && first_val == -1) {
       cls = 6;  // the row holds only -1
       col = width;
@@ -112,7 +141,9 @@ sa_status launch_validate(sparse_attn_ctx* c, const void* idx, int64_t batch, in
                           uint64_t* first_bad) {
   const int64_t rows = batch * heads * q_seq;
   if (rows <= 0) return SA_OK;
-  const int64_t blocks = (rows + 3) / 4;
+  // few long rows: a block per row (four waves on its columns); else a wave per row
+  const int wide = (rows < 4 * kNumCUs && width >= 1024) ? 1 : 0;
+  const int64_t blocks = wide ? rows : (rows + 3) / 4;
   if (blocks > 0x7fffffffLL) return set_error(c, SA_E_SHAPE, "validate_indices: too many rows");
   // the context's block gathers the first failure's detail; caller-owned
   // words and slots only get the OR and the atomic minimum
@@ -120,11 +151,11 @@ sa_status launch_validate(sparse_attn_ctx* c, const void* idx, int64_t batch, in
   if (c->cfg.index_dtype == SA_IDX_I64) {
     hipLaunchKernelGGL(validate_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, c->stream, idx,
                        rows, q_seq, heads * q_seq, width, valid_len, cache_len, word, row_class,
-                       first_bad, eb);
+                       first_bad, eb, wide);
   } else {
     hipLaunchKernelGGL(validate_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, c->stream,
                        idx, rows, q_seq, heads * q_seq, width, valid_len, cache_len, word,
-                       row_class, first_bad, eb);
+                       row_class, first_bad, eb, wide);
   }
   return check_hip(c, hipGetLastError(), "validate_indices");
 }
