@@ -648,24 +648,35 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
 __global__ void __launch_bounds__(256)
 gqa_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                    uint16_t* __restrict__ y, int64_t rows, int splits) {
+  constexpr int SMAX = 16;  // the most splits gqa_splits takes
   const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   if (row >= rows) return;
   const int d = (threadIdx.x & 31) * 4;
+  // every split's values loaded at once (indices clamped, extra ones ignored)
+  float2 ml[SMAX];
+  float4 v[SMAX];
+#pragma unroll
+  for (int j = 0; j < SMAX; j++) {
+    const int64_t pj = row * splits + min(j, splits - 1);
+    ml[j] = *(const float2*)(part_ml + pj * 2);
+    v[j] = *(const float4*)(part_o + pj * gq::D + d);
+  }
   float M = -INFINITY;
-  for (int j = 0; j < splits; j++) M = fmaxf(M, part_ml[(row * splits + j) * 2]);
+#pragma unroll
+  for (int j = 0; j < SMAX; j++)
+    if (j < splits) M = fmaxf(M, ml[j].x);
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (M != -INFINITY) {
-    for (int j = 0; j < splits; j++) {
-      const float2 ml = *(const float2*)(part_ml + (row * splits + j) * 2);
-      if (ml.x == -INFINITY) continue;  // this split saw no key of the row
-      const float w = exp2f(ml.x - M);
-      const float4 v = *(const float4*)(part_o + (row * splits + j) * gq::D + d);
-      L += ml.y * w;
-      acc.x += v.x * w;
-      acc.y += v.y * w;
-      acc.z += v.z * w;
-      acc.w += v.w * w;
+#pragma unroll
+    for (int j = 0; j < SMAX; j++) {
+      if (j >= splits || ml[j].x == -INFINITY) continue;  // past the splits, or a split that saw no key of the row
+      const float w = exp2f(ml[j].x - M);
+      L += ml[j].y * w;
+      acc.x += v[j].x * w;
+      acc.y += v[j].y * w;
+      acc.z += v[j].z * w;
+      acc.w += v[j].w * w;
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
