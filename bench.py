@@ -242,7 +242,8 @@ class CapacitySetup(Setup):
     the device, per-batch live lengths carried only by the bias's -inf
     frontier, and a step of capacity_lengths (valid length and write position
     from the bias) -> in-place kv_append at the write position ->
-    forward_bias with fused validation against the recovered lengths."""
+    forward_bias with fused validation against the recovered lengths (one
+    sparse_attn_capacity_step call)."""
 
     def __init__(self, name, rotate):
         import numpy as np
@@ -293,11 +294,8 @@ class CapacitySetup(Setup):
     def step(self, i):
         w, c = self.w, self.ctx
         r = i % len(self.idxs)
-        c.reset_error_async()
-        c.capacity_lengths(self.bias, w.batch, w.q_seq, w.cap, w.cur, self.vl, self.wp)
-        c.kv_append(w.batch, self.k, self.v, w.cap, self.wp, self.cur_k, self.cur_v, w.cur, self.k, self.v, w.cap)
-        c.forward_bias(self.qs[r], w.batch, w.q_seq, self.k, self.v, w.cap, self.vl, self.idxs[r], 1, w.width,
-                       self.bias, self.y, fused_validate=True)
+        c.capacity_step(self.qs[r], w.batch, w.q_seq, self.k, self.v, w.cap, self.cur_k, self.cur_v, w.cur,
+                        self.idxs[r], 1, w.width, self.bias, self.y, self.vl, self.wp, reset_error=True)
 
     def kernel_work(self):
         kw = Setup.kernel_work(self)
@@ -319,7 +317,8 @@ class CapacitySetup(Setup):
                             f"bf16 bias, {w.cur} current row, top-{w.topk}, "
                             f"{'graph replay' if use_graph else 'eager'}, {nset} rotating index sets",
                 "selected_tokens_per_step": tokens, "splits": self.splits,
-                "step_calls": "reset_error_async + capacity_lengths + kv_append + forward_bias",
+                "step_calls": "sparse_attn_capacity_step (reset, lengths + in-place append in one launch, "
+                              "validation, biased forward)",
                 "step_hbm_GBps": self.step_bytes() / (ms_per_step / 1e3) / 1e9}
 
     def oracle_inputs(self, b, r=0):

@@ -240,6 +240,28 @@ sa_status sparse_attn_capacity_lengths(sparse_attn_ctx* ctx, const void* bias, c
                                        int64_t cache_capacity, int64_t cur_len, int32_t* valid_len,
                                        int32_t* write_pos);
 
+/* One capacity-mode attention step over separate K and V caches kept in
+ * place (IndexShare's capacity branch: `capacity_write_pos`, the two
+ * `build_present_capacity` launches and the rows), the same as
+ *   [sparse_attn_reset_error_async if reset_error]
+ *   sparse_attn_capacity_lengths(bias, ..., cur_len, valid_len, write_pos)
+ *   sparse_attn_kv_append(past = present = cache, past_len = write_pos, cur)
+ *   sparse_attn_forward_bias(present = cache, valid_len, bias, fused_validate = 1)
+ *   cache_k, cache_v [B, Hkv, cache_capacity, D] read and written; cur_k,
+ *                    cur_v [B, Hkv, cur_len, D]; 1 <= cur_len <= cache_capacity
+ *   valid_len, write_pos  device int32 [B] outputs
+ * The lengths and the append are one launch when the rows are a multiple of
+ * 16 bytes and the four tensors 16-byte aligned (Dk == Dv). Host errors:
+ * those of the four calls, checked before anything is launched;
+ * SA_E_UNSUPPORTED for a shared-latent or fp8 cache. Asynchronous and
+ * capturable. */
+sa_status sparse_attn_capacity_step(sparse_attn_ctx* ctx, const void* q, int64_t batch, int64_t q_seq,
+                                    void* cache_k, void* cache_v, int64_t cache_capacity, const void* cur_k,
+                                    const void* cur_v, int64_t cur_len, const void* indices,
+                                    int64_t index_heads, int64_t width, const void* bias,
+                                    const int64_t* bias_shape, int32_t bias_rank, void* y,
+                                    int32_t* valid_len, int32_t* write_pos, int32_t reset_error);
+
 /* One attention step over a shared-latent cache kept in place (capacity
  * mode): the same as
  *   [sparse_attn_reset_error_async if reset_error]

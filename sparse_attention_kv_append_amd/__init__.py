@@ -37,7 +37,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_DTYPE", 4: 
 EXPORTS = [
     "sparse_attn_create", "sparse_attn_destroy", "sparse_attn_set_stream",
     "sparse_attn_kv_append", "sparse_attn_validate_indices", "sparse_attn_forward", "sparse_attn_step",
-    "sparse_attn_forward_bias", "sparse_attn_capacity_lengths",
+    "sparse_attn_forward_bias", "sparse_attn_capacity_lengths", "sparse_attn_capacity_step",
     "sparse_attn_csa_forward", "sparse_attn_csa_index_select", "sparse_attn_csa_index_workspace_bytes",
     "sparse_attn_reset_error_async", "sparse_attn_read_error", "sparse_attn_last_error",
     "sparse_attn_query_plan", "sparse_attn_profile_enable", "sparse_attn_profile_read",
@@ -93,6 +93,8 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
         "sparse_attn_forward": ([V, V, I64, I64, V, V, I64, V, V, I64, I64, V, I32], st),
         "sparse_attn_forward_bias": ([V, V, I64, I64, V, V, I64, V, V, I64, I64, V, V, I32, V, I32], st),
         "sparse_attn_capacity_lengths": ([V, V, V, I32, I64, I64, I64, I64, V, V], st),
+        "sparse_attn_capacity_step": ([V, V, I64, I64, V, V, I64, V, V, I64, V, I64, I64, V, V, I32, V, V, V, I32],
+                                      st),
         "sparse_attn_step": ([V, V, I64, I64, V, I64, V, V, I64, I32, V, V, I64, I64, V, I32], st),
         "sparse_attn_csa_forward": ([V, V, I64, I64, I64, V, I64, V, I64, V, I64, I64, V, V, V, V,
                                      ctypes.c_float, V], st),
@@ -218,6 +220,19 @@ class Context:
         self._check(self.lib.sparse_attn_capacity_lengths(
             self.handle, _ptr(bias), shape, len(dims), batch, q_seq, cache_capacity, cur_len,
             _ptr(valid_len), _ptr(write_pos)))
+
+    def capacity_step(self, q, batch, q_seq, cache_k, cache_v, cache_capacity, cur_k, cur_v, cur_len, indices,
+                      index_heads, width, bias, y, valid_len, write_pos, reset_error=True):
+        """Capacity-mode step over separate K/V caches: lengths from the bias,
+        in-place append at the write position, biased forward with fused
+        validation."""
+        self._sync_stream()
+        dims = [int(d) for d in bias.shape]
+        shape = (ctypes.c_int64 * max(4, len(dims)))(*dims)
+        self._check(self.lib.sparse_attn_capacity_step(
+            self.handle, _ptr(q), batch, q_seq, _ptr(cache_k), _ptr(cache_v), cache_capacity, _ptr(cur_k),
+            _ptr(cur_v), cur_len, _ptr(indices), index_heads, width, _ptr(bias), shape, len(dims), _ptr(y),
+            _ptr(valid_len), _ptr(write_pos), int(reset_error)))
 
     def step(self, q, batch, q_seq, cache, cache_capacity, past_len, cur, cur_len, present_len, indices,
              index_heads, width, y, reset_error=True, cur_is_unquantized_bf16=False):

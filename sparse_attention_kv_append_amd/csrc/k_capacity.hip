@@ -47,16 +47,14 @@ __device__ __forceinline__ int vec_best(uint4 v, int64_t e0, int64_t bd3, int64_
   return bd3 == 1 ? (int)keys : (int)(e0 % bd3) + last + 1;
 }
 
+// 1 + the largest finite column of batch entry b's bias slice, reduced over
+// the workgroup (every thread returns it)
 template <int DT, bool VEC>
-__global__ void __launch_bounds__(kCapThreads)
-capacity_lengths_kernel(const void* __restrict__ bias, int64_t bd0, int64_t bd1, int64_t bd2, int64_t bd3,
-                        int64_t keys, int64_t cur_len, int32_t* __restrict__ valid_len,
-                        int32_t* __restrict__ write_pos) {
-  __shared__ int best_s;
-  const int64_t b = blockIdx.x;
+__device__ __forceinline__ int capacity_scan(const void* __restrict__ bias, int64_t b, int64_t bd0, int64_t bd1,
+                                             int64_t bd2, int64_t bd3, int64_t keys, int* best_s) {
   const int64_t n = bd1 * bd2 * bd3;  // elements of one batch entry's slice
   const int64_t base = (bd0 == 1 ? 0 : b) * n;
-  if (threadIdx.x == 0) best_s = 0;
+  if (threadIdx.x == 0) *best_s = 0;
   __syncthreads();
   int best = 0;  // 1 + largest finite column seen by this thread
   if constexpr (VEC) {
@@ -85,12 +83,56 @@ capacity_lengths_kernel(const void* __restrict__ bias, int64_t bd0, int64_t bd1,
     }
   }
   best = wave_max_nonneg(best);
-  if ((threadIdx.x & 63) == 0) atomicMax(&best_s, best);
+  if ((threadIdx.x & 63) == 0) atomicMax(best_s, best);
   __syncthreads();
+  return *best_s;
+}
+
+template <int DT, bool VEC>
+__global__ void __launch_bounds__(kCapThreads)
+capacity_lengths_kernel(const void* __restrict__ bias, int64_t bd0, int64_t bd1, int64_t bd2, int64_t bd3,
+                        int64_t keys, int64_t cur_len, int32_t* __restrict__ valid_len,
+                        int32_t* __restrict__ write_pos) {
+  __shared__ int best_s;
+  const int64_t b = blockIdx.x;
+  const int v = capacity_scan<DT, VEC>(bias, b, bd0, bd1, bd2, bd3, keys, &best_s);
   if (threadIdx.x == 0) {
-    const int v = best_s;
     valid_len[b] = v;
     write_pos[b] = v >= cur_len ? (int32_t)(v - cur_len) : 0;
+  }
+}
+
+// The lengths, then this batch entry's current K and V rows written in place
+// at the write position (IndexShare's `capacity_write_pos` followed by its
+// two `build_present_capacity` launches, as one): rows of `row_bytes`, a
+// multiple of 16, for every kv head.
+template <int DT, bool VEC>
+__global__ void __launch_bounds__(kCapThreads)
+capacity_append_kernel(const void* __restrict__ bias, int64_t bd0, int64_t bd1, int64_t bd2, int64_t bd3,
+                       int64_t keys, int64_t cur_len, int32_t* __restrict__ valid_len,
+                       int32_t* __restrict__ write_pos, const uint4* __restrict__ cur_k,
+                       const uint4* __restrict__ cur_v, uint4* __restrict__ cache_k, uint4* __restrict__ cache_v,
+                       int64_t heads, int64_t row_bytes) {
+  __shared__ int best_s;
+  const int64_t b = blockIdx.x;
+  const int v = capacity_scan<DT, VEC>(bias, b, bd0, bd1, bd2, bd3, keys, &best_s);
+  const int64_t wp = v >= cur_len ? (int64_t)v - cur_len : 0;  // wp + cur_len <= keys
+  if (threadIdx.x == 0) {
+    valid_len[b] = v;
+    write_pos[b] = (int32_t)wp;
+  }
+  const int64_t ru = row_bytes / 16;     // 16-byte units per row
+  const int64_t per = heads * cur_len * ru;  // units of one tensor for this batch entry
+  for (int64_t u = threadIdx.x; u < 2 * per; u += kCapThreads) {
+    const bool second = u >= per;
+    const int64_t e = second ? u - per : u;
+    const int64_t h = e / (cur_len * ru);
+    const int64_t rem = e - h * cur_len * ru;  // (row t, unit) of the current rows
+    const int64_t t = rem / ru, k = rem - t * ru;
+    const int64_t src = ((b * heads + h) * cur_len + t) * ru + k;
+    const int64_t dst = ((b * heads + h) * keys + wp + t) * ru + k;
+    if (second) cache_v[dst] = cur_v[src];
+    else cache_k[dst] = cur_k[src];
   }
 }
 
@@ -116,6 +158,35 @@ sa_status launch_capacity_lengths(sparse_attn_ctx* c, const void* bias, int dtyp
 #undef SA_CAP_V
 #undef SA_CAP
   return check_hip(c, hipGetLastError(), "capacity_lengths");
+}
+
+}  // namespace sa
+
+namespace sa {
+
+sa_status launch_capacity_append(sparse_attn_ctx* c, const void* bias, int dtype, const int64_t* bd, int64_t batch,
+                                 int64_t keys, int64_t cur_len, int32_t* valid_len, int32_t* write_pos,
+                                 const void* cur_k, const void* cur_v, void* cache_k, void* cache_v, int64_t heads,
+                                 int64_t row_bytes) {
+  const dim3 grid((unsigned)batch), block(kCapThreads);
+  const int per = dtype == SA_F32 ? 4 : 8;
+  const bool vec = bd[3] % per == 0 && ((uintptr_t)bias & 15) == 0;
+#define SA_CAPA(DT, V)                                                                                      \
+  hipLaunchKernelGGL((capacity_append_kernel<DT, V>), grid, block, 0, c->stream, bias, bd[0], bd[1], bd[2], \
+                     bd[3], keys, cur_len, valid_len, write_pos, (const uint4*)cur_k, (const uint4*)cur_v,   \
+                     (uint4*)cache_k, (uint4*)cache_v, heads, row_bytes)
+#define SA_CAPA_V(DT) \
+  if (vec) { SA_CAPA(DT, true); } else { SA_CAPA(DT, false); }
+  if (dtype == SA_F32) {
+    SA_CAPA_V(SA_F32);
+  } else if (dtype == SA_F16) {
+    SA_CAPA_V(SA_F16);
+  } else {
+    SA_CAPA_V(SA_BF16);
+  }
+#undef SA_CAPA_V
+#undef SA_CAPA
+  return check_hip(c, hipGetLastError(), "capacity append");
 }
 
 }  // namespace sa

@@ -451,6 +451,57 @@ sa_status sparse_attn_capacity_lengths(sparse_attn_ctx* c, const void* bias, con
   return sa::launch_capacity_lengths(c, bias, k.dtype, bd, batch, cache_capacity, cur_len, valid_len, write_pos);
 }
 
+sa_status sparse_attn_capacity_step(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq, void* cache_k,
+                                    void* cache_v, int64_t cache_capacity, const void* cur_k, const void* cur_v,
+                                    int64_t cur_len, const void* indices, int64_t index_heads, int64_t width,
+                                    const void* bias, const int64_t* bias_shape, int32_t bias_rank, void* y,
+                                    int32_t* valid_len, int32_t* write_pos, int32_t reset_error) {
+  if (!live(c)) return SA_E_STATE;
+  const sa_config& k = c->cfg;
+  c->last_error.clear();
+  if (k.kv_layout != SA_KV_SEPARATE || k.cache_format != SA_CACHE_DENSE)
+    return set_error(c, SA_E_UNSUPPORTED, "capacity_step: needs separate dense K and V caches");
+  if (!cache_k || !cache_v || !cur_k || !cur_v)
+    return set_error(c, SA_E_ARG, "capacity_step: cache_k, cache_v, cur_k and cur_v are required");
+  if (cur_len <= 0 || cur_len > cache_capacity)
+    return set_error(c, SA_E_CAPACITY, "capacity_step: cur_len must be in [1, cache_capacity]");
+  if (cache_capacity > k.max_cache_len)
+    return set_error(c, SA_E_STATE, fmt("capacity_step: cache capacity %lld above max_cache_len %lld", cache_capacity,
+                                        k.max_cache_len));
+  // argument checks of the three calls, before anything is launched
+  sa_status s = check_index_geometry(c, batch, index_heads, q_seq, width);
+  if (s != SA_OK) return s;
+  if (!q || !indices || !y) return set_error(c, SA_E_ARG, "capacity_step: q, indices and y are required");
+  if (!bias)
+    return set_error(c, SA_E_ARG,
+                     "capacity_step: capacity-mode IndexShare requires attention_bias to derive the valid length");
+  if (!valid_len || !write_pos) return set_error(c, SA_E_ARG, "capacity_step: valid_len and write_pos are required");
+  if (cache_capacity > 0x7fffffffLL) return set_error(c, SA_E_ARG, "capacity_step: cache capacity must be below 2^31");
+  const int64_t target[4] = {batch, k.num_heads, q_seq, cache_capacity};
+  int64_t bd[4];
+  s = bias_dims(c, "capacity_step", bias_shape, bias_rank, target, bd);
+  if (s != SA_OK) return s;
+  if (reset_error) {
+    s = sa::launch_reset_error(c);
+    if (s != SA_OK) return s;
+  }
+  const int64_t row = k.head_dim_qk * elem_bytes(k.dtype);
+  const uintptr_t mis = (uintptr_t)cache_k | (uintptr_t)cache_v | (uintptr_t)cur_k | (uintptr_t)cur_v;
+  if (k.head_dim_v == k.head_dim_qk && row % 16 == 0 && (mis & 15) == 0) {
+    // lengths and the in-place append in one launch
+    s = sa::launch_capacity_append(c, bias, k.dtype, bd, batch, cache_capacity, cur_len, valid_len, write_pos, cur_k,
+                                   cur_v, cache_k, cache_v, k.kv_num_heads, row);
+  } else {
+    s = sa::launch_capacity_lengths(c, bias, k.dtype, bd, batch, cache_capacity, cur_len, valid_len, write_pos);
+    if (s == SA_OK)
+      s = sparse_attn_kv_append(c, batch, cache_k, cache_v, cache_capacity, write_pos, cur_k, cur_v, cur_len, 0,
+                                cache_k, cache_v, cache_capacity, nullptr);
+  }
+  if (s != SA_OK) return s;
+  return forward_impl(c, q, batch, q_seq, cache_k, cache_v, cache_capacity, valid_len, indices, index_heads, width, y,
+                      1, nullptr, bias, bd);
+}
+
 sa_status sparse_attn_step(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq, void* cache,
                            int64_t cache_capacity, const int32_t* past_len, const void* cur, int64_t cur_len,
                            int32_t cur_is_unquantized_bf16, int32_t* present_len, const void* indices,

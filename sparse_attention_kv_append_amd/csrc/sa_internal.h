@@ -180,6 +180,12 @@ sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a);
 sa_status launch_capacity_lengths(sparse_attn_ctx* c, const void* bias, int dtype, const int64_t* bd,
                                   int64_t batch, int64_t keys, int64_t cur_len, int32_t* valid_len,
                                   int32_t* write_pos);
+// the same, then each batch entry's current K and V rows (row_bytes, a
+// multiple of 16; 16-byte aligned tensors) written in place at its write position
+sa_status launch_capacity_append(sparse_attn_ctx* c, const void* bias, int dtype, const int64_t* bd, int64_t batch,
+                                 int64_t keys, int64_t cur_len, int32_t* valid_len, int32_t* write_pos,
+                                 const void* cur_k, const void* cur_v, void* cache_k, void* cache_v, int64_t heads,
+                                 int64_t row_bytes);
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
 sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                                 const AppendArgs* app = nullptr);

@@ -77,6 +77,8 @@ def test_null_and_unknown_context_rejected_without_launch():
     assert lib.sparse_attn_forward_bias(None, None, 1, 1, None, None, 1, None, None, 1, 1, None, None, 0,
                                         None, 0) == sa.SA_E_STATE
     assert lib.sparse_attn_capacity_lengths(None, None, None, 0, 1, 1, 1, 1, None, None) == sa.SA_E_STATE
+    assert lib.sparse_attn_capacity_step(None, None, 1, 1, None, None, 1, None, None, 1, None, 1, 1, None, None, 0,
+                                         None, None, None, 1) == sa.SA_E_STATE
     fake = ctypes.c_void_p(0x1234)
     assert lib.sparse_attn_capacity_lengths(fake, None, None, 0, 1, 1, 1, 1, None, None) == sa.SA_E_STATE
     assert lib.sparse_attn_forward(fake, None, 1, 1, None, None, 1, None, None, 1, 1, None, 0) == sa.SA_E_STATE

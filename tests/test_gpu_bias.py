@@ -150,6 +150,20 @@ def test_bias_host_errors():
     assert e.value.status == sa.SA_E_SHAPE
     assert ctx.lib.sparse_attn_capacity_lengths(ctx.handle, None, None, 0, w.batch, w.q_seq, w.cap, 1,
                                                 vl.data_ptr(), vl.data_ptr()) == sa.SA_E_ARG
+    cur = torch.zeros((w.batch, w.hkv, 1, w.dk), device=dev)
+    for bad_bias, cur_len, status in [(torch.zeros((1, 1, 1, 1, 1), device=dev), 1, sa.SA_E_SHAPE),
+                                      (torch.zeros((w.cap,), device=dev), 0, sa.SA_E_CAPACITY),
+                                      (torch.zeros((w.cap,), device=dev), w.cap + 1, sa.SA_E_CAPACITY)]:
+        with pytest.raises(sa.SparseAttnError) as e:
+            ctx.capacity_step(q, w.batch, w.q_seq, k, k.clone(), w.cap, cur, cur, cur_len, idx, 1, w.width,
+                              bad_bias, y, vl, vl)
+        assert e.value.status == status
+    ctx.destroy()
+    wl = W.WORKLOADS["decode_bf16"].scaled(batch=1, past=10, width=8, topk=8)
+    ctx = make_ctx(wl)  # a shared-latent cache: no capacity step over it
+    with pytest.raises(sa.SparseAttnError) as e:
+        ctx.capacity_step(q, 1, 1, k, k, w.cap, cur, cur, 1, idx, 1, 8, torch.zeros((w.cap,), device=dev), y, vl, vl)
+    assert e.value.status == sa.SA_E_UNSUPPORTED
     ctx.destroy()
 
 
@@ -197,7 +211,7 @@ def capacity_oracle(w, inp):
     return valid, wpos, pk, pv
 
 
-def capacity_device(w, inp, ctx=None):
+def capacity_device(w, inp, ctx=None, one_call=False):
     """capacity_lengths -> in-place kv_append at write_pos -> forward_bias with
     fused validation against valid_len, all on the context's stream."""
     import torch
@@ -209,11 +223,15 @@ def capacity_device(w, inp, ctx=None):
     vl = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
     wp = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
     y = torch.full((w.batch, w.hq, w.q_seq, w.dv), float("nan"), dtype=y_dtype(w), device="cuda")
-    ctx.reset_error_async()
-    ctx.capacity_lengths(bias, w.batch, w.q_seq, w.cap, w.cur, vl, wp)
-    ctx.kv_append(w.batch, kc, vc, w.cap, wp, tt(inp["cur_k"]), tt(inp["cur_v"]), w.cur, kc, vc, w.cap)
-    ctx.forward_bias(tt(inp["q"]), w.batch, w.q_seq, kc, vc, w.cap, vl, tt(inp["indices"]), 1, w.width, bias, y,
-                     fused_validate=True)
+    if one_call:
+        ctx.capacity_step(tt(inp["q"]), w.batch, w.q_seq, kc, vc, w.cap, tt(inp["cur_k"]), tt(inp["cur_v"]), w.cur,
+                          tt(inp["indices"]), 1, w.width, bias, y, vl, wp, reset_error=True)
+    else:
+        ctx.reset_error_async()
+        ctx.capacity_lengths(bias, w.batch, w.q_seq, w.cap, w.cur, vl, wp)
+        ctx.kv_append(w.batch, kc, vc, w.cap, wp, tt(inp["cur_k"]), tt(inp["cur_v"]), w.cur, kc, vc, w.cap)
+        ctx.forward_bias(tt(inp["q"]), w.batch, w.q_seq, kc, vc, w.cap, vl, tt(inp["indices"]), 1, w.width, bias, y,
+                         fused_validate=True)
     word, _, msg = ctx.read_error()
     out = dict(valid=to_np(vl), wpos=to_np(wp), k=to_np(kc), v=to_np(vc), y=y_as_f32(y), word=word, msg=msg)
     if own:
@@ -226,14 +244,16 @@ def capacity_device(w, inp, ctx=None):
                                 # bf16 with 128 dims: the grouped-query kernel
                                 dict(dtype=W.DT_BF16, dk=128, dv=128, q_seq=1, cur=1, seed=11),
                                 dict(dtype=W.DT_BF16, dk=128, dv=128, hq=16, hkv=2, seed=12)])
-def test_capacity_step_matches_oracle(kw):
+@pytest.mark.parametrize("one_call", [False, True])
+def test_capacity_step_matches_oracle(kw, one_call):
+    """The capacity step as four calls and as sparse_attn_capacity_step."""
     w = W.CAPACITY_WORKLOADS["capacity_small"].scaled(**kw)
     inp = W.make_capacity_numpy(w)
-    banner(f"capacity step {w.name} {kw}")
+    banner(f"capacity step {w.name} {kw} one_call={one_call}")
     valid, wpos, pk, pv = capacity_oracle(w, inp)
     ref = oracle.forward(inp["q"], pk, pv, inp["indices"], q_dtype=w.dtype, cache_fmt=w.dtype,
                          kv_layout=w.layout, hkv=w.hkv, dv=w.dv, scale=w.scale, bias=inp["bias"], threads=8)
-    d = capacity_device(w, inp)
+    d = capacity_device(w, inp, one_call=one_call)
     assert d["word"] == 0, d["msg"]
     np.testing.assert_array_equal(d["valid"], valid)
     np.testing.assert_array_equal(d["wpos"], wpos)
