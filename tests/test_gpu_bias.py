@@ -243,7 +243,9 @@ def capacity_device(w, inp, ctx=None, one_call=False):
                                 dict(batch=2, hq=4, hkv=4, q_seq=4, cur=4, width=300, topk=300, seed=10),
                                 # bf16 with 128 dims: the grouped-query kernel
                                 dict(dtype=W.DT_BF16, dk=128, dv=128, q_seq=1, cur=1, seed=11),
-                                dict(dtype=W.DT_BF16, dk=128, dv=128, hq=16, hkv=2, seed=12)])
+                                dict(dtype=W.DT_BF16, dk=128, dv=128, hq=16, hkv=2, seed=12),
+                                # rows not a multiple of 16 bytes: the one-call step takes the two launches
+                                dict(dk=66, dv=66, seed=13), dict(dtype=W.DT_BF16, dk=72, dv=72, seed=14)])
 @pytest.mark.parametrize("one_call", [False, True])
 def test_capacity_step_matches_oracle(kw, one_call):
     """The capacity step as four calls and as sparse_attn_capacity_step."""
