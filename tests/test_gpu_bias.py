@@ -113,18 +113,21 @@ def test_forward_bias_none_is_the_plain_forward():
     check_close(y, ref, w.dtype, "no bias")
 
 
-def test_forward_bias_masked_rows_give_zeros():
-    w = CASES["grouped_bf16_per_head"]
+@pytest.mark.parametrize("name", ["grouped_bf16_per_head", "gqa_uniform_decode", "gqa_causal_softcap"])
+def test_forward_bias_masked_rows_give_zeros(name):
+    """Rows whose every key is masked give zeros (generic kernel; grouped-query
+    kernel with and without split-KV)."""
+    w = CASES[name]
     inp = W.make_numpy(w)
     b32 = np.zeros((w.batch, w.hq, w.q_seq, 1), np.float32)
-    b32[1, 3, 2] = -np.inf
+    b32[1, 3, w.q_seq - 1] = -np.inf
     b32[0, :, 0] = -np.inf
     bias = bias_store(b32, w.dtype)
     ref = oracle_bias(w, inp, bias)
-    assert not ref[1, 3, 2].any() and not ref[0, :, 0].any()
+    assert not ref[1, 3, w.q_seq - 1].any() and not ref[0, :, 0].any()
     y, word, msg = run_bias(w, inp, bias)
     assert word == 0, msg
-    assert not y[1, 3, 2].any() and not y[0, :, 0].any()
+    assert not y[1, 3, w.q_seq - 1].any() and not y[0, :, 0].any()
     check_close(y, ref, w.dtype, "masked rows")
 
 
