@@ -293,3 +293,42 @@ def test_capacity_decode_fullsize_sampled_rows():
         np.testing.assert_array_equal(kb.view(np.uint16), inp["cur_k"])
         check_close(y[b:b + 1], ref, w.dtype, f"batch entry {b}")
     s.ctx.destroy()
+
+
+def test_capacity_step_graph_replays_match_eager():
+    """sparse_attn_capacity_step captured in a HIP graph (lengths + append
+    launch, validation, grouped-query forward with bias and split-KV, combine):
+    every replay, with eager work between them, equals the eager call."""
+    import torch
+    w = W.CAPACITY_WORKLOADS["capacity_small"].scaled(dtype=W.DT_BF16, dk=128, dv=128, q_seq=1, cur=1,
+                                                      capacity=2000, width=600, topk=560, seed=21,
+                                                      extra={"valid_lo": 900})
+    inp = W.make_capacity_numpy(w)
+    ctx = make_ctx(w)
+    path, splits = ctx.query_plan(w.batch, w.q_seq, 1, w.width)
+    banner(f"capacity step graph: path {path} splits {splits}")
+    assert path == 4 and splits > 1
+    e = capacity_device(w, inp, ctx=ctx, one_call=True)
+    assert e["word"] == 0, e["msg"]
+    k0, v0 = tt(inp["past_k"]), tt(inp["past_v"])
+    kc, vc = k0.clone(), v0.clone()
+    q, ck, cv, ix, bias = tt(inp["q"]), tt(inp["cur_k"]), tt(inp["cur_v"]), tt(inp["indices"]), tt(inp["bias"])
+    vl = torch.zeros((w.batch,), dtype=torch.int32, device="cuda")
+    wp = torch.zeros_like(vl)
+    y = torch.zeros((w.batch, w.hq, w.q_seq, w.dv), dtype=torch.bfloat16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ctx.capacity_step(q, w.batch, w.q_seq, kc, vc, w.cap, ck, cv, w.cur, ix, 1, w.width, bias, y, vl, wp,
+                          reset_error=True)
+    for rep in range(3):
+        y.zero_()
+        kc.copy_(k0)  # eager work between replays
+        vc.copy_(v0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y_as_f32(y), e["y"]), rep
+        assert np.array_equal(to_np(vl), e["valid"]) and np.array_equal(to_np(wp), e["wpos"])
+        assert np.array_equal(raw_bytes(to_np(kc)), raw_bytes(e["k"])) and np.array_equal(raw_bytes(to_np(vc)),
+                                                                                         raw_bytes(e["v"]))
+        assert ctx.read_error()[0] == 0
+    ctx.destroy()
