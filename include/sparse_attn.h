@@ -107,14 +107,24 @@ typedef struct {
   int64_t max_cache_len;  /* largest cache capacity (rows per (batch, kv head))         */
 } sa_config;
 
-/* Create a context: checks the config, allocates the device error word and
- * the split-K partial buffers sized from the max_* fields (stable addresses
- * for the context's lifetime). hip_stream may be NULL (the null stream).
- * Returns SA_E_ARG / SA_E_DTYPE / SA_E_UNSUPPORTED for a bad config. */
+/* Create a context: checks the config against the operator's attribute rules
+ * (IndexShare page, kernel `create`: num_heads and kv_num_heads positive,
+ * scale finite and > 0 when given; `launch_rows` takes an absent scale as
+ * 1/sqrt(head size), here scale 0; head sizes as `validate_shapes` requires
+ * them, with the shared-latent and fp8_e4m3_block64 forms of the CSA CPU
+ * page's `CacheFormat`), then allocates the device error word and the split-K
+ * partial buffers sized from the max_* fields (IndexShare `ensure_scratch`:
+ * buffers sized once, at addresses that stay fixed so a captured graph can
+ * keep them). hip_stream may be NULL (the null stream).
+ * Returns SA_E_ARG / SA_E_DTYPE / SA_E_SHAPE / SA_E_UNSUPPORTED for a bad
+ * config (nothing allocated), SA_E_HIP if an allocation fails (everything
+ * already allocated is released). *out is NULL on failure. */
 sa_status sparse_attn_create(const sa_config* cfg, void* hip_stream, sparse_attn_ctx** out);
 
-/* Release the context's device buffers after draining its stream. NULL is
- * accepted and ignored. */
+/* Release the context's device buffers after draining its stream (IndexShare
+ * page, the kernel's `drop`: its scratch lives exactly as long as the
+ * operator instance). NULL is accepted and ignored; a
+ * pointer that is not a live context returns SA_E_STATE and frees nothing. */
 sa_status sparse_attn_destroy(sparse_attn_ctx* ctx);
 
 /* Change the stream later calls are launched on. */
@@ -131,14 +141,16 @@ sa_status sparse_attn_set_stream(sparse_attn_ctx* ctx, void* hip_stream);
  *   present_k/present_v [B, Hkv, present_capacity, row]
  * `row` is Dk (K) / Dv (V) elements of the config dtype, or one fp8 record.
  * present == past is the in-place capacity mode: only the cur_len new rows
- * are written. present != past is concat mode: past rows are copied too.
+ * are written, and past_capacity must equal present_capacity (one row stride;
+ * SA_E_ARG otherwise). present != past is concat mode: past rows are copied too.
  * SHARED_LATENT: pass past_v, cur_v and present_v as NULL.
  * cur_is_unquantized_bf16 (fp8 caches only): cur_k is bf16 [B, Hkv, cur_len, Dk]
  * and each new row is quantized on the device into a record (block scale
  * floor(log2 amax) - 8 + 127, E4M3FN nearest-even saturating at 448; the CSA
  * CPU page's `finalize_attention_record` pack loop); otherwise cur_k holds
  * records and the append is a byte copy.
- * present_len: optional device int32 [B] output, past_len[b] + cur_len.
+ * present_len: optional device int32 [B] output, past_len[b] + cur_len
+ * (written for cur_len == 0 too).
  * Host errors: SA_E_CAPACITY when past_len is NULL and
  * past_capacity + cur_len > present_capacity. Device errors:
  * SA_ERR_APPEND_CAPACITY, SA_ERR_QUANT_NONFINITE.
@@ -285,7 +297,11 @@ sa_status sparse_attn_capacity_step(sparse_attn_ctx* ctx, const void* q, int64_t
  * they latch them (a capacity failure appends nothing and sets
  * SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY; a non-finite bf16 row is left
  * unwritten and sets SA_ERR_QUANT_NONFINITE | SA_ERR_APPEND_ANY).
- * SA_E_UNSUPPORTED for separate K/V caches. Asynchronous and capturable. */
+ * SA_E_UNSUPPORTED for separate K/V caches. Every host check of the three
+ * calls (including the index geometry and the q / indices / y pointers) is
+ * made before the reset or the append is launched, so a rejected step leaves
+ * the cache, present_len and the error word as they were. Asynchronous and
+ * capturable. */
 sa_status sparse_attn_step(sparse_attn_ctx* ctx, const void* q, int64_t batch, int64_t q_seq, void* cache,
                            int64_t cache_capacity, const int32_t* past_len, const void* cur,
                            int64_t cur_len, int32_t cur_is_unquantized_bf16, int32_t* present_len,
@@ -385,7 +401,11 @@ sa_status sparse_attn_csa_forward(sparse_attn_ctx* ctx, const float* query, int6
                                   float* y);
 
 /* Zero the context's error word and set first_bad to UINT64_MAX, with a tiny
- * kernel on the stream (no memset node, so it is safe inside a graph). */
+ * kernel on the stream (no memset node, so it is safe inside a graph). This is
+ * the reset of IndexShare's capture-error word (page module doc on capture:
+ * `validate_index_rows` latches INDEX_SHARE_CAPTURE_ERROR_INDEX into a
+ * persistent word that the host reads outside the captured region).
+ * SA_E_STATE for a dead context; otherwise only a launch failure (SA_E_HIP). */
 sa_status sparse_attn_reset_error_async(sparse_attn_ctx* ctx);
 
 /* Synchronise the stream and copy the context's error word and first_bad slot

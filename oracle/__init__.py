@@ -65,6 +65,8 @@ def _load():
         P, I64, U8P = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint8)
         lib.oracle_bf16_from_f32.argtypes = [ctypes.c_float]
         lib.oracle_bf16_from_f32.restype = ctypes.c_uint16
+        lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f32.restype = ctypes.c_float
         lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
         lib.oracle_e8m0_value.restype = ctypes.c_double
         lib.oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
@@ -129,6 +131,17 @@ def bf16_bits(x) -> np.ndarray:
 def bf16_round_f32(x) -> np.ndarray:
     """fp32 values rounded to bf16 (nearest-even) and widened back."""
     return (bf16_bits(x).astype(np.uint32) << 16).view(np.float32)
+
+
+def f16_to_f32(bits) -> np.ndarray:
+    """IEEE binary16 bit patterns -> fp32 values (the oracle's widening of f16 inputs)."""
+    lib = _load()
+    b = np.asarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    flat_in, flat_out = b.reshape(-1), out.reshape(-1)
+    for i in range(flat_in.size):
+        flat_out[i] = lib.oracle_f16_to_f32(int(flat_in[i]))
+    return out
 
 
 def e4m3fn_value(code: int) -> float:

@@ -83,6 +83,9 @@ static float or_f16_to_f32(uint16_t h) {
   return (float)(sign ? -v : v);
 }
 
+/* The same widening, exported so that tests can check it over every bit pattern. */
+float oracle_f16_to_f32(uint16_t h) { return or_f16_to_f32(h); }
+
 /* fp32 -> bf16 round to nearest, ties to even; NaN stays a quiet NaN. */
 uint16_t oracle_bf16_from_f32(float x) {
   uint32_t w;

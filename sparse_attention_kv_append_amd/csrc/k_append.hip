@@ -160,8 +160,11 @@ sa_status launch_append_quantize(sparse_attn_ctx* c, int64_t batch, int64_t head
                                  const int32_t* past_len, int64_t past_cap, void* present,
                                  int64_t present_cap, int32_t* present_len) {
   const int64_t rows = batch * heads * cur_len;
-  if (rows <= 0) return SA_OK;
   const int64_t rec = (dk - rope) / 64 * 65 + 2 * rope;
+  // no current rows: present_len (and the capacity check) as the copy path does
+  if (rows <= 0)
+    return launch_append_copy(c, batch, heads, rec, nullptr, past_cap, past_len, nullptr, 0, present, present_cap,
+                              false, present_len);
   const int64_t blocks = (rows + 3) / 4;
   if (blocks > 0x7fffffffLL) return set_error(c, SA_E_SHAPE, "kv_append: too many rows");
   hipLaunchKernelGGL(append_quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, c->stream,

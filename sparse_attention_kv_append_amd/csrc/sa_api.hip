@@ -233,6 +233,12 @@ sa_status sparse_attn_kv_append(sparse_attn_ctx* c, int64_t batch, const void* p
                          past_capacity, cur_len, present_capacity));
   if (cur_len > present_capacity)
     return set_error(c, SA_E_CAPACITY, "kv_append: current rows exceed present capacity");
+  // in place (present aliases past): both views must use the one row stride
+  if (past_capacity > 0 && past_capacity != present_capacity &&
+      (present_k == past_k || (!latent && present_v == past_v)))
+    return set_error(c, SA_E_ARG,
+                     fmt("kv_append: in place (present aliases past) needs past_capacity %lld == present_capacity %lld",
+                         past_capacity, present_capacity));
   const int64_t heads = k.kv_num_heads;
   const int64_t krow = fp8 ? record_bytes(k.head_dim_qk, k.rope_dim) : k.head_dim_qk * elem_bytes(k.dtype);
   const bool copy_past = past_capacity > 0 && present_k != past_k;
@@ -521,6 +527,10 @@ sa_status sparse_attn_step(sparse_attn_ctx* c, const void* q, int64_t batch, int
     return set_error(c, SA_E_CAPACITY, "step: current rows exceed the cache capacity");
   if (cur_is_unquantized_bf16 && k.cache_format != SA_CACHE_FP8_E4M3_BLOCK64)
     return set_error(c, SA_E_DTYPE, "step: cur_is_unquantized_bf16 needs an fp8_e4m3_block64 cache");
+  // the forward's argument checks too, before the reset or the append is launched
+  if (!q || !indices || !y) return set_error(c, SA_E_ARG, "step: q, indices and y are required");
+  sa_status gs = check_index_geometry(c, batch, index_heads, q_seq, width);
+  if (gs != SA_OK) return gs;
   const int path = sa::forward_path(k, index_heads);
   if ((path == 2 || path == 3) && cur_len <= sa::kFusedAppendRows) {
     sa::AppendArgs app;

@@ -243,3 +243,95 @@ def test_step_graph_replays_match_eager():
         assert torch.equal(c_g, c_eager) and torch.equal(prl, p_eager)
         assert ctx.read_error()[0] == 0
     ctx.destroy()
+
+
+@pytest.mark.parametrize("name", ["decode_split", "long_cur"])
+def test_rejected_step_launches_nothing(name):
+    """A step the host rejects (index heads neither 1 nor Hq, a NULL query, an
+    index width above the context's maximum) returns its status before the
+    reset or the append is launched: the cache bytes, present_len and an
+    earlier latched error word are all unchanged. long_cur takes the
+    three-call form of the step, decode_split the one-launch form."""
+    import torch
+    import sparse_attention_kv_append_amd as sa
+    w = CASES[name]
+    banner(f"rejected step {name}")
+    inp, idx, cache = setup(w)
+    ctx = make_ctx(w)
+    early = idx.copy()
+    r = early[-1, 0, -1]
+    r[1], r[2] = r[2], r[1]
+    ctx.reset_error_async()
+    ctx.validate_indices(tt(early), w.batch, 1, w.q_seq, w.width, valid_len=tt(inp["valid_len"]))
+    e_word, e_fb, e_msg = ctx.read_error()
+    assert e_word == (sa_bits("ORDER") | 512)
+    B = w.batch
+    c = cache.clone()
+    plen, cur, q, ix = tt(inp["past_len"]), tt(inp["cur_k"]), tt(inp["q"]), tt(idx)
+    prl = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    y = torch.zeros((B, w.hq, w.q_seq, w.dv), dtype=torch.bfloat16, device="cuda")
+    bad_calls = [
+        (sa.SA_E_SHAPE, dict(q=q, index_heads=2, width=w.width)),
+        (sa.SA_E_ARG, dict(q=None, index_heads=1, width=w.width)),
+        (sa.SA_E_STATE, dict(q=q, index_heads=1, width=w.width + 1)),
+    ]
+    for status, kw in bad_calls:
+        with pytest.raises(sa.SparseAttnError) as ei:
+            ctx.step(kw["q"], B, w.q_seq, c, w.cap, plen, cur, w.cur, prl, ix, kw["index_heads"], kw["width"], y,
+                     reset_error=True)
+        assert ei.value.status == status, (ei.value.status, kw)
+    torch.cuda.synchronize()
+    assert torch.equal(c, cache)
+    assert (prl == -7).all()
+    assert ctx.read_error() == (e_word, e_fb, e_msg)
+    ctx.destroy()
+
+
+def test_inplace_append_with_mismatched_capacity_is_rejected():
+    """In place (present aliases past) with past_capacity != present_capacity
+    would read the new layout at the wrong row stride: SA_E_ARG, nothing written."""
+    import torch
+    import sparse_attention_kv_append_amd as sa
+    w = CASES["decode_split"]
+    banner("in-place append capacity mismatch")
+    inp, idx, cache = setup(w)
+    ctx = make_ctx(w)
+    c = cache.clone()
+    prl = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
+    with pytest.raises(sa.SparseAttnError) as ei:
+        ctx.kv_append(w.batch, c, None, w.cap - 8, tt(inp["past_len"]), tt(inp["cur_k"]), None, w.cur, c, None,
+                      w.cap, present_len=prl)
+    assert ei.value.status == sa.SA_E_ARG
+    torch.cuda.synchronize()
+    assert torch.equal(c, cache) and (prl == -7).all()
+    # the same call with matching capacities appends
+    ctx.kv_append(w.batch, c, None, w.cap, tt(inp["past_len"]), tt(inp["cur_k"]), None, w.cur, c, None, w.cap,
+                  present_len=prl)
+    torch.cuda.synchronize()
+    assert torch.equal(prl, tt(inp["valid_len"]))
+    ctx.destroy()
+
+
+def test_quantize_append_of_no_rows_writes_present_len():
+    """fp8 quantize-on-append with cur_len == 0 still writes present_len
+    (= past_len) and checks the capacity, as the byte-copy append does."""
+    import torch
+    w = CASES["fp8_split"]
+    banner("fp8 quantize append of zero rows")
+    inp, idx, cache = setup(w)
+    ctx = make_ctx(w)
+    c = cache.clone()
+    prl = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
+    ctx.reset_error_async()
+    ctx.kv_append(w.batch, c, None, w.cap, tt(inp["past_len"]), tt(inp["cur_k"]), None, 0, c, None, w.cap,
+                  present_len=prl, cur_is_unquantized_bf16=True)
+    assert ctx.read_error()[0] == 0
+    assert torch.equal(prl, tt(inp["past_len"])) and torch.equal(c, cache)
+    # a past length beyond the capacity is latched, as on the copy path
+    pl = inp["past_len"].copy()
+    pl[1] = w.cap + 1
+    ctx.kv_append(w.batch, c, None, w.cap, tt(pl), tt(inp["cur_k"]), None, 0, c, None, w.cap,
+                  present_len=prl, cur_is_unquantized_bf16=True)
+    want = sa_bits("APPEND_CAPACITY") | sa_bits("APPEND_ANY")
+    assert ctx.read_error()[0] & want == want
+    ctx.destroy()

@@ -143,3 +143,84 @@ def test_record_layout_and_round_trip():
     assert np.array_equal(oracle.fp8_pack_rows(dec, rope), rec)
     # the decoded values are exactly representable in bf16 for these scales
     assert np.array_equal(oracle.bf16_round_f32(dec), dec)
+
+
+def test_f16_widening_every_bit_pattern():
+    """The f16 inputs' widening against numpy's IEEE binary16 type for all
+    65,536 bit patterns: subnormals (2^-24 step), normals, +-0, +-inf, NaN."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_to_f32(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))  # signed zeros too
+    # closed-form anchors of the format
+    assert ours[0x0001] == 2.0 ** -24 and ours[0x03FF] == 1023 * 2.0 ** -24
+    assert ours[0x0400] == 2.0 ** -14 and ours[0x3C00] == 1.0 and ours[0x7BFF] == 65504.0
+    assert ours[0xC000] == -2.0 and np.signbit(ours[0x8000]) and ours[0x8000] == 0.0
+
+
+# E4M3FN codes written out from the format: (E << 3) | M, value (1 + M/8) 2^(E-7)
+# for E >= 1 and M 2^-9 for E = 0. Each entry is an exact midpoint between two
+# neighbouring codes (or a value that must round to a signed zero) and the code
+# that round-to-nearest-even gives it.
+E4M3_MIDPOINTS = [
+    (1.0625, 0x38),          # between 1.0 (0x38, M=0) and 1.125 (0x39): even M=0
+    (1.1875, 0x3A),          # between 1.125 (0x39) and 1.25 (0x3A, M=2): even M=2
+    (-1.3125, 0xBA),         # between -1.25 (0xBA) and -1.375 (0xBB): even
+    (232.0, 0x76),           # between 224 (0x76, E=14 M=6) and 240 (0x77): even M=6
+    (248.0, 0x78),           # between 240 (0x77) and 256 (0x78, next binade): even M=0
+    (3.0 * 2.0 ** -10, 0x02),  # subnormal: between 1 (0x01) and 2 (0x02) x 2^-9
+    (5.0 * 2.0 ** -10, 0x02),  # between 2 (0x02) and 3 (0x03) x 2^-9
+    (15.0 * 2.0 ** -10, 0x08),  # between 7 x 2^-9 (0x07) and 2^-6 (0x08, smallest normal)
+    (2.0 ** -10, 0x00),      # between 0 and 2^-9: even code 0
+    (-(2.0 ** -10), 0x80),   # the same, negative: -0
+    (-(2.0 ** -11), 0x80),   # rounds to zero: keeps its sign
+    (-(2.0 ** -30), 0x80),
+]
+
+
+def test_quantizer_exact_midpoints_and_negative_zero():
+    """Round-to-nearest-even at exact E4M3FN midpoints and the sign of values
+    that round to zero. The block's maximum 300 fixes the scale byte at 127
+    (floor(log2 300) = 8), so the planted values are encoded unscaled. About
+    one bf16 value in 16 lands on such a midpoint, so the quantize-on-append
+    bytes depend on this rule."""
+    x = np.zeros(64, np.float32)
+    x[0] = 300.0
+    vals = [v for v, _ in E4M3_MIDPOINTS]
+    x[1:1 + len(vals)] = np.array(vals, np.float32)
+    assert np.array_equal(x[1:1 + len(vals)].astype(np.float64), np.array(vals))  # planted exactly
+    scale, codes = oracle.fp8_quantize_block64(x)
+    assert scale == 127
+    want = np.array([c for _, c in E4M3_MIDPOINTS], np.uint8)
+    assert np.array_equal(codes[1:1 + len(vals)], want), (codes[1:1 + len(vals)], want)
+    # the library's nearest-even cast agrees on every planted value
+    ref = torch.from_numpy(x.astype(np.float64)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    # the same midpoints under a non-trivial scale: maximum 300 * 2^-20 gives
+    # scale byte 107 and the block is divided exactly by 2^-20
+    y = (x.astype(np.float64) * 2.0 ** -20).astype(np.float32)
+    scale2, codes2 = oracle.fp8_quantize_block64(y)
+    assert scale2 == 107 and np.array_equal(codes2, codes)
+
+
+def test_quantizer_midpoints_of_every_binade_match_library():
+    """Every midpoint between neighbouring finite E4M3FN magnitudes (both signs)
+    rounds as the library's nearest-even cast does."""
+    mags = np.array(sorted({abs(oracle.e4m3fn_value(c)) for c in range(0x7F)}))
+    mids = (mags[:-1] + mags[1:]) / 2.0          # 126 exact midpoints, 0 .. 416
+    vals = np.concatenate([mids, -mids])
+    for start in range(0, len(vals), 63):
+        x = np.zeros(64, np.float32)
+        x[0] = 448.0                              # scale byte 127
+        chunk = vals[start:start + 63]
+        x[1:1 + len(chunk)] = chunk.astype(np.float32)
+        assert np.array_equal(x[1:1 + len(chunk)].astype(np.float64), chunk)
+        scale, codes = oracle.fp8_quantize_block64(x)
+        assert scale == 127
+        ref = torch.from_numpy(x.astype(np.float64)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes, ref)
+        # and the chosen code's mantissa is even (a tie never picks the odd neighbour)
+        sel = codes[1:1 + len(chunk)]
+        assert np.all((sel & 1) == 0), sel

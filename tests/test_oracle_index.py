@@ -207,3 +207,68 @@ def test_ties_nonfinite_and_geometry_flagged():
     assert flags & oracle.SEL_NONFINITE
     _, flags = oracle.csa_index_select(iq, iw, keys, 0, 5)
     assert flags == oracle.SEL_GEOMETRY
+
+
+def test_index_query_bf16_rounding_after_the_hadamard_scale_decides_a_code():
+    """A hand-worked query where the bf16 rounding that follows the 1/sqrt(128)
+    scale (the CPU page's `hadamard_bf16`) changes the FP4 block scale.
+
+    src = 0.7109375 e_0 + 0.703125 e_1 (both exact in bf16), position 0 (the
+    RoPE is the identity there). The Walsh-Hadamard output in natural
+    (Sylvester) order is h_i = x_0 + (-1)^i x_1: 1.4140625 at even i, 0.0078125
+    at odd i, exact in fp32. Times fl32(1/sqrt(128)) = 0.088388346 these are
+    0.12498665 and 6.905e-4. bf16 spacing below 0.125 is 2^-11, and
+    0.125 - 0.12498665 < 2^-12, so the even entries round up to exactly 0.125.
+    FP4 per 32 values: amax 0.125 = 2^-3 gives scale 2^(-3-2) = 2^-5 and code
+    0.125 / 2^-5 = 4 (value 0.125); the odd entries are 0.0221 of the scale
+    and become 0. Without that rounding the maximum 0.12498665 < 2^-3 would
+    give scale 2^-6, 7.9991 saturating to code 6, value 0.09375."""
+    src = np.zeros(128, np.float32)
+    src[0], src[1] = 0.7109375, 0.703125
+    q = oracle.finalize_index_query(src, 64, 0)
+    assert np.all(q[0::2] == 0.125), q[0::2]
+    assert np.all(q[1::2] == 0.0), q[1::2]
+
+
+# Ramp of the compressed RoPE's frequency blend, worked out by hand: 0 up to
+# pair 15, rising by a tenth per pair, 1 from pair 25 on (the CPU page's
+# `apply_compressed_rope`: low 15, high 25, factor 16).
+ROPE_RAMP = {14: 0.0, 15: 0.0, 16: 0.1, 17: 0.2, 18: 0.3, 19: 0.4, 20: 0.5, 21: 0.6, 22: 0.7,
+             23: 0.8, 24: 0.9, 25: 1.0, 26: 1.0}
+
+
+@pytest.mark.parametrize("pos", [65535, 40961])
+def test_rope_ramp_over_pairs_15_to_25_at_large_positions(pos):
+    """Every pair of the blend region rotated at a large position, against
+    complex multiplication in float64 by e^(i pos freq_p) with
+    freq_p = b_p (1 - ramp_p) + b_p / 16 ramp_p and b_p = 160000^(-2p/64).
+    At these positions a ramp that is off by one pair or a wrong denominator
+    moves the angle by a radian or more; the oracle's fp32 angle and bf16
+    output stay within 2^-8 of the float64 value."""
+    t = np.zeros(64, np.float32)
+    t[0::2], t[1::2] = 0.75, -0.5
+    r = oracle.compressed_rope(t, pos).astype(np.float64)
+    for p, ramp in ROPE_RAMP.items():
+        b = 160000.0 ** (-2.0 * p / 64.0)
+        freq = b * (1.0 - ramp) + b / 16.0 * ramp
+        z = (0.75 - 0.5j) * np.exp(1j * pos * freq)
+        assert abs(r[2 * p] - z.real) <= 2 ** -8 and abs(r[2 * p + 1] - z.imag) <= 2 ** -8, (p, r[2 * p:2 * p + 2], z)
+
+
+def test_tied_scores_are_ordered_by_ascending_record():
+    """Equal scores rank by ascending record (the CUDA page's (-score, +record)
+    order): identical keys at records 3, 7 and 12 score alike, and a full
+    selection lists them adjacent in record order."""
+    iq, iw, keys, total = make(B=1, S=1, R=20, total=80)
+    keys2 = keys.copy()
+    keys2[0, 7] = keys2[0, 3]
+    keys2[0, 12] = keys2[0, 3]
+    sel, flags, sc = oracle.csa_index_select(iq, iw, keys2, total, 20, with_scores=True)
+    assert flags & oracle.SEL_TIE
+    s = sc[0, 0, :20]
+    assert s[3] == s[7] == s[12]
+    row = list(sel[0, 0])
+    i3 = row.index(3)
+    assert row[i3:i3 + 3] == [3, 7, 12], row
+    order = np.lexsort((np.arange(20), -s.astype(np.float64)))
+    assert row == list(order)
