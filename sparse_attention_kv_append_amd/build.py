@@ -25,13 +25,17 @@ COMMON = [
 ]
 
 
+# Per-file code generation options (none needed at present).
+EXTRA: dict = {}
+
+
 def sources():
     return sorted(CSRC.glob("*.hip"))
 
 
 def _compile(src: Path) -> Path:
     obj = BUILD_DIR / (src.stem + ".o")
-    cmd = [HIPCC, *COMMON, "-c", str(src), "-o", str(obj)]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src.name, []), "-c", str(src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src.name}:\n{r.stdout}\n{r.stderr}")

@@ -1,0 +1,726 @@
+// Shared-latent selected-token attention over bf16 rows, the form for rows
+// whose keys are split over several workgroups (decode): gfx950 matrix cores
+// fed by a direct-to-LDS gather, with the value half of each gathered tile
+// read from LDS once.
+//
+// The operation is IndexShare's `index_share_row` with one kv head shared by
+// all 64 query heads and one index list per (batch, query); the 576-wide
+// latent row is the key and its first 512 dims are the value (the CSA pages'
+// record that is both key and value). Per 32-key tile a workgroup computes
+// S^T = K_sel . Q^T and O^T += V_sel^T . P^T on v_mfma_f32_16x16x32_bf16.
+//
+// Wave w plays two roles per tile:
+//  * scores and softmax of heads 16 w .. 16 w + 15 over the tile's 32 keys
+//    (all 576 dims; its 16 heads' Q in registers), probabilities rounded to
+//    bf16 into an LDS exchange (two 4 KB buffers, by tile parity);
+//  * PV of dv 128 w .. 128 w + 127 for all 64 heads over the tile's keys,
+//    reading the probabilities of all four head blocks from the exchange.
+// So the value half of a tile is read from LDS once (with the transposing
+// ds_read_b64_tr_b16, the slower of the two reads) and the key half four
+// times, instead of four times each when every wave covers all 512 dv of
+// its own 16 heads. The scores of tile t+1 are interleaved with the PV of
+// tile t, so a tile needs one workgroup barrier, and the ring keeps two tiles
+// in flight while two are read. Each head's softmax reference is its first
+// tile's maximum, held fixed, so the O^T accumulators are only touched by the
+// MFMAs; a score more than 2^TAU_HARD above it restarts the workgroup's key
+// range with the maxima seen as references.
+//
+// Gather: rows go from HBM straight into LDS (global_load_lds, 16 B per lane),
+// chunk c of ring row R stored at chunk c ^ (R & 6); under that swizzle the K
+// reads (16 rows, one chunk) and the transposing V reads are bank-conflict
+// free. The workgroup's Q rows (64 x 1152 bytes) come in through the same
+// path into two ring slots before the first tiles, as whole cache lines.
+#include <type_traits>
+
+#include "sa_mfma_dev.h"
+#include "sa_validate_dev.h"
+
+namespace sa {
+
+namespace lhd {
+constexpr int DK = 576;
+constexpr int DV = 512;
+constexpr int NH = 64;
+constexpr int KT = 32;                          // keys per tile
+constexpr int NSTAGE = 4;                       // tiles in the LDS ring: two read, two in flight
+constexpr int ROWB = DK * 2;                    // 1152 bytes per cache row
+constexpr int TILE_BYTES = KT * ROWB;           // 36864
+constexpr int HALF_ROWS = 16 * ROWB;            // byte offset of keys 16..31 of a tile
+constexpr int THREADS = 256;
+constexpr int WAVES = THREADS / 64;
+constexpr int WAVE_LOADS = TILE_BYTES / 1024 / WAVES;  // 9 wave-wide 1 KB loads per tile
+constexpr int KSTEPS = DK / 32;                 // 18 k-steps of S^T
+constexpr int DVW = DV / 4 / 16;                // 8 dv tiles of O^T per wave
+constexpr int KEYCAP = 1792;                    // keys staged in LDS at a time (what the LDS leaves)
+constexpr int RING_BYTES = NSTAGE * TILE_BYTES; // 147456
+constexpr int P_OFF = RING_BYTES;               // bf16 probabilities [buffer][head block][lane] x 16 B
+constexpr int P_BYTES = 2 * 4 * 64 * 16;        // 8192: two buffers, alternating by tile
+constexpr int KEYS_OFF = P_OFF + P_BYTES;
+constexpr int MISC_OFF = KEYS_OFF + KEYCAP * 4;
+constexpr int MISC_BYTES = 1024;
+constexpr size_t LDS_BYTES = (size_t)MISC_OFF + MISC_BYTES;  // 163840
+constexpr float TAU_HARD = 100.0f;              // largest exponent taken against the reference
+static_assert(LDS_BYTES <= 163840, "one workgroup per CU");
+// misc layout (4-byte words): [0] restart request, [8 + w] wave w's key count,
+// [12 + w] wave w saw a freshly appended key, [16..17] workgroup first
+// violation (8 bytes), [32 ..] per-wave exchange of 32 floats (w * 32 + head),
+// [32 ..] each head's (reference, row sum) at the end, 2 x 64 floats
+constexpr int M_RESTART = 0, M_LAST = 8, M_FRESH = 12, M_MINKEY = 16, M_XCH = 32;
+static_assert((M_XCH + 128) * 4 <= MISC_BYTES, "misc layout");
+}  // namespace lhd
+
+// APPEND (with FUSED): the launch also appends the batch's cur_len current
+// rows to the cache in place (rows past_len[b] ..) and writes present_len[b];
+// a workgroup that gathers one of them writes the batch's new rows itself
+// before it gathers, so it reads its own writes whatever other workgroups do;
+// with `reset` the launch's last finisher replaces the error word instead of
+// adding to it.
+template <bool I64, bool FUSED, bool SOFTCAP, bool APPEND>
+__global__ void __launch_bounds__(lhd::THREADS, 1)
+latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
+                     const void* __restrict__ idx, const int32_t* __restrict__ valid_len,
+                     uint16_t* __restrict__ y, float* __restrict__ part_o, float* __restrict__ part_ml,
+                     int64_t q_seq, int64_t rows, int64_t cap, int64_t width, int splits, float scale,
+                     float softcap, ErrorBlock* __restrict__ eb, unsigned long long* __restrict__ row_key,
+                     unsigned* __restrict__ row_done, const uint8_t* __restrict__ cur,
+                     const int32_t* __restrict__ past_len, int32_t* __restrict__ present_len, int64_t cur_len,
+                     int reset) {
+  using namespace lhd;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  lds_u8* ring = (lds_u8*)lds_raw;
+  int* keys_s = (int*)(lds_raw + KEYS_OFF);
+  int* misc = (int*)(lds_raw + MISC_OFF);
+  float* xch = (float*)(misc + M_XCH);
+  unsigned long long* minkey_s = (unsigned long long*)(misc + M_MINKEY);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+
+  int split;
+  int64_t row;
+  if (splits == 1) {
+    row = rows - 1 - (int64_t)blockIdx.x;
+    split = 0;
+  } else {
+    row = (int64_t)(blockIdx.x % (unsigned)rows);  // a row's splits share blockIdx % 8 (XCD)
+    split = (int)(blockIdx.x / (unsigned)rows);
+  }
+  const int64_t b = row / q_seq;
+  const int64_t qi = row - b * q_seq;
+  int64_t bound;
+  int64_t app_p = 0;
+  bool app_ok = false;
+  if constexpr (APPEND) {
+    app_p = (int64_t)past_len[b];
+    app_ok = app_p >= 0 && app_p + cur_len <= cap;  // else nothing is appended and the word says so
+    bound = app_p + cur_len;
+  } else {
+    bound = valid_len ? (int64_t)valid_len[b] : cap;
+  }
+  bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
+  const int64_t ibase = row * width;
+  const uint8_t* cache_b = cache + b * cap * ROWB;
+  const __amdgpu_buffer_rsrc_t crsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)cache_b, (short)0, (int)(cap * ROWB), 0x00020000);
+
+  // columns of the index row this workgroup owns
+  const int wtiles = (int)((width + KT - 1) / KT);
+  const int tps = (wtiles + splits - 1) / splits;
+  const int c0 = (int)min((int64_t)split * tps * KT, width);
+  const int c1 = (int)min((int64_t)c0 + (int64_t)tps * KT, width);
+
+  // ---- per-lane LDS offsets within a tile
+  // K (A operand of S^T): row c16 (+16 for keys 16..31), logical chunk
+  // 4 S + g, stored at (4 S + g) ^ (c16 & 6) = 4 (S ^ f2) + (g ^ (kf & 2));
+  // one base per parity of S, 64 S an immediate.
+  const int kf = c16 & 6;
+  const int kbase = c16 * ROWB + ((g ^ (kf & 2)) << 4);
+  const int kbase_e = kbase + ((kf >> 2) << 6);
+  const int kbase_o = kbase - ((kf >> 2) << 6);
+  // V^T (A operand of O^T): lane 4 jj + qq of group g points at row 4 g + jj,
+  // dv 16 dt + 4 qq, i.e. chunk 2 dt + (qq >> 1) stored at 2 (dt ^ f') +
+  // (qq >> 1); this wave's dv tiles are dt = 8 wave + d: base for d mod 4
+  // = k is vcommon + ((k ^ vflip) << 5), 32 (d & ~3) an immediate, keys
+  // 16..31 at + HALF_ROWS.
+  int vcommon, vflip;
+  {
+    const int jj = c16 >> 2, qq = c16 & 3;
+    const int R = 4 * g + jj;
+    vflip = (R & 6) >> 1;
+    vcommon = R * ROWB + 256 * wave + ((qq >> 1) << 4) + ((qq & 1) << 3);
+  }
+  // probability exchange: [buffer][head block][lane] x 16 bytes, the B operand
+  // of head block h as the MFMA takes it (lane (c16, g): head c16, keys
+  // 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3)
+  const uint32_t p_base = (uint32_t)(uintptr_t)(lds_raw + P_OFF);
+  const uint32_t p_wr = p_base + (uint32_t)((wave * 64 + lane) * 16);
+  const uint32_t p_rd = p_base + (uint32_t)(lane * 16);
+  // gather: this wave's 9 loads per tile cover 1 KB blocks 9 wave + i of the
+  // tile; lane l of block k fills tile slot 64 k + l = row R, chunk p, which
+  // holds logical chunk p ^ (R & 6) of that row (recomputed per use: cheaper
+  // than 18 registers held across the loop)
+  auto ld_row = [&](int i) { return (64 * (WAVE_LOADS * wave + i) + lane) / 72; };
+  auto ld_off = [&](int i) {
+    const int sl = 64 * (WAVE_LOADS * wave + i) + lane;
+    const int R = sl / 72;
+    return ((sl - 72 * R) ^ (R & 6)) << 4;
+  };
+  const float f = SOFTCAP ? kLog2eL : scale * kLog2eL;  // scores -> log2 units
+
+  bf16x8_l qreg[KSTEPS];
+  float m_floor = -INFINITY;  // this lane's head: the maxima of an abandoned pass
+  f32x4_l o[DVW][4];
+  float m_ref, l_run, m_seen;
+  unsigned long long mk = ~0ull;
+  int vhi = c0;
+
+  // Stage columns [st0, st1): keys (clamped into the cache) to keys_s, each
+  // wave's count of keys up to its last non-padding column to misc, and the
+  // columns not validated before checked. `between` runs after the index
+  // loads are issued and before they are used (the first stage sends this
+  // wave's Q loads out there, so their latency overlaps the index loads'
+  // and the compiler's counted wait for the indices leaves them in flight).
+  // Called with no reader of keys_s / misc left.
+  auto stage_keys = [&](int st0, int st1, auto&& between) {
+    constexpr int PER = KEYCAP / THREADS;
+    const int need = (st1 - st0 + THREADS - 1) / THREADS;  // uniform
+    const bool check = FUSED && st0 >= vhi;
+    // raw index words (widened where they are used, so no instruction
+    // consumes a load before `between` has issued its own)
+    using IdxT = typename std::conditional<I64, int64_t, int32_t>::type;
+    const IdxT* ip = (const IdxT*)idx + ibase;
+    IdxT v[PER], u[PER];
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      if (k == 0 || k < need) {
+        const int c = min(st0 + tid + THREADS * k, st1 - 1);
+        v[k] = ip[c];
+        if (check) u[k] = ip[max(c - 1, 0)];
+      }
+    }
+    between();
+    int last = 0, fresh = 0;
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int s = tid + THREADS * k;
+      const int c = st0 + s;
+      if ((k == 0 || k < need) && c < st1) {
+        const int64_t vk = (int64_t)v[k];
+        keys_s[s] = (int)((vk >= 0 && vk < bound) ? vk : 0);  // clamp: a bad row stays in bounds
+        if (vk != -1) last = s + 1;
+        if (APPEND && vk >= app_p && vk < bound) fresh = 1;
+        if (check && column_class(c, vk, (int64_t)u[k], bound))
+          mk = min(mk, (unsigned long long)(row * (width + 1) + c));
+      }
+    }
+    if (check) vhi = st1;
+    last = wave_max_nonneg(last);
+    if (lane == 0) misc[M_LAST + wave] = last;
+    if constexpr (APPEND) {
+      fresh = wave_max_nonneg(fresh);
+      if (lane == 0) misc[M_FRESH + wave] = fresh;
+    }
+    if (tid == 0) misc[M_RESTART] = 0;
+  };
+  const bool duty = split == 0 && qi == 0;
+  bool app_done = false;
+  auto append_rows = [&]() {
+    if (app_ok) {
+      const uint4* src = (const uint4*)(cur + b * cur_len * ROWB);
+      uint4* dst = (uint4*)(cache + (b * cap + app_p) * ROWB);
+      for (int u = tid; u < cur_len * (ROWB / 16); u += THREADS) dst[u] = src[u];
+    }
+    app_done = true;
+  };
+
+  // ---- the current stage: its key count, tile count and gathers
+  int kcount = 0, ntile = 0;
+  // Stage columns [st0, st1) and make them visible (an LDS-only barrier:
+  // loads issued in `between` stay in flight); with APPEND, a stage that
+  // gathers a freshly appended row first stores the batch's current rows.
+  auto stage_sync = [&](int st0, int st1, auto&& between) {
+    stage_keys(st0, st1, between);
+    lds_barrier();
+    kcount = max(max(misc[M_LAST], misc[M_LAST + 1]), max(misc[M_LAST + 2], misc[M_LAST + 3]));
+    ntile = (kcount + KT - 1) / KT;
+    if constexpr (APPEND) {
+      if ((misc[M_FRESH] | misc[M_FRESH + 1] | misc[M_FRESH + 2] | misc[M_FRESH + 3]) != 0) {
+        if (!app_done) append_rows();
+        __syncthreads();  // the stores have landed before the gathers
+      }
+    }
+  };
+  // The gather of tile tt: this wave's nine 1 KB loads, buffer loads from the
+  // batch's cache rows at byte offsets goff[i]. A slot past the keys gets an
+  // offset beyond the buffer's size, for which the range check returns zeros
+  // (its V rows must not hold garbage: P = 0 there, and 0 * inf is NaN). A
+  // tile past the last one is "gathered" too (all offsets out of range), so
+  // the issue is unconditional and the counted waits stay exact; its key
+  // reads are clamped into the staged keys.
+  uint32_t goff[WAVE_LOADS];
+  auto gather_offsets = [&](int tt) {
+    const int tk = tt < ntile ? tt : 0;
+    int gkey[WAVE_LOADS];
+#pragma unroll
+    for (int i = 0; i < WAVE_LOADS; i++) gkey[i] = keys_s[tk * KT + ld_row(i)];
+#pragma unroll
+    for (int i = 0; i < WAVE_LOADS; i++) {
+      goff[i] = tt * KT + ld_row(i) < kcount ? __umul24((uint32_t)gkey[i], (uint32_t)ROWB) + (uint32_t)ld_off(i)
+                                             : 0x80000000u;
+      asm volatile("" : "+v"(goff[i]));
+    }
+  };
+  auto gather_issue = [&](int tt) {
+    lds_u8* dst0 = ring + (tt % NSTAGE) * TILE_BYTES + (WAVE_LOADS * wave) * 1024;
+#pragma unroll
+    for (int i = 0; i < WAVE_LOADS; i++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (__attribute__((address_space(3))) void*)(dst0 + i * 1024), 16,
+                                               goff[i], 0, 0, 0);
+  };
+
+  // ---- the first stage. The workgroup's Q (64 head rows of 1152 bytes: two
+  // tiles' worth) goes into ring slots 2 and 3 with the tiles' own gather
+  // pattern and swizzle (whole cache lines, each row fetched once), in flight
+  // with the index loads; each wave then reads its 16 heads' B operands with
+  // the K-read pattern (lane (c16, g) holds dims 32 S + 8 g .. + 8 of head
+  // 16 wave + c16), and the slots go back to the ring.
+  bool pro_done = false;
+  if (c0 < c1) {
+    const uint16_t* qrow0 = q + ((b * NH) * q_seq + qi) * DK;
+    const int qstride = (int)(q_seq * ROWB);  // bytes between heads (q_seq < 256 here)
+    const __amdgpu_buffer_rsrc_t qrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)qrow0, (short)0, (NH - 1) * qstride + ROWB, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      lds_u8* dst0 = ring + (2 + u) * TILE_BYTES + (WAVE_LOADS * wave) * 1024;
+#pragma unroll
+      for (int i = 0; i < WAVE_LOADS; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (__attribute__((address_space(3))) void*)(dst0 + i * 1024), 16,
+                                                 (uint32_t)((32 * u + ld_row(i)) * qstride + ld_off(i)), 0, 0, 0);
+    }
+    // the index loads; the compiler's wait for them also covers the older Q loads
+    stage_sync(c0, min(c0 + KEYCAP, c1), []() {});
+    {
+      // head 16 wave + c16 is row 16 (wave & 1) + c16 of slot 2 + (wave >> 1)
+      const lds_u8* qt = ring + (2 + (wave >> 1)) * TILE_BYTES + (wave & 1) * HALF_ROWS + kbase_e;
+      const int odd = kbase_o - kbase_e;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; s++) {
+        const u32x4_l raw = *(const lds_u32x4*)(qt + 64 * s + ((s & 1) ? odd : 0));
+        qreg[s] = __builtin_bit_cast(bf16x8_l, raw);
+      }
+    }
+    lds_barrier();  // every wave has its Q: slots 2 and 3 return to the ring
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; p++) {
+      gather_offsets(p);
+      gather_issue(p);
+    }
+    gather_offsets(NSTAGE - 1);
+    pro_done = true;
+  }
+
+  const uint32_t p_buf = 4096;  // the two probability buffers alternate by tile parity
+  f32x4_l sacc[2][2];           // [key block][k-step parity]
+  // ---- softmax of tile tt from sacc into probability buffer pb: lane holds
+  // keys 4 g + r and 16 + 4 g + r of head 16 wave + c16, in log2 units
+  // rounded once (the maximum then gives exp2(0) exactly); the pass's first
+  // tile fixes the head's reference
+  auto softmax_write = [&](bool first, int tt, uint32_t pb) {
+    float x[8];
+    {
+      const f32x4_l s0 = sacc[0][0] + sacc[0][1], s1 = sacc[1][0] + sacc[1][1];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        x[r] = s0[r];
+        x[4 + r] = s1[r];
+      }
+    }
+    if constexpr (SOFTCAP) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) x[i] = softcap * tanhf(x[i] * scale / softcap);
+    }
+    if ((tt + 1) * KT > kcount) {  // uniform: only the last tile has empty slots
+      const int slot_base = tt * KT + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        if (slot_base + (i < 4 ? i : 12 + i) >= kcount) x[i] = -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) x[i] *= f;
+    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    tmax = max_x32(max_x16(tmax));
+    m_seen = fmaxf(m_seen, tmax);
+    if (first) m_ref = fmaxf(tmax, m_floor);
+    // a score more than 2^TAU_HARD above the reference: the pass is redone
+    if (tmax > m_ref + TAU_HARD) misc[M_RESTART] = 1;  // benign race: every writer stores 1
+    const float nm = m_ref == -INFINITY ? 0.0f : -m_ref;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) pv[i] = __builtin_amdgcn_exp2f(x[i] + nm);
+    l_run += sum_x32(sum_x16(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]))));
+    ds_write_b128_at(p_wr + pb, (u32x4_l){pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                         pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
+  };
+  auto zero_s = [&]() {
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) sacc[kb][0] = sacc[kb][1] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
+  };
+  auto tile_addr = [&](int tt) { return (uint32_t)(uintptr_t)(ring + (tt % NSTAGE) * TILE_BYTES); };
+  u32x4_l kr0[KSTEPS], kr1[KSTEPS];
+  s16x4_l vr0[DVW], vr1[DVW];
+  uint32_t ka_e = 0, ka_o = 0, va[4] = {0, 0, 0, 0};
+  auto set_k = [&](int tt) {
+    const uint32_t T = tile_addr(tt);
+    ka_e = T + kbase_e;
+    ka_o = T + kbase_o;
+  };
+  auto set_v = [&](int tt) {
+    const uint32_t T = tile_addr(tt);
+#pragma unroll
+    for (int k = 0; k < 4; k++) va[k] = T + vcommon + ((k ^ vflip) << 5);
+  };
+  auto kread = [&](auto sc) {
+    constexpr int S = decltype(sc)::value;
+    const uint32_t a = (S & 1) ? ka_o : ka_e;
+    kr0[S] = ds_read_b128_at<64 * S>(a);
+    kr1[S] = ds_read_b128_at<64 * S + HALF_ROWS>(a);
+  };
+  auto kmfma = [&](auto sc) {
+    constexpr int S = decltype(sc)::value;
+    sacc[0][S & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_l, kr0[S]), qreg[S],
+                                                             sacc[0][S & 1], 0, 0, 0);
+    sacc[1][S & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_l, kr1[S]), qreg[S],
+                                                             sacc[1][S & 1], 0, 0, 0);
+  };
+  auto vread = [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    vr0[D] = ds_read_tr16_at<32 * (D & ~3)>(va[D & 3]);
+    vr1[D] = ds_read_tr16_at<32 * (D & ~3) + HALF_ROWS>(va[D & 3]);
+  };
+  // PV of dv tile D for head blocks HB0 and HB0 + 1
+  auto vmfma2 = [&](auto dc, auto hc, const bf16x8_l* pb) {
+    constexpr int D = decltype(dc)::value;
+    constexpr int HB0 = decltype(hc)::value;
+    const s16x4_l a8[2] = {vr0[D], vr1[D]};
+    const bf16x8_l a = __builtin_bit_cast(bf16x8_l, a8);
+    o[D][HB0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[HB0], o[D][HB0], 0, 0, 0);
+    o[D][HB0 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[HB0 + 1], o[D][HB0 + 1], 0, 0, 0);
+  };
+  // the four head blocks' probabilities of tile tt (buffer by parity)
+  auto pread = [&](int tt, u32x4_l* pr) {
+    const uint32_t a = p_rd + ((tt & 1) ? p_buf : 0u);
+    pr[0] = ds_read_b128_at<0>(a);
+    pr[1] = ds_read_b128_at<1024>(a);
+    pr[2] = ds_read_b128_at<2048>(a);
+    pr[3] = ds_read_b128_at<3072>(a);
+  };
+
+  bool first_tile = true;
+  for (;;) {
+#pragma unroll
+    for (int d = 0; d < DVW; d++)
+#pragma unroll
+      for (int h = 0; h < 4; h++) o[d][h] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
+    l_run = 0.0f;
+    m_seen = m_floor;
+    m_ref = -INFINITY;
+    bool restart = false;
+    first_tile = true;
+
+    for (int st0 = c0; st0 < c1 && !restart; st0 += KEYCAP) {
+      const int st1 = min(st0 + KEYCAP, c1);
+      if (!pro_done) {
+        __syncthreads();  // the previous stage's readers are done with keys_s / misc / the ring
+        stage_sync(st0, st1, []() {});
+#pragma unroll
+        for (int p = 0; p < NSTAGE - 1; p++) {
+          gather_offsets(p);
+          gather_issue(p);
+        }
+        gather_offsets(NSTAGE - 1);
+      }
+      pro_done = false;
+      if (ntile == 0) continue;  // uniform: only padding in these columns
+
+      // ---- tile 0: S alone, the K reads KD k-steps ahead of their MFMAs
+      // (tiles 1 .. NSTAGE-2 may stay in flight)
+      wait_vm<(NSTAGE - 2) * WAVE_LOADS>();
+      lds_barrier();
+      set_k(0);
+      zero_s();
+      {
+        constexpr int KD = 4;
+        static_for<KD>(kread);
+        static_for<KSTEPS>([&](auto sc) {
+          constexpr int S = decltype(sc)::value;
+          if constexpr (S + KD < KSTEPS) kread(std::integral_constant<int, S + KD>{});
+          constexpr int LATER = (KD < KSTEPS - 1 - S ? KD : KSTEPS - 1 - S);
+          lgkm_wait_tied<2 * LATER>(kr0[S], kr1[S]);
+          kmfma(sc);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      softmax_write(first_tile, 0, 0u);
+      first_tile = false;
+
+      // ---- steady state: S of tile t+1 interleaved with PV of tile t. Step
+      // J does k-step J of the scores (2 K reads, 2 MFMAs) and, for J < 16,
+      // half of dv tile J / 2 of the PV (2 MFMAs; its 2 V reads at even J),
+      // the reads PL steps ahead; then the softmax of tile t+1 into the other
+      // probability buffer. This wave's gather of tile t+3 goes out one load
+      // per step (a burst of every wave's loads after the barrier stalls issue).
+      for (int t = 0; t < ntile; t++) {
+        wait_vm<(NSTAGE - 3) * WAVE_LOADS>();  // tile t+1 has landed for this wave (t+2 may stay in flight)
+        lds_barrier();  // and for everyone; P(t) is complete; tile t-1's slot is free
+        const int tn = t + NSTAGE - 1;
+        lds_u8* gdst = ring + (tn % NSTAGE) * TILE_BYTES + (WAVE_LOADS * wave) * 1024;
+        auto gather_one = [&](int i) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (__attribute__((address_space(3))) void*)(gdst + i * 1024), 16,
+                                                   goff[i], 0, 0, 0);
+        };
+        u32x4_l pr[4];
+        pread(t, pr);
+        set_v(t);
+        bf16x8_l pb[4];
+        if (t + 1 < ntile) {
+          set_k(t + 1);
+          zero_s();
+          constexpr int PL = 2;
+          auto step_reads = [](int j) { return j < KSTEPS ? 2 + ((j % 2 == 0 && j / 2 < DVW) ? 2 : 0) : 0; };
+          auto sread = [&](auto jc) {
+            constexpr int J = decltype(jc)::value;
+            if constexpr (J < KSTEPS) kread(jc);
+            if constexpr (J % 2 == 0 && J / 2 < DVW) vread(std::integral_constant<int, J / 2>{});
+          };
+          static_for<PL>(sread);
+          static_for<KSTEPS>([&](auto jc) {
+            constexpr int J = decltype(jc)::value;
+            if constexpr (J + PL < KSTEPS) sread(std::integral_constant<int, J + PL>{});
+            if constexpr (J < WAVE_LOADS) gather_one(J);
+            // LDS reads issued after step J's: those of steps J+1 .. J+PL
+            constexpr int LATER = step_reads(J + 1) + step_reads(J + 2);
+            if constexpr (J == 0) {
+              // the probability reads were issued before every step read
+              lgkm_wait_tied<LATER + step_reads(0) + 2>(pr[0], pr[1]);
+              lgkm_wait_tied<LATER + step_reads(0)>(pr[2], pr[3]);
+#pragma unroll
+              for (int h = 0; h < 4; h++) pb[h] = __builtin_bit_cast(bf16x8_l, pr[h]);
+            }
+            if constexpr (J % 2 == 0 && J / 2 < DVW) {
+              lgkm_wait4<LATER>(kr0[J], kr1[J], vr0[J / 2], vr1[J / 2]);
+            } else {
+              lgkm_wait_tied<LATER>(kr0[J], kr1[J]);
+            }
+            kmfma(jc);
+            if constexpr (J / 2 < DVW)
+              vmfma2(std::integral_constant<int, J / 2>{}, std::integral_constant<int, 2 * (J % 2)>{}, pb);
+            __builtin_amdgcn_sched_barrier(0);
+          });
+          softmax_write(false, t + 1, ((t + 1) & 1) ? p_buf : 0u);
+        } else {
+          // the last tile's PV alone, the reads VD dv tiles ahead
+          constexpr int VD = 4;
+          static_for<VD>(vread);
+          static_for<DVW>([&](auto dc) {
+            constexpr int D = decltype(dc)::value;
+            constexpr int AHEAD = (VD - 1 < DVW - 1 - D ? VD - 1 : DVW - 1 - D);
+            if constexpr (D == 0) {
+              lgkm_wait_tied<2 * VD + 2>(pr[0], pr[1]);
+              lgkm_wait_tied<2 * VD>(pr[2], pr[3]);
+#pragma unroll
+              for (int h = 0; h < 4; h++) pb[h] = __builtin_bit_cast(bf16x8_l, pr[h]);
+            }
+            lgkm_wait_tied<2 * AHEAD>(vr0[D], vr1[D]);
+            vmfma2(dc, std::integral_constant<int, 0>{}, pb);
+            vmfma2(dc, std::integral_constant<int, 2>{}, pb);
+            if constexpr (D < WAVE_LOADS) gather_one(D);
+            if constexpr (D + VD < DVW) vread(std::integral_constant<int, D + VD>{});
+            __builtin_amdgcn_sched_barrier(0);
+          });
+          gather_one(DVW);  // the ninth load (eight dv tiles)
+        }
+        gather_offsets(t + NSTAGE);  // offsets of the next iteration's gather
+      }
+      __syncthreads();
+      restart = misc[M_RESTART] != 0;
+    }
+    if (!restart) break;
+    m_floor = m_seen;
+  }
+
+  // ---- each head's reference and row sum to the waves that hold its outputs
+  __syncthreads();
+  if (g == 0) {
+    xch[16 * wave + c16] = m_ref;
+    xch[64 + 16 * wave + c16] = l_run;
+  }
+  if constexpr (FUSED) {
+    if (c0 == 0 && tid == 0 && width > 0 && load_index<I64>(idx, ibase) == -1)
+      mk = min(mk, (unsigned long long)(row * (width + 1) + width));  // all -1, unless a column fails
+    if (tid == 0) *minkey_s = ~0ull;
+  }
+  __syncthreads();
+  if constexpr (FUSED) {
+    if (mk != ~0ull) atomicMin(minkey_s, mk);
+  }
+
+  // ---- epilogue: lane holds O^T[128 wave + 16 d + 4 g + r][16 h + c16]
+  if (splits == 1) {
+    constexpr int YROW = 1024 + 16;  // padded: the 16 heads of one write hit distinct banks
+    __syncthreads();                 // the ring is free
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      const float lt = xch[64 + 16 * h + c16];
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      lds_u8* yl = ring + (16 * h + c16) * YROW + 256 * wave + 8 * g;
+#pragma unroll
+      for (int d = 0; d < DVW; d++) {
+        const uint32_t lo = pack_bf16x2(o[d][h][0] * inv, o[d][h][1] * inv);
+        const uint32_t hi = pack_bf16x2(o[d][h][2] * inv, o[d][h][3] * inv);
+        *(__attribute__((address_space(3))) u32x2_l*)(yl + 32 * d) = (u32x2_l){lo, hi};
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int hq = 0; hq < 16; hq++) {
+      const int hd = 16 * wave + hq;
+      const u32x4_l v = *(const lds_u32x4*)(ring + hd * YROW + 16 * lane);
+      *(u32x4_l*)(y + ((b * NH + hd) * q_seq + qi) * DV + 8 * lane) = v;
+    }
+  } else {
+    // unnormalised partials; the combine kernel merges them after this launch.
+    // They are stored device-coherent (sc1: written through the XCD's L2),
+    // so the fences of the row finishers below do not have to write back
+    // 128 KB of dirty partials per workgroup first.
+    const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(part_o + (row * splits + split) * NH * DV), (short)0, NH * DV * 4, 0x00020000);
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      const int obase = ((16 * h + c16) * DV + 128 * wave + 4 * g) * 4;
+#pragma unroll
+      for (int d = 0; d < DVW; d++)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_l, o[d][h]), prsrc, obase + 64 * d, 0, 16);
+    }
+    if (g == 0) {
+      const int64_t pr = (row * splits + split) * NH + 16 * wave + c16;
+      part_ml[pr * 2] = m_ref;
+      part_ml[pr * 2 + 1] = l_run;
+    }
+  }
+  if constexpr (APPEND) {
+    if (duty) {
+      if (!app_done) append_rows();
+      if (tid == 0) {
+        if (app_ok) present_len[b] = (int32_t)(app_p + cur_len);
+        else atomicOr(&eb->call_word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
+      }
+    }
+  }
+
+  // ---- error block: the finisher of each row records the row's first
+  // violation and counts itself toward the launch's last-arrival record
+  if constexpr (FUSED) {
+    if (tid == 0) {
+      unsigned long long k = *minkey_s;
+      bool finisher = true;
+      if (splits > 1) {
+        if (k != ~0ull) {
+          atomicMin(&row_key[row], k);
+          __threadfence();
+        }
+        finisher = atomicAdd(&row_done[row], 1u) == (unsigned)splits - 1;
+        if (finisher) {
+          row_done[row] = 0u;
+          k = atomicExch(&row_key[row], ~0ull);
+        }
+      }
+      if (finisher && k != ~0ull) {
+        const int64_t col = (int64_t)(k % (unsigned long long)(width + 1));
+        int cls = 6;
+        if (col < width) {
+          const int64_t v = load_index<I64>(idx, ibase + col);
+          const int64_t u = col > 0 ? load_index<I64>(idx, ibase + col - 1) : 0;
+          cls = column_class(col, v, u, bound);
+        }
+        atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
+        atomicMin((unsigned long long*)&eb->call_key, k);
+      }
+      if (finisher)
+        finish_launch<I64>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap, (unsigned)rows,
+                           reset != 0);
+    }
+  }
+}
+
+static bool g_lhd_attr[12] = {};
+
+sa_status launch_forward_latent_decode(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
+                                       const AppendArgs* app) {
+  using namespace lhd;
+  const int64_t rows = a.batch * a.q_seq;
+  if (rows <= 0) return SA_OK;
+  if (splits > 1 && rows * splits > c->partial_rows)
+    return set_error(c, SA_E_STATE, "forward: split-K partials exceed the context's buffers");
+  if (rows > c->rows_cap) return set_error(c, SA_E_STATE, "forward: more rows than the context holds");
+  const int64_t wgs = rows * splits;
+  if (wgs > 0x7fffffffLL) return set_error(c, SA_E_SHAPE, "forward: too many rows for one launch");
+  const bool cap_on = a.softcap != 0.0f;
+  if (app && (!fused || app->cur_len < 0 || app->cur_len > kFusedAppendRows))
+    return set_error(c, SA_E_STATE, "forward: in-launch append needs fused validation and at most 8 rows");
+  const int variant = app ? 8 + (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0)
+                          : (a.idx64 ? 1 : 0) + (fused ? 2 : 0) + (cap_on ? 4 : 0);
+  const void* fns[12] = {(const void*)latent_decode_kernel<false, false, false, false>,
+                         (const void*)latent_decode_kernel<true, false, false, false>,
+                         (const void*)latent_decode_kernel<false, true, false, false>,
+                         (const void*)latent_decode_kernel<true, true, false, false>,
+                         (const void*)latent_decode_kernel<false, false, true, false>,
+                         (const void*)latent_decode_kernel<true, false, true, false>,
+                         (const void*)latent_decode_kernel<false, true, true, false>,
+                         (const void*)latent_decode_kernel<true, true, true, false>,
+                         (const void*)latent_decode_kernel<false, true, false, true>,
+                         (const void*)latent_decode_kernel<true, true, false, true>,
+                         (const void*)latent_decode_kernel<false, true, true, true>,
+                         (const void*)latent_decode_kernel<true, true, true, true>};
+  if (!g_lhd_attr[variant]) {
+    hipError_t e = hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+    if (e != hipSuccess) return check_hip(c, e, "forward (latent decode) LDS attribute");
+    g_lhd_attr[variant] = true;
+  }
+  const dim3 grid((unsigned)wgs), block(THREADS);
+  prof_begin(c);
+  const uint8_t* cur = app ? (const uint8_t*)app->cur : nullptr;
+  const int32_t* plen = app ? app->past_len : nullptr;
+  int32_t* prlen = app ? app->present_len : nullptr;
+  const int64_t clen = app ? app->cur_len : 0;
+  const int reset = app ? app->reset : 0;
+#define SA_LHD(I, F, C, A)                                                                            \
+  hipLaunchKernelGGL((latent_decode_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,           \
+                     (const uint16_t*)a.q, (uint8_t*)a.k, a.idx, a.valid_len, (uint16_t*)a.y,         \
+                     c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width, splits, a.scale,     \
+                     a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset)
+  switch (variant) {
+    case 0: SA_LHD(false, false, false, false); break;
+    case 1: SA_LHD(true, false, false, false); break;
+    case 2: SA_LHD(false, true, false, false); break;
+    case 3: SA_LHD(true, true, false, false); break;
+    case 4: SA_LHD(false, false, true, false); break;
+    case 5: SA_LHD(true, false, true, false); break;
+    case 6: SA_LHD(false, true, true, false); break;
+    case 7: SA_LHD(true, true, true, false); break;
+    case 8: SA_LHD(false, true, false, true); break;
+    case 9: SA_LHD(true, true, false, true); break;
+    case 10: SA_LHD(false, true, true, true); break;
+    default: SA_LHD(true, true, true, true); break;
+  }
+#undef SA_LHD
+  prof_end(c);
+  sa_status s = check_hip(c, hipGetLastError(), "forward (latent decode)");
+  if (s != SA_OK || splits == 1) return s;
+  return launch_mla_combine(c, rows, a.q_seq, splits, (uint16_t*)a.y);
+}
+
+}  // namespace sa

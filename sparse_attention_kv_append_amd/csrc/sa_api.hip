@@ -379,7 +379,11 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
   if (app && path != 2 && path != 3)
     return set_error(c, SA_E_UNSUPPORTED, "step: the in-launch append needs a shared-latent MFMA path");
   switch (path) {
-    case 2: return sa::launch_forward_latent(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0, app);
+    case 2: {
+      const int splits = sa::mla_splits(batch * q_seq, width);
+      return splits > 1 ? sa::launch_forward_latent_decode(c, a, splits, fused_validate != 0, app)
+                        : sa::launch_forward_latent(c, a, splits, fused_validate != 0, app);
+    }
     case 3: return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0, app);
     case 1: return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
     case 4: return sa::launch_forward_gqa(c, a);

@@ -189,6 +189,11 @@ sa_status launch_capacity_append(sparse_attn_ctx* c, const void* bias, int dtype
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
 sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                                 const AppendArgs* app = nullptr);
+// the same rows when their keys are split over several workgroups (decode):
+// waves split into (head half, key half) for the scores and (head half, dv
+// half) for the outputs, exchanging bf16 probabilities through LDS
+sa_status launch_forward_latent_decode(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
+                                       const AppendArgs* app = nullptr);
 sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                               const AppendArgs* app = nullptr);
 sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a);

@@ -96,6 +96,11 @@ __device__ __forceinline__ void lgkm_wait6(A& a0, A& a1, B& b0, B& b1, B& b2, B&
   asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3) : "n"(N) : "memory");
 }
 template <int N, typename A, typename B>
+__device__ __forceinline__ void lgkm_wait4(A& a0, A& a1, B& b0, B& b1) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1) : "n"(N) : "memory");
+}
+template <int N, typename A, typename B>
 __device__ __forceinline__ void lgkm_wait3(A& a0, B& b0, B& b1) {
   static_assert(N >= 0 && N <= 15, "lgkmcnt range");
   asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a0), "+v"(b0), "+v"(b1) : "n"(N) : "memory");
