@@ -69,6 +69,8 @@ def parse():
 # only used while their hash is unchanged)
 KERNEL_SOURCES = {
     "latent_forward_kernel": ["k_forward_latent.hip", "sa_internal.h", "sa_validate_dev.h", "sa_mfma_dev.h"],
+    "latent_decode_kernel": ["k_forward_latent_decode.hip", "sa_internal.h", "sa_validate_dev.h",
+                             "sa_mfma_dev.h"],
     "pair_forward_kernel": ["k_forward_pair.hip", "sa_internal.h", "sa_validate_dev.h", "sa_mfma_dev.h",
                             "sa_quant_dev.h"],
     "mla_forward_kernel": ["k_forward_mla.hip", "sa_internal.h"],
@@ -668,6 +670,8 @@ def make_setup(name, rotate):
 
 
 def kernel_name(setup):
+    if setup.path == 2 and setup.splits > 1:
+        return "latent_decode_kernel"
     return {0: "generic_forward_kernel", 1: "mla_forward_kernel", 2: "latent_forward_kernel",
             3: "pair_forward_kernel", 4: "gqa_forward_kernel", 5: "csa_attention_kernel",
             6: "csa_index_score_kernel"}[setup.path]

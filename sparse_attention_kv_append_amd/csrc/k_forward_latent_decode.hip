@@ -1,7 +1,7 @@
 // Shared-latent selected-token attention over bf16 rows, the form for rows
 // whose keys are split over several workgroups (decode): gfx950 matrix cores
-// fed by a direct-to-LDS gather, with the value half of each gathered tile
-// read from LDS once.
+// fed by a direct-to-LDS gather, two waves per SIMD, with the value half of
+// each gathered tile read from LDS once.
 //
 // The operation is IndexShare's `index_share_row` with one kv head shared by
 // all 64 query heads and one index list per (batch, query); the 576-wide
@@ -9,21 +9,24 @@
 // record that is both key and value). Per 32-key tile a workgroup computes
 // S^T = K_sel . Q^T and O^T += V_sel^T . P^T on v_mfma_f32_16x16x32_bf16.
 //
-// Wave w plays two roles per tile:
-//  * scores and softmax of heads 16 w .. 16 w + 15 over the tile's 32 keys
-//    (all 576 dims; its 16 heads' Q in registers), probabilities rounded to
-//    bf16 into an LDS exchange (two 4 KB buffers, by tile parity);
-//  * PV of dv 128 w .. 128 w + 127 for all 64 heads over the tile's keys,
-//    reading the probabilities of all four head blocks from the exchange.
-// So the value half of a tile is read from LDS once (with the transposing
+// Eight waves, w = 2 hb + kh, play two roles per tile:
+//  * scores and softmax of head block hb (heads 16 hb .. 16 hb + 15) over the
+//    tile's keys 16 kh .. 16 kh + 15 (all 576 dims; the block's Q in
+//    registers), probabilities rounded to bf16 into an LDS exchange (two
+//    4 KB buffers, by tile parity);
+//  * PV of dv 64 w .. 64 w + 63 for all 64 heads over the tile's 32 keys,
+//    reading both key halves of all four head blocks from the exchange.
+// The value half of a tile is read from LDS once (with the transposing
 // ds_read_b64_tr_b16, the slower of the two reads) and the key half four
-// times, instead of four times each when every wave covers all 512 dv of
-// its own 16 heads. The scores of tile t+1 are interleaved with the PV of
-// tile t, so a tile needs one workgroup barrier, and the ring keeps two tiles
-// in flight while two are read. Each head's softmax reference is its first
-// tile's maximum, held fixed, so the O^T accumulators are only touched by the
-// MFMAs; a score more than 2^TAU_HARD above it restarts the workgroup's key
-// range with the maxima seen as references.
+// times. Every wave holds about 200 registers, so two share a SIMD and one
+// issues MFMAs while the other waits on memory or LDS. The scores of tile
+// t+1 are interleaved with the PV of tile t, so a tile needs one workgroup
+// barrier, and the ring keeps two tiles in flight while two are read. The two
+// waves of a head block agree on one softmax reference per head (the maximum
+// of its first tile over both key halves, through LDS) and keep it fixed, so
+// the O^T accumulators are only touched by the MFMAs; a score more than
+// 2^TAU_HARD above it restarts the workgroup's key range with the maxima seen
+// as references.
 //
 // Gather: rows go from HBM straight into LDS (global_load_lds, 16 B per lane),
 // chunk c of ring row R stored at chunk c ^ (R & 6); under that swizzle the K
@@ -46,27 +49,30 @@ constexpr int NSTAGE = 4;                       // tiles in the LDS ring: two re
 constexpr int ROWB = DK * 2;                    // 1152 bytes per cache row
 constexpr int TILE_BYTES = KT * ROWB;           // 36864
 constexpr int HALF_ROWS = 16 * ROWB;            // byte offset of keys 16..31 of a tile
-constexpr int THREADS = 256;
+constexpr int THREADS = 512;
 constexpr int WAVES = THREADS / 64;
-constexpr int WAVE_LOADS = TILE_BYTES / 1024 / WAVES;  // 9 wave-wide 1 KB loads per tile
+constexpr int TILE_LOADS = TILE_BYTES / 1024;   // 36 wave-wide 1 KB loads per tile:
+constexpr int MAX_LOADS = 5;                    //   waves 0-3 issue 5, waves 4-7 issue 4
 constexpr int KSTEPS = DK / 32;                 // 18 k-steps of S^T
-constexpr int DVW = DV / 4 / 16;                // 8 dv tiles of O^T per wave
-constexpr int KEYCAP = 1792;                    // keys staged in LDS at a time (what the LDS leaves)
+constexpr int DVW = DV / WAVES / 16;            // 4 dv tiles of O^T per wave
+constexpr int KEYCAP = 1696;                    // keys staged in LDS at a time (what the LDS leaves)
 constexpr int RING_BYTES = NSTAGE * TILE_BYTES; // 147456
-constexpr int P_OFF = RING_BYTES;               // bf16 probabilities [buffer][head block][lane] x 16 B
+constexpr int P_OFF = RING_BYTES;               // bf16 probabilities [buffer][head block][lane][kh] x 8 B
 constexpr int P_BYTES = 2 * 4 * 64 * 16;        // 8192: two buffers, alternating by tile
 constexpr int KEYS_OFF = P_OFF + P_BYTES;
 constexpr int MISC_OFF = KEYS_OFF + KEYCAP * 4;
-constexpr int MISC_BYTES = 1024;
+constexpr int MISC_BYTES = 1408;
 constexpr size_t LDS_BYTES = (size_t)MISC_OFF + MISC_BYTES;  // 163840
 constexpr float TAU_HARD = 100.0f;              // largest exponent taken against the reference
 static_assert(LDS_BYTES <= 163840, "one workgroup per CU");
+static_assert(4 * MAX_LOADS + 4 * (MAX_LOADS - 1) == TILE_LOADS, "gather split over the waves");
 // misc layout (4-byte words): [0] restart request, [8 + w] wave w's key count,
-// [12 + w] wave w saw a freshly appended key, [16..17] workgroup first
-// violation (8 bytes), [32 ..] per-wave exchange of 32 floats (w * 32 + head),
-// [32 ..] each head's (reference, row sum) at the end, 2 x 64 floats
-constexpr int M_RESTART = 0, M_LAST = 8, M_FRESH = 12, M_MINKEY = 16, M_XCH = 32;
-static_assert((M_XCH + 128) * 4 <= MISC_BYTES, "misc layout");
+// [16 + w] wave w saw a freshly appended key, [24..25] workgroup first
+// violation (8 bytes), [32 + h] head h's floor for the reference (the maxima
+// of an abandoned pass), [96 ..] per-wave exchange of 16 floats (w * 16 + c16)
+// and, at the end, each wave's (reference, row sum) per head, 2 x 128 floats
+constexpr int M_RESTART = 0, M_LAST = 8, M_FRESH = 16, M_MINKEY = 24, M_FLOOR = 32, M_XCH = 96;
+static_assert((M_XCH + 256) * 4 <= MISC_BYTES, "misc layout");
 }  // namespace lhd
 
 // APPEND (with FUSED): the launch also appends the batch's cur_len current
@@ -91,13 +97,19 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
   int* keys_s = (int*)(lds_raw + KEYS_OFF);
   int* misc = (int*)(lds_raw + MISC_OFF);
   float* xch = (float*)(misc + M_XCH);
+  float* floor_s = (float*)(misc + M_FLOOR);
   unsigned long long* minkey_s = (unsigned long long*)(misc + M_MINKEY);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hb = wave >> 1;  // head block of the scores
+  const int kh = wave & 1;   // key half of the scores
   const int g = lane >> 4;
   const int c16 = lane & 15;
+  // this wave's share of a tile's 36 gather loads
+  const int nload = wave < 4 ? MAX_LOADS : MAX_LOADS - 1;
+  const int block0 = wave < 4 ? MAX_LOADS * wave : (MAX_LOADS - 1) * wave + 4;
 
   int split;
   int64_t row;
@@ -133,45 +145,43 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
   const int c1 = (int)min((int64_t)c0 + (int64_t)tps * KT, width);
 
   // ---- per-lane LDS offsets within a tile
-  // K (A operand of S^T): row c16 (+16 for keys 16..31), logical chunk
-  // 4 S + g, stored at (4 S + g) ^ (c16 & 6) = 4 (S ^ f2) + (g ^ (kf & 2));
-  // one base per parity of S, 64 S an immediate.
+  // K (A operand of S^T): row 16 kh + c16, logical chunk 4 S + g, stored at
+  // (4 S + g) ^ (c16 & 6) = 4 (S ^ f2) + (g ^ (kf & 2)); one base per parity
+  // of S, 64 S an immediate.
   const int kf = c16 & 6;
-  const int kbase = c16 * ROWB + ((g ^ (kf & 2)) << 4);
+  const int kbase = kh * HALF_ROWS + c16 * ROWB + ((g ^ (kf & 2)) << 4);
   const int kbase_e = kbase + ((kf >> 2) << 6);
   const int kbase_o = kbase - ((kf >> 2) << 6);
   // V^T (A operand of O^T): lane 4 jj + qq of group g points at row 4 g + jj,
   // dv 16 dt + 4 qq, i.e. chunk 2 dt + (qq >> 1) stored at 2 (dt ^ f') +
-  // (qq >> 1); this wave's dv tiles are dt = 8 wave + d: base for d mod 4
-  // = k is vcommon + ((k ^ vflip) << 5), 32 (d & ~3) an immediate, keys
-  // 16..31 at + HALF_ROWS.
+  // (qq >> 1); this wave's dv tiles are dt = 4 wave + d, at
+  // vcommon + ((d ^ vflip) << 5), keys 16..31 at + HALF_ROWS.
   int vcommon, vflip;
   {
     const int jj = c16 >> 2, qq = c16 & 3;
     const int R = 4 * g + jj;
     vflip = (R & 6) >> 1;
-    vcommon = R * ROWB + 256 * wave + ((qq >> 1) << 4) + ((qq & 1) << 3);
+    vcommon = R * ROWB + 128 * wave + ((qq >> 1) << 4) + ((qq & 1) << 3);
   }
-  // probability exchange: [buffer][head block][lane] x 16 bytes, the B operand
-  // of head block h as the MFMA takes it (lane (c16, g): head c16, keys
-  // 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3)
+  // probability exchange: [buffer][head block][lane][kh] x 8 bytes; a PV read
+  // of 16 bytes at [buffer][h][lane] is the B operand of head block h as the
+  // MFMA takes it (lane (c16, g): head c16, keys 4 g .. 4 g + 3, then
+  // 16 + 4 g .. 16 + 4 g + 3)
   const uint32_t p_base = (uint32_t)(uintptr_t)(lds_raw + P_OFF);
-  const uint32_t p_wr = p_base + (uint32_t)((wave * 64 + lane) * 16);
+  const uint32_t p_wr = p_base + (uint32_t)((hb * 64 + lane) * 16 + kh * 8);
   const uint32_t p_rd = p_base + (uint32_t)(lane * 16);
-  // gather: this wave's 9 loads per tile cover 1 KB blocks 9 wave + i of the
-  // tile; lane l of block k fills tile slot 64 k + l = row R, chunk p, which
-  // holds logical chunk p ^ (R & 6) of that row (recomputed per use: cheaper
-  // than 18 registers held across the loop)
-  auto ld_row = [&](int i) { return (64 * (WAVE_LOADS * wave + i) + lane) / 72; };
+  // gather: this wave's loads cover 1 KB blocks block0 + i of the tile; lane
+  // l of block k fills tile slot 64 k + l = row R, chunk p, which holds
+  // logical chunk p ^ (R & 6) of that row
+  auto ld_row = [&](int i) { return (64 * (block0 + i) + lane) / 72; };
   auto ld_off = [&](int i) {
-    const int sl = 64 * (WAVE_LOADS * wave + i) + lane;
+    const int sl = 64 * (block0 + i) + lane;
     const int R = sl / 72;
     return ((sl - 72 * R) ^ (R & 6)) << 4;
   };
   const float f = SOFTCAP ? kLog2eL : scale * kLog2eL;  // scores -> log2 units
 
   bf16x8_l qreg[KSTEPS];
-  float m_floor = -INFINITY;  // this lane's head: the maxima of an abandoned pass
   f32x4_l o[DVW][4];
   float m_ref, l_run, m_seen;
   unsigned long long mk = ~0ull;
@@ -179,17 +189,12 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
 
   // Stage columns [st0, st1): keys (clamped into the cache) to keys_s, each
   // wave's count of keys up to its last non-padding column to misc, and the
-  // columns not validated before checked. `between` runs after the index
-  // loads are issued and before they are used (the first stage sends this
-  // wave's Q loads out there, so their latency overlaps the index loads'
-  // and the compiler's counted wait for the indices leaves them in flight).
-  // Called with no reader of keys_s / misc left.
-  auto stage_keys = [&](int st0, int st1, auto&& between) {
-    constexpr int PER = KEYCAP / THREADS;
+  // columns not validated before checked. Called with no reader of keys_s /
+  // misc left. The raw index words are widened where they are used.
+  auto stage_keys = [&](int st0, int st1) {
+    constexpr int PER = (KEYCAP + THREADS - 1) / THREADS;
     const int need = (st1 - st0 + THREADS - 1) / THREADS;  // uniform
     const bool check = FUSED && st0 >= vhi;
-    // raw index words (widened where they are used, so no instruction
-    // consumes a load before `between` has issued its own)
     using IdxT = typename std::conditional<I64, int64_t, int32_t>::type;
     const IdxT* ip = (const IdxT*)idx + ibase;
     IdxT v[PER], u[PER];
@@ -201,7 +206,6 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
         if (check) u[k] = ip[max(c - 1, 0)];
       }
     }
-    between();
     int last = 0, fresh = 0;
 #pragma unroll
     for (int k = 0; k < PER; k++) {
@@ -238,55 +242,82 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
 
   // ---- the current stage: its key count, tile count and gathers
   int kcount = 0, ntile = 0;
-  // Stage columns [st0, st1) and make them visible (an LDS-only barrier:
-  // loads issued in `between` stay in flight); with APPEND, a stage that
+  // Stage columns [st0, st1) and make them visible; with APPEND, a stage that
   // gathers a freshly appended row first stores the batch's current rows.
-  auto stage_sync = [&](int st0, int st1, auto&& between) {
-    stage_keys(st0, st1, between);
+  // Nothing of the ring is in flight here but the first stage's Q loads:
+  // they are waited for explicitly (the compiler may issue the index loads
+  // ahead of them, and its wait for those would not cover them).
+  auto stage_sync = [&](int st0, int st1) {
+    stage_keys(st0, st1);
+    wait_vm<0>();
     lds_barrier();
-    kcount = max(max(misc[M_LAST], misc[M_LAST + 1]), max(misc[M_LAST + 2], misc[M_LAST + 3]));
+    int kc = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; w++) kc = max(kc, misc[M_LAST + w]);
+    kcount = kc;
     ntile = (kcount + KT - 1) / KT;
     if constexpr (APPEND) {
-      if ((misc[M_FRESH] | misc[M_FRESH + 1] | misc[M_FRESH + 2] | misc[M_FRESH + 3]) != 0) {
+      int fr = 0;
+#pragma unroll
+      for (int w = 0; w < WAVES; w++) fr |= misc[M_FRESH + w];
+      if (fr != 0) {
         if (!app_done) append_rows();
         __syncthreads();  // the stores have landed before the gathers
       }
     }
   };
-  // The gather of tile tt: this wave's nine 1 KB loads, buffer loads from the
-  // batch's cache rows at byte offsets goff[i]. A slot past the keys gets an
-  // offset beyond the buffer's size, for which the range check returns zeros
-  // (its V rows must not hold garbage: P = 0 there, and 0 * inf is NaN). A
-  // tile past the last one is "gathered" too (all offsets out of range), so
-  // the issue is unconditional and the counted waits stay exact; its key
-  // reads are clamped into the staged keys.
-  uint32_t goff[WAVE_LOADS];
+  // The gather of tile tt: this wave's loads, buffer loads from the batch's
+  // cache rows at byte offsets goff[i]. A slot past the keys gets an offset
+  // beyond the buffer's size, for which the range check returns zeros (its V
+  // rows must not hold garbage: P = 0 there, and 0 * inf is NaN). A tile past
+  // the last one is "gathered" too (all offsets out of range), so the issue
+  // is unconditional and the counted waits stay exact; its key reads are
+  // clamped into the staged keys.
+  uint32_t goff[MAX_LOADS];
+  // (the slot geometry is recomputed from the lane id each time rather than
+  // held in ten registers across the kernel)
   auto gather_offsets = [&](int tt) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
     const int tk = tt < ntile ? tt : 0;
-    int gkey[WAVE_LOADS];
+    int gkey[MAX_LOADS], grow[MAX_LOADS];
 #pragma unroll
-    for (int i = 0; i < WAVE_LOADS; i++) gkey[i] = keys_s[tk * KT + ld_row(i)];
+    for (int i = 0; i < MAX_LOADS; i++) {
+      grow[i] = (64 * (block0 + i) + ln) / 72;
+      gkey[i] = keys_s[tk * KT + min(grow[i], KT - 1)];
+    }
 #pragma unroll
-    for (int i = 0; i < WAVE_LOADS; i++) {
-      goff[i] = tt * KT + ld_row(i) < kcount ? __umul24((uint32_t)gkey[i], (uint32_t)ROWB) + (uint32_t)ld_off(i)
-                                             : 0x80000000u;
+    for (int i = 0; i < MAX_LOADS; i++) {
+      const int sl = 64 * (block0 + i) + ln;
+      const int lo = ((sl - 72 * grow[i]) ^ (grow[i] & 6)) << 4;
+      goff[i] = tt * KT + grow[i] < kcount ? __umul24((uint32_t)gkey[i], (uint32_t)ROWB) + (uint32_t)lo : 0x80000000u;
       asm volatile("" : "+v"(goff[i]));
     }
   };
+  auto gather_one = [&](int tt, int i) {
+    lds_u8* dst = ring + (tt % NSTAGE) * TILE_BYTES + (block0 + i) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (__attribute__((address_space(3))) void*)dst, 16, goff[i], 0, 0,
+                                             0);
+  };
   auto gather_issue = [&](int tt) {
-    lds_u8* dst0 = ring + (tt % NSTAGE) * TILE_BYTES + (WAVE_LOADS * wave) * 1024;
 #pragma unroll
-    for (int i = 0; i < WAVE_LOADS; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (__attribute__((address_space(3))) void*)(dst0 + i * 1024), 16,
-                                               goff[i], 0, 0, 0);
+    for (int i = 0; i < MAX_LOADS; i++)
+      if (i < nload) gather_one(tt, i);
+  };
+  // counted waits: this wave's loads of `tiles` later tiles may stay in flight
+  auto wait_tiles = [&](auto tiles) {
+    constexpr int T = decltype(tiles)::value;
+    if (wave < 4) wait_vm<T * MAX_LOADS>();
+    else wait_vm<T * (MAX_LOADS - 1)>();
   };
 
   // ---- the first stage. The workgroup's Q (64 head rows of 1152 bytes: two
   // tiles' worth) goes into ring slots 2 and 3 with the tiles' own gather
   // pattern and swizzle (whole cache lines, each row fetched once), in flight
-  // with the index loads; each wave then reads its 16 heads' B operands with
-  // the K-read pattern (lane (c16, g) holds dims 32 S + 8 g .. + 8 of head
-  // 16 wave + c16), and the slots go back to the ring.
+  // with the index loads; each wave then reads its head block's B operands
+  // with the K-read pattern (lane (c16, g) holds dims 32 S + 8 g .. + 8 of
+  // head 16 hb + c16), and the slots go back to the ring.
+  if (tid < NH) floor_s[tid] = -INFINITY;  // read after the first stage's barrier
   bool pro_done = false;
   if (c0 < c1) {
     const uint16_t* qrow0 = q + ((b * NH) * q_seq + qi) * DK;
@@ -294,18 +325,18 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
     const __amdgpu_buffer_rsrc_t qrsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)qrow0, (short)0, (NH - 1) * qstride + ROWB, 0x00020000);
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      lds_u8* dst0 = ring + (2 + u) * TILE_BYTES + (WAVE_LOADS * wave) * 1024;
+    for (int u = 0; u < 2; u++)
 #pragma unroll
-      for (int i = 0; i < WAVE_LOADS; i++)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (__attribute__((address_space(3))) void*)(dst0 + i * 1024), 16,
-                                                 (uint32_t)((32 * u + ld_row(i)) * qstride + ld_off(i)), 0, 0, 0);
-    }
+      for (int i = 0; i < MAX_LOADS; i++)
+        if (i < nload)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              qrsrc, (__attribute__((address_space(3))) void*)(ring + (2 + u) * TILE_BYTES + (block0 + i) * 1024), 16,
+              (uint32_t)((32 * u + ld_row(i)) * qstride + ld_off(i)), 0, 0, 0);
     // the index loads; the compiler's wait for them also covers the older Q loads
-    stage_sync(c0, min(c0 + KEYCAP, c1), []() {});
+    stage_sync(c0, min(c0 + KEYCAP, c1));
     {
-      // head 16 wave + c16 is row 16 (wave & 1) + c16 of slot 2 + (wave >> 1)
-      const lds_u8* qt = ring + (2 + (wave >> 1)) * TILE_BYTES + (wave & 1) * HALF_ROWS + kbase_e;
+      // head 16 hb + c16 is row 16 (hb & 1) + c16 of slot 2 + (hb >> 1)
+      const lds_u8* qt = ring + (2 + (hb >> 1)) * TILE_BYTES + (hb & 1) * HALF_ROWS + (kbase_e - kh * HALF_ROWS);
       const int odd = kbase_o - kbase_e;
 #pragma unroll
       for (int s = 0; s < KSTEPS; s++) {
@@ -324,55 +355,58 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
   }
 
   const uint32_t p_buf = 4096;  // the two probability buffers alternate by tile parity
-  f32x4_l sacc[2][2];           // [key block][k-step parity]
+  f32x4_l sacc;
   // ---- softmax of tile tt from sacc into probability buffer pb: lane holds
-  // keys 4 g + r and 16 + 4 g + r of head 16 wave + c16, in log2 units
-  // rounded once (the maximum then gives exp2(0) exactly); the pass's first
-  // tile fixes the head's reference
+  // keys 16 kh + 4 g + r of head 16 hb + c16, in log2 units rounded once (the
+  // maximum then gives exp2(0) exactly); the pass's first tile fixes the
+  // reference of both waves of the head block
   auto softmax_write = [&](bool first, int tt, uint32_t pb) {
-    float x[8];
+    // the scores come straight from the last matrix instruction, sometimes
+    // across a branch, where the compiler has been seen to leave too little
+    // padding before the first read: eight slots here, tied to the values
+    asm volatile("s_nop 7" : "+v"(sacc));
+    float x[4];
     {
-      const f32x4_l s0 = sacc[0][0] + sacc[0][1], s1 = sacc[1][0] + sacc[1][1];
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        x[r] = s0[r];
-        x[4 + r] = s1[r];
-      }
+      for (int r = 0; r < 4; r++) x[r] = sacc[r];
     }
     if constexpr (SOFTCAP) {
 #pragma unroll
-      for (int i = 0; i < 8; i++) x[i] = softcap * tanhf(x[i] * scale / softcap);
+      for (int r = 0; r < 4; r++) x[r] = softcap * tanhf(x[r] * scale / softcap);
     }
     if ((tt + 1) * KT > kcount) {  // uniform: only the last tile has empty slots
-      const int slot_base = tt * KT + 4 * g;
+      const int slot_base = tt * KT + 16 * kh + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 8; i++)
-        if (slot_base + (i < 4 ? i : 12 + i) >= kcount) x[i] = -INFINITY;
+      for (int r = 0; r < 4; r++)
+        if (slot_base + r >= kcount) x[r] = -INFINITY;
     }
 #pragma unroll
-    for (int i = 0; i < 8; i++) x[i] *= f;
-    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    tmax = max_x32(max_x16(tmax));
+    for (int r = 0; r < 4; r++) x[r] *= f;
+    const float tmax = max_x32(max_x16(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))));
     m_seen = fmaxf(m_seen, tmax);
-    if (first) m_ref = fmaxf(tmax, m_floor);
+    if (first) {  // uniform
+      int ln = lane;  // the exchange addresses are recomputed rather than held
+      asm volatile("" : "+v"(ln));
+      const int cc = ln & 15;
+      if (ln < 16) xch[16 * wave + cc] = tmax;
+      lds_barrier();
+      const float other = xch[16 * (wave ^ 1) + cc];
+      const float both = kh == 0 ? fmaxf(tmax, other) : fmaxf(other, tmax);
+      m_ref = fmaxf(both, floor_s[16 * hb + cc]);
+    }
     // a score more than 2^TAU_HARD above the reference: the pass is redone
     if (tmax > m_ref + TAU_HARD) misc[M_RESTART] = 1;  // benign race: every writer stores 1
     const float nm = m_ref == -INFINITY ? 0.0f : -m_ref;
-    float pv[8];
+    float pv[4];
 #pragma unroll
-    for (int i = 0; i < 8; i++) pv[i] = __builtin_amdgcn_exp2f(x[i] + nm);
-    l_run += sum_x32(sum_x16(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]))));
-    ds_write_b128_at(p_wr + pb, (u32x4_l){pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                         pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
-  };
-  auto zero_s = [&]() {
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++) sacc[kb][0] = sacc[kb][1] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 4; r++) pv[r] = __builtin_amdgcn_exp2f(x[r] + nm);
+    l_run += sum_x32(sum_x16((pv[0] + pv[1]) + (pv[2] + pv[3])));
+    ds_write_b64_at(p_wr + pb, (u32x2_l){pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])});
   };
   auto tile_addr = [&](int tt) { return (uint32_t)(uintptr_t)(ring + (tt % NSTAGE) * TILE_BYTES); };
-  u32x4_l kr0[KSTEPS], kr1[KSTEPS];
+  u32x4_l kr[KSTEPS];
   s16x4_l vr0[DVW], vr1[DVW];
-  uint32_t ka_e = 0, ka_o = 0, va[4] = {0, 0, 0, 0};
+  uint32_t ka_e = 0, ka_o = 0, va[DVW] = {0, 0, 0, 0};
   auto set_k = [&](int tt) {
     const uint32_t T = tile_addr(tt);
     ka_e = T + kbase_e;
@@ -381,34 +415,27 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
   auto set_v = [&](int tt) {
     const uint32_t T = tile_addr(tt);
 #pragma unroll
-    for (int k = 0; k < 4; k++) va[k] = T + vcommon + ((k ^ vflip) << 5);
+    for (int d = 0; d < DVW; d++) va[d] = T + vcommon + ((d ^ vflip) << 5);
   };
   auto kread = [&](auto sc) {
     constexpr int S = decltype(sc)::value;
-    const uint32_t a = (S & 1) ? ka_o : ka_e;
-    kr0[S] = ds_read_b128_at<64 * S>(a);
-    kr1[S] = ds_read_b128_at<64 * S + HALF_ROWS>(a);
+    kr[S] = ds_read_b128_at<64 * S>((S & 1) ? ka_o : ka_e);
   };
   auto kmfma = [&](auto sc) {
     constexpr int S = decltype(sc)::value;
-    sacc[0][S & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_l, kr0[S]), qreg[S],
-                                                             sacc[0][S & 1], 0, 0, 0);
-    sacc[1][S & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_l, kr1[S]), qreg[S],
-                                                             sacc[1][S & 1], 0, 0, 0);
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_l, kr[S]), qreg[S], sacc, 0, 0, 0);
   };
   auto vread = [&](auto dc) {
     constexpr int D = decltype(dc)::value;
-    vr0[D] = ds_read_tr16_at<32 * (D & ~3)>(va[D & 3]);
-    vr1[D] = ds_read_tr16_at<32 * (D & ~3) + HALF_ROWS>(va[D & 3]);
+    vr0[D] = ds_read_tr16_at<0>(va[D]);
+    vr1[D] = ds_read_tr16_at<HALF_ROWS>(va[D]);
   };
-  // PV of dv tile D for head blocks HB0 and HB0 + 1
-  auto vmfma2 = [&](auto dc, auto hc, const bf16x8_l* pb) {
+  // PV of dv tile D for head block H
+  auto vmfma = [&](auto dc, auto hc, const bf16x8_l* pb) {
     constexpr int D = decltype(dc)::value;
-    constexpr int HB0 = decltype(hc)::value;
+    constexpr int H = decltype(hc)::value;
     const s16x4_l a8[2] = {vr0[D], vr1[D]};
-    const bf16x8_l a = __builtin_bit_cast(bf16x8_l, a8);
-    o[D][HB0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[HB0], o[D][HB0], 0, 0, 0);
-    o[D][HB0 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[HB0 + 1], o[D][HB0 + 1], 0, 0, 0);
+    o[D][H] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_l, a8), pb[H], o[D][H], 0, 0, 0);
   };
   // the four head blocks' probabilities of tile tt (buffer by parity)
   auto pread = [&](int tt, u32x4_l* pr) {
@@ -418,6 +445,17 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
     pr[2] = ds_read_b128_at<2048>(a);
     pr[3] = ds_read_b128_at<3072>(a);
   };
+  // the same, returned complete: reads and wait in one statement, so no copy
+  // of a register still being written can be placed between them
+  auto pread_now = [&](int tt, u32x4_l* pr) {
+    const uint32_t a = p_rd + ((tt & 1) ? p_buf : 0u);
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(pr[0]), "=&v"(pr[1]), "=&v"(pr[2]), "=&v"(pr[3])
+        : "v"(a)
+        : "memory");
+  };
 
   bool first_tile = true;
   for (;;) {
@@ -426,7 +464,7 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
 #pragma unroll
       for (int h = 0; h < 4; h++) o[d][h] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
     l_run = 0.0f;
-    m_seen = m_floor;
+    m_seen = -INFINITY;
     m_ref = -INFINITY;
     bool restart = false;
     first_tile = true;
@@ -435,7 +473,7 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
       const int st1 = min(st0 + KEYCAP, c1);
       if (!pro_done) {
         __syncthreads();  // the previous stage's readers are done with keys_s / misc / the ring
-        stage_sync(st0, st1, []() {});
+        stage_sync(st0, st1);
 #pragma unroll
         for (int p = 0; p < NSTAGE - 1; p++) {
           gather_offsets(p);
@@ -448,18 +486,18 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
 
       // ---- tile 0: S alone, the K reads KD k-steps ahead of their MFMAs
       // (tiles 1 .. NSTAGE-2 may stay in flight)
-      wait_vm<(NSTAGE - 2) * WAVE_LOADS>();
+      wait_tiles(std::integral_constant<int, NSTAGE - 2>{});
       lds_barrier();
       set_k(0);
-      zero_s();
+      sacc = (f32x4_l){0.f, 0.f, 0.f, 0.f};
       {
-        constexpr int KD = 4;
+        constexpr int KD = 6;
         static_for<KD>(kread);
         static_for<KSTEPS>([&](auto sc) {
           constexpr int S = decltype(sc)::value;
           if constexpr (S + KD < KSTEPS) kread(std::integral_constant<int, S + KD>{});
           constexpr int LATER = (KD < KSTEPS - 1 - S ? KD : KSTEPS - 1 - S);
-          lgkm_wait_tied<2 * LATER>(kr0[S], kr1[S]);
+          lgkm_wait_tied1<LATER>(kr[S]);
           kmfma(sc);
           __builtin_amdgcn_sched_barrier(0);
         });
@@ -468,80 +506,71 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
       first_tile = false;
 
       // ---- steady state: S of tile t+1 interleaved with PV of tile t. Step
-      // J does k-step J of the scores (2 K reads, 2 MFMAs) and, for J < 16,
-      // half of dv tile J / 2 of the PV (2 MFMAs; its 2 V reads at even J),
-      // the reads PL steps ahead; then the softmax of tile t+1 into the other
-      // probability buffer. This wave's gather of tile t+3 goes out one load
-      // per step (a burst of every wave's loads after the barrier stalls issue).
+      // J does k-step J of the scores (1 K read, 1 MFMA) and, for J < 16, the
+      // PV of dv tile J / 4 for head block J % 4 (1 MFMA; the tile's 2 V reads
+      // at J % 4 == 0), the reads PL steps ahead; then the softmax of tile t+1
+      // into the other probability buffer. This wave's gather of tile t+3 goes
+      // out one load per step.
       for (int t = 0; t < ntile; t++) {
-        wait_vm<(NSTAGE - 3) * WAVE_LOADS>();  // tile t+1 has landed for this wave (t+2 may stay in flight)
+        wait_tiles(std::integral_constant<int, NSTAGE - 3>{});  // tile t+1 has landed for this wave
         lds_barrier();  // and for everyone; P(t) is complete; tile t-1's slot is free
         const int tn = t + NSTAGE - 1;
-        lds_u8* gdst = ring + (tn % NSTAGE) * TILE_BYTES + (WAVE_LOADS * wave) * 1024;
-        auto gather_one = [&](int i) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, (__attribute__((address_space(3))) void*)(gdst + i * 1024), 16,
-                                                   goff[i], 0, 0, 0);
-        };
         u32x4_l pr[4];
-        pread(t, pr);
         set_v(t);
         bf16x8_l pb[4];
         if (t + 1 < ntile) {
+          pread(t, pr);
           set_k(t + 1);
-          zero_s();
-          constexpr int PL = 2;
-          auto step_reads = [](int j) { return j < KSTEPS ? 2 + ((j % 2 == 0 && j / 2 < DVW) ? 2 : 0) : 0; };
+          sacc = (f32x4_l){0.f, 0.f, 0.f, 0.f};
+          constexpr int PL = 3;
+          auto step_reads = [](int j) { return j < KSTEPS ? 1 + ((j < 4 * DVW && j % 4 == 0) ? 2 : 0) : 0; };
           auto sread = [&](auto jc) {
             constexpr int J = decltype(jc)::value;
             if constexpr (J < KSTEPS) kread(jc);
-            if constexpr (J % 2 == 0 && J / 2 < DVW) vread(std::integral_constant<int, J / 2>{});
+            if constexpr (J < 4 * DVW && J % 4 == 0) vread(std::integral_constant<int, J / 4>{});
           };
           static_for<PL>(sread);
           static_for<KSTEPS>([&](auto jc) {
             constexpr int J = decltype(jc)::value;
             if constexpr (J + PL < KSTEPS) sread(std::integral_constant<int, J + PL>{});
-            if constexpr (J < WAVE_LOADS) gather_one(J);
+            if constexpr (J < MAX_LOADS) {
+              if (J < nload) gather_one(tn, J);
+            }
             // LDS reads issued after step J's: those of steps J+1 .. J+PL
-            constexpr int LATER = step_reads(J + 1) + step_reads(J + 2);
+            constexpr int LATER = step_reads(J + 1) + step_reads(J + 2) + step_reads(J + 3);
             if constexpr (J == 0) {
               // the probability reads were issued before every step read
-              lgkm_wait_tied<LATER + step_reads(0) + 2>(pr[0], pr[1]);
-              lgkm_wait_tied<LATER + step_reads(0)>(pr[2], pr[3]);
+              constexpr int AFTER_P = LATER + step_reads(0);
+              lgkm_wait_tied<AFTER_P + 2>(pr[0], pr[1]);
+              lgkm_wait_tied<AFTER_P>(pr[2], pr[3]);
 #pragma unroll
               for (int h = 0; h < 4; h++) pb[h] = __builtin_bit_cast(bf16x8_l, pr[h]);
             }
-            if constexpr (J % 2 == 0 && J / 2 < DVW) {
-              lgkm_wait4<LATER>(kr0[J], kr1[J], vr0[J / 2], vr1[J / 2]);
+            if constexpr (J < 4 * DVW && J % 4 == 0) {
+              lgkm_wait3<LATER>(kr[J], vr0[J / 4], vr1[J / 4]);
             } else {
-              lgkm_wait_tied<LATER>(kr0[J], kr1[J]);
+              lgkm_wait_tied1<LATER>(kr[J]);
             }
             kmfma(jc);
-            if constexpr (J / 2 < DVW)
-              vmfma2(std::integral_constant<int, J / 2>{}, std::integral_constant<int, 2 * (J % 2)>{}, pb);
+            if constexpr (J < 4 * DVW)
+              vmfma(std::integral_constant<int, J / 4>{}, std::integral_constant<int, J % 4>{}, pb);
             __builtin_amdgcn_sched_barrier(0);
           });
           softmax_write(false, t + 1, ((t + 1) & 1) ? p_buf : 0u);
         } else {
-          // the last tile's PV alone, the reads VD dv tiles ahead
-          constexpr int VD = 4;
-          static_for<VD>(vread);
+          // the last tile's PV alone: its probabilities, then all of its V
+          // reads ahead
+          pread_now(t, pr);
+#pragma unroll
+          for (int h = 0; h < 4; h++) pb[h] = __builtin_bit_cast(bf16x8_l, pr[h]);
+          static_for<DVW>(vread);
           static_for<DVW>([&](auto dc) {
             constexpr int D = decltype(dc)::value;
-            constexpr int AHEAD = (VD - 1 < DVW - 1 - D ? VD - 1 : DVW - 1 - D);
-            if constexpr (D == 0) {
-              lgkm_wait_tied<2 * VD + 2>(pr[0], pr[1]);
-              lgkm_wait_tied<2 * VD>(pr[2], pr[3]);
-#pragma unroll
-              for (int h = 0; h < 4; h++) pb[h] = __builtin_bit_cast(bf16x8_l, pr[h]);
-            }
-            lgkm_wait_tied<2 * AHEAD>(vr0[D], vr1[D]);
-            vmfma2(dc, std::integral_constant<int, 0>{}, pb);
-            vmfma2(dc, std::integral_constant<int, 2>{}, pb);
-            if constexpr (D < WAVE_LOADS) gather_one(D);
-            if constexpr (D + VD < DVW) vread(std::integral_constant<int, D + VD>{});
+            lgkm_wait_tied<2 * (DVW - 1 - D)>(vr0[D], vr1[D]);
+            static_for<4>([&](auto hc) { vmfma(dc, hc, pb); });
             __builtin_amdgcn_sched_barrier(0);
           });
-          gather_one(DVW);  // the ninth load (eight dv tiles)
+          gather_issue(tn);
         }
         gather_offsets(t + NSTAGE);  // offsets of the next iteration's gather
       }
@@ -549,14 +578,22 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
       restart = misc[M_RESTART] != 0;
     }
     if (!restart) break;
-    m_floor = m_seen;
+    // both waves of a head block restart from the same maxima
+    __syncthreads();
+    if (g == 0) xch[16 * wave + c16] = m_seen;
+    __syncthreads();
+    if (kh == 0 && g == 0) {
+      const float other = xch[16 * (wave ^ 1) + c16];
+      floor_s[16 * hb + c16] = fmaxf(floor_s[16 * hb + c16], fmaxf(m_seen, other));
+    }
   }
 
-  // ---- each head's reference and row sum to the waves that hold its outputs
+  // ---- each head's reference and both key halves' row sums, to the waves
+  // that hold its outputs: xch[w * 16 + c16] = reference, xch[128 + ...] = sum
   __syncthreads();
   if (g == 0) {
     xch[16 * wave + c16] = m_ref;
-    xch[64 + 16 * wave + c16] = l_run;
+    xch[128 + 16 * wave + c16] = l_run;
   }
   if constexpr (FUSED) {
     if (c0 == 0 && tid == 0 && width > 0 && load_index<I64>(idx, ibase) == -1)
@@ -567,16 +604,18 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
   if constexpr (FUSED) {
     if (mk != ~0ull) atomicMin(minkey_s, mk);
   }
+  // the row sum of head 16 h + c16, key halves added in order
+  auto l_total = [&](int h) { return xch[128 + 32 * h + c16] + xch[128 + 32 * h + 16 + c16]; };
 
-  // ---- epilogue: lane holds O^T[128 wave + 16 d + 4 g + r][16 h + c16]
+  // ---- epilogue: lane holds O^T[64 wave + 16 d + 4 g + r][16 h + c16]
   if (splits == 1) {
     constexpr int YROW = 1024 + 16;  // padded: the 16 heads of one write hit distinct banks
     __syncthreads();                 // the ring is free
 #pragma unroll
     for (int h = 0; h < 4; h++) {
-      const float lt = xch[64 + 16 * h + c16];
+      const float lt = l_total(h);
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      lds_u8* yl = ring + (16 * h + c16) * YROW + 256 * wave + 8 * g;
+      lds_u8* yl = ring + (16 * h + c16) * YROW + 128 * wave + 8 * g;
 #pragma unroll
       for (int d = 0; d < DVW; d++) {
         const uint32_t lo = pack_bf16x2(o[d][h][0] * inv, o[d][h][1] * inv);
@@ -586,8 +625,8 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
     }
     __syncthreads();
 #pragma unroll 4
-    for (int hq = 0; hq < 16; hq++) {
-      const int hd = 16 * wave + hq;
+    for (int hq = 0; hq < 8; hq++) {
+      const int hd = 8 * wave + hq;
       const u32x4_l v = *(const lds_u32x4*)(ring + hd * YROW + 16 * lane);
       *(u32x4_l*)(y + ((b * NH + hd) * q_seq + qi) * DV + 8 * lane) = v;
     }
@@ -600,15 +639,15 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
         (void*)(part_o + (row * splits + split) * NH * DV), (short)0, NH * DV * 4, 0x00020000);
 #pragma unroll
     for (int h = 0; h < 4; h++) {
-      const int obase = ((16 * h + c16) * DV + 128 * wave + 4 * g) * 4;
+      const int obase = ((16 * h + c16) * DV + 64 * wave + 4 * g) * 4;
 #pragma unroll
       for (int d = 0; d < DVW; d++)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_l, o[d][h]), prsrc, obase + 64 * d, 0, 16);
     }
-    if (g == 0) {
-      const int64_t pr = (row * splits + split) * NH + 16 * wave + c16;
+    if (kh == 0 && g == 0) {
+      const int64_t pr = (row * splits + split) * NH + 16 * hb + c16;
       part_ml[pr * 2] = m_ref;
-      part_ml[pr * 2 + 1] = l_run;
+      part_ml[pr * 2 + 1] = l_total(hb);
     }
   }
   if constexpr (APPEND) {
