@@ -414,8 +414,39 @@ sa_status sparse_attn_reset_error_async(sparse_attn_ctx* ctx);
  * IndexShare wording of the first failing row into sparse_attn_last_error(). */
 sa_status sparse_attn_read_error(sparse_attn_ctx* ctx, uint32_t* word, uint64_t* first_bad);
 
-/* The last host-side message for this context ("" if none). */
+/* The last host-side message for this context ("" if none). With ctx NULL:
+ * the message of this thread's last sparse_attn_forward_latent_static call. */
 const char* sparse_attn_last_error(const sparse_attn_ctx* ctx);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture without a memory pool, tight serving loops, harnesses that forbid
+ * hipMalloc): sparse_attn_forward with fused_validate = 0 on a context of
+ * layout SHARED_LATENT, dense bf16 cache, 64 query heads, Dk 576, Dv 512 and
+ * one index list per (batch, query), but without any context. No call
+ * allocates: the split-K partials live in a static device array of
+ * SA_STATIC_SCRATCH_BYTES, one per GPU the library runs on, reserved when the
+ * library is loaded there and held until the process ends.
+ *   q, cache, valid_len, indices, y   as sparse_attn_forward (cache is the
+ *                  shared-latent present cache [B, 1, cache_capacity, 576]
+ *                  bf16; indices [B, 1, Sq, W] of index_dtype)
+ *   index_dtype    SA_IDX_I32 or SA_IDX_I64
+ *   scale, softcap as sa_config (scale 0 -> 1/sqrt(576); softcap 0 -> off)
+ *   hip_stream     the stream to launch on (NULL: the null stream)
+ * Results equal sparse_attn_forward's on the same inputs (same kernels and
+ * split count). Index rows are not validated. Errors, before any launch:
+ * SA_E_ARG (NULL tensor, non-positive size, scale or softcap negative or not
+ * finite), SA_E_DTYPE (index_dtype), SA_E_UNSUPPORTED (capacity beyond the
+ * kernels' 32-bit offsets), SA_E_CAPACITY when batch * Sq rows at the planned
+ * split count need more partials (rows * splits * 131,584 bytes) than the
+ * scratch holds; SA_E_HIP for a failed launch. The message is
+ * sparse_attn_last_error(NULL). Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (different streams, host threads)
+ * race and must be ordered by the caller. Asynchronous and capturable. */
+#define SA_STATIC_SCRATCH_BYTES (48u << 20)
+sa_status sparse_attn_forward_latent_static(const void* q, int64_t batch, int64_t q_seq, const void* cache,
+                                            int64_t cache_capacity, const int32_t* valid_len,
+                                            const void* indices, int32_t index_dtype, int64_t width,
+                                            float scale, float softcap, void* y, void* hip_stream);
 
 /* Report which forward path and split count a call with these sizes takes:
  * *path = 0 generic (VALU), 1 shared-latent MFMA over fp8_e4m3_block64

@@ -29,6 +29,7 @@ SA_ERR_SENTINEL, SA_ERR_AFTER_PAD, SA_ERR_RANGE = 0x01, 0x02, 0x04
 SA_ERR_DUPLICATE, SA_ERR_ORDER, SA_ERR_ALL_PAD = 0x08, 0x10, 0x20
 SA_ERR_APPEND_CAPACITY, SA_ERR_QUANT_NONFINITE = 0x40, 0x80
 SA_ERR_INDEX_ANY, SA_ERR_APPEND_ANY = 512, 1024
+SA_STATIC_SCRATCH_BYTES = 48 << 20
 SA_ERR_CSA_GEOMETRY, SA_ERR_CSA_DENOM, SA_ERR_INDEX_NONFINITE = 0x100, 0x800, 0x1000
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_DTYPE", 4: "SA_E_CAPACITY",
@@ -41,7 +42,7 @@ EXPORTS = [
     "sparse_attn_csa_forward", "sparse_attn_csa_index_select", "sparse_attn_csa_index_workspace_bytes",
     "sparse_attn_reset_error_async", "sparse_attn_read_error", "sparse_attn_last_error",
     "sparse_attn_query_plan", "sparse_attn_profile_enable", "sparse_attn_profile_read",
-    "sparse_attn_version",
+    "sparse_attn_version", "sparse_attn_forward_latent_static",
 ]
 
 
@@ -109,6 +110,8 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
         "sparse_attn_profile_enable": ([V, I32], st),
         "sparse_attn_profile_read": ([V, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)], st),
         "sparse_attn_version": ([], ctypes.c_char_p),
+        "sparse_attn_forward_latent_static": ([V, I64, I64, V, I64, V, V, I32, I64, ctypes.c_float,
+                                               ctypes.c_float, V, V], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -309,6 +312,19 @@ class Context:
         self._check(self.lib.sparse_attn_query_plan(self.handle, batch, q_seq, index_heads, width,
                                                     ctypes.byref(p), ctypes.byref(s)))
         return int(p.value), int(s.value)
+
+
+def forward_latent_static(q, batch, q_seq, cache, cache_capacity, valid_len, indices, width, y, *,
+                          index_dtype=SA_IDX_I32, scale=0.0, softcap=0.0, stream=None):
+    """sparse_attn_forward_latent_static on the current (or given) torch stream:
+    the shared-latent bf16 forward without a context, its split-K partials in
+    the library's static per-GPU scratch."""
+    lib = load()
+    st = lib.sparse_attn_forward_latent_static(
+        _ptr(q), batch, q_seq, _ptr(cache), cache_capacity, _ptr(valid_len), _ptr(indices),
+        index_dtype, width, scale, softcap, _ptr(y), _stream_handle(stream))
+    if st != SA_OK:
+        raise SparseAttnError(st, lib.sparse_attn_last_error(None).decode())
 
 
 def __getattr__(name):

@@ -33,6 +33,32 @@ std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0
   return buf;
 }
 
+// ---- scratch of the allocation-free forward: the split-K partials of
+// sparse_attn_forward_latent_static live here, one copy per GPU the library
+// runs on, held until the process ends. Host code never passes `scratch`
+// itself (on the host it names a stand-in, not device memory): it passes the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[SA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+thread_local std::string g_static_error;
+
+// The device address of this device's scratch, looked up once per device
+// with that device current.
+hipError_t scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 namespace sa {
@@ -742,8 +768,108 @@ sa_status sparse_attn_profile_read(sparse_attn_ctx* c, double* total_ms, int64_t
 }
 
 const char* sparse_attn_last_error(const sparse_attn_ctx* c) {
+  if (!c) return g_static_error.c_str();
   if (!live(c)) return "invalid or destroyed sparse_attn context";
   return c->last_error.c_str();
+}
+
+sa_status sparse_attn_forward_latent_static(const void* q, int64_t batch, int64_t q_seq, const void* cache,
+                                            int64_t cache_capacity, const int32_t* valid_len,
+                                            const void* indices, int32_t index_dtype, int64_t width,
+                                            float scale, float softcap, void* y, void* hip_stream) {
+  g_static_error.clear();
+  auto fail = [](sa_status st, const std::string& m) {
+    g_static_error = "forward_latent_static: " + m;
+    return st;
+  };
+  if (!q || !cache || !indices || !y) return fail(SA_E_ARG, "q, cache, indices and y are required");
+  if (batch <= 0 || q_seq <= 0 || width <= 0 || cache_capacity <= 0)
+    return fail(SA_E_ARG, "batch, q_seq, width and cache_capacity must be positive");
+  if (index_dtype != SA_IDX_I32 && index_dtype != SA_IDX_I64) return fail(SA_E_DTYPE, "index_dtype must be SA_IDX_I32 or SA_IDX_I64");
+  if (!isfinite(scale) || scale < 0.0f || !isfinite(softcap) || softcap < 0.0f)
+    return fail(SA_E_ARG, "scale and softcap must be finite and >= 0");
+  if (width > 0x7fffffffLL) return fail(SA_E_UNSUPPORTED, "index width above 2^31 - 1");
+  // a context on the stack: the same configuration checks and kernels as
+  // sparse_attn_forward on a shared-latent bf16 context, with no device memory
+  // of its own
+  sparse_attn_ctx sh;
+  sh.magic = sa::kMagic;
+  sa_config& k = sh.cfg;
+  k = sa_config{};
+  k.num_heads = 64;
+  k.kv_num_heads = 1;
+  k.head_dim_qk = 576;
+  k.head_dim_v = 512;
+  k.rope_dim = 64;
+  k.dtype = SA_BF16;
+  k.cache_format = SA_CACHE_DENSE;
+  k.kv_layout = SA_KV_SHARED_LATENT;
+  k.index_dtype = index_dtype;
+  k.scale = scale == 0.0f ? 1.0f / sqrtf(576.0f) : scale;
+  k.softcap = softcap;
+  k.max_batch = batch;
+  k.max_q_seq = q_seq;
+  k.max_index_width = width;
+  k.max_cache_len = cache_capacity;
+  if (sa::forward_path(k, 1) != 2)
+    return fail(SA_E_UNSUPPORTED, fmt("cache capacity %lld is beyond the shared-latent kernels' reach", cache_capacity));
+  sh.stream = (hipStream_t)hip_stream;
+  sh.err = nullptr;  // the unvalidated kernels never touch the error block
+  sh.gpart_o = sh.gpart_ml = nullptr;
+  sh.gpart_rows = 0;
+  sh.zeros = nullptr;
+  sh.row_key = nullptr;
+  sh.row_done = nullptr;
+  sh.prof_n = 0;
+  const int64_t rows = batch * q_seq;
+  sh.rows_cap = rows;
+  const int splits = sa::mla_splits(rows, width);
+  sh.partial_o = sh.partial_ml = nullptr;
+  sh.partial_rows = 0;
+  if (splits > 1) {
+    const int64_t parts = rows * splits;
+    const int64_t o_bytes = (parts * 64 * 512 * 4 + 255) / 256 * 256;
+    const int64_t need = o_bytes + parts * 64 * 2 * 4;
+    if (need > (int64_t)SA_STATIC_SCRATCH_BYTES)
+      return fail(SA_E_CAPACITY, fmt("%lld rows in %lld splits need %lld bytes of split-K partials; the static scratch holds %lld",
+                                     rows, splits, need, (long long)SA_STATIC_SCRATCH_BYTES));
+    hipError_t e = hipGetDevice(&sh.device);
+    if (e != hipSuccess) return fail(SA_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (sh.device < 0 || sh.device >= kMaxDevices) return fail(SA_E_UNSUPPORTED, fmt("device %lld beyond the first 64", sh.device));
+    void* base = nullptr;
+    e = scratch_address(sh.device, &base);
+    if (e != hipSuccess) return fail(SA_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    sh.partial_o = (float*)base;
+    sh.partial_ml = (float*)((uint8_t*)base + o_bytes);
+    sh.partial_rows = parts;
+  }
+  sa::FwdArgs a;
+  a.q = q;
+  a.k = cache;
+  a.v = nullptr;
+  a.idx = indices;
+  a.valid_len = valid_len;
+  a.y = y;
+  a.batch = batch;
+  a.hq = k.num_heads;
+  a.hkv = k.kv_num_heads;
+  a.q_seq = q_seq;
+  a.dk = k.head_dim_qk;
+  a.dv = k.head_dim_v;
+  a.rope = k.rope_dim;
+  a.cap = cache_capacity;
+  a.index_heads = 1;
+  a.width = width;
+  a.scale = k.scale;
+  a.softcap = k.softcap;
+  a.dtype = k.dtype;
+  a.cache_format = k.cache_format;
+  a.kv_layout = k.kv_layout;
+  a.idx64 = index_dtype == SA_IDX_I64;
+  const sa_status st = splits > 1 ? sa::launch_forward_latent_decode(&sh, a, splits, false, nullptr)
+                                  : sa::launch_forward_latent(&sh, a, 1, false, nullptr);
+  if (st != SA_OK) g_static_error = "forward_latent_static: " + sh.last_error;
+  return st;
 }
 
 }  // extern "C"

@@ -83,4 +83,24 @@ def test_null_and_unknown_context_rejected_without_launch():
     assert lib.sparse_attn_capacity_lengths(fake, None, None, 0, 1, 1, 1, 1, None, None) == sa.SA_E_STATE
     assert lib.sparse_attn_forward(fake, None, 1, 1, None, None, 1, None, None, 1, 1, None, 0) == sa.SA_E_STATE
     assert lib.sparse_attn_destroy(None) == sa.SA_OK
-    assert b"invalid" in lib.sparse_attn_last_error(None)
+    assert b"invalid" in lib.sparse_attn_last_error(fake)
+
+
+def test_static_forward_checks_arguments_before_any_hip_call():
+    """The allocation-free forward rejects bad arguments and a split-K plan
+    whose partials exceed its static scratch on the host, before touching the
+    device (so this runs without a GPU)."""
+    lib = sa.load()
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails before a launch
+    f = lib.sparse_attn_forward_latent_static
+    assert f(None, 1, 1, p, 64, None, p, sa.SA_IDX_I32, 64, 0.0, 0.0, p, None) == sa.SA_E_ARG
+    assert b"required" in lib.sparse_attn_last_error(None)
+    assert f(p, 0, 1, p, 64, None, p, sa.SA_IDX_I32, 64, 0.0, 0.0, p, None) == sa.SA_E_ARG
+    assert f(p, 1, 1, p, 64, None, p, 7, 64, 0.0, 0.0, p, None) == sa.SA_E_DTYPE
+    assert f(p, 1, 1, p, 64, None, p, sa.SA_IDX_I32, 64, -1.0, 0.0, p, None) == sa.SA_E_ARG
+    assert f(p, 1, 1, p, 64, None, p, sa.SA_IDX_I32, 64, 0.0, float("nan"), p, None) == sa.SA_E_ARG
+    # 200 rows of 4096 columns plan 2 splits: 400 partials of 131,584 bytes > 48 MiB
+    assert f(p, 200, 1, p, 8192, None, p, sa.SA_IDX_I32, 4096, 0.0, 0.0, p, None) == sa.SA_E_CAPACITY
+    msg = lib.sparse_attn_last_error(None)
+    assert b"static scratch holds 50331648" in msg and b"52633600" in msg, msg
+    assert sa.SA_STATIC_SCRATCH_BYTES == 48 << 20
