@@ -189,34 +189,39 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
 
   // Stage columns [st0, st1): keys (clamped into the cache) to keys_s, each
   // wave's count of keys up to its last non-padding column to misc, and the
-  // columns not validated before checked. Called with no reader of keys_s /
-  // misc left. The raw index words are widened where they are used.
-  auto stage_keys = [&](int st0, int st1) {
-    constexpr int PER = (KEYCAP + THREADS - 1) / THREADS;
+  // columns not validated before checked. load_keys issues the index loads
+  // (the raw words are widened where they are used); keys_to_lds, called with
+  // no reader of keys_s / misc left, consumes them.
+  constexpr int PER = (KEYCAP + THREADS - 1) / THREADS;
+  using IdxT = typename std::conditional<I64, int64_t, int32_t>::type;
+  IdxT kv[PER], ku[PER];
+  auto load_keys = [&](int st0, int st1) {
     const int need = (st1 - st0 + THREADS - 1) / THREADS;  // uniform
     const bool check = FUSED && st0 >= vhi;
-    using IdxT = typename std::conditional<I64, int64_t, int32_t>::type;
     const IdxT* ip = (const IdxT*)idx + ibase;
-    IdxT v[PER], u[PER];
 #pragma unroll
     for (int k = 0; k < PER; k++) {
       if (k == 0 || k < need) {
         const int c = min(st0 + tid + THREADS * k, st1 - 1);
-        v[k] = ip[c];
-        if (check) u[k] = ip[max(c - 1, 0)];
+        kv[k] = ip[c];
+        if (check) ku[k] = ip[max(c - 1, 0)];
       }
     }
+  };
+  auto keys_to_lds = [&](int st0, int st1) {
+    const int need = (st1 - st0 + THREADS - 1) / THREADS;
+    const bool check = FUSED && st0 >= vhi;
     int last = 0, fresh = 0;
 #pragma unroll
     for (int k = 0; k < PER; k++) {
       const int s = tid + THREADS * k;
       const int c = st0 + s;
       if ((k == 0 || k < need) && c < st1) {
-        const int64_t vk = (int64_t)v[k];
+        const int64_t vk = (int64_t)kv[k];
         keys_s[s] = (int)((vk >= 0 && vk < bound) ? vk : 0);  // clamp: a bad row stays in bounds
         if (vk != -1) last = s + 1;
         if (APPEND && vk >= app_p && vk < bound) fresh = 1;
-        if (check && column_class(c, vk, (int64_t)u[k], bound))
+        if (check && column_class(c, vk, (int64_t)ku[k], bound))
           mk = min(mk, (unsigned long long)(row * (width + 1) + c));
       }
     }
@@ -242,15 +247,10 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
 
   // ---- the current stage: its key count, tile count and gathers
   int kcount = 0, ntile = 0;
-  // Stage columns [st0, st1) and make them visible; with APPEND, a stage that
-  // gathers a freshly appended row first stores the batch's current rows.
-  // Nothing of the ring is in flight here but the first stage's Q loads:
-  // they are waited for explicitly (the compiler may issue the index loads
-  // ahead of them, and its wait for those would not cover them).
-  auto stage_sync = [&](int st0, int st1) {
-    stage_keys(st0, st1);
-    wait_vm<0>();
-    lds_barrier();
+  // After the staged keys are visible: the stage's key and tile counts; with
+  // APPEND, a stage that gathers a freshly appended row first stores the
+  // batch's current rows.
+  auto stage_counts = [&]() {
     int kc = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; w++) kc = max(kc, misc[M_LAST + w]);
@@ -311,15 +311,20 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
     else wait_vm<T * (MAX_LOADS - 1)>();
   };
 
-  // ---- the first stage. The workgroup's Q (64 head rows of 1152 bytes: two
-  // tiles' worth) goes into ring slots 2 and 3 with the tiles' own gather
-  // pattern and swizzle (whole cache lines, each row fetched once), in flight
-  // with the index loads; each wave then reads its head block's B operands
-  // with the K-read pattern (lane (c16, g) holds dims 32 S + 8 g .. + 8 of
-  // head 16 hb + c16), and the slots go back to the ring.
+  // ---- the first stage. The index loads go out first; the workgroup's Q (64
+  // head rows of 1152 bytes: two tiles' worth) follows into ring slots 2 and
+  // 3 with the tiles' own gather pattern and swizzle (whole cache lines, each
+  // row fetched once). Tiles 0 and 1 are gathered as soon as the keys are
+  // staged, while Q is still landing; then each wave reads its head block's B
+  // operands with the K-read pattern (lane (c16, g) holds dims 32 S + 8 g ..
+  // + 8 of head 16 hb + c16) by counted reads (a compiler-visible read of the
+  // ring would wait for the tile gathers too), and slots 2 and 3 return to
+  // the ring.
   if (tid < NH) floor_s[tid] = -INFINITY;  // read after the first stage's barrier
   bool pro_done = false;
   if (c0 < c1) {
+    const int st1 = min(c0 + KEYCAP, c1);
+    load_keys(c0, st1);
     const uint16_t* qrow0 = q + ((b * NH) * q_seq + qi) * DK;
     const int qstride = (int)(q_seq * ROWB);  // bytes between heads (q_seq < 256 here)
     const __amdgpu_buffer_rsrc_t qrsrc =
@@ -332,24 +337,36 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               qrsrc, (__attribute__((address_space(3))) void*)(ring + (2 + u) * TILE_BYTES + (block0 + i) * 1024), 16,
               (uint32_t)((32 * u + ld_row(i)) * qstride + ld_off(i)), 0, 0, 0);
-    // the index loads; the compiler's wait for them also covers the older Q loads
-    stage_sync(c0, min(c0 + KEYCAP, c1));
+    keys_to_lds(c0, st1);
+    lds_barrier();
+    stage_counts();
+    gather_offsets(0);
+    gather_issue(0);
+    gather_offsets(1);
+    gather_issue(1);
+    wait_tiles(std::integral_constant<int, 2>{});  // this wave's Q loads have landed (tiles 0, 1 in flight)
+    lds_barrier();                                 // and everyone's
     {
       // head 16 hb + c16 is row 16 (hb & 1) + c16 of slot 2 + (hb >> 1)
-      const lds_u8* qt = ring + (2 + (hb >> 1)) * TILE_BYTES + (hb & 1) * HALF_ROWS + (kbase_e - kh * HALF_ROWS);
-      const int odd = kbase_o - kbase_e;
+      const uint32_t qa_e = (uint32_t)(uintptr_t)(ring + (2 + (hb >> 1)) * TILE_BYTES + (hb & 1) * HALF_ROWS) +
+                            (uint32_t)(kbase_e - kh * HALF_ROWS);
+      const uint32_t qa_o = qa_e + (uint32_t)(kbase_o - kbase_e);
+      u32x4_l qraw[KSTEPS];
+      static_for<KSTEPS>([&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        qraw[S] = ds_read_b128_at<64 * S>((S & 1) ? qa_o : qa_e);
+      });
+      static_for<KSTEPS / 2>([&](auto pc) {
+        constexpr int P = decltype(pc)::value;
+        constexpr int LATER = KSTEPS - 2 * P - 2;
+        lgkm_wait_tied<(LATER > 15 ? 15 : LATER)>(qraw[2 * P], qraw[2 * P + 1]);
+      });
 #pragma unroll
-      for (int s = 0; s < KSTEPS; s++) {
-        const u32x4_l raw = *(const lds_u32x4*)(qt + 64 * s + ((s & 1) ? odd : 0));
-        qreg[s] = __builtin_bit_cast(bf16x8_l, raw);
-      }
+      for (int s = 0; s < KSTEPS; s++) qreg[s] = __builtin_bit_cast(bf16x8_l, qraw[s]);
     }
     lds_barrier();  // every wave has its Q: slots 2 and 3 return to the ring
-#pragma unroll
-    for (int p = 0; p < NSTAGE - 1; p++) {
-      gather_offsets(p);
-      gather_issue(p);
-    }
+    gather_offsets(2);
+    gather_issue(2);
     gather_offsets(NSTAGE - 1);
     pro_done = true;
   }
@@ -473,7 +490,10 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
       const int st1 = min(st0 + KEYCAP, c1);
       if (!pro_done) {
         __syncthreads();  // the previous stage's readers are done with keys_s / misc / the ring
-        stage_sync(st0, st1);
+        load_keys(st0, st1);
+        keys_to_lds(st0, st1);
+        lds_barrier();
+        stage_counts();
 #pragma unroll
         for (int p = 0; p < NSTAGE - 1; p++) {
           gather_offsets(p);
@@ -660,39 +680,117 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
     }
   }
 
-  // ---- error block: the finisher of each row records the row's first
-  // violation and counts itself toward the launch's last-arrival record
+  // ---- error block: this workgroup's first violation goes to the row's slot;
+  // the merge kernel that follows the launch records each row's first
+  // violation and finishes the launch's record
   if constexpr (FUSED) {
+    __syncthreads();  // every wave's LDS minimum is in
     if (tid == 0) {
-      unsigned long long k = *minkey_s;
-      bool finisher = true;
-      if (splits > 1) {
-        if (k != ~0ull) {
-          atomicMin(&row_key[row], k);
-          __threadfence();
-        }
-        finisher = atomicAdd(&row_done[row], 1u) == (unsigned)splits - 1;
-        if (finisher) {
-          row_done[row] = 0u;
-          k = atomicExch(&row_key[row], ~0ull);
-        }
-      }
-      if (finisher && k != ~0ull) {
-        const int64_t col = (int64_t)(k % (unsigned long long)(width + 1));
-        int cls = 6;
-        if (col < width) {
-          const int64_t v = load_index<I64>(idx, ibase + col);
-          const int64_t u = col > 0 ? load_index<I64>(idx, ibase + col - 1) : 0;
-          cls = column_class(col, v, u, bound);
-        }
-        atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
-        atomicMin((unsigned long long*)&eb->call_key, k);
-      }
-      if (finisher)
-        finish_launch<I64>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap, (unsigned)rows,
-                           reset != 0);
+      const unsigned long long k = *minkey_s;
+      if (k != ~0ull) atomicMin(&row_key[row], k);
     }
   }
+}
+
+// Log-sum-exp merge of the split partials (standard Attention page,
+// `attention_combine`; m in log2 units): M = max_j m_j and
+// y = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M). One 128-thread workgroup
+// per (row, head), each thread 4 channels; block i serves row i % rows, on
+// the XCD that wrote that row's partials. Each round loads 8 splits before
+// using any. With FIN (fused validation) the workgroup of head 0 of each row
+// then turns the row's first violation (the minimum the split workgroups left
+// in row_key) into its class bit and counts the row toward the launch's
+// record: the finish that would otherwise cost the attention launch a
+// device-wide round trip per workgroup at its end.
+template <bool FIN, bool I64>
+__global__ void __launch_bounds__(128)
+latent_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, uint16_t* __restrict__ y,
+                    int64_t rows, int64_t q_seq, int splits, ErrorBlock* __restrict__ eb,
+                    unsigned long long* __restrict__ row_key, const void* __restrict__ idx, int64_t width,
+                    const int32_t* __restrict__ valid_len, const int32_t* __restrict__ past_len,
+                    const int32_t* __restrict__ present_len, int64_t cur_len, int64_t cap, int reset) {
+  using namespace lhd;
+  constexpr int CH = 8;
+  const int64_t row = (int64_t)(blockIdx.x % (unsigned)rows);
+  const int head = (int)(blockIdx.x / (unsigned)rows);
+  const int64_t b = row / q_seq, qi = row - b * q_seq;
+  const int d = threadIdx.x * 4;
+  float M = -INFINITY, L = 0.0f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < splits; j0 += CH) {
+    float2 ml[CH];
+    float4 v[CH];
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+      const int64_t pr = (row * splits + j0 + j) * NH + head;
+      if (j0 + j < splits) {
+        ml[j] = *(const float2*)(part_ml + pr * 2);
+        v[j] = *(const float4*)(part_o + pr * DV + d);
+      } else {
+        ml[j] = make_float2(-INFINITY, 0.0f);
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < CH; j++) Mn = fmaxf(Mn, ml[j].x);
+    if (Mn == -INFINITY) continue;  // no key in these splits yet
+    const float r = M == -INFINITY ? 0.0f : exp2f(M - Mn);
+    L *= r;
+#pragma unroll
+    for (int e = 0; e < 4; e++) acc[e] *= r;
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+      const float w = ml[j].x == -INFINITY ? 0.0f : exp2f(ml[j].x - Mn);
+      L += ml[j].y * w;
+      acc[0] += v[j].x * w;
+      acc[1] += v[j].y * w;
+      acc[2] += v[j].z * w;
+      acc[3] += v[j].w * w;
+    }
+    M = Mn;
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  *(uint2*)(y + ((b * NH + head) * q_seq + qi) * DV + d) =
+      make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+
+  if constexpr (FIN) {
+    if (head != 0 || threadIdx.x != 0) return;
+    const unsigned long long k = atomicExch(&row_key[row], ~0ull);
+    if (k != ~0ull) {
+      const int64_t col = (int64_t)(k % (unsigned long long)(width + 1));
+      int cls = 6;
+      if (col < width) {
+        int64_t bound = past_len ? (int64_t)past_len[b] + cur_len : (valid_len ? (int64_t)valid_len[b] : cap);
+        bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
+        const int64_t v = load_index<I64>(idx, row * width + col);
+        const int64_t u = col > 0 ? load_index<I64>(idx, row * width + col - 1) : 0;
+        cls = column_class(col, v, u, bound);
+      }
+      atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
+      atomicMin((unsigned long long*)&eb->call_key, k);
+    }
+    finish_launch<I64>(eb, idx, width, q_seq, q_seq, past_len ? present_len : valid_len, cap, (unsigned)rows,
+                       reset != 0);
+  }
+}
+
+static sa_status launch_latent_merge(sparse_attn_ctx* c, const FwdArgs& a, int64_t rows, int splits, bool fused,
+                                     const AppendArgs* app) {
+  const dim3 grid((unsigned)(rows * lhd::NH)), block(lhd::DV / 4);
+  const int32_t* plen = app ? app->past_len : nullptr;
+  int32_t* prlen = app ? app->present_len : nullptr;
+  const int64_t clen = app ? app->cur_len : 0;
+  const int reset = app ? app->reset : 0;
+#define SA_MERGE(F, I)                                                                                     \
+  hipLaunchKernelGGL((latent_merge_kernel<F, I>), grid, block, 0, c->stream, c->partial_o, c->partial_ml,      \
+                     (uint16_t*)a.y, rows, a.q_seq, splits, c->err, c->row_key, a.idx, a.width, a.valid_len, \
+                     plen, prlen, clen, a.cap, reset)
+  if (!fused) SA_MERGE(false, false);
+  else if (a.idx64) SA_MERGE(true, true);
+  else SA_MERGE(true, false);
+#undef SA_MERGE
+  return check_hip(c, hipGetLastError(), "forward (merge)");
 }
 
 static bool g_lhd_attr[12] = {};
@@ -759,7 +857,7 @@ sa_status launch_forward_latent_decode(sparse_attn_ctx* c, const FwdArgs& a, int
   prof_end(c);
   sa_status s = check_hip(c, hipGetLastError(), "forward (latent decode)");
   if (s != SA_OK || splits == 1) return s;
-  return launch_mla_combine(c, rows, a.q_seq, splits, (uint16_t*)a.y);
+  return launch_latent_merge(c, a, rows, splits, fused, app);
 }
 
 }  // namespace sa
