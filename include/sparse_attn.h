@@ -331,10 +331,13 @@ sa_status sparse_attn_step(sparse_attn_ctx* ctx, const void* q, int64_t batch, i
  *   selected      [B, out_heads, S, K] int32 out; every index-head row gets the
  *                 same selection (as the pages replicate it); 1 <= K <= 2048
  *   workspace     device scratch of sparse_attn_csa_index_workspace_bytes(B, S, H,
- *                 key_cap) bytes, owned by the caller (the scores and the
- *                 finalized queries); contents on return are unspecified
- * Exact score ties, which the CPU page rejects, are ordered by ascending
- * record. Host errors: SA_E_ARG (NULL pointer, size < 1), SA_E_UNSUPPORTED
+ *                 key_cap) bytes, owned by the caller (the scores, the
+ *                 finalized queries and their block scale exponents);
+ *                 contents on return are unspecified
+ * Each head dot equals the CPU page's ascending fp32 fold for any block
+ * scales: the matrix-core dot is used where no partial sum can round, the
+ * fold itself elsewhere. Exact score ties, which the CPU page rejects, are
+ * ordered by ascending record. Host errors: SA_E_ARG (NULL pointer, size < 1), SA_E_UNSUPPORTED
  * (H, K or key_cap out of range). Device: SA_ERR_CSA_GEOMETRY when total < S
  * (nothing written); SA_ERR_INDEX_NONFINITE when a score is not finite (it is
  * still ranked, by the fp32 total order). Asynchronous and capturable. */

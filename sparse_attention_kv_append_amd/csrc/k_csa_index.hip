@@ -64,8 +64,8 @@ __device__ __forceinline__ float bf16_round(float x) { return bf16_to_f32(f32_to
 
 // lane l of the wave holds elements 2l, 2l+1 of one head's 128 values
 __global__ void __launch_bounds__(256)
-csa_index_finalize_kernel(const float* __restrict__ iq, uint16_t* __restrict__ qf, int64_t rows, int H,
-                          int S, const int64_t* __restrict__ total_ptr) {
+csa_index_finalize_kernel(const float* __restrict__ iq, uint16_t* __restrict__ qf, uint8_t* __restrict__ qe,
+                          int64_t rows, int H, int S, const int64_t* __restrict__ total_ptr) {
   using namespace cx;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, s, h) row
   if (wid >= rows) return;
@@ -125,9 +125,56 @@ csa_index_finalize_kernel(const float* __restrict__ iq, uint16_t* __restrict__ q
   const float q1 = copysignf(e2m1_round(fabsf(v1) * inv), v1) * sc;
   const uint32_t packed = (uint32_t)f32_to_bf16_rne(q0) | ((uint32_t)f32_to_bf16_rne(q1) << 16);
   ((uint32_t*)(qf + wid * D))[lane] = packed;
+  if ((lane & 15) == 0) qe[wid * 4 + (lane >> 4)] = (uint8_t)e;  // the block's scale exponent (E8M0 byte)
 }
 
 // ---------------------------------------------------------------- score
+
+// Exactness of a head dot taken by the matrix cores. With biased scale
+// exponents q_c (query block c, from the finalize) and k_c (key block c), the
+// products of block c are multiples of 2^(q_c + k_c - 256 - 2) and at most 36
+// times 2^(q_c + k_c - 254); every partial sum of the 128 products is then an
+// exact fp32 number (so any order of summation gives the same value) when
+// each factor is normal (2 <= q_c, k_c <= 252), no product or sum leaves the
+// normal range (q_c + k_c - 254 in [-124, 115]) and the block exponents span
+// at most 9 (4608 * 2^9 * 4 < 2^24). qr packs the query's lowest and highest
+// block exponent; the key's come in klo, khi; the per-block test runs only
+// when the ranges alone do not settle it.
+__device__ __forceinline__ bool dot_is_exact(int qr, int klo, int khi, uint32_t qx, const uint8_t* kk) {
+  const int qlo = qr & 255, qhi = qr >> 8;
+  if (qlo < 2 || qhi > 252 || klo < 2 || khi > 252) return false;
+  const int lo = qlo + klo - 254, hi = qhi + khi - 254;
+  if (lo >= -124 && hi <= 115 && hi - lo <= 9) return true;
+  int elo = 1 << 20, ehi = -(1 << 20);
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const int e = (int)((qx >> (8 * c)) & 255u) + (int)kk[17 * c] - 254;
+    elo = min(elo, e);
+    ehi = max(ehi, e);
+  }
+  return elo >= -124 && ehi <= 115 && ehi - elo <= 9;
+}
+
+// The head dot in the pages' order: q (bf16, exact in fp32) times the
+// decoded key value (E2M1 magnitude times the block's E8M0 scale, 255 = NaN),
+// each product rounded, folded in ascending dimension order.
+__device__ __noinline__ float ordered_dot(const uint16_t* __restrict__ qh, const uint8_t* kk) {
+  const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  float acc = 0.0f;
+  for (int c = 0; c < 4; c++) {
+    const uint32_t e = kk[17 * c];
+    const float sc = e == 255u ? __uint_as_float(0x7fc00000u) : (e ? __uint_as_float(e << 23) : 5.877471754e-39f);
+    for (int i = 0; i < 32; i++) {
+      const uint32_t code = ((uint32_t)kk[17 * c + 1 + (i >> 1)] >> (4 * (i & 1))) & 15u;
+      const float m = mag[code & 7u];
+      const float kv = ((code & 8u) ? -m : m) * sc;
+      const float prod = bf16_to_f32(qh[32 * c + i]) * kv;
+      acc = acc + prod;
+    }
+  }
+  return acc;
+}
+
 
 // A workgroup scores RC records of one (batch, query) in passes of RB: the
 // pass's keys (68 B each, contiguous) are copied to LDS from registers loaded
@@ -136,9 +183,9 @@ csa_index_finalize_kernel(const float* __restrict__ iq, uint16_t* __restrict__ q
 // 0..RB-1 take the head sums (one record each).
 template <int HT>
 __global__ void __launch_bounds__(256)
-csa_index_score_kernel(const uint16_t* __restrict__ qf, const float* __restrict__ iw,
-                       const uint8_t* __restrict__ keys, float* __restrict__ scores, int S,
-                       int64_t kcap, const int64_t* __restrict__ total_ptr, ErrorBlock* __restrict__ eb) {
+csa_index_score_kernel(const uint16_t* __restrict__ qf, const uint8_t* __restrict__ qe,
+                       const float* __restrict__ iw, const uint8_t* __restrict__ keys, float* __restrict__ scores,
+                       int S, int64_t kcap, const int64_t* __restrict__ total_ptr, ErrorBlock* __restrict__ eb) {
   using namespace cx;
   constexpr int H = 16 * HT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -170,6 +217,21 @@ csa_index_score_kernel(const uint16_t* __restrict__ qf, const float* __restrict_
 
   uint8_t* kl = smem;                          // RB keys, 68 B each
   float* dt = (float*)(smem + RB * KB);        // [RB][DSTR] dot products
+  // per head: the query blocks' scale exponents (4 bytes) and their range
+  uint32_t* qx = (uint32_t*)(smem + RB * KB + RB * DSTR * 4);
+  int* qr = (int*)(qx + HMAX);
+  if (tid < H) {
+    const uint32_t x = *(const uint32_t*)(qe + (row * H + tid) * 4);
+    int lo = 255, hi = 0;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const int e = (int)((x >> (8 * c)) & 255u);
+      lo = min(lo, e);
+      hi = max(hi, e);
+    }
+    qx[tid] = x;
+    qr[tid] = lo | (hi << 8);
+  }  // read after the first pass's barriers
   const uint32_t* kb = (const uint32_t*)(keys + (b * kcap) * KB);
   constexpr int KW = RB * KB / 4;              // dwords of a pass's keys
   constexpr int KL = (KW + 255) / 256;         // loads per thread
@@ -239,13 +301,27 @@ csa_index_score_kernel(const uint16_t* __restrict__ qf, const float* __restrict_
     const int64_t r = r0 + tid;
     if (tid < RB && r < c1) {
       const f32x4_l* d4 = (const f32x4_l*)(dt + tid * DSTR);
+      const uint8_t* kk = kl + tid * KB;
+      int klo = 255, khi = 0;
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        klo = min(klo, (int)kk[17 * c]);
+        khi = max(khi, (int)kk[17 * c]);
+      }
       float score = 0.0f;
 #pragma unroll
       for (int h4 = 0; h4 < H / 4; h4++) {
         const f32x4_l x4 = d4[h4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const float x = x4[j];
+          float x = x4[j];
+          // The matrix dot equals the pages' ascending fp32 fold when no
+          // partial sum rounds: every factor a normal number and the block
+          // products within 2^9 of each other. Otherwise the fold is redone
+          // in the pages' order (rare: keys and queries of widely spread
+          // block scales).
+          const int h = 4 * h4 + j;
+          if (!dot_is_exact(qr[h], klo, khi, qx[h], kk)) x = ordered_dot(qrow + (int64_t)h * D, kk);
           const float relu = x > 0.0f ? x : 0.0f;
           const float t0 = relu * wv[4 * h4 + j];
           const float t1 = t0 * ws;
@@ -441,9 +517,10 @@ csa_index_select_kernel(const float* __restrict__ scores, int32_t* __restrict__ 
 }
 
 size_t csa_index_workspace_bytes(int64_t rows, int64_t H, int64_t kcap) {
-  // scores fp32 [rows][kcap], then the finalized queries bf16 [rows][H][128]
+  // scores fp32 [rows][kcap], then the finalized queries bf16 [rows][H][128],
+  // then their block scale exponents u8 [rows][H][4]
   const size_t sb = ((size_t)rows * (size_t)kcap * 4 + 255) & ~(size_t)255;
-  return sb + (size_t)rows * (size_t)H * cx::D * 2;
+  return sb + (size_t)rows * (size_t)H * cx::D * 2 + (size_t)rows * (size_t)H * 4;
 }
 
 sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
@@ -452,7 +529,8 @@ sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
   float* scores = (float*)a.workspace;
   const size_t sb = ((size_t)rows * (size_t)a.key_cap * 4 + 255) & ~(size_t)255;
   uint16_t* qf = (uint16_t*)((uint8_t*)a.workspace + sb);
-  const size_t score_lds = (size_t)RB * KB + (size_t)RB * DSTR * 4;
+  uint8_t* qe = (uint8_t*)(qf + (size_t)rows * (size_t)a.heads * D);
+  const size_t score_lds = (size_t)RB * KB + (size_t)RB * DSTR * 4 + (size_t)HMAX * 8;
   const size_t select_lds = (size_t)64 * 4 + (size_t)KMAX * 8;
   const void* score_fns[4] = {(const void*)csa_index_score_kernel<1>, (const void*)csa_index_score_kernel<2>,
                               (const void*)csa_index_score_kernel<3>, (const void*)csa_index_score_kernel<4>};
@@ -469,13 +547,13 @@ sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
   }
   const int64_t hrows = rows * a.heads;
   hipLaunchKernelGGL(csa_index_finalize_kernel, dim3((unsigned)((hrows + 3) / 4)), dim3(256), 0, c->stream,
-                     a.iq, qf, hrows, (int)a.heads, (int)a.q_seq, a.total);
+                     a.iq, qf, qe, hrows, (int)a.heads, (int)a.q_seq, a.total);
   sa_status st = check_hip(c, hipGetLastError(), "csa index finalize");
   if (st != SA_OK) return st;
   prof_begin(c);
   const dim3 sgrid((unsigned)((a.key_cap + RC - 1) / RC), (unsigned)rows);
 #define SA_IDX_SCORE(HTV)                                                                                       \
-  hipLaunchKernelGGL(csa_index_score_kernel<HTV>, sgrid, dim3(256), score_lds, c->stream, qf, a.iw, a.keys, scores, \
+  hipLaunchKernelGGL(csa_index_score_kernel<HTV>, sgrid, dim3(256), score_lds, c->stream, qf, qe, a.iw, a.keys, scores, \
                      (int)a.q_seq, a.key_cap, a.total, c->err)
   switch (a.heads / 16) {
     case 1: SA_IDX_SCORE(1); break;

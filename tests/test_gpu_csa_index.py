@@ -98,6 +98,53 @@ def test_index_select_matches_oracle(ctx, kw):
     assert same == w.batch * w.seq
 
 
+def run_and_compare(ctx, w, inp):
+    osel, flags, scores = oracle.csa_index_select(inp["index_query"], inp["index_weight"], inp["index_keys"],
+                                                  w.total, w.topk, with_scores=True)
+    gsel, word, msg, gscores = run_gpu(ctx, inp, w.total, w.topk, w.out_heads)
+    # exact ties (many keys of one dominant block score 0 over every head) are
+    # ordered by ascending record on both sides
+    assert (flags & ~oracle.SEL_TIE) == 0 and word == 0, (flags, msg)
+    for b in range(w.batch):
+        for s in range(w.seq):
+            n = min((w.total - w.seq + s + 1) // 4, w.key_cap)
+            np.testing.assert_array_equal(gscores[b, s, :n], scores[b, s, :n], err_msg=f"scores of row {(b, s)}")
+            np.testing.assert_array_equal(gsel[b, 0, s], osel[b, s], err_msg=f"selection of row {(b, s)}")
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(heads=64, key_cap=1500, total=5000, topk=512)])
+def test_index_select_on_keys_of_uneven_blocks_quantized_by_the_oracle(ctx, kw):
+    """Keys from the oracle's own FP4 quantizer on data whose 32-dim blocks
+    differ in magnitude by up to 2^24: their scale bytes spread far beyond a
+    range where the matrix dot is exact, so the ordered fold decides."""
+    w = W.CSA_INDEX_WORKLOADS["csa_index_small"].scaled(**kw)
+    inp = W.make_csa_index_numpy(w)
+    rng = np.random.default_rng(77)
+    raw = rng.standard_normal((w.batch, w.key_cap, 128)).astype(np.float32)
+    raw *= np.repeat(np.exp2(rng.integers(-12, 13, (w.batch, w.key_cap, 4))).astype(np.float32), 32, axis=-1)
+    inp["index_keys"] = oracle.fp4_pack_keys(raw)
+    sb = inp["index_keys"][:, :, 0::17].astype(int)
+    assert (sb.max(-1) - sb.min(-1)).max() >= 16  # blocks of one key far apart
+    banner(f"csa index, oracle-quantized uneven keys {w}")
+    run_and_compare(ctx, w, inp)
+
+
+def test_index_select_on_planted_wide_scale_bytes(ctx):
+    """Random codes with block scale bytes planted over 0..200 within one key
+    (subnormal and zero-exponent key values among them): bit-exact scores
+    and selection."""
+    w = W.CSA_INDEX_WORKLOADS["csa_index_small"].scaled(heads=32, key_cap=700, total=2400, topk=96)
+    inp = W.make_csa_index_numpy(w)
+    rng = np.random.default_rng(78)
+    keys = inp["index_keys"]
+    keys[:, :, 0::17] = rng.integers(90, 170, keys[:, :, 0::17].shape, dtype=np.uint8)
+    keys[:, ::7, 0] = 0                        # 2^-127: subnormal key values
+    keys[:, 3::11, 17] = rng.integers(1, 12, keys[:, 3::11, 17].shape, dtype=np.uint8)
+    keys[:, 5::13, 51] = 200
+    banner(f"csa index, planted wide scale bytes {w}")
+    run_and_compare(ctx, w, inp)
+
+
 def test_index_select_geometry_and_nonfinite(ctx):
     import sparse_attention_kv_append_amd as sa
     w = W.CSA_INDEX_WORKLOADS["csa_index_small"]
