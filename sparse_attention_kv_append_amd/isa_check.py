@@ -74,6 +74,7 @@ class _Insn:
     line: int
     op: str
     args: str
+    asm: bool = False  # written as inline assembly (the compiler does not know its effects)
 
 
 @dataclass
@@ -111,7 +112,14 @@ def _blocks(body):
         blocks.append(nb)
         cur = nb
 
+    in_asm = False
     for no, raw in body:
+        if ";;#ASMSTART" in raw:
+            in_asm = True
+            continue
+        if ";;#ASMEND" in raw:
+            in_asm = False
+            continue
         m = _LABEL.match(raw)
         if m:
             prev = cur
@@ -128,7 +136,7 @@ def _blocks(body):
         if ends:  # code after an unconditional end starts a block of its own
             new(f"<after {no}>")
             ends = False
-        cur.insns.append(_Insn(no, op, args))
+        cur.insns.append(_Insn(no, op, args, in_asm))
         if op == "s_branch":
             cur.succ.append((None, args.strip()))
             ends = True
@@ -242,6 +250,9 @@ def _wait_states(insn: _Insn) -> int:
 
 def _step_mfma(state: dict, insn: _Insn, hazards: list | None, fname: str):
     """Transfer one instruction: state maps a register to (slots still owed, line of its matrix write)."""
+    if insn.op in ("s_swappc_b64", "s_call_b64"):
+        state.clear()  # the call and the callee's prologue are far more than any padding
+        return
     if state and hazards is not None:
         if insn.op.startswith("v_mfma"):
             ops = [o.strip() for o in insn.args.split(",")]
@@ -277,7 +288,13 @@ def _merge_mfma(a: dict, b: dict) -> dict:
 
 
 def _step(state: dict, insn: _Insn, hazards: list | None, fname: str):
-    """Transfer one instruction: state maps line -> (later LDS ops, dest regs)."""
+    """Transfer one instruction: state maps line -> (later LDS ops, dest regs).
+    Only reads written as inline assembly are tracked (the compiler waits for
+    its own), but every LDS operation counts toward the later ones. A call
+    waits for everything: a callee starts with a full s_waitcnt."""
+    if insn.op in ("s_swappc_b64", "s_call_b64"):
+        state.clear()
+        return
     if insn.op == "s_waitcnt":
         n = _lgkm_wait(insn.args)
         if n is not None:
@@ -303,7 +320,7 @@ def _step(state: dict, insn: _Insn, hazards: list | None, fname: str):
                 state[k] = (min(later + 1, _CAP), regs)
             else:
                 del state[k]
-        if dest:
+        if dest and insn.asm:
             state[insn.line] = (0, dest)
 
 

@@ -20,8 +20,17 @@ from sparse_attention_kv_append_amd import isa_check as ic
 
 
 def wrap(body):
-    return "_Z4testv:\n" + "\n".join("\t" + ln if not ln.startswith(".") else ln for ln in body) + \
-        "\n.Lfunc_end0:\n"
+    """A kernel listing; every LDS read in it is marked as inline assembly
+    (the only reads the checker tracks: the compiler waits for its own)."""
+    out = []
+    for ln in body:
+        if ln.startswith("."):
+            out.append(ln)
+        elif ln.startswith("ds_read"):
+            out += ["\t;;#ASMSTART", "\t" + ln, "\t;;#ASMEND"]
+        else:
+            out.append("\t" + ln)
+    return "_Z4testv:\n" + "\n".join(out) + "\n.Lfunc_end0:\n"
 
 
 def test_copy_before_the_wait_is_flagged():
@@ -104,6 +113,15 @@ def test_flag_guarded_paths_that_cannot_both_run_are_kept_apart():
     # without the flag the same join is a hazard
     asm2 = asm.replace("s_mov_b64 s[8:9], -1", "s_mov_b64 s[8:9], s[2:3]")
     assert len(ic.check_asm(asm2)) == 1
+
+
+def test_compiler_reads_and_calls_are_left_to_the_compiler():
+    # a read the compiler issued itself (no inline-assembly markers) is its
+    # business; a call waits for everything at the callee's entry
+    asm = ("_Z4testv:\n\tds_read_b128 v[4:7], v1\n\tv_mov_b32_e32 v20, v4\n"
+           "\t;;#ASMSTART\n\tds_read_b128 v[8:11], v1\n\t;;#ASMEND\n"
+           "\ts_swappc_b64 s[30:31], s[0:1]\n\tv_mov_b32_e32 v8, v0\n\ts_endpgm\n.Lfunc_end0:\n")
+    assert ic.check_asm(asm) == []
 
 
 def test_matrix_result_read_too_soon_is_flagged_across_a_branch():
