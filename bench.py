@@ -56,6 +56,12 @@ def parse():
     p.add_argument("--rotate", type=int, default=8, help="independent (query, index) sets")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
+    p.add_argument("--no-also", action="store_true",
+                   help="default workload only: skip the decode_fp8 / prefill_bf16 figures and the concat copy")
+    p.add_argument("--also-steps", type=int, default=20, help="steps timed for each extra workload")
+    p.add_argument("--stats-digest", metavar="KERNEL_STATS_CSV",
+                   help="turn a rocprofv3 --kernel-trace --stats CSV of this script into the committed "
+                        "summary of the workload's main kernel")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--pmc-run", action="store_true",
                    help="counter pass: a 256 MiB device copy (calibration), then W + K eager steps")
@@ -80,6 +86,16 @@ KERNEL_SOURCES = {
     "csa_index_score_kernel": ["k_csa_index.hip", "sa_internal.h", "sa_mfma_dev.h"],
 }
 CALIB_BYTES = 256 << 20
+
+
+def cpu_threads():
+    """Threads of the CPU baseline: the host's CPUs, capped by the CPU share the
+    environment grants (OMP_NUM_THREADS, set on shared GPU hosts)."""
+    n = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return n
 
 
 def source_hash(*names):
@@ -234,8 +250,8 @@ class Setup:
                                else "reset_error_async + kv_append + forward"),
                 "step_hbm_GBps": self.step_bytes() / (ms_per_step / 1e3) / 1e9}
 
-    def cpu_baseline(self, target_s):
-        return cpu_baseline(self, target_s)
+    def cpu_baseline(self, target_s, threads=None):
+        return cpu_baseline(self, target_s, threads)
 
 
 class CapacitySetup(Setup):
@@ -351,7 +367,7 @@ class CapacitySetup(Setup):
         on batch entries taken in order until about target_s seconds of oracle
         time; only the oracle calls are timed."""
         w = self.w
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = cpu_threads()
         n, t, done = 0, 0.0, 0
         while t < target_s and done < 4 * w.batch:
             b = done % w.batch
@@ -361,7 +377,8 @@ class CapacitySetup(Setup):
             t += time.perf_counter() - t0
             n += int((inp["indices"] >= 0).sum())
             done += 1
-        return {"value": n / t, "unit": "selected tokens/s", "cores": threads, "kind": "oracle",
+        return {"value": n / t, "unit": "selected tokens/s", "cores": threads, "host_cpus": os.cpu_count(),
+                "kind": "oracle",
                 "sample": f"{done} batch entries (in order, cycling over {w.batch}) of the same workload, "
                           f"all {w.hq} heads, {n} selected keys, {t:.1f} s of oracle time"}
 
@@ -517,7 +534,7 @@ class CsaSetup:
         repeated until the target time is reached."""
         import threading
         w = self.w
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = cpu_threads()
         nb = min(w.batch, threads)
         inputs = self.oracle_inputs(list(range(nb)))
         ndense = sum(self._dense())
@@ -536,7 +553,8 @@ class CsaSetup:
         while total_t < target_s and reps < 200:
             total_t += run()
             reps += 1
-        return {"value": cands * reps / total_t, "unit": "candidates/s", "cores": nb, "kind": "oracle",
+        return {"value": cands * reps / total_t, "unit": "candidates/s", "cores": nb,
+                "host_cpus": os.cpu_count(), "kind": "oracle",
                 "sample": f"the first {nb} (batch, query) rows of the same workload x {reps}, one thread each, "
                           f"all {w.heads} heads, {cands * reps} candidates, {total_t:.1f} s of oracle time"}
 
@@ -637,7 +655,7 @@ class CsaIndexSetup:
 
         import oracle
         w = self.w
-        threads = max(1, min(16, os.cpu_count() or 1))
+        threads = cpu_threads()
         nb = min(w.batch, threads)
         inputs = [self.oracle_inputs(b) for b in range(nb)]
 
@@ -655,7 +673,8 @@ class CsaIndexSetup:
             total_t += time.perf_counter() - t0
             reps += 1
         recs = nb * sum(self._n()) * reps
-        return {"value": recs / total_t, "unit": "records scored/s", "cores": nb, "kind": "oracle",
+        return {"value": recs / total_t, "unit": "records scored/s", "cores": nb,
+                "host_cpus": os.cpu_count(), "kind": "oracle",
                 "sample": f"the first {nb} (batch, query) rows of the same workload x {reps}, one thread each, "
                           f"all {w.heads} index heads, {recs} records scored and ranked, {total_t:.1f} s"}
 
@@ -864,12 +883,12 @@ def oracle_row(setup, inp, threads):
     return y[0, :, 0, :]
 
 
-def cpu_baseline(setup, target_s):
+def cpu_baseline(setup, target_s, threads=None):
     """The oracle (unchanged) on a bounded sample: the first rows of the same
     workload, each over a compact cache of its selected keys. Only the oracle
     calls are timed, not the input preparation."""
     w = setup.w
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = threads or cpu_threads()
 
     def run(nrows_b):
         rows = [(rb // w.q_seq, rb % w.q_seq) for rb in range(nrows_b)]
@@ -895,15 +914,203 @@ def cpu_baseline(setup, target_s):
             dn, dt = run(nb)
             n, t = n + dn, t + dt
     what = f"all {total_rows}" if nb == total_rows else f"first {nb} of {total_rows}"
-    return {"value": n / t, "unit": "selected tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": n / t, "unit": "selected tokens/s", "cores": threads, "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{what} (batch, query) rows of the same workload x {reps}, all {w.hq} heads, "
                       f"{n} selected keys, {t:.1f} s of oracle time"}
+
+
+def stats_file(setup):
+    return PROFILES / f"{kernel_name(setup)}_{setup.name}_stats.md"
+
+
+def stats_for(setup):
+    """The main kernel's average duration in the committed rocprofv3 summary of
+    this workload, if that summary was taken on the current kernel source."""
+    f = stats_file(setup)
+    if not f.exists():
+        return None
+    text = f.read_text()
+    name = kernel_name(setup)
+    if f"source hash: {source_hash(*KERNEL_SOURCES[name])}" not in text:
+        return None
+    best = None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) > 4 and name in cells[1]:
+            calls, avg = int(cells[2]), float(cells[3])
+            if best is None or calls > best[0]:
+                best = (calls, avg)
+    if best is None:
+        return None
+    return {"file": str(f.relative_to(ROOT)), "avg_us": best[1]}
+
+
+def stats_digest(args):
+    """A committed summary of a rocprofv3 --kernel-trace --stats run of this
+    script (its kernel_stats.csv), with the source hash of the main kernel."""
+    import csv
+    s_name = args.workload
+    rows = list(csv.DictReader(open(args.stats_digest)))
+    mains = [r["Name"] for r in rows if any(n in r["Name"] for n in KERNEL_SOURCES)]
+    assert mains, "no main kernel in the CSV"
+    main = max((r for r in rows if r["Name"] in mains), key=lambda r: int(r["Calls"]))["Name"]
+    name = next(n for n in KERNEL_SOURCES if n in main)
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python3 bench.py "
+           f"--workload {s_name} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline --no-also")
+    out = [f"# rocprofv3 kernel statistics: {s_name}", "",
+           "Command (run from the repository root on one MI355X), then "
+           f"`python3 bench.py --workload {s_name} --stats-digest <dir>/run_kernel_stats.csv`:", "",
+           "```", cmd, "```", "",
+           f"main kernel: `{name}`; sources {', '.join(KERNEL_SOURCES[name])}; "
+           f"source hash: {source_hash(*KERNEL_SOURCES[name])}", "",
+           "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        n = r["Name"]
+        short = n.split("(")[0] if ("sa::" in n or "__amd" in n) else n.split("<")[0] + "<...>"
+        out.append(f"| `{short[:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    PROFILES.mkdir(exist_ok=True)
+    f = PROFILES / f"{name}_{s_name}_stats.md"
+    f.write_text("\n".join(out) + "\n")
+    print(f"wrote {f}")
+
+
+def measure(s, steps, warmup, use_graph):
+    """W warmup steps, then exactly `steps` steps between events: graph replays
+    of one captured pass over the rotation sets (and one more graph of the
+    remaining sets when `steps` is not a multiple of their number), then an
+    eager pass of the same steps with the main kernel's dispatch-stamped
+    events. Returns (ms per step, main kernel seconds per launch)."""
+    torch = s.torch
+    for i in range(warmup):
+        s.step(i)
+    torch.cuda.synchronize()
+    word, _, msg = s.ctx.read_error()
+    assert word == 0, msg
+    nset = len(s.idxs)
+    full, rem = divmod(steps, nset)
+    graphs = {}
+    if use_graph:
+        for n in {nset if full else 0, rem} - {0}:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    s.step(i)
+            graphs[n] = g
+        for g in graphs.values():
+            g.replay()
+        torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if use_graph:
+        for _ in range(full):
+            graphs[nset].replay()
+        if rem:
+            graphs[rem].replay()
+    else:
+        for i in range(steps):
+            s.step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / steps
+    word, _, msg = s.ctx.read_error()
+    assert word == 0, msg
+    s.ctx.profile_enable(steps)
+    for i in range(steps):
+        s.step(i)
+    k_ms, k_n = s.ctx.profile_read()
+    s.ctx.profile_enable(0)
+    return ms_per_step, k_ms / max(k_n, 1) / 1e3
+
+
+def kernel_record(s, k_avg_s):
+    kw = s.kernel_work()
+    bound, peak, unit, achieved = s.roofline(kw, k_avg_s)
+    rec = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+           "traffic": counters_for(s), "kernel": kernel_name(s), "kernel_avg_us": k_avg_s * 1e6,
+           "algorithmic_bytes_per_launch": kw["bytes"], "algorithmic_flops_per_launch": kw["flops"]}
+    prof = stats_for(s)
+    if prof:
+        _, _, _, a_prof = s.roofline(kw, prof["avg_us"] / 1e6)
+        prof["frac"] = a_prof / peak
+        rec["profile"] = prof
+    return rec
+
+
+def concat_append_figure(s, reps=5):
+    """kv_append in concat mode over the workload's whole cache: the past copied
+    into a fresh present plus the current rows, timed with events."""
+    torch, w = s.torch, s.w
+    if s.fp8 or w.layout != s.W.LAYOUT_SHARED_LATENT:
+        return None
+    B, cap = w.batch, w.cap
+    past = s.k[:, :, :w.past]
+    present = torch.empty_like(s.k)
+    plen = torch.full((B,), w.past, dtype=torch.int32, device="cuda")
+    vlen = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    call = lambda: s.ctx.kv_append(B, past, None, w.past, plen, s.cur_k, None, w.cur, present, None, cap,
+                                   present_len=vlen)
+    call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    row = w.dk * 2
+    nbytes = B * (w.past * row * 2 + w.cur * row * 2)   # past read + written, current read + written
+    del present
+    return {"what": f"kv_append concat: {B} x {w.past} past rows of {row} B copied into a fresh present "
+                    f"+ {w.cur} current row", "bytes": nbytes, "us": us,
+            "GBps": nbytes / (us / 1e6) / 1e9, "frac": nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS}
+
+
+def c0_single_thread(target_s=1.0):
+    """The oracle on the tiny fp32 workload (append + validation + forward), one
+    thread, repeated until about target_s seconds."""
+    import oracle
+    import sa_workloads as W
+    w = W.WORKLOADS["tiny_f32"]
+    inp = W.make_numpy(w)
+    n, t, reps = 0, 0.0, 0
+    while t < target_s and reps < 100000:
+        t0 = time.perf_counter()
+        pk = oracle.kv_append(inp["past_k"].copy(), inp["past_len"], inp["cur_k"])
+        pv = oracle.kv_append(inp["past_v"].copy(), inp["past_len"], inp["cur_v"])
+        oracle.forward(inp["q"], pk, pv, inp["indices"], q_dtype=w.dtype, cache_fmt=w.dtype,
+                       kv_layout=w.layout, hkv=w.hkv, dv=w.dv, scale=w.scale, softcap=w.softcap, threads=1)
+        t += time.perf_counter() - t0
+        n += int((inp["indices"] >= 0).sum())
+        reps += 1
+    return {"value": n / t, "unit": "selected tokens/s", "cores": 1, "workload": "tiny_f32",
+            "sample": f"the whole tiny_f32 workload (append, forward) x {reps}, {n} selected keys, {t:.2f} s"}
+
+
+def also_record(name, args):
+    """Step time, main-kernel time, roofline and traffic of another workload, for
+    the default line."""
+    import torch
+    s = make_setup(name, args.rotate)
+    ms, k_avg = measure(s, args.also_steps, 4, not args.no_graph)
+    rec = {"workload": name, "ms_per_step": ms, "steps": args.also_steps, "splits": s.splits,
+           "roofline": kernel_record(s, k_avg)}
+    s.ctx.destroy()
+    del s
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
     args = parse()
     if args.digest:
         digest(args)
+        return
+    if args.stats_digest:
+        stats_digest(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -917,51 +1124,11 @@ def main():
     print(f"bench: workload {args.workload}, building inputs", file=sys.stderr, flush=True)
     s = make_setup(args.workload, args.rotate)
     print(f"bench: path {kernel_name(s)} splits {s.splits}", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        s.step(i)
-    torch.cuda.synchronize()
-    word, _, msg = s.ctx.read_error()
-    assert word == 0, msg
-
-    nset = len(s.idxs)
     use_graph = not args.no_graph
     steps = args.steps
-    if use_graph:
-        steps = max(nset, (steps // nset) * nset)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(nset):
-                s.step(i)
-        g.replay()
-        torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    if use_graph:
-        for _ in range(steps // nset):
-            g.replay()
-    else:
-        for i in range(steps):
-            s.step(i)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    word, _, msg = s.ctx.read_error()
-    assert word == 0, msg
-    ms_per_step = ms_total / steps
-
-    # eager pass with the library's event pair around the main kernel
-    s.ctx.profile_enable(steps)
-    for i in range(steps):
-        s.step(i)
-    k_ms, k_n = s.ctx.profile_read()
-    s.ctx.profile_enable(0)
-    k_avg_s = k_ms / max(k_n, 1) / 1e3
-
+    ms_per_step, k_avg_s = measure(s, steps, args.warmup, use_graph)
+    nset = len(s.idxs)
     tokens = s.tokens_per_step()
-    kw = s.kernel_work()
-    bound, peak, unit, achieved = s.roofline(kw, k_avg_s)
-    traffic = counters_for(s)
     result = {
         "metric": "selected KV tokens attended/sec (decode) + achieved HBM GB/s % of peak",
         "value": tokens / (ms_per_step / 1e3),
@@ -976,18 +1143,30 @@ def main():
         "dtype": s.dtype_name(),
         "data": "synthetic",
         "config": s.config(use_graph, nset, tokens, ms_per_step),
-        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": traffic, "kernel": kernel_name(s),
-                     "kernel_avg_us": k_avg_s * 1e6,
-                     "algorithmic_bytes_per_launch": kw["bytes"],
-                     "algorithmic_flops_per_launch": kw["flops"]},
+        "roofline": kernel_record(s, k_avg_s),
     }
+    if args.workload == "decode_bf16" and not args.no_also:
+        print("bench: concat-append copy figure", file=sys.stderr, flush=True)
+        result["concat_append"] = concat_append_figure(s)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = s.cpu_baseline(args.cpu_seconds)
+        cb = s.cpu_baseline(args.cpu_seconds)
+        if isinstance(s, Setup) and not isinstance(s, CapacitySetup):
+            one = s.cpu_baseline(max(2.0, args.cpu_seconds / 4), threads=1)
+            cb["single_thread"] = {"value": one["value"], "unit": one["unit"], "sample": one["sample"]}
+            cb["c0_single_thread"] = c0_single_thread()
+        result["cpu_baseline"] = cb
     else:
         result["cpu_baseline"] = None
     s.ctx.destroy()
+    del s
+    torch.cuda.empty_cache()
+    if args.workload == "decode_bf16" and not args.no_also:
+        also = []
+        for name in ("decode_fp8", "prefill_bf16"):
+            print(f"bench: also {name}", file=sys.stderr, flush=True)
+            also.append(also_record(name, args))
+        result["also"] = also
     print(json.dumps(result), flush=True)
 
 

@@ -575,9 +575,9 @@ sa_status launch_csa_attention(sparse_attn_ctx* c, const CsaArgs& a) {
     if (e != hipSuccess) return check_hip(c, e, "csa attention LDS attribute");
     attr_set[variant] = true;
   }
-  prof_begin(c);
+  const ProfEvents pe = prof_next(c);
 #define SA_CSA_LAUNCH(BV)                                                                                     \
-  hipLaunchKernelGGL((csa_attention_kernel<BV>), grid, block, LDS_BYTES, c->stream, a.q, a.ckv, a.rec, a.sel, \
+  SA_MAIN_LAUNCH(pe, (csa_attention_kernel<BV>), grid, block, LDS_BYTES, c->stream, a.q, a.ckv, a.rec, a.sel, \
                      a.sink, a.bias, a.total, a.y, (int)a.batch, (int)a.q_seq, (int)a.heads, (int)a.cur_len,  \
                      a.record_cap, (int)a.index_heads, (int)a.topk, (int)a.bias_dims[0], (int)a.bias_dims[1], \
                      (int)a.bias_dims[2], (int)a.bias_dims[3], a.scale, c->err)
@@ -586,7 +586,6 @@ sa_status launch_csa_attention(sparse_attn_ctx* c, const CsaArgs& a) {
   else
     SA_CSA_LAUNCH(false);
 #undef SA_CSA_LAUNCH
-  prof_end(c);
   return check_hip(c, hipGetLastError(), "csa attention");
 }
 

@@ -550,10 +550,10 @@ sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
                      a.iq, qf, qe, hrows, (int)a.heads, (int)a.q_seq, a.total);
   sa_status st = check_hip(c, hipGetLastError(), "csa index finalize");
   if (st != SA_OK) return st;
-  prof_begin(c);
+  const ProfEvents pe = prof_next(c);
   const dim3 sgrid((unsigned)((a.key_cap + RC - 1) / RC), (unsigned)rows);
 #define SA_IDX_SCORE(HTV)                                                                                       \
-  hipLaunchKernelGGL(csa_index_score_kernel<HTV>, sgrid, dim3(256), score_lds, c->stream, qf, qe, a.iw, a.keys, scores, \
+  SA_MAIN_LAUNCH(pe, csa_index_score_kernel<HTV>, sgrid, dim3(256), score_lds, c->stream, qf, qe, a.iw, a.keys, scores, \
                      (int)a.q_seq, a.key_cap, a.total, c->err)
   switch (a.heads / 16) {
     case 1: SA_IDX_SCORE(1); break;
@@ -562,7 +562,6 @@ sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
     default: SA_IDX_SCORE(4); break;
   }
 #undef SA_IDX_SCORE
-  prof_end(c);
   st = check_hip(c, hipGetLastError(), "csa index score");
   if (st != SA_OK) return st;
   hipLaunchKernelGGL(csa_index_select_kernel, dim3((unsigned)rows), dim3(1024), select_lds, c->stream, scores,

@@ -311,9 +311,9 @@ sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a) {
                                                kGenThreads + 4 * kGenMaxHeads + kGenMaxHeads + 1);
   const dim3 grid((unsigned)wgs), block(kGenThreads);
   const bool fp8 = a.cache_format == SA_CACHE_FP8_E4M3_BLOCK64;
-  prof_begin(c);
+  const ProfEvents pe = prof_next(c);
 #define SA_GEN(DT, F8, I)                                                                        \
-  hipLaunchKernelGGL((generic_forward_kernel<DT, F8, I>), grid, block, smem, c->stream, a.q, a.k, \
+  SA_MAIN_LAUNCH(pe, (generic_forward_kernel<DT, F8, I>), grid, block, smem, c->stream, a.q, a.k, \
                      a.v, a.idx, a.valid_len, a.y, a.hq, a.hkv, a.q_seq, (int)a.dk, (int)a.dv,    \
                      (int)a.rope, a.cap, a.index_heads, a.width, head_chunks, a.scale, a.softcap,  \
                      a.bias, a.bd[0], a.bd[1], a.bd[2], a.bd[3])
@@ -330,7 +330,6 @@ sa_status launch_forward_generic(sparse_attn_ctx* c, const FwdArgs& a) {
   }
 #undef SA_GEN_I
 #undef SA_GEN
-  prof_end(c);
   return check_hip(c, hipGetLastError(), "forward (generic)");
 }
 

@@ -749,9 +749,9 @@ sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
     g_gqa_attr[variant] = true;
   }
   const dim3 grid((unsigned)wgs), block(THREADS);
-  prof_begin(c);
+  const ProfEvents pe = prof_next(c);
 #define SA_GQA(I, C, BI)                                                                                     \
-  hipLaunchKernelGGL((gqa_forward_kernel<I, C, BI>), grid, block, lds, c->stream, (const uint16_t*)a.q,      \
+  SA_MAIN_LAUNCH(pe, (gqa_forward_kernel<I, C, BI>), grid, block, lds, c->stream, (const uint16_t*)a.q,      \
                      (const uint8_t*)a.k, (const uint8_t*)a.v, a.idx, a.valid_len, (uint16_t*)a.y, a.batch, \
                      a.hkv, a.q_seq, a.cap, a.width, group, (int)nqb, a.scale, a.softcap,                    \
                      (const uint16_t*)a.bias, a.bd[0], a.bd[1], a.bd[2], a.bd[3], splits, c->gpart_o,    \
@@ -767,7 +767,6 @@ sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
     default: SA_GQA(true, true, true); break;
   }
 #undef SA_GQA
-  prof_end(c);
   sa_status st = check_hip(c, hipGetLastError(), "forward (gqa)");
   if (st != SA_OK || splits == 1) return st;
   const int64_t rows = a.batch * a.hq * a.q_seq;

@@ -621,14 +621,14 @@ sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits
     g_latent_attr[variant] = true;
   }
   const dim3 grid((unsigned)wgs), block(THREADS);
-  prof_begin(c);
+  const ProfEvents pe = prof_next(c);
   const uint8_t* cur = app ? (const uint8_t*)app->cur : nullptr;
   const int32_t* plen = app ? app->past_len : nullptr;
   int32_t* prlen = app ? app->present_len : nullptr;
   const int64_t clen = app ? app->cur_len : 0;
   const int reset = app ? app->reset : 0;
 #define SA_LAT(I, F, C, A)                                                                            \
-  hipLaunchKernelGGL((latent_forward_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,          \
+  SA_MAIN_LAUNCH(pe, (latent_forward_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,          \
                      (const uint16_t*)a.q, (uint8_t*)a.k, a.idx, a.valid_len, (uint16_t*)a.y,         \
                      c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width, splits, a.scale,     \
                      a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset)
@@ -647,7 +647,6 @@ sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits
     default: SA_LAT(true, true, true, true); break;
   }
 #undef SA_LAT
-  prof_end(c);
   sa_status s = check_hip(c, hipGetLastError(), "forward (latent)");
   if (s != SA_OK || splits == 1) return s;
   return launch_mla_combine(c, rows, a.q_seq, splits, (uint16_t*)a.y);

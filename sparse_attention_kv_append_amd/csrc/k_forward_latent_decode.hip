@@ -627,8 +627,12 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
   // the row sum of head 16 h + c16, key halves added in order
   auto l_total = [&](int h) { return xch[128 + 32 * h + c16] + xch[128 + 32 * h + 16 + c16]; };
 
-  // ---- epilogue: lane holds O^T[64 wave + 16 d + 4 g + r][16 h + c16]
-  if (splits == 1) {
+  // ---- epilogue: lane holds O^T[64 wave + 16 d + 4 g + r][16 h + c16]. Every
+  // head's output is normalised by its row sum and rounded to bf16, then
+  // written as whole 1 KB rows through LDS: to Y when the keys are not split,
+  // else to the split's partial (the merge kernel combines the splits with
+  // their (reference, row sum) pairs, which stay fp32).
+  {
     constexpr int YROW = 1024 + 16;  // padded: the 16 heads of one write hit distinct banks
     __syncthreads();                 // the ring is free
 #pragma unroll
@@ -643,31 +647,19 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
         *(__attribute__((address_space(3))) u32x2_l*)(yl + 32 * d) = (u32x2_l){lo, hi};
       }
     }
+    if (splits > 1 && kh == 0 && g == 0) {
+      const int64_t pr = (row * splits + split) * NH + 16 * hb + c16;
+      part_ml[pr * 2] = m_ref;
+      part_ml[pr * 2 + 1] = l_total(hb);
+    }
     __syncthreads();
+    uint16_t* dst = splits == 1 ? y + (b * NH * q_seq + qi) * DV : (uint16_t*)part_o + (row * splits + split) * NH * DV;
+    const int64_t hstride = splits == 1 ? q_seq * DV : DV;
 #pragma unroll 4
     for (int hq = 0; hq < 8; hq++) {
       const int hd = 8 * wave + hq;
       const u32x4_l v = *(const lds_u32x4*)(ring + hd * YROW + 16 * lane);
-      *(u32x4_l*)(y + ((b * NH + hd) * q_seq + qi) * DV + 8 * lane) = v;
-    }
-  } else {
-    // unnormalised partials; the combine kernel merges them after this launch.
-    // They are stored device-coherent (sc1: written through the XCD's L2),
-    // so the fences of the row finishers below do not have to write back
-    // 128 KB of dirty partials per workgroup first.
-    const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(part_o + (row * splits + split) * NH * DV), (short)0, NH * DV * 4, 0x00020000);
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-      const int obase = ((16 * h + c16) * DV + 64 * wave + 4 * g) * 4;
-#pragma unroll
-      for (int d = 0; d < DVW; d++)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_l, o[d][h]), prsrc, obase + 64 * d, 0, 16);
-    }
-    if (kh == 0 && g == 0) {
-      const int64_t pr = (row * splits + split) * NH + 16 * hb + c16;
-      part_ml[pr * 2] = m_ref;
-      part_ml[pr * 2 + 1] = l_total(hb);
+      *(u32x4_l*)(dst + hd * hstride + 8 * lane) = v;
     }
   }
   if constexpr (APPEND) {
@@ -694,7 +686,9 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
 
 // Log-sum-exp merge of the split partials (standard Attention page,
 // `attention_combine`; m in log2 units): M = max_j m_j and
-// y = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M). One 128-thread workgroup
+// y = sum_j l_j 2^(m_j - M) o_j / sum_j l_j 2^(m_j - M), o_j the split's
+// output normalised by its own row sum l_j and stored as bf16 (Y's own
+// precision: the merge adds at most one bf16 rounding of each split's output). One 128-thread workgroup
 // per (row, head), each thread 4 channels; block i serves row i % rows, on
 // the XCD that wrote that row's partials. Each round loads 8 splits before
 // using any. With FIN (fused validation) the workgroup of head 0 of each row
@@ -704,7 +698,7 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
 // device-wide round trip per workgroup at its end.
 template <bool FIN, bool I64>
 __global__ void __launch_bounds__(128)
-latent_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, uint16_t* __restrict__ y,
+latent_merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, uint16_t* __restrict__ y,
                     int64_t rows, int64_t q_seq, int splits, ErrorBlock* __restrict__ eb,
                     unsigned long long* __restrict__ row_key, const void* __restrict__ idx, int64_t width,
                     const int32_t* __restrict__ valid_len, const int32_t* __restrict__ past_len,
@@ -715,20 +709,22 @@ latent_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ 
   const int head = (int)(blockIdx.x / (unsigned)rows);
   const int64_t b = row / q_seq, qi = row - b * q_seq;
   const int d = threadIdx.x * 4;
+  // y = sum_j w_j o_j / sum_j w_j with w_j = l_j 2^(m_j - M) and o_j the
+  // split's normalised output; M is raised as later splits come in
   float M = -INFINITY, L = 0.0f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < splits; j0 += CH) {
     float2 ml[CH];
-    float4 v[CH];
+    uint2 v[CH];
 #pragma unroll
     for (int j = 0; j < CH; j++) {
       const int64_t pr = (row * splits + j0 + j) * NH + head;
       if (j0 + j < splits) {
         ml[j] = *(const float2*)(part_ml + pr * 2);
-        v[j] = *(const float4*)(part_o + pr * DV + d);
+        v[j] = *(const uint2*)(part_o + pr * DV + d);
       } else {
         ml[j] = make_float2(-INFINITY, 0.0f);
-        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        v[j] = make_uint2(0u, 0u);
       }
     }
     float Mn = M;
@@ -741,12 +737,12 @@ latent_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ 
     for (int e = 0; e < 4; e++) acc[e] *= r;
 #pragma unroll
     for (int j = 0; j < CH; j++) {
-      const float w = ml[j].x == -INFINITY ? 0.0f : exp2f(ml[j].x - Mn);
-      L += ml[j].y * w;
-      acc[0] += v[j].x * w;
-      acc[1] += v[j].y * w;
-      acc[2] += v[j].z * w;
-      acc[3] += v[j].w * w;
+      const float w = ml[j].x == -INFINITY ? 0.0f : ml[j].y * exp2f(ml[j].x - Mn);
+      L += w;
+      acc[0] += w * __uint_as_float(v[j].x << 16);
+      acc[1] += w * __uint_as_float(v[j].x & 0xffff0000u);
+      acc[2] += w * __uint_as_float(v[j].y << 16);
+      acc[3] += w * __uint_as_float(v[j].y & 0xffff0000u);
     }
     M = Mn;
   }
@@ -770,8 +766,9 @@ latent_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ 
       atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
       atomicMin((unsigned long long*)&eb->call_key, k);
     }
-    finish_launch<I64>(eb, idx, width, q_seq, q_seq, past_len ? present_len : valid_len, cap, (unsigned)rows,
-                       reset != 0);
+    // the launch's other inputs were written before it began: no cache fences
+    finish_launch<I64, false>(eb, idx, width, q_seq, q_seq, past_len ? present_len : valid_len, cap,
+                              (unsigned)rows, reset != 0);
   }
 }
 
@@ -783,7 +780,8 @@ static sa_status launch_latent_merge(sparse_attn_ctx* c, const FwdArgs& a, int64
   const int64_t clen = app ? app->cur_len : 0;
   const int reset = app ? app->reset : 0;
 #define SA_MERGE(F, I)                                                                                     \
-  hipLaunchKernelGGL((latent_merge_kernel<F, I>), grid, block, 0, c->stream, c->partial_o, c->partial_ml,      \
+  hipLaunchKernelGGL((latent_merge_kernel<F, I>), grid, block, 0, c->stream, (const uint16_t*)c->partial_o,      \
+                     c->partial_ml,                                                                         \
                      (uint16_t*)a.y, rows, a.q_seq, splits, c->err, c->row_key, a.idx, a.width, a.valid_len, \
                      plen, prlen, clen, a.cap, reset)
   if (!fused) SA_MERGE(false, false);
@@ -828,14 +826,14 @@ sa_status launch_forward_latent_decode(sparse_attn_ctx* c, const FwdArgs& a, int
     g_lhd_attr[variant] = true;
   }
   const dim3 grid((unsigned)wgs), block(THREADS);
-  prof_begin(c);
+  const ProfEvents pe = prof_next(c);
   const uint8_t* cur = app ? (const uint8_t*)app->cur : nullptr;
   const int32_t* plen = app ? app->past_len : nullptr;
   int32_t* prlen = app ? app->present_len : nullptr;
   const int64_t clen = app ? app->cur_len : 0;
   const int reset = app ? app->reset : 0;
 #define SA_LHD(I, F, C, A)                                                                            \
-  hipLaunchKernelGGL((latent_decode_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,           \
+  SA_MAIN_LAUNCH(pe, (latent_decode_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,           \
                      (const uint16_t*)a.q, (uint8_t*)a.k, a.idx, a.valid_len, (uint16_t*)a.y,         \
                      c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width, splits, a.scale,     \
                      a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset)
@@ -854,7 +852,6 @@ sa_status launch_forward_latent_decode(sparse_attn_ctx* c, const FwdArgs& a, int
     default: SA_LHD(true, true, true, true); break;
   }
 #undef SA_LHD
-  prof_end(c);
   sa_status s = check_hip(c, hipGetLastError(), "forward (latent decode)");
   if (s != SA_OK || splits == 1) return s;
   return launch_latent_merge(c, a, rows, splits, fused, app);

@@ -451,9 +451,9 @@ sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits) {
     g_mla_attr_set[variant] = true;
   }
   const dim3 grid((unsigned)wgs), block(THREADS);
-  prof_begin(c);
+  const ProfEvents pe = prof_next(c);
 #define SA_MLA(F8, I)                                                                             \
-  hipLaunchKernelGGL((mla_forward_kernel<F8, I>), grid, block, LDS_BYTES, c->stream,              \
+  SA_MAIN_LAUNCH(pe, (mla_forward_kernel<F8, I>), grid, block, LDS_BYTES, c->stream,              \
                      (const uint16_t*)a.q, (const uint8_t*)a.k, a.idx, a.valid_len,               \
                      (uint16_t*)a.y, c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width, \
                      splits, a.scale, a.softcap)
@@ -464,7 +464,6 @@ sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits) {
     default: SA_MLA(true, true); break;
   }
 #undef SA_MLA
-  prof_end(c);
   sa_status s = check_hip(c, hipGetLastError(), "forward (mla)");
   if (s != SA_OK || splits == 1) return s;
   return launch_mla_combine(c, rows, a.q_seq, splits, (uint16_t*)a.y);

@@ -745,7 +745,7 @@ sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, 
     g_pair_attr[variant] = true;
   }
   const dim3 grid((unsigned)wgs), block(THREADS);
-  prof_begin(c);
+  const ProfEvents pe = prof_next(c);
   const void* cur = app ? app->cur : nullptr;
   const int32_t* plen = app ? app->past_len : nullptr;
   int32_t* prlen = app ? app->present_len : nullptr;
@@ -753,7 +753,7 @@ sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, 
   const int reset = app ? app->reset : 0;
   const int quant = app ? app->quant : 0;
 #define SA_PAIR(I, F, C, A)                                                                           \
-  hipLaunchKernelGGL((pair_forward_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,            \
+  SA_MAIN_LAUNCH(pe, (pair_forward_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,            \
                      (const uint16_t*)a.q, (uint8_t*)a.k, a.idx, a.valid_len, (uint16_t*)a.y,         \
                      c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width, splits, a.scale,     \
                      a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset, quant)
@@ -772,7 +772,6 @@ sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, 
     default: SA_PAIR(true, true, true, true); break;
   }
 #undef SA_PAIR
-  prof_end(c);
   sa_status s = check_hip(c, hipGetLastError(), "forward (fp8 pair)");
   if (s != SA_OK || splits == 1) return s;
   return launch_mla_combine(c, rows, a.q_seq, splits, (uint16_t*)a.y);

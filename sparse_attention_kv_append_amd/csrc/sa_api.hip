@@ -73,15 +73,14 @@ sa_status check_hip(sparse_attn_ctx* c, hipError_t e, const char* what) {
   return set_error(c, SA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-void prof_begin(sparse_attn_ctx* c) {
-  if (c->prof_n < (int64_t)c->prof_start.size()) (void)hipEventRecord(c->prof_start[c->prof_n], c->stream);
-}
-
-void prof_end(sparse_attn_ctx* c) {
-  if (c->prof_n < (int64_t)c->prof_stop.size()) {
-    (void)hipEventRecord(c->prof_stop[c->prof_n], c->stream);
+ProfEvents prof_next(sparse_attn_ctx* c) {
+  ProfEvents pe;
+  if (c->prof_n < (int64_t)c->prof_start.size()) {
+    pe.start = c->prof_start[c->prof_n];
+    pe.stop = c->prof_stop[c->prof_n];
     c->prof_n++;
   }
+  return pe;
 }
 
 void free_buffers(sparse_attn_ctx* c) {

@@ -2,6 +2,7 @@
 // launchers, the context, small device helpers). Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -228,9 +229,21 @@ sa_status launch_mla_combine(sparse_attn_ctx* c, int64_t rows, int64_t q_seq, in
 
 sa_status set_error(sparse_attn_ctx* c, sa_status s, const std::string& msg);
 void free_buffers(sparse_attn_ctx* c);
-// event pair around the main forward kernel when profiling is on
-void prof_begin(sparse_attn_ctx* c);
-void prof_end(sparse_attn_ctx* c);
+// Optional timing of a call's main kernel: the event pair the next launch
+// carries (null when timing is off or its slots are used up). The launch
+// takes the events with hipExtLaunchKernel, which stamps them with the
+// dispatch's own start and end, so the time is the kernel's alone.
+struct ProfEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfEvents prof_next(sparse_attn_ctx* c);
+#define SA_MAIN_LAUNCH(pe, kernel, grid, block, shmem, stream, ...)                                        \
+  do {                                                                                                     \
+    if ((pe).start)                                                                                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (pe).start, (pe).stop, 0u, __VA_ARGS__);  \
+    else                                                                                                   \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                                \
+  } while (0)
 sa_status check_hip(sparse_attn_ctx* c, hipError_t e, const char* what);
 
 }  // namespace sa

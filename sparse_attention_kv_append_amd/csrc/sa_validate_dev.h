@@ -31,15 +31,19 @@ __device__ __forceinline__ int column_class(int64_t c, int64_t v, int64_t u, int
 // a reset followed by itself), records the launch's first violation (class,
 // values, position) if no earlier launch since the reset failed, then re-arms
 // the per-launch slots and counter for the next launch on the stream.
-template <bool I64>
+// FENCE = false: every value the participants read was written before the
+// launch began or by device-scope atomics, which a plain wait for completion
+// orders; the whole-cache fences are then left out.
+template <bool I64, bool FENCE = true>
 __device__ __forceinline__ void finish_launch(ErrorBlock* __restrict__ eb, const void* __restrict__ idx,
                                               int64_t width, int64_t q_seq, int64_t rows_per_batch,
                                               const int32_t* __restrict__ valid_len, int64_t cache_len,
                                               unsigned expected, bool reset = false) {
-  __threadfence();
+  if constexpr (FENCE) __threadfence();
+  else __builtin_amdgcn_s_waitcnt(0);  // this thread's atomics have completed
   const unsigned done = atomicAdd(&eb->done_blocks, 1u);
   if (done != expected - 1) return;
-  __threadfence();
+  if constexpr (FENCE) __threadfence();
   const unsigned bits = atomicExch(&eb->call_word, 0u);
   if (reset) {
     eb->word = bits;
@@ -69,7 +73,7 @@ __device__ __forceinline__ void finish_launch(ErrorBlock* __restrict__ eb, const
     eb->detail_q = (r - b * rows_per_batch) % q_seq;
     eb->detail_col = c;
     eb->first_bad = key;
-    __threadfence();
+    if constexpr (FENCE) __threadfence();
     eb->detail_class = k;
   }
   eb->call_key = ~0ull;
