@@ -566,6 +566,9 @@ class CsaIndexSetup:
 
     path = 6
     splits = 1
+    # among 16384 fp32 scores per row, exactly equal scores (which the CPU page
+    # rejects) occur by chance in synthetic data; the device reports them
+    tolerated_bits = 0x2000  # SA_ERR_INDEX_TIE
 
     def __init__(self, name, rotate):
         import torch
@@ -727,7 +730,7 @@ def pmc_run(args):
         s.step(i)
     torch.cuda.synchronize()
     word, _, msg = s.ctx.read_error()
-    assert word == 0, msg
+    assert word & ~getattr(s, "tolerated_bits", 0) == 0, msg
     print(json.dumps({"pmc_run": args.workload, "kernel": kernel_name(s),
                       "steps": args.warmup + args.steps}), flush=True)
 
@@ -983,11 +986,12 @@ def measure(s, steps, warmup, use_graph):
     eager pass of the same steps with the main kernel's dispatch-stamped
     events. Returns (ms per step, main kernel seconds per launch)."""
     torch = s.torch
+    ok = getattr(s, "tolerated_bits", 0)
     for i in range(warmup):
         s.step(i)
     torch.cuda.synchronize()
     word, _, msg = s.ctx.read_error()
-    assert word == 0, msg
+    assert word & ~ok == 0, msg
     nset = len(s.idxs)
     full, rem = divmod(steps, nset)
     graphs = {}
@@ -1016,7 +1020,7 @@ def measure(s, steps, warmup, use_graph):
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / steps
     word, _, msg = s.ctx.read_error()
-    assert word == 0, msg
+    assert word & ~ok == 0, msg
     s.ctx.profile_enable(steps)
     for i in range(steps):
         s.step(i)

@@ -88,6 +88,10 @@ enum { SA_IDX_I32 = 0, SA_IDX_I64 = 1 };
                                         denominator not finite and positive      */
 #define SA_ERR_INDEX_NONFINITE 0x1000u /* sparse_attn_csa_index_select: a record's
                                           score is not finite                     */
+#define SA_ERR_INDEX_TIE 0x2000u       /* sparse_attn_csa_index_select: two of a
+                                          row's candidate scores are equal (the CSA
+                                          CPU page's select_ratio4_topk rejects
+                                          such a row)                             */
 
 typedef struct {
   int32_t num_heads;      /* Hq > 0 (IndexShare attr num_heads)                         */
@@ -337,7 +341,9 @@ sa_status sparse_attn_step(sparse_attn_ctx* ctx, const void* q, int64_t batch, i
  * Each head dot equals the CPU page's ascending fp32 fold for any block
  * scales: the matrix-core dot is used where no partial sum can round, the
  * fold itself elsewhere. Exact score ties, which the CPU page rejects, are
- * ordered by ascending record. Host errors: SA_E_ARG (NULL pointer, size < 1), SA_E_UNSUPPORTED
+ * ordered by ascending record and reported as SA_ERR_INDEX_TIE (float
+ * equality of any two of a row's candidate scores; a NaN equals nothing).
+ * Host errors: SA_E_ARG (NULL pointer, size < 1), SA_E_UNSUPPORTED
  * (H, K or key_cap out of range). Device: SA_ERR_CSA_GEOMETRY when total < S
  * (nothing written); SA_ERR_INDEX_NONFINITE when a score is not finite (it is
  * still ranked, by the fp32 total order). Asynchronous and capturable. */

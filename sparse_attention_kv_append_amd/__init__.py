@@ -31,6 +31,7 @@ SA_ERR_APPEND_CAPACITY, SA_ERR_QUANT_NONFINITE = 0x40, 0x80
 SA_ERR_INDEX_ANY, SA_ERR_APPEND_ANY = 512, 1024
 SA_STATIC_SCRATCH_BYTES = 48 << 20
 SA_ERR_CSA_GEOMETRY, SA_ERR_CSA_DENOM, SA_ERR_INDEX_NONFINITE = 0x100, 0x800, 0x1000
+SA_ERR_INDEX_TIE = 0x2000
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_DTYPE", 4: "SA_E_CAPACITY",
                 5: "SA_E_UNSUPPORTED", 6: "SA_E_HIP", 7: "SA_E_STATE", 8: "SA_E_INDEX"}

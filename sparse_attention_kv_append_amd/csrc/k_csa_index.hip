@@ -140,11 +140,16 @@ csa_index_finalize_kernel(const float* __restrict__ iq, uint16_t* __restrict__ q
 // at most 9 (4608 * 2^9 * 4 < 2^24). qr packs the query's lowest and highest
 // block exponent; the key's come in klo, khi; the per-block test runs only
 // when the ranges alone do not settle it.
-__device__ __forceinline__ bool dot_is_exact(int qr, int klo, int khi, uint32_t qx, const uint8_t* kk) {
+__device__ __forceinline__ bool range_is_exact(int qr, int klo, int khi) {
   const int qlo = qr & 255, qhi = qr >> 8;
   if (qlo < 2 || qhi > 252 || klo < 2 || khi > 252) return false;
   const int lo = qlo + klo - 254, hi = qhi + khi - 254;
-  if (lo >= -124 && hi <= 115 && hi - lo <= 9) return true;
+  return lo >= -124 && hi <= 115 && hi - lo <= 9;
+}
+
+__device__ __forceinline__ bool dot_is_exact(int qr, int klo, int khi, uint32_t qx, const uint8_t* kk) {
+  if (range_is_exact(qr, klo, khi)) return true;
+  if ((qr & 255) < 2 || (qr >> 8) > 252 || klo < 2 || khi > 252) return false;
   int elo = 1 << 20, ehi = -(1 << 20);
 #pragma unroll
   for (int c = 0; c < 4; c++) {
@@ -158,12 +163,14 @@ __device__ __forceinline__ bool dot_is_exact(int qr, int klo, int khi, uint32_t 
 // The head dot in the pages' order: q (bf16, exact in fp32) times the
 // decoded key value (E2M1 magnitude times the block's E8M0 scale, 255 = NaN),
 // each product rounded, folded in ascending dimension order.
-__device__ __noinline__ float ordered_dot(const uint16_t* __restrict__ qh, const uint8_t* kk) {
+__device__ __forceinline__ float ordered_dot(const uint16_t* __restrict__ qh, const uint8_t* kk) {
   const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
   float acc = 0.0f;
+#pragma unroll 1
   for (int c = 0; c < 4; c++) {
     const uint32_t e = kk[17 * c];
     const float sc = e == 255u ? __uint_as_float(0x7fc00000u) : (e ? __uint_as_float(e << 23) : 5.877471754e-39f);
+#pragma unroll 1
     for (int i = 0; i < 32; i++) {
       const uint32_t code = ((uint32_t)kk[17 * c + 1 + (i >> 1)] >> (4 * (i & 1))) & 15u;
       const float m = mag[code & 7u];
@@ -218,19 +225,28 @@ csa_index_score_kernel(const uint16_t* __restrict__ qf, const uint8_t* __restric
   uint8_t* kl = smem;                          // RB keys, 68 B each
   float* dt = (float*)(smem + RB * KB);        // [RB][DSTR] dot products
   // per head: the query blocks' scale exponents (4 bytes) and their range
+  // (and, in qr[HMAX], the range over all heads)
   uint32_t* qx = (uint32_t*)(smem + RB * KB + RB * DSTR * 4);
   int* qr = (int*)(qx + HMAX);
-  if (tid < H) {
-    const uint32_t x = *(const uint32_t*)(qe + (row * H + tid) * 4);
+  if (w == 0) {
     int lo = 255, hi = 0;
+    if (tid < H) {
+      const uint32_t x = *(const uint32_t*)(qe + (row * H + tid) * 4);
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const int e = (int)((x >> (8 * c)) & 255u);
-      lo = min(lo, e);
-      hi = max(hi, e);
+      for (int c = 0; c < 4; c++) {
+        const int e = (int)((x >> (8 * c)) & 255u);
+        lo = min(lo, e);
+        hi = max(hi, e);
+      }
+      qx[tid] = x;
+      qr[tid] = lo | (hi << 8);
     }
-    qx[tid] = x;
-    qr[tid] = lo | (hi << 8);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo = min(lo, __shfl_xor(lo, o));
+      hi = max(hi, __shfl_xor(hi, o));
+    }
+    if (tid == 0) qr[HMAX] = lo | (hi << 8);
   }  // read after the first pass's barriers
   const uint32_t* kb = (const uint32_t*)(keys + (b * kcap) * KB);
   constexpr int KW = RB * KB / 4;              // dwords of a pass's keys
@@ -300,7 +316,7 @@ csa_index_score_kernel(const uint16_t* __restrict__ qf, const uint8_t* __restric
     // one record per thread: the head sum in ascending head order
     const int64_t r = r0 + tid;
     if (tid < RB && r < c1) {
-      const f32x4_l* d4 = (const f32x4_l*)(dt + tid * DSTR);
+      float* drow = dt + tid * DSTR;
       const uint8_t* kk = kl + tid * KB;
       int klo = 255, khi = 0;
 #pragma unroll
@@ -308,20 +324,24 @@ csa_index_score_kernel(const uint16_t* __restrict__ qf, const uint8_t* __restric
         klo = min(klo, (int)kk[17 * c]);
         khi = max(khi, (int)kk[17 * c]);
       }
+      // The matrix dot equals the pages' ascending fp32 fold when no partial
+      // sum rounds: every factor a normal number and the block products within
+      // 2^9 of each other. Where the exponent ranges over all heads do not
+      // settle that, the heads that fail are redone in the pages' order (rare:
+      // keys and queries of widely spread block scales).
+      if (!range_is_exact(qr[HMAX], klo, khi)) {
+#pragma unroll 1
+        for (int h = 0; h < H; h++)
+          if (!dot_is_exact(qr[h], klo, khi, qx[h], kk)) drow[h] = ordered_dot(qrow + (int64_t)h * D, kk);
+      }
+      const f32x4_l* d4 = (const f32x4_l*)drow;
       float score = 0.0f;
 #pragma unroll
       for (int h4 = 0; h4 < H / 4; h4++) {
         const f32x4_l x4 = d4[h4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          float x = x4[j];
-          // The matrix dot equals the pages' ascending fp32 fold when no
-          // partial sum rounds: every factor a normal number and the block
-          // products within 2^9 of each other. Otherwise the fold is redone
-          // in the pages' order (rare: keys and queries of widely spread
-          // block scales).
-          const int h = 4 * h4 + j;
-          if (!dot_is_exact(qr[h], klo, khi, qx[h], kk)) x = ordered_dot(qrow + (int64_t)h * D, kk);
+          const float x = x4[j];
           const float relu = x > 0.0f ? x : 0.0f;
           const float t0 = relu * wv[4 * h4 + j];
           const float t1 = t0 * ws;
@@ -372,6 +392,40 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 // score's key); the k-th largest key is found by a binary search over key
 // values (counting probes reduced without atomics), the winners are placed by
 // a scan, and sorted by rank (each winner counts the larger ones).
+// Exact score ties, which the CSA CPU page rejects (`select_ratio4_topk`),
+// are found by workgroups of their own beside the row's select workgroup: the
+// row's scores are split by a hash of their value into P parts and each part
+// inserted into an LDS hash table (linear probing, 2^15 slots, key 0 = empty);
+// meeting its own key again is a tie. Scores compare as floats: -0 counts as
+// +0, a NaN equals nothing. Equal scores share a part, so the parts together
+// see every equal pair.
+constexpr int TIE_SLOTS = 1 << 15;
+__device__ __forceinline__ void tie_part(const float* __restrict__ src, int n, uint32_t p, uint32_t P,
+                                         uint32_t* __restrict__ tab, ErrorBlock* __restrict__ eb) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < TIE_SLOTS / 4; i += 1024) ((uint4*)tab)[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  bool tie = false;
+  for (int i = tid; i < n; i += 1024) {
+    float x = src[i];
+    if (x != x) continue;     // NaN
+    if (x == 0.0f) x = 0.0f;  // -0 -> +0
+    const uint32_t key = total_key(x);  // never 0 for a number
+    if ((uint32_t)(((uint64_t)(key * 0x85EBCA6Bu) * P) >> 32) != p) continue;
+    uint32_t h = (key * 0x9E3779B1u) >> 17;
+    for (int probe = 0; probe < TIE_SLOTS; probe++) {
+      const uint32_t prev = atomicCAS(&tab[h], 0u, key);
+      if (prev == 0u) break;
+      if (prev == key) {
+        tie = true;
+        break;
+      }
+      h = (h + 1u) & (TIE_SLOTS - 1);
+    }
+  }
+  if (__syncthreads_or(tie) && tid == 0) atomicOr(&eb->word, SA_ERR_INDEX_TIE);
+}
+
 template <int NJ>
 __device__ __forceinline__ void select_row(const float* __restrict__ src, int32_t* __restrict__ outb, int n,
                                            int K, int S, int out_heads, uint8_t* smem) {
@@ -494,19 +548,23 @@ csa_index_select_kernel(const float* __restrict__ scores, int32_t* __restrict__ 
                         ErrorBlock* __restrict__ eb) {
   using namespace cx;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int64_t row = blockIdx.x;  // (b, s)
+  const int64_t row = blockIdx.y;  // (b, s); x = 0 selects, x >= 1 looks for ties
   const int s = (int)(row % S);
   const int64_t b = row / S;
   const int64_t pos = *total_ptr - S + s;
   int32_t* outb = sel + (b * out_heads * S + s) * K;  // head 0 row; head h at + h S K
   if (pos < s) {  // total < S
-    if (row == 0 && threadIdx.x == 0) atomicOr(&eb->word, SA_ERR_CSA_GEOMETRY);
+    if (row == 0 && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&eb->word, SA_ERR_CSA_GEOMETRY);
     return;
   }
   int64_t n64 = (pos + 1) / 4;
   if (n64 > kcap) n64 = kcap;
   const int n = (int)n64;
   const float* src = scores + row * kcap;
+  if (blockIdx.x > 0) {
+    tie_part(src, n, blockIdx.x - 1, gridDim.x - 1, (uint32_t*)smem, eb);
+    return;
+  }
   // registers per thread sized to the records (uniform branch)
   if (n <= 1024 * 4)
     select_row<4>(src, outb, n, K, S, out_heads, smem);
@@ -530,8 +588,8 @@ sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
   const size_t sb = ((size_t)rows * (size_t)a.key_cap * 4 + 255) & ~(size_t)255;
   uint16_t* qf = (uint16_t*)((uint8_t*)a.workspace + sb);
   uint8_t* qe = (uint8_t*)(qf + (size_t)rows * (size_t)a.heads * D);
-  const size_t score_lds = (size_t)RB * KB + (size_t)RB * DSTR * 4 + (size_t)HMAX * 8;
-  const size_t select_lds = (size_t)64 * 4 + (size_t)KMAX * 8;
+  const size_t score_lds = (size_t)RB * KB + (size_t)RB * DSTR * 4 + (size_t)HMAX * 8 + 16;
+  const size_t select_lds = std::max((size_t)64 * 4 + (size_t)KMAX * 8, (size_t)TIE_SLOTS * 4);
   const void* score_fns[4] = {(const void*)csa_index_score_kernel<1>, (const void*)csa_index_score_kernel<2>,
                               (const void*)csa_index_score_kernel<3>, (const void*)csa_index_score_kernel<4>};
   static bool attr = false;
@@ -564,7 +622,9 @@ sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
 #undef SA_IDX_SCORE
   st = check_hip(c, hipGetLastError(), "csa index score");
   if (st != SA_OK) return st;
-  hipLaunchKernelGGL(csa_index_select_kernel, dim3((unsigned)rows), dim3(1024), select_lds, c->stream, scores,
+  // tie parts per row: enough to fill the chip beside the select workgroups
+  const unsigned parts = (unsigned)std::max<int64_t>(1, std::min<int64_t>(3, 256 / rows - 1));
+  hipLaunchKernelGGL(csa_index_select_kernel, dim3(1 + parts, (unsigned)rows), dim3(1024), select_lds, c->stream, scores,
                      a.selected, (int)a.q_seq, (int)a.out_heads, a.key_cap, (int)a.topk, a.total, c->err);
   return check_hip(c, hipGetLastError(), "csa index select");
 }
