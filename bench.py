@@ -63,6 +63,9 @@ def parse():
                    help="turn a rocprofv3 --kernel-trace --stats CSV of this script into the committed "
                         "summary of the workload's main kernel")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--trials", type=int, default=20,
+                   help="extra timed trials (>= 200 replayed steps each) whose median is reported")
+    p.add_argument("--no-peaks", action="store_true", help="skip re-measuring the copy and MFMA peaks")
     p.add_argument("--pmc-run", action="store_true",
                    help="counter pass: a 256 MiB device copy (calibration), then W + K eager steps")
     p.add_argument("--digest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -979,12 +982,13 @@ def stats_digest(args):
     print(f"wrote {f}")
 
 
-def measure(s, steps, warmup, use_graph):
+def measure(s, steps, warmup, use_graph, n_trials=0):
     """W warmup steps, then exactly `steps` steps between events: graph replays
     of one captured pass over the rotation sets (and one more graph of the
     remaining sets when `steps` is not a multiple of their number), then an
     eager pass of the same steps with the main kernel's dispatch-stamped
-    events. Returns (ms per step, main kernel seconds per launch)."""
+    events, then `n_trials` more timed trials of at least 200 replayed steps
+    each. Returns (ms per step, main kernel seconds per launch, trials)."""
     torch = s.torch
     ok = getattr(s, "tolerated_bits", 0)
     for i in range(warmup):
@@ -1026,15 +1030,78 @@ def measure(s, steps, warmup, use_graph):
         s.step(i)
     k_ms, k_n = s.ctx.profile_read()
     s.ctx.profile_enable(0)
-    return ms_per_step, k_ms / max(k_n, 1) / 1e3
+    trials = None
+    if use_graph and n_trials > 0:
+        import statistics
+        per = nset if nset in graphs else rem
+        g = graphs[per]
+        reps = max(1, -(-200 // per))
+        ts = []
+        for _ in range(n_trials):
+            start.record()
+            for _ in range(reps):
+                g.replay()
+            stop.record()
+            torch.cuda.synchronize()
+            ts.append(start.elapsed_time(stop) / (reps * per))
+        word, _, msg = s.ctx.read_error()
+        assert word & ~ok == 0, msg
+        ts.sort()
+        trials = {"n": n_trials, "steps_each": reps * per, "median_ms_per_step": statistics.median(ts),
+                  "min_ms_per_step": ts[0], "max_ms_per_step": ts[-1]}
+    return ms_per_step, k_ms / max(k_n, 1) / 1e3, trials
 
 
-def kernel_record(s, k_avg_s):
+def measured_peaks(torch, sa, copy_bytes=1 << 30, reps=8):
+    """The device's attainable HBM rate (a streaming copy, read + write bytes)
+    and bf16 matrix-core rate (independent 16x16x32 products on every SIMD),
+    each the best of `reps` timed launches after a warmup."""
+    ctx = sa.Context(num_heads=16, kv_num_heads=1, head_dim_qk=64, head_dim_v=64, dtype=sa.SA_F32)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(call):
+        call()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b) / 1e3)
+        return min(t)
+
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    t_copy = best(lambda: ctx.measure_copy(dst, src, copy_bytes))
+    sink = torch.empty(sa.SA_PEAK_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    t_read = best(lambda: ctx.measure_read(sink, src, copy_bytes))
+    del src, dst, sink
+    wgs, iters = 256 * 8, 2048
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    t_mfma = best(lambda: ctx.measure_mfma(out, wgs, iters))
+    ctx.destroy()
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": 2 * copy_bytes / t_copy / 1e9, "hbm_read_GBps": copy_bytes / t_read / 1e9,
+            "mfma_bf16_TFLOPs": wgs * 4 * iters * 8 * 16384 / t_mfma / 1e12,
+            "how": f"best of {reps}: streaming copy of {copy_bytes >> 20} MiB (read + write bytes), streaming "
+                   f"read of the same; {wgs} workgroups x 4 waves x {iters} x 8 independent bf16 16x16x32 "
+                   f"matrix-core products"}
+
+
+def kernel_record(s, k_avg_s, peaks=None):
     kw = s.kernel_work()
     bound, peak, unit, achieved = s.roofline(kw, k_avg_s)
     rec = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
            "traffic": counters_for(s), "kernel": kernel_name(s), "kernel_avg_us": k_avg_s * 1e6,
            "algorithmic_bytes_per_launch": kw["bytes"], "algorithmic_flops_per_launch": kw["flops"]}
+    if peaks:
+        # the attention kernels' HBM bytes are almost all reads: the read rate is their ceiling
+        mp = peaks["hbm_read_GBps"] if unit == "GB/s" else peaks["mfma_bf16_TFLOPs"] if unit == "TFLOP/s" else None
+        if mp:
+            rec["measured_peak"] = mp
+            rec["frac_measured"] = achieved / mp
     prof = stats_for(s)
     if prof:
         _, _, _, a_prof = s.roofline(kw, prof["avg_us"] / 1e6)
@@ -1094,14 +1161,14 @@ def c0_single_thread(target_s=1.0):
             "sample": f"the whole tiny_f32 workload (append, forward) x {reps}, {n} selected keys, {t:.2f} s"}
 
 
-def also_record(name, args):
+def also_record(name, args, peaks=None):
     """Step time, main-kernel time, roofline and traffic of another workload, for
     the default line."""
     import torch
     s = make_setup(name, args.rotate)
-    ms, k_avg = measure(s, args.also_steps, 4, not args.no_graph)
+    ms, k_avg, trials = measure(s, args.also_steps, 4, not args.no_graph, args.trials)
     rec = {"workload": name, "ms_per_step": ms, "steps": args.also_steps, "splits": s.splits,
-           "roofline": kernel_record(s, k_avg)}
+           "trials": trials, "roofline": kernel_record(s, k_avg, peaks)}
     s.ctx.destroy()
     del s
     torch.cuda.empty_cache()
@@ -1130,7 +1197,11 @@ def main():
     print(f"bench: path {kernel_name(s)} splits {s.splits}", file=sys.stderr, flush=True)
     use_graph = not args.no_graph
     steps = args.steps
-    ms_per_step, k_avg_s = measure(s, steps, args.warmup, use_graph)
+    ms_per_step, k_avg_s, trials = measure(s, steps, args.warmup, use_graph, args.trials)
+    peaks = None
+    if not args.no_peaks:
+        print("bench: measuring the copy and matrix-core peaks", file=sys.stderr, flush=True)
+        peaks = measured_peaks(torch, s.sa)
     nset = len(s.idxs)
     tokens = s.tokens_per_step()
     result = {
@@ -1147,7 +1218,9 @@ def main():
         "dtype": s.dtype_name(),
         "data": "synthetic",
         "config": s.config(use_graph, nset, tokens, ms_per_step),
-        "roofline": kernel_record(s, k_avg_s),
+        "roofline": kernel_record(s, k_avg_s, peaks),
+        "trials": trials,
+        "peaks_measured": peaks,
     }
     if args.workload == "decode_bf16" and not args.no_also:
         print("bench: concat-append copy figure", file=sys.stderr, flush=True)
@@ -1169,7 +1242,7 @@ def main():
         also = []
         for name in ("decode_fp8", "prefill_bf16"):
             print(f"bench: also {name}", file=sys.stderr, flush=True)
-            also.append(also_record(name, args))
+            also.append(also_record(name, args, peaks))
         result["also"] = also
     print(json.dumps(result), flush=True)
 

@@ -479,6 +479,29 @@ sa_status sparse_attn_profile_enable(sparse_attn_ctx* ctx, int32_t max_launches)
  * number of timed launches since the last read, and start counting again. */
 sa_status sparse_attn_profile_read(sparse_attn_ctx* ctx, double* total_ms, int64_t* launches);
 
+/* Measurement aids (not part of the attention path): kernels that measure the
+ * device's attainable peaks, against which the kernels' roofline fractions are
+ * reported beside the vendor figures. Both launch asynchronously on the
+ * context stream; the caller times them (e.g. with events on that stream).
+ *
+ * sparse_attn_measure_copy: copies `bytes` from src to dst (device buffers,
+ * 16-byte aligned, not overlapping, bytes a positive multiple of 16) with
+ * streaming loads and stores; HBM traffic = 2 * bytes.
+ * sparse_attn_measure_read: reads `bytes` from src (16-byte aligned, bytes a
+ * positive multiple of 16) with streaming loads; sink is device uint32
+ * [SA_PEAK_READ_SINK_WORDS], of which the first
+ * min(ceil(bytes / 16384), 1024) * 256 words are written (values meaningless).
+ * sparse_attn_measure_mfma: `workgroups` workgroups of 4 waves, each wave
+ * running iters x 8 independent bf16 16x16x32 matrix-core products, i.e.
+ * workgroups * 4 * iters * 8 * 16384 flops; out is device float
+ * [workgroups * 256] (written, values meaningless). workgroups in 1..65536,
+ * iters in 1..2^20.
+ * Host errors: SA_E_ARG for the conditions above. */
+#define SA_PEAK_READ_SINK_WORDS (1024 * 256)
+sa_status sparse_attn_measure_copy(sparse_attn_ctx* ctx, void* dst, const void* src, int64_t bytes);
+sa_status sparse_attn_measure_read(sparse_attn_ctx* ctx, uint32_t* sink, const void* src, int64_t bytes);
+sa_status sparse_attn_measure_mfma(sparse_attn_ctx* ctx, float* out, int64_t workgroups, int32_t iters);
+
 /* Library version string. */
 const char* sparse_attn_version(void);
 

@@ -32,6 +32,7 @@ SA_ERR_INDEX_ANY, SA_ERR_APPEND_ANY = 512, 1024
 SA_STATIC_SCRATCH_BYTES = 48 << 20
 SA_ERR_CSA_GEOMETRY, SA_ERR_CSA_DENOM, SA_ERR_INDEX_NONFINITE = 0x100, 0x800, 0x1000
 SA_ERR_INDEX_TIE = 0x2000
+SA_PEAK_READ_SINK_WORDS = 1024 * 256
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_DTYPE", 4: "SA_E_CAPACITY",
                 5: "SA_E_UNSUPPORTED", 6: "SA_E_HIP", 7: "SA_E_STATE", 8: "SA_E_INDEX"}
@@ -44,6 +45,7 @@ EXPORTS = [
     "sparse_attn_reset_error_async", "sparse_attn_read_error", "sparse_attn_last_error",
     "sparse_attn_query_plan", "sparse_attn_profile_enable", "sparse_attn_profile_read",
     "sparse_attn_version", "sparse_attn_forward_latent_static",
+    "sparse_attn_measure_copy", "sparse_attn_measure_read", "sparse_attn_measure_mfma",
 ]
 
 
@@ -113,6 +115,9 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
         "sparse_attn_version": ([], ctypes.c_char_p),
         "sparse_attn_forward_latent_static": ([V, I64, I64, V, I64, V, V, I32, I64, ctypes.c_float,
                                                ctypes.c_float, V, V], st),
+        "sparse_attn_measure_copy": ([V, V, V, I64], st),
+        "sparse_attn_measure_read": ([V, V, V, I64], st),
+        "sparse_attn_measure_mfma": ([V, V, I64, I32], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -307,6 +312,21 @@ class Context:
         ms, n = ctypes.c_double(), ctypes.c_int64()
         self._check(self.lib.sparse_attn_profile_read(self.handle, ctypes.byref(ms), ctypes.byref(n)))
         return float(ms.value), int(n.value)
+
+    def measure_copy(self, dst, src, nbytes):
+        """Streaming device copy of nbytes (peak probe; HBM traffic 2 * nbytes)."""
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_measure_copy(self.handle, _ptr(dst), _ptr(src), nbytes))
+
+    def measure_read(self, sink, src, nbytes):
+        """Streaming device read of nbytes (peak probe); sink: uint32 [SA_PEAK_READ_SINK_WORDS]."""
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_measure_read(self.handle, _ptr(sink), _ptr(src), nbytes))
+
+    def measure_mfma(self, out, workgroups, iters):
+        """bf16 matrix-core loop (peak probe): workgroups * 4 * iters * 8 * 16384 flops."""
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_measure_mfma(self.handle, _ptr(out), workgroups, iters))
 
     def query_plan(self, batch, q_seq, index_heads, width):
         p, s = ctypes.c_int32(), ctypes.c_int32()

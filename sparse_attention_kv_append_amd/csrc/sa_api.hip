@@ -229,6 +229,30 @@ sa_status sparse_attn_reset_error_async(sparse_attn_ctx* c) {
   return sa::launch_reset_error(c);
 }
 
+sa_status sparse_attn_measure_copy(sparse_attn_ctx* c, void* dst, const void* src, int64_t bytes) {
+  if (!live(c)) return SA_E_STATE;
+  if (!dst || !src || bytes < 16 || bytes % 16 || ((uintptr_t)dst | (uintptr_t)src) % 16)
+    return set_error(c, SA_E_ARG, "measure_copy: NULL buffer, or size or address not a positive multiple of 16");
+  const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
+  if (d < s + (uintptr_t)bytes && s < d + (uintptr_t)bytes)
+    return set_error(c, SA_E_ARG, "measure_copy: buffers overlap");
+  return sa::launch_peak_copy(c, dst, src, bytes, nullptr);
+}
+
+sa_status sparse_attn_measure_read(sparse_attn_ctx* c, uint32_t* sink, const void* src, int64_t bytes) {
+  if (!live(c)) return SA_E_STATE;
+  if (!sink || !src || bytes < 16 || bytes % 16 || (uintptr_t)src % 16)
+    return set_error(c, SA_E_ARG, "measure_read: NULL buffer, or size or address not a positive multiple of 16");
+  return sa::launch_peak_copy(c, nullptr, src, bytes, sink);
+}
+
+sa_status sparse_attn_measure_mfma(sparse_attn_ctx* c, float* out, int64_t workgroups, int32_t iters) {
+  if (!live(c)) return SA_E_STATE;
+  if (!out || workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20))
+    return set_error(c, SA_E_ARG, "measure_mfma: NULL output, workgroups outside 1..65536 or iters outside 1..2^20");
+  return sa::launch_peak_mfma(c, out, workgroups, iters);
+}
+
 sa_status sparse_attn_kv_append(sparse_attn_ctx* c, int64_t batch, const void* past_k,
                                 const void* past_v, int64_t past_capacity, const int32_t* past_len,
                                 const void* cur_k, const void* cur_v, int64_t cur_len,

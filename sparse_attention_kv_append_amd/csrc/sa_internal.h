@@ -117,6 +117,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---- host launchers (one per translation unit) ---------------------------
 
 sa_status launch_reset_error(sparse_attn_ctx* c);
+constexpr int PEAK_READ_BLOCKS = 1024;  // workgroups (of 256 threads) of the read probe
+sa_status launch_peak_copy(sparse_attn_ctx* c, void* dst, const void* src, int64_t bytes, void* sink);
+sa_status launch_peak_mfma(sparse_attn_ctx* c, float* out, int64_t blocks, int iters);
 sa_status launch_append_copy(sparse_attn_ctx* c, int64_t batch, int64_t heads, int64_t row_bytes,
                              const void* past, int64_t past_cap, const int32_t* past_len,
                              const void* cur, int64_t cur_len, void* present, int64_t present_cap,
