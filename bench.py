@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--workload", default="decode_bf16",
                    choices=["decode_bf16", "decode_fp8", "prefill_bf16", "dense_gqa", "csa_decode",
-                            "csa_index_decode", "capacity_decode", "gqa_decode_b2"])
+                            "csa_index_decode", "capacity_decode", "capacity_latent_decode", "gqa_decode_b2"])
     p.add_argument("--rotate", type=int, default=8, help="independent (query, index) sets")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
@@ -259,12 +259,12 @@ class Setup:
 
 class CapacitySetup(Setup):
     """Capacity-mode decode with the optional attention bias (IndexShare's
-    fixed-capacity present): bf16 K and V caches of `capacity` rows drawn on
-    the device, per-batch live lengths carried only by the bias's -inf
-    frontier, and a step of capacity_lengths (valid length and write position
-    from the bias) -> in-place kv_append at the write position ->
-    forward_bias with fused validation against the recovered lengths (one
-    sparse_attn_capacity_step call)."""
+    fixed-capacity present): bf16 K and V caches (or one shared-latent cache)
+    of `capacity` rows drawn on the device, per-batch live lengths carried
+    only by the bias's -inf frontier, and a step of capacity_lengths (valid
+    length and write position from the bias) -> in-place kv_append at the
+    write position -> forward_bias with fused validation against the
+    recovered lengths (one sparse_attn_capacity_step call)."""
 
     def __init__(self, name, rotate):
         import numpy as np
@@ -278,18 +278,20 @@ class CapacitySetup(Setup):
         self.R = rotate
         dev = "cuda"
         B, Hq, Hkv, Sq, Dk, Dv, cap = w.batch, w.hq, w.hkv, w.q_seq, w.dk, w.dv, w.cap
-        assert w.dtype == W.DT_BF16 and w.layout == W.LAYOUT_SEPARATE
+        assert w.dtype == W.DT_BF16 and w.cache_format == W.CACHE_DENSE
+        self.latent = latent = w.layout == W.LAYOUT_SHARED_LATENT
         self.ctx = sa.Context(num_heads=Hq, kv_num_heads=Hkv, head_dim_qk=Dk, head_dim_v=Dv, dtype=w.dtype,
-                              kv_layout=sa.SA_KV_SEPARATE, scale=w.scale, softcap=w.softcap, max_batch=B,
+                              kv_layout=sa.SA_KV_SHARED_LATENT if latent else sa.SA_KV_SEPARATE,
+                              scale=w.scale, softcap=w.softcap, max_batch=B,
                               max_q_seq=Sq, max_index_width=w.width, max_cache_len=cap)
         seed = w.seed
         gen = lambda shape, s: W.torch_normal_bf16(shape, s, dev)
         self.k = gen((B, Hkv, cap, Dk), seed * 1000)
-        self.v = gen((B, Hkv, cap, Dv), seed * 1000 + 1)
+        self.v = None if latent else gen((B, Hkv, cap, Dv), seed * 1000 + 1)
         self.cur_k = gen((B, Hkv, w.cur, Dk), seed * 1000 + 998)
-        self.cur_v = gen((B, Hkv, w.cur, Dv), seed * 1000 + 999)
+        self.cur_v = None if latent else gen((B, Hkv, w.cur, Dv), seed * 1000 + 999)
         # the caches as drawn, before any step writes the current rows (oracle inputs)
-        self.k0, self.v0 = self.k.clone(), self.v.clone()
+        self.k0, self.v0 = self.k.clone(), None if latent else self.v.clone()
         rng = np.random.default_rng(seed)
         self.valid, bias32 = W.capacity_frontier(w, rng)
         self.bias_host = W.store_elems(bias32, w.dtype)
@@ -305,9 +307,11 @@ class CapacitySetup(Setup):
         self.wp = torch.zeros((B,), dtype=torch.int32, device=dev)
         self.fp8 = False
         self.selected = [int((ih >= 0).sum()) for ih in self.idx_host]
-        # a biased forward runs on the grouped-query kernel where the plan takes it, else generic
+        # a biased forward runs on the grouped-query or shared-latent MFMA
+        # kernel where the plan takes one (the general latent kernel on a bf16
+        # shared-latent cache, never the decode kernel), else generic
         plan, nsplit = self.ctx.query_plan(B, Sq, 1, w.width)
-        self.path, self.splits = (4, nsplit) if plan == 4 else (0, 1)
+        self.path, self.splits = (plan, nsplit) if plan in (2, 3, 4) else (0, 1)
 
     def fused_step(self):
         return False
@@ -332,8 +336,10 @@ class CapacitySetup(Setup):
 
     def config(self, use_graph, nset, tokens, ms_per_step):
         w = self.w
+        layout = (f"one shared-latent row of {w.dk} dims (V = its first {w.dv})" if self.latent
+                  else f"{w.hkv} kv heads, head dim {w.dk}")
         return {"workload": f"{w.name}: capacity mode, batch {w.batch}, q_seq {w.q_seq}, {w.hq} q heads / "
-                            f"{w.hkv} kv heads, head dim {w.dk}, capacity {w.cap}, live lengths "
+                            f"{layout}, capacity {w.cap}, live lengths "
                             f"{int(self.valid.min())}..{int(self.valid.max())} from a [B, 1, {w.q_seq}, {w.cap}] "
                             f"bf16 bias, {w.cur} current row, top-{w.topk}, "
                             f"{'graph replay' if use_graph else 'eager'}, {nset} rotating index sets",
@@ -344,11 +350,13 @@ class CapacitySetup(Setup):
 
     def oracle_inputs(self, b, r=0):
         """Host copies of batch entry b's inputs (storage bits): q, past_k,
-        past_v (as drawn), cur_k, cur_v, indices, bias."""
+        past_v (as drawn; None for a shared-latent cache), cur_k, cur_v,
+        indices, bias."""
         np = self.np
-        bits = lambda t: t.contiguous().view(self.torch.int16).cpu().numpy().view(np.uint16)
-        return dict(q=bits(self.qs[r][b:b + 1]), past_k=bits(self.k0[b:b + 1]), past_v=bits(self.v0[b:b + 1]),
-                    cur_k=bits(self.cur_k[b:b + 1]), cur_v=bits(self.cur_v[b:b + 1]),
+        bits = lambda t: None if t is None else t.contiguous().view(self.torch.int16).cpu().numpy().view(np.uint16)
+        one = lambda t: None if t is None else t[b:b + 1]
+        return dict(q=bits(self.qs[r][b:b + 1]), past_k=bits(self.k0[b:b + 1]), past_v=bits(one(self.v0)),
+                    cur_k=bits(self.cur_k[b:b + 1]), cur_v=bits(one(self.cur_v)),
                     indices=self.idx_host[r][b:b + 1], bias=self.bias_host[b:b + 1])
 
     def oracle_y(self, inp, threads):
@@ -359,7 +367,7 @@ class CapacitySetup(Setup):
         valid, wpos = oracle.capacity_lengths(inp["bias"], w.cap, w.cur, batch=1, heads=w.hq, q_seq=w.q_seq,
                                               bias_dtype=w.dtype)
         pk = oracle.kv_append(inp["past_k"].copy(), wpos, inp["cur_k"])
-        pv = oracle.kv_append(inp["past_v"].copy(), wpos, inp["cur_v"])
+        pv = None if inp["past_v"] is None else oracle.kv_append(inp["past_v"].copy(), wpos, inp["cur_v"])
         y = oracle.forward(inp["q"], pk, pv, inp["indices"], q_dtype=w.dtype, cache_fmt=w.dtype,
                            kv_layout=w.layout, hkv=w.hkv, dv=w.dv, scale=w.scale, softcap=w.softcap,
                            bias=inp["bias"], threads=threads)
@@ -695,7 +703,7 @@ def make_setup(name, rotate):
 
 
 def kernel_name(setup):
-    if setup.path == 2 and setup.splits > 1:
+    if setup.path == 2 and setup.splits > 1 and not isinstance(setup, CapacitySetup):
         return "latent_decode_kernel"
     return {0: "generic_forward_kernel", 1: "mla_forward_kernel", 2: "latent_forward_kernel",
             3: "pair_forward_kernel", 4: "gqa_forward_kernel", 5: "csa_attention_kernel",

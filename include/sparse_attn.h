@@ -224,8 +224,11 @@ sa_status sparse_attn_forward(sparse_attn_ctx* ctx, const void* q, int64_t batch
  * For output row (b, h, q) and selected key k (its cache position, clamped as
  * in sparse_attn_forward) the score becomes softcap(scale * q.k) +
  * bias[b, h, q, k]; a row whose scores are all -inf gives zeros. A biased
- * call runs on the grouped-query kernel (sparse_attn_query_plan path 4) when
- * the configuration takes it, else on the generic vector kernel (path 0). Host errors: those of sparse_attn_forward, and
+ * call runs on the MFMA kernel of its layout (sparse_attn_query_plan path 4
+ * grouped-query, 2 bf16 shared-latent, 3 fp8 shared-latent records; on path
+ * 2 the general latent kernel with its split-K combine, not the decode
+ * kernel) when the configuration takes one, else on the generic vector
+ * kernel (path 0). Host errors: those of sparse_attn_forward, and
  * SA_E_SHAPE for a rank above 4 or an extent that does not broadcast.
  * Asynchronous and capturable. */
 sa_status sparse_attn_forward_bias(sparse_attn_ctx* ctx, const void* q, int64_t batch, int64_t q_seq,
@@ -256,21 +259,26 @@ sa_status sparse_attn_capacity_lengths(sparse_attn_ctx* ctx, const void* bias, c
                                        int64_t cache_capacity, int64_t cur_len, int32_t* valid_len,
                                        int32_t* write_pos);
 
-/* One capacity-mode attention step over separate K and V caches kept in
- * place (IndexShare's capacity branch: `capacity_write_pos`, the two
- * `build_present_capacity` launches and the rows), the same as
+/* One capacity-mode attention step over a cache kept in place (IndexShare's
+ * capacity branch: `capacity_write_pos`, the `build_present_capacity`
+ * launches and the rows; the branch does not depend on the layout), the
+ * same as
  *   [sparse_attn_reset_error_async if reset_error]
  *   sparse_attn_capacity_lengths(bias, ..., cur_len, valid_len, write_pos)
  *   sparse_attn_kv_append(past = present = cache, past_len = write_pos, cur)
  *   sparse_attn_forward_bias(present = cache, valid_len, bias, fused_validate = 1)
  *   cache_k, cache_v [B, Hkv, cache_capacity, D] read and written; cur_k,
- *                    cur_v [B, Hkv, cur_len, D]; 1 <= cur_len <= cache_capacity
+ *                    cur_v [B, Hkv, cur_len, D]; 1 <= cur_len <= cache_capacity.
+ *                    A shared-latent cache passes cache_k (its bf16 rows or
+ *                    fp8 records) and cur_k (rows in the cache's own format)
+ *                    with cache_v = cur_v = NULL.
  *   valid_len, write_pos  device int32 [B] outputs
- * The lengths and the append are one launch when the rows are a multiple of
- * 16 bytes and the four tensors 16-byte aligned (Dk == Dv). Host errors:
- * those of the four calls, checked before anything is launched;
- * SA_E_UNSUPPORTED for a shared-latent or fp8 cache. Asynchronous and
- * capturable. */
+ * The lengths and the append are one launch when the cache is dense, its rows
+ * a multiple of 16 bytes and the tensors 16-byte aligned (Dk == Dv for
+ * separate caches). Host errors: those of the four calls, checked before
+ * anything is launched; SA_E_ARG for a V tensor passed with a shared-latent
+ * cache or missing with separate ones; SA_E_UNSUPPORTED for separate caches
+ * that are not dense. Asynchronous and capturable. */
 sa_status sparse_attn_capacity_step(sparse_attn_ctx* ctx, const void* q, int64_t batch, int64_t q_seq,
                                     void* cache_k, void* cache_v, int64_t cache_capacity, const void* cur_k,
                                     const void* cur_v, int64_t cur_len, const void* indices,

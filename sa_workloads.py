@@ -245,6 +245,13 @@ CAPACITY_WORKLOADS = {
                                 cache_format=CACHE_DENSE, scale=float(1.0 / np.sqrt(np.float32(128.0))),
                                 pattern="causal_prefill", seed=6, capacity=16384,
                                 extra={"valid_lo": 8192}),
+    # the decode_bf16 shapes (64 heads over one 576-dim shared-latent row of
+    # which the first 512 dims are V) in capacity mode
+    "capacity_latent_decode": Workload("capacity_latent_decode", batch=32, hq=64, hkv=1, q_seq=1, dk=576,
+                                       dv=512, past=0, cur=1, width=2048, topk=2048, dtype=DT_BF16,
+                                       layout=LAYOUT_SHARED_LATENT, cache_format=CACHE_DENSE,
+                                       scale=float(1.0 / np.sqrt(np.float32(576.0))), pattern="causal_prefill",
+                                       seed=7, capacity=32769, extra={"valid_lo": 16384}),
 }
 
 

@@ -7,12 +7,13 @@
 // rows go to write = valid - cur_len (0 when valid < cur_len).
 //
 // The pages give one thread per batch entry looping over every broadcast
-// (h, q, k). Here one 256-thread workgroup per batch entry reads each element
-// of the entry's slice of the bias exactly once, coalesced, in 16-byte
-// vectors (four per thread in flight) when the rows are whole vectors: an
-// extent of 1 along heads or queries is not expanded, and an extent of 1
-// along keys makes a finite element stand for every column. Finiteness is
-// read from the exponent bits. The per-thread maxima are reduced with wave
+// (h, q, k). Here one 256-thread workgroup per batch entry reads the entry's
+// slice of the bias coalesced: in 16-byte vectors (four per thread in
+// flight) when the rows are whole vectors, else each row from its end down,
+// stopping at the first chunk that holds a finite element. An extent of 1
+// along heads or queries is not expanded, and an extent of 1 along keys
+// makes a finite element stand for every column. Finiteness is read from the
+// exponent bits (vector path). The per-thread maxima are reduced with wave
 // shuffles and one LDS atomic per wave.
 #include "sa_internal.h"
 #include "sa_mfma_dev.h"
@@ -74,11 +75,30 @@ __device__ __forceinline__ int capacity_scan(const void* __restrict__ bias, int6
         best = max(best, vec_best<DT>(vals[u], (v0 + (int64_t)u * kCapThreads) * PER, bd3, keys));
     }
   } else {
-    for (int64_t e = threadIdx.x; e < n; e += kCapThreads) {
-      const float v = load_elem<DT>(bias, base + e);
-      if (isfinite(v)) {
-        const int64_t k = bd3 == 1 ? keys - 1 : e % bd3;
-        best = max(best, (int)(k + 1));
+    // rows that are not whole vectors: each (h, q) row is scanned from its
+    // last column down in chunks of kCapThreads * 8 columns (eight loads per
+    // thread in flight), and the row ends at the first chunk holding a finite
+    // element, since no lower column can raise the row's maximum; a frontier
+    // near the end of the row touches one or two chunks
+    constexpr int CH = kCapThreads * 8;
+    const int64_t rows = bd1 * bd2;
+    for (int64_t r = 0; r < rows; r++) {
+      const int64_t rb = base + r * bd3;
+      for (int64_t top = bd3; top > 0; top -= CH) {
+        int found = 0;  // 1 + the largest finite column of this chunk seen by this thread
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const int64_t k = top - 1 - (threadIdx.x + (int64_t)u * kCapThreads);
+          v[u] = k >= 0 ? load_elem<DT>(bias, rb + k) : __builtin_nanf("");
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const int64_t k = top - 1 - (threadIdx.x + (int64_t)u * kCapThreads);
+          if (isfinite(v[u])) found = max(found, bd3 == 1 ? (int)keys : (int)(k + 1));
+        }
+        best = max(best, found);
+        if (__syncthreads_or(found > 0)) break;  // uniform
       }
     }
   }
@@ -123,7 +143,8 @@ capacity_append_kernel(const void* __restrict__ bias, int64_t bd0, int64_t bd1, 
   }
   const int64_t ru = row_bytes / 16;     // 16-byte units per row
   const int64_t per = heads * cur_len * ru;  // units of one tensor for this batch entry
-  for (int64_t u = threadIdx.x; u < 2 * per; u += kCapThreads) {
+  const int64_t units = cache_v ? 2 * per : per;  // a shared-latent cache has no V tensor
+  for (int64_t u = threadIdx.x; u < units; u += kCapThreads) {
     const bool second = u >= per;
     const int64_t e = second ? u - per : u;
     const int64_t h = e / (cur_len * ru);

@@ -66,7 +66,11 @@ __host__ __device__ constexpr int step_reads(int j) {
 // every workgroup writes its batch's new rows itself before it gathers, so it
 // reads its own writes whatever other workgroups do; with `reset` the
 // launch's last workgroup replaces the error word instead of adding to it.
-template <bool I64, bool FUSED, bool SOFTCAP, bool APPEND>
+// BIAS: the additive attention bias (bf16, IndexShare `bias_at`) of each
+// selected key is added to its scaled (and softcapped) score; its shape,
+// right-aligned against [batch, 64, q_seq, cap], is bd0..bd3, each extent 1
+// (broadcast) or the full one.
+template <bool I64, bool FUSED, bool SOFTCAP, bool APPEND, bool BIAS>
 __global__ void __launch_bounds__(lat::THREADS, 1)
 latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
                       const void* __restrict__ idx, const int32_t* __restrict__ valid_len,
@@ -76,7 +80,8 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
                       float softcap, ErrorBlock* __restrict__ eb,
                       unsigned long long* __restrict__ row_key, unsigned* __restrict__ row_done,
                       const uint8_t* __restrict__ cur, const int32_t* __restrict__ past_len,
-                      int32_t* __restrict__ present_len, int64_t cur_len, int reset) {
+                      int32_t* __restrict__ present_len, int64_t cur_len, int reset,
+                      const uint16_t* __restrict__ bias, int64_t bd0, int64_t bd1, int64_t bd2, int64_t bd3) {
   using namespace lat;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lds_u8* ring = (lds_u8*)lds_raw;
@@ -158,6 +163,11 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
     ld_off[i] = (p ^ (R & 6)) << 4;
   }
   const float f = SOFTCAP ? kLog2eL : scale * kLog2eL;  // scores -> log2 units
+  // the bias row of this lane's head (element 0 when the key extent is 1)
+  const uint16_t* brow = bias;
+  if constexpr (BIAS)
+    brow = bias + (((bd0 == 1 ? 0 : b) * bd1 + (bd1 == 1 ? 0 : head)) * bd2 + (bd2 == 1 ? 0 : qi)) * bd3;
+  const bool bkey = BIAS && bd3 != 1;
 
   // ---- softmax state. Each head's reference m_ref is its first tile's max
   // and then stays fixed: exp2(x - m_ref) of a later, larger score is a
@@ -367,6 +377,22 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
 #pragma unroll
         for (int kh = 0; kh < 2; kh++) sa[kh][0] = sa[kh][1] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
       };
+      // BIAS: the lane's eight bias values of tile tt (its head, the keys of
+      // slots 4g + i and 16 + 4g + i), loaded a tile ahead of their softmax as
+      // ordinary loads (the compiler places the wait at the use; they are
+      // older than the refill's gathers, so the counted gather waits cover
+      // them too). Staged keys are already clamped into the cache.
+      uint16_t bv[8];
+      auto bias_load = [&](int tt) {
+        if constexpr (BIAS) {
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            const int slot = tt * KT + 4 * g + (i < 4 ? i : 12 + i);
+            const int key = slot < kcount ? keys_s[slot] : 0;
+            bv[i] = brow[bkey ? key : 0];
+          }
+        }
+      };
       // softmax of tile tt from sa; lane holds keys 4g + r and 16 + 4g + r of
       // its head. Scores are taken to log2 units with one multiply by f.
       // Returns P^T.
@@ -382,6 +408,11 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
 #pragma unroll
           for (int i = 0; i < 8; i++) x[i] = softcap * tanhf(x[i] * scale / softcap);
         }
+        if constexpr (BIAS) {
+          // the bias joins the scaled (and softcapped) score, then log2 units
+#pragma unroll
+          for (int i = 0; i < 8; i++) x[i] = ((SOFTCAP ? x[i] : x[i] * scale) + bf16_to_f32(bv[i])) * kLog2eL;
+        }
         if ((tt + 1) * KT > kcount) {  // uniform: only the last tile has empty slots
           const int slot_base = tt * KT + 4 * g;
 #pragma unroll
@@ -390,8 +421,10 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
         }
         // scores in log2 units, rounded once: the maximum then gives exp2(0)
         // exactly (an FMA against a rounded maximum can overflow for huge scores)
+        if constexpr (!BIAS) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) x[i] *= f;
+          for (int i = 0; i < 8; i++) x[i] *= f;
+        }
         float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         tmax = max_x32(max_x16(tmax));
         m_seen = fmaxf(m_seen, tmax);
@@ -412,6 +445,7 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
 
       // ---- tile 0: S alone, the reads KD k-steps ahead of their MFMAs
       // (tiles 1 .. NSTAGE-2 may stay in flight)
+      bias_load(0);
       wait_vm<(NSTAGE - 2) * WAVE_LOADS>();
       lds_barrier();
       set_k(0);
@@ -438,6 +472,7 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
         lds_barrier();          // and for everyone; tile t-1's slot is free
         const int tn = t + NSTAGE - 1;  // refills tile t-1's slot; offsets read last iteration
         gather_keys(tn + 1);  // in order ahead of the step reads; consumed after the softmax
+        bias_load(t + 1);
         set_k(t + 1);
         set_v(t);
         zero_s();
@@ -587,7 +622,7 @@ bool latent_supported(const sa_config& cfg, int64_t index_heads) {
          cfg.max_cache_len <= (int64_t)(0x7fffffffLL / lat::ROWB);
 }
 
-static bool g_latent_attr[12] = {};
+static bool g_latent_attr[20] = {};
 
 sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused, const AppendArgs* app) {
   using namespace lat;
@@ -601,20 +636,30 @@ sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits
   const bool cap_on = a.softcap != 0.0f;
   if (app && (!fused || app->cur_len < 0 || app->cur_len > kFusedAppendRows))
     return set_error(c, SA_E_STATE, "forward: in-launch append needs fused validation and at most 8 rows");
+  const bool bias_on = a.bias != nullptr;
+  if (app && bias_on) return set_error(c, SA_E_STATE, "forward: in-launch append takes no bias");
   const int variant = app ? 8 + (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0)
-                          : (a.idx64 ? 1 : 0) + (fused ? 2 : 0) + (cap_on ? 4 : 0);
-  const void* fns[12] = {(const void*)latent_forward_kernel<false, false, false, false>,
-                         (const void*)latent_forward_kernel<true, false, false, false>,
-                         (const void*)latent_forward_kernel<false, true, false, false>,
-                         (const void*)latent_forward_kernel<true, true, false, false>,
-                         (const void*)latent_forward_kernel<false, false, true, false>,
-                         (const void*)latent_forward_kernel<true, false, true, false>,
-                         (const void*)latent_forward_kernel<false, true, true, false>,
-                         (const void*)latent_forward_kernel<true, true, true, false>,
-                         (const void*)latent_forward_kernel<false, true, false, true>,
-                         (const void*)latent_forward_kernel<true, true, false, true>,
-                         (const void*)latent_forward_kernel<false, true, true, true>,
-                         (const void*)latent_forward_kernel<true, true, true, true>};
+                          : (bias_on ? 12 : 0) + (a.idx64 ? 1 : 0) + (fused ? 2 : 0) + (cap_on ? 4 : 0);
+  const void* fns[20] = {(const void*)latent_forward_kernel<false, false, false, false, false>,
+                         (const void*)latent_forward_kernel<true, false, false, false, false>,
+                         (const void*)latent_forward_kernel<false, true, false, false, false>,
+                         (const void*)latent_forward_kernel<true, true, false, false, false>,
+                         (const void*)latent_forward_kernel<false, false, true, false, false>,
+                         (const void*)latent_forward_kernel<true, false, true, false, false>,
+                         (const void*)latent_forward_kernel<false, true, true, false, false>,
+                         (const void*)latent_forward_kernel<true, true, true, false, false>,
+                         (const void*)latent_forward_kernel<false, true, false, true, false>,
+                         (const void*)latent_forward_kernel<true, true, false, true, false>,
+                         (const void*)latent_forward_kernel<false, true, true, true, false>,
+                         (const void*)latent_forward_kernel<true, true, true, true, false>,
+                         (const void*)latent_forward_kernel<false, false, false, false, true>,
+                         (const void*)latent_forward_kernel<true, false, false, false, true>,
+                         (const void*)latent_forward_kernel<false, true, false, false, true>,
+                         (const void*)latent_forward_kernel<true, true, false, false, true>,
+                         (const void*)latent_forward_kernel<false, false, true, false, true>,
+                         (const void*)latent_forward_kernel<true, false, true, false, true>,
+                         (const void*)latent_forward_kernel<false, true, true, false, true>,
+                         (const void*)latent_forward_kernel<true, true, true, false, true>};
   if (!g_latent_attr[variant]) {
     hipError_t e = hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
     if (e != hipSuccess) return check_hip(c, e, "forward (latent) LDS attribute");
@@ -627,24 +672,33 @@ sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits
   int32_t* prlen = app ? app->present_len : nullptr;
   const int64_t clen = app ? app->cur_len : 0;
   const int reset = app ? app->reset : 0;
-#define SA_LAT(I, F, C, A)                                                                            \
-  SA_MAIN_LAUNCH(pe, (latent_forward_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,          \
+#define SA_LAT(I, F, C, A, B)                                                                         \
+  SA_MAIN_LAUNCH(pe, (latent_forward_kernel<I, F, C, A, B>), grid, block, LDS_BYTES, c->stream,       \
                      (const uint16_t*)a.q, (uint8_t*)a.k, a.idx, a.valid_len, (uint16_t*)a.y,         \
                      c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width, splits, a.scale,     \
-                     a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset)
+                     a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset,       \
+                     (const uint16_t*)a.bias, a.bd[0], a.bd[1], a.bd[2], a.bd[3])
   switch (variant) {
-    case 0: SA_LAT(false, false, false, false); break;
-    case 1: SA_LAT(true, false, false, false); break;
-    case 2: SA_LAT(false, true, false, false); break;
-    case 3: SA_LAT(true, true, false, false); break;
-    case 4: SA_LAT(false, false, true, false); break;
-    case 5: SA_LAT(true, false, true, false); break;
-    case 6: SA_LAT(false, true, true, false); break;
-    case 7: SA_LAT(true, true, true, false); break;
-    case 8: SA_LAT(false, true, false, true); break;
-    case 9: SA_LAT(true, true, false, true); break;
-    case 10: SA_LAT(false, true, true, true); break;
-    default: SA_LAT(true, true, true, true); break;
+    case 0: SA_LAT(false, false, false, false, false); break;
+    case 1: SA_LAT(true, false, false, false, false); break;
+    case 2: SA_LAT(false, true, false, false, false); break;
+    case 3: SA_LAT(true, true, false, false, false); break;
+    case 4: SA_LAT(false, false, true, false, false); break;
+    case 5: SA_LAT(true, false, true, false, false); break;
+    case 6: SA_LAT(false, true, true, false, false); break;
+    case 7: SA_LAT(true, true, true, false, false); break;
+    case 8: SA_LAT(false, true, false, true, false); break;
+    case 9: SA_LAT(true, true, false, true, false); break;
+    case 10: SA_LAT(false, true, true, true, false); break;
+    case 11: SA_LAT(true, true, true, true, false); break;
+    case 12: SA_LAT(false, false, false, false, true); break;
+    case 13: SA_LAT(true, false, false, false, true); break;
+    case 14: SA_LAT(false, true, false, false, true); break;
+    case 15: SA_LAT(true, true, false, false, true); break;
+    case 16: SA_LAT(false, false, true, false, true); break;
+    case 17: SA_LAT(true, false, true, false, true); break;
+    case 18: SA_LAT(false, true, true, false, true); break;
+    default: SA_LAT(true, true, true, false, true); break;
   }
 #undef SA_LAT
   sa_status s = check_hip(c, hipGetLastError(), "forward (latent)");

@@ -83,7 +83,11 @@ struct PairRaw {
 // batch's new records itself and waits for them before it loads any, so it
 // reads its own writes; with `reset` the launch's last workgroup replaces
 // the error word instead of adding to it.
-template <bool I64, bool FUSED, bool SOFTCAP, bool APPEND>
+// BIAS: the additive attention bias (bf16, IndexShare `bias_at`) of each
+// selected key is added to its scaled (and softcapped) score; its shape,
+// right-aligned against [batch, 64, q_seq, cap], is bd0..bd3, each extent 1
+// (broadcast) or the full one.
+template <bool I64, bool FUSED, bool SOFTCAP, bool APPEND, bool BIAS>
 __global__ void __launch_bounds__(pk::THREADS, 1)
 pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
                     const void* __restrict__ idx, const int32_t* __restrict__ valid_len,
@@ -92,7 +96,8 @@ pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
                     float softcap, ErrorBlock* __restrict__ eb,
                     unsigned long long* __restrict__ row_key, unsigned* __restrict__ row_done,
                     const void* __restrict__ cur, const int32_t* __restrict__ past_len,
-                    int32_t* __restrict__ present_len, int64_t cur_len, int reset, int cur_quant) {
+                    int32_t* __restrict__ present_len, int64_t cur_len, int reset, int cur_quant,
+                    const uint16_t* __restrict__ bias, int64_t bd0, int64_t bd1, int64_t bd2, int64_t bd3) {
   using namespace pk;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   lds_u8* ring = (lds_u8*)lds_raw;
@@ -182,6 +187,14 @@ pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
   }
   const uint32_t wrope = (uint32_t)(dk * ROWB + 16 * (64 + (dj ^ (dk & 6))));
   const float f = SOFTCAP ? kLog2eL : scale * kLog2eL;  // scores -> log2 units
+  // the bias rows of this lane's two heads (element 0 when the key extent is 1)
+  const uint16_t* brow0 = bias;
+  int64_t bstep = 0;  // head0 + 16 relative to head0
+  if constexpr (BIAS) {
+    brow0 = bias + (((bd0 == 1 ? 0 : b) * bd1 + (bd1 == 1 ? 0 : head0)) * bd2 + (bd2 == 1 ? 0 : qi)) * bd3;
+    bstep = bd1 == 1 ? 0 : 16 * bd2 * bd3;
+  }
+  const bool bkey = BIAS && bd3 != 1;
   const uint32_t px_own = (uint32_t)(uintptr_t)(px + (wave * 64 + lane) * 16);
   const uint32_t px_peer = (uint32_t)(uintptr_t)(px + ((wave ^ 1) * 64 + lane) * 16);
   constexpr int PXH = WAVES * 64 * 16;  // second exchange buffer
@@ -344,6 +357,24 @@ pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
         ds_write_b128_off<0>(T + wrope, R.rope);
       };
 
+      // BIAS: the lane's bias values of tile tt (keys of slots 16 half + 4g + i,
+      // heads head0 and head0 + 16), loaded ahead of their softmax as ordinary
+      // loads issued before the record loads of the same iteration (the
+      // compiler's wait at the use leaves those in flight). Staged keys are
+      // already clamped into the cache.
+      uint16_t bv0[4], bv1[4];
+      auto bias_load = [&](int tt) {
+        if constexpr (BIAS) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int slot = tt * KT + 16 * half + 4 * g + i;
+            const int64_t kc = bkey && slot < kcount ? keys_s[slot] : 0;
+            bv0[i] = brow0[kc];
+            bv1[i] = brow0[bstep + kc];
+          }
+        }
+      };
+      bias_load(0);  // before the record loads: its wait leaves them in flight
       PairRaw ra, rb;
       issue(ra, rec_base(0));
       issue(rb, rec_base(1));
@@ -440,6 +471,14 @@ pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
             x1[i] = softcap * tanhf(x1[i] * scale / softcap);
           }
         }
+        if constexpr (BIAS) {
+          // the bias joins the scaled (and softcapped) score, then log2 units
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            x0[i] = ((SOFTCAP ? x0[i] : x0[i] * scale) + bf16_to_f32(bv0[i])) * kLog2eL;
+            x1[i] = ((SOFTCAP ? x1[i] : x1[i] * scale) + bf16_to_f32(bv1[i])) * kLog2eL;
+          }
+        }
         if ((tt + 1) * KT > kcount) {  // uniform: only the last tile has empty slots
           const int slot_base = tt * KT + 16 * half + 4 * g;
 #pragma unroll
@@ -448,10 +487,12 @@ pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
         }
         // scores in log2 units, rounded once: the maximum then gives exp2(0)
         // exactly (an FMA against a rounded maximum can overflow for huge scores)
+        if constexpr (!BIAS) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          x0[i] *= f;
-          x1[i] *= f;
+          for (int i = 0; i < 4; i++) {
+            x0[i] *= f;
+            x1[i] *= f;
+          }
         }
         const float lm0 = fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3]));
         const float lm1 = fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3]));
@@ -519,6 +560,7 @@ pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
       // decode of tile t+2 (its records were loaded one iteration earlier)
       auto iteration = [&](int t, PairRaw& rnext, PairRaw& rdec) {
         lds_barrier();  // tile t+1 decoded, tile t's exchange visible, tile t-1's slot free
+        bias_load(t + 1);         // older than tile t+3's record loads
         issue(rnext, base_next);  // tile t+3
         take_peer(t, pown);
         set_k(t + 1);
@@ -710,7 +752,7 @@ bool pair_supported(const sa_config& cfg, int64_t index_heads) {
          cfg.rope_dim == pk::DK - pk::NOPE && cfg.max_cache_len <= (int64_t)(0x7fffffffLL / pk::REC);
 }
 
-static bool g_pair_attr[12] = {};
+static bool g_pair_attr[20] = {};
 
 sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused, const AppendArgs* app) {
   using namespace pk;
@@ -725,20 +767,30 @@ sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, 
   const bool cap_on = a.softcap != 0.0f;
   if (app && (!fused || app->cur_len < 0 || app->cur_len > kFusedAppendRows))
     return set_error(c, SA_E_STATE, "forward: in-launch append needs fused validation and at most 8 rows");
+  const bool bias_on = a.bias != nullptr;
+  if (app && bias_on) return set_error(c, SA_E_STATE, "forward: in-launch append takes no bias");
   const int variant = app ? 8 + (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0)
-                          : (a.idx64 ? 1 : 0) + (fused ? 2 : 0) + (cap_on ? 4 : 0);
-  const void* fns[12] = {(const void*)pair_forward_kernel<false, false, false, false>,
-                         (const void*)pair_forward_kernel<true, false, false, false>,
-                         (const void*)pair_forward_kernel<false, true, false, false>,
-                         (const void*)pair_forward_kernel<true, true, false, false>,
-                         (const void*)pair_forward_kernel<false, false, true, false>,
-                         (const void*)pair_forward_kernel<true, false, true, false>,
-                         (const void*)pair_forward_kernel<false, true, true, false>,
-                         (const void*)pair_forward_kernel<true, true, true, false>,
-                         (const void*)pair_forward_kernel<false, true, false, true>,
-                         (const void*)pair_forward_kernel<true, true, false, true>,
-                         (const void*)pair_forward_kernel<false, true, true, true>,
-                         (const void*)pair_forward_kernel<true, true, true, true>};
+                          : (bias_on ? 12 : 0) + (a.idx64 ? 1 : 0) + (fused ? 2 : 0) + (cap_on ? 4 : 0);
+  const void* fns[20] = {(const void*)pair_forward_kernel<false, false, false, false, false>,
+                         (const void*)pair_forward_kernel<true, false, false, false, false>,
+                         (const void*)pair_forward_kernel<false, true, false, false, false>,
+                         (const void*)pair_forward_kernel<true, true, false, false, false>,
+                         (const void*)pair_forward_kernel<false, false, true, false, false>,
+                         (const void*)pair_forward_kernel<true, false, true, false, false>,
+                         (const void*)pair_forward_kernel<false, true, true, false, false>,
+                         (const void*)pair_forward_kernel<true, true, true, false, false>,
+                         (const void*)pair_forward_kernel<false, true, false, true, false>,
+                         (const void*)pair_forward_kernel<true, true, false, true, false>,
+                         (const void*)pair_forward_kernel<false, true, true, true, false>,
+                         (const void*)pair_forward_kernel<true, true, true, true, false>,
+                         (const void*)pair_forward_kernel<false, false, false, false, true>,
+                         (const void*)pair_forward_kernel<true, false, false, false, true>,
+                         (const void*)pair_forward_kernel<false, true, false, false, true>,
+                         (const void*)pair_forward_kernel<true, true, false, false, true>,
+                         (const void*)pair_forward_kernel<false, false, true, false, true>,
+                         (const void*)pair_forward_kernel<true, false, true, false, true>,
+                         (const void*)pair_forward_kernel<false, true, true, false, true>,
+                         (const void*)pair_forward_kernel<true, true, true, false, true>};
   if (!g_pair_attr[variant]) {
     hipError_t e = hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
     if (e != hipSuccess) return check_hip(c, e, "forward (fp8 pair) LDS attribute");
@@ -752,24 +804,33 @@ sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, 
   const int64_t clen = app ? app->cur_len : 0;
   const int reset = app ? app->reset : 0;
   const int quant = app ? app->quant : 0;
-#define SA_PAIR(I, F, C, A)                                                                           \
-  SA_MAIN_LAUNCH(pe, (pair_forward_kernel<I, F, C, A>), grid, block, LDS_BYTES, c->stream,            \
+#define SA_PAIR(I, F, C, A, B)                                                                        \
+  SA_MAIN_LAUNCH(pe, (pair_forward_kernel<I, F, C, A, B>), grid, block, LDS_BYTES, c->stream,         \
                      (const uint16_t*)a.q, (uint8_t*)a.k, a.idx, a.valid_len, (uint16_t*)a.y,         \
                      c->partial_o, c->partial_ml, a.q_seq, rows, a.cap, a.width, splits, a.scale,     \
-                     a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset, quant)
+                     a.softcap, c->err, c->row_key, c->row_done, cur, plen, prlen, clen, reset, quant, \
+                     (const uint16_t*)a.bias, a.bd[0], a.bd[1], a.bd[2], a.bd[3])
   switch (variant) {
-    case 0: SA_PAIR(false, false, false, false); break;
-    case 1: SA_PAIR(true, false, false, false); break;
-    case 2: SA_PAIR(false, true, false, false); break;
-    case 3: SA_PAIR(true, true, false, false); break;
-    case 4: SA_PAIR(false, false, true, false); break;
-    case 5: SA_PAIR(true, false, true, false); break;
-    case 6: SA_PAIR(false, true, true, false); break;
-    case 7: SA_PAIR(true, true, true, false); break;
-    case 8: SA_PAIR(false, true, false, true); break;
-    case 9: SA_PAIR(true, true, false, true); break;
-    case 10: SA_PAIR(false, true, true, true); break;
-    default: SA_PAIR(true, true, true, true); break;
+    case 0: SA_PAIR(false, false, false, false, false); break;
+    case 1: SA_PAIR(true, false, false, false, false); break;
+    case 2: SA_PAIR(false, true, false, false, false); break;
+    case 3: SA_PAIR(true, true, false, false, false); break;
+    case 4: SA_PAIR(false, false, true, false, false); break;
+    case 5: SA_PAIR(true, false, true, false, false); break;
+    case 6: SA_PAIR(false, true, true, false, false); break;
+    case 7: SA_PAIR(true, true, true, false, false); break;
+    case 8: SA_PAIR(false, true, false, true, false); break;
+    case 9: SA_PAIR(true, true, false, true, false); break;
+    case 10: SA_PAIR(false, true, true, true, false); break;
+    case 11: SA_PAIR(true, true, true, true, false); break;
+    case 12: SA_PAIR(false, false, false, false, true); break;
+    case 13: SA_PAIR(true, false, false, false, true); break;
+    case 14: SA_PAIR(false, true, false, false, true); break;
+    case 15: SA_PAIR(true, true, false, false, true); break;
+    case 16: SA_PAIR(false, false, true, false, true); break;
+    case 17: SA_PAIR(true, false, true, false, true); break;
+    case 18: SA_PAIR(false, true, true, false, true); break;
+    default: SA_PAIR(true, true, true, false, true); break;
   }
 #undef SA_PAIR
   sa_status s = check_hip(c, hipGetLastError(), "forward (fp8 pair)");

@@ -390,9 +390,14 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
   if (s != SA_OK) return s;
   // the shared-latent MFMA kernels validate their own columns; other paths
   // run the validation kernel first on the same stream
-  // a biased forward runs on the grouped-query kernel where it applies, else
-  // on the generic kernel
-  const int path = bias ? (sa::gqa_supported(k, index_heads) ? 4 : 0) : sa::forward_path(k, index_heads);
+  // a biased forward runs on the MFMA kernel of its layout where there is one
+  // (a bf16 shared-latent cache takes the general latent kernel with its
+  // split-K combine, not the decode kernel), else on the generic kernel
+  const int path = !bias                                 ? sa::forward_path(k, index_heads)
+                   : sa::gqa_supported(k, index_heads)    ? 4
+                   : sa::latent_supported(k, index_heads) ? 2
+                   : sa::pair_supported(k, index_heads)   ? 3
+                                                          : 0;
   if (fused_validate && path != 2 && path != 3) {
     s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
                                      cache_capacity, nullptr, nullptr, nullptr);
@@ -430,8 +435,8 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
   switch (path) {
     case 2: {
       const int splits = sa::mla_splits(batch * q_seq, width);
-      return splits > 1 ? sa::launch_forward_latent_decode(c, a, splits, fused_validate != 0, app)
-                        : sa::launch_forward_latent(c, a, splits, fused_validate != 0, app);
+      return splits > 1 && !bias ? sa::launch_forward_latent_decode(c, a, splits, fused_validate != 0, app)
+                                 : sa::launch_forward_latent(c, a, splits, fused_validate != 0, app);
     }
     case 3: return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0, app);
     case 1: return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
@@ -518,10 +523,12 @@ sa_status sparse_attn_capacity_step(sparse_attn_ctx* c, const void* q, int64_t b
   if (!live(c)) return SA_E_STATE;
   const sa_config& k = c->cfg;
   c->last_error.clear();
-  if (k.kv_layout != SA_KV_SEPARATE || k.cache_format != SA_CACHE_DENSE)
-    return set_error(c, SA_E_UNSUPPORTED, "capacity_step: needs separate dense K and V caches");
-  if (!cache_k || !cache_v || !cur_k || !cur_v)
-    return set_error(c, SA_E_ARG, "capacity_step: cache_k, cache_v, cur_k and cur_v are required");
+  const bool latent = k.kv_layout == SA_KV_SHARED_LATENT;
+  if (!latent && k.cache_format != SA_CACHE_DENSE)
+    return set_error(c, SA_E_UNSUPPORTED, "capacity_step: separate K and V caches must be dense");
+  if (latent ? (!cache_k || !cur_k || cache_v || cur_v) : (!cache_k || !cache_v || !cur_k || !cur_v))
+    return set_error(c, SA_E_ARG, latent ? "capacity_step: a shared-latent cache takes cache_k and cur_k only"
+                                         : "capacity_step: cache_k, cache_v, cur_k and cur_v are required");
   if (cur_len <= 0 || cur_len > cache_capacity)
     return set_error(c, SA_E_CAPACITY, "capacity_step: cur_len must be in [1, cache_capacity]");
   if (cache_capacity > k.max_cache_len)
@@ -546,7 +553,9 @@ sa_status sparse_attn_capacity_step(sparse_attn_ctx* c, const void* q, int64_t b
   }
   const int64_t row = k.head_dim_qk * elem_bytes(k.dtype);
   const uintptr_t mis = (uintptr_t)cache_k | (uintptr_t)cache_v | (uintptr_t)cur_k | (uintptr_t)cur_v;
-  if (k.head_dim_v == k.head_dim_qk && row % 16 == 0 && (mis & 15) == 0) {
+  // fp8 records (648 bytes, not whole 16-byte units) go through kv_append
+  if (k.cache_format == SA_CACHE_DENSE && (latent || k.head_dim_v == k.head_dim_qk) && row % 16 == 0 &&
+      (mis & 15) == 0) {
     // lengths and the in-place append in one launch
     s = sa::launch_capacity_append(c, bias, k.dtype, bd, batch, cache_capacity, cur_len, valid_len, write_pos, cur_k,
                                    cur_v, cache_k, cache_v, k.kv_num_heads, row);

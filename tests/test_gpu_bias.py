@@ -35,17 +35,21 @@ def bias_store(b32, dtype):
     return oracle.bf16_bits(np.ascontiguousarray(b32, np.float32))
 
 
-def run_bias(w, inp, bias, *, fp8=False):
-    """Device forward_bias over the oracle's present; returns (y, word, msg)."""
+def run_bias(w, inp, bias, *, fp8=False, idx64=False, path=None):
+    """Device forward_bias over the oracle's present; returns (y, word, msg).
+    With `path`, the configuration's plan must name that kernel."""
     import torch
     pk, pv = present_host(inp)
     kc = oracle_records(pk, w) if fp8 else pk
-    ctx = make_ctx(w)
+    ctx = make_ctx(w, idx64=idx64)
+    if path is not None:
+        assert ctx.query_plan(w.batch, w.q_seq, inp["indices"].shape[1], w.width)[0] == path
     y = torch.full((w.batch, w.hq, w.q_seq, w.dv), float("nan"), dtype=y_dtype(w), device="cuda")
     vl = torch.tensor(np.full(w.batch, w.total, np.int32), device="cuda")
+    idx = inp["indices"].astype(np.int64) if idx64 else inp["indices"]
     ctx.reset_error_async()
     ctx.forward_bias(tt(inp["q"]), w.batch, w.q_seq, tt(kc), None if pv is None else tt(pv), w.cap, vl,
-                     tt(inp["indices"]), inp["indices"].shape[1], w.width, None if bias is None else tt(bias),
+                     tt(idx), inp["indices"].shape[1], w.width, None if bias is None else tt(bias),
                      y, fused_validate=True)
     word, _, msg = ctx.read_error()
     ctx.destroy()
@@ -76,7 +80,21 @@ CASES = {
                                                         width=100, topk=90, pattern="uniform", softcap=0.0),
     "fp8_records": W.WORKLOADS["decode_fp8"].scaled(batch=2, hq=16, past=300, topk=100, width=128),
     "latent_bf16": W.WORKLOADS["decode_bf16"].scaled(batch=3, hq=16, past=400, topk=260, width=300),
+    # 64 heads of 576 / 512 dims: the shared-latent MFMA kernels (plan path 2
+    # bf16 rows, 3 fp8 records), split over several workgroups per row and
+    # merged by the combine, or one workgroup per row
+    "latent_mfma_split": W.WORKLOADS["decode_bf16"].scaled(batch=3, past=1500, topk=700, width=710,
+                                                           capacity=1600),
+    "latent_mfma_rows": W.WORKLOADS["decode_bf16"].scaled(batch=1, q_seq=40, cur=40, past=600, topk=500,
+                                                          width=520, capacity=700),
+    "latent_mfma_softcap": W.WORKLOADS["decode_bf16"].scaled(batch=2, past=900, topk=400, width=400,
+                                                             capacity=1000, softcap=30.0),
+    "fp8_pair_split": W.WORKLOADS["decode_fp8"].scaled(batch=2, past=1200, topk=650, width=650, capacity=1300),
+    "fp8_pair_rows": W.WORKLOADS["decode_fp8"].scaled(batch=1, q_seq=40, cur=40, past=400, topk=300,
+                                                      width=300, capacity=500),
 }
+MFMA_PATH = {"latent_mfma_split": 2, "latent_mfma_rows": 2, "latent_mfma_softcap": 2, "fp8_pair_split": 3,
+             "fp8_pair_rows": 3}
 SHAPES = ["full", "b11k", "sk", "h11", "scalar"]
 
 
@@ -99,9 +117,37 @@ def test_forward_bias_matches_oracle(name, shape):
     bias = make_bias(w, shape)
     banner(f"forward_bias {name} bias {shape} {bias.shape}")
     ref = oracle_bias(w, inp, bias, fp8=fp8)
-    y, word, msg = run_bias(w, inp, bias, fp8=fp8)
+    y, word, msg = run_bias(w, inp, bias, fp8=fp8, path=MFMA_PATH.get(name))
     assert word == 0, msg
     check_close(y, ref, w.dtype, f"{name}/{shape}")
+
+
+@pytest.mark.parametrize("name", ["latent_mfma_split", "fp8_pair_rows"])
+def test_forward_bias_mfma_int64_indices(name):
+    w = CASES[name]
+    fp8 = w.cache_format == W.CACHE_FP8
+    inp = W.make_numpy(w)
+    bias = make_bias(w, "full", seed=4)
+    banner(f"forward_bias {name} int64 indices")
+    ref = oracle_bias(w, inp, bias, fp8=fp8)
+    y, word, msg = run_bias(w, inp, bias, fp8=fp8, idx64=True, path=MFMA_PATH[name])
+    assert word == 0, msg
+    check_close(y, ref, w.dtype, f"{name}/i64")
+
+
+@pytest.mark.parametrize("name", ["latent_mfma_split", "fp8_pair_split"])
+def test_forward_bias_mfma_flags_bad_index(name):
+    """A biased call on the shared-latent kernels still validates its index
+    rows in the launch: the word and the first failing column equal the
+    oracle's."""
+    w = CASES[name]
+    fp8 = w.cache_format == W.CACHE_FP8
+    inp = W.make_numpy(w)
+    inp["indices"][1, 0, 0, 5] = inp["indices"][1, 0, 0, 4]  # a repeated key: not strictly increasing
+    word_ref, _, _, _ = oracle.validate_indices(inp["indices"], np.full(w.batch, w.total, np.int32))
+    assert word_ref != 0
+    y, word, msg = run_bias(w, inp, make_bias(w, "b11k"), fp8=fp8, path=MFMA_PATH[name])
+    assert word == word_ref, msg
 
 
 def test_forward_bias_none_is_the_plain_forward():
@@ -113,21 +159,25 @@ def test_forward_bias_none_is_the_plain_forward():
     check_close(y, ref, w.dtype, "no bias")
 
 
-@pytest.mark.parametrize("name", ["grouped_bf16_per_head", "gqa_uniform_decode", "gqa_causal_softcap"])
+@pytest.mark.parametrize("name", ["grouped_bf16_per_head", "gqa_uniform_decode", "gqa_causal_softcap",
+                                  "latent_mfma_split", "latent_mfma_rows", "fp8_pair_split", "fp8_pair_rows"])
 def test_forward_bias_masked_rows_give_zeros(name):
     """Rows whose every key is masked give zeros (generic kernel; grouped-query
-    kernel with and without split-KV)."""
+    kernel with and without split-KV; the shared-latent kernels with and
+    without splits)."""
     w = CASES[name]
+    fp8 = w.cache_format == W.CACHE_FP8
     inp = W.make_numpy(w)
     b32 = np.zeros((w.batch, w.hq, w.q_seq, 1), np.float32)
-    b32[1, 3, w.q_seq - 1] = -np.inf
+    last = (min(1, w.batch - 1), 3, w.q_seq - 1)
+    b32[last] = -np.inf
     b32[0, :, 0] = -np.inf
     bias = bias_store(b32, w.dtype)
-    ref = oracle_bias(w, inp, bias)
-    assert not ref[1, 3, w.q_seq - 1].any() and not ref[0, :, 0].any()
-    y, word, msg = run_bias(w, inp, bias)
+    ref = oracle_bias(w, inp, bias, fp8=fp8)
+    assert not ref[last].any() and not ref[0, :, 0].any()
+    y, word, msg = run_bias(w, inp, bias, fp8=fp8, path=MFMA_PATH.get(name))
     assert word == 0, msg
-    assert not y[1, 3, w.q_seq - 1].any() and not y[0, :, 0].any()
+    assert not y[last].any() and not y[0, :, 0].any()
     check_close(y, ref, w.dtype, "masked rows")
 
 
@@ -162,11 +212,18 @@ def test_bias_host_errors():
                               bad_bias, y, vl, vl)
         assert e.value.status == status
     ctx.destroy()
+    # separate caches need both V tensors
+    ctx = make_ctx(w)
+    with pytest.raises(sa.SparseAttnError) as e:
+        ctx.capacity_step(q, w.batch, w.q_seq, k, None, w.cap, cur, cur, 1, idx, 1, w.width,
+                          torch.zeros((w.cap,), device=dev), y, vl, vl)
+    assert e.value.status == sa.SA_E_ARG
+    ctx.destroy()
     wl = W.WORKLOADS["decode_bf16"].scaled(batch=1, past=10, width=8, topk=8)
-    ctx = make_ctx(wl)  # a shared-latent cache: no capacity step over it
+    ctx = make_ctx(wl)  # a shared-latent cache takes no V tensors
     with pytest.raises(sa.SparseAttnError) as e:
         ctx.capacity_step(q, 1, 1, k, k, w.cap, cur, cur, 1, idx, 1, 8, torch.zeros((w.cap,), device=dev), y, vl, vl)
-    assert e.value.status == sa.SA_E_UNSUPPORTED
+    assert e.value.status == sa.SA_E_ARG
     ctx.destroy()
 
 
@@ -266,17 +323,20 @@ def test_capacity_step_matches_oracle(kw, one_call):
     check_close(d["y"], ref, w.dtype, "capacity step")
 
 
-def test_capacity_decode_fullsize_sampled_rows():
-    """The benchmark's capacity-mode decode (batch 32, 32 q heads / 8 kv heads,
-    head dim 128, capacity 16384, top-2048, bf16) in its launch
+@pytest.mark.parametrize("name", ["capacity_decode", "capacity_latent_decode"])
+def test_capacity_decode_fullsize_sampled_rows(name):
+    """The benchmark's capacity-mode decodes (batch 32, 32 q heads / 8 kv heads,
+    head dim 128, capacity 16384, top-2048, bf16; and the shared-latent one:
+    64 heads over one 576-dim row, capacity 32769) in their launch
     configuration: lengths and write positions exact, the appended rows
     exact, Y of sampled batch entries (all heads) against the oracle's
     capacity step on those entries."""
     import torch
 
     import bench
-    banner("capacity decode full size: building inputs")
-    s = bench.CapacitySetup("capacity_decode", 1)
+    banner(f"{name} full size: building inputs")
+    s = bench.CapacitySetup(name, 1)
+    assert s.path == (2 if name == "capacity_latent_decode" else 4)
     s.step(0)
     torch.cuda.synchronize()
     word, _, msg = s.ctx.read_error()
@@ -285,7 +345,7 @@ def test_capacity_decode_fullsize_sampled_rows():
     vl, wp = to_np(s.vl), to_np(s.wp)
     y = y_as_f32(s.y)
     for b in [0, 7, 19, 31]:
-        banner(f"capacity decode full size: oracle on batch entry {b}")
+        banner(f"{name} full size: oracle on batch entry {b}")
         inp = s.oracle_inputs(b)
         ref, valid, wpos = s.oracle_y(inp, 8)
         assert vl[b] == valid[0] and wp[b] == wpos[0]
@@ -332,3 +392,67 @@ def test_capacity_step_graph_replays_match_eager():
                                                                                          raw_bytes(e["v"]))
         assert ctx.read_error()[0] == 0
     ctx.destroy()
+
+
+LATENT_CAPACITY = {
+    "latent_bf16": W.WORKLOADS["decode_bf16"].scaled(batch=3, past=700, topk=500, width=520, capacity=900),
+    "latent_bf16_rows": W.WORKLOADS["decode_bf16"].scaled(batch=2, q_seq=3, cur=3, past=300, topk=250,
+                                                          width=260, capacity=400, seed=31),
+    "fp8_records": W.WORKLOADS["decode_fp8"].scaled(batch=3, past=600, topk=400, width=420, capacity=800),
+}
+
+
+@pytest.mark.parametrize("name", list(LATENT_CAPACITY))
+def test_capacity_step_shared_latent(name):
+    """sparse_attn_capacity_step over a shared-latent cache (bf16 rows in one
+    launch with the lengths; fp8 records through kv_append): lengths, write
+    positions and the in-place present bit-exact, Y within tolerance, on the
+    shared-latent MFMA kernel of the layout. The bias frontier of batch entry
+    b sits at total - b, so the write positions differ from the generator's
+    past length; index rows are cut to the recovered length."""
+    import torch
+    w = LATENT_CAPACITY[name]
+    fp8 = w.cache_format == W.CACHE_FP8
+    inp = W.make_numpy(w)
+    B, cap = w.batch, w.cap
+    rng = np.random.default_rng(40)
+    b32 = rng.standard_normal((B, 1, w.q_seq, cap)).astype(np.float32)
+    for b in range(B):
+        b32[b, :, :, w.total - b:] = -np.inf
+        b32[b, :, :, rng.integers(0, w.total - b - 1, 5)] = -np.inf  # holes do not move the frontier
+    bias = bias_store(b32, w.dtype)
+    valid, wpos = oracle.capacity_lengths(bias, cap, w.cur, batch=B, heads=w.hq, q_seq=w.q_seq, bias_dtype=w.dtype)
+    assert list(valid) == [w.total - b for b in range(B)]
+    idx = inp["indices"].copy()
+    for b in range(B):  # keep each row valid against its batch entry's length (sorted: cut the tail)
+        row = idx[b]
+        row[row >= valid[b]] = -1
+        for r in row.reshape(-1, w.width):
+            keep = r[r >= 0]
+            r[:] = -1
+            r[:len(keep)] = keep
+    word, _, _, _ = oracle.validate_indices(idx, valid)
+    assert word == 0
+    past, cur = inp["past_k"], inp["cur_k"]
+    if fp8:
+        past, cur = oracle_records(past, w), oracle_records(cur, w)
+    present = oracle.kv_append(past.copy(), wpos, cur)
+    fmt = oracle.FP8_BLOCK64 if fp8 else w.dtype
+    ref = oracle.forward(inp["q"], present, None, idx, q_dtype=w.dtype, cache_fmt=fmt, kv_layout=w.layout,
+                         hkv=w.hkv, dv=w.dv, rope=w.rope, scale=w.scale, softcap=w.softcap, bias=bias, threads=8)
+    banner(f"capacity step shared-latent {name}")
+    ctx = make_ctx(w)
+    assert ctx.query_plan(B, w.q_seq, 1, w.width)[0] == (3 if fp8 else 2)
+    kc = tt(past)
+    vl = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    wp = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    y = torch.full((B, w.hq, w.q_seq, w.dv), float("nan"), dtype=y_dtype(w), device="cuda")
+    ctx.capacity_step(tt(inp["q"]), B, w.q_seq, kc, None, cap, tt(cur), None, w.cur, tt(idx), 1, w.width,
+                      tt(bias), y, vl, wp, reset_error=True)
+    word, _, msg = ctx.read_error()
+    ctx.destroy()
+    assert word == 0, msg
+    np.testing.assert_array_equal(to_np(vl), valid)
+    np.testing.assert_array_equal(to_np(wp), wpos)
+    assert np.array_equal(raw_bytes(to_np(kc)), raw_bytes(present))
+    check_close(y_as_f32(y), ref, w.dtype, f"capacity step {name}")
