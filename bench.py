@@ -179,13 +179,19 @@ class Setup:
         self.path, self.splits = self.ctx.query_plan(B, Sq, 1, w.width)
 
     def fused_step(self):
-        """True when the step is one sparse_attn_step call: the shared-latent
-        MFMA paths take reset + in-place append (+ quantize) + forward in one launch."""
-        return self.path in (2, 3) and self.w.cur <= 8
+        """True when the step is one library call that the library runs as one
+        forward launch (plus its combine): sparse_attn_step on the
+        shared-latent MFMA paths (at most 8 current rows), sparse_attn_step_kv
+        on the grouped-query path."""
+        return (self.path in (2, 3) and self.w.cur <= 8) or self.path == 4
 
     def step(self, i):
         w, c = self.w, self.ctx
         r = i % len(self.idxs)
+        if self.path == 4:
+            c.step_kv(self.qs[r % len(self.qs)], w.batch, w.q_seq, self.k, self.v, w.cap, self.plen, self.cur_k,
+                      self.cur_v, w.cur, self.vlen, self.idxs[r], 1, w.width, self.y, reset_error=True)
+            return
         if self.fused_step():
             c.step(self.qs[r % len(self.qs)], w.batch, w.q_seq, self.k, w.cap, self.plen, self.cur_k, w.cur,
                    self.vlen, self.idxs[r], 1, w.width, self.y, reset_error=True,
@@ -249,7 +255,9 @@ class Setup:
                             f"index width {w.width}, {'graph replay' if use_graph else 'eager'}, "
                             f"{nset} rotating index sets",
                 "selected_tokens_per_step": tokens, "splits": self.splits,
-                "step_calls": ("sparse_attn_step (reset + append + forward in one launch)" if self.fused_step()
+                "step_calls": ("sparse_attn_step_kv (reset + append + validation + forward in one launch)"
+                               if self.path == 4 else
+                               "sparse_attn_step (reset + append + forward in one launch)" if self.fused_step()
                                else "reset_error_async + kv_append + forward"),
                 "step_hbm_GBps": self.step_bytes() / (ms_per_step / 1e3) / 1e9}
 

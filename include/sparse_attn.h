@@ -320,6 +320,29 @@ sa_status sparse_attn_step(sparse_attn_ctx* ctx, const void* q, int64_t batch, i
                            const void* indices, int64_t index_heads, int64_t width, void* y,
                            int32_t reset_error);
 
+/* The same step over separate K and V caches kept in place:
+ *   [sparse_attn_reset_error_async if reset_error]
+ *   sparse_attn_kv_append(past = present = (cache_k, cache_v), past_len, cur_k, cur_v, present_len)
+ *   sparse_attn_forward(present = (cache_k, cache_v), valid_len = present_len, fused_validate = 1)
+ * cache_k, cache_v [B, Hkv, cache_capacity, D] read and written; cur_k, cur_v
+ * [B, Hkv, cur_len, D] (config dtype); past_len [B] read and present_len [B]
+ * written on the device; 0 <= cur_len <= cache_capacity.
+ * On the grouped-query MFMA path (sparse_attn_query_plan path 4), when a
+ * workgroup's (query, head) rows fill at most half its waves (decode-like:
+ * min(q_seq, 128 / group) * group <= 64) and the four tensors are 16-byte
+ * aligned, this is ONE forward launch (plus the split-KV combine): every workgroup writes its (batch, kv head)'s current rows into
+ * the caches before it gathers, checks its share of the index columns, and
+ * the launch's last arrival merges (or, with reset_error, replaces) the error
+ * word. In every other case the three calls above run in sequence. Errors:
+ * host-side statuses of those calls (SA_E_UNSUPPORTED for a shared-latent
+ * cache), all checked before anything is launched; device-side bits as they
+ * latch them (a capacity failure appends nothing and sets
+ * SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY). Asynchronous and capturable. */
+sa_status sparse_attn_step_kv(sparse_attn_ctx* ctx, const void* q, int64_t batch, int64_t q_seq, void* cache_k,
+                              void* cache_v, int64_t cache_capacity, const int32_t* past_len, const void* cur_k,
+                              const void* cur_v, int64_t cur_len, int32_t* present_len, const void* indices,
+                              int64_t index_heads, int64_t width, void* y, int32_t reset_error);
+
 /* CSA ratio-4 selection producer (the indexer): the index-selection stage of
  * the compressed-sparse-attention operator's ratio-4 path (onnx-runtime-ep-cpu,
  * src/kernels/compressed_sparse_attention.rs, `select_ratio4_topk` and

@@ -45,7 +45,7 @@ EXPORTS = [
     "sparse_attn_reset_error_async", "sparse_attn_read_error", "sparse_attn_last_error",
     "sparse_attn_query_plan", "sparse_attn_profile_enable", "sparse_attn_profile_read",
     "sparse_attn_version", "sparse_attn_forward_latent_static",
-    "sparse_attn_measure_copy", "sparse_attn_measure_read", "sparse_attn_measure_mfma",
+    "sparse_attn_measure_copy", "sparse_attn_measure_read", "sparse_attn_measure_mfma", "sparse_attn_step_kv",
 ]
 
 
@@ -100,6 +100,7 @@ def load(path: Path | str | None = None) -> ctypes.CDLL:
         "sparse_attn_capacity_step": ([V, V, I64, I64, V, V, I64, V, V, I64, V, I64, I64, V, V, I32, V, V, V, I32],
                                       st),
         "sparse_attn_step": ([V, V, I64, I64, V, I64, V, V, I64, I32, V, V, I64, I64, V, I32], st),
+        "sparse_attn_step_kv": ([V, V, I64, I64, V, V, I64, V, V, V, I64, V, V, I64, I64, V, I32], st),
         "sparse_attn_csa_forward": ([V, V, I64, I64, I64, V, I64, V, I64, V, I64, I64, V, V, V, V,
                                      ctypes.c_float, V], st),
         "sparse_attn_csa_index_select": ([V, V, V, V, I64, I64, I64, I64, V, I64, I64, V, V], st),
@@ -252,6 +253,16 @@ class Context:
             self.handle, _ptr(q), batch, q_seq, _ptr(cache), cache_capacity, _ptr(past_len), _ptr(cur),
             cur_len, int(cur_is_unquantized_bf16), _ptr(present_len), _ptr(indices), index_heads, width,
             _ptr(y), int(reset_error)))
+
+    def step_kv(self, q, batch, q_seq, cache_k, cache_v, cache_capacity, past_len, cur_k, cur_v, cur_len,
+                present_len, indices, index_heads, width, y, reset_error=True):
+        """Reset (optional) + in-place append + forward with fused validation
+        on separate K/V caches, one launch on the grouped-query path."""
+        self._sync_stream()
+        self._check(self.lib.sparse_attn_step_kv(
+            self.handle, _ptr(q), batch, q_seq, _ptr(cache_k), _ptr(cache_v), cache_capacity, _ptr(past_len),
+            _ptr(cur_k), _ptr(cur_v), cur_len, _ptr(present_len), _ptr(indices), index_heads, width, _ptr(y),
+            int(reset_error)))
 
     def csa_forward(self, query, current_kv, records, selected, head_sink, total_len, y, *,
                     scale=0.0, bias=None):

@@ -37,6 +37,7 @@
 // bank groups per pass) and c ^ 2 (R & 7) for V (the transposing V reads of
 // 8 rows x 32 bytes hit 64 distinct banks).
 #include "sa_mfma_dev.h"
+#include "sa_validate_dev.h"
 
 namespace sa {
 
@@ -64,21 +65,39 @@ template <bool I64> constexpr int part_off() { return IDX_OFF + IDX_SLOTS * idx_
 constexpr int PART_BYTES = 2 * KT * WAVES * 4;   // per slot: max, min [32 columns][wave] (int32)
 template <bool I64> constexpr int nrow_off() { return part_off<I64>() + 2 * PART_BYTES; }
 template <bool I64> constexpr int flag_off() { return nrow_off<I64>() + RMAX * 4; }
-template <bool I64> constexpr size_t lds_bytes() { return (size_t)flag_off<I64>() + WAVES * 8 * 4; }
+template <bool I64> constexpr int rmin_off() { return flag_off<I64>() + WAVES * 8 * 4; }
+template <bool I64> constexpr size_t lds_bytes() { return (size_t)rmin_off<I64>() + RMAX * 8; }
+static_assert(flag_off<false>() % 8 == 0 && flag_off<true>() % 8 == 0, "8-byte row minima");
 }  // namespace gq
 
 // LDS reads of step j of the interleaved S / PV loop: the K read of (k-step
 // j >> 1, key half j & 1) and the two transposing V reads of dv tile j
 __host__ __device__ constexpr int gqa_step_reads(int j) { return j < 8 ? 3 : 0; }
 
-template <bool I64, bool SOFTCAP, bool BIAS>
+// FUSED: the launch validates its index rows (IndexShare host-validator
+// rules, each column against its left neighbour): the kv heads of a
+// (batch, query block, split) share its columns out, every workgroup counts
+// one arrival per query row it covers, and the last arrival of a row records
+// the row's first violation, then counts toward the launch's last-arrival
+// record of the error block (with `reset` that record replaces the word).
+// APPEND (with FUSED): the launch also appends the current K/V rows in place
+// (rows past_len[b] ..): every workgroup writes its (batch, kv head)'s rows
+// itself and waits for the stores before any gather, so it reads its own
+// writes; the workgroup of kv head 0, query block 0 and split 0 writes
+// present_len[b] (or flags a row count that does not fit the capacity).
+template <bool I64, bool SOFTCAP, bool BIAS, bool FUSED, bool APPEND>
 __global__ void __launch_bounds__(gq::THREADS, 1)
-gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+gqa_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                    const void* __restrict__ idx, const int32_t* __restrict__ valid_len, uint16_t* __restrict__ y,
                    int64_t batch, int64_t hkv, int64_t q_seq, int64_t cap, int64_t width, int group, int nqb,
                    float scale, float softcap, const uint16_t* __restrict__ bias, int64_t bd0, int64_t bd1,
                    int64_t bd2, int64_t bd3, int splits, float* __restrict__ part_o,
-                   float* __restrict__ part_ml) {
+                   float* __restrict__ part_ml, ErrorBlock* __restrict__ eb,
+                   unsigned long long* __restrict__ row_key, unsigned* __restrict__ row_done,
+                   const uint8_t* __restrict__ cur_k, const uint8_t* __restrict__ cur_v,
+                   const int32_t* __restrict__ past_len, int32_t* __restrict__ present_len, int64_t cur_len,
+                   int reset) {
+  static_assert(FUSED || !APPEND, "the in-launch append reports through the fused error record");
   static_assert(gq::RB == 1, "the bias prefetch holds one row block per wave");
   using namespace gq;
   constexpr int ITB = idx_tile_bytes<I64>();
@@ -89,6 +108,8 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   int* part = (int*)(lds_raw + part_off<I64>());          // [2 slots][max | min][32 columns][wave]
   int* n_s = (int*)(lds_raw + nrow_off<I64>());          // [RMAX] first -1 column of each query row
   int* flag_s = (int*)(lds_raw + flag_off<I64>());       // [wave][8] tile flags, per wave
+  // [RMAX] fused validation: each query row's smallest failing key
+  unsigned long long* rmin = (unsigned long long*)(lds_raw + rmin_off<I64>());
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -112,6 +133,13 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   const int rlive = (int)min((int64_t)R, q_seq - q0);  // queries that exist
   const int hq = (int)(hkv * group);
   int64_t bound = valid_len ? (int64_t)valid_len[b] : cap;
+  int64_t app_p = 0;
+  bool app_ok = false;
+  if constexpr (APPEND) {
+    app_p = (int64_t)past_len[b];
+    app_ok = app_p >= 0 && app_p + cur_len <= cap;  // else nothing is appended and the word says so
+    bound = app_p + cur_len;
+  }
   bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
   // tiles [xo, xo + ntile_w) of the index rows; the kernel numbers them from 0
   const int ntile_all = (int)((width + KT - 1) / KT);
@@ -149,6 +177,23 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   // ---- buffers: this (batch, kv head)'s K and V rows; the index rows of the
   // workgroup's queries (reads past the live queries return zeros)
   const int64_t kv_base = (b * hkv + kvh) * cap * ROWB;
+  if constexpr (APPEND) {
+    // this (batch, kv head)'s current rows, written before any gather and
+    // waited for (every workgroup that may read them writes them itself)
+    if (app_ok) {
+      const int64_t n16 = cur_len * (ROWB / 16);
+      const uint4* sk = (const uint4*)(cur_k + pr * cur_len * ROWB);
+      const uint4* sv = (const uint4*)(cur_v + pr * cur_len * ROWB);
+      uint4* dk = (uint4*)(kc + kv_base + app_p * ROWB);
+      uint4* dv = (uint4*)(vc + kv_base + app_p * ROWB);
+      for (int64_t u = tid; u < n16; u += THREADS) {
+        dk[u] = sk[u];
+        dv[u] = sv[u];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+    __syncthreads();
+  }
   const __amdgpu_buffer_rsrc_t krsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)(kc + kv_base), (short)0, (int)(cap * ROWB), 0x00020000);
   const __amdgpu_buffer_rsrc_t vrsrc =
@@ -157,7 +202,41 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
   const __amdgpu_buffer_rsrc_t irsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)ibase, (short)0, (int)min((int64_t)0x7fffffff, (int64_t)rlive * width * ISZ), 0x00020000);
 
-  for (int i = tid; i < RMAX; i += THREADS) n_s[i] = 0x7fffffff;
+  for (int i = tid; i < RMAX; i += THREADS) {
+    n_s[i] = 0x7fffffff;
+    if constexpr (FUSED) rmin[i] = ~0ull;
+  }
+  const int64_t irow0 = b * q_seq + q0;  // index row of query q0 (one index head)
+  constexpr int FR = RMAX / (THREADS / 32);  // rows each folding thread visits
+  // FUSED: the index columns this workgroup validates at its end (kv head h
+  // takes the h-th slice of the block's columns, for every query row); when
+  // they fit two per thread they are loaded here, in flight with the rest of
+  // the launch, so the check at the end does not wait on memory
+  int64_t vmb = 0, vme = 0;
+  int64_t pv[2] = {-1, -1}, pu[2] = {0, 0};
+  bool pre = false;
+  if constexpr (FUSED) {
+    const int64_t cb = (int64_t)xo * KT;
+    const int64_t ce = min((int64_t)(xo + ntile_w) * KT, width);
+    const int64_t ncols = ce > cb ? ce - cb : 0;
+    const int64_t chunk = (ncols + hkv - 1) / hkv;
+    vmb = cb + min(ncols, kvh * chunk);
+    vme = min(cb + ncols, vmb + chunk);
+    const int64_t mc = vme - vmb;
+    pre = mc > 0 && (int64_t)rlive * mc <= 2 * THREADS;  // uniform
+    if (pre) {
+#pragma unroll
+      for (int k = 0; k < 2; k++) {
+        const int64_t e = tid + (int64_t)THREADS * k;
+        if (e < (int64_t)rlive * mc) {
+          const int64_t r = e / mc, c = vmb + (e - r * mc);
+          const int64_t off = (irow0 + r) * width + c;
+          pv[k] = load_index<I64>(idx, off);
+          pu[k] = c > 0 ? load_index<I64>(idx, off - 1) : 0;
+        }
+      }
+    }
+  }
 
   // ---- index tiles: lane l of load i of wave w copies dword d = 64 (IL w + i) + l
   // of the tile's [RMAX][32] block (row r = d / (32 ISZ / 4), column j)
@@ -191,7 +270,7 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
     const int64_t col = (int64_t)(xo + x) * KT + j;
     int mx = -1, mn = 0x7fffffff;
 #pragma unroll
-    for (int k = 0; k < RMAX / (THREADS / 32); k++) {
+    for (int k = 0; k < FR; k++) {
       const int r = tg + (THREADS / 32) * k;
       if (r < rlive) {
         const int64_t v = col < width ? idx_at(slot, r, j) : -1;
@@ -626,18 +705,97 @@ gqa_forward_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k
       for (int dt = 0; dt < DVT; dt++) *(f32x4_l*)(op + 16 * dt) = o[rb][dt];
       if (g == 0) *(float2*)(part_ml + prow * 2) = make_float2(m_run[rb], l_run[rb]);
     }
-    return;
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++) {
+      if (!row_on[rb]) continue;
+      const float inv = l_run[rb] > 0.0f ? 1.0f / l_run[rb] : 0.0f;
+      uint16_t* yp = y + (((b * hq + row_h[rb]) * q_seq + q0 + row_q[rb]) * D) + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < DVT; dt++) {
+        const u32x2_l w2 = {pack_bf16x2(o[rb][dt][0] * inv, o[rb][dt][1] * inv),
+                            pack_bf16x2(o[rb][dt][2] * inv, o[rb][dt][3] * inv)};
+        *(u32x2_l*)(yp + 16 * dt) = w2;
+      }
+    }
   }
+  if constexpr (!FUSED) return;
+
+  // ---- fused validation (launched with the in-launch append, for
+  // decode-like blocks, where most waves hold no row): the kv heads of this (batch, query block, split) share its
+  // columns out; kv head h checks the h-th slice for every query row of the
+  // block, from memory (the index rows are in L2), each column against its
+  // left neighbour. A failing column, or a first column of -1 (a row of
+  // padding only), lowers its row's minimum key in LDS.
+  const bool duty = kvh == 0 && qb == 0 && sp == 0;
+  if constexpr (APPEND) {
+    if (duty && tid == 0) {
+      // a device-scope atomic store: the launch's record reads it without a fence
+      if (app_ok) atomicExch(&present_len[b], (int32_t)(app_p + cur_len));
+      else atomicOr(&eb->call_word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
+    }
+  }
+  {
+    const int64_t mb = vmb, me = vme;
+    const uint32_t rmin_a = (uint32_t)(uintptr_t)(lds + rmin_off<I64>());
+    if (pre) {  // the values loaded at the start
+      const int64_t mc = me - mb;
 #pragma unroll
-  for (int rb = 0; rb < RB; rb++) {
-    if (!row_on[rb]) continue;
-    const float inv = l_run[rb] > 0.0f ? 1.0f / l_run[rb] : 0.0f;
-    uint16_t* yp = y + (((b * hq + row_h[rb]) * q_seq + q0 + row_q[rb]) * D) + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < DVT; dt++) {
-      const u32x2_l w2 = {pack_bf16x2(o[rb][dt][0] * inv, o[rb][dt][1] * inv),
-                          pack_bf16x2(o[rb][dt][2] * inv, o[rb][dt][3] * inv)};
-      *(u32x2_l*)(yp + 16 * dt) = w2;
+      for (int k = 0; k < 2; k++) {
+        const int64_t e = tid + (int64_t)THREADS * k;
+        if (e < (int64_t)rlive * mc) {
+          const int64_t r = e / mc, c = mb + (e - r * mc);
+          if (column_class(c, pv[k], pu[k], bound))
+            ds_min_u64_at(rmin_a + 8u * (uint32_t)r, (unsigned long long)((irow0 + r) * (width + 1) + c));
+        }
+      }
+    }
+    for (int r = 0; r < rlive && me > mb && !pre; r++) {  // uniform
+      const int64_t rb0 = (irow0 + r) * width;
+      for (int64_t c0 = mb + tid; c0 < me; c0 += 2 * THREADS) {
+        const int64_t c1 = c0 + THREADS;
+        const int64_t v0 = load_index<I64>(idx, rb0 + c0);
+        const int64_t u0 = c0 > 0 ? load_index<I64>(idx, rb0 + c0 - 1) : 0;
+        const int64_t v1 = c1 < me ? load_index<I64>(idx, rb0 + c1) : -1;
+        const int64_t u1 = c1 < me ? load_index<I64>(idx, rb0 + c1 - 1) : 0;
+        if (column_class(c0, v0, u0, bound))
+          ds_min_u64_at(rmin_a + 8u * (uint32_t)r, (unsigned long long)((irow0 + r) * (width + 1) + c0));
+        if (column_class(c1, v1, u1, bound))
+          ds_min_u64_at(rmin_a + 8u * (uint32_t)r, (unsigned long long)((irow0 + r) * (width + 1) + c1));
+      }
+    }
+    // a row whose first entry is -1 holds only padding (unless a column fails)
+    if (xo == 0 && kvh == 0 && width > 0 && tid < rlive && load_index<I64>(idx, (irow0 + tid) * width) == -1)
+      ds_min_u64_at(rmin_a + 8u * (uint32_t)tid, (unsigned long long)((irow0 + tid) * (width + 1) + width));
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this thread's LDS minima have landed
+  __syncthreads();
+  // ---- arrivals: the splits x kv heads workgroups of a query row each count
+  // one; the last records the row's first violation and counts toward the
+  // launch's record
+  if (tid < rlive) {
+    const int64_t irow = irow0 + tid;
+    unsigned long long k = rmin[tid];
+    if (k != ~0ull) atomicMin(&row_key[irow], k);
+    // the row minimum (and present_len) are device-scope atomics: waiting for
+    // them to complete orders them before the count
+    __builtin_amdgcn_s_waitcnt(0);
+    if (atomicAdd(&row_done[irow], 1u) == (unsigned)(splits * hkv) - 1) {
+      atomicExch(&row_done[irow], 0u);        // re-armed for the next launch
+      k = atomicExch(&row_key[irow], ~0ull);  // every workgroup's minimum, re-armed
+      if (k != ~0ull) {
+        const int64_t col = (int64_t)(k % (unsigned long long)(width + 1));
+        int cls = 6;
+        if (col < width) {
+          const int64_t v = load_index<I64>(idx, irow * width + col);
+          const int64_t u = col > 0 ? load_index<I64>(idx, irow * width + col - 1) : 0;
+          cls = column_class(col, v, u, bound);
+        }
+        atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
+        atomicMin((unsigned long long*)&eb->call_key, k);
+      }
+      finish_launch<I64, false>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap,
+                                (unsigned)(batch * q_seq), reset != 0);
     }
   }
 }
@@ -710,6 +868,17 @@ int gqa_splits(const sparse_attn_ctx* c, int64_t batch, int64_t q_seq, int64_t w
   return (int)s;
 }
 
+// The launch validates its own index rows (and may append) when a workgroup's
+// rows fill at most half of its waves (decode-like blocks): the idle waves
+// leave room for the check at the end. Larger blocks keep the standalone
+// validation kernel, which reads the rows once for all kv heads.
+bool gqa_fuses(const sa_config& cfg, int64_t q_seq) {
+  using namespace gq;
+  const int64_t group = cfg.num_heads / cfg.kv_num_heads;
+  const int64_t R = group >= MROWS ? 1 : std::min<int64_t>(RMAX, MROWS / group);
+  return std::min<int64_t>(R, q_seq) * group <= MROWS / 2;
+}
+
 bool gqa_supported(const sa_config& cfg, int64_t index_heads) {
   if (cfg.dtype != SA_BF16 || cfg.kv_layout != SA_KV_SEPARATE || cfg.cache_format != SA_CACHE_DENSE) return false;
   if (index_heads != 1 || cfg.head_dim_qk != gq::D || cfg.head_dim_v != gq::D) return false;
@@ -719,9 +888,9 @@ bool gqa_supported(const sa_config& cfg, int64_t index_heads) {
   return cfg.max_cache_len <= (int64_t)(0x7fffffffLL / gq::ROWB);
 }
 
-static bool g_gqa_attr[8] = {false, false, false, false, false, false, false, false};
+static bool g_gqa_attr[16] = {};
 
-sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
+sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a, bool fused, const AppendArgs* app) {
   using namespace gq;
   const int group = (int)(a.hq / a.hkv);
   const int R = group >= MROWS ? 1 : std::min(RMAX, MROWS / group);
@@ -736,12 +905,23 @@ sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
     return set_error(c, SA_E_SHAPE, "forward: index rows too wide for 32-bit offsets");
   const bool cap_on = a.softcap != 0.0f;
   const bool bias_on = a.bias != nullptr;
-  const int variant = (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0) + (bias_on ? 4 : 0);
-  const void* fns[8] = {
-      (const void*)gqa_forward_kernel<false, false, false>, (const void*)gqa_forward_kernel<true, false, false>,
-      (const void*)gqa_forward_kernel<false, true, false>,  (const void*)gqa_forward_kernel<true, true, false>,
-      (const void*)gqa_forward_kernel<false, false, true>,  (const void*)gqa_forward_kernel<true, false, true>,
-      (const void*)gqa_forward_kernel<false, true, true>,   (const void*)gqa_forward_kernel<true, true, true>};
+  // the launch validates itself only together with the in-launch append (a
+  // plain forward keeps the standalone validation kernel, which measured
+  // faster than the check at the end of every workgroup)
+  if (fused != (app != nullptr)) return set_error(c, SA_E_STATE, "forward: in-launch validation comes with the append");
+  if (fused && (!c->row_key || !c->row_done))
+    return set_error(c, SA_E_STATE, "forward: fused validation needs the context's row buffers");
+  if (fused && a.batch * a.q_seq > c->rows_cap)
+    return set_error(c, SA_E_STATE, "forward: more index rows than the context holds");
+  const int mode = app ? 1 : 0;
+  const int variant = (a.idx64 ? 1 : 0) + (cap_on ? 2 : 0) + (bias_on ? 4 : 0) + 8 * mode;
+#define SA_GQA_FN(M)                                                                                        \
+  (const void*)gqa_forward_kernel<false, false, false, M, M>, (const void*)gqa_forward_kernel<true, false, false, M, M>, \
+      (const void*)gqa_forward_kernel<false, true, false, M, M>, (const void*)gqa_forward_kernel<true, true, false, M, M>, \
+      (const void*)gqa_forward_kernel<false, false, true, M, M>, (const void*)gqa_forward_kernel<true, false, true, M, M>, \
+      (const void*)gqa_forward_kernel<false, true, true, M, M>, (const void*)gqa_forward_kernel<true, true, true, M, M>
+  const void* fns[16] = {SA_GQA_FN(false), SA_GQA_FN(true)};
+#undef SA_GQA_FN
   const size_t lds = a.idx64 ? lds_bytes<true>() : lds_bytes<false>();
   if (!g_gqa_attr[variant]) {
     hipError_t e = hipFuncSetAttribute(fns[variant], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -750,22 +930,35 @@ sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a) {
   }
   const dim3 grid((unsigned)wgs), block(THREADS);
   const ProfEvents pe = prof_next(c);
-#define SA_GQA(I, C, BI)                                                                                     \
-  SA_MAIN_LAUNCH(pe, (gqa_forward_kernel<I, C, BI>), grid, block, lds, c->stream, (const uint16_t*)a.q,      \
-                     (const uint8_t*)a.k, (const uint8_t*)a.v, a.idx, a.valid_len, (uint16_t*)a.y, a.batch, \
-                     a.hkv, a.q_seq, a.cap, a.width, group, (int)nqb, a.scale, a.softcap,                    \
-                     (const uint16_t*)a.bias, a.bd[0], a.bd[1], a.bd[2], a.bd[3], splits, c->gpart_o,    \
-                     c->gpart_ml)
-  switch (variant) {
-    case 0: SA_GQA(false, false, false); break;
-    case 1: SA_GQA(true, false, false); break;
-    case 2: SA_GQA(false, true, false); break;
-    case 3: SA_GQA(true, true, false); break;
-    case 4: SA_GQA(false, false, true); break;
-    case 5: SA_GQA(true, false, true); break;
-    case 6: SA_GQA(false, true, true); break;
-    default: SA_GQA(true, true, true); break;
+  const uint8_t* cur_k = app ? (const uint8_t*)app->cur : nullptr;
+  const uint8_t* cur_v = app ? (const uint8_t*)app->cur_v : nullptr;
+  const int32_t* plen = app ? app->past_len : nullptr;
+  int32_t* prlen = app ? app->present_len : nullptr;
+  const int64_t clen = app ? app->cur_len : 0;
+  const int reset = app ? app->reset : 0;
+#define SA_GQA(I, C, BI, F, A)                                                                                \
+  SA_MAIN_LAUNCH(pe, (gqa_forward_kernel<I, C, BI, F, A>), grid, block, lds, c->stream, (const uint16_t*)a.q, \
+                     (uint8_t*)a.k, (uint8_t*)a.v, a.idx, a.valid_len, (uint16_t*)a.y, a.batch, a.hkv,        \
+                     a.q_seq, a.cap, a.width, group, (int)nqb, a.scale, a.softcap, (const uint16_t*)a.bias,    \
+                     a.bd[0], a.bd[1], a.bd[2], a.bd[3], splits, c->gpart_o, c->gpart_ml, c->err, c->row_key,  \
+                     c->row_done, cur_k, cur_v, plen, prlen, clen, reset)
+#define SA_GQA_M(F, A)                                   \
+  switch (variant & 7) {                                 \
+    case 0: SA_GQA(false, false, false, F, A); break;    \
+    case 1: SA_GQA(true, false, false, F, A); break;     \
+    case 2: SA_GQA(false, true, false, F, A); break;     \
+    case 3: SA_GQA(true, true, false, F, A); break;      \
+    case 4: SA_GQA(false, false, true, F, A); break;     \
+    case 5: SA_GQA(true, false, true, F, A); break;      \
+    case 6: SA_GQA(false, true, true, F, A); break;      \
+    default: SA_GQA(true, true, true, F, A); break;      \
   }
+  if (mode == 0) {
+    SA_GQA_M(false, false)
+  } else {
+    SA_GQA_M(true, true)
+  }
+#undef SA_GQA_M
 #undef SA_GQA
   sa_status st = check_hip(c, hipGetLastError(), "forward (gqa)");
   if (st != SA_OK || splits == 1) return st;

@@ -180,7 +180,7 @@ sa_status sparse_attn_create(const sa_config* cfg, void* hip_stream, sparse_attn
   }
   if (e == hipSuccess) e = hipMalloc((void**)&c->zeros, 1024);
   if (e == hipSuccess) e = hipMemset(c->zeros, 0, 1024);
-  if (e == hipSuccess && mla) {
+  if (e == hipSuccess && (mla || sa::gqa_supported(k, 1))) {
     e = hipMalloc((void**)&c->row_key, (size_t)c->rows_cap * sizeof(unsigned long long));
     if (e == hipSuccess) e = hipMemset(c->row_key, 0xff, (size_t)c->rows_cap * sizeof(unsigned long long));
     if (e == hipSuccess) e = hipMalloc((void**)&c->row_done, (size_t)c->rows_cap * sizeof(unsigned));
@@ -398,7 +398,8 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
                    : sa::latent_supported(k, index_heads) ? 2
                    : sa::pair_supported(k, index_heads)   ? 3
                                                           : 0;
-  if (fused_validate && path != 2 && path != 3) {
+  const bool gqa_fused = path == 4 && app && sa::gqa_fuses(k, q_seq);
+  if (fused_validate && path != 2 && path != 3 && !gqa_fused) {
     s = sparse_attn_validate_indices(c, indices, batch, index_heads, q_seq, width, valid_len,
                                      cache_capacity, nullptr, nullptr, nullptr);
     if (s != SA_OK) return s;
@@ -430,8 +431,8 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
     a.bias = bias;
     for (int i = 0; i < 4; i++) a.bd[i] = bd[i];
   }
-  if (app && path != 2 && path != 3)
-    return set_error(c, SA_E_UNSUPPORTED, "step: the in-launch append needs a shared-latent MFMA path");
+  if (app && (path == 4 ? (!app->cur_v || !gqa_fused) : (path != 2 && path != 3)))
+    return set_error(c, SA_E_UNSUPPORTED, "step: the in-launch append needs an MFMA path of the cache's layout");
   switch (path) {
     case 2: {
       const int splits = sa::mla_splits(batch * q_seq, width);
@@ -440,7 +441,7 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
     }
     case 3: return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0, app);
     case 1: return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
-    case 4: return sa::launch_forward_gqa(c, a);
+    case 4: return sa::launch_forward_gqa(c, a, gqa_fused, gqa_fused ? app : nullptr);
     default: return sa::launch_forward_generic(c, a);
   }
 }
@@ -612,6 +613,50 @@ sa_status sparse_attn_step(sparse_attn_ctx* c, const void* q, int64_t batch, int
                               cur_is_unquantized_bf16, cache, nullptr, cache_capacity, present_len);
   if (s == SA_OK)
     s = sparse_attn_forward(c, q, batch, q_seq, cache, nullptr, cache_capacity, present_len, indices,
+                            index_heads, width, y, 1);
+  return s;
+}
+
+sa_status sparse_attn_step_kv(sparse_attn_ctx* c, const void* q, int64_t batch, int64_t q_seq, void* cache_k,
+                              void* cache_v, int64_t cache_capacity, const int32_t* past_len, const void* cur_k,
+                              const void* cur_v, int64_t cur_len, int32_t* present_len, const void* indices,
+                              int64_t index_heads, int64_t width, void* y, int32_t reset_error) {
+  if (!live(c)) return SA_E_STATE;
+  c->last_error.clear();
+  const sa_config& k = c->cfg;
+  if (k.kv_layout != SA_KV_SEPARATE)
+    return set_error(c, SA_E_UNSUPPORTED, "step_kv: separate K and V caches only (use sparse_attn_step)");
+  if (!cache_k || !cache_v || !cur_k || !cur_v || !past_len || !present_len)
+    return set_error(c, SA_E_ARG, "step_kv: cache_k, cache_v, cur_k, cur_v, past_len and present_len are required");
+  if (batch <= 0 || batch > k.max_batch)
+    return set_error(c, SA_E_STATE, fmt("step_kv: batch %lld outside [1, max_batch %lld]", batch, k.max_batch));
+  if (cur_len < 0 || cache_capacity <= 0 || cache_capacity > k.max_cache_len)
+    return set_error(c, SA_E_ARG, "step_kv: negative cur_len or cache capacity outside [1, max_cache_len]");
+  if (cur_len > cache_capacity) return set_error(c, SA_E_CAPACITY, "step_kv: current rows exceed the cache capacity");
+  if (!q || !indices || !y) return set_error(c, SA_E_ARG, "step_kv: q, indices and y are required");
+  sa_status gs = check_index_geometry(c, batch, index_heads, q_seq, width);
+  if (gs != SA_OK) return gs;
+  const int path = sa::forward_path(k, index_heads);
+  const uintptr_t mis = (uintptr_t)cache_k | (uintptr_t)cache_v | (uintptr_t)cur_k | (uintptr_t)cur_v;
+  if (path == 4 && sa::gqa_fuses(k, q_seq) && (mis & 15) == 0) {
+    sa::AppendArgs app;
+    app.cur = cur_k;
+    app.cur_v = cur_v;
+    app.past_len = past_len;
+    app.present_len = present_len;
+    app.cur_len = cur_len;
+    app.reset = reset_error != 0;
+    app.quant = 0;
+    return forward_impl(c, q, batch, q_seq, cache_k, cache_v, cache_capacity, present_len, indices, index_heads,
+                        width, y, 1, &app);
+  }
+  sa_status s = SA_OK;
+  if (reset_error) s = sa::launch_reset_error(c);
+  if (s == SA_OK)
+    s = sparse_attn_kv_append(c, batch, cache_k, cache_v, cache_capacity, past_len, cur_k, cur_v, cur_len, 0,
+                              cache_k, cache_v, cache_capacity, present_len);
+  if (s == SA_OK)
+    s = sparse_attn_forward(c, q, batch, q_seq, cache_k, cache_v, cache_capacity, present_len, indices,
                             index_heads, width, y, 1);
   return s;
 }

@@ -154,6 +154,7 @@ struct FwdArgs {
 // already in the cache's storage format, written in place
 struct AppendArgs {
   const void* cur;
+  const void* cur_v = nullptr;  // separate K/V caches: the current V rows (cur holds K)
   const int32_t* past_len;
   int32_t* present_len;
   int64_t cur_len;
@@ -200,7 +201,11 @@ sa_status launch_forward_latent_decode(sparse_attn_ctx* c, const FwdArgs& a, int
                                        const AppendArgs* app = nullptr);
 sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                               const AppendArgs* app = nullptr);
-sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a);
+// whether a grouped-query launch over q_seq queries validates (and appends) itself
+bool gqa_fuses(const sa_config& cfg, int64_t q_seq);
+// fused (exactly when app is given): the launch validates its index columns,
+// records the error block itself and appends the current K/V rows in place
+sa_status launch_forward_gqa(sparse_attn_ctx* c, const FwdArgs& a, bool fused, const AppendArgs* app);
 // CSA ratio-4 selected sink attention (512-dim rows, 583-byte records)
 struct CsaArgs {
   const float* q;          // [B, S, H, 512]

@@ -51,6 +51,10 @@ __device__ __forceinline__ void ds_min_i32_at(uint32_t addr, int v) {
   asm volatile("ds_min_i32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
+__device__ __forceinline__ void ds_min_u64_at(uint32_t addr, unsigned long long v) {
+  asm volatile("ds_min_u64 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
 // LDS reads issued as inline asm with an immediate offset. The compiler
 // would wait for every outstanding LDS DMA before its own LDS reads, and
 // drains all reads at each of its waits; these are waited for explicitly.

@@ -2,8 +2,9 @@
 violations: the error word, the first failing (row, column) and the message
 equal the oracle validator's verdict, on every forward path. The generic and
 grouped-query paths run the standalone validation kernel before their
-forward; the shared-latent paths validate inside the attention kernels, each
-workgroup its own columns.
+forward (the grouped-query kernel validates in its launch only inside the
+one-launch step, which tests/test_gpu_step_kv.py covers); the shared-latent
+paths validate inside the attention kernels, each workgroup its own columns.
 
 Y of such a launch is not compared (the caller discards it): the launch only
 has to stay in bounds and finish. Rows wider than one 2048-key stage of a
@@ -81,6 +82,16 @@ CASES = {
                                       pattern="causal_prefill"), 3, 17, (2048, 2100)),
     "gqa": (W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=12, past=500, cur=12,
                                             width=520, topk=520), 4, 18, None),
+    # decode rows split over 6 workgroups per (batch, kv head), eight kv heads
+    "gqa_split_decode": (W.WORKLOADS["dense_gqa"].scaled(batch=6, hq=32, hkv=8, q_seq=1, past=5000, cur=1,
+                                                         width=4000, topk=3900, pattern="uniform",
+                                                         softcap=0.0), 4, 20, None),
+    "gqa_split_decode_late": (W.WORKLOADS["dense_gqa"].scaled(batch=6, hq=32, hkv=8, q_seq=1, past=5000, cur=1,
+                                                              width=4000, topk=3990, pattern="uniform",
+                                                              softcap=0.0), 4, 21, (3700, 4000)),
+    # one kv head per query head (32 queries per workgroup), three query blocks
+    "gqa_group1": (W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=4, hkv=4, q_seq=70, past=300, cur=70,
+                                                   width=380, topk=380), 4, 22, None),
     "generic": (W.WORKLOADS["dense_gqa"].scaled(batch=2, hq=8, hkv=2, q_seq=12, past=500, cur=12,
                                                 width=520, topk=520, dtype=W.DT_F16), 0, 19, None),
 }
