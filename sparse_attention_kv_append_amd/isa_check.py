@@ -386,6 +386,12 @@ def check_asm(asm: str) -> list:
 
 
 def checked_sources() -> list:
-    """The sources whose kernels wait for inline-assembly LDS reads by count
-    or use matrix instructions."""
-    return [s for s in _build.sources() if "lgkm_wait" in s.read_text() or "mfma" in s.read_text()]
+    """The sources that define kernels which wait for inline-assembly LDS
+    reads by count or use matrix instructions (host-only sources that merely
+    name such a launcher are left out: their device code holds no kernel)."""
+    out = []
+    for s in _build.sources():
+        t = s.read_text()
+        if "__global__" in t and ("lgkm_wait" in t or "mfma" in t):
+            out.append(s)
+    return out
