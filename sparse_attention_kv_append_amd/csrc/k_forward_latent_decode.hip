@@ -75,6 +75,9 @@ constexpr int M_RESTART = 0, M_LAST = 8, M_FRESH = 16, M_MINKEY = 24, M_FLOOR = 
 static_assert((M_XCH + 256) * 4 <= MISC_BYTES, "misc layout");
 }  // namespace lhd
 
+// cache policy of a store written through the XCD's L2 (sc1)
+constexpr int kWriteThrough = 16;
+
 // APPEND (with FUSED): the launch also appends the batch's cur_len current
 // rows to the cache in place (rows past_len[b] ..) and writes present_len[b];
 // a workgroup that gathers one of them writes the batch's new rows itself
@@ -631,7 +634,9 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
   // head's output is normalised by its row sum and rounded to bf16, then
   // written as whole 1 KB rows through LDS: to Y when the keys are not split,
   // else to the split's partial (the merge kernel combines the splits with
-  // their (reference, row sum) pairs, which stay fp32).
+  // their (reference, row sum) pairs, which stay fp32). The partials are
+  // written through the L2 as they are stored, so the end of the launch has
+  // no 16 MB of dirty partials to write back before the merge can start.
   {
     constexpr int YROW = 1024 + 16;  // padded: the 16 heads of one write hit distinct banks
     __syncthreads();                 // the ring is free
@@ -648,18 +653,29 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
       }
     }
     if (splits > 1 && kh == 0 && g == 0) {
-      const int64_t pr = (row * splits + split) * NH + 16 * hb + c16;
-      part_ml[pr * 2] = m_ref;
-      part_ml[pr * 2 + 1] = l_total(hb);
+      const __amdgpu_buffer_rsrc_t mrsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(part_ml + ((row * splits + split) * NH) * 2), (short)0, NH * 8, 0x00020000);
+      const u32x2_l ml = {__float_as_uint(m_ref), __float_as_uint(l_total(hb))};
+      __builtin_amdgcn_raw_buffer_store_b64(ml, mrsrc, (16 * hb + c16) * 8, 0, kWriteThrough);
     }
     __syncthreads();
-    uint16_t* dst = splits == 1 ? y + (b * NH * q_seq + qi) * DV : (uint16_t*)part_o + (row * splits + split) * NH * DV;
-    const int64_t hstride = splits == 1 ? q_seq * DV : DV;
+    if (splits == 1) {
+      uint16_t* dst = y + (b * NH * q_seq + qi) * DV;
 #pragma unroll 4
-    for (int hq = 0; hq < 8; hq++) {
-      const int hd = 8 * wave + hq;
-      const u32x4_l v = *(const lds_u32x4*)(ring + hd * YROW + 16 * lane);
-      *(u32x4_l*)(dst + hd * hstride + 8 * lane) = v;
+      for (int hq = 0; hq < 8; hq++) {
+        const int hd = 8 * wave + hq;
+        const u32x4_l v = *(const lds_u32x4*)(ring + hd * YROW + 16 * lane);
+        *(u32x4_l*)(dst + hd * q_seq * DV + 8 * lane) = v;
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((uint16_t*)part_o + (row * splits + split) * NH * DV), (short)0, NH * DV * 2, 0x00020000);
+#pragma unroll 4
+      for (int hq = 0; hq < 8; hq++) {
+        const int hd = 8 * wave + hq;
+        const u32x4_l v = *(const lds_u32x4*)(ring + hd * YROW + 16 * lane);
+        __builtin_amdgcn_raw_buffer_store_b128(v, prsrc, hd * (DV * 2) + 16 * lane, 0, kWriteThrough);
+      }
     }
   }
   if constexpr (APPEND) {
