@@ -711,7 +711,7 @@ def make_setup(name, rotate):
 
 
 def kernel_name(setup):
-    if setup.path == 2 and setup.splits > 1 and not isinstance(setup, CapacitySetup):
+    if setup.path == 2 and not isinstance(setup, CapacitySetup):
         return "latent_decode_kernel"
     return {0: "generic_forward_kernel", 1: "mla_forward_kernel", 2: "latent_forward_kernel",
             3: "pair_forward_kernel", 4: "gqa_forward_kernel", 5: "csa_attention_kernel",

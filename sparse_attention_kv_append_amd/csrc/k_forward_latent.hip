@@ -1,5 +1,7 @@
 // Shared-latent selected-token attention over bf16 rows on the gfx950 matrix
-// cores, fed by a direct-to-LDS gather.
+// cores, fed by a direct-to-LDS gather: the form for rows with an attention
+// bias (the eight-wave kernel of k_forward_latent_decode.hip takes the rows
+// without one).
 //
 // All 64 query heads of a (batch, query) row read one kv head through one
 // index row (IndexShare with kv_num_heads = 1 and a shared index list; the

@@ -1,7 +1,8 @@
-// Shared-latent selected-token attention over bf16 rows, the form for rows
-// whose keys are split over several workgroups (decode): gfx950 matrix cores
-// fed by a direct-to-LDS gather, two waves per SIMD, with the value half of
-// each gathered tile read from LDS once.
+// Shared-latent selected-token attention over bf16 rows without an attention
+// bias: gfx950 matrix cores fed by a direct-to-LDS gather, two waves per
+// SIMD, with the value half of each gathered tile read from LDS once. Decode
+// rows split their keys over several workgroups (merged by a second kernel);
+// prefill rows take one workgroup each, the longest rows first.
 //
 // The operation is IndexShare's `index_share_row` with one kv head shared by
 // all 64 query heads and one index list per (batch, query); the 576-wide
@@ -682,20 +683,29 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
     if (duty) {
       if (!app_done) append_rows();
       if (tid == 0) {
-        if (app_ok) present_len[b] = (int32_t)(app_p + cur_len);
+        // an atomic store: this launch's finisher may read it
+        if (app_ok) atomicExch(&present_len[b], (int32_t)(app_p + cur_len));
         else atomicOr(&eb->call_word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
       }
     }
   }
 
-  // ---- error block: this workgroup's first violation goes to the row's slot;
-  // the merge kernel that follows the launch records each row's first
-  // violation and finishes the launch's record
+  // ---- error block: with split keys this workgroup's first violation goes
+  // to the row's slot, and the merge kernel that follows the launch records
+  // each row's first violation and finishes the launch's record; a row's only
+  // workgroup records its row and counts it toward the launch's record itself
   if constexpr (FUSED) {
     __syncthreads();  // every wave's LDS minimum is in
     if (tid == 0) {
       const unsigned long long k = *minkey_s;
-      if (k != ~0ull) atomicMin(&row_key[row], k);
+      if (splits == 1) {
+        if (k != ~0ull) record_row_violation<I64>(eb, idx, row, width, k, bound);
+        // present_len is stored atomically above and read atomically there
+        finish_launch<I64, false>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap,
+                                  (unsigned)rows, reset != 0);
+      } else if (k != ~0ull) {
+        atomicMin(&row_key[row], k);
+      }
     }
   }
 }
@@ -770,17 +780,9 @@ latent_merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict
     if (head != 0 || threadIdx.x != 0) return;
     const unsigned long long k = atomicExch(&row_key[row], ~0ull);
     if (k != ~0ull) {
-      const int64_t col = (int64_t)(k % (unsigned long long)(width + 1));
-      int cls = 6;
-      if (col < width) {
-        int64_t bound = past_len ? (int64_t)past_len[b] + cur_len : (valid_len ? (int64_t)valid_len[b] : cap);
-        bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
-        const int64_t v = load_index<I64>(idx, row * width + col);
-        const int64_t u = col > 0 ? load_index<I64>(idx, row * width + col - 1) : 0;
-        cls = column_class(col, v, u, bound);
-      }
-      atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
-      atomicMin((unsigned long long*)&eb->call_key, k);
+      int64_t bound = past_len ? (int64_t)past_len[b] + cur_len : (valid_len ? (int64_t)valid_len[b] : cap);
+      bound = bound < 0 ? 0 : (bound > cap ? cap : bound);
+      record_row_violation<I64>(eb, idx, row, width, k, bound);
     }
     // the launch's other inputs were written before it began: no cache fences
     finish_launch<I64, false>(eb, idx, width, q_seq, q_seq, past_len ? present_len : valid_len, cap,
@@ -809,11 +811,18 @@ static sa_status launch_latent_merge(sparse_attn_ctx* c, const FwdArgs& a, int64
 
 static bool g_lhd_attr[12] = {};
 
+// The kernel addresses a row's 64 query heads from one buffer resource:
+// 63 head strides of q_seq rows plus one row must fit its 32-bit range.
+bool latent_decode_fits(int64_t q_seq) {
+  return q_seq >= 1 && (lhd::NH - 1) * q_seq * lhd::ROWB + lhd::ROWB <= 0x7fffffffLL;
+}
+
 sa_status launch_forward_latent_decode(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                                        const AppendArgs* app) {
   using namespace lhd;
   const int64_t rows = a.batch * a.q_seq;
   if (rows <= 0) return SA_OK;
+  if (!latent_decode_fits(a.q_seq)) return set_error(c, SA_E_STATE, "forward: q_seq too large for the decode kernel");
   if (splits > 1 && rows * splits > c->partial_rows)
     return set_error(c, SA_E_STATE, "forward: split-K partials exceed the context's buffers");
   if (rows > c->rows_cap) return set_error(c, SA_E_STATE, "forward: more rows than the context holds");

@@ -436,8 +436,9 @@ static sa_status forward_impl(sparse_attn_ctx* c, const void* q, int64_t batch, 
   switch (path) {
     case 2: {
       const int splits = sa::mla_splits(batch * q_seq, width);
-      return splits > 1 && !bias ? sa::launch_forward_latent_decode(c, a, splits, fused_validate != 0, app)
-                                 : sa::launch_forward_latent(c, a, splits, fused_validate != 0, app);
+      return !bias && sa::latent_decode_fits(q_seq)
+                 ? sa::launch_forward_latent_decode(c, a, splits, fused_validate != 0, app)
+                 : sa::launch_forward_latent(c, a, splits, fused_validate != 0, app);
     }
     case 3: return sa::launch_forward_pair(c, a, sa::mla_splits(batch * q_seq, width), fused_validate != 0, app);
     case 1: return sa::launch_forward_mla(c, a, sa::mla_splits(batch * q_seq, width));
@@ -943,8 +944,8 @@ sa_status sparse_attn_forward_latent_static(const void* q, int64_t batch, int64_
   a.cache_format = k.cache_format;
   a.kv_layout = k.kv_layout;
   a.idx64 = index_dtype == SA_IDX_I64;
-  const sa_status st = splits > 1 ? sa::launch_forward_latent_decode(&sh, a, splits, false, nullptr)
-                                  : sa::launch_forward_latent(&sh, a, 1, false, nullptr);
+  const sa_status st = sa::latent_decode_fits(q_seq) ? sa::launch_forward_latent_decode(&sh, a, splits, false, nullptr)
+                                                     : sa::launch_forward_latent(&sh, a, splits, false, nullptr);
   if (st != SA_OK) g_static_error = "forward_latent_static: " + sh.last_error;
   return st;
 }

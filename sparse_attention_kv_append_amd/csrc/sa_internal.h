@@ -194,9 +194,12 @@ sa_status launch_capacity_append(sparse_attn_ctx* c, const void* bias, int dtype
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
 sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                                 const AppendArgs* app = nullptr);
-// the same rows when their keys are split over several workgroups (decode):
-// waves split into (head half, key half) for the scores and (head half, dv
-// half) for the outputs, exchanging bf16 probabilities through LDS
+// the same rows without a bias on the eight-wave kernel: each wave scores one
+// 16-head block over one key half and does the PV of one dv eighth for all
+// heads, exchanging bf16 probabilities through LDS; split keys are merged by
+// a second kernel
+// whether a launch over q_seq queries fits the eight-wave kernel's addressing
+bool latent_decode_fits(int64_t q_seq);
 sa_status launch_forward_latent_decode(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                                        const AppendArgs* app = nullptr);
 sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,

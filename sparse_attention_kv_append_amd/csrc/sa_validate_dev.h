@@ -22,6 +22,24 @@ __device__ __forceinline__ int column_class(int64_t c, int64_t v, int64_t u, int
   return 0;
 }
 
+// A row's first violation k (row * (width + 1) + column; column == width:
+// the row holds only -1) turned into its class bit in the launch's word and
+// offered as the launch's first key.
+template <bool I64>
+__device__ __forceinline__ void record_row_violation(ErrorBlock* __restrict__ eb, const void* __restrict__ idx,
+                                                     int64_t row, int64_t width, unsigned long long k,
+                                                     int64_t bound) {
+  const int64_t col = (int64_t)(k % (unsigned long long)(width + 1));
+  int cls = 6;
+  if (col < width) {
+    const int64_t v = load_index<I64>(idx, row * width + col);
+    const int64_t u = col > 0 ? load_index<I64>(idx, row * width + col - 1) : 0;
+    cls = column_class(col, v, u, bound);
+  }
+  atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
+  atomicMin((unsigned long long*)&eb->call_key, k);
+}
+
 // Called by one thread of each of the `expected` participants of a launch
 // that gathers into the context's error block (every block of the validation
 // kernel; the finisher of every row in the forward kernel), after its
@@ -57,7 +75,9 @@ __device__ __forceinline__ void finish_launch(ErrorBlock* __restrict__ eb, const
     const int64_t r = (int64_t)(key / (unsigned long long)(width + 1));
     const int64_t c = (int64_t)(key % (unsigned long long)(width + 1));
     const int64_t b = r / rows_per_batch;
-    const int64_t bound = valid_len ? (int64_t)valid_len[b] : cache_len;
+    // an atomic load: a length stored (atomically) in this launch is seen
+    const int64_t bound =
+        valid_len ? (int64_t)__hip_atomic_load(&valid_len[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : cache_len;
     int64_t v = -1, u = 0;
     int k = 6;  // column == width: the row holds only -1
     if (c < width) {
