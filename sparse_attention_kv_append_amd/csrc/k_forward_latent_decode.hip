@@ -76,9 +76,6 @@ constexpr int M_RESTART = 0, M_LAST = 8, M_FRESH = 16, M_MINKEY = 24, M_FLOOR = 
 static_assert((M_XCH + 256) * 4 <= MISC_BYTES, "misc layout");
 }  // namespace lhd
 
-// cache policy of a store written through the XCD's L2 (sc1)
-constexpr int kWriteThrough = 16;
-
 // APPEND (with FUSED): the launch also appends the batch's cur_len current
 // rows to the cache in place (rows past_len[b] ..) and writes present_len[b];
 // a workgroup that gathers one of them writes the batch's new rows itself
@@ -790,7 +787,7 @@ latent_merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict
   }
 }
 
-static sa_status launch_latent_merge(sparse_attn_ctx* c, const FwdArgs& a, int64_t rows, int splits, bool fused,
+sa_status launch_latent_merge(sparse_attn_ctx* c, const FwdArgs& a, int64_t rows, int splits, bool fused,
                                      const AppendArgs* app) {
   const dim3 grid((unsigned)(rows * lhd::NH)), block(lhd::DV / 4);
   const int32_t* plen = app ? app->past_len : nullptr;

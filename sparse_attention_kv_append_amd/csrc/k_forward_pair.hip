@@ -659,10 +659,14 @@ pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
     l0 = s0 + __uint_as_float(pl[0]);
     l1 = s1 + __uint_as_float(pl[1]);
   }
-  // lane holds O^T[256 half + 16 dt + 4g + r][head0 (+16)]
-  if (splits == 1) {
-    // bf16 rows through LDS (the ring is free): head h's 512 values at
-    // h * YROW, then every lane stores 16 contiguous bytes of one head's row
+  // lane holds O^T[256 half + 16 dt + 4g + r][head0 (+16)]. Every head's
+  // output is normalised by its row sum and rounded to bf16 into LDS rows
+  // (the ring is free), then each lane stores 16 contiguous bytes of one
+  // head's row: to Y when the keys are not split, else to the split's partial
+  // (with its fp32 (reference, row sum) pairs, merged by the bf16 merge
+  // kernel), written through the L2 so the launch's end has no dirty
+  // partials to write back.
+  {
     constexpr int YROW = 1024 + 16;
     __syncthreads();
     const float inv0 = l0 > 0.0f ? 1.0f / l0 : 0.0f;
@@ -676,28 +680,31 @@ pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
       *(__attribute__((address_space(3))) u32x2_l*)(y1 + 32 * dt) =
           (u32x2_l){pack_bf16x2(o1[dt][0] * inv1, o1[dt][1] * inv1), pack_bf16x2(o1[dt][2] * inv1, o1[dt][3] * inv1)};
     }
+    if (splits > 1 && g == 0 && half == 0) {
+      const __amdgpu_buffer_rsrc_t mrsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(part_ml + (row * splits + split) * NH * 2), (short)0, NH * 8, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2_l){__float_as_uint(m_ref0), __float_as_uint(l0)}, mrsrc,
+                                            head0 * 8, 0, kWriteThrough);
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2_l){__float_as_uint(m_ref1), __float_as_uint(l1)}, mrsrc,
+                                            (head0 + 16) * 8, 0, kWriteThrough);
+    }
     __syncthreads();
+    if (splits == 1) {
 #pragma unroll 4
-    for (int hh = 0; hh < 16; hh++) {
-      const int h = 16 * wave + hh;
-      const u32x4_l v = *(const lds_u32x4*)(ring + h * YROW + 16 * lane);
-      *(u32x4_l*)(y + ((b * NH + h) * q_seq + qi) * DV + 8 * lane) = v;
-    }
-  } else {
-    // unnormalised partials; the combine kernel merges them after this launch
-    const int64_t pr0 = (row * splits + split) * NH + head0;
-    float* op0 = part_o + pr0 * DV + (DV / 2) * half + 4 * g;
-    float* op1 = op0 + 16 * DV;
-#pragma unroll
-    for (int dt = 0; dt < DVT; dt++) {
-      *(float4*)(op0 + 16 * dt) = make_float4(o0[dt][0], o0[dt][1], o0[dt][2], o0[dt][3]);
-      *(float4*)(op1 + 16 * dt) = make_float4(o1[dt][0], o1[dt][1], o1[dt][2], o1[dt][3]);
-    }
-    if (g == 0 && half == 0) {
-      part_ml[pr0 * 2] = m_ref0;
-      part_ml[pr0 * 2 + 1] = l0;
-      part_ml[(pr0 + 16) * 2] = m_ref1;
-      part_ml[(pr0 + 16) * 2 + 1] = l1;
+      for (int hh = 0; hh < 16; hh++) {
+        const int h = 16 * wave + hh;
+        const u32x4_l v = *(const lds_u32x4*)(ring + h * YROW + 16 * lane);
+        *(u32x4_l*)(y + ((b * NH + h) * q_seq + qi) * DV + 8 * lane) = v;
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((uint16_t*)part_o + (row * splits + split) * NH * DV), (short)0, NH * DV * 2, 0x00020000);
+#pragma unroll 4
+      for (int hh = 0; hh < 16; hh++) {
+        const int h = 16 * wave + hh;
+        const u32x4_l v = *(const lds_u32x4*)(ring + h * YROW + 16 * lane);
+        __builtin_amdgcn_raw_buffer_store_b128(v, prsrc, h * (DV * 2) + 16 * lane, 0, kWriteThrough);
+      }
     }
   }
   if constexpr (APPEND) {
@@ -705,44 +712,29 @@ pair_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache,
       if (!app_done) append_rows();
       if (app_bad && lane == 0) atomicOr(&eb->call_word, SA_ERR_QUANT_NONFINITE | SA_ERR_APPEND_ANY);
       if (tid == 0) {
-        if (app_ok) present_len[b] = (int32_t)(app_p + cur_len);
+        // an atomic store: this launch's finisher may read it
+        if (app_ok) atomicExch(&present_len[b], (int32_t)(app_p + cur_len));
         else atomicOr(&eb->call_word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
       }
     }
   }
   if constexpr (FUSED) __syncthreads();  // minkey_s is complete
 
-  // ---- error block: the finisher of each row records the row's first
-  // violation and counts itself toward the launch's last-arrival record
+  // ---- error block: with split keys this workgroup's first violation goes
+  // to the row's slot, and the merge kernel that follows the launch records
+  // each row's first violation and finishes the launch's record; a row's only
+  // workgroup records its row and counts it toward the launch's record itself
   if constexpr (FUSED) {
     if (tid == 0) {
-      unsigned long long k = *minkey_s;
-      bool finisher = true;
-      if (splits > 1) {
-        if (k != ~0ull) {
-          atomicMin(&row_key[row], k);
-          __threadfence();
-        }
-        finisher = atomicAdd(&row_done[row], 1u) == (unsigned)splits - 1;
-        if (finisher) {
-          row_done[row] = 0u;
-          k = atomicExch(&row_key[row], ~0ull);
-        }
+      const unsigned long long k = *minkey_s;
+      if (splits == 1) {
+        if (k != ~0ull) record_row_violation<I64>(eb, idx, row, width, k, bound);
+        // present_len is stored atomically above and read atomically there
+        finish_launch<I64, false>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap,
+                                  (unsigned)rows, reset != 0);
+      } else if (k != ~0ull) {
+        atomicMin(&row_key[row], k);
       }
-      if (finisher && k != ~0ull) {
-        const int64_t col = (int64_t)(k % (unsigned long long)(width + 1));
-        int cls = 6;
-        if (col < width) {
-          const int64_t v = load_index<I64>(idx, ibase + col);
-          const int64_t u = col > 0 ? load_index<I64>(idx, ibase + col - 1) : 0;
-          cls = column_class(col, v, u, bound);
-        }
-        atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
-        atomicMin((unsigned long long*)&eb->call_key, k);
-      }
-      if (finisher)
-        finish_launch<I64>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap, (unsigned)rows,
-                           reset != 0);
     }
   }
 }
@@ -835,7 +827,7 @@ sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, 
 #undef SA_PAIR
   sa_status s = check_hip(c, hipGetLastError(), "forward (fp8 pair)");
   if (s != SA_OK || splits == 1) return s;
-  return launch_mla_combine(c, rows, a.q_seq, splits, (uint16_t*)a.y);
+  return launch_latent_merge(c, a, rows, splits, fused, app);
 }
 
 }  // namespace sa

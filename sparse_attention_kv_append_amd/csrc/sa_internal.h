@@ -200,6 +200,11 @@ sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits
 // a second kernel
 // whether a launch over q_seq queries fits the eight-wave kernel's addressing
 bool latent_decode_fits(int64_t q_seq);
+// log-sum-exp merge of split partials written as normalised bf16 rows with
+// their fp32 (reference, row sum) pairs; with fused validation it also records
+// each row's first violation and finishes the launch's record
+sa_status launch_latent_merge(sparse_attn_ctx* c, const FwdArgs& a, int64_t rows, int splits, bool fused,
+                              const AppendArgs* app);
 sa_status launch_forward_latent_decode(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                                        const AppendArgs* app = nullptr);
 sa_status launch_forward_pair(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,

@@ -37,6 +37,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_l){a, b}, bf16x2_l));
 }
 
+// cache policy of a buffer store written through the XCD's L2 (sc1): a
+// launch's end then has no dirty lines of it to write back
+constexpr int kWriteThrough = 16;
+
 // vmcnt-only wait (gfx9 encoding: expcnt and lgkmcnt left at their maxima)
 template <int N>
 __device__ __forceinline__ void wait_vm() {
