@@ -363,35 +363,12 @@ __device__ __forceinline__ uint32_t total_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// inclusive prefix sum over the 64 lanes of a wave
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-// sum over the 64 lanes (every lane gets it): row rotations (DPP) within each
-// 16-lane row, then the gfx950 permlane swaps across rows
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);  // row_ror:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false);  // row_ror:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false);  // row_ror:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false);  // row_ror:1
-  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = a[0] + a[1];
-  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return c[0] + c[1];
-}
-
 // One workgroup per (batch, query). Thread t holds the total-order keys of
-// records t, t + 256, ... in registers (key 0 for padding, below every
+// records t, t + 1024, ... in registers (key 0 for padding, below every
 // score's key); the k-th largest key is found by a binary search over key
-// values (counting probes reduced without atomics), the winners are placed by
-// a scan, and sorted by rank (each winner counts the larger ones).
+// values (each probe counted by wave ballots and summed over the waves
+// through LDS), the winners take slots by one LDS atomic per wave and key
+// register, and are sorted by rank (each winner counts the larger ones).
 // Exact score ties, which the CSA CPU page rejects (`select_ratio4_topk`),
 // are found by workgroups of their own beside the row's select workgroup: the
 // row's scores are split by a hash of their value into P parts and each part
@@ -432,7 +409,9 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int32_
   using namespace cx;
   constexpr int NT = 1024, NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  uint32_t* tot = (uint32_t*)smem;                            // [3 NW] probe (two) and scan partials
+  // [2 NW] probe partials (two buffers), [NW] partials of keys at the cut,
+  // [48] winner slot counter
+  uint32_t* tot = (uint32_t*)smem;
   unsigned long long* win = (unsigned long long*)(tot + 64);  // [KMAX] winners (key, ~record)
   uint32_t kv[NJ];
 #pragma unroll
@@ -441,9 +420,27 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int32_
     const uint32_t x = total_key(src[i < n ? i : 0]);
     kv[j] = i < n ? x : 0u;
   }
+  // the sum of this wave's partials over the NW waves (four 16-byte reads)
+  auto sum_parts = [&](int base) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < NW / 4; q++) {
+      const uint4 v = *(const uint4*)(tot + base + 4 * q);
+      c += (v.x + v.y) + (v.z + v.w);
+    }
+    return c;
+  };
+  // keys of this wave that satisfy pred, counted by ballots (uniform)
+  auto wave_count = [&](auto pred) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) c += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(pred(kv[j], j)));
+    return c;
+  };
   const int k = min(K, n);
   uint32_t T = 0;
   int need = k;
+  if (tid == 0) tot[48] = 0u;
   if (k > 0 && k < n) {
     uint64_t lo = 1, hi = 1ull << 32;  // count(>= lo) >= k (every real key is >= 1), count(>= hi) < k
     uint32_t c_hi = 0;
@@ -451,15 +448,11 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int32_
     while (hi - lo > 1) {
       const uint64_t mid = lo + ((hi - lo) >> 1);
       const uint32_t t = (uint32_t)mid;
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int j = 0; j < NJ; j++) cnt += kv[j] >= t ? 1u : 0u;
-      cnt = wave_sum_u32(cnt);
+      const uint32_t cnt = wave_count([&](uint32_t x, int) { return x >= t; });
       if (lane == 0) tot[NW * par + w] = cnt;
       __syncthreads();
-      uint32_t c = 0;
-#pragma unroll
-      for (int q = 0; q < NW; q++) c += tot[NW * par + q];
+      // uniform: the loop's control stays on the scalar unit
+      const uint32_t c = __builtin_amdgcn_readfirstlane(sum_parts(NW * par));
       par ^= 1;
       if (c >= (uint32_t)k) {
         lo = mid;
@@ -473,40 +466,29 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int32_
   }
   // winners: keys > T, and keys == T unless they straddle the cut
   uint32_t eq = 0;
-  if (k < n) {
-#pragma unroll
-    for (int j = 0; j < NJ; j++) eq += (kv[j] == T) ? 1u : 0u;
-  }
-  eq = wave_sum_u32(eq);
+  if (k < n) eq = wave_count([&](uint32_t x, int) { return x == T; });
+  if (lane == 0) tot[2 * NW + w] = eq;
   __syncthreads();
-  if (lane == 0) tot[w] = eq;
-  __syncthreads();
-  uint32_t n_eq = 0;
-#pragma unroll
-  for (int q = 0; q < NW; q++) n_eq += tot[q];
+  const uint32_t n_eq = __builtin_amdgcn_readfirstlane(sum_parts(2 * NW));
   const bool split_ties = k < n && n_eq > (uint32_t)need;
-  uint32_t mine = 0;
-#pragma unroll
-  for (int j = 0; j < NJ; j++) {
-    const uint32_t x = kv[j];
-    mine += (tid + NT * j < n && (k >= n || x > T || (x == T && !split_ties))) ? 1u : 0u;
-  }
-  const uint32_t inc = wave_incl_scan(mine);
-  if (lane == 63) tot[2 * NW + w] = inc;
-  __syncthreads();
-  uint32_t slot = inc - mine, n_win = 0;
-  for (int q = 0; q < NW; q++) {
-    const uint32_t v = tot[2 * NW + q];
-    if (q < w) slot += v;
-    n_win += v;
-  }
+  // each wave takes slots for its winners of one register at a time (one
+  // LDS atomic per wave); the order of the slots does not matter, the rank
+  // sort below orders the winners
 #pragma unroll
   for (int j = 0; j < NJ; j++) {
     const int i = tid + NT * j;
     const uint32_t x = kv[j];
-    if (i < n && (k >= n || x > T || (x == T && !split_ties)))
-      win[slot++] = ((unsigned long long)x << 32) | (uint32_t)(~(uint32_t)i);
+    const bool won = i < n && (k >= n || x > T || (x == T && !split_ties));
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(won);
+    if (bal == 0) continue;  // uniform
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&tot[48], (uint32_t)__builtin_popcountll(bal));
+    base = __builtin_amdgcn_readfirstlane(base);
+    const uint32_t before = (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    if (won) win[base + before] = ((unsigned long long)x << 32) | (uint32_t)(~(uint32_t)i);
   }
+  __syncthreads();
+  const uint32_t n_win = tot[48];
   if (split_ties && w == 0) {
     // equal keys at the cut: the first `need` of them in ascending record order
     uint32_t taken = 0;
@@ -522,20 +504,32 @@ __device__ __forceinline__ void select_row(const float* __restrict__ src, int32_
   }
   __syncthreads();
   // rank sort: the winners' composite keys are distinct; a winner's output
-  // position is the number of larger ones (every thread reads the same
-  // winner at the same time: LDS broadcast)
-  int32_t* out0 = outb;
-  for (int a = tid; a < k; a += NT) {
+  // position is the number of larger ones. Two threads count for each winner,
+  // over one half of the winners each (the halves in different waves, so the
+  // waves of a half read the same winner at the same time: LDS broadcast), and
+  // add their counts in LDS.
+  int* rk = (int*)(win + KMAX);  // [KMAX] ranks
+  for (int a = tid; a < k; a += NT) rk[a] = 0;
+  __syncthreads();
+  const int hk = (k + 1) >> 1;
+  for (int it = tid; it < 2 * k; it += NT) {
+    const int a = it < k ? it : it - k;
+    const int q0 = it < k ? 0 : hk, q1 = it < k ? hk : k;
     const unsigned long long x = win[a];
     int r8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int q = 0;
-    for (; q + 8 <= k; q += 8) {
+    int q = q0;
+    for (; q + 8 <= q1; q += 8) {
 #pragma unroll
       for (int u = 0; u < 8; u++) r8[u] += win[q + u] > x ? 1 : 0;
     }
-    for (; q < k; q++) r8[0] += win[q] > x ? 1 : 0;
-    const int rank = ((r8[0] + r8[1]) + (r8[2] + r8[3])) + ((r8[4] + r8[5]) + (r8[6] + r8[7]));
-    const int32_t rec = (int32_t)(~(uint32_t)(x & 0xffffffffull));
+    for (; q < q1; q++) r8[0] += win[q] > x ? 1 : 0;
+    atomicAdd(&rk[a], ((r8[0] + r8[1]) + (r8[2] + r8[3])) + ((r8[4] + r8[5]) + (r8[6] + r8[7])));
+  }
+  __syncthreads();
+  int32_t* out0 = outb;
+  for (int a = tid; a < k; a += NT) {
+    const int32_t rec = (int32_t)(~(uint32_t)(win[a] & 0xffffffffull));
+    const int rank = rk[a];
     for (int h = 0; h < out_heads; h++) out0[(int64_t)h * S * K + rank] = rec;
   }
   for (int j = k + tid; j < K; j += NT)
@@ -589,7 +583,7 @@ sa_status launch_csa_index_select(sparse_attn_ctx* c, const CsaIndexArgs& a) {
   uint16_t* qf = (uint16_t*)((uint8_t*)a.workspace + sb);
   uint8_t* qe = (uint8_t*)(qf + (size_t)rows * (size_t)a.heads * D);
   const size_t score_lds = (size_t)RB * KB + (size_t)RB * DSTR * 4 + (size_t)HMAX * 8 + 16;
-  const size_t select_lds = std::max((size_t)64 * 4 + (size_t)KMAX * 8, (size_t)TIE_SLOTS * 4);
+  const size_t select_lds = std::max((size_t)64 * 4 + (size_t)KMAX * 12, (size_t)TIE_SLOTS * 4);
   const void* score_fns[4] = {(const void*)csa_index_score_kernel<1>, (const void*)csa_index_score_kernel<2>,
                               (const void*)csa_index_score_kernel<3>, (const void*)csa_index_score_kernel<4>};
   static bool attr = false;
