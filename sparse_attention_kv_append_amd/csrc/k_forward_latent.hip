@@ -8,8 +8,8 @@
 // latent row is 576 wide and its first 512 dims are V). Per 32-key tile:
 // S^T = K_sel . Q^T and O^T += V_sel^T . P^T on v_mfma_f32_16x16x32_bf16, an
 // online softmax per head, and optionally a split of the row's keys over
-// several workgroups merged by log-sum-exp (the combine kernel of the
-// register-staged shared-latent path).
+// several workgroups merged by log-sum-exp (the bf16 merge kernel of the
+// eight-wave kernel).
 //
 // Data movement:
 //  * the gathered rows go from HBM straight into LDS (global_load_lds, 16 B
@@ -29,8 +29,9 @@
 //  * each head keeps a fixed softmax reference (its first tile's max), so the
 //    O^T accumulators are only ever touched by the MFMAs;
 //  * with fused validation each workgroup checks its own columns of the index
-//    row (IndexShare host-validator rules) while it stages the keys, and only
-//    the finisher of each row touches the error block, after the attention.
+//    row (IndexShare host-validator rules) while it stages the keys; a row's
+//    first violation is recorded by its only workgroup, or, with split keys,
+//    by the merge kernel that follows the launch.
 #include "sa_mfma_dev.h"
 #include "sa_validate_dev.h"
 
@@ -541,10 +542,14 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
     if (mk != ~0ull) atomicMin(minkey_s, mk);
   }
 
-  // ---- epilogue: lane holds O^T[16 dt + 4g + r][16 wave + c16]
-  if (splits == 1) {
-    // bf16 rows through LDS (the ring is free): head h's 512 values at
-    // h * YROW, then every lane stores 16 contiguous bytes of one head's row
+  // ---- epilogue: lane holds O^T[16 dt + 4g + r][16 wave + c16]. Every
+  // head's output is normalised by its row sum and rounded to bf16 into LDS
+  // rows (the ring is free), then each lane stores 16 contiguous bytes of one
+  // head's row: to Y when the keys are not split, else to the split's partial
+  // (with its fp32 (reference, row sum) pairs, merged by the bf16 merge
+  // kernel), written through the L2 so the launch's end has no dirty
+  // partials to write back.
+  {
     constexpr int YROW = 1024 + 16;  // padded: the 16 heads of one write hit distinct banks
     __syncthreads();
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
@@ -555,66 +560,58 @@ latent_forward_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cach
       const uint32_t hi = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
       *(__attribute__((address_space(3))) u32x2_l*)(yl + 32 * dt) = (u32x2_l){lo, hi};
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int hh = 0; hh < 16; hh++) {
-      const int h = 16 * wave + hh;
-      const u32x4_l v = *(const lds_u32x4*)(ring + h * YROW + 16 * lane);
-      *(u32x4_l*)(y + ((b * NH + h) * q_seq + qi) * DV + 8 * lane) = v;
+    if (splits > 1 && g == 0) {
+      const __amdgpu_buffer_rsrc_t mrsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(part_ml + (row * splits + split) * NH * 2), (short)0, NH * 8, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2_l){__float_as_uint(m_ref), __float_as_uint(l_run)}, mrsrc,
+                                            head * 8, 0, kWriteThrough);
     }
-  } else {
-    // unnormalised partials; the combine kernel merges them after this launch
-    const int64_t pr = (row * splits + split) * NH + head;
-    float* op = part_o + pr * DV + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < DVT; dt++) *(float4*)(op + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (g == 0) {
-      part_ml[pr * 2] = m_ref;
-      part_ml[pr * 2 + 1] = l_run;
+    __syncthreads();
+    if (splits == 1) {
+#pragma unroll 4
+      for (int hh = 0; hh < 16; hh++) {
+        const int h = 16 * wave + hh;
+        const u32x4_l v = *(const lds_u32x4*)(ring + h * YROW + 16 * lane);
+        *(u32x4_l*)(y + ((b * NH + h) * q_seq + qi) * DV + 8 * lane) = v;
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((uint16_t*)part_o + (row * splits + split) * NH * DV), (short)0, NH * DV * 2, 0x00020000);
+#pragma unroll 4
+      for (int hh = 0; hh < 16; hh++) {
+        const int h = 16 * wave + hh;
+        const u32x4_l v = *(const lds_u32x4*)(ring + h * YROW + 16 * lane);
+        __builtin_amdgcn_raw_buffer_store_b128(v, prsrc, h * (DV * 2) + 16 * lane, 0, kWriteThrough);
+      }
     }
   }
   if constexpr (APPEND) {
     if (duty) {
       if (!app_done) append_rows();
       if (tid == 0) {
-        if (app_ok) present_len[b] = (int32_t)(app_p + cur_len);
+        // an atomic store: this launch's finisher may read it
+        if (app_ok) atomicExch(&present_len[b], (int32_t)(app_p + cur_len));
         else atomicOr(&eb->call_word, SA_ERR_APPEND_CAPACITY | SA_ERR_APPEND_ANY);
       }
     }
   }
   if constexpr (FUSED) __syncthreads();  // minkey_s is complete
 
-  // ---- error block: the finisher of each row records the row's first
-  // violation and counts itself toward the launch's last-arrival record
+  // ---- error block: with split keys this workgroup's first violation goes
+  // to the row's slot, and the merge kernel that follows the launch records
+  // each row's first violation and finishes the launch's record; a row's only
+  // workgroup records its row and counts it toward the launch's record itself
   if constexpr (FUSED) {
     if (tid == 0) {
-      unsigned long long k = *minkey_s;
-      bool finisher = true;
-      if (splits > 1) {
-        if (k != ~0ull) {
-          atomicMin(&row_key[row], k);
-          __threadfence();  // the row minimum is visible before this split is counted
-        }
-        finisher = atomicAdd(&row_done[row], 1u) == (unsigned)splits - 1;
-        if (finisher) {
-          row_done[row] = 0u;                    // re-armed for the next launch
-          k = atomicExch(&row_key[row], ~0ull);  // every split's minimum, re-armed
-        }
+      const unsigned long long k = *minkey_s;
+      if (splits == 1) {
+        if (k != ~0ull) record_row_violation<I64>(eb, idx, row, width, k, bound);
+        // present_len is stored atomically above and read atomically there
+        finish_launch<I64, false>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap,
+                                  (unsigned)rows, reset != 0);
+      } else if (k != ~0ull) {
+        atomicMin(&row_key[row], k);
       }
-      if (finisher && k != ~0ull) {
-        const int64_t col = (int64_t)(k % (unsigned long long)(width + 1));
-        int cls = 6;
-        if (col < width) {
-          const int64_t v = load_index<I64>(idx, ibase + col);
-          const int64_t u = col > 0 ? load_index<I64>(idx, ibase + col - 1) : 0;
-          cls = column_class(col, v, u, bound);
-        }
-        atomicOr(&eb->call_word, (1u << (cls - 1)) | SA_ERR_INDEX_ANY);
-        atomicMin((unsigned long long*)&eb->call_key, k);
-      }
-      if (finisher)
-        finish_launch<I64>(eb, idx, width, q_seq, q_seq, APPEND ? present_len : valid_len, cap, (unsigned)rows,
-                           reset != 0);
     }
   }
 }
@@ -705,7 +702,7 @@ sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits
 #undef SA_LAT
   sa_status s = check_hip(c, hipGetLastError(), "forward (latent)");
   if (s != SA_OK || splits == 1) return s;
-  return launch_mla_combine(c, rows, a.q_seq, splits, (uint16_t*)a.y);
+  return launch_latent_merge(c, a, rows, splits, fused, app);
 }
 
 }  // namespace sa
