@@ -9,8 +9,9 @@
 // The pages give one thread per batch entry looping over every broadcast
 // (h, q, k). Here one 256-thread workgroup per batch entry reads the entry's
 // slice of the bias coalesced: in 16-byte vectors (four per thread in
-// flight) when the rows are whole vectors, else each row from its end down,
-// stopping at the first chunk that holds a finite element. An extent of 1
+// flight) when the rows are whole vectors, else each row from its end down in
+// batches of aligned 16-byte vectors (sixteen per thread in flight), stopping
+// at the first batch that holds a finite element. An extent of 1
 // along heads or queries is not expanded, and an extent of 1 along keys
 // makes a finite element stand for every column. Finiteness is read from the
 // exponent bits (vector path). The per-thread maxima are reduced with wave
@@ -22,6 +23,7 @@ namespace sa {
 
 constexpr int kCapThreads = 256;
 constexpr int kCapUnroll = 4;  // 16-byte loads per thread in flight at once
+constexpr int kRowUnroll = 16;  // the same, scanning one row that is not whole vectors
 
 // finite test on the raw bits of one element (exponent not all ones)
 template <int DT>
@@ -76,30 +78,58 @@ __device__ __forceinline__ int capacity_scan(const void* __restrict__ bias, int6
     }
   } else {
     // rows that are not whole vectors: each (h, q) row is scanned from its
-    // last column down in chunks of kCapThreads * 8 columns (eight loads per
-    // thread in flight), and the row ends at the first chunk holding a finite
-    // element, since no lower column can raise the row's maximum; a frontier
-    // near the end of the row touches one or two chunks
-    constexpr int CH = kCapThreads * 8;
+    // last column down in batches of kCapThreads x kRowUnroll 16-byte
+    // vectors (aligned to their own address; the at most 2 x (PER - 1)
+    // elements before the first and after the last whole vector by single
+    // loads, in the first batch), all of a batch's loads in flight at once;
+    // the row ends at the first batch holding a finite element, since no
+    // lower column can raise the row's maximum
+    constexpr int ES = DT == SA_F32 ? 4 : 2;
+    constexpr int PER = 16 / ES;
+    constexpr int64_t BATCH = (int64_t)kCapThreads * kRowUnroll;  // vectors per batch
     const int64_t rows = bd1 * bd2;
     for (int64_t r = 0; r < rows; r++) {
       const int64_t rb = base + r * bd3;
-      for (int64_t top = bd3; top > 0; top -= CH) {
-        int found = 0;  // 1 + the largest finite column of this chunk seen by this thread
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-          const int64_t k = top - 1 - (threadIdx.x + (int64_t)u * kCapThreads);
-          v[u] = k >= 0 ? load_elem<DT>(bias, rb + k) : __builtin_nanf("");
-        }
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-          const int64_t k = top - 1 - (threadIdx.x + (int64_t)u * kCapThreads);
-          if (isfinite(v[u])) found = max(found, bd3 == 1 ? (int)keys : (int)(k + 1));
-        }
-        best = max(best, found);
-        if (__syncthreads_or(found > 0)) break;  // uniform
+      if (bd3 == 1) {  // one element stands for every key
+        if (threadIdx.x == 0 && isfinite(load_elem<DT>(bias, rb))) best = (int)keys;
+        continue;
       }
+      const uintptr_t addr = (uintptr_t)bias + (uintptr_t)(rb * ES);
+      const int64_t ka = min((int64_t)(((addr + 15) & ~(uintptr_t)15) - addr) / ES, bd3);  // first aligned column
+      const int64_t nvec = (bd3 - ka) / PER;
+      const int64_t kt = ka + nvec * PER;  // first column after the last whole vector
+      const uint4* __restrict__ vp = (const uint4*)(addr + (uintptr_t)(ka * ES));
+      // the loose elements: threads 0 .. PER-2 take those before the first
+      // whole vector (the row's lowest columns: they count only when nothing
+      // above them is finite), threads PER .. 2 PER - 2 those after the last
+      // (its highest: they count with the first batch)
+      int found = 0;  // 1 + the largest finite column at or above the current batch
+      int low = 0;    // 1 + the largest finite column before the first whole vector
+      {
+        const int t = (int)threadIdx.x;
+        if (t < PER - 1 && t < ka && isfinite(load_elem<DT>(bias, rb + t))) low = t + 1;
+        if (t >= PER && t < 2 * PER - 1 && kt + (t - PER) < bd3 &&
+            isfinite(load_elem<DT>(bias, rb + kt + (t - PER))))
+          found = (int)(kt + (t - PER) + 1);
+      }
+      for (int64_t top = nvec; ; top -= BATCH) {
+        uint4 vals[kRowUnroll];
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; u++) {
+          const int64_t v = top - 1 - (threadIdx.x + (int64_t)u * kCapThreads);
+          vals[u] = v >= 0 ? vp[v] : make_uint4(0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu);  // NaN: skipped
+        }
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; u++) {
+          const int64_t v = top - 1 - (threadIdx.x + (int64_t)u * kCapThreads);
+          if (v >= 0) {
+            const int c = vec_best<DT>(vals[u], 0, (int64_t)1 << 62, keys);  // 1 + its last finite lane, or 0
+            if (c > 0) found = max(found, (int)(ka + v * PER + c));
+          }
+        }
+        if (__syncthreads_or(found > 0) || top <= BATCH) break;  // uniform
+      }
+      best = max(best, max(found, low));
     }
   }
   best = wave_max_nonneg(best);

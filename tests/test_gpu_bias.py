@@ -232,7 +232,11 @@ def test_bias_host_errors():
                                          (W.DT_F16, (1, 8, 1, 300)), (W.DT_F32, (3, 8, 2, 1)),
                                          # rows of whole 16-byte vectors: the vector path
                                          (W.DT_BF16, (3, 1, 2, 320)), (W.DT_F16, (1, 8, 2, 4096)),
-                                         (W.DT_F32, (3, 8, 1, 4100)), (W.DT_BF16, (16384,))])
+                                         (W.DT_F32, (3, 8, 1, 4100)), (W.DT_BF16, (16384,)),
+                                         # long rows that are not whole vectors: scanned from the
+                                         # end in batches of 4096 vectors, loose elements at both ends
+                                         (W.DT_BF16, (70001,)), (W.DT_F32, (3, 1, 1, 40001)),
+                                         (W.DT_F16, (1, 8, 2, 32769))])
 def test_capacity_lengths_match_oracle(dtype, shape):
     import torch
     cap = shape[-1] if shape[-1] > 1 else 300
