@@ -273,9 +273,9 @@ sa_status sparse_attn_capacity_lengths(sparse_attn_ctx* ctx, const void* bias, c
  *                    fp8 records) and cur_k (rows in the cache's own format)
  *                    with cache_v = cur_v = NULL.
  *   valid_len, write_pos  device int32 [B] outputs
- * The lengths and the append are one launch when the cache is dense, its rows
- * a multiple of 16 bytes and the tensors 16-byte aligned (Dk == Dv for
- * separate caches). Host errors: those of the four calls, checked before
+ * The reset, the lengths and the append are one launch when the cache is
+ * dense, its rows a multiple of 16 bytes and the tensors 16-byte aligned
+ * (Dk == Dv for separate caches). Host errors: those of the four calls, checked before
  * anything is launched; SA_E_ARG for a V tensor passed with a shared-latent
  * cache or missing with separate ones; SA_E_UNSUPPORTED for separate caches
  * that are not dense. Asynchronous and capturable. */

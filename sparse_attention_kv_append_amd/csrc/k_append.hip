@@ -13,14 +13,7 @@
 namespace sa {
 
 __global__ void reset_error_kernel(ErrorBlock* err) {
-  if (threadIdx.x == 0) {
-    err->word = 0u;
-    err->done_blocks = 0u;
-    err->first_bad = ~0ull;
-    err->call_key = ~0ull;
-    err->detail_class = 0;
-    err->call_word = 0u;
-  }
+  if (threadIdx.x == 0) clear_error_block(err);
 }
 
 sa_status launch_reset_error(sparse_attn_ctx* c) {

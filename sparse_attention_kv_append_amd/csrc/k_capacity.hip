@@ -162,9 +162,11 @@ capacity_append_kernel(const void* __restrict__ bias, int64_t bd0, int64_t bd1, 
                        int64_t keys, int64_t cur_len, int32_t* __restrict__ valid_len,
                        int32_t* __restrict__ write_pos, const uint4* __restrict__ cur_k,
                        const uint4* __restrict__ cur_v, uint4* __restrict__ cache_k, uint4* __restrict__ cache_v,
-                       int64_t heads, int64_t row_bytes) {
+                       int64_t heads, int64_t row_bytes, ErrorBlock* __restrict__ reset_eb) {
   __shared__ int best_s;
   const int64_t b = blockIdx.x;
+  // the step's error reset (no other work of the launch touches the block)
+  if (reset_eb && b == 0 && threadIdx.x == 0) clear_error_block(reset_eb);
   const int v = capacity_scan<DT, VEC>(bias, b, bd0, bd1, bd2, bd3, keys, &best_s);
   const int64_t wp = v >= cur_len ? (int64_t)v - cur_len : 0;  // wp + cur_len <= keys
   if (threadIdx.x == 0) {
@@ -218,14 +220,14 @@ namespace sa {
 sa_status launch_capacity_append(sparse_attn_ctx* c, const void* bias, int dtype, const int64_t* bd, int64_t batch,
                                  int64_t keys, int64_t cur_len, int32_t* valid_len, int32_t* write_pos,
                                  const void* cur_k, const void* cur_v, void* cache_k, void* cache_v, int64_t heads,
-                                 int64_t row_bytes) {
+                                 int64_t row_bytes, ErrorBlock* reset_eb) {
   const dim3 grid((unsigned)batch), block(kCapThreads);
   const int per = dtype == SA_F32 ? 4 : 8;
   const bool vec = bd[3] % per == 0 && ((uintptr_t)bias & 15) == 0;
 #define SA_CAPA(DT, V)                                                                                      \
   hipLaunchKernelGGL((capacity_append_kernel<DT, V>), grid, block, 0, c->stream, bias, bd[0], bd[1], bd[2], \
                      bd[3], keys, cur_len, valid_len, write_pos, (const uint4*)cur_k, (const uint4*)cur_v,   \
-                     (uint4*)cache_k, (uint4*)cache_v, heads, row_bytes)
+                     (uint4*)cache_k, (uint4*)cache_v, heads, row_bytes, reset_eb)
 #define SA_CAPA_V(DT) \
   if (vec) { SA_CAPA(DT, true); } else { SA_CAPA(DT, false); }
   if (dtype == SA_F32) {

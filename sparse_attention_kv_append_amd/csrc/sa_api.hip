@@ -549,19 +549,19 @@ sa_status sparse_attn_capacity_step(sparse_attn_ctx* c, const void* q, int64_t b
   int64_t bd[4];
   s = bias_dims(c, "capacity_step", bias_shape, bias_rank, target, bd);
   if (s != SA_OK) return s;
-  if (reset_error) {
-    s = sa::launch_reset_error(c);
-    if (s != SA_OK) return s;
-  }
   const int64_t row = k.head_dim_qk * elem_bytes(k.dtype);
   const uintptr_t mis = (uintptr_t)cache_k | (uintptr_t)cache_v | (uintptr_t)cur_k | (uintptr_t)cur_v;
   // fp8 records (648 bytes, not whole 16-byte units) go through kv_append
   if (k.cache_format == SA_CACHE_DENSE && (latent || k.head_dim_v == k.head_dim_qk) && row % 16 == 0 &&
       (mis & 15) == 0) {
-    // lengths and the in-place append in one launch
+    // the reset, the lengths and the in-place append in one launch
     s = sa::launch_capacity_append(c, bias, k.dtype, bd, batch, cache_capacity, cur_len, valid_len, write_pos, cur_k,
-                                   cur_v, cache_k, cache_v, k.kv_num_heads, row);
+                                   cur_v, cache_k, cache_v, k.kv_num_heads, row, reset_error ? c->err : nullptr);
   } else {
+    if (reset_error) {
+      s = sa::launch_reset_error(c);
+      if (s != SA_OK) return s;
+    }
     s = sa::launch_capacity_lengths(c, bias, k.dtype, bd, batch, cache_capacity, cur_len, valid_len, write_pos);
     if (s == SA_OK)
       s = sparse_attn_kv_append(c, batch, cache_k, cache_v, cache_capacity, write_pos, cur_k, cur_v, cur_len, 0,

@@ -71,6 +71,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(w >> 16);
 }
 
+// the state of a reset error block (no bit latched, no violation recorded,
+// the per-launch slots and counter armed); written by one thread
+__device__ __forceinline__ void clear_error_block(ErrorBlock* e) {
+  e->word = 0u;
+  e->done_blocks = 0u;
+  e->first_bad = ~0ull;
+  e->call_key = ~0ull;
+  e->detail_class = 0;
+  e->call_word = 0u;
+}
+
 template <int DT>
 __device__ __forceinline__ float load_elem(const void* p, int64_t i) {
   if constexpr (DT == SA_F32) {
@@ -187,10 +198,12 @@ sa_status launch_capacity_lengths(sparse_attn_ctx* c, const void* bias, int dtyp
                                   int32_t* write_pos);
 // the same, then each batch entry's current K and V rows (row_bytes, a
 // multiple of 16; 16-byte aligned tensors) written in place at its write position
+// (with reset_eb: the launch also resets that error block, as
+// launch_reset_error would just before it)
 sa_status launch_capacity_append(sparse_attn_ctx* c, const void* bias, int dtype, const int64_t* bd, int64_t batch,
                                  int64_t keys, int64_t cur_len, int32_t* valid_len, int32_t* write_pos,
                                  const void* cur_k, const void* cur_v, void* cache_k, void* cache_v, int64_t heads,
-                                 int64_t row_bytes);
+                                 int64_t row_bytes, ErrorBlock* reset_eb = nullptr);
 sa_status launch_forward_mla(sparse_attn_ctx* c, const FwdArgs& a, int splits);
 sa_status launch_forward_latent(sparse_attn_ctx* c, const FwdArgs& a, int splits, bool fused,
                                 const AppendArgs* app = nullptr);
