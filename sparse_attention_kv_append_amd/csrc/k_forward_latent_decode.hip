@@ -327,7 +327,7 @@ latent_decode_kernel(const uint16_t* __restrict__ q, uint8_t* __restrict__ cache
     const int st1 = min(c0 + KEYCAP, c1);
     load_keys(c0, st1);
     const uint16_t* qrow0 = q + ((b * NH) * q_seq + qi) * DK;
-    const int qstride = (int)(q_seq * ROWB);  // bytes between heads (q_seq < 256 here)
+    const int qstride = (int)(q_seq * ROWB);  // bytes between heads (63 strides fit 32 bits: checked at launch)
     const __amdgpu_buffer_rsrc_t qrsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)qrow0, (short)0, (NH - 1) * qstride + ROWB, 0x00020000);
 #pragma unroll
