@@ -26,9 +26,13 @@ CASES = {
     "long_cur": DEC.scaled(batch=2, q_seq=12, cur=12, past=300, topk=200, width=210, capacity=330),
     "fp8_split": FP8.scaled(batch=6, past=1200, topk=650, width=650, capacity=1300),
     "fp8_multi_row": FP8.scaled(batch=2, q_seq=3, cur=3, past=400, topk=300, width=300, capacity=420),
+    # 260 rows: one workgroup per row, which records its own row's verdict and
+    # counts toward the launch's record in the same launch as the append
+    "one_split_rows": DEC.scaled(batch=130, q_seq=2, cur=2, past=200, topk=100, width=110, capacity=240),
+    "fp8_one_split_rows": FP8.scaled(batch=130, q_seq=2, cur=2, past=200, topk=100, width=110, capacity=240),
 }
 # fp8 current rows as packed records (byte append) or as bf16 rows quantized on the device
-QUANT = {"fp8_split": [False, True], "fp8_multi_row": [True]}
+QUANT = {"fp8_split": [False, True], "fp8_multi_row": [True], "fp8_one_split_rows": [True]}
 
 
 def banner(msg):
@@ -155,7 +159,7 @@ def bad_rows(idx):
     return out
 
 
-@pytest.mark.parametrize("name", ["decode_split", "long_cur"])
+@pytest.mark.parametrize("name", ["decode_split", "long_cur", "one_split_rows", "fp8_one_split_rows"])
 def test_step_reset_semantics(name):
     """Without reset the step adds its bits to an earlier launch's; with reset
     it replaces them (word, first failing position and message)."""
