@@ -35,6 +35,14 @@ CASES = {
     "causal_group32": GQA.scaled(batch=1, hq=32, hkv=1, q_seq=7, past=90, cur=7, width=100, topk=100),
     "decode_group4": GQA.scaled(batch=3, hq=8, hkv=2, q_seq=1, past=333, cur=1, width=340, topk=200,
                                 pattern="uniform"),
+    # small softcaps, where c tanh(s / c) is far from s: softcap 1 saturates
+    # most scores, softcap 12 bends a few
+    "causal_softcap1": GQA.scaled(batch=2, hq=8, hkv=2, q_seq=40, past=600, cur=40, width=660, topk=660,
+                                  softcap=1.0),
+    "causal_softcap12": GQA.scaled(batch=2, hq=8, hkv=2, q_seq=40, past=600, cur=40, width=660, topk=660,
+                                   softcap=12.0),
+    "decode_softcap12": GQA.scaled(batch=3, hq=8, hkv=2, q_seq=1, past=333, cur=1, width=340, topk=200,
+                                   pattern="uniform", softcap=12.0),
 }
 
 
