@@ -460,3 +460,47 @@ def test_capacity_step_shared_latent(name):
     np.testing.assert_array_equal(to_np(wp), wpos)
     assert np.array_equal(raw_bytes(to_np(kc)), raw_bytes(present))
     check_close(y_as_f32(y), ref, w.dtype, f"capacity step {name}")
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=W.DT_BF16, dk=128, dv=128, q_seq=1, cur=1, seed=11),  # one launch
+                                dict(dk=66, dv=66, seed=13)])                                      # two launches
+def test_capacity_step_reset_semantics(kw):
+    """Without reset the capacity step adds its bits to an earlier launch's;
+    with reset it replaces them, whether the reset rides in the length and
+    append launch or is a launch of its own."""
+    import torch
+    w = W.CAPACITY_WORKLOADS["capacity_small"].scaled(**kw)
+    inp = W.make_capacity_numpy(w)
+    banner(f"capacity step reset semantics {kw}")
+    ctx = make_ctx(w)
+    early = inp["indices"].copy()
+    r = early[-1, 0, -1]
+    r[1], r[2] = r[2], r[1]
+    full = torch.full((w.batch,), w.cap, dtype=torch.int32, device="cuda")
+
+    def latch_early():
+        ctx.reset_error_async()
+        ctx.validate_indices(tt(early), w.batch, 1, w.q_seq, w.width, valid_len=full)
+        return ctx.read_error()
+
+    def step(reset):
+        kc, vc = tt(inp["past_k"]), tt(inp["past_v"])
+        vl = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
+        wp = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
+        y = torch.zeros((w.batch, w.hq, w.q_seq, w.dv), dtype=y_dtype(w), device="cuda")
+        ctx.capacity_step(tt(inp["q"]), w.batch, w.q_seq, kc, vc, w.cap, tt(inp["cur_k"]), tt(inp["cur_v"]), w.cur,
+                          tt(inp["indices"]), 1, w.width, tt(inp["bias"]), y, vl, wp, reset_error=reset)
+        return ctx.read_error()
+
+    e_word, e_fb, e_msg = latch_early()
+    assert e_word == (sa_bits("ORDER") | 512)
+    assert step(False) == (e_word, e_fb, e_msg)  # kept
+    latch_early()
+    w1, fb1, _ = step(True)
+    assert w1 == 0 and fb1 == 2 ** 64 - 1         # replaced by a clean launch
+    ctx.destroy()
+
+
+def sa_bits(name):
+    import sparse_attention_kv_append_amd as sa
+    return getattr(sa, "SA_ERR_" + name)
