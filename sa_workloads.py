@@ -138,6 +138,12 @@ WORKLOADS = {
                              past=0, cur=4096, width=2048, topk=2048, dtype=DT_BF16,
                              layout=LAYOUT_SHARED_LATENT, cache_format=CACHE_DENSE, rope=64,
                              scale=1.0 / 24.0, pattern="causal_prefill", seed=3),
+    # a prefill with more query rows than the eight-wave kernel addresses
+    # (63 head strides of q_seq rows must fit 32 bits): the four-wave kernel
+    "prefill_long_q": Workload("prefill_long_q", batch=1, hq=64, hkv=1, q_seq=29700, dk=576, dv=512, past=0,
+                               cur=29700, width=16, topk=16, dtype=DT_BF16, layout=LAYOUT_SHARED_LATENT,
+                               cache_format=CACHE_DENSE, rope=64, scale=1.0 / 24.0, pattern="causal_prefill",
+                               seed=6),
     "dense_gqa": Workload("dense_gqa", batch=8, hq=32, hkv=8, q_seq=128, dk=128, dv=128,
                           past=8064, cur=128, width=8192, topk=8192, dtype=DT_BF16,
                           layout=LAYOUT_SEPARATE, cache_format=CACHE_DENSE,

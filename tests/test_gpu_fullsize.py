@@ -28,6 +28,9 @@ SAMPLES = {
     "prefill_bf16": [(0, 0), (0, 1), (0, 2046), (0, 2047), (0, 2048), (0, 3001), (0, 4095)],
     "dense_gqa": [(0, 0), (3, 64), (7, 127)],
     "gqa_decode_b2": [(0, 0), (1, 0)],
+    # 29700 query rows: past the eight-wave kernel's addressing, so the
+    # four-wave kernel runs; rows at both ends and at the limit
+    "prefill_long_q": [(0, 0), (0, 15), (0, 29589), (0, 29699)],
 }
 
 
