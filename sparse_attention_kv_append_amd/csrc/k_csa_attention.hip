@@ -19,13 +19,17 @@
 // three, and its product drops the terms below 2^-16 relative (x2*y3, x3*y2,
 // x3*y3). Accumulation is fp32 on the matrix cores.
 //
-// Work split: one workgroup of four waves per (batch, query, 16-head group);
-// wave w owns dims 128w .. 128w+127 of every key and of the output. Per tile
-// each wave stages its own 128-dim slice of the 32 keys into LDS (bf16; a
-// current_kv slice as three bf16 planes), computes the partial S^T over its
-// dims, and the four partials are summed through LDS (one barrier per tile)
-// in a fixed order, so every wave holds the same scores, maxima and sums.
-// Global loads run two tiles ahead in registers.
+// Work split: one workgroup of eight waves per (batch, query, 16-head group),
+// in two streams of four. The candidates are cut into units (16 window rows,
+// or 32 selected records); stream z takes units z, z + 2, z + 4, .. and keeps
+// its own online softmax, and the two merge at the end. In a stream, wave w
+// owns dims 128w .. 128w+127 of every key and of the output: per unit it
+// stages its own 128-dim slice into LDS (bf16; a current_kv slice as three
+// bf16 planes), computes the partial S^T over its dims, and the four partials
+// are summed through LDS (one barrier per pair of units) in a fixed order, so
+// the four waves of a stream hold the same scores, maxima and sums. The two
+// streams' waves of one slice share a SIMD, so one's matrix work and loads
+// overlap the other's softmax and waits. Global loads run one unit ahead.
 //
 // LDS rows of 256 bytes hold 16-byte chunk c of key row R at chunk
 // c ^ 2 (R & 7) ^ ((R >> 3) & 1): the K reads (16 rows x one chunk) and the
@@ -40,29 +44,32 @@ constexpr int D = 512;                  // logical dims of a key / value / query
 constexpr int REC = 583;                // record bytes: 7 x (1 + 64) + 64 x 2
 constexpr int TAILB = 455;              // first BF16 tail byte of a record
 constexpr int WIN = 128;                // dense window
-constexpr int KT = 32;                  // keys per tile
+constexpr int KT = 32;                  // records per record unit
+constexpr int DKT = 16;                 // window rows per dense unit
 constexpr int NH = 16;                  // heads per workgroup
-constexpr int THREADS = 256;
+constexpr int THREADS = 512;            // two streams of four waves
 constexpr int ROWB = 256;               // bytes of one key's 128-dim bf16 slice
-constexpr int PLANE = KT * ROWB;        // 8192
-constexpr int SLOT = 3 * PLANE;         // per wave: three planes
-constexpr int HALF = 16 * ROWB;         // keys 16..31 of a plane
+constexpr int HALF = 16 * ROWB;         // 16 rows: a dense plane, or records 16..31 of a unit
+constexpr int SLOT = 3 * HALF;          // per wave: three dense planes or one record unit
 constexpr int KMAX = 2048;              // selected width limit (the index row lives in LDS)
-constexpr int EXCH_OFF = 4 * SLOT;      // partial-score exchange, two buffers
+constexpr int EXCH_OFF = 8 * SLOT;      // partial-score exchange, two buffers per stream
 constexpr int EXCH_WAVE = 64 * 32;
 constexpr int EXCH_BUF = 4 * EXCH_WAVE;
-constexpr int IDX_OFF = EXCH_OFF + 2 * EXCH_BUF;
+constexpr int IDX_OFF = EXCH_OFF + 4 * EXCH_BUF;
 constexpr int MISC_OFF = IDX_OFF + KMAX * 4;
 constexpr size_t LDS_BYTES = (size_t)MISC_OFF + 16;
+static_assert(LDS_BYTES <= 160 * 1024, "one workgroup per CU");
+static_assert(SLOT >= 8 * 64 * 16 + 3 * 64 * 4, "a slot holds a stream's end state");
 }  // namespace cs
 
 __device__ __forceinline__ int csa_swz(int R, int ch) { return ch ^ (2 * (R & 7)) ^ ((R >> 3) & 1); }
 
-// x = p1 + p2 + p3 exactly for eight fp32 values: three packed bf16x8 pieces,
-// each the nearest bf16 to the remainder of the previous ones
-__device__ __forceinline__ void split3x8(const float (&x)[8], u32x4_l& p1, u32x4_l& p2, u32x4_l& p3) {
+// x = p1 + p2 + p3 exactly for 2N fp32 values: three packed bf16 pieces, each
+// the nearest bf16 to the remainder of the previous ones
+template <int N, typename V>
+__device__ __forceinline__ void split3(const float (&x)[2 * N], V& p1, V& p2, V& p3) {
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < N; i++) {
     const float a = x[2 * i], b = x[2 * i + 1];
     const uint32_t h = pack_bf16x2(a, b);
     const float ra = a - __uint_as_float(h << 16), rb = b - __uint_as_float(h & 0xffff0000u);
@@ -74,14 +81,20 @@ __device__ __forceinline__ void split3x8(const float (&x)[8], u32x4_l& p1, u32x4
   }
 }
 
+typedef unsigned u32x2_l __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ f32x4_l mfma_bf16(u32x4_l a, u32x4_l b, f32x4_l c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_l, a), __builtin_bit_cast(bf16x8_l, b),
                                                  c, 0, 0, 0);
 }
+// the 16-key contraction of a dense unit's O^T update
+__device__ __forceinline__ f32x4_l mfma_bf16_k16(s16x4_l a, u32x2_l b, f32x4_l c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4_l, b), c, 0, 0, 0);
+}
 
-// The body of one wave. TAILW: the wave whose slice holds the BF16 tail
-// (wave 3); the two instantiations issue fixed, different load counts per
-// tile, so the compiler's wait counts stay exact across the loop.
+// The body of one wave. TAILW: a wave whose slice holds the BF16 tail (slice
+// 3); the two instantiations issue fixed, different load counts per unit, so
+// the compiler's wait counts stay exact across the loop.
 template <bool BIAS, bool TAILW>
 __device__ __forceinline__ void
 csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8_t* __restrict__ rec,
@@ -92,7 +105,14 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
   using namespace cs;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  // the wave index as a scalar: the unit loop's branches and the load
+  // descriptors derive from the stream, and stay uniform only if the
+  // compiler knows it is
+  const int wv8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // dim slice, stream: stream 1's slices are rotated by one, so the two
+  // waves of slice 3 (which also decode the BF16 tail) sit on different SIMDs
+  const int z = wv8 >> 2, w = (wv8 + z) & 3;
   const int i16 = lane & 15, g = lane >> 4;
   const int HG = H / NH;
   const int G = B * S * HG;
@@ -142,16 +162,19 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
       if (cand) last = j + 1;
       if ((int64_t)v >= vr) bad = 1;
     }
-    if (last) atomicMax(&misc[0], last);
-    if (bad) atomicOr(&misc[1], 1);
+    // one LDS atomic per wave
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) last = max(last, __shfl_xor(last, off));
+    if (lane == 0 && last) atomicMax(&misc[0], last);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(&misc[1], 1);
   }
   __syncthreads();
-  // wave-uniform by construction; readfirstlane tells the compiler so, and
-  // the tile loop's branches stay scalar (no exec-masked paths)
+  // workgroup-uniform by construction; readfirstlane tells the compiler so,
+  // and the unit loop's branches stay scalar (no exec-masked paths)
   const int nsel = __builtin_amdgcn_readfirstlane(misc[0]);  // slots up to the last index >= 0
   if (misc[1] && tid == 0) atomicOr(&eb->word, SA_ERR_RANGE | SA_ERR_INDEX_ANY);
-  const int nDT = __builtin_amdgcn_readfirstlane((nd + KT - 1) / KT);
-  const int T = nDT + (nsel + KT - 1) / KT;
+  const int nDU = __builtin_amdgcn_readfirstlane((nd + DKT - 1) / DKT);  // dense units
+  const int NU = nDU + (nsel + KT - 1) / KT;                             // all units
 
   // ---- the query slice as three bf16 pieces (B operand of S^T = K . Q^T):
   // lane (head i16, g) holds dims 32 c + 8 g .. + 7 of the wave's slice
@@ -163,11 +186,11 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
     const float4 x0 = *(const float4*)(q + qrow + 128 * w + 32 * c + 8 * g);
     const float4 x1 = *(const float4*)(q + qrow + 128 * w + 32 * c + 8 * g + 4);
     const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    split3x8(xv, qb[0][c], qb[1][c], qb[2][c]);
+    split3<4>(xv, qb[0][c], qb[1][c], qb[2][c]);
   }
 
   // ---- per-lane LDS offsets (within a plane)
-  uint32_t kofs[4];  // K: row i16 (+HALF for keys 16..31), chunk 4 c + g
+  uint32_t kofs[4];  // K: row i16 (+HALF for records 16..31), chunk 4 c + g
 #pragma unroll
   for (int c = 0; c < 4; c++) kofs[c] = (uint32_t)(i16 * ROWB + 16 * csa_swz(i16, 4 * c + g));
   uint32_t vofs[8];  // V^T: lane 4 jj + qq of group g reads row 4 g + jj, dims 16 dt + 4 qq
@@ -177,8 +200,7 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) vofs[dt] = (uint32_t)(R * ROWB + 16 * csa_swz(R, 2 * dt + (qq >> 1)) + 8 * (qq & 1));
   }
-  const uint32_t slot = (uint32_t)(w * SLOT);
-  uint8_t* const slotp = smem + slot;
+  uint8_t* const slotp = smem + wv8 * SLOT;
 
   // ---- global sources
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -189,54 +211,49 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
   if (BIAS)
     bias_row = ((((int64_t)(bb == 1 ? 0 : b) * bh + (bh == 1 ? 0 : head)) * bs + (bs == 1 ? 0 : s)) * bk);
   const int64_t cand_last = Dn + K - 1;
-  constexpr bool tailw = TAILW;  // wave 3's slice is block 6 plus the BF16 tail
+  constexpr bool tailw = TAILW;  // slice 3 is block 6 plus the BF16 tail
 
-  // Loads run in units: a dense tile is two units (keys 0..15, 16..31), a
-  // record tile one. Every unit issues the same instructions (8 x 16 bytes per
-  // lane, plus 3 single bytes in the tail wave and 8 bias words with a bias),
-  // addressed by the unit's kind and out of range where unused, so the
-  // compiler's wait counts are exact and loads run two units ahead.
-  const int NU = 2 * nDT + (T - nDT);
-  u32x4_l raw[2][8];
-  uint32_t rby[2][3];
-  uint32_t rsh[2], rsc[2];
-  float braw[2][8];
-  float bcur[8];  // the bias of the tile being computed (taken out of braw when staged)
+  // Every unit issues the same instructions (8 x 16 bytes per lane, plus 3
+  // single bytes in the tail wave and 8 bias words with a bias), addressed by
+  // the unit's kind and out of range where unused, so the compiler's wait
+  // counts are exact.
+  u32x4_l raw[8];
+  uint32_t rby[3];
+  uint32_t rsh = 0, rsc = 0;
+  float braw[8];
+  float bcur[8];  // the bias of the unit being computed (taken out of braw when staged)
   constexpr uint32_t OOB = 0x80000000u;
 
-  auto issue = [&](int u, auto setc) {
-    constexpr int SET = decltype(setc)::value;
-    const bool dn = u < 2 * nDT;  // uniform
-    const int tile = dn ? (u >> 1) : nDT + (u - 2 * nDT);
-    const int half = dn ? (u & 1) : 0;
-    // dense unit: lane loads key 16 half + (lane >> 4) + 4 gI, 32-byte chunk lane & 15
+  auto issue = [&](int u) {
+    const bool dn = u < nDU;  // uniform
+    // dense unit: lane loads window row 16 u + (lane >> 4) + 4 gI, 32-byte chunk lane & 15
     const int cc = lane & 15;
     uint32_t doff[4];
 #pragma unroll
     for (int gI = 0; gI < 4; gI++) {
-      const int c = KT * tile + 16 * half + (lane >> 4) + 4 * gI;
+      const int c = DKT * u + (lane >> 4) + 4 * gI;
       doff[gI] = (dn && c < nd) ? (uint32_t)(((r0 + c) * D + 128 * w + 8 * cc) * 4) : OOB;
     }
     // record unit: lane loads 64 dims (block 2 w + hb, or the tail) of slot k
     const int k = lane & 31, hb = lane >> 5;
-    int j = KT * (tile - nDT) + k;
+    int j = KT * (u - nDU) + k;
     j = j < 0 ? 0 : (j > KMAX - 1 ? KMAX - 1 : j);
     const int32_t r = idxl[j];
-    const bool ok = !dn && tile < T && r >= 0;
+    const bool ok = !dn && u < NU && r >= 0;
     const bool tail = tailw && hb;
     // a coded block's window starts at the dword of its first code (the scale
     // byte, one before, is loaded by itself); the tail's at its first byte
     const int64_t a = (int64_t)r * REC + (tail ? TAILB : 65 * (2 * w + hb) + 1);
     const uint32_t a4 = ok ? (uint32_t)(a & ~(int64_t)3) : OOB;
-    rsh[SET] = (uint32_t)(a & 3);
-    rsc[SET] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rrsrc, ok ? (uint32_t)(a - 1) : OOB, 0, 0);
+    rsh = (uint32_t)(a & 3);
+    rsc = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rrsrc, ok ? (uint32_t)(a - 1) : OOB, 0, 0);
     const __amdgpu_buffer_rsrc_t rs = dn ? krsrc : rrsrc;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       // records: 80 bytes cover a coded block; the tail wave's lanes take 128
       const uint32_t ro = (i < 5 || tailw) ? (a4 == OOB ? OOB : a4 + 16 * i) : OOB;
       const uint32_t off = dn ? (doff[i >> 1] == OOB ? OOB : doff[i >> 1] + 16 * (i & 1)) : ro;
-      raw[SET][i] = __builtin_bit_cast(u32x4_l, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      raw[i] = __builtin_bit_cast(u32x4_l, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
     if (tailw) {
       // the tail's last bytes sit in dword 32 of the window; for the last
@@ -245,97 +262,104 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
       // needed bytes are loaded one by one
 #pragma unroll
       for (int i = 0; i < 3; i++)
-        rby[SET][i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rrsrc, a4 == OOB ? OOB : a4 + 128 + i, 0, 0);
+        rby[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rrsrc, a4 == OOB ? OOB : a4 + 128 + i, 0, 0);
     }
     if (BIAS) {
-      // lane (head i16, g): keys 16 hh + 4 g + r of the tile
+      // lane (head i16, g): keys 16 hh + 4 g + r of a record unit, keys
+      // 4 g + r of a dense unit (its words 4..7 repeat 0..3)
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         const int kk = 16 * (i >> 2) + 4 * g + (i & 3);
-        int64_t c = dn ? (int64_t)(KT * tile + kk) : Dn + (int64_t)(KT * (tile - nDT) + kk);
+        int64_t c = dn ? (int64_t)(DKT * u + 4 * g + (i & 3)) : Dn + (int64_t)(KT * (u - nDU) + kk);
         c = c < cand_last ? c : cand_last;
-        braw[SET][i] = bias[bias_row + (bk == 1 ? 0 : c)];
+        braw[i] = bias[bias_row + (bk == 1 ? 0 : c)];
       }
     }
   };
 
   // per-lane LDS write offsets of a unit (fixed over the loop)
-  uint32_t dwo[2][4], rwo[8];
+  uint32_t dwo[4], rwo[8];
 #pragma unroll
-  for (int hf = 0; hf < 2; hf++)
-#pragma unroll
-    for (int gI = 0; gI < 4; gI++) {
-      const int kr = 16 * hf + (lane >> 4) + 4 * gI;
-      dwo[hf][gI] = (uint32_t)(kr * ROWB + 16 * csa_swz(kr, lane & 15));
-    }
+  for (int gI = 0; gI < 4; gI++) {
+    const int kr = (lane >> 4) + 4 * gI;
+    dwo[gI] = (uint32_t)(kr * ROWB + 16 * csa_swz(kr, lane & 15));
+  }
 #pragma unroll
   for (int qd = 0; qd < 8; qd++)
     rwo[qd] = (uint32_t)((lane & 31) * ROWB + 16 * csa_swz(lane & 31, 8 * (lane >> 5) + qd));
 
-  // write unit u from register set SET into the wave's LDS slot
-  auto stage = [&](int u, auto setc) {
-    constexpr int SET = decltype(setc)::value;
+  // write unit u from the load registers into the wave's LDS slot
+  auto stage = [&](int u) {
     if (BIAS) {
 #pragma unroll
-      for (int i = 0; i < 8; i++) bcur[i] = braw[SET][i];
+      for (int i = 0; i < 8; i++) bcur[i] = braw[i];
     }
-    if (u < 2 * nDT) {
-      const int cc = lane & 15;
-      const int half = u & 1;
+    if (u < nDU) {
 #pragma unroll
       for (int gI = 0; gI < 4; gI++) {
-        const int kr = 16 * half + (lane >> 4) + 4 * gI;
-        const u32x4_l lo = raw[SET][2 * gI], hi = raw[SET][2 * gI + 1];
+        const u32x4_l lo = raw[2 * gI], hi = raw[2 * gI + 1];
         const float xv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]),
                              __uint_as_float(lo[3]), __uint_as_float(hi[0]), __uint_as_float(hi[1]),
                              __uint_as_float(hi[2]), __uint_as_float(hi[3])};
         u32x4_l p1, p2, p3;
-        split3x8(xv, p1, p2, p3);
-        const uint32_t o = half ? dwo[1][gI] : dwo[0][gI];
-        *(lds_u32x4*)(slotp + o) = p1;
-        *(lds_u32x4*)(slotp + PLANE + o) = p2;
-        *(lds_u32x4*)(slotp + 2 * PLANE + o) = p3;
+        split3<4>(xv, p1, p2, p3);
+        *(lds_u32x4*)(slotp + dwo[gI]) = p1;
+        *(lds_u32x4*)(slotp + HALF + dwo[gI]) = p2;
+        *(lds_u32x4*)(slotp + 2 * HALF + dwo[gI]) = p3;
       }
     } else {
-      const int k = lane & 31, hb = lane >> 5;
-      const uint32_t sh = rsh[SET];
+      const int hb = lane >> 5;
+      const uint32_t sh = rsh;
       uint32_t wv[32];
       if (tailw && hb) {
         uint32_t Dw[33];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-          Dw[4 * i] = raw[SET][i][0];
-          Dw[4 * i + 1] = raw[SET][i][1];
-          Dw[4 * i + 2] = raw[SET][i][2];
-          Dw[4 * i + 3] = raw[SET][i][3];
+          Dw[4 * i] = raw[i][0];
+          Dw[4 * i + 1] = raw[i][1];
+          Dw[4 * i + 2] = raw[i][2];
+          Dw[4 * i + 3] = raw[i][3];
         }
-        Dw[32] = (rby[SET][0] & 0xffu) | ((rby[SET][1] & 0xffu) << 8) | ((rby[SET][2] & 0xffu) << 16);
+        Dw[32] = (rby[0] & 0xffu) | ((rby[1] & 0xffu) << 8) | ((rby[2] & 0xffu) << 16);
 #pragma unroll
         for (int i = 0; i < 32; i++) wv[i] = __builtin_amdgcn_alignbyte(Dw[i + 1], Dw[i], sh);
       } else {
         uint32_t Dw[20];  // codes from byte sh of Dw[0]: 64 + 3 bytes fit 17 dwords
 #pragma unroll
         for (int i = 0; i < 5; i++) {
-          Dw[4 * i] = raw[SET][i][0];
-          Dw[4 * i + 1] = raw[SET][i][1];
-          Dw[4 * i + 2] = raw[SET][i][2];
-          Dw[4 * i + 3] = raw[SET][i][3];
+          Dw[4 * i] = raw[i][0];
+          Dw[4 * i + 1] = raw[i][1];
+          Dw[4 * i + 2] = raw[i][2];
+          Dw[4 * i + 3] = raw[i][3];
         }
-        const uint32_t e = rsc[SET] & 0xffu;
+        const uint32_t e = rsc & 0xffu;
         uint32_t cw[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) cw[i] = __builtin_amdgcn_alignbyte(Dw[i + 1], Dw[i], sh);
-        if (__builtin_amdgcn_ballot_w64(e < 10u || e > 246u) == 0) {
-          const float sc = __uint_as_float(e << 23);
+        // scale bytes 10..246: v_cvt_scalef32_pk_bf16_fp8 is exact (every
+        // code times 2^(e-127) is a bf16 normal); a lane with another byte
+        // redoes its row on the integer path after the stores, in a block
+        // of its own so the common path carries none of it
+        const bool ext = e < 10u || e > 246u;
+        const float sc = __uint_as_float((ext ? 127u : e) << 23);
 #pragma unroll
-          for (int i = 0; i < 16; i++) {
-            wv[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[i], sc, false));
-            wv[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[i], sc, true));
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; i++) fp8x4_to_bf16x4(cw[i], e, wv[2 * i], wv[2 * i + 1]);
+        for (int i = 0; i < 16; i++) {
+          wv[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[i], sc, false));
+          wv[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[i], sc, true));
         }
+#pragma unroll
+        for (int qd = 0; qd < 8; qd++)
+          *(lds_u32x4*)(slotp + rwo[qd]) = (u32x4_l){wv[4 * qd], wv[4 * qd + 1], wv[4 * qd + 2], wv[4 * qd + 3]};
+        if (__builtin_amdgcn_ballot_w64(ext) != 0) {
+          if (ext) {
+#pragma unroll
+            for (int i = 0; i < 16; i++) fp8x4_to_bf16x4(cw[i], e, wv[2 * i], wv[2 * i + 1]);
+#pragma unroll
+            for (int qd = 0; qd < 8; qd++)
+              *(lds_u32x4*)(slotp + rwo[qd]) = (u32x4_l){wv[4 * qd], wv[4 * qd + 1], wv[4 * qd + 2], wv[4 * qd + 3]};
+          }
+        }
+        return;
       }
 #pragma unroll
       for (int qd = 0; qd < 8; qd++)
@@ -350,38 +374,38 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
   float m_run = -INFINITY, m_ref = -INFINITY, l_run = 0.0f;
   constexpr float kTau = 8.0f;  // p <= 2^8 against the reference
 
-  auto compute = [&](int t, int xb) {
-    const bool dense = t < nDT;
-    // ---- partial S^T over this wave's dims: one accumulator per (key half,
-    // query piece), so consecutive MFMAs are independent
-    f32x4_l acc[2][3];
+  // exchange buffers of this stream; lane's partial at lane * 16 (+1024 for
+  // records 16..31 of a record unit)
+  uint8_t* const exs = smem + EXCH_OFF + z * 2 * EXCH_BUF;
+
+  // ---- partial S^T of unit u over this wave's dims, written to the exchange
+  auto scores_out = [&](int u, int xb) {
+    uint8_t* ex = exs + xb * EXCH_BUF + w * EXCH_WAVE + lane * 16;
+    if (u < nDU) {
+      // piece products of weight >= 2^-16: (1,1) (1,2) (2,1) (1,3) (2,2) (3,1),
+      // one accumulator per query piece so consecutive MFMAs are independent
+      f32x4_l acc[3];
 #pragma unroll
-    for (int hh = 0; hh < 2; hh++)
-#pragma unroll
-      for (int pc = 0; pc < 3; pc++) acc[hh][pc] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
-    if (dense) {
+      for (int pc = 0; pc < 3; pc++) acc[pc] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; c++) {
-        u32x4_l k[2][3];
+        u32x4_l k[3];
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++)
-#pragma unroll
-          for (int pl = 0; pl < 3; pl++) k[hh][pl] = *(const lds_u32x4*)(slotp + pl * PLANE + kofs[c] + hh * HALF);
-        // piece products of weight >= 2^-16: (1,1) (1,2) (2,1) (1,3) (2,2) (3,1)
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) acc[hh][0] = mfma_bf16(k[hh][0], qb[0][c], acc[hh][0]);
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) acc[hh][1] = mfma_bf16(k[hh][0], qb[1][c], acc[hh][1]);
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) acc[hh][2] = mfma_bf16(k[hh][1], qb[0][c], acc[hh][2]);
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) acc[hh][1] = mfma_bf16(k[hh][0], qb[2][c], acc[hh][1]);
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) acc[hh][2] = mfma_bf16(k[hh][1], qb[1][c], acc[hh][2]);
-#pragma unroll
-        for (int hh = 0; hh < 2; hh++) acc[hh][0] = mfma_bf16(k[hh][2], qb[0][c], acc[hh][0]);
+        for (int pl = 0; pl < 3; pl++) k[pl] = *(const lds_u32x4*)(slotp + pl * HALF + kofs[c]);
+        acc[0] = mfma_bf16(k[0], qb[0][c], acc[0]);
+        acc[1] = mfma_bf16(k[0], qb[1][c], acc[1]);
+        acc[2] = mfma_bf16(k[1], qb[0][c], acc[2]);
+        acc[1] = mfma_bf16(k[0], qb[2][c], acc[1]);
+        acc[2] = mfma_bf16(k[1], qb[1][c], acc[2]);
+        acc[0] = mfma_bf16(k[2], qb[0][c], acc[0]);
       }
+      *(lds_u32x4*)ex = __builtin_bit_cast(u32x4_l, (acc[0] + acc[1]) + acc[2]);
     } else {
+      f32x4_l acc[2][3];
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+        for (int pc = 0; pc < 3; pc++) acc[hh][pc] = (f32x4_l){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; c++) {
         u32x4_l k[2];
@@ -392,49 +416,44 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
 #pragma unroll
           for (int hh = 0; hh < 2; hh++) acc[hh][pc] = mfma_bf16(k[hh], qb[pc][c], acc[hh][pc]);
       }
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++)
+        *(lds_u32x4*)(ex + 1024 * hh) = __builtin_bit_cast(u32x4_l, (acc[hh][0] + acc[hh][1]) + acc[hh][2]);
     }
-    f32x4_l accs[2];
+  };
+
+  // ---- sum of the stream's four partials (fixed order: identical in its
+  // waves), online softmax (log2 units), O^T += V^T . P^T over this wave's
+  // 128 output dims. NV: scores per lane (4 for a dense unit, 8 for records).
+  auto update = [&](int u, int xb, auto nvc) {
+    constexpr int NV = decltype(nvc)::value;
+    const uint8_t* ex = exs + xb * EXCH_BUF + lane * 16;
+    float sv[NV];
 #pragma unroll
-    for (int hh = 0; hh < 2; hh++) accs[hh] = (acc[hh][0] + acc[hh][1]) + acc[hh][2];
-    // ---- sum the four waves' partials (fixed order: identical in every wave)
-    uint8_t* ex = smem + EXCH_OFF + xb * EXCH_BUF;
-    *(lds_u32x4*)(ex + w * EXCH_WAVE + lane * 32) = __builtin_bit_cast(u32x4_l, accs[0]);
-    *(lds_u32x4*)(ex + w * EXCH_WAVE + lane * 32 + 16) = __builtin_bit_cast(u32x4_l, accs[1]);
-    lds_barrier();
-    float sv[8];
-    {
-      f32x4_l s0 = __builtin_bit_cast(f32x4_l, *(const lds_u32x4*)(ex + lane * 32));
-      f32x4_l s1 = __builtin_bit_cast(f32x4_l, *(const lds_u32x4*)(ex + lane * 32 + 16));
+    for (int hh = 0; hh < NV / 4; hh++) {
+      f32x4_l sum = __builtin_bit_cast(f32x4_l, *(const lds_u32x4*)(ex + 1024 * hh));
 #pragma unroll
-      for (int ww = 1; ww < 4; ww++) {
-        s0 += __builtin_bit_cast(f32x4_l, *(const lds_u32x4*)(ex + ww * EXCH_WAVE + lane * 32));
-        s1 += __builtin_bit_cast(f32x4_l, *(const lds_u32x4*)(ex + ww * EXCH_WAVE + lane * 32 + 16));
-      }
+      for (int ww = 1; ww < 4; ww++)
+        sum += __builtin_bit_cast(f32x4_l, *(const lds_u32x4*)(ex + ww * EXCH_WAVE + 1024 * hh));
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        sv[r] = s0[r];
-        sv[4 + r] = s1[r];
-      }
+      for (int r = 0; r < 4; r++) sv[4 * hh + r] = sum[r];
     }
-    // ---- validity, bias, online softmax (log2 units)
-    bool valid[8];
-    if (dense) {
+    bool valid[NV];
+    if constexpr (NV == 4) {
 #pragma unroll
-      for (int i = 0; i < 8; i++) valid[i] = KT * t + 16 * (i >> 2) + 4 * g + (i & 3) < nd;
+      for (int i = 0; i < NV; i++) valid[i] = DKT * u + 4 * g + i < nd;
     } else {
-      const int j0 = KT * (t - nDT) + 4 * g;
+      const int j0 = KT * (u - nDU) + 4 * g;
 #pragma unroll
-      for (int hh = 0; hh < 2; hh++) {
+      for (int hh = 0; hh < NV / 4; hh++) {
         const u32x4_l iv = *(const __attribute__((address_space(3))) u32x4_l*)(idxl + j0 + 16 * hh);
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-          valid[4 * hh + r] = (int32_t)iv[r] >= 0;
-        }
+        for (int r = 0; r < 4; r++) valid[4 * hh + r] = (int32_t)iv[r] >= 0;
       }
     }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < NV; i++) {
       float x = sv[i] * fs;
       if (BIAS) x += bcur[i] * kLog2eL;
       sv[i] = valid[i] ? x : -INFINITY;
@@ -453,49 +472,52 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
       for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
       m_ref = m_new;
     }
-    float pv[8], psum = 0.0f;
+    float pv[NV], psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      pv[i] = sv[i] == -INFINITY ? 0.0f : exp2f(sv[i] - m_ref);
+    for (int i = 0; i < NV; i++) {
+      // the hardware exp2: a result below 2^-126 may flush to zero, far
+      // below an fp32 ulp of the sum (which holds a term >= 1)
+      pv[i] = sv[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[i] - m_ref);
       psum += pv[i];
     }
     psum = sum_x32(sum_x16(psum));
     l_run += psum;
-    u32x4_l pb[3];
-    split3x8(pv, pb[0], pb[1], pb[2]);
-    // ---- O^T += V^T . P^T over this wave's 128 output dims; the eight dv
-    // tiles' MFMAs of one piece product are independent of each other
     typedef __attribute__((address_space(3))) s16x4_l lds_s16x4;
-    auto vload = [&](int pl, int dt) {
-      const s16x4_l a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + pl * PLANE + vofs[dt]));
-      const s16x4_l a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + pl * PLANE + vofs[dt] + HALF));
-      const s16x4_l a8[2] = {a0, a1};
-      return __builtin_bit_cast(u32x4_l, a8);
+    auto vload = [&](int pl, int dt, int hh) {
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + pl * HALF + vofs[dt] + hh * HALF));
     };
-    if (dense) {
-      u32x4_l v0[8], v1[8];
+    if constexpr (NV == 4) {
+      // the three planes of 16 keys; piece products as for the scores
+      u32x2_l pb[3];
+      split3<2>(*(const float(*)[4])pv, pb[0], pb[1], pb[2]);
+      s16x4_l v0[8], v1[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) v0[dt] = vload(0, dt);
+      for (int dt = 0; dt < 8; dt++) v0[dt] = vload(0, dt, 0);
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) v1[dt] = vload(1, dt);
+      for (int dt = 0; dt < 8; dt++) v1[dt] = vload(1, dt, 0);
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v0[dt], pb[0], o[dt]);
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v0[dt], pb[0], o[dt]);
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v0[dt], pb[1], o[dt]);
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v0[dt], pb[1], o[dt]);
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v1[dt], pb[0], o[dt]);
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v1[dt], pb[0], o[dt]);
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v0[dt], pb[2], o[dt]);
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v0[dt], pb[2], o[dt]);
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v1[dt], pb[1], o[dt]);
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v1[dt], pb[1], o[dt]);
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) v0[dt] = vload(2, dt);
+      for (int dt = 0; dt < 8; dt++) v0[dt] = vload(2, dt, 0);
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v0[dt], pb[0], o[dt]);
+      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v0[dt], pb[0], o[dt]);
     } else {
+      u32x4_l pb[3];
+      split3<4>(*(const float(*)[8])pv, pb[0], pb[1], pb[2]);
       u32x4_l v[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) v[dt] = vload(0, dt);
+      for (int dt = 0; dt < 8; dt++) {
+        const s16x4_l a8[2] = {vload(0, dt, 0), vload(0, dt, 1)};
+        v[dt] = __builtin_bit_cast(u32x4_l, a8);
+      }
 #pragma unroll
       for (int pc = 0; pc < 3; pc++)
 #pragma unroll
@@ -503,46 +525,61 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
     }
   };
 
-  const std::integral_constant<int, 0> set0;
-  const std::integral_constant<int, 1> set1;
-  // unit u completes a tile when it is a record unit or a dense tile's second half
-  auto unit_tile = [&](int u) { return u < 2 * nDT ? (u >> 1) : nDT + (u - 2 * nDT); };
-  auto completes = [&](int u) { return u >= 2 * nDT || (u & 1); };
-  int xb = 0;
-  issue(0, set0);
-  issue(1, set1);
-  int u = 0;
-  for (; u + 1 < NU; u += 2) {
-    stage(u, set0);
-    issue(u + 2, set0);
-    if (completes(u)) {
-      compute(unit_tile(u), xb);
-      xb ^= 1;
+  // ---- the unit loop: stream z takes units z, z + 2, ..; both streams run
+  // the same number of iterations, one barrier each, so every wave meets
+  // every barrier
+  const std::integral_constant<int, 4> nv4;
+  const std::integral_constant<int, 8> nv8;
+  const int NI = (NU + 1) >> 1;
+  issue(z);
+  for (int it = 0; it < NI; it++) {
+    const int u = 2 * it + z;
+    const bool has = u < NU;  // uniform
+    const int xb = it & 1;
+    if (has) stage(u);
+    issue(u + 2);
+    if (has) scores_out(u, xb);
+    lds_barrier();
+    if (has) {
+      if (u < nDU)
+        update(u, xb, nv4);
+      else
+        update(u, xb, nv8);
     }
-    stage(u + 1, set1);
-    issue(u + 3, set1);
-    if (completes(u + 1)) {
-      compute(unit_tile(u + 1), xb);
-      xb ^= 1;
-    }
-  }
-  if (u < NU) {
-    stage(u, set0);
-    compute(unit_tile(u), xb);
   }
 
-  // ---- Y = O / (l + exp(sink - m)); a head with no candidate gives zeros
-  // against the true maximum m: den = l e^(m_ref - m) + e^(sink - m)
-  const bool none = m_run == -INFINITY;
-  const float fr = none ? 0.0f : exp2f(m_ref - m_run);
-  const float den = l_run * fr + exp2f(sink[head] * kLog2eL - m_run);
+  // ---- merge the streams: stream 1 leaves (O, m_run, m_ref, l) in its slot,
+  // stream 0 combines and writes Y = O / (l + exp(sink - m)) against the true
+  // maximum m; a head with no candidate gives zeros
+  float* const endst = (float*)slotp;
+  if (z == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) *(lds_u32x4*)(slotp + 16 * (8 * lane + dt)) = __builtin_bit_cast(u32x4_l, o[dt]);
+    endst[8 * 64 * 4 + lane] = m_run;
+    endst[8 * 64 * 4 + 64 + lane] = m_ref;
+    endst[8 * 64 * 4 + 128 + lane] = l_run;
+  }
+  __syncthreads();
+  if (z == 1) return;
+  const uint8_t* const pslot = smem + (4 + ((w + 3) & 3)) * SLOT;  // stream 1's wave of slice w
+  const float* const pend = (const float*)pslot;
+  const float m1 = pend[8 * 64 * 4 + lane], mr1 = pend[8 * 64 * 4 + 64 + lane], l1 = pend[8 * 64 * 4 + 128 + lane];
+  const float mx = fmaxf(m_run, m1);
+  const bool none = mx == -INFINITY;
+  // each stream's terms are scaled from its reference to mx (a stream with no
+  // candidate has reference -inf and weight 0)
+  const float f0 = none ? 0.0f : exp2f(m_ref - mx);
+  const float f1 = none ? 0.0f : exp2f(mr1 - mx);
+  const float den = l_run * f0 + l1 * f1 + exp2f(sink[head] * kLog2eL - mx);
   const bool bad = !none && !(den > 0.0f && den < INFINITY);
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(&eb->word, SA_ERR_CSA_DENOM);
-  const float inv = none ? 0.0f : fr / den;
+  const float inv = none ? 0.0f : 1.0f / den;
   float* yrow = y + qrow + 128 * w + 4 * g;
 #pragma unroll
   for (int dt = 0; dt < 8; dt++) {
-    const f32x4_l r = o[dt] * inv;
+    const f32x4_l o1 = __builtin_bit_cast(f32x4_l, *(const lds_u32x4*)(pslot + 16 * (8 * lane + dt)));
+    f32x4_l r = (o[dt] * f0 + o1 * f1) * inv;
+    if (none) r = (f32x4_l){0.f, 0.f, 0.f, 0.f};
     *(float4*)(yrow + 16 * dt) = make_float4(r[0], r[1], r[2], r[3]);
   }
 }
@@ -555,7 +592,8 @@ csa_attention_kernel(const float* __restrict__ q, const float* __restrict__ ckv,
                      const int64_t* __restrict__ total_ptr, float* __restrict__ y, int B, int S, int H,
                      int Tcur, int64_t rcap, int idx_heads, int K, int bb, int bh, int bs, int bk,
                      float scale, ErrorBlock* __restrict__ eb) {
-  if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) == 3)
+  const int wv8 = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (((wv8 + (wv8 >> 2)) & 3) == 3)
     csa_wave<BIAS, true>(q, ckv, rec, sel, sink, bias, total_ptr, y, B, S, H, Tcur, rcap, idx_heads, K, bb, bh,
                          bs, bk, scale, eb);
   else
