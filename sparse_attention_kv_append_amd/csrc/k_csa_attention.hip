@@ -56,7 +56,7 @@ constexpr int EXCH_OFF = 8 * SLOT;      // partial-score exchange, two buffers p
 constexpr int EXCH_WAVE = 64 * 32;
 constexpr int EXCH_BUF = 4 * EXCH_WAVE;
 constexpr int IDX_OFF = EXCH_OFF + 4 * EXCH_BUF;
-constexpr int MISC_OFF = IDX_OFF + KMAX * 4;
+constexpr int MISC_OFF = IDX_OFF + (KMAX + KT) * 4;  // the row plus one unit of padding
 constexpr size_t LDS_BYTES = (size_t)MISC_OFF + 16;
 static_assert(LDS_BYTES <= 160 * 1024, "one workgroup per CU");
 static_assert(SLOT >= 8 * 64 * 16 + 3 * 64 * 4, "a slot holds a stream's end state");
@@ -149,6 +149,7 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
     misc[0] = 0;
     misc[1] = 0;
   }
+  if (tid < KT) idxl[KMAX + tid] = -1;  // read by a unit past the end
   __syncthreads();
   {
     const int32_t* srow = sel + ((int64_t)b * idx_heads * S + s) * K;
@@ -424,13 +425,21 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
 
   // ---- sum of the stream's four partials (fixed order: identical in its
   // waves), online softmax (log2 units), O^T += V^T . P^T over this wave's
-  // 128 output dims. NV: scores per lane (4 for a dense unit, 8 for records).
-  auto update = [&](int u, int xb, auto nvc) {
-    constexpr int NV = decltype(nvc)::value;
+  // 128 output dims. One code path for both kinds of unit, so O stays in
+  // place across the loop. Lane (head i16, g) holds 8 scores: keys 4g+r and
+  // 16+4g+r of a record unit; of a dense unit only the first four are keys.
+  //
+  // A k=32 product takes two 4-key operand halves: for a record unit the
+  // two key halves of one bf16 plane; for a dense unit two of its planes
+  // over the same 4 keys, with the probability pieces doubled to match, so
+  // its six piece products (1,1)+(2,1), (1,2)+(2,2), (1,3)+(3,1) also take
+  // three products per output tile.
+  auto update = [&](int u, int xb) {
+    const bool dense = u < nDU;  // uniform
     const uint8_t* ex = exs + xb * EXCH_BUF + lane * 16;
-    float sv[NV];
+    float sv[8];
 #pragma unroll
-    for (int hh = 0; hh < NV / 4; hh++) {
+    for (int hh = 0; hh < 2; hh++) {
       f32x4_l sum = __builtin_bit_cast(f32x4_l, *(const lds_u32x4*)(ex + 1024 * hh));
 #pragma unroll
       for (int ww = 1; ww < 4; ww++)
@@ -438,14 +447,14 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
 #pragma unroll
       for (int r = 0; r < 4; r++) sv[4 * hh + r] = sum[r];
     }
-    bool valid[NV];
-    if constexpr (NV == 4) {
+    bool valid[8];
+    if (dense) {
 #pragma unroll
-      for (int i = 0; i < NV; i++) valid[i] = DKT * u + 4 * g + i < nd;
+      for (int i = 0; i < 8; i++) valid[i] = i < 4 && DKT * u + 4 * g + i < nd;
     } else {
       const int j0 = KT * (u - nDU) + 4 * g;
 #pragma unroll
-      for (int hh = 0; hh < NV / 4; hh++) {
+      for (int hh = 0; hh < 2; hh++) {
         const u32x4_l iv = *(const __attribute__((address_space(3))) u32x4_l*)(idxl + j0 + 16 * hh);
 #pragma unroll
         for (int r = 0; r < 4; r++) valid[4 * hh + r] = (int32_t)iv[r] >= 0;
@@ -453,7 +462,7 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
     }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
+    for (int i = 0; i < 8; i++) {
       float x = sv[i] * fs;
       if (BIAS) x += bcur[i] * kLog2eL;
       sv[i] = valid[i] ? x : -INFINITY;
@@ -472,9 +481,9 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
       for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
       m_ref = m_new;
     }
-    float pv[NV], psum = 0.0f;
+    float pv[8], psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
+    for (int i = 0; i < 8; i++) {
       // the hardware exp2: a result below 2^-126 may flush to zero, far
       // below an fp32 ulp of the sum (which holds a term >= 1)
       pv[i] = sv[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[i] - m_ref);
@@ -482,70 +491,47 @@ csa_wave(const float* __restrict__ q, const float* __restrict__ ckv, const uint8
     }
     psum = sum_x32(sum_x16(psum));
     l_run += psum;
+#pragma unroll
+    for (int i = 0; i < 4; i++) pv[4 + i] = dense ? pv[i] : pv[4 + i];
+    u32x4_l pb[3];
+    split3<4>(pv, pb[0], pb[1], pb[2]);
+    u32x4_l pb2 = pb[2];  // dense: (piece 3, piece 1) of the four keys
+    pb2[2] = dense ? pb[0][0] : pb2[2];
+    pb2[3] = dense ? pb[0][1] : pb2[3];
     typedef __attribute__((address_space(3))) s16x4_l lds_s16x4;
-    auto vload = [&](int pl, int dt, int hh) {
-      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + pl * HALF + vofs[dt] + hh * HALF));
-    };
-    if constexpr (NV == 4) {
-      // the three planes of 16 keys; piece products as for the scores
-      u32x2_l pb[3];
-      split3<2>(*(const float(*)[4])pv, pb[0], pb[1], pb[2]);
-      s16x4_l v0[8], v1[8];
+    auto vload = [&](uint32_t off) { return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slotp + off)); };
+    const uint32_t hi2 = dense ? 2 * HALF : HALF;  // second half of the third product's operand
+    u32x4_l va[8], vb[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) v0[dt] = vload(0, dt, 0);
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) v1[dt] = vload(1, dt, 0);
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v0[dt], pb[0], o[dt]);
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v0[dt], pb[1], o[dt]);
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v1[dt], pb[0], o[dt]);
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v0[dt], pb[2], o[dt]);
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v1[dt], pb[1], o[dt]);
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) v0[dt] = vload(2, dt, 0);
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16_k16(v0[dt], pb[0], o[dt]);
-    } else {
-      u32x4_l pb[3];
-      split3<4>(*(const float(*)[8])pv, pb[0], pb[1], pb[2]);
-      u32x4_l v[8];
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) {
-        const s16x4_l a8[2] = {vload(0, dt, 0), vload(0, dt, 1)};
-        v[dt] = __builtin_bit_cast(u32x4_l, a8);
-      }
-#pragma unroll
-      for (int pc = 0; pc < 3; pc++)
-#pragma unroll
-        for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(v[dt], pb[pc], o[dt]);
+    for (int dt = 0; dt < 8; dt++) {
+      const s16x4_l lo = vload(vofs[dt]), hi = vload(vofs[dt] + HALF), h2 = vload(vofs[dt] + hi2);
+      const s16x4_l a8[2] = {lo, hi}, b8[2] = {lo, h2};
+      va[dt] = __builtin_bit_cast(u32x4_l, a8);
+      vb[dt] = __builtin_bit_cast(u32x4_l, b8);
     }
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(va[dt], pb[0], o[dt]);
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(va[dt], pb[1], o[dt]);
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) o[dt] = mfma_bf16(vb[dt], pb2, o[dt]);
   };
 
   // ---- the unit loop: stream z takes units z, z + 2, ..; both streams run
   // the same number of iterations, one barrier each, so every wave meets
-  // every barrier
-  const std::integral_constant<int, 4> nv4;
-  const std::integral_constant<int, 8> nv8;
+  // every barrier. A stream with no unit left in the last iteration runs a
+  // unit past the end: its loads are out of range (zeros), its index slots
+  // are padding, so it adds nothing.
   const int NI = (NU + 1) >> 1;
   issue(z);
   for (int it = 0; it < NI; it++) {
     const int u = 2 * it + z;
-    const bool has = u < NU;  // uniform
     const int xb = it & 1;
-    if (has) stage(u);
+    stage(u);
     issue(u + 2);
-    if (has) scores_out(u, xb);
+    scores_out(u, xb);
     lds_barrier();
-    if (has) {
-      if (u < nDU)
-        update(u, xb, nv4);
-      else
-        update(u, xb, nv8);
-    }
+    update(u, xb);
   }
 
   // ---- merge the streams: stream 1 leaves (O, m_run, m_ref, l) in its slot,
