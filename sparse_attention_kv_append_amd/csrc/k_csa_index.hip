@@ -248,28 +248,35 @@ csa_index_score_kernel(const uint16_t* __restrict__ qf, const uint8_t* __restric
     }
     if (tid == 0) qr[HMAX] = lo | (hi << 8);
   }  // read after the first pass's barriers
-  const uint32_t* kb = (const uint32_t*)(keys + (b * kcap) * KB);
+  // keys of the next two passes in flight (two register sets), each issue
+  // the same loads with out-of-range offsets past the workgroup's records,
+  // so the compiler's wait counts are exact
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(keys + (b * kcap) * KB), (short)0, (int)(kcap * KB), 0x00020000);
   constexpr int KW = RB * KB / 4;              // dwords of a pass's keys
   constexpr int KL = (KW + 255) / 256;         // loads per thread
-  uint32_t kr[KL];
-  auto load_keys = [&](int64_t r0) {
-    const int64_t lim = (min((int64_t)RB, kcap - r0)) * (KB / 4);  // dwords inside the capacity
+  uint32_t kra[KL], krb[KL];
+  auto load_keys = [&](uint32_t (&kr)[KL], int64_t r0) {
+    const int64_t left = c1 - r0;
+    const int64_t lim = (left < 0 ? 0 : (left > RB ? RB : left)) * (KB / 4);  // dwords of this pass's records
 #pragma unroll
     for (int j = 0; j < KL; j++) {
       const int i = tid + 256 * j;
-      kr[j] = (i < KW && i < lim) ? kb[r0 * (KB / 4) + i] : 0u;
+      const uint32_t off = (i < KW && i < lim) ? (uint32_t)((r0 * (KB / 4) + i) * 4) : 0x80000000u;
+      kr[j] = __builtin_amdgcn_raw_buffer_load_b32(krs, off, 0, 0);
     }
   };
   bool bad = false;
-  load_keys(c0);
-  for (int64_t r0 = c0; r0 < c1; r0 += RB) {
+  load_keys(kra, c0);
+  load_keys(krb, c0 + RB);
+  auto pass = [&](int64_t r0, uint32_t (&kr)[KL]) {
     __syncthreads();  // the previous pass's LDS reads are done
 #pragma unroll
     for (int j = 0; j < KL; j++) {
       const int i = tid + 256 * j;
       if (i < KW) ((uint32_t*)kl)[i] = kr[j];
     }
-    if (r0 + RB < c1) load_keys(r0 + RB);
+    load_keys(kr, r0 + 2 * RB);
     __syncthreads();
     // S^T for the wave's two record tiles: all operand reads first, then the MFMAs
     bf16x8_l av[2][4];
@@ -351,6 +358,10 @@ csa_index_score_kernel(const uint16_t* __restrict__ qf, const uint8_t* __restric
       bad |= !isfinite(score);
       scores[row * kcap + r] = score;
     }
+  };
+  for (int64_t r0 = c0; r0 < c1; r0 += 2 * RB) {
+    pass(r0, kra);
+    if (r0 + RB < c1) pass(r0 + RB, krb);
   }
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(&eb->word, SA_ERR_INDEX_NONFINITE);
 }
