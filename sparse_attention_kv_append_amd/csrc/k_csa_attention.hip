@@ -27,9 +27,9 @@
 // stages its own 128-dim slice into LDS (bf16; a current_kv slice as three
 // bf16 planes), computes the partial S^T over its dims, and the four partials
 // are summed through LDS (one barrier per pair of units) in a fixed order, so
-// the four waves of a stream hold the same scores, maxima and sums. The two
-// streams' waves of one slice share a SIMD, so one's matrix work and loads
-// overlap the other's softmax and waits. Global loads run one unit ahead.
+// the four waves of a stream hold the same scores, maxima and sums. With
+// two waves per SIMD, one wave's matrix work and loads overlap the other's
+// softmax and waits. Global loads run one unit ahead.
 //
 // LDS rows of 256 bytes hold 16-byte chunk c of key row R at chunk
 // c ^ 2 (R & 7) ^ ((R >> 3) & 1): the K reads (16 rows x one chunk) and the
